@@ -1,0 +1,249 @@
+/*
+ * kvc.h -- C ABI of libkvc: KV-cache scoring and compression for one attention layer on an
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library scores every cached KV unit by the attention it receives and compresses the
+ * cache to a mixed-width, partly evicted form:
+ *
+ *   kvc_row_lse            row log-sum-exp of the causal, scaled logits        (pass 1)
+ *   kvc_score_tokens       per-token scores, RDKV sum or KVzip+ max            (pass 2)
+ *   kvc_channel_weights    RDKV K-channel weights
+ *   kvc_allocate_bits      Lagrangian width allocation over {0,2,4,8,16}, or top-k keep
+ *   kvc_quantize_pack      group quantisation and packing into the width zones
+ *   kvc_compressed_attend  attention output and LSE over a packed cache
+ *
+ * Sources (summary pages of the papers; section numbers are the pages' own):
+ *   "RDKV - rate-distortion bit allocation for joint eviction and quantization of the KV
+ *    cache": §2.1 distortion weights and objective, §2.2 three-stage allocation, §2.3 packed
+ *    zones with fused dequantisation.
+ *   "KVzap - fast, adaptive and faithful KV cache pruning": §2.1 KVzip+ score, §2.2 one score
+ *    per KV head, §2.3 fixed-budget keep of KVzip.
+ *   "KVSculpt: KV Cache Compression as Distillation": §2 loss terms (output error and LSE
+ *    error) that the fidelity attend measures.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Memory: the caller owns all memory.  Every pointer argument named as data (q, k, v, lse,
+ *   scores, weights, bits, packed buffers, ws, result) is DEVICE memory on the current HIP
+ *   device; descriptors and kvc_packed_cache structs are HOST memory holding device
+ *   pointers.  The library never allocates device memory and keeps no per-call state.
+ *   Outputs must not alias inputs.  Data pointers must be 16-byte aligned.
+ * Layouts (row-major, bf16 = IEEE bfloat16 bit patterns):
+ *   Q      bf16 [H_q][Nq][d]     K, V  bf16 [H_kv][N][d]
+ *   lse    f32  [H_q][Nq]        scores f32 [H_kv][N]      w_c f32 [H_kv][d]
+ *   bits_v u8   [H_kv][N]        bits_k u8  [H_kv][d]
+ *   query head h reads KV head h / (H_q / H_kv).  Query row i sits at position N - Nq + i
+ *   (the rows are the last Nq positions); with causal = 1 it sees key t iff t <= N - Nq + i.
+ * Streams: every call only enqueues work on `hip_stream` (a hipStream_t; NULL = the default
+ *   stream) and returns; there is no hidden synchronisation.
+ * Errors: argument errors are detected on the host and returned before anything is
+ *   enqueued.  KVC_ERR_HIP means a HIP runtime call failed; kvc_last_error() gives the
+ *   detail (thread-local).  Data errors only visible on the device (a width outside
+ *   {0,2,4,8,16}, a packed cache that does not match the descriptor) are recorded in the
+ *   status word at the start of `ws`; read it with kvc_get_device_status().
+ */
+#ifndef KVC_H_
+#define KVC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVC_OK = 0,
+  KVC_ERR_INVALID_ARG = 1,   /* null pointer, bad shape, misalignment, bad enum value      */
+  KVC_ERR_UNSUPPORTED = 2,   /* valid request outside what is built (head_dim, group size) */
+  KVC_ERR_WORKSPACE = 3,     /* ws_bytes smaller than kvc_workspace_size()                  */
+  KVC_ERR_NO_DEVICE = 4,     /* no HIP device, or the current device is not gfx950          */
+  KVC_ERR_HIP = 5,           /* a HIP runtime call failed (detail in kvc_last_error())      */
+  KVC_ERR_DEVICE_DATA = 6    /* device-side data error (see kvc_get_device_status())        */
+} kvc_status;
+
+/* One attention layer.  Limits: H_q % H_kv == 0, 1 <= H_kv, H_q / H_kv <= 16,
+ * head_dim in {64, 128}, 1 <= Nq <= N < 2^29.  softmax_scale == 0 means 1/sqrt(head_dim). */
+typedef struct {
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t causal;            /* 1: row i sees keys t <= N - Nq + i; 0: every row sees all N */
+  int64_t n_keys;            /* N  */
+  int64_t n_queries;         /* Nq */
+  float softmax_scale;
+  int32_t reserved;          /* must be 0 */
+} kvc_layer_desc;
+
+/* Operation ids for kvc_workspace_size(). */
+enum {
+  KVC_OP_ROW_LSE = 0,
+  KVC_OP_SCORE_TOKENS = 1,
+  KVC_OP_CHANNEL_WEIGHTS = 2,
+  KVC_OP_ALLOCATE_BITS = 3,
+  KVC_OP_QUANTIZE_PACK = 4,
+  KVC_OP_COMPRESSED_ATTEND = 5
+};
+
+/* Bytes of device workspace `op` needs for `desc` (`mode` = score mode or allocation stage,
+ * ignored otherwise).  Returns 0 for an invalid descriptor.  A larger workspace is fine. */
+size_t kvc_workspace_size(int32_t op, const kvc_layer_desc* desc, int32_t mode);
+
+/* Pass 1.  lse[h][i] = ln sum_{t visible} exp(scale * q_{h,i} . k_{g(h),t}) (natural log, the
+ * scale included): the attention mass KVSculpt's loss matches (KVSculpt §2) and the
+ * normaliser of RDKV's attention probabilities (RDKV §2.1).  bf16 matrix-core products with
+ * float32 accumulation.  Workspace: none (ws may be NULL when ws_bytes == 0). */
+kvc_status kvc_row_lse(const kvc_layer_desc* desc, const void* q, const void* k, float* lse,
+                       void* ws, size_t ws_bytes, void* hip_stream);
+
+typedef enum { KVC_SCORE_SUM = 0, KVC_SCORE_MAX = 1 } kvc_score_mode;
+
+/* Extra inputs of the KVzip+ score (KVzap §2.1); required iff mode == KVC_SCORE_MAX. */
+typedef struct {
+  const void* hidden;        /* bf16 [Nq][D_h]: hidden state h_j of each query row          */
+  const void* w_o;           /* bf16 [D_h][H_q*d]: output projection, Linear weight (out x in) */
+  const void* v;             /* bf16 [H_kv][N][d] */
+  int32_t hidden_dim;        /* D_h, a positive multiple of 8 */
+  int32_t reserved;          /* must be 0 */
+} kvc_kvzip_args;
+
+/* Pass 2.  With a = exp(scale q.k - lse) (lse from kvc_row_lse):
+ *   SUM: scores[g][t] = sum over the group's query heads h and visible rows i of a_{h,i,t}
+ *        (RDKV §2.1 token distortion weight);
+ *   MAX: scores[g][t] = max over the group's heads h of
+ *        ( max over visible rows j of a_{h,j,t} * ||hidden_j|| ) / ||W_O^(h) v_{g,t}||,
+ *        W_O^(h) = columns [h*d, (h+1)*d) of W_O (KVzap §2.1, one score per KV head §2.2);
+ *        a zero value norm gives +inf (0 if the numerator is 0).
+ * Column reductions run in a fixed order: results are bitwise reproducible. */
+kvc_status kvc_score_tokens(const kvc_layer_desc* desc, kvc_score_mode mode, const void* q,
+                            const void* k, const float* lse, const kvc_kvzip_args* zip,
+                            float* scores, void* ws, size_t ws_bytes, void* hip_stream);
+
+/* RDKV §2.1 channel weight: w_c[g][c] = scale * ||Q_g[:,c]||_2 * ||K_g[:,c]||_2, Q_g stacking
+ * every row of every query head of group g, K_g the whole cache of head g (computed once on the
+ * full cache, RDKV §2.2 stage 1).  Sums of squares are accumulated in float64. */
+kvc_status kvc_channel_weights(const kvc_layer_desc* desc, const void* q, const void* k,
+                               float* w_c, void* ws, size_t ws_bytes, void* hip_stream);
+
+typedef enum {
+  KVC_ALLOC_V_TOKENS = 0,    /* RDKV stage 2: units (g,t), size d                            */
+  KVC_ALLOC_K_CHANNELS = 1,  /* RDKV stage 3: units (g,c), size R_g = #tokens with bits_v > 0 */
+  KVC_ALLOC_TOPK = 2         /* KVzip fixed budget: keep floor(rho*N) best tokens per head    */
+} kvc_alloc_stage;
+
+/* Allocation result, written to DEVICE memory by kvc_allocate_bits. */
+typedef struct {
+  double lambda;             /* lambda* (V/K stages); the kept score threshold (TOPK)         */
+  int64_t budget_bits;       /* B = floor(avg * elements covered) (V/K); kept*d*keep_bits (TOPK) */
+  int64_t used_bits;         /* sum_u size_u * b_u                                             */
+  double distortion;         /* sum_u c_u 2^-b_u (V/K); 0 (TOPK)                               */
+} kvc_alloc_result;
+
+/* RDKV §2.1-§2.2: minimise sum_u c_u 2^-b_u subject to sum_u size_u b_u <= B over widths
+ * {0,2,4,8,16}, c_u = float32(weight_u * sigma_u) (sigma NULL: c_u = weight_u), by reverse
+ * water-filling with one multiplier per call.  Exact rule: the key of step k of unit u is
+ * (c_u * num_k) / (size_u * den_k) in float64 with theta_k = num_k/den_k = 3/8, 3/32, 15/1024,
+ * 255/524288; lambda* is the smallest key (or 0) whose rate of steps with key > lambda* fits
+ * B; every step with key > lambda* is taken, then steps with key == lambda* in ascending unit
+ * index (unit = g*N + t or g*d + c) until the first that does not fit.  Units with c_u <= 0,
+ * NaN, or size 0 get width 0.  B = floor(avg_bits_per_elem * E), E = H_kv*N*d (V stage) or
+ * d * sum_g R_g (K stage, counted on the device from bits_v).
+ * TOPK (KVzap §2.3 describes KVzip's fixed keep): per KV head keep the floor(keep_fraction*N)
+ * highest scores at width keep_bits (ties to the lower index), others 0.
+ * weight: f32 [H_kv][N] (V, TOPK) or [H_kv][d] (K).  sigma: same shape or NULL (ignored by
+ * TOPK).  bits_v: u8 [H_kv][N], K stage only (else NULL).  bits_out: u8, same shape as
+ * weight.  result_dev: device kvc_alloc_result, may be NULL.
+ * Errors: avg_bits_per_elem < 0 or not finite, keep_fraction outside [0,1], keep_bits not in
+ * {2,4,8,16}.  A width outside {0,2,4,8,16} in bits_v sets the device status. */
+kvc_status kvc_allocate_bits(const kvc_layer_desc* desc, kvc_alloc_stage stage,
+                             const float* weight, const float* sigma, const uint8_t* bits_v,
+                             double avg_bits_per_elem, double keep_fraction, uint8_t keep_bits,
+                             uint8_t* bits_out, kvc_alloc_result* result_dev, void* ws,
+                             size_t ws_bytes, void* hip_stream);
+
+/* ---- Packed cache ------------------------------------------------------------------------
+ * RDKV §2.3 stores retained rows grouped by width so each width has one dequantisation
+ * path.  This library's layout (its own format; a token is retained iff bits_v > 0; zone z
+ * holds width {2,4,8,16}[z]; group = 32 elements):
+ *   header  i64 [16 + 24*H_kv].  [0..3] H_kv, d, N, 32; [4..9] totals of v_idx, v_words,
+ *           v_par pairs, k_keep, k_words, k_par pairs.  Per head g at 16 + 24*g:
+ *           [0..3] tokens per zone, [4] R_g, [5..8] v_idx offset per zone, [9..12] v_words
+ *           offset per zone, [13..16] v_par offset per zone (pairs), [17] k_keep/k_vloc
+ *           offset, [18] k_words offset, [19] k_par offset (pairs), [20] words per K group
+ *           (sum_c bits_k), [21] quantised K channels (width 2/4/8), [22] K groups
+ *           ceil(R_g/32), [23] 0.  Heads are concatenated in order, zones in width order.
+ *   v_idx   i32  token ids of each (head, zone), ascending
+ *   v_words u32  per listed token: d/32 groups x b words
+ *   v_par   f32  (scale, zero) per listed token and group, zones 2/4/8 only
+ *   k_keep  i32  retained tokens of each head, ascending
+ *   k_vloc  i32  per retained token: zone << 29 | position within its V zone
+ *   k_words u32  per head, per group j of 32 retained tokens, per channel c ascending with
+ *                bits_k[c] > 0: bits_k[c] words (a short last group is padded with code 0)
+ *   k_par   f32  (scale, zero) per (group j, channel c with bits_k[c] in {2,4,8})
+ *   k_width u8   [H_kv][d] copy of bits_k
+ * Quantiser per group x at width b in {2,4,8}: z = min x, s = float32(float64(max - min) /
+ * (2^b - 1)), code = clamp(round_half_even(float64(x - z) / s), 0, 2^b - 1), every code 0
+ * when s == 0; element e uses bits [e*b, e*b + b) of the group's little-endian u32 stream;
+ * b = 16 stores the raw bf16 bits.  V groups run over the d channels of one token, K groups
+ * over 32 consecutive retained tokens of one channel. */
+enum {
+  KVC_PK_HEADER = 0, KVC_PK_V_IDX, KVC_PK_V_WORDS, KVC_PK_V_PAR, KVC_PK_K_KEEP,
+  KVC_PK_K_VLOC, KVC_PK_K_WORDS, KVC_PK_K_PAR, KVC_PK_K_WIDTH, KVC_PK_NBUF
+};
+#define KVC_HDR_GLOBAL 16
+#define KVC_HDR_PER_HEAD 24
+
+typedef struct {
+  int64_t* header;
+  int32_t* v_idx;
+  uint32_t* v_words;
+  float* v_par;
+  int32_t* k_keep;
+  int32_t* k_vloc;
+  uint32_t* k_words;
+  float* k_par;
+  uint8_t* k_width;
+} kvc_packed_cache;
+
+/* Worst-case bytes of each packed buffer (indexed by KVC_PK_*) for `desc`. */
+kvc_status kvc_packed_capacity(const kvc_layer_desc* desc, int32_t group_size,
+                               size_t bytes_per_buffer[KVC_PK_NBUF]);
+
+/* Quantise and pack K and V at the widths bits_v (per token) and bits_k (per channel),
+ * RDKV §2.2 stages 2-3 and §2.3 zones.  `out` is a host struct of device buffers of at least
+ * kvc_packed_capacity() bytes.  Only retained units are read.  group_size must be 32. */
+kvc_status kvc_quantize_pack(const kvc_layer_desc* desc, const void* k, const void* v,
+                             const uint8_t* bits_v, const uint8_t* bits_k, int32_t group_size,
+                             const kvc_packed_cache* out, void* ws, size_t ws_bytes,
+                             void* hip_stream);
+
+/* Attention of Q (the last Nq = desc->n_queries rows of the sequence, [H_q][Nq][d]) over the
+ * retained tokens of a packed cache, dequantised on the fly (x = zero + scale*code; width 0
+ * channels are 0; width 16 exact): out f32 [H_q][Nq][d] and lse f32 [H_q][Nq]
+ * (RDKV §2.3 decode over packed zones; the two outputs whose errors form KVSculpt's loss,
+ * §2).  A row with no visible retained token gets lse = -inf and out = 0.  The packed cache's
+ * header must match desc (H_kv, d, N); a mismatch sets the device status. */
+kvc_status kvc_compressed_attend(const kvc_layer_desc* desc, const void* q,
+                                 const kvc_packed_cache* cache, float* out, float* lse,
+                                 void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Device status codes (bit set). */
+#define KVC_DEV_BAD_WIDTH 1
+#define KVC_DEV_BAD_CACHE 2
+
+/* Copy the device status word at the start of `ws` to *code (synchronises `hip_stream`). */
+kvc_status kvc_get_device_status(const void* ws, int32_t* code, void* hip_stream);
+
+const char* kvc_status_string(kvc_status status);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char* kvc_last_error(void);
+
+/* Library version, e.g. "kvc 0.1.0 gfx950". */
+const char* kvc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H_ */

@@ -1,0 +1,51 @@
+// Device helpers shared by the libkvc kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvc.h"
+
+namespace kvc {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 32x32x16 bf16 matrix-core product, fp32 accumulate.
+// Lane l supplies A[m = l%32][k = 8*(l/32) + j] and B[k = 8*(l/32) + j][n = l%32], j = 0..7, and
+// holds D[m = 8*(i/4) + 4*(l/32) + i%4][n = l%32] in element i (i = 0..15).
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32h(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Row (m) index of accumulator element i held by a lane in half `hi` (= lane / 32).
+__device__ __forceinline__ int acc_row(int i, int hi) { return 8 * (i >> 2) + 4 * hi + (i & 3); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Exchange with the lane 32 apart (the other half of a 32x32 accumulator column).
+__device__ __forceinline__ float swap_half(float x) { return __shfl_xor(x, 32, 64); }
+
+// Record a device-side data error in the workspace status word.
+__device__ __forceinline__ void set_status(int32_t* status, int32_t code) {
+  if (status) atomicOr(status, code);
+}
+
+__device__ __forceinline__ bool valid_width(uint32_t b) {
+  return b == 0 || b == 2 || b == 4 || b == 8 || b == 16;
+}
+
+}  // namespace kvc

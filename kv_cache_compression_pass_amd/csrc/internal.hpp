@@ -1,0 +1,69 @@
+// Host-side internal interface between the C ABI layer (api.cpp) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kvc.h"
+
+namespace kvc {
+
+// Validated view of a kvc_layer_desc.
+struct Layer {
+  int hq, hkv, d, G, causal;
+  int64_t n, nq;
+  double scale;     // softmax scale (float64; 1/sqrt(d) unless the caller fixed one)
+  float c_log2;     // float32(scale * log2(e)): logits in the base-2 domain
+};
+
+// Bump allocator over the caller's workspace.  Offset 0 holds the device status word.
+struct WsPlan {
+  size_t off = 256;
+  size_t take(size_t bytes) {
+    size_t o = off;
+    off += (bytes + 255) & ~size_t(255);
+    return o;
+  }
+};
+
+// ---- scorer ------------------------------------------------------------------------------
+constexpr int kScoreTileKeys = 256;   // keys per pass-2 block
+int score_chunk_rows(const Layer& L);  // query rows per pass-2 block (multiple of 64)
+int score_max_chunks(const Layer& L);
+size_t score_ws_bytes(const Layer& L, int mode, int hidden_dim);
+hipError_t launch_row_lse(const Layer& L, const uint16_t* q, const uint16_t* k, float* lse,
+                          hipStream_t s);
+hipError_t launch_score(const Layer& L, int mode, const uint16_t* q, const uint16_t* k,
+                        const float* lse, const uint16_t* hidden, const uint16_t* w_o,
+                        const uint16_t* v, int hidden_dim, float* scores, char* ws,
+                        hipStream_t s);
+
+// ---- channel weights --------------------------------------------------------------------
+size_t chanw_ws_bytes(const Layer& L);
+hipError_t launch_channel_weights(const Layer& L, const uint16_t* q, const uint16_t* k,
+                                  float* w_c, char* ws, hipStream_t s);
+
+// ---- allocation -------------------------------------------------------------------------
+size_t alloc_ws_bytes(const Layer& L, int stage);
+hipError_t launch_allocate(const Layer& L, int stage, const float* weight, const float* sigma,
+                           const uint8_t* bits_v, double avg_bits, double keep_fraction,
+                           int keep_bits, uint8_t* bits_out, kvc_alloc_result* result,
+                           char* ws, hipStream_t s);
+
+// ---- quantise / pack --------------------------------------------------------------------
+void packed_capacity(const Layer& L, size_t bytes[KVC_PK_NBUF]);
+size_t pack_ws_bytes(const Layer& L);
+hipError_t launch_pack(const Layer& L, const uint16_t* k, const uint16_t* v,
+                       const uint8_t* bits_v, const uint8_t* bits_k,
+                       const kvc_packed_cache& out, char* ws, hipStream_t s);
+
+// ---- compressed attend ------------------------------------------------------------------
+size_t attend_ws_bytes(const Layer& L);
+hipError_t launch_attend(const Layer& L, const uint16_t* q, const kvc_packed_cache& cache,
+                         float* out, float* lse, char* ws, hipStream_t s);
+
+// ---- misc ------------------------------------------------------------------------------
+hipError_t launch_reset_status(char* ws, hipStream_t s);
+
+}  // namespace kvc

@@ -110,7 +110,7 @@ def value_out_norms(w_o, v, n_q_heads, tokens=None):
     return out
 
 
-def token_scores_max(q, k, lse, hidden, w_o, v, scale=None, causal=True):
+def token_scores_max(q, k, lse, hidden, w_o, v, scale=None, causal=True, tokens=None):
     """KVzip+ score, maximised over the query heads of each KV group.
 
     s+[g,t] = max_{h: g(h)=g} ( max_{j: p_j >= t} a_{h,j,t} * ||h_j|| ) / ||W_O^{(h)} v_{g,t}||.
@@ -118,6 +118,7 @@ def token_scores_max(q, k, lse, hidden, w_o, v, scale=None, causal=True):
     normalised by its value's output-projection norm relative to the hidden-state norm) and
     §2.2 (one score per KV head).  The j range is the visible query rows (self included);
     the group reduction is a max.  A zero value norm gives +inf (0 if the numerator is 0).
+    ``tokens`` restricts the output to those columns (same values, fewer columns computed).
     """
     Q, K = as_f64(q), as_f64(k)
     L = np.asarray(lse, dtype=np.float64)
@@ -125,18 +126,19 @@ def token_scores_max(q, k, lse, hidden, w_o, v, scale=None, causal=True):
     hkv, n, _ = K.shape
     G = hq // hkv
     sc = default_scale(d, scale)
+    cols = np.arange(n) if tokens is None else np.asarray(tokens)
     hn = hidden_row_norms(hidden)
-    won = value_out_norms(w_o, v, hq)
-    num = np.zeros((hq, n))
+    won = value_out_norms(w_o, v, hq, cols)
+    num = np.zeros((hq, cols.size))
     for h in range(hq):
         for r0 in range(0, nq, _ROWS):
             r1 = min(nq, r0 + _ROWS)
-            a = _probabilities(Q, K, L, h, G, r0, r1, sc, causal)
+            a = _probabilities(Q, K, L, h, G, r0, r1, sc, causal)[:, cols]
             num[h] = np.maximum(num[h], (a * hn[r0:r1, None]).max(axis=0))
     with np.errstate(divide="ignore", invalid="ignore"):
         ratio = num / won
     ratio[(num == 0) & (won == 0)] = 0.0
-    return ratio.reshape(hkv, G, n).max(axis=1)
+    return ratio.reshape(hkv, G, cols.size).max(axis=1)
 
 
 def channel_weights(q, k, scale=None):

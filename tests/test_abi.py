@@ -1,0 +1,144 @@
+"""The C ABI on the host: the library loads, exports every symbol include/kvc.h declares, and
+rejects bad arguments with the documented status before touching a device.  No compute call
+is made here (valid requests on a machine without a GPU stop at KVC_ERR_NO_DEVICE)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_compression_pass_amd import _lib as C
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(C.LIB_PATH):
+        pytest.fail("libkvc.so is not built (run __graft_entry__.build())")
+    return C.load()
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "kvc.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvc_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(C.EXPORTED)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kvc_version().decode().startswith("kvc ")
+    for code, name in C.STATUS_NAMES.items():
+        assert lib.kvc_status_string(code).decode() == name
+
+
+def _desc(**kw):
+    d = dict(n_q_heads=4, n_kv_heads=2, head_dim=64, causal=1, n_keys=128, n_queries=64,
+             softmax_scale=0.0, reserved=0)
+    d.update(kw)
+    return C.LayerDesc(**d)
+
+
+FAKE = 0x10000          # an aligned non-null address; never dereferenced on these paths
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_q_heads=3, n_kv_heads=2), 1),
+    (dict(n_q_heads=0), 1),
+    (dict(head_dim=96), 2),
+    (dict(head_dim=-1), 1),
+    (dict(n_queries=129), 1),
+    (dict(n_keys=0), 1),
+    (dict(causal=2), 1),
+    (dict(reserved=1), 1),
+    (dict(softmax_scale=-1.0), 1),
+    (dict(n_q_heads=34, n_kv_heads=2), 2),
+    (dict(n_keys=1 << 29, n_queries=1), 2),
+])
+def test_bad_descriptor(lib, kw, status):
+    d = _desc(**kw)
+    st = lib.kvc_row_lse(ctypes.byref(d), FAKE, FAKE, FAKE, None, 0, None)
+    assert st == status, lib.kvc_last_error()
+    assert lib.kvc_last_error().decode() != ""
+    assert lib.kvc_workspace_size(C.OP_SCORE_TOKENS, ctypes.byref(d), 0) == 0
+
+
+def test_null_and_misaligned_pointers(lib):
+    d = _desc()
+    assert lib.kvc_row_lse(None, FAKE, FAKE, FAKE, None, 0, None) == 1
+    assert lib.kvc_row_lse(ctypes.byref(d), None, FAKE, FAKE, None, 0, None) == 1
+    assert lib.kvc_row_lse(ctypes.byref(d), FAKE + 2, FAKE, FAKE, None, 0, None) == 1
+    assert "aligned" in lib.kvc_last_error().decode()
+    assert lib.kvc_row_lse(ctypes.byref(d), FAKE, FAKE, None, None, 0, None) == 1
+
+
+def test_workspace_errors(lib):
+    d = _desc()
+    need = lib.kvc_workspace_size(C.OP_SCORE_TOKENS, ctypes.byref(d), C.SCORE_SUM)
+    assert need > 256
+    st = lib.kvc_score_tokens(ctypes.byref(d), C.SCORE_SUM, FAKE, FAKE, FAKE, None, FAKE, None, 0, None)
+    assert st == 3
+    st = lib.kvc_score_tokens(ctypes.byref(d), C.SCORE_SUM, FAKE, FAKE, FAKE, None, FAKE, FAKE, need - 1, None)
+    assert st == 3
+    st = lib.kvc_score_tokens(ctypes.byref(d), 7, FAKE, FAKE, FAKE, None, FAKE, FAKE, need, None)
+    assert st == 1
+    # MAX mode without kvzip arguments
+    st = lib.kvc_score_tokens(ctypes.byref(d), C.SCORE_MAX, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None)
+    assert st == 1
+
+
+def test_allocation_argument_errors(lib):
+    d = _desc()
+    ws = 1 << 20
+    big = 1 << 30
+    st = lib.kvc_allocate_bits(ctypes.byref(d), C.ALLOC_V_TOKENS, FAKE, None, None, -1.0, 0.0, 16, FAKE, None, ws, big, None)
+    assert st == 1
+    st = lib.kvc_allocate_bits(ctypes.byref(d), C.ALLOC_V_TOKENS, FAKE, None, None, float("nan"), 0.0, 16, FAKE, None, ws, big, None)
+    assert st == 1
+    st = lib.kvc_allocate_bits(ctypes.byref(d), C.ALLOC_K_CHANNELS, FAKE, None, None, 2.0, 0.0, 16, FAKE, None, ws, big, None)
+    assert st == 1      # K stage needs bits_v
+    st = lib.kvc_allocate_bits(ctypes.byref(d), C.ALLOC_TOPK, FAKE, None, None, 0.0, 1.5, 16, FAKE, None, ws, big, None)
+    assert st == 1
+    st = lib.kvc_allocate_bits(ctypes.byref(d), C.ALLOC_TOPK, FAKE, None, None, 0.0, 0.25, 3, FAKE, None, ws, big, None)
+    assert st == 1
+    st = lib.kvc_allocate_bits(ctypes.byref(d), 9, FAKE, None, None, 1.0, 0.0, 16, FAKE, None, ws, big, None)
+    assert st == 1
+    st = lib.kvc_allocate_bits(ctypes.byref(d), C.ALLOC_V_TOKENS, FAKE, None, None, 2.0, 0.0, 16, FAKE, None, ws, 16, None)
+    assert st == 3
+
+
+def test_pack_capacity_and_errors(lib):
+    d = _desc(n_kv_heads=2, n_q_heads=2, head_dim=128, n_keys=100, n_queries=100)
+    arr = (ctypes.c_size_t * C.PK_NBUF)()
+    assert lib.kvc_packed_capacity(ctypes.byref(d), 32, arr) == 0
+    caps = list(arr)
+    T = 2 * 100
+    assert caps[0] == 8 * (16 + 2 * 24)
+    assert caps[1] == 4 * T and caps[4] == 4 * T and caps[5] == 4 * T
+    assert caps[2] == 4 * T * 4 * 16            # all tokens at 16 bits: raw bf16 size
+    assert caps[6] == 4 * 2 * 4 * 16 * 128      # ceil(100/32) = 4 groups per head
+    assert caps[8] == 2 * 128
+    assert lib.kvc_packed_capacity(ctypes.byref(d), 64, arr) == 2
+    cache = C.PackedCacheC(*([FAKE] * C.PK_NBUF))
+    st = lib.kvc_quantize_pack(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 16, ctypes.byref(cache), FAKE, 1 << 30, None)
+    assert st == 2
+    cache.k_words = None
+    st = lib.kvc_quantize_pack(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 32, ctypes.byref(cache), FAKE, 1 << 30, None)
+    assert st == 1
+
+
+def test_valid_request_without_device_reports_no_device(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    d = _desc()
+    st = lib.kvc_row_lse(ctypes.byref(d), FAKE, FAKE, FAKE, None, 0, None)
+    assert st == 4, lib.kvc_last_error()

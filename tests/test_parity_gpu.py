@@ -1,0 +1,236 @@
+"""GPU parity: every C-ABI call against the float64 oracle on the same seeded inputs.
+
+Bars (derived in the design doc from the arithmetic): row LSE 1e-4 abs; token scores rel 1e-3
+(floor 1e-30); channel weights rel 1e-5; widths, results and packed buffers bit-exact from
+identical float32 weights / widths; compressed attention output 2e-2 abs and LSE 1e-3 abs.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compression_pass_amd as kvc
+import oracle
+from workloads import make_inputs
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU parity tests need a GPU"
+    kvc.load()
+
+
+SMALL = [
+    # name, H_q, H_kv, d, N, Nq, causal, avg_bits
+    ("g4_d128_ragged", 8, 2, 128, 1000, 1000, True, 3.0),
+    ("g1_d64_q_lt_n", 2, 2, 64, 700, 300, True, 2.5),
+    ("g2_d128_noncausal", 4, 2, 128, 333, 129, False, 4.0),
+    ("g4_d128_one_row", 4, 1, 128, 517, 1, True, 2.0),
+    ("g1_d64_one_key", 1, 1, 64, 1, 1, True, 4.0),
+    ("g3_d64_two_tiles", 6, 2, 64, 300, 257, True, 1.5),
+    ("g4_d128_outliers", 8, 2, 128, 1536, 1536, True, 3.0),
+]
+
+
+def _pipeline(name, hq, hkv, d, N, Nq, causal, avg, seed, x=None, n_fid=64):
+    print(f"case {name}: H_q={hq} H_kv={hkv} d={d} N={N} Nq={Nq} causal={causal}", flush=True)
+    if x is None:
+        x = make_inputs(hq, hkv, d, N, Nq, seed=seed, k_outliers=("outliers" in name))
+    desc = H.desc_of(hq, hkv, d, N, Nq, causal)
+    q, k, v = H.dev_bf16(x["q"]), H.dev_bf16(x["k"]), H.dev_bf16(x["v"])
+
+    lse_t = H.row_lse(desc, q, k)
+    lse_r = oracle.row_lse(x["q"], x["k"], causal=causal)
+    H.assert_abs(lse_t.cpu().numpy(), lse_r, 1e-4, "row_lse")
+
+    w_g = H.score_sum(desc, q, k, lse_t).cpu().numpy()
+    w_r = oracle.token_scores_sum(x["q"], x["k"], lse_r, causal=causal)
+    H.assert_rel(w_g, w_r, 1e-3, what="token scores (sum)")
+
+    wc_g = H.channel_weights(desc, q, k).cpu().numpy()
+    wc_r = oracle.channel_weights(x["q"], x["k"])
+    H.assert_rel(wc_g, wc_r, 1e-5, what="channel weights")
+
+    # allocation from identical float32 weights (the oracle's, rounded once)
+    w32 = w_r.astype(np.float32)
+    bv_g, res_v, st = H.allocate(desc, kvc.ALLOC_V_TOKENS, H.dev_f32(w32), avg)
+    bv_r, info_v = oracle.allocate_v_tokens(w32, avg, d)
+    assert st == 0
+    np.testing.assert_array_equal(bv_g.cpu().numpy(), bv_r)
+    assert res_v["lam"] == info_v["lam"] and res_v["used"] == info_v["used"]
+    assert res_v["budget"] == info_v["budget"]
+    assert res_v["distortion"] == pytest.approx(info_v["distortion"], rel=1e-12)
+    wc32 = wc_r.astype(np.float32)
+    bk_g, res_k, st = H.allocate(desc, kvc.ALLOC_K_CHANNELS, H.dev_f32(wc32), avg, bits_v=H.dev_u8(bv_r))
+    bk_r, info_k = oracle.allocate_k_channels(wc32, bv_r, avg)
+    assert st == 0
+    np.testing.assert_array_equal(bk_g.cpu().numpy(), bk_r)
+    assert res_k["lam"] == info_k["lam"] and res_k["used"] == info_k["used"]
+    assert res_k["budget"] == info_k["budget"]
+
+    # pack from identical widths: every buffer bit-exact
+    cache, st = H.pack(desc, k, v, H.dev_u8(bv_r), H.dev_u8(bk_r))
+    assert st == 0
+    H.compare_packed(cache.to_numpy(), oracle.pack_cache(x["k"], x["v"], bv_r, bk_r))
+
+    # fidelity attend on the last rows: compressed, then the all-16 cache
+    nf = min(Nq, n_fid)
+    qf_bits = np.ascontiguousarray(x["q"][:, Nq - nf:, :])
+    desc_f = H.desc_of(hq, hkv, d, N, nf, causal)
+    out_g, lh_g, st = H.attend(desc_f, H.dev_bf16(qf_bits), cache)
+    assert st == 0
+    out_r, lh_r = oracle.compressed_attend(qf_bits, x["k"], x["v"], bv_r, bk_r, causal=causal)
+    H.assert_abs(out_g.cpu().numpy(), out_r, 2e-2, "compressed attend output")
+    H.assert_abs(lh_g.cpu().numpy(), lh_r, 1e-3, "compressed attend lse")
+    full_v = np.full((hkv, N), 16, np.uint8)
+    full_k = np.full((hkv, d), 16, np.uint8)
+    cache16, st = H.pack(desc, k, v, H.dev_u8(full_v), H.dev_u8(full_k))
+    y_g, l_g, st2 = H.attend(desc_f, H.dev_bf16(qf_bits), cache16)
+    assert st == 0 and st2 == 0
+    y_r, l_r = oracle.full_attend(qf_bits, x["k"], x["v"], causal=causal)
+    H.assert_abs(y_g.cpu().numpy(), y_r, 2e-2, "full attend output")
+    H.assert_abs(l_g.cpu().numpy(), l_r, 1e-3, "full attend lse")
+    return x
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_pipeline(case):
+    name, hq, hkv, d, N, Nq, causal, avg = case
+    _pipeline(name, hq, hkv, d, N, Nq, causal, avg, seed=abs(hash(name)) % 1000)
+
+
+def test_config0_tiny_full_parity():
+    from workloads import get_config, make_config_inputs
+    cfg = get_config(0)
+    x = make_config_inputs(cfg)
+    _pipeline("config0", cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_keys, cfg.n_queries,
+              True, cfg.avg_bits, seed=None, x=x, n_fid=cfg.fidelity_rows)
+
+
+MAXCASES = [
+    # name, H_q, H_kv, d, N, Nq, D_h, causal
+    ("max_g7_d128", 14, 2, 128, 600, 600, 256, True),
+    ("max_g2_d64_q_lt_n", 4, 2, 64, 300, 200, 96, True),
+    ("max_g1_d128_noncausal", 2, 2, 128, 129, 64, 40, False),
+]
+
+
+@pytest.mark.parametrize("case", MAXCASES, ids=[c[0] for c in MAXCASES])
+def test_max_scores_and_topk(case):
+    name, hq, hkv, d, N, Nq, Dh, causal = case
+    print(f"case {name}", flush=True)
+    x = make_inputs(hq, hkv, d, N, Nq, seed=77, hidden_dim=Dh)
+    desc = H.desc_of(hq, hkv, d, N, Nq, causal)
+    q, k, v = H.dev_bf16(x["q"]), H.dev_bf16(x["k"]), H.dev_bf16(x["v"])
+    lse_t = H.row_lse(desc, q, k)
+    lse_r = oracle.row_lse(x["q"], x["k"], causal=causal)
+    s_g = H.score_max(desc, q, k, lse_t, H.dev_bf16(x["hidden"]), H.dev_bf16(x["w_o"]), v).cpu().numpy()
+    s_r = oracle.token_scores_max(x["q"], x["k"], lse_r, x["hidden"], x["w_o"], x["v"], causal=causal)
+    H.assert_rel(s_g, s_r, 1e-3, what="KVzip+ scores")
+    s32 = s_r.astype(np.float32)
+    for frac in (0.25, 0.0, 1.0, 0.5):
+        b_g, res, st = H.allocate(desc, kvc.ALLOC_TOPK, H.dev_f32(s32), keep_fraction=frac, keep_bits=16)
+        b_r = oracle.topk_keep(s32, frac, 16)
+        np.testing.assert_array_equal(b_g.cpu().numpy(), b_r)
+        assert res["used"] == int(b_r.astype(np.int64).sum()) * d
+    cache, st = H.pack(desc, k, v, H.dev_u8(b_r), H.dev_u8(np.full((hkv, d), 16, np.uint8)))
+    H.compare_packed(cache.to_numpy(), oracle.pack_cache(x["k"], x["v"], b_r, np.full((hkv, d), 16, np.uint8)))
+
+
+def test_allocation_ties_zeros_and_extremes():
+    print("case allocation edge cases", flush=True)
+    hkv, N, d = 3, 2000, 64
+    desc = H.desc_of(hkv, hkv, d, N, N, True)
+    rng = np.random.default_rng(5)
+    w = rng.integers(0, 6, (hkv, N)).astype(np.float32) * np.float32(0.125)   # many ties, zeros
+    for avg in (0.0, 0.3, 1.0, 2.0, 3.0, 4.0, 7.5, 16.0, 20.0):
+        b_g, res, st = H.allocate(desc, kvc.ALLOC_V_TOKENS, H.dev_f32(w), avg)
+        b_r, info = oracle.allocate_v_tokens(w, avg, d)
+        np.testing.assert_array_equal(b_g.cpu().numpy(), b_r, err_msg=f"avg {avg}")
+        assert res["lam"] == info["lam"] and res["used"] == info["used"]
+        assert res["budget"] == info["budget"]
+    sigma = rng.uniform(0.5, 2.0, (hkv, N)).astype(np.float32)
+    b_g, res, st = H.allocate(desc, kvc.ALLOC_V_TOKENS, H.dev_f32(w), 2.5, sigma=H.dev_f32(sigma))
+    b_r, info = oracle.allocate_v_tokens(w, 2.5, d, sigma=sigma)
+    np.testing.assert_array_equal(b_g.cpu().numpy(), b_r)
+    # K stage where one head keeps nothing
+    bv = rng.choice(np.array([0, 2, 4, 8, 16], np.uint8), (hkv, N))
+    bv[1] = 0
+    wc = rng.exponential(1.0, (hkv, d)).astype(np.float32)
+    b_g, res, st = H.allocate(desc, kvc.ALLOC_K_CHANNELS, H.dev_f32(wc), 3.0, bits_v=H.dev_u8(bv))
+    b_r, info = oracle.allocate_k_channels(wc, bv, 3.0)
+    np.testing.assert_array_equal(b_g.cpu().numpy(), b_r)
+    assert res["lam"] == info["lam"] and res["used"] == info["used"]
+
+
+def test_bad_width_sets_device_status():
+    print("case bad width status", flush=True)
+    x = make_inputs(2, 1, 64, 100, 100, seed=3)
+    desc = H.desc_of(2, 1, 64, 100, 100, True)
+    bv = np.full((1, 100), 4, np.uint8)
+    bv[0, 7] = 3
+    bk = np.full((1, 64), 8, np.uint8)
+    cache, st = H.pack(desc, H.dev_bf16(x["k"]), H.dev_bf16(x["v"]), H.dev_u8(bv), H.dev_u8(bk))
+    assert st & kvc.DEV_BAD_WIDTH
+    bv[0, 7] = 4
+    cache, st = H.pack(desc, H.dev_bf16(x["k"]), H.dev_bf16(x["v"]), H.dev_u8(bv), H.dev_u8(bk))
+    assert st == 0
+    wc = np.ones((1, 64), np.float32)
+    bv[0, 9] = 5
+    _, _, st = H.allocate(desc, kvc.ALLOC_K_CHANNELS, H.dev_f32(wc), 2.0, bits_v=H.dev_u8(bv))
+    assert st & kvc.DEV_BAD_WIDTH
+
+
+def test_evict_everything_and_empty_rows():
+    print("case evict everything", flush=True)
+    hq, hkv, d, N, Nq = 4, 2, 128, 300, 40
+    x = make_inputs(hq, hkv, d, N, Nq, seed=9)
+    desc = H.desc_of(hq, hkv, d, N, Nq, True)
+    k, v = H.dev_bf16(x["k"]), H.dev_bf16(x["v"])
+    bv = np.zeros((hkv, N), np.uint8)
+    bv[1, :5] = 8                     # head 1 keeps 5 early tokens; head 0 keeps nothing
+    bk = np.full((hkv, d), 4, np.uint8)
+    cache, st = H.pack(desc, k, v, H.dev_u8(bv), H.dev_u8(bk))
+    H.compare_packed(cache.to_numpy(), oracle.pack_cache(x["k"], x["v"], bv, bk))
+    out_g, lh_g, st = H.attend(desc, H.dev_bf16(x["q"]), cache)
+    out_r, lh_r = oracle.compressed_attend(x["q"], x["k"], x["v"], bv, bk)
+    H.assert_abs(out_g.cpu().numpy(), out_r, 2e-2, "out")
+    H.assert_abs(lh_g.cpu().numpy(), lh_r, 1e-3, "lse")
+    assert np.isneginf(lh_g.cpu().numpy()[:2]).all()
+
+
+def test_determinism_bitwise():
+    print("case determinism", flush=True)
+    hq, hkv, d, N, Nq = 8, 2, 128, 2048, 2048
+    x = make_inputs(hq, hkv, d, N, Nq, seed=31, k_outliers=True)
+    desc = H.desc_of(hq, hkv, d, N, Nq, True)
+    q, k, v = H.dev_bf16(x["q"]), H.dev_bf16(x["k"]), H.dev_bf16(x["v"])
+    runs = []
+    for _ in range(2):
+        lse = H.row_lse(desc, q, k)
+        w = H.score_sum(desc, q, k, lse)
+        wc = H.channel_weights(desc, q, k)
+        bv, _, _ = H.allocate(desc, kvc.ALLOC_V_TOKENS, w, 2.0)
+        bk, _, _ = H.allocate(desc, kvc.ALLOC_K_CHANNELS, wc, 2.0, bits_v=bv)
+        cache, _ = H.pack(desc, k, v, bv, bk)
+        runs.append((lse.cpu().numpy(), w.cpu().numpy(), wc.cpu().numpy(), bv.cpu().numpy(),
+                     bk.cpu().numpy(), cache.to_numpy()))
+    a, b = runs
+    for i in range(5):
+        assert a[i].tobytes() == b[i].tobytes()
+    H.compare_packed(a[5], b[5])
+    # the whole GPU pipeline vs the oracle pipeline: report width mismatches, each must sit
+    # at a key within tolerance of lambda*
+    w_r = oracle.token_scores_sum(x["q"], x["k"], oracle.row_lse(x["q"], x["k"]))
+    bv_r, info = oracle.allocate_v_tokens(w_r.astype(np.float32), 2.0, d)
+    mism = np.argwhere(a[3] != bv_r)
+    print(f"end-to-end V widths differing from the oracle pipeline: {len(mism)} of {bv_r.size}")
+    lam = info["lam"]
+    for g, t in mism:
+        ks = oracle.step_keys(np.array([w_r[g, t]], np.float32), np.array([d]))[0]
+        assert np.min(np.abs(ks - lam)) <= 2e-3 * lam

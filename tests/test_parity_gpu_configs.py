@@ -1,0 +1,145 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration the benchmark
+times.  Where the float64 oracle cannot redo the whole layer in seconds, it checks outputs it
+can compute exactly on their own (sampled rows; the last key columns, which only the last
+rows see; one KV head) plus properties that hold at any size (every attention row sums to
+one, so sum_t w[g,t] = G * Nq)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compression_pass_amd as kvc
+import oracle
+from workloads import get_config, make_config_inputs
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+TAIL = 256
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU parity tests need a GPU"
+    kvc.load()
+
+
+def _sampled_rows(x, cfg, lse_g, rng, n=12):
+    """Oracle LSE of single rows: row i only depends on q_i and the keys up to its position."""
+    N, Nq, G = cfg.n_keys, cfg.n_queries, cfg.gqa
+    picks = [(0, 0), (cfg.n_q_heads - 1, Nq - 1)]
+    picks += [(int(rng.integers(cfg.n_q_heads)), int(rng.integers(Nq))) for _ in range(n)]
+    for h, i in picks:
+        p = N - Nq + i
+        ref = oracle.row_lse(x["q"][h:h + 1, i:i + 1], x["k"][h // G:h // G + 1, :p + 1])[0, 0]
+        assert abs(float(lse_g[h, i]) - ref) <= 1e-4, (h, i, float(lse_g[h, i]), ref)
+
+
+def _tail_scores(x, cfg):
+    """Exact oracle w[:, t] for the last TAIL keys: only the last TAIL rows see them."""
+    Nq = cfg.n_queries
+    r0 = Nq - TAIL
+    q_sub = np.ascontiguousarray(x["q"][:, r0:, :])
+    lse_sub = oracle.row_lse(q_sub, x["k"])
+    w_sub = oracle.token_scores_sum(q_sub, x["k"], lse_sub)
+    return w_sub[:, -TAIL:]
+
+
+def _synthetic_weights(shape, total_per_head, seed):
+    """Seeded heavy-tailed positive weights normalised like attention column sums."""
+    rng = np.random.default_rng(seed)
+    w = np.exp(rng.normal(0.0, 1.5, shape))
+    w *= total_per_head / w.sum(axis=1, keepdims=True)
+    return w.astype(np.float32)
+
+
+@pytest.mark.parametrize("ci", [1, 2, 4])
+def test_sum_config_full_size(ci):
+    cfg = get_config(ci)
+    print(f"config {ci} ({cfg.name}): inputs", flush=True)
+    x = make_config_inputs(cfg)
+    hq, hkv, d, N, Nq = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_keys, cfg.n_queries
+    desc = H.desc_of(hq, hkv, d, N, Nq, True)
+    q, k, v = H.dev_bf16(x["q"]), H.dev_bf16(x["k"]), H.dev_bf16(x["v"])
+    rng = np.random.default_rng(ci)
+
+    print(f"config {ci}: row_lse + scores", flush=True)
+    lse_t = H.row_lse(desc, q, k)
+    lse_g = lse_t.cpu().numpy()
+    _sampled_rows(x, cfg, lse_g, rng)
+    w_g = H.score_sum(desc, q, k, lse_t).cpu().numpy()
+    np.testing.assert_allclose(w_g.astype(np.float64).sum(axis=1), cfg.gqa * Nq, rtol=2e-5)
+    H.assert_rel(w_g[:, -TAIL:], _tail_scores(x, cfg), 1e-3, what="tail token scores")
+    if ci == 4:
+        # config 4 (Nq = 512): one KV head exactly, every column
+        G = cfg.gqa
+        lse_r = oracle.row_lse(x["q"][:G], x["k"][:1])
+        w_r = oracle.token_scores_sum(x["q"][:G], x["k"][:1], lse_r)
+        H.assert_rel(w_g[:1], w_r, 1e-3, what="head-0 token scores")
+
+    print(f"config {ci}: channel weights", flush=True)
+    wc_g = H.channel_weights(desc, q, k).cpu().numpy()
+    H.assert_rel(wc_g, oracle.channel_weights(x["q"], x["k"]), 1e-5, what="channel weights")
+
+    print(f"config {ci}: allocation", flush=True)
+    w32 = _synthetic_weights((hkv, N), cfg.gqa * Nq, seed=100 + ci)
+    bv_g, res, st = H.allocate(desc, kvc.ALLOC_V_TOKENS, H.dev_f32(w32), cfg.avg_bits)
+    bv_r, info = oracle.allocate_v_tokens(w32, cfg.avg_bits, d)
+    np.testing.assert_array_equal(bv_g.cpu().numpy(), bv_r)
+    assert res["lam"] == info["lam"] and res["used"] == info["used"] and res["budget"] == info["budget"]
+    wc32 = oracle.channel_weights(x["q"], x["k"]).astype(np.float32)
+    bk_g, resk, st = H.allocate(desc, kvc.ALLOC_K_CHANNELS, H.dev_f32(wc32), cfg.avg_bits,
+                                bits_v=H.dev_u8(bv_r))
+    bk_r, infok = oracle.allocate_k_channels(wc32, bv_r, cfg.avg_bits)
+    np.testing.assert_array_equal(bk_g.cpu().numpy(), bk_r)
+    assert resk["lam"] == infok["lam"] and resk["used"] == infok["used"]
+
+    print(f"config {ci}: pack", flush=True)
+    cache, st = H.pack(desc, k, v, H.dev_u8(bv_r), H.dev_u8(bk_r))
+    assert st == 0
+    H.compare_packed(cache.to_numpy(), oracle.pack_cache(x["k"], x["v"], bv_r, bk_r))
+
+    print(f"config {ci}: attend", flush=True)
+    nf = cfg.fidelity_rows
+    heads = slice(0, cfg.gqa)          # oracle on KV head 0's query heads
+    qf = np.ascontiguousarray(x["q"][:, Nq - nf:, :])
+    desc_f = H.desc_of(hq, hkv, d, N, nf, True)
+    out_g, lh_g, st = H.attend(desc_f, H.dev_bf16(qf), cache)
+    assert st == 0
+    out_r, lh_r = oracle.compressed_attend(qf[heads], x["k"][:1], x["v"][:1], bv_r[:1], bk_r[:1])
+    H.assert_abs(out_g.cpu().numpy()[heads], out_r, 2e-2, "attend output")
+    H.assert_abs(lh_g.cpu().numpy()[heads], lh_r, 1e-3, "attend lse")
+
+
+def test_config3_kvzip_full_size():
+    cfg = get_config(3)
+    print("config 3: inputs", flush=True)
+    x = make_config_inputs(cfg)
+    hq, hkv, d, N, Nq = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_keys, cfg.n_queries
+    desc = H.desc_of(hq, hkv, d, N, Nq, True)
+    q, k, v = H.dev_bf16(x["q"]), H.dev_bf16(x["k"]), H.dev_bf16(x["v"])
+    print("config 3: row_lse + max scores", flush=True)
+    lse_t = H.row_lse(desc, q, k)
+    _sampled_rows(x, cfg, lse_t.cpu().numpy(), np.random.default_rng(3))
+    s_g = H.score_max(desc, q, k, lse_t, H.dev_bf16(x["hidden"]), H.dev_bf16(x["w_o"]), v).cpu().numpy()
+    r0 = Nq - TAIL
+    q_sub = np.ascontiguousarray(x["q"][:, r0:, :])
+    lse_sub = oracle.row_lse(q_sub, x["k"])
+    cols = np.arange(N - TAIL, N)
+    s_r = oracle.token_scores_max(q_sub, x["k"], lse_sub, x["hidden"][r0:], x["w_o"], x["v"], tokens=cols)
+    H.assert_rel(s_g[:, -TAIL:], s_r, 1e-3, what="tail KVzip+ scores")
+    assert np.isfinite(s_g).all() and (s_g > 0).all()
+    print("config 3: top-k + pack", flush=True)
+    s32 = _synthetic_weights((hkv, N), 1.0, seed=303)
+    kk = math.floor(cfg.keep_fraction * N)
+    for g in range(hkv):                   # plant ties straddling each head's threshold
+        thr = np.sort(s32[g])[::-1][kk - 1]
+        s32[g, 50 + 97 * np.arange(40)] = thr
+    b_g, res, st = H.allocate(desc, kvc.ALLOC_TOPK, H.dev_f32(s32), keep_fraction=cfg.keep_fraction)
+    b_r = oracle.topk_keep(s32, cfg.keep_fraction, 16)
+    np.testing.assert_array_equal(b_g.cpu().numpy(), b_r)
+    bk = np.full((hkv, d), 16, np.uint8)
+    cache, st = H.pack(desc, k, v, H.dev_u8(b_r), H.dev_u8(bk))
+    H.compare_packed(cache.to_numpy(), oracle.pack_cache(x["k"], x["v"], b_r, bk))

@@ -16,11 +16,18 @@ import numpy as np
 from .configs import WorkloadConfig, get_config
 
 
-def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to bfloat16 (nearest, ties to even); return the uint16 bits."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    bias = np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))
-    return ((u + bias) >> np.uint64(16)).astype(np.uint16)
+def f32_to_bf16_bits(x: np.ndarray, chunk: int = 1 << 24) -> np.ndarray:
+    """Round finite float32 values to bfloat16 (nearest, ties to even); return the uint16 bits."""
+    src = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    out = np.empty(src.size, dtype=np.uint16)
+    for p in range(0, src.size, chunk):
+        u = src[p:p + chunk].view(np.uint32).copy()
+        lsb = (u >> np.uint32(16)) & np.uint32(1)
+        u += np.uint32(0x7FFF)
+        u += lsb
+        u >>= np.uint32(16)
+        out[p:p + chunk] = u
+    return out.reshape(np.shape(x))
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
