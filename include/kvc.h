@@ -92,7 +92,7 @@ size_t kvc_workspace_size(int32_t op, const kvc_layer_desc* desc, int32_t mode);
 /* Pass 1.  lse[h][i] = ln sum_{t visible} exp(scale * q_{h,i} . k_{g(h),t}) (natural log, the
  * scale included): the attention mass KVSculpt's loss matches (KVSculpt §2) and the
  * normaliser of RDKV's attention probabilities (RDKV §2.1).  bf16 matrix-core products with
- * float32 accumulation.  Workspace: none (ws may be NULL when ws_bytes == 0). */
+ * float32 accumulation.  Workspace: kvc_workspace_size(KVC_OP_ROW_LSE, desc, 0) bytes. */
 kvc_status kvc_row_lse(const kvc_layer_desc* desc, const void* q, const void* k, float* lse,
                        void* ws, size_t ws_bytes, void* hip_stream);
 

@@ -151,7 +151,7 @@ size_t kvc_workspace_size(int32_t op, const kvc_layer_desc* desc, int32_t mode) 
   if (make_layer(desc, &L) != KVC_OK) return 0;
   g_last_error = saved;
   switch (op) {
-    case KVC_OP_ROW_LSE: return 0;
+    case KVC_OP_ROW_LSE: return lse_ws_bytes(L);
     case KVC_OP_SCORE_TOKENS:
       if (mode != KVC_SCORE_SUM && mode != KVC_SCORE_MAX) return 0;
       return score_ws_bytes(L, mode, 0);
@@ -172,10 +172,10 @@ kvc_status kvc_row_lse(const kvc_layer_desc* desc, const void* q, const void* k,
   KVC_TRY(need_bf16(q, "q"));
   KVC_TRY(need_bf16(k, "k"));
   KVC_TRY(need_ptr(lse, 4, "lse"));
-  (void)ws;
-  (void)ws_bytes;
+  KVC_TRY(need_ws(ws, ws_bytes, lse_ws_bytes(L)));
   KVC_TRY(need_device());
-  return finish(launch_row_lse(L, (const uint16_t*)q, (const uint16_t*)k, lse, (hipStream_t)hip_stream),
+  return finish(launch_row_lse(L, (const uint16_t*)q, (const uint16_t*)k, lse, (char*)ws,
+                               (hipStream_t)hip_stream),
                 "kvc_row_lse launch");
 }
 

@@ -28,12 +28,20 @@ struct WsPlan {
 };
 
 // ---- scorer ------------------------------------------------------------------------------
-constexpr int kScoreTileKeys = 256;   // keys per pass-2 block
-int score_chunk_rows(const Layer& L);  // query rows per pass-2 block (multiple of 64)
-int score_max_chunks(const Layer& L);
+// Both passes split the layer into work items (KV head g, 256-row tile rt, key chunk ch,
+// query head of the group hl); a block of 4 waves handles one item.
+struct ScorePlan {
+  int nRT;          // 256-row tiles
+  int KC;           // keys per chunk (multiple of 64)
+  int maxCh;        // chunks of the longest row tile
+  int64_t W;        // work items H_kv * nRT * maxCh * G (some are empty)
+  int64_t Npad;     // N rounded up to 256
+};
+ScorePlan score_plan(const Layer& L);
+size_t lse_ws_bytes(const Layer& L);
 size_t score_ws_bytes(const Layer& L, int mode, int hidden_dim);
 hipError_t launch_row_lse(const Layer& L, const uint16_t* q, const uint16_t* k, float* lse,
-                          hipStream_t s);
+                          char* ws, hipStream_t s);
 hipError_t launch_score(const Layer& L, int mode, const uint16_t* q, const uint16_t* k,
                         const float* lse, const uint16_t* hidden, const uint16_t* w_o,
                         const uint16_t* v, int hidden_dim, float* scores, char* ws,

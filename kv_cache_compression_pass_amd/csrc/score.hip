@@ -5,8 +5,18 @@
 // normaliser of RDKV's attention probabilities, RDKV summary §2.1).  Pass 2 recomputes
 // a = exp(s q.k - l) and reduces it over query rows per key: the RDKV token weight (sum,
 // RDKV summary §2.1) or the KVzip+ numerator max_j a_{j,t} ||h_j|| (KVzap summary §2.1).
-// Both passes run QK^T on 32x32x16 bf16 matrix cores with fp32 accumulation; logits are
-// handled in the base-2 domain (x = s*log2(e) * q.k) so each probability is one exp2.
+//
+// Both passes run QK^T on 32x32x16 bf16 matrix cores with fp32 accumulation, and handle the
+// logits in the base-2 domain (x = s*log2(e) * q.k) so a probability is one exp2.
+// Work item = (KV head g, 256-row tile, key chunk, query head of the group); a block of 4
+// waves owns one item: each wave keeps the bf16 fragments of its 64 query rows in registers
+// and the chunk's keys stream through LDS in 64-key tiles (double buffered).  The same
+// register fragments serve both passes: pass 1 multiplies K x Q^T so a lane owns a query row
+// (row max / sum-exp in-lane), pass 2 multiplies Q x K^T so a lane owns a key (column sums
+// in-lane).  Blocks are mapped XCD-aware: the work items of one KV head run on one XCD so
+// its keys stay in that XCD's L2.  Pass 1 writes per-chunk (max, sum) partials that a tiny
+// kernel combines into l; pass 2 writes per-(head, row tile) column partials that a second
+// kernel reduces in a fixed order, so every result is bitwise reproducible.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -15,102 +25,132 @@ namespace kvc {
 namespace {
 
 constexpr int kThreads = 256;   // 4 waves per block in both passes
+constexpr int kRowsPerBlock = 256;
 constexpr int kPad = 8;         // bf16 elements of padding per LDS row (16 bytes)
+constexpr int kXcds = 8;        // MI355X: blocks are dealt round-robin to 8 XCDs
 
+struct Decomp {
+  int G, nRT, maxCh, KC;
+  int64_t W;
+};
+
+// Work item of a block.  Items are ordered (g, row tile descending, chunk, head in group),
+// and block b runs on XCD b % 8, so XCD x receives the x-th eighth of the items.
+__device__ __forceinline__ bool decode_work(const Decomp& dc, int& g, int& rt, int& ch, int& hl) {
+  const int64_t b = blockIdx.x;
+  const int64_t per = (dc.W + kXcds - 1) / kXcds;
+  int64_t w = (b % kXcds) * per + b / kXcds;
+  if (w >= dc.W) return false;
+  hl = (int)(w % dc.G);
+  w /= dc.G;
+  ch = (int)(w % dc.maxCh);
+  w /= dc.maxCh;
+  rt = dc.nRT - 1 - (int)(w % dc.nRT);
+  g = (int)(w / dc.nRT);
+  return true;
+}
+
+// Last key (exclusive) that any row of row tile rt can see.
+__device__ __forceinline__ int64_t tile_kend(int rt, int64_t N, int64_t Nq, int causal) {
+  if (!causal) return N;
+  int64_t last = (int64_t)(rt + 1) * kRowsPerBlock;
+  if (last > Nq) last = Nq;
+  int64_t e = N - Nq + last;
+  return e < N ? e : N;
+}
+
+// 64 rows x D bf16 from global into registers (D/32 16-byte chunks per thread); rows at or
+// beyond `limit` read as zero.
 template <int D>
-__device__ __forceinline__ void load_rows_to_regs(uint4 (&r)[D / 32], const uint16_t* base,
-                                                  int64_t row0, int64_t nrows_valid,
-                                                  int64_t row_limit) {
-  // 64 rows x D bf16 = 64*D/8 chunks of 16 bytes; 256 threads -> D/32 chunks each.
-  constexpr int kChunksPerRow = D / 8;
+__device__ __forceinline__ void load_tile_regs(uint4 (&r)[D / 32], const uint16_t* base,
+                                               int64_t row0, int64_t limit) {
+  constexpr int CPR = D / 8;
 #pragma unroll
   for (int j = 0; j < D / 32; ++j) {
-    int chunk = threadIdx.x + j * kThreads;
-    int rr = chunk / kChunksPerRow;
-    int cc = chunk % kChunksPerRow;
-    int64_t row = row0 + rr;
-    if (rr < nrows_valid && row < row_limit) {
-      r[j] = *reinterpret_cast<const uint4*>(base + row * D + cc * 8);
-    } else {
-      r[j] = make_uint4(0, 0, 0, 0);
-    }
+    const int chunk = threadIdx.x + j * kThreads;
+    const int rr = chunk / CPR, cc = chunk % CPR;
+    const int64_t row = row0 + rr;
+    r[j] = (row < limit) ? *reinterpret_cast<const uint4*>(base + row * D + cc * 8)
+                         : make_uint4(0, 0, 0, 0);
   }
 }
 
 template <int D>
-__device__ __forceinline__ void store_regs_to_lds(const uint4 (&r)[D / 32], uint16_t* lds) {
-  constexpr int kChunksPerRow = D / 8;
+__device__ __forceinline__ void store_tile_lds(const uint4 (&r)[D / 32], uint16_t* lds) {
+  constexpr int CPR = D / 8;
   constexpr int RS = D + kPad;
 #pragma unroll
   for (int j = 0; j < D / 32; ++j) {
-    int chunk = threadIdx.x + j * kThreads;
-    int rr = chunk / kChunksPerRow;
-    int cc = chunk % kChunksPerRow;
+    const int chunk = threadIdx.x + j * kThreads;
+    const int rr = chunk / CPR, cc = chunk % CPR;
     *reinterpret_cast<uint4*>(lds + rr * RS + cc * 8) = r[j];
   }
 }
 
+// bf16 fragments of this wave's 64 query rows: qf[nb][ks] holds row 32*nb + lane%32,
+// columns ks*16 + 8*(lane/32) .. +8.  Rows at or beyond Nq are zero.
+template <int D>
+__device__ __forceinline__ void load_q_frags(bf16x8 (&qf)[2][D / 16], const uint16_t* q, int h,
+                                             int64_t Nq, int64_t row0, int hi, int lo) {
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int64_t row = row0 + 32 * nb + lo;
+    const bool ok = row < Nq;
+    const uint16_t* qp = q + ((int64_t)h * Nq + (ok ? row : 0)) * D + 8 * hi;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      qf[nb][ks] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(qp + ks * 16) : make_uint4(0, 0, 0, 0));
+  }
+}
+
 // ---------------------------------------------------------------------------------------
-// Pass 1.  Block = (256 query rows, q head h); wave w owns rows [64w, 64w+64) of the tile.
-// K streams through LDS in 64-key tiles (double buffered); Q^T stays in registers.
-// D[m = key][n = row]: a lane holds one row and 16 keys per 32x32 block, so the online
-// max / sum-exp updates are in-lane plus one exchange with the lane 32 apart.
+// Pass 1: per chunk, m = max_t x and l = sum_t 2^(x - m) for every row, x = c * q.k.
+// D[m = key][n = row]: a lane holds one row and 16 keys of each 32-key block.
 // ---------------------------------------------------------------------------------------
 template <int D>
-__global__ void __launch_bounds__(kThreads)
-lse_pass1(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-          float* __restrict__ lse, int G, int64_t N, int64_t Nq, int causal, float c) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+lse_partial(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+            float2* __restrict__ part, float* __restrict__ lse, Decomp dc, int64_t N, int64_t Nq,
+            int causal, float c) {
   constexpr int RS = D + kPad;
   constexpr int KS = D / 16;
   __shared__ __attribute__((aligned(16))) uint16_t kt[2][64 * RS];
+  int g, rt, ch, hl;
+  if (!decode_work(dc, g, rt, ch, hl)) return;
+  const int64_t kend = tile_kend(rt, N, Nq, causal);
+  const int64_t k0 = (int64_t)ch * dc.KC;
+  if (k0 >= kend) return;                       // empty item: uniform for the block
+  const int64_t k1 = (k0 + dc.KC < kend) ? k0 + dc.KC : kend;
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hi = lane >> 5, lo = lane & 31;
-  const int h = blockIdx.y;
-  const int g = h / G;
+  const int h = g * dc.G + hl;
   const int64_t off = N - Nq;
-  const int64_t i_block = (int64_t)blockIdx.x * 256;
-  const int64_t i_wave = i_block + 64 * wave;
-
-  const uint16_t* kh = k + (int64_t)g * N * D;
-
-  // Q^T operand for this wave's 64 rows (2 column blocks of 32 rows).
-  bf16x8 qb[2][KS];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    int64_t row = i_wave + 32 * nb + lo;
-    bool ok = row < Nq;
-    const uint16_t* qp = q + ((int64_t)h * Nq + (ok ? row : 0)) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 v = ok ? *reinterpret_cast<const uint4*>(qp + ks * 16 + 8 * hi) : make_uint4(0, 0, 0, 0);
-      qb[nb][ks] = as_bf16x8(v);
-    }
-  }
-
-  const int64_t last_row_block = (i_block + 256 < Nq ? i_block + 256 : Nq) - 1;
-  const int64_t kend = causal ? (off + last_row_block + 1 < N ? off + last_row_block + 1 : N) : N;
+  const int64_t i_wave = (int64_t)rt * kRowsPerBlock + 64 * wave;
   int64_t kend_wave = 0;
   if (i_wave < Nq) {
-    int64_t lr = (i_wave + 63 < Nq ? i_wave + 63 : Nq - 1);
-    kend_wave = causal ? (off + lr + 1 < N ? off + lr + 1 : N) : N;
+    const int64_t lr = (i_wave + 63 < Nq) ? i_wave + 63 : Nq - 1;
+    kend_wave = causal ? ((off + lr + 1 < N) ? off + lr + 1 : N) : N;
   }
-  const int ntiles = (int)((kend + 63) / 64);
+  const uint16_t* kh = k + (int64_t)g * N * D;
+
+  bf16x8 qf[2][KS];
+  load_q_frags<D>(qf, q, h, Nq, i_wave, hi, lo);
 
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
+  const int ntiles = (int)((k1 - k0 + 63) / 64);
 
   uint4 pre[D / 32];
-  load_rows_to_regs<D>(pre, kh, 0, 64, N);
-  store_regs_to_lds<D>(pre, kt[0]);
+  load_tile_regs<D>(pre, kh, k0, N);
+  store_tile_lds<D>(pre, kt[0]);
   __syncthreads();
 
   for (int j = 0; j < ntiles; ++j) {
-    const int64_t t0 = (int64_t)j * 64;
-    if (j + 1 < ntiles) load_rows_to_regs<D>(pre, kh, t0 + 64, 64, N);
-    const uint16_t* kl = kt[j & 1];
+    const int64_t t0 = k0 + (int64_t)j * 64;
+    if (j + 1 < ntiles) load_tile_regs<D>(pre, kh, t0 + 64, N);
     if (t0 < kend_wave) {
+      const uint16_t* kl = kt[j & 1];
       f32x16 acc[2][2];
 #pragma unroll
       for (int a = 0; a < 2; ++a)
@@ -121,274 +161,271 @@ lse_pass1(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(kl + (mb * 32 + lo) * RS + ks * 16 + 8 * hi));
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(a, qb[nb][ks], acc[mb][nb]);
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(kl + (kb * 32 + lo) * RS + ks * 16 + 8 * hi));
+          acc[kb][0] = mfma32(a, qf[0][ks], acc[kb][0]);
+          acc[kb][1] = mfma32(a, qf[1][ks], acc[kb][1]);
         }
       }
       const bool full = (!causal || t0 + 63 <= off + i_wave) && (t0 + 64 <= N);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        const int64_t pos = off + i_wave + 32 * nb + lo;
-        float x[2][16];
-        float tmax = -INFINITY;
+        if (!full) {
+          const int64_t pos = off + i_wave + 32 * nb + lo;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float v = acc[mb][nb][i] * c;
-            if (!full) {
-              int64_t t = t0 + 32 * mb + acc_row(i, hi);
-              if (t >= N || (causal && t > pos)) v = -INFINITY;
+            for (int i = 0; i < 16; ++i) {
+              const int64_t t = t0 + 32 * kb + acc_row(i, hi);
+              if (t >= N || (causal && t > pos)) acc[kb][nb][i] = -INFINITY;
             }
-            x[mb][i] = v;
-            tmax = fmaxf(tmax, v);
-          }
+        }
+        float tmax = acc[0][nb][0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, acc[0][nb][i]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, acc[1][nb][i]);
         tmax = fmaxf(tmax, swap_half(tmax));
-        const float mnew = fmaxf(m_run[nb], tmax);
+        const float mnew = fmaxf(m_run[nb], tmax * c);
         if (mnew > -INFINITY) {
-          float s0 = 0.f, s1 = 0.f;
+          const float nm = -mnew;
+          float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
           for (int i = 0; i < 16; i += 2) {
-            s0 += fast_exp2(x[0][i] - mnew) + fast_exp2(x[0][i + 1] - mnew);
-            s1 += fast_exp2(x[1][i] - mnew) + fast_exp2(x[1][i + 1] - mnew);
+            s0 += fast_exp2(fmaf(acc[0][nb][i], c, nm));
+            s1 += fast_exp2(fmaf(acc[0][nb][i + 1], c, nm));
+            s2 += fast_exp2(fmaf(acc[1][nb][i], c, nm));
+            s3 += fast_exp2(fmaf(acc[1][nb][i + 1], c, nm));
           }
-          l_run[nb] = l_run[nb] * fast_exp2(m_run[nb] - mnew) + (s0 + s1);
+          l_run[nb] = fmaf(l_run[nb], fast_exp2(m_run[nb] - mnew), (s0 + s1) + (s2 + s3));
           m_run[nb] = mnew;
         }
       }
     }
-    if (j + 1 < ntiles) store_regs_to_lds<D>(pre, kt[(j + 1) & 1]);
+    if (j + 1 < ntiles) store_tile_lds<D>(pre, kt[(j + 1) & 1]);
     __syncthreads();
   }
 
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    float lt = l_run[nb] + swap_half(l_run[nb]);
-    int64_t row = i_wave + 32 * nb + lo;
+    const float lt = l_run[nb] + swap_half(l_run[nb]);
+    const int64_t row = i_wave + 32 * nb + lo;
     if (hi == 0 && row < Nq) {
-      float out = (m_run[nb] > -INFINITY) ? (m_run[nb] + log2f(lt)) * kLn2 : -INFINITY;
-      lse[(int64_t)h * Nq + row] = out;
+      if (dc.maxCh == 1)   // one chunk covers the row: write l itself
+        lse[(int64_t)h * Nq + row] = (m_run[nb] > -INFINITY) ? (m_run[nb] + log2f(lt)) * kLn2 : -INFINITY;
+      else
+        part[((int64_t)h * Nq + row) * dc.maxCh + ch] = make_float2(m_run[nb], lt);
     }
   }
 }
 
+// l = (M + log2 sum_c l_c 2^(m_c - M)) * ln 2 over the chunks of the row's tile.
+__global__ void lse_combine(const float2* __restrict__ part, float* __restrict__ lse, int Hq,
+                            int64_t N, int64_t Nq, int causal, int KC, int maxCh) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)Hq * Nq) return;
+  const int64_t row = idx % Nq;
+  const int rt = (int)(row / kRowsPerBlock);
+  const int nch = (int)((tile_kend(rt, N, Nq, causal) + KC - 1) / KC);
+  const float2* p = part + idx * maxCh;
+  float M = -INFINITY;
+  for (int ch = 0; ch < nch; ++ch) M = fmaxf(M, p[ch].x);
+  float L = 0.f;
+  for (int ch = 0; ch < nch; ++ch)
+    if (p[ch].x > -INFINITY) L += p[ch].y * exp2f(p[ch].x - M);
+  lse[idx] = (M > -INFINITY) ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
 // ---------------------------------------------------------------------------------------
-// Pass 2.  Block = (256-key tile, query-row chunk, KV head g); wave w owns keys
-// [t0 + 64w, t0 + 64w + 64) whose K^T operand stays in registers.  The block walks the
-// group's query heads and the chunk's rows in 64-row sub-tiles staged through LDS together
-// with each row's base-2 offset (lse*log2e, minus log2||h|| in MAX mode).
-// D[m = row][n = key]: a lane holds one key and 16 rows per 32x32 block, so the column
-// reduction is in-lane plus one exchange with the lane 32 apart.  Each block writes its
-// partial column sums (or maxima per query head) to the workspace; a second kernel
-// reduces the chunks in a fixed order, so results are bitwise reproducible.
+// Pass 2: column reductions.  D[m = row][n = key] (operands swapped): a lane holds one key
+// and 16 rows of each 32-row block.  SUM: partial = sum_rows 2^(x - l'), l' = l*log2(e);
+// MAX: partial = max_rows (x - l'), l' = l*log2(e) - log2||h||.  One partial per
+// (query head, row tile, key), the four waves' rows summed (or maxed) in a fixed order.
 // ---------------------------------------------------------------------------------------
 template <int D, bool MAXMODE>
-__global__ void __launch_bounds__(kThreads)
-score_pass2(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-            const float* __restrict__ lse, const float* __restrict__ hlog2,
-            float* __restrict__ partial, int G, int64_t N, int64_t Nq, int causal, float c,
-            int QC, int maxC, int64_t Npad) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+score_partial(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+              const float* __restrict__ lse, const float* __restrict__ hlog2,
+              float* __restrict__ part, Decomp dc, int64_t N, int64_t Nq, int causal, float c,
+              int64_t Npad) {
   constexpr int RS = D + kPad;
   constexpr int KS = D / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t qt[2][64 * RS];
-  __shared__ float lt[2][64];
+  __shared__ __attribute__((aligned(16))) uint16_t kt[2][64 * RS];
+  __shared__ float cb[2][4][64];
+  __shared__ float lrow[kRowsPerBlock];
+  int g, rt, ch, hl;
+  if (!decode_work(dc, g, rt, ch, hl)) return;
+  const int64_t kend = tile_kend(rt, N, Nq, causal);
+  const int64_t k0 = (int64_t)ch * dc.KC;
+  if (k0 >= kend) return;
+  const int64_t k1 = (k0 + dc.KC < kend) ? k0 + dc.KC : kend;
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hi = lane >> 5, lo = lane & 31;
-  const int tile = blockIdx.x;
-  const int chunk = blockIdx.y;
-  const int g = blockIdx.z;
+  const int h = g * dc.G + hl;
   const int64_t off = N - Nq;
-  const int64_t t0 = (int64_t)tile * kScoreTileKeys;
-  const int64_t kw0 = t0 + 64 * wave;
-
-  int64_t i_first = 0;
-  if (causal) {
-    int64_t f = t0 - off;
-    i_first = f > 0 ? (f & ~int64_t(63)) : 0;
+  const int64_t i_block = (int64_t)rt * kRowsPerBlock;
+  const int64_t i_wave = i_block + 64 * wave;
+  int64_t kend_wave = 0;
+  if (i_wave < Nq) {
+    const int64_t lr = (i_wave + 63 < Nq) ? i_wave + 63 : Nq - 1;
+    kend_wave = causal ? ((off + lr + 1 < N) ? off + lr + 1 : N) : N;
   }
-  const int64_t r_begin = i_first + (int64_t)chunk * QC;
-  if (r_begin >= Nq) return;   // uniform for the block
-  const int64_t r_end = (r_begin + QC < Nq) ? r_begin + QC : Nq;
-  const int nsub = (int)((r_end - r_begin + 63) / 64);
-  const int total_it = G * nsub;
-
-  // K^T operand: this wave's 64 keys (2 column blocks of 32 keys).
   const uint16_t* kh = k + (int64_t)g * N * D;
-  bf16x8 kb[2][KS];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    int64_t t = kw0 + 32 * nb + lo;
-    const uint16_t* kp = kh + (t < N ? t : N - 1) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kb[nb][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(kp + ks * 16 + 8 * hi));
-  }
+  float* out = part + ((int64_t)h * dc.nRT + rt) * Npad;
 
-  float colacc[2];
-  colacc[0] = colacc[1] = MAXMODE ? -INFINITY : 0.f;
-
-  auto row_offset = [&](int hh, int64_t row) -> float {
-    if (row >= Nq) return INFINITY;
-    float l2 = lse[(int64_t)hh * Nq + row] * kLog2e;
-    if (MAXMODE) l2 -= hlog2[row];
-    return l2;
-  };
-
-  // stage iteration 0
-  uint4 pre[D / 32];
-  float lpre = 0.f;
   {
-    const int hh = g * G;
-    load_rows_to_regs<D>(pre, q + (int64_t)hh * Nq * D, r_begin, 64, Nq);
-    if (threadIdx.x < 64) lpre = row_offset(hh, r_begin + threadIdx.x);
-    store_regs_to_lds<D>(pre, qt[0]);
-    if (threadIdx.x < 64) lt[0][threadIdx.x] = lpre;
-  }
-  __syncthreads();
-
-  for (int it = 0; it < total_it; ++it) {
-    const int hl = it / nsub;
-    const int sub = it % nsub;
-    const int64_t r = r_begin + (int64_t)sub * 64;
-    const int buf = it & 1;
-    if (it + 1 < total_it) {
-      const int hl2 = (it + 1) / nsub;
-      const int64_t r2 = r_begin + (int64_t)((it + 1) % nsub) * 64;
-      const int hh2 = g * G + hl2;
-      load_rows_to_regs<D>(pre, q + (int64_t)hh2 * Nq * D, r2, 64, Nq);
-      if (threadIdx.x < 64) lpre = row_offset(hh2, r2 + threadIdx.x);
+    const int64_t row = i_block + threadIdx.x;
+    float v = INFINITY;                            // rows beyond Nq contribute nothing
+    if (row < Nq) {
+      v = lse[(int64_t)h * Nq + row] * kLog2e;
+      if (MAXMODE) v -= hlog2[row];
     }
-    const int64_t pp = off + r;       // position of the sub-tile's first row
-    const bool any = !causal || kw0 <= pp + 63;
-    if (any) {
-      const uint16_t* ql = qt[buf];
-      f32x16 acc[2][2];
+    lrow[threadIdx.x] = v;
+  }
+  bf16x8 qf[2][KS];
+  load_q_frags<D>(qf, q, h, Nq, i_wave, hi, lo);
+
+  uint4 pre[D / 32];
+  load_tile_regs<D>(pre, kh, k0, N);
+  store_tile_lds<D>(pre, kt[0]);
+  __syncthreads();
+  float lv[2][16];
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+  for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+    for (int i = 0; i < 16; ++i) lv[mb][i] = lrow[64 * wave + 32 * mb + acc_row(i, hi)];
+
+  const int ntiles = (int)((k1 - k0 + 63) / 64);
+  for (int j = 0; j < ntiles; ++j) {
+    const int64_t t0 = k0 + (int64_t)j * 64;
+    if (j + 1 < ntiles) load_tile_regs<D>(pre, kh, t0 + 64, N);
+    // the previous tile's wave partials are complete (barrier at the end of j-1)
+    if (j > 0 && threadIdx.x < 64) {
+      const float* cp = &cb[(j - 1) & 1][0][threadIdx.x];
+      float r;
+      if (MAXMODE) r = fmaxf(fmaxf(cp[0], cp[64]), fmaxf(cp[128], cp[192]));
+      else r = (cp[0] + cp[64]) + (cp[128] + cp[192]);
+      out[t0 - 64 + threadIdx.x] = r;
+    }
+    const uint16_t* kl = kt[j & 1];
+    const bool any = t0 < kend_wave;
+    const bool full = (!causal || t0 + 63 <= off + i_wave) && (t0 + 64 <= N);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+    for (int kb = 0; kb < 2; ++kb) {
+      float colv = MAXMODE ? -INFINITY : 0.f;
+      if (any) {
+        f32x16 acc[2];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+        for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(ql + (mb * 32 + lo) * RS + ks * 16 + 8 * hi));
+          for (int i = 0; i < 16; ++i) acc[a][i] = 0.f;
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(a, kb[nb][ks], acc[mb][nb]);
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4*>(kl + (kb * 32 + lo) * RS + ks * 16 + 8 * hi));
+          acc[0] = mfma32(qf[0][ks], b, acc[0]);
+          acc[1] = mfma32(qf[1][ks], b, acc[1]);
         }
-      }
-      float lv[2][16];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) lv[mb][i] = lt[buf][32 * mb + acc_row(i, hi)];
-      const bool full = !causal || kw0 + 63 <= pp;
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int64_t t = kw0 + 32 * nb + lo;
+        const int64_t t = t0 + 32 * kb + lo;
         if (MAXMODE) {
-          float mx = -INFINITY;
+          float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              float x = fmaf(acc[mb][nb][i], c, -lv[mb][i]);
-              if (!full && t > pp + 32 * mb + acc_row(i, hi)) x = -INFINITY;
-              mx = fmaxf(mx, x);
+            for (int i = 0; i < 16; i += 2) {
+              float x0 = fmaf(acc[mb][i], c, -lv[mb][i]);
+              float x1 = fmaf(acc[mb][i + 1], c, -lv[mb][i + 1]);
+              if (!full) {
+                const int64_t p0 = off + i_wave + 32 * mb + acc_row(i, hi);
+                if (t >= N || (causal && t > p0)) x0 = -INFINITY;
+                if (t >= N || (causal && t > p0 + 1)) x1 = -INFINITY;
+              }
+              mx0 = fmaxf(mx0, x0);
+              mx1 = fmaxf(mx1, x1);
             }
-          colacc[nb] = fmaxf(colacc[nb], mx);
+          colv = fmaxf(mx0, mx1);
+          colv = fmaxf(colv, swap_half(colv));
         } else {
-          float s[2];
+          float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
-            float e[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              float x = fmaf(acc[mb][nb][i], c, -lv[mb][i]);
-              if (!full && t > pp + 32 * mb + acc_row(i, hi)) x = -INFINITY;
-              e[i] = fast_exp2(x);
+          for (int i = 0; i < 16; i += 2) {
+            float x0 = fmaf(acc[0][i], c, -lv[0][i]);
+            float x1 = fmaf(acc[0][i + 1], c, -lv[0][i + 1]);
+            float x2 = fmaf(acc[1][i], c, -lv[1][i]);
+            float x3 = fmaf(acc[1][i + 1], c, -lv[1][i + 1]);
+            if (!full) {
+              const int64_t p0 = off + i_wave + acc_row(i, hi);
+              if (t >= N || (causal && t > p0)) x0 = -INFINITY;
+              if (t >= N || (causal && t > p0 + 1)) x1 = -INFINITY;
+              if (t >= N || (causal && t > p0 + 32)) x2 = -INFINITY;
+              if (t >= N || (causal && t > p0 + 33)) x3 = -INFINITY;
             }
-#pragma unroll
-            for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-              for (int i = 0; i < w; ++i) e[i] += e[i + w];
-            s[mb] = e[0];
+            s0 += fast_exp2(x0);
+            s1 += fast_exp2(x1);
+            s2 += fast_exp2(x2);
+            s3 += fast_exp2(x3);
           }
-          colacc[nb] += s[0] + s[1];
+          colv = (s0 + s1) + (s2 + s3);
+          colv = colv + swap_half(colv);
         }
       }
+      if (hi == 0) cb[j & 1][wave][32 * kb + lo] = colv;
     }
-    if (MAXMODE && sub == nsub - 1) {
-      // finished query head hl: write its column maxima
-      const int hh = g * G + hl;
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        float m = fmaxf(colacc[nb], swap_half(colacc[nb]));
-        if (hi == 0) partial[((int64_t)hh * maxC + chunk) * Npad + kw0 + 32 * nb + lo] = m;
-        colacc[nb] = -INFINITY;
-      }
-    }
-    if (it + 1 < total_it) {
-      store_regs_to_lds<D>(pre, qt[buf ^ 1]);
-      if (threadIdx.x < 64) lt[buf ^ 1][threadIdx.x] = lpre;
-    }
+    if (j + 1 < ntiles) store_tile_lds<D>(pre, kt[(j + 1) & 1]);
     __syncthreads();
   }
-
-  if (!MAXMODE) {
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      float s = colacc[nb] + swap_half(colacc[nb]);
-      if (hi == 0) partial[((int64_t)g * maxC + chunk) * Npad + kw0 + 32 * nb + lo] = s;
-    }
+  if (threadIdx.x < 64) {
+    const float* cp = &cb[(ntiles - 1) & 1][0][threadIdx.x];
+    float r;
+    if (MAXMODE) r = fmaxf(fmaxf(cp[0], cp[64]), fmaxf(cp[128], cp[192]));
+    else r = (cp[0] + cp[64]) + (cp[128] + cp[192]);
+    out[k0 + (int64_t)(ntiles - 1) * 64 + threadIdx.x] = r;
   }
 }
 
-__device__ __forceinline__ int chunks_of_tile(int64_t t0, int64_t N, int64_t Nq, int causal, int QC) {
-  int64_t i_first = 0;
-  if (causal) {
-    int64_t f = t0 - (N - Nq);
-    i_first = f > 0 ? (f & ~int64_t(63)) : 0;
-  }
-  if (i_first >= Nq) return 0;
-  return (int)((Nq - i_first + QC - 1) / QC);
-}
-
-// w[g][t] = sum over chunks (ascending) of the partial column sums.
-__global__ void score_reduce_sum(const float* __restrict__ partial, float* __restrict__ scores,
-                                 int64_t N, int64_t Nq, int causal, int QC, int maxC,
-                                 int64_t Npad, int Hkv) {
-  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// SUM: w[g][t] = sum over the group's heads, then over the row tiles that see t (ascending).
+__global__ void score_reduce_sum(const float* __restrict__ part, float* __restrict__ scores,
+                                 int Hkv, int G, int nRT, int64_t N, int64_t Nq, int causal,
+                                 int64_t Npad) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)Hkv * N) return;
-  int g = (int)(idx / N);
-  int64_t t = idx % N;
-  int nc = chunks_of_tile((t / kScoreTileKeys) * kScoreTileKeys, N, Nq, causal, QC);
+  const int g = (int)(idx / N);
+  const int64_t t = idx % N;
+  int rt0 = 0;
+  if (causal) {
+    const int64_t rel = t - (N - Nq);                 // first row index that sees t
+    rt0 = rel > 0 ? (int)(rel / kRowsPerBlock) : 0;
+  }
   float s = 0.f;
-  for (int ch = 0; ch < nc; ++ch) s += partial[((int64_t)g * maxC + ch) * Npad + t];
+  for (int hl = 0; hl < G; ++hl) {
+    const float* p = part + ((int64_t)(g * G + hl) * nRT) * Npad + t;
+    for (int rt = rt0; rt < nRT; ++rt) s += p[(int64_t)rt * Npad];
+  }
   scores[idx] = s;
 }
 
-// s+[g][t] = max over the group's heads h of exp2(max over chunks of partial) / ||W_O^h v||.
-__global__ void score_reduce_max(const float* __restrict__ partial, const float* __restrict__ won,
-                                 float* __restrict__ scores, int64_t N, int64_t Nq, int causal,
-                                 int QC, int maxC, int64_t Npad, int Hkv, int G) {
-  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// MAX: s+[g][t] = max over the group's heads h of 2^(max over row tiles of part) / ||W_O^h v_t||.
+__global__ void score_reduce_max(const float* __restrict__ part, const float* __restrict__ won,
+                                 float* __restrict__ scores, int Hkv, int G, int nRT, int64_t N,
+                                 int64_t Nq, int causal, int64_t Npad) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)Hkv * N) return;
-  int g = (int)(idx / N);
-  int64_t t = idx % N;
-  int nc = chunks_of_tile((t / kScoreTileKeys) * kScoreTileKeys, N, Nq, causal, QC);
+  const int g = (int)(idx / N);
+  const int64_t t = idx % N;
+  int rt0 = 0;
+  if (causal) {
+    const int64_t rel = t - (N - Nq);
+    rt0 = rel > 0 ? (int)(rel / kRowsPerBlock) : 0;
+  }
   float best = 0.f;
   for (int hl = 0; hl < G; ++hl) {
-    int hh = g * G + hl;
+    const int hh = g * G + hl;
+    const float* p = part + ((int64_t)hh * nRT) * Npad + t;
     float m = -INFINITY;
-    for (int ch = 0; ch < nc; ++ch) m = fmaxf(m, partial[((int64_t)hh * maxC + ch) * Npad + t]);
-    float num = exp2f(m);
-    float den = won[(int64_t)hh * N + t];
-    float r = (num == 0.f && den == 0.f) ? 0.f : num / den;
+    for (int rt = rt0; rt < nRT; ++rt) m = fmaxf(m, p[(int64_t)rt * Npad]);
+    const float num = exp2f(m);
+    const float den = won[(int64_t)hh * N + t];
+    const float r = (num == 0.f && den == 0.f) ? 0.f : num / den;
     best = fmaxf(best, r);
   }
   scores[idx] = best;
@@ -510,46 +547,88 @@ value_out_norm(const uint16_t* __restrict__ v, const float* __restrict__ gram,
 
 }  // namespace
 
-int score_chunk_rows(const Layer& L) {
-  // Split a tile's query rows so that no tile has more than 16 chunks; at least 256 rows.
-  int64_t rows = (L.nq + 15) / 16;
-  int64_t qc = ((rows + 255) / 256) * 256;
-  if (qc < 256) qc = 256;
-  return (int)qc;
+ScorePlan score_plan(const Layer& L) {
+  ScorePlan p;
+  p.nRT = (int)((L.nq + kRowsPerBlock - 1) / kRowsPerBlock);
+  p.Npad = ((L.n + 255) / 256) * 256;
+  auto kend = [&](int rt) -> int64_t {
+    if (!L.causal) return L.n;
+    int64_t last = (int64_t)(rt + 1) * kRowsPerBlock;
+    if (last > L.nq) last = L.nq;
+    int64_t e = L.n - L.nq + last;
+    return e < L.n ? e : L.n;
+  };
+  int64_t kmax = 0;
+  for (int rt = 0; rt < p.nRT; ++rt) kmax = kend(rt) > kmax ? kend(rt) : kmax;
+  // With >= 1024 (head, row tile) items one chunk per item balances well (longest items run
+  // first); otherwise split the keys into chunks (<= 2048, >= 512 keys) until there are
+  // >= 2048 non-empty items.
+  int KC = (int)(((kmax + 63) / 64) * 64);
+  if ((int64_t)p.nRT * L.hq < 1024) {
+    KC = 2048;
+    for (; KC > 512; KC /= 2) {
+      int64_t items = 0;
+      for (int rt = 0; rt < p.nRT; ++rt) items += (kend(rt) + KC - 1) / KC;
+      if (items * L.hq >= 2048) break;
+    }
+  }
+  p.KC = KC;
+  p.maxCh = (int)((kmax + KC - 1) / KC);
+  p.W = (int64_t)L.hkv * p.nRT * p.maxCh * L.G;
+  return p;
 }
 
-int score_max_chunks(const Layer& L) {
-  int QC = score_chunk_rows(L);
-  return (int)((L.nq + QC - 1) / QC);
+static Decomp decomp_of(const Layer& L, const ScorePlan& p) {
+  Decomp d;
+  d.G = L.G;
+  d.nRT = p.nRT;
+  d.maxCh = p.maxCh;
+  d.KC = p.KC;
+  d.W = p.W;
+  return d;
 }
 
-static int64_t npad_of(const Layer& L) {
-  return ((L.n + kScoreTileKeys - 1) / kScoreTileKeys) * kScoreTileKeys;
+static unsigned grid_of(const ScorePlan& p) {
+  return (unsigned)(((p.W + kXcds - 1) / kXcds) * kXcds);
 }
 
 static constexpr int kGramSplits = 14;
 
+size_t lse_ws_bytes(const Layer& L) {
+  const ScorePlan p = score_plan(L);
+  WsPlan w;
+  w.take((size_t)L.hq * L.nq * p.maxCh * sizeof(float2));
+  return w.off;
+}
+
 size_t score_ws_bytes(const Layer& L, int mode, int hidden_dim) {
   (void)hidden_dim;
-  WsPlan p;
-  int64_t units = (mode == KVC_SCORE_MAX) ? L.hq : L.hkv;
-  p.take((size_t)units * score_max_chunks(L) * npad_of(L) * sizeof(float));
+  const ScorePlan p = score_plan(L);
+  WsPlan w;
+  w.take((size_t)L.hq * p.nRT * p.Npad * sizeof(float));
   if (mode == KVC_SCORE_MAX) {
-    p.take((size_t)L.nq * sizeof(float));                                  // log2 ||h||
-    p.take((size_t)L.hq * kGramSplits * L.d * L.d * sizeof(float));        // gram partials
-    p.take((size_t)L.hq * L.d * L.d * sizeof(float));                      // gram
-    p.take((size_t)L.hq * L.n * sizeof(float));                            // ||W_O^h v||
+    w.take((size_t)L.nq * sizeof(float));                                  // log2 ||h||
+    w.take((size_t)L.hq * kGramSplits * L.d * L.d * sizeof(float));        // gram partials
+    w.take((size_t)L.hq * L.d * L.d * sizeof(float));                      // gram
+    w.take((size_t)L.hq * L.n * sizeof(float));                            // ||W_O^h v||
   }
-  return p.off;
+  return w.off;
 }
 
 hipError_t launch_row_lse(const Layer& L, const uint16_t* q, const uint16_t* k, float* lse,
-                          hipStream_t s) {
-  dim3 grid((unsigned)((L.nq + 255) / 256), (unsigned)L.hq);
+                          char* ws, hipStream_t s) {
+  const ScorePlan p = score_plan(L);
+  const Decomp dc = decomp_of(L, p);
+  WsPlan w;
+  float2* part = reinterpret_cast<float2*>(ws + w.take((size_t)L.hq * L.nq * p.maxCh * sizeof(float2)));
   if (L.d == 128)
-    lse_pass1<128><<<grid, kThreads, 0, s>>>(q, k, lse, L.G, L.n, L.nq, L.causal, L.c_log2);
+    lse_partial<128><<<grid_of(p), kThreads, 0, s>>>(q, k, part, lse, dc, L.n, L.nq, L.causal, L.c_log2);
   else
-    lse_pass1<64><<<grid, kThreads, 0, s>>>(q, k, lse, L.G, L.n, L.nq, L.causal, L.c_log2);
+    lse_partial<64><<<grid_of(p), kThreads, 0, s>>>(q, k, part, lse, dc, L.n, L.nq, L.causal, L.c_log2);
+  if (p.maxCh > 1) {
+    const int64_t rows = (int64_t)L.hq * L.nq;
+    lse_combine<<<(unsigned)((rows + 255) / 256), 256, 0, s>>>(part, lse, L.hq, L.n, L.nq, L.causal, p.KC, p.maxCh);
+  }
   return hipGetLastError();
 }
 
@@ -557,29 +636,26 @@ hipError_t launch_score(const Layer& L, int mode, const uint16_t* q, const uint1
                         const float* lse, const uint16_t* hidden, const uint16_t* w_o,
                         const uint16_t* v, int hidden_dim, float* scores, char* ws,
                         hipStream_t s) {
-  const int QC = score_chunk_rows(L);
-  const int maxC = score_max_chunks(L);
-  const int64_t Npad = npad_of(L);
-  const int ntiles = (int)(Npad / kScoreTileKeys);
-  WsPlan p;
+  const ScorePlan p = score_plan(L);
+  const Decomp dc = decomp_of(L, p);
   const bool mx = (mode == KVC_SCORE_MAX);
-  int64_t units = mx ? L.hq : L.hkv;
-  float* partial = reinterpret_cast<float*>(ws + p.take((size_t)units * maxC * Npad * sizeof(float)));
+  WsPlan w;
+  float* part = reinterpret_cast<float*>(ws + w.take((size_t)L.hq * p.nRT * p.Npad * sizeof(float)));
   float* hlog2 = nullptr;
   float* won = nullptr;
   if (mx) {
-    hlog2 = reinterpret_cast<float*>(ws + p.take((size_t)L.nq * sizeof(float)));
-    float* gp = reinterpret_cast<float*>(ws + p.take((size_t)L.hq * kGramSplits * L.d * L.d * sizeof(float)));
-    float* gram = reinterpret_cast<float*>(ws + p.take((size_t)L.hq * L.d * L.d * sizeof(float)));
-    won = reinterpret_cast<float*>(ws + p.take((size_t)L.hq * L.n * sizeof(float)));
+    hlog2 = reinterpret_cast<float*>(ws + w.take((size_t)L.nq * sizeof(float)));
+    float* gp = reinterpret_cast<float*>(ws + w.take((size_t)L.hq * kGramSplits * L.d * L.d * sizeof(float)));
+    float* gram = reinterpret_cast<float*>(ws + w.take((size_t)L.hq * L.d * L.d * sizeof(float)));
+    won = reinterpret_cast<float*>(ws + w.take((size_t)L.hq * L.n * sizeof(float)));
     hidden_log2_norm<<<(unsigned)L.nq, 256, 0, s>>>(hidden, hlog2, hidden_dim);
-    int rps = (hidden_dim + kGramSplits - 1) / kGramSplits;
+    const int rps = (hidden_dim + kGramSplits - 1) / kGramSplits;
     dim3 gg((unsigned)L.hq, kGramSplits);
     if (L.d == 128)
       wo_gram_partial<128><<<gg, 256, 0, s>>>(w_o, gp, L.hq, hidden_dim, rps);
     else
       wo_gram_partial<64><<<gg, 256, 0, s>>>(w_o, gp, L.hq, hidden_dim, rps);
-    int64_t ng = (int64_t)L.hq * L.d * L.d;
+    const int64_t ng = (int64_t)L.hq * L.d * L.d;
     wo_gram_reduce<<<(unsigned)((ng + 255) / 256), 256, 0, s>>>(gp, gram, L.hq, kGramSplits, L.d * L.d);
     dim3 gv((unsigned)((L.n + 255) / 256), (unsigned)L.hq);
     if (L.d == 128)
@@ -587,24 +663,24 @@ hipError_t launch_score(const Layer& L, int mode, const uint16_t* q, const uint1
     else
       value_out_norm<64><<<gv, 256, 0, s>>>(v, gram, won, L.G, L.n);
   }
-  dim3 grid((unsigned)ntiles, (unsigned)maxC, (unsigned)L.hkv);
+  const unsigned grid = grid_of(p);
   if (L.d == 128) {
     if (mx)
-      score_pass2<128, true><<<grid, kThreads, 0, s>>>(q, k, lse, hlog2, partial, L.G, L.n, L.nq, L.causal, L.c_log2, QC, maxC, Npad);
+      score_partial<128, true><<<grid, kThreads, 0, s>>>(q, k, lse, hlog2, part, dc, L.n, L.nq, L.causal, L.c_log2, p.Npad);
     else
-      score_pass2<128, false><<<grid, kThreads, 0, s>>>(q, k, lse, nullptr, partial, L.G, L.n, L.nq, L.causal, L.c_log2, QC, maxC, Npad);
+      score_partial<128, false><<<grid, kThreads, 0, s>>>(q, k, lse, nullptr, part, dc, L.n, L.nq, L.causal, L.c_log2, p.Npad);
   } else {
     if (mx)
-      score_pass2<64, true><<<grid, kThreads, 0, s>>>(q, k, lse, hlog2, partial, L.G, L.n, L.nq, L.causal, L.c_log2, QC, maxC, Npad);
+      score_partial<64, true><<<grid, kThreads, 0, s>>>(q, k, lse, hlog2, part, dc, L.n, L.nq, L.causal, L.c_log2, p.Npad);
     else
-      score_pass2<64, false><<<grid, kThreads, 0, s>>>(q, k, lse, nullptr, partial, L.G, L.n, L.nq, L.causal, L.c_log2, QC, maxC, Npad);
+      score_partial<64, false><<<grid, kThreads, 0, s>>>(q, k, lse, nullptr, part, dc, L.n, L.nq, L.causal, L.c_log2, p.Npad);
   }
-  int64_t total = (int64_t)L.hkv * L.n;
-  unsigned rb = (unsigned)((total + 255) / 256);
+  const int64_t total = (int64_t)L.hkv * L.n;
+  const unsigned rb = (unsigned)((total + 255) / 256);
   if (mx)
-    score_reduce_max<<<rb, 256, 0, s>>>(partial, won, scores, L.n, L.nq, L.causal, QC, maxC, Npad, L.hkv, L.G);
+    score_reduce_max<<<rb, 256, 0, s>>>(part, won, scores, L.hkv, L.G, p.nRT, L.n, L.nq, L.causal, p.Npad);
   else
-    score_reduce_sum<<<rb, 256, 0, s>>>(partial, scores, L.n, L.nq, L.causal, QC, maxC, Npad, L.hkv);
+    score_reduce_sum<<<rb, 256, 0, s>>>(part, scores, L.hkv, L.G, p.nRT, L.n, L.nq, L.causal, p.Npad);
   return hipGetLastError();
 }
 

@@ -27,7 +27,7 @@ def desc_of(hq, hkv, d, N, Nq, causal=True, scale=0.0):
 
 def row_lse(desc, q, k):
     lse = torch.empty(desc.n_q_heads, desc.n_queries, dtype=torch.float32, device=DEV)
-    kvc.kvc_row_lse(desc, q, k, lse)
+    kvc.kvc_row_lse(desc, q, k, lse, kvc.workspace(kvc.OP_ROW_LSE, desc, 0, DEV))
     torch.cuda.synchronize()
     return lse
 

@@ -140,5 +140,8 @@ def test_valid_request_without_device_reports_no_device(lib):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     d = _desc()
+    need = lib.kvc_workspace_size(C.OP_ROW_LSE, ctypes.byref(d), 0)
     st = lib.kvc_row_lse(ctypes.byref(d), FAKE, FAKE, FAKE, None, 0, None)
+    assert st == 3, lib.kvc_last_error()
+    st = lib.kvc_row_lse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, need, None)
     assert st == 4, lib.kvc_last_error()
