@@ -10,11 +10,18 @@
 // cumulative rate fits, stopping at the first that does not.
 //
 // GPU plan: positive float64 keys order like their bit patterns, so lambda* is found by a
-// weighted MSB-first radix select over the 64-bit patterns (8 passes of 8 bits: block-private
-// LDS histograms of integer rates, one global integer histogram per pass, a one-block digit
-// choice).  Integer histograms make the selection exact and order-independent.  The tie rule
-// is an ordered exclusive scan over units (block sums, a one-block scan, then per-unit
-// ranks).  Top-k uses the same machinery per KV head on order-preserving 32-bit score keys.
+// weighted MSB-first radix select over the 64-bit patterns (11-bit digits; integer
+// histograms of step rates, so the selection is exact and independent of summation order).
+// Each bin also records its smallest and largest key: once the chosen bin holds a single key
+// value, that value is lambda* and the remaining passes do nothing.  The tie rule is an
+// ordered exclusive scan over units.  Top-k runs the same select per KV head on
+// order-preserving 32-bit score keys with weight 1.
+//
+// Two launch shapes:
+//  * small stages (<= 2048 units, e.g. the K-channel stage): one block does everything in LDS;
+//  * larger stages: per pass a histogram kernel (block-private LDS bins flushed with integer
+//    atomics) and a one-block select kernel; then tie sums, their scan, and the assignment.
+//    Kernel boundaries order every step; no cross-block fences are needed.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -22,332 +29,561 @@ namespace kvc {
 
 namespace {
 
-constexpr int kUnitsPerBlock = 1024;   // 256 threads x 4 units
-constexpr int kMaxSeg = 1024;          // segments (KV heads) for top-k
+constexpr int kUnitsPerBlock = 1024;   // multi-block path: 256 threads x 4 units
+constexpr int kSmallUnits = 2048;      // single-block path: up to 8192 keys in LDS
+constexpr int kMaxSeg = 1024;
+constexpr int kDigitBits = 11;
+constexpr int kBins = 1 << kDigitBits;
 
 __constant__ uint32_t kThetaNum[4] = {3u, 3u, 15u, 255u};
 __constant__ uint32_t kThetaDen[4] = {8u, 32u, 1024u, 524288u};
 __constant__ uint32_t kLevels[5] = {0u, 2u, 4u, 8u, 16u};
 
 struct SelState {
-  uint64_t prefix;      // selected key bits so far
+  uint64_t prefix;      // selected key bits so far (the full key once done)
   int64_t brem;         // budget left for keys above the prefix
-  int64_t budget;       // B
-  int64_t elements;     // E (V/K) or kept tokens per head (top-k)
+  int64_t budget;       // B (V/K); kept tokens per head (top-k)
   int32_t all_fit;      // every positive key fits: lambda* = 0, no ties
   int32_t none;         // top-k with k == 0
-  int64_t pad[2];
+  int32_t done;         // lambda* known
+  int32_t pad;
 };
 
 struct AllocWs {
   int32_t* status;
   SelState* st;         // [nseg]
-  int64_t* hist;        // [passes][nseg][256]
-  uint64_t* keys;       // [U][kpu]
-  int64_t* rcount;      // [Hkv] retained tokens per head (K stage)
-  int64_t* bsum;        // [nseg][nblk] tie rate per block
+  int64_t* hist;        // [nseg][kBins]  (the current pass)
+  uint64_t* hmin;       // [nseg][kBins]
+  uint64_t* hmax;       // [nseg][kBins]
+  uint64_t* keys;       // [U][4] (V/K)
+  int64_t* rcount;      // [Hkv]
+  int64_t* bsum;        // [nseg][nblk]
   int64_t* bexcl;       // [nseg][nblk]
   int64_t* used_part;   // [nseg][nblk]
   double* dist_part;    // [nseg][nblk]
 };
 
-// ---- stage setup -----------------------------------------------------------------------
-
-// R_g = #tokens with bits_v > 0 (one block per head); a width outside {0,2,4,8,16} is a
-// device data error.
-__global__ void __launch_bounds__(256)
-count_retained(const uint8_t* __restrict__ bits_v, int64_t N, int64_t* __restrict__ rcount,
-               int32_t* status) {
-  const int g = blockIdx.x;
-  int64_t cnt = 0;
-  bool bad = false;
-  for (int64_t t = threadIdx.x; t < N; t += 256) {
-    uint32_t b = bits_v[(int64_t)g * N + t];
-    cnt += (b > 0);
-    bad |= !valid_width(b);
-  }
-  __shared__ int64_t red[256];
-  red[threadIdx.x] = cnt;
-  __syncthreads();
-  for (int w = 128; w >= 1; w >>= 1) {
-    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-    __syncthreads();
-  }
-  if (bad) set_status(status, KVC_DEV_BAD_WIDTH);
-  if (threadIdx.x == 0) rcount[g] = red[0];
+// Digit of pass p: bits [lo, hi) counted from the top of an nb-bit key.
+struct Digit {
+  int lo, hi;
+  uint64_t himask;      // bits at or above hi
+};
+__host__ __device__ __forceinline__ Digit digit_of(int pass, int nb) {
+  Digit d;
+  d.hi = nb - kDigitBits * pass;
+  d.lo = d.hi - kDigitBits > 0 ? d.hi - kDigitBits : 0;
+  d.himask = (d.hi >= 64) ? 0ull : (~0ull << d.hi);
+  return d;
 }
+__host__ __device__ __forceinline__ int passes_of(int nb) { return (nb + kDigitBits - 1) / kDigitBits; }
 
-// Zero the histograms and set B.  stage: 0 V, 1 K, 2 top-k.
-__global__ void __launch_bounds__(256)
-alloc_init(SelState* st, int64_t* hist, int64_t hist_len, int stage, int nseg, int Hkv, int d,
-           int64_t N, const int64_t* rcount, double avg, double keep_fraction) {
-  for (int64_t i = threadIdx.x; i < hist_len; i += 256) hist[i] = 0;
-  if (threadIdx.x == 0) {
-    for (int sgi = 0; sgi < nseg; ++sgi) {
-      SelState s;
-      s.prefix = 0;
-      s.all_fit = 0;
-      s.none = 0;
-      s.pad[0] = s.pad[1] = 0;
-      if (stage == 0) {
-        s.elements = (int64_t)Hkv * N * d;
-        s.budget = (int64_t)floor(avg * (double)s.elements);
-        s.brem = s.budget;
-      } else if (stage == 1) {
-        int64_t r = 0;
-        for (int g = 0; g < Hkv; ++g) r += rcount[g];
-        s.elements = (int64_t)d * r;
-        s.budget = (int64_t)floor(avg * (double)s.elements);
-        s.brem = s.budget;
-      } else {
-        int64_t kk = (int64_t)floor(keep_fraction * (double)N);
-        s.elements = kk;
-        s.budget = kk - 1;       // select the kk-th largest: count above <= kk-1 < count at-or-above
-        s.brem = kk - 1;
-        s.none = (kk == 0);
-      }
-      st[sgi] = s;
-    }
-  }
-}
-
-__device__ __forceinline__ int64_t unit_size(int stage, int d, int64_t u, const int64_t* rcount) {
-  return stage == 0 ? (int64_t)d : rcount[u / d];
-}
-
-// Keys of the four steps of every unit (0 when the unit can never be granted bits).
-__global__ void __launch_bounds__(256)
-alloc_keys(const float* __restrict__ weight, const float* __restrict__ sigma, int64_t U, int stage,
-           int d, const int64_t* __restrict__ rcount, uint64_t* __restrict__ keys) {
-  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (u >= U) return;
-  float c = weight[u];
-  if (sigma) c = c * sigma[u];          // one float32 rounding of w * sigma
-  const int64_t s = unit_size(stage, d, u, rcount);
-  uint64_t kk[4] = {0, 0, 0, 0};
-  if (c > 0.f && s > 0) {
-    const double cd = (double)c;
-    const double sd = (double)s;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      double key = (cd * (double)kThetaNum[k]) / (sd * (double)kThetaDen[k]);
-      kk[k] = __double_as_longlong(key);
-    }
-  }
-  uint4* o = reinterpret_cast<uint4*>(keys + u * 4);
-  o[0] = make_uint4((uint32_t)kk[0], (uint32_t)(kk[0] >> 32), (uint32_t)kk[1], (uint32_t)(kk[1] >> 32));
-  o[1] = make_uint4((uint32_t)kk[2], (uint32_t)(kk[2] >> 32), (uint32_t)kk[3], (uint32_t)(kk[3] >> 32));
-}
-
-// Order-preserving 32-bit key of a float score (larger score -> larger key).
 __device__ __forceinline__ uint32_t score_key(float f) {
-  uint32_t b = __float_as_uint(f);
+  const uint32_t b = __float_as_uint(f);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// ---- weighted radix select ---------------------------------------------------------------
+__device__ __forceinline__ void unit_keys(float c, int64_t s, uint64_t (&kk)[4]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) kk[k] = 0;
+  if (c > 0.f && s > 0) {
+    const double cd = (double)c, sd = (double)s;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      kk[k] = (uint64_t)__double_as_longlong((cd * (double)kThetaNum[k]) / (sd * (double)kThetaDen[k]));
+  }
+}
 
-// One pass of the MSB-first select.  V/K: 64-bit keys, 4 per unit, weight = step rate; top-k:
-// 32-bit score keys, 1 per token, weight 1, one segment per KV head (grid.y).
+__device__ __forceinline__ int64_t step_rate(int64_t s, int k) {
+  return s * (int64_t)(kLevels[k + 1] - kLevels[k]);
+}
+
+// Steps with key > lam (all positive keys when everything fits) and the rate of the step
+// tied at lam (0 if none).
+__device__ __forceinline__ int64_t steps_and_tie(const uint64_t (&kk)[4], int64_t s, uint64_t lam,
+                                                 bool all_fit, int* n) {
+  int c = 0;
+  int64_t tie = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (kk[k] == 0) continue;
+    if (all_fit || kk[k] > lam) ++c;
+    else if (kk[k] == lam) tie = step_rate(s, k);
+  }
+  *n = c;
+  return all_fit ? 0 : tie;
+}
+
+// Block-wide inclusive scan (wave shuffles, then wave totals through LDS; integer: exact).
+// Every thread of the block calls it.  wave_tot holds >= blockDim.x / 64 entries.
+__device__ __forceinline__ int64_t block_scan_incl(int64_t v, int64_t* wave_tot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  if (lane == 63) wave_tot[wave] = v;
+  __syncthreads();
+  int64_t off = 0;
+  for (int w = 0; w < wave; ++w) off += wave_tot[w];
+  __syncthreads();
+  return v + off;
+}
+
+// Choose this pass's digit of one segment from its kBins-bin histogram.  NT threads (the
+// whole block; it holds barriers), each owning kBins/NT consecutive bins in descending digit
+// order.
+template <int NT>
+__device__ void select_digit(SelState* st, const int64_t* hist, const uint64_t* hmin,
+                             const uint64_t* hmax, int pass, int nb, int64_t* wave_tot) {
+  const SelState s = *st;
+  constexpr int PER = kBins / NT;
+  const int i = threadIdx.x;
+  int64_t hv[PER];
+  int64_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    hv[j] = hist[kBins - 1 - (PER * i + j)];
+    mine += hv[j];
+  }
+  const int64_t incl_t = block_scan_incl(mine, wave_tot);
+  if (s.done || s.none) return;               // uniform
+  int64_t run = incl_t - mine;                 // cumulative weight of higher digits
+  const bool last = (i == NT - 1);
+  if (pass == 0 && last && incl_t <= s.brem) {
+    st->all_fit = 1;                           // every positive step fits: lambda* = 0
+    st->done = 1;
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int64_t excl = run;
+    run += hv[j];
+    if (excl <= s.brem && run > s.brem) {      // exactly one bin overall
+      const int digit = kBins - 1 - (PER * i + j);
+      const Digit dg = digit_of(pass, nb);
+      const uint64_t mn = hmin[digit], mx = hmax[digit];
+      SelState n = s;
+      n.brem = s.brem - excl;
+      n.prefix = s.prefix | ((uint64_t)digit << dg.lo);
+      if (mn == mx) {          // a single key value left in the bin: it is lambda*
+        n.prefix = mn;
+        n.done = 1;
+      } else if (dg.lo == 0) {
+        n.done = 1;
+      }
+      *st = n;
+    }
+  }
+}
+
+// ======================= single-block path (V/K stages, <= 2048 units) ===================
+__global__ void __launch_bounds__(1024)
+alloc_small(const float* __restrict__ weight, const float* __restrict__ sigma,
+            const uint8_t* __restrict__ bits_v, int stage, int Hkv, int64_t N, int d, double avg,
+            uint8_t* __restrict__ bits_out, kvc_alloc_result* result, int32_t* status) {
+  __shared__ uint64_t keys[kSmallUnits * 4];
+  __shared__ int64_t hist[kBins];
+  __shared__ uint64_t hmin[kBins], hmax[kBins];
+  __shared__ int64_t wave_tot[16];
+  __shared__ int32_t rc[256];
+  __shared__ SelState st;
+  __shared__ int32_t bad;
+  __shared__ double dbuf[16];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int U = (stage == KVC_ALLOC_V_TOKENS) ? (int)(Hkv * N) : Hkv * d;
+  if (tid == 0) bad = 0;
+  for (int g = tid; g < Hkv; g += 1024) rc[g] = 0;
+  __syncthreads();
+  if (stage == KVC_ALLOC_K_CHANNELS) {        // R_g from bits_v: per-thread counts, LDS sums
+    bool b_bad = false;
+    for (int g = 0; g < Hkv; ++g) {
+      int cnt = 0;
+      for (int64_t t = tid * 4; t < N; t += 4096) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (t + j < N) {
+            const uint32_t b = bits_v[(int64_t)g * N + t + j];
+            cnt += (b > 0);
+            b_bad |= !valid_width(b);
+          }
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+      if (lane == 0 && cnt) atomicAdd(&rc[g], cnt);
+    }
+    if (b_bad) bad = 1;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int64_t E;
+    if (stage == KVC_ALLOC_V_TOKENS) {
+      E = (int64_t)Hkv * N * d;
+    } else {
+      int64_t r = 0;
+      for (int g = 0; g < Hkv; ++g) r += rc[g];
+      E = (int64_t)d * r;
+    }
+    st.prefix = 0;
+    st.budget = (int64_t)floor(avg * (double)E);
+    st.brem = st.budget;
+    st.all_fit = 0;
+    st.none = 0;
+    st.done = 0;
+    st.pad = 0;
+    *status = bad ? KVC_DEV_BAD_WIDTH : 0;
+  }
+  for (int u = tid; u < U; u += 1024) {
+    float c = weight[u];
+    if (sigma) c = c * sigma[u];
+    const int64_t s = (stage == KVC_ALLOC_V_TOKENS) ? (int64_t)d : (int64_t)rc[u / d];
+    uint64_t kk[4];
+    unit_keys(c, s, kk);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) keys[u * 4 + k] = kk[k];
+  }
+  const int npass = passes_of(64);
+  for (int pass = 0; pass < npass; ++pass) {
+    __syncthreads();
+    if (st.done) break;                         // uniform: read after a barrier
+    for (int b = tid; b < kBins; b += 1024) {
+      hist[b] = 0;
+      hmin[b] = ~0ull;
+      hmax[b] = 0;
+    }
+    __syncthreads();
+    const Digit dg = digit_of(pass, 64);
+    const uint64_t pre = st.prefix & dg.himask;
+    const uint64_t dmask = (1ull << (dg.hi - dg.lo)) - 1;
+    for (int e = tid; e < U * 4; e += 1024) {
+      const uint64_t key = keys[e];
+      if (key != 0 && (key & dg.himask) == pre) {
+        const int u = e >> 2, k = e & 3;
+        const int64_t s = (stage == KVC_ALLOC_V_TOKENS) ? (int64_t)d : (int64_t)rc[u / d];
+        const int b = (int)((key >> dg.lo) & dmask);
+        atomicAdd((unsigned long long*)&hist[b], (unsigned long long)step_rate(s, k));
+        atomicMin((unsigned long long*)&hmin[b], (unsigned long long)key);
+        atomicMax((unsigned long long*)&hmax[b], (unsigned long long)key);
+      }
+    }
+    __syncthreads();
+    select_digit<1024>(&st, hist, hmin, hmax, pass, 64, wave_tot);
+  }
+  __syncthreads();
+  const SelState S = st;
+  const uint64_t lam = S.all_fit ? 0ull : S.prefix;
+  // ordered tie scan: thread i owns units [2i, 2i + 2)
+  int64_t tie[2] = {0, 0};
+  int n[2] = {0, 0};
+  int64_t tsum = 0;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int u = 2 * tid + j;
+    if (u < U) {
+      uint64_t kk[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) kk[k] = keys[u * 4 + k];
+      const int64_t s = (stage == KVC_ALLOC_V_TOKENS) ? (int64_t)d : (int64_t)rc[u / d];
+      tie[j] = steps_and_tie(kk, s, lam, S.all_fit != 0, &n[j]);
+      tsum += tie[j];
+    }
+  }
+  const int64_t incl = block_scan_incl(tsum, wave_tot);
+  int64_t run = incl - tsum;
+  int64_t used = 0;
+  double dist = 0.0;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int u = 2 * tid + j;
+    if (u >= U) continue;
+    int nn = n[j];
+    if (tie[j] > 0) {
+      run += tie[j];
+      if (run <= S.brem) nn += 1;
+    }
+    const uint32_t b = kLevels[nn];
+    bits_out[u] = (uint8_t)b;
+    const int64_t s = (stage == KVC_ALLOC_V_TOKENS) ? (int64_t)d : (int64_t)rc[u / d];
+    used += s * (int64_t)b;
+    float c = weight[u];
+    if (sigma) c = c * sigma[u];
+    dist += ldexp((double)c, -(int)b);
+  }
+  const int64_t used_tot = block_scan_incl(used, wave_tot);
+  // distortion: fixed-order tree within each wave, then the 16 wave sums in order
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const double t = __shfl_down(dist, o, 64);
+    if (lane < o) dist += t;
+  }
+  if (lane == 0) dbuf[wave] = dist;
+  __syncthreads();
+  if (tid == 1023 && result) {
+    double dt = 0.0;
+    for (int w = 0; w < 16; ++w) dt += dbuf[w];
+    kvc_alloc_result r;
+    r.lambda = S.all_fit ? 0.0 : __longlong_as_double((long long)S.prefix);
+    r.budget_bits = S.budget;
+    r.used_bits = used_tot;
+    r.distortion = dt;
+    *result = r;
+  }
+}
+
+// ======================= multi-block path =================================================
+
+// Count R_g (K stage), set the budgets, clear the first pass's histogram.  One block.
+__global__ void __launch_bounds__(1024)
+alloc_begin(AllocWs a, int stage, int nseg, int Hkv, int64_t N, int d,
+            const uint8_t* __restrict__ bits_v, double avg, double keep_fraction) {
+  __shared__ int64_t rsum;
+  __shared__ int32_t bad;
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid == 0) {
+    rsum = 0;
+    bad = 0;
+  }
+  for (int64_t i = tid; i < (int64_t)nseg * kBins; i += 1024) {
+    a.hist[i] = 0;
+    a.hmin[i] = ~0ull;
+    a.hmax[i] = 0;
+  }
+  __syncthreads();
+  if (stage == KVC_ALLOC_K_CHANNELS) {
+    bool b_bad = false;
+    for (int g = 0; g < Hkv; ++g) {
+      unsigned long long cnt = 0;
+      for (int64_t t = tid; t < N; t += 1024) {
+        const uint32_t b = bits_v[(int64_t)g * N + t];
+        cnt += (b > 0);
+        b_bad |= !valid_width(b);
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+      if (lane == 0 && cnt) atomicAdd((unsigned long long*)&a.rcount[g], cnt);
+    }
+    if (b_bad) bad = 1;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    *a.status = bad ? KVC_DEV_BAD_WIDTH : 0;
+    if (stage == KVC_ALLOC_K_CHANNELS)
+      for (int g = 0; g < Hkv; ++g) rsum += a.rcount[g];
+  }
+  __syncthreads();
+  for (int sgi = tid; sgi < nseg; sgi += 1024) {
+    SelState s;
+    s.prefix = 0;
+    s.all_fit = 0;
+    s.none = 0;
+    s.done = 0;
+    s.pad = 0;
+    if (stage == KVC_ALLOC_TOPK) {
+      const int64_t kk = (int64_t)floor(keep_fraction * (double)N);
+      s.budget = kk;
+      s.brem = kk - 1;           // the kk-th largest: count above <= kk-1 < count at-or-above
+      s.none = (kk == 0);
+    } else {
+      const int64_t E = (stage == KVC_ALLOC_V_TOKENS) ? (int64_t)Hkv * N * d : (int64_t)d * rsum;
+      s.budget = (int64_t)floor(avg * (double)E);
+      s.brem = s.budget;
+    }
+    a.st[sgi] = s;
+  }
+}
+
+__global__ void zero_counts(int64_t* rcount, int Hkv) {
+  if ((int)threadIdx.x < Hkv) rcount[threadIdx.x] = 0;
+}
+
+__device__ __forceinline__ int64_t unit_size(int stage, int d, int64_t u, const int64_t* rcount) {
+  return stage == KVC_ALLOC_V_TOKENS ? (int64_t)d : rcount[u / d];
+}
+
+__device__ __forceinline__ void load_keys(const uint64_t* keys, int64_t u, uint64_t (&kk)[4]) {
+  const uint4* kp = reinterpret_cast<const uint4*>(keys + u * 4);
+  const uint4 x = kp[0], y = kp[1];
+  kk[0] = (uint64_t)x.x | ((uint64_t)x.y << 32);
+  kk[1] = (uint64_t)x.z | ((uint64_t)x.w << 32);
+  kk[2] = (uint64_t)y.x | ((uint64_t)y.y << 32);
+  kk[3] = (uint64_t)y.z | ((uint64_t)y.w << 32);
+}
+
+// Histogram of one pass.  V/K: keys computed on pass 0 (and stored), 4 per unit, weight =
+// step rate.  Top-k: 32-bit score keys, 1 per token, weight 1, one segment per KV head.
 template <bool TOPK>
 __global__ void __launch_bounds__(256)
-alloc_hist(const uint64_t* __restrict__ keys, const float* __restrict__ scores, int64_t U,
-           int64_t seg_len, int stage, int d, const int64_t* __restrict__ rcount,
-           const SelState* __restrict__ st, int64_t* __restrict__ hist, int pass, int nbytes) {
+alloc_hist(AllocWs a, const float* __restrict__ weight, const float* __restrict__ sigma,
+           int64_t seg_len, int stage, int d, int pass, int nb) {
+  __shared__ int64_t h[kBins];
+  __shared__ uint64_t hmn[kBins], hmx[kBins];
   const int seg = blockIdx.y;
-  const SelState s = st[seg];
-  if (s.all_fit || s.none) return;
-  __shared__ int64_t h[256];
-  h[threadIdx.x] = 0;
+  const SelState s = a.st[seg];
+  const bool active = !(s.done || s.none);
+  const bool make_keys = !TOPK && pass == 0;
+  if (!active && !make_keys) return;           // uniform for the block
+  for (int b = threadIdx.x; b < kBins; b += 256) {
+    h[b] = 0;
+    hmn[b] = ~0ull;
+    hmx[b] = 0;
+  }
   __syncthreads();
-  const int shift = 8 * (nbytes - 1 - pass);
-  const uint64_t himask = (pass == 0) ? 0ull : (~0ull << (shift + 8));
+  const Digit dg = digit_of(pass, nb);
+  const uint64_t pre = s.prefix & dg.himask;
+  const uint64_t dmask = (1ull << (dg.hi - dg.lo)) - 1;
   const int64_t base = (int64_t)blockIdx.x * kUnitsPerBlock;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int64_t ul = base + threadIdx.x + j * 256;
+    if (ul >= seg_len) continue;
     if (TOPK) {
-      if (ul < seg_len) {
-        uint64_t key = score_key(scores[(int64_t)seg * seg_len + ul]);
-        if ((key & himask) == (s.prefix & himask)) atomicAdd((unsigned long long*)&h[(key >> shift) & 255], 1ull);
+      const uint64_t key = score_key(weight[(int64_t)seg * seg_len + ul]);
+      if ((key & dg.himask) == pre) {
+        const int b = (int)((key >> dg.lo) & dmask);
+        atomicAdd((unsigned long long*)&h[b], 1ull);
+        atomicMin((unsigned long long*)&hmn[b], (unsigned long long)key);
+        atomicMax((unsigned long long*)&hmx[b], (unsigned long long)key);
       }
     } else {
-      if (ul < U) {
-        const int64_t sz = unit_size(stage, d, ul, rcount);
-        const uint4* kp = reinterpret_cast<const uint4*>(keys + ul * 4);
-        uint4 a = kp[0], b = kp[1];
-        uint64_t kk[4] = {(uint64_t)a.x | ((uint64_t)a.y << 32), (uint64_t)a.z | ((uint64_t)a.w << 32),
-                          (uint64_t)b.x | ((uint64_t)b.y << 32), (uint64_t)b.z | ((uint64_t)b.w << 32)};
+      const int64_t sz = unit_size(stage, d, ul, a.rcount);
+      uint64_t kk[4];
+      if (make_keys) {
+        float c = weight[ul];
+        if (sigma) c = c * sigma[ul];
+        unit_keys(c, sz, kk);
+        uint4* o = reinterpret_cast<uint4*>(a.keys + ul * 4);
+        o[0] = make_uint4((uint32_t)kk[0], (uint32_t)(kk[0] >> 32), (uint32_t)kk[1], (uint32_t)(kk[1] >> 32));
+        o[1] = make_uint4((uint32_t)kk[2], (uint32_t)(kk[2] >> 32), (uint32_t)kk[3], (uint32_t)(kk[3] >> 32));
+      } else {
+        load_keys(a.keys, ul, kk);
+      }
+      if (active) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          if (kk[k] != 0 && (kk[k] & himask) == (s.prefix & himask)) {
-            int64_t w = sz * (int64_t)(kLevels[k + 1] - kLevels[k]);
-            atomicAdd((unsigned long long*)&h[(kk[k] >> shift) & 255], (unsigned long long)w);
+          if (kk[k] != 0 && (kk[k] & dg.himask) == pre) {
+            const int b = (int)((kk[k] >> dg.lo) & dmask);
+            atomicAdd((unsigned long long*)&h[b], (unsigned long long)step_rate(sz, k));
+            atomicMin((unsigned long long*)&hmn[b], (unsigned long long)kk[k]);
+            atomicMax((unsigned long long*)&hmx[b], (unsigned long long)kk[k]);
           }
         }
       }
     }
   }
   __syncthreads();
-  int64_t v = h[threadIdx.x];
-  if (v) atomicAdd((unsigned long long*)&hist[((int64_t)pass * gridDim.y + seg) * 256 + threadIdx.x], (unsigned long long)v);
-}
-
-// Choose this pass's digit: scanning digits from high to low, the first whose inclusive
-// cumulative weight exceeds the remaining budget.  One block per segment.
-__global__ void __launch_bounds__(256)
-alloc_select(SelState* st, const int64_t* __restrict__ hist, int pass, int nbytes, int nseg) {
-  const int seg = blockIdx.x;
-  SelState s = st[seg];
-  if (s.all_fit || s.none) return;
-  const int i = threadIdx.x;                  // position in descending digit order
-  const int digit = 255 - i;
-  const int64_t hv = hist[((int64_t)pass * nseg + seg) * 256 + digit];
-  __shared__ int64_t cum[256];
-  cum[i] = hv;
-  __syncthreads();
-  for (int w = 1; w < 256; w <<= 1) {          // inclusive scan (Hillis-Steele)
-    int64_t add = (i >= w) ? cum[i - w] : 0;
-    __syncthreads();
-    cum[i] += add;
-    __syncthreads();
-  }
-  const int64_t incl = cum[i];
-  const int64_t excl = incl - hv;
-  if (pass == 0 && i == 255 && incl <= s.brem) {
-    st[seg].all_fit = 1;                      // every positive step fits
-    return;
-  }
-  if (excl <= s.brem && incl > s.brem) {      // exactly one thread
-    const int shift = 8 * (nbytes - 1 - pass);
-    st[seg].prefix = s.prefix | ((uint64_t)digit << shift);
-    st[seg].brem = s.brem - excl;
-  }
-}
-
-// ---- ordered tie scan and assignment ----------------------------------------------------
-
-__device__ __forceinline__ int64_t tie_rate_of_unit(const uint64_t* keys, int64_t u, int64_t sz,
-                                                    uint64_t lam, int* nsteps) {
-  const uint4* kp = reinterpret_cast<const uint4*>(keys + u * 4);
-  uint4 a = kp[0], b = kp[1];
-  uint64_t kk[4] = {(uint64_t)a.x | ((uint64_t)a.y << 32), (uint64_t)a.z | ((uint64_t)a.w << 32),
-                    (uint64_t)b.x | ((uint64_t)b.y << 32), (uint64_t)b.z | ((uint64_t)b.w << 32)};
-  int n = 0;
-  int64_t tie = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    if (kk[k] != 0) {
-      if (kk[k] > lam) ++n;
-      else if (kk[k] == lam) tie = sz * (int64_t)(kLevels[k + 1] - kLevels[k]);
+  if (!active) return;
+  for (int b = threadIdx.x; b < kBins; b += 256) {
+    if (h[b]) {
+      const int64_t gi = (int64_t)seg * kBins + b;
+      atomicAdd((unsigned long long*)&a.hist[gi], (unsigned long long)h[b]);
+      atomicMin((unsigned long long*)&a.hmin[gi], (unsigned long long)hmn[b]);
+      atomicMax((unsigned long long*)&a.hmax[gi], (unsigned long long)hmx[b]);
     }
   }
-  *nsteps = n;
-  return tie;
+}
+
+// Digit choice of one pass (one block per segment), then clear the histogram for the next.
+__global__ void __launch_bounds__(256)
+alloc_select(AllocWs a, int pass, int nb) {
+  __shared__ int64_t wave_tot[4];
+  const int seg = blockIdx.x;
+  SelState* st = &a.st[seg];
+  if (st->done || st->none) return;            // uniform
+  int64_t* hist = a.hist + (int64_t)seg * kBins;
+  uint64_t* hmin = a.hmin + (int64_t)seg * kBins;
+  uint64_t* hmax = a.hmax + (int64_t)seg * kBins;
+  select_digit<256>(st, hist, hmin, hmax, pass, nb, wave_tot);
+  __syncthreads();
+  for (int b = threadIdx.x; b < kBins; b += 256) {
+    hist[b] = 0;
+    hmin[b] = ~0ull;
+    hmax[b] = 0;
+  }
 }
 
 template <bool TOPK>
-__device__ __forceinline__ int64_t unit_tie(const uint64_t* keys, const float* scores, int64_t u,
+__device__ __forceinline__ int64_t unit_tie(const AllocWs& a, const float* weight, int64_t u,
                                             int64_t seg, int64_t seg_len, int stage, int d,
-                                            const int64_t* rcount, const SelState& s, int* n) {
+                                            const SelState& s, int* n) {
+  if (u >= seg_len) {
+    *n = 0;
+    return 0;
+  }
   if (TOPK) {
-    if (u >= seg_len || s.none) { *n = 0; return 0; }
-    uint64_t key = score_key(scores[seg * seg_len + u]);
-    *n = key > s.prefix ? 1 : 0;
-    return key == s.prefix ? 1 : 0;
-  } else {
-    if (u >= seg_len) { *n = 0; return 0; }
-    if (s.all_fit) {
-      int nn = 0;
-      tie_rate_of_unit(keys, u, unit_size(stage, d, u, rcount), 0ull, &nn);
-      *n = nn;
+    if (s.none) {
+      *n = 0;
       return 0;
     }
-    return tie_rate_of_unit(keys, u, unit_size(stage, d, u, rcount), s.prefix, n);
+    const uint64_t key = score_key(weight[seg * seg_len + u]);
+    *n = key > s.prefix ? 1 : 0;
+    return key == s.prefix ? 1 : 0;
   }
+  uint64_t kk[4];
+  load_keys(a.keys, u, kk);
+  return steps_and_tie(kk, unit_size(stage, d, u, a.rcount), s.prefix, s.all_fit != 0, n);
 }
 
-// Block sums of the tie rates (4 units per thread, units in index order).
+// Block sums of the tie rates (units in index order, 4 per thread).
 template <bool TOPK>
 __global__ void __launch_bounds__(256)
-alloc_tie_sum(const uint64_t* __restrict__ keys, const float* __restrict__ scores, int64_t seg_len,
-              int stage, int d, const int64_t* __restrict__ rcount, const SelState* __restrict__ st,
-              int64_t* __restrict__ bsum) {
+alloc_ties(AllocWs a, const float* __restrict__ weight, int64_t seg_len, int stage, int d) {
+  __shared__ int64_t wave_tot[4];
   const int seg = blockIdx.y;
-  const SelState s = st[seg];
+  const SelState s = a.st[seg];
   const int64_t base = (int64_t)blockIdx.x * kUnitsPerBlock + threadIdx.x * 4;
   int64_t t = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     int n;
-    t += unit_tie<TOPK>(keys, scores, base + j, seg, seg_len, stage, d, rcount, s, &n);
+    t += unit_tie<TOPK>(a, weight, base + j, seg, seg_len, stage, d, s, &n);
   }
-  __shared__ int64_t red[256];
-  red[threadIdx.x] = t;
-  __syncthreads();
-  for (int w = 128; w >= 1; w >>= 1) {
-    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) bsum[(int64_t)seg * gridDim.x + blockIdx.x] = red[0];
+  const int64_t tot = block_scan_incl(t, wave_tot);
+  if (threadIdx.x == 255) a.bsum[(int64_t)seg * gridDim.x + blockIdx.x] = tot;
 }
 
-// Exclusive scan of the block sums of each segment (one block per segment).
-__global__ void __launch_bounds__(1024)
-alloc_tie_scan(const int64_t* __restrict__ bsum, int64_t* __restrict__ bexcl, int nblk) {
+// Exclusive scan of the block sums of each segment, in block order (one block per segment).
+__global__ void __launch_bounds__(256)
+alloc_tie_scan(AllocWs a, int nblk) {
+  __shared__ int64_t wave_tot[4];
+  __shared__ int64_t blk_total;
   const int seg = blockIdx.x;
-  __shared__ int64_t buf[1024];
   int64_t carry = 0;
-  for (int b0 = 0; b0 < nblk; b0 += 1024) {
-    const int i = threadIdx.x;
-    int64_t v = (b0 + i < nblk) ? bsum[(int64_t)seg * nblk + b0 + i] : 0;
-    buf[i] = v;
+  for (int b0 = 0; b0 < nblk; b0 += 256) {
+    const int b = b0 + threadIdx.x;
+    const int64_t v = (b < nblk) ? a.bsum[(int64_t)seg * nblk + b] : 0;
+    const int64_t incl = block_scan_incl(v, wave_tot);
+    if (b < nblk) a.bexcl[(int64_t)seg * nblk + b] = carry + incl - v;
+    if (threadIdx.x == 255) blk_total = incl;
     __syncthreads();
-    for (int w = 1; w < 1024; w <<= 1) {
-      int64_t add = (i >= w) ? buf[i - w] : 0;
-      __syncthreads();
-      buf[i] += add;
-      __syncthreads();
-    }
-    if (b0 + i < nblk) bexcl[(int64_t)seg * nblk + b0 + i] = carry + buf[i] - v;
-    int64_t tot = buf[1023];
+    carry += blk_total;
     __syncthreads();
-    carry += tot;
   }
 }
 
-// Final widths: steps with key > lambda*, plus the tied step when the inclusive prefix of tie
-// rates (ascending unit index) still fits the remaining budget.  Also per-block partial sums
-// of the used rate and the distortion, reduced later in a fixed order.
+// Final widths: steps with key > lambda*, plus the tied step while the inclusive prefix of tie
+// rates fits the remaining budget; per-block used rate and distortion.
 template <bool TOPK>
 __global__ void __launch_bounds__(256)
-alloc_assign(const uint64_t* __restrict__ keys, const float* __restrict__ weight,
-             const float* __restrict__ sigma, int64_t seg_len, int stage, int d,
-             const int64_t* __restrict__ rcount, const SelState* __restrict__ st,
-             const int64_t* __restrict__ bexcl, uint8_t* __restrict__ bits_out, int keep_bits,
-             int64_t* __restrict__ used_part, double* __restrict__ dist_part) {
+alloc_assign(AllocWs a, const float* __restrict__ weight, const float* __restrict__ sigma,
+             int64_t seg_len, int stage, int d, int keep_bits, uint8_t* __restrict__ bits_out) {
+  __shared__ int64_t wave_tot[4];
+  __shared__ double dbuf[4];
   const int seg = blockIdx.y;
-  const SelState s = st[seg];
+  const SelState s = a.st[seg];
   const int64_t base = (int64_t)blockIdx.x * kUnitsPerBlock + threadIdx.x * 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int64_t tie[4];
   int n[4];
   int64_t tsum = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    tie[j] = unit_tie<TOPK>(keys, weight, base + j, seg, seg_len, stage, d, rcount, s, &n[j]);
+    tie[j] = unit_tie<TOPK>(a, weight, base + j, seg, seg_len, stage, d, s, &n[j]);
     tsum += tie[j];
   }
-  __shared__ int64_t buf[256];
-  const int i = threadIdx.x;
-  buf[i] = tsum;
-  __syncthreads();
-  for (int w = 1; w < 256; w <<= 1) {
-    int64_t add = (i >= w) ? buf[i - w] : 0;
-    __syncthreads();
-    buf[i] += add;
-    __syncthreads();
-  }
-  int64_t run = bexcl[(int64_t)seg * gridDim.x + blockIdx.x] + buf[i] - tsum;
+  const int64_t incl = block_scan_incl(tsum, wave_tot);
+  int64_t run = a.bexcl[(int64_t)seg * gridDim.x + blockIdx.x] + incl - tsum;
   const int64_t cap = TOPK ? s.brem + 1 : s.brem;
   int64_t used = 0;
   double dist = 0.0;
@@ -360,66 +596,60 @@ alloc_assign(const uint64_t* __restrict__ keys, const float* __restrict__ weight
       run += tie[j];
       if (run <= cap) nn += 1;
     }
-    uint32_t b = TOPK ? (nn ? (uint32_t)keep_bits : 0u) : kLevels[nn];
+    const uint32_t b = TOPK ? (nn ? (uint32_t)keep_bits : 0u) : kLevels[nn];
     bits_out[(int64_t)seg * seg_len + u] = (uint8_t)b;
-    if (!TOPK) {
-      const int64_t sz = unit_size(stage, d, u, rcount);
-      used += sz * (int64_t)b;
+    if (TOPK) {
+      used += (int64_t)b * d;
+    } else {
+      used += unit_size(stage, d, u, a.rcount) * (int64_t)b;
       float c = weight[u];
       if (sigma) c = c * sigma[u];
       dist += ldexp((double)c, -(int)b);
-    } else {
-      used += (int64_t)b * d;
     }
   }
-  __shared__ int64_t ru[256];
-  __shared__ double rd[256];
-  ru[i] = used;
-  rd[i] = dist;
+  const int64_t used_blk = block_scan_incl(used, wave_tot);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const double t = __shfl_down(dist, o, 64);
+    if (lane < o) dist += t;
+  }
+  if (lane == 0) dbuf[wave] = dist;
   __syncthreads();
-  for (int w = 128; w >= 1; w >>= 1) {
-    if (i < w) {
-      ru[i] += ru[i + w];
-      rd[i] += rd[i + w];
-    }
-    __syncthreads();
-  }
-  if (i == 0) {
-    used_part[(int64_t)seg * gridDim.x + blockIdx.x] = ru[0];
-    dist_part[(int64_t)seg * gridDim.x + blockIdx.x] = rd[0];
+  if (threadIdx.x == 255) {
+    a.used_part[(int64_t)seg * gridDim.x + blockIdx.x] = used_blk;
+    a.dist_part[(int64_t)seg * gridDim.x + blockIdx.x] = (dbuf[0] + dbuf[1]) + (dbuf[2] + dbuf[3]);
   }
 }
 
-__global__ void alloc_finalize(const SelState* __restrict__ st, const int64_t* __restrict__ used_part,
-                               const double* __restrict__ dist_part, int nseg, int nblk, int topk,
-                               kvc_alloc_result* result) {
-  if (threadIdx.x != 0 || blockIdx.x != 0 || result == nullptr) return;
-  int64_t used = 0;
-  double dist = 0.0;
-  for (int sgi = 0; sgi < nseg; ++sgi)
-    for (int b = 0; b < nblk; ++b) {
-      used += used_part[(int64_t)sgi * nblk + b];
-      dist += dist_part[(int64_t)sgi * nblk + b];
-    }
+// Sum the per-block used rate and distortion in block order and write the result.
+__global__ void alloc_finalize(const AllocWs a, int nparts, int topk, kvc_alloc_result* result) {
+  if (threadIdx.x != 0 || result == nullptr) return;
+  int64_t ut = 0;
+  double dt = 0.0;
+  for (int i = 0; i < nparts; ++i) {
+    ut += a.used_part[i];
+    dt += a.dist_part[i];
+  }
   kvc_alloc_result r;
   if (topk) {
     r.lambda = 0.0;
-    r.budget_bits = used;
-    r.used_bits = used;
+    r.budget_bits = ut;
+    r.used_bits = ut;
     r.distortion = 0.0;
   } else {
-    const SelState s = st[0];
-    r.lambda = s.all_fit ? 0.0 : __longlong_as_double((long long)s.prefix);
-    r.budget_bits = s.budget;
-    r.used_bits = used;
-    r.distortion = dist;
+    const SelState s0 = a.st[0];
+    r.lambda = s0.all_fit ? 0.0 : __longlong_as_double((long long)s0.prefix);
+    r.budget_bits = s0.budget;
+    r.used_bits = ut;
+    r.distortion = dt;
   }
   *result = r;
 }
 
 struct Plan {
-  int nseg, nblk, passes, nbytes;
+  int nseg, nblk, nb;
   int64_t U, seg_len;
+  bool small;
 };
 
 Plan plan_of(const Layer& L, int stage) {
@@ -428,35 +658,40 @@ Plan plan_of(const Layer& L, int stage) {
     p.nseg = L.hkv;
     p.seg_len = L.n;
     p.U = L.n * L.hkv;
-    p.nbytes = 4;
+    p.nb = 32;
   } else {
     p.nseg = 1;
     p.U = (stage == KVC_ALLOC_V_TOKENS) ? (int64_t)L.hkv * L.n : (int64_t)L.hkv * L.d;
     p.seg_len = p.U;
-    p.nbytes = 8;
+    p.nb = 64;
   }
-  p.passes = p.nbytes;
+  p.small = (stage != KVC_ALLOC_TOPK) && p.U <= kSmallUnits;
   p.nblk = (int)((p.seg_len + kUnitsPerBlock - 1) / kUnitsPerBlock);
   return p;
 }
 
 AllocWs carve(const Layer& L, int stage, char* ws, size_t* total) {
-  Plan p = plan_of(L, stage);
+  const Plan p = plan_of(L, stage);
   WsPlan w;
   AllocWs a{};
-  size_t o_st = w.take(sizeof(SelState) * p.nseg);
-  size_t o_h = w.take(sizeof(int64_t) * p.passes * p.nseg * 256);
-  size_t o_k = w.take(stage == KVC_ALLOC_TOPK ? 0 : sizeof(uint64_t) * 4 * p.U);
-  size_t o_r = w.take(sizeof(int64_t) * L.hkv);
-  size_t o_b = w.take(sizeof(int64_t) * p.nseg * p.nblk);
-  size_t o_e = w.take(sizeof(int64_t) * p.nseg * p.nblk);
-  size_t o_u = w.take(sizeof(int64_t) * p.nseg * p.nblk);
-  size_t o_d = w.take(sizeof(double) * p.nseg * p.nblk);
+  const size_t hn = (size_t)p.nseg * kBins;
+  const size_t o_st = w.take(sizeof(SelState) * p.nseg);
+  const size_t o_h = w.take(sizeof(int64_t) * hn);
+  const size_t o_mn = w.take(sizeof(uint64_t) * hn);
+  const size_t o_mx = w.take(sizeof(uint64_t) * hn);
+  const size_t o_k = w.take(stage == KVC_ALLOC_TOPK ? 0 : sizeof(uint64_t) * 4 * p.U);
+  const size_t o_r = w.take(sizeof(int64_t) * L.hkv);
+  const size_t o_b = w.take(sizeof(int64_t) * p.nseg * p.nblk);
+  const size_t o_e = w.take(sizeof(int64_t) * p.nseg * p.nblk);
+  const size_t o_u = w.take(sizeof(int64_t) * p.nseg * p.nblk);
+  const size_t o_d = w.take(sizeof(double) * p.nseg * p.nblk);
   if (total) *total = w.off;
   if (ws) {
     a.status = reinterpret_cast<int32_t*>(ws);
     a.st = reinterpret_cast<SelState*>(ws + o_st);
     a.hist = reinterpret_cast<int64_t*>(ws + o_h);
+    a.hmin = reinterpret_cast<uint64_t*>(ws + o_mn);
+    a.hmax = reinterpret_cast<uint64_t*>(ws + o_mx);
     a.keys = reinterpret_cast<uint64_t*>(ws + o_k);
     a.rcount = reinterpret_cast<int64_t*>(ws + o_r);
     a.bsum = reinterpret_cast<int64_t*>(ws + o_b);
@@ -482,33 +717,33 @@ hipError_t launch_allocate(const Layer& L, int stage, const float* weight, const
   const Plan p = plan_of(L, stage);
   if (p.nseg > kMaxSeg) return hipErrorInvalidValue;
   AllocWs a = carve(L, stage, ws, nullptr);
+  if (p.small) {
+    alloc_small<<<1, 1024, 0, s>>>(weight, sigma, bits_v, stage, L.hkv, L.n, L.d, avg_bits,
+                                   bits_out, result, a.status);
+    return hipGetLastError();
+  }
   const bool topk = (stage == KVC_ALLOC_TOPK);
-  (void)launch_reset_status(ws, s);
-  if (stage == KVC_ALLOC_K_CHANNELS)
-    count_retained<<<L.hkv, 256, 0, s>>>(bits_v, L.n, a.rcount, a.status);
-  const int64_t hist_len = (int64_t)p.passes * p.nseg * 256;
-  alloc_init<<<1, 256, 0, s>>>(a.st, a.hist, hist_len, stage, p.nseg, L.hkv, L.d, L.n, a.rcount,
-                               avg_bits, keep_fraction);
-  if (!topk)
-    alloc_keys<<<(unsigned)((p.U + 255) / 256), 256, 0, s>>>(weight, sigma, p.U, stage, L.d, a.rcount, a.keys);
-  dim3 g2((unsigned)p.nblk, (unsigned)p.nseg);
-  for (int pass = 0; pass < p.passes; ++pass) {
+  if (stage == KVC_ALLOC_K_CHANNELS) zero_counts<<<1, 256, 0, s>>>(a.rcount, L.hkv);
+  alloc_begin<<<1, 1024, 0, s>>>(a, stage, p.nseg, L.hkv, L.n, L.d, bits_v, avg_bits, keep_fraction);
+  const dim3 g2((unsigned)p.nblk, (unsigned)p.nseg);
+  const int npass = passes_of(p.nb);
+  for (int pass = 0; pass < npass; ++pass) {
     if (topk)
-      alloc_hist<true><<<g2, 256, 0, s>>>(nullptr, weight, p.U, p.seg_len, stage, L.d, a.rcount, a.st, a.hist, pass, p.nbytes);
+      alloc_hist<true><<<g2, 256, 0, s>>>(a, weight, nullptr, p.seg_len, stage, L.d, pass, p.nb);
     else
-      alloc_hist<false><<<g2, 256, 0, s>>>(a.keys, nullptr, p.U, p.seg_len, stage, L.d, a.rcount, a.st, a.hist, pass, p.nbytes);
-    alloc_select<<<p.nseg, 256, 0, s>>>(a.st, a.hist, pass, p.nbytes, p.nseg);
+      alloc_hist<false><<<g2, 256, 0, s>>>(a, weight, sigma, p.seg_len, stage, L.d, pass, p.nb);
+    alloc_select<<<p.nseg, 256, 0, s>>>(a, pass, p.nb);
   }
   if (topk) {
-    alloc_tie_sum<true><<<g2, 256, 0, s>>>(nullptr, weight, p.seg_len, stage, L.d, a.rcount, a.st, a.bsum);
-    alloc_tie_scan<<<p.nseg, 1024, 0, s>>>(a.bsum, a.bexcl, p.nblk);
-    alloc_assign<true><<<g2, 256, 0, s>>>(nullptr, weight, nullptr, p.seg_len, stage, L.d, a.rcount, a.st, a.bexcl, bits_out, keep_bits, a.used_part, a.dist_part);
+    alloc_ties<true><<<g2, 256, 0, s>>>(a, weight, p.seg_len, stage, L.d);
+    alloc_tie_scan<<<p.nseg, 256, 0, s>>>(a, p.nblk);
+    alloc_assign<true><<<g2, 256, 0, s>>>(a, weight, nullptr, p.seg_len, stage, L.d, keep_bits, bits_out);
   } else {
-    alloc_tie_sum<false><<<g2, 256, 0, s>>>(a.keys, nullptr, p.seg_len, stage, L.d, a.rcount, a.st, a.bsum);
-    alloc_tie_scan<<<p.nseg, 1024, 0, s>>>(a.bsum, a.bexcl, p.nblk);
-    alloc_assign<false><<<g2, 256, 0, s>>>(a.keys, weight, sigma, p.seg_len, stage, L.d, a.rcount, a.st, a.bexcl, bits_out, keep_bits, a.used_part, a.dist_part);
+    alloc_ties<false><<<g2, 256, 0, s>>>(a, weight, p.seg_len, stage, L.d);
+    alloc_tie_scan<<<p.nseg, 256, 0, s>>>(a, p.nblk);
+    alloc_assign<false><<<g2, 256, 0, s>>>(a, weight, sigma, p.seg_len, stage, L.d, keep_bits, bits_out);
   }
-  alloc_finalize<<<1, 64, 0, s>>>(a.st, a.used_part, a.dist_part, p.nseg, p.nblk, topk ? 1 : 0, result);
+  alloc_finalize<<<1, 64, 0, s>>>(a, p.nblk * p.nseg, topk ? 1 : 0, result);
   return hipGetLastError();
 }
 

@@ -9,7 +9,7 @@ namespace kvc {
 
 namespace {
 
-constexpr int kRowsPerBlock = 256;
+constexpr int kRowsPerBlock = 512;
 
 // grid: x = row block, y = source (0: the G*Nq stacked query rows of group g, 1: the N keys
 // of head g), z = g.  part[g][src][block][c].
@@ -62,17 +62,32 @@ chanw_partial(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   }
 }
 
-__global__ void chanw_finish(const double* __restrict__ part, float* __restrict__ w_c, int D,
-                             int Hkv, int G, int64_t N, int64_t Nq, int nblk, double scale) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= Hkv * D) return;
-  const int g = idx / D, c = idx % D;
-  const int nbq = (int)(((int64_t)G * Nq + kRowsPerBlock - 1) / kRowsPerBlock);
-  const int nbk = (int)((N + kRowsPerBlock - 1) / kRowsPerBlock);
-  double sq = 0.0, sk = 0.0;
-  for (int b = 0; b < nbq; ++b) sq += part[(((int64_t)g * 2 + 0) * nblk + b) * D + c];
-  for (int b = 0; b < nbk; ++b) sk += part[(((int64_t)g * 2 + 1) * nblk + b) * D + c];
-  w_c[idx] = (float)(scale * sqrt(sq) * sqrt(sk));
+// One block per KV head: thread (src, c) sums its partials in ascending block order.
+__global__ void __launch_bounds__(256)
+chanw_finish(const double* __restrict__ part, float* __restrict__ w_c, int D, int G, int64_t N,
+             int64_t Nq, int nblk, double scale) {
+  __shared__ double sums[2][128];
+  const int g = blockIdx.x;
+  const int src = threadIdx.x / D;
+  const int c = threadIdx.x % D;
+  if (src < 2) {
+    const int64_t rows = src == 0 ? (int64_t)G * Nq : N;
+    const int nb = (int)((rows + kRowsPerBlock - 1) / kRowsPerBlock);
+    const double* p = part + (((int64_t)g * 2 + src) * nblk) * D + c;
+    double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+    int b = 0;
+    for (; b + 4 <= nb; b += 4) {
+      s0 += p[(int64_t)b * D];
+      s1 += p[(int64_t)(b + 1) * D];
+      s2 += p[(int64_t)(b + 2) * D];
+      s3 += p[(int64_t)(b + 3) * D];
+    }
+    for (; b < nb; ++b) s0 += p[(int64_t)b * D];
+    sums[src][c] = (s0 + s1) + (s2 + s3);
+  }
+  __syncthreads();
+  if (threadIdx.x < D)
+    w_c[(int64_t)g * D + threadIdx.x] = (float)(scale * sqrt(sums[0][threadIdx.x]) * sqrt(sums[1][threadIdx.x]));
 }
 
 int nblk_of(const Layer& L) {
@@ -99,8 +114,7 @@ hipError_t launch_channel_weights(const Layer& L, const uint16_t* q, const uint1
     chanw_partial<128><<<grid, 256, 0, s>>>(q, k, part, L.G, L.n, L.nq, nblk);
   else
     chanw_partial<64><<<grid, 256, 0, s>>>(q, k, part, L.G, L.n, L.nq, nblk);
-  int tot = L.hkv * L.d;
-  chanw_finish<<<(tot + 255) / 256, 256, 0, s>>>(part, w_c, L.d, L.hkv, L.G, L.n, L.nq, nblk, L.scale);
+  chanw_finish<<<(unsigned)L.hkv, 256, 0, s>>>(part, w_c, L.d, L.G, L.n, L.nq, nblk, L.scale);
   return hipGetLastError();
 }
 

@@ -6,8 +6,8 @@
 //   pack_count   per (1024-token chunk, head): tokens per width zone; width validation
 //   pack_layout  one block: per-chunk zone bases, the header, the k_width copy
 //   pack_index   per chunk: ordered ranks -> v_idx, k_keep, k_vloc
-//   pack_v       one thread per (retained token, 32-channel group): quantise V
-//   pack_k       one block per (32 retained tokens, head): quantise every K channel
+//   pack_kv      one block per (32 retained tokens, head): quantise every K channel and
+//                every V group of those tokens
 // The quantiser does its division in float64 exactly as the definition reads
 // (z = min, s = float32(float64(max - min) / (2^b - 1)), code = rint(float64(x - z) / s)), so
 // codes, scales and zeros are bit-exact against a float64 reference.
@@ -60,14 +60,19 @@ pack_count(const uint8_t* __restrict__ bits_v, const uint8_t* __restrict__ bits_
   if (threadIdx.x < 4) cnt[((int64_t)g * nchunk + ch) * 4 + threadIdx.x] = c4[threadIdx.x];
 }
 
-// Header and per-chunk bases.  One block; thread (g, z) scans its chunks, thread 0 lays out the
-// heads in order.
+// Header and per-chunk bases.  One block: threads (g, z) scan their chunks, the K-channel
+// widths are summed per head in parallel, then thread 0 lays the heads out in order.
 __global__ void __launch_bounds__(1024)
 pack_layout(const int32_t* __restrict__ cnt, const uint8_t* __restrict__ bits_k, int Hkv, int d,
             int64_t N, int nchunk, int64_t* __restrict__ base, int64_t* __restrict__ rbase,
             int64_t* __restrict__ header, uint8_t* __restrict__ k_width) {
   __shared__ int64_t tot[1024];      // tokens per (g, z)
+  __shared__ int32_t wk_s[256], qk_s[256];
   const int tid = threadIdx.x;
+  for (int g = tid; g < Hkv; g += blockDim.x) {
+    wk_s[g] = 0;
+    qk_s[g] = 0;
+  }
   for (int gz = tid; gz < Hkv * 4; gz += blockDim.x) {
     const int g = gz / 4, z = gz % 4;
     int64_t run = 0;
@@ -85,13 +90,19 @@ pack_layout(const int32_t* __restrict__ cnt, const uint8_t* __restrict__ bits_k,
       run += (int64_t)cc[0] + cc[1] + cc[2] + cc[3];
     }
   }
-  for (int e = tid; e < Hkv * d; e += blockDim.x) k_width[e] = bits_k[e];
+  __syncthreads();
+  for (int e = tid; e < Hkv * d; e += blockDim.x) {
+    const uint32_t b = bits_k[e];
+    k_width[e] = (uint8_t)b;
+    if (valid_width(b) && b) atomicAdd(&wk_s[e / d], (int32_t)b);   // integer sums: order-free
+    if (b == 2 || b == 4 || b == 8) atomicAdd(&qk_s[e / d], 1);
+  }
+  for (int i = tid; i < KVC_HDR_GLOBAL + Hkv * KVC_HDR_PER_HEAD; i += blockDim.x) header[i] = 0;
   __syncthreads();
   if (tid == 0) {
     const int gpr = d / 32;
     const int widths[4] = {2, 4, 8, 16};
     int64_t o_vi = 0, o_vw = 0, o_vp = 0, o_kk = 0, o_kw = 0, o_kp = 0;
-    for (int i = 0; i < KVC_HDR_GLOBAL + Hkv * KVC_HDR_PER_HEAD; ++i) header[i] = 0;
     header[0] = Hkv;
     header[1] = d;
     header[2] = N;
@@ -110,12 +121,7 @@ pack_layout(const int32_t* __restrict__ cnt, const uint8_t* __restrict__ bits_k,
         o_vp += (z < 3) ? nv * gpr : 0;
         R += nv;
       }
-      int64_t wk = 0, qk = 0;
-      for (int c = 0; c < d; ++c) {
-        uint32_t b = bits_k[(int64_t)g * d + c];
-        wk += valid_width(b) ? b : 0;
-        qk += (b == 2 || b == 4 || b == 8);
-      }
+      const int64_t wk = wk_s[g], qk = qk_s[g];
       const int64_t ng = (R + 31) / 32;
       hp[4] = R;
       hp[17] = o_kk;
@@ -213,62 +219,17 @@ __device__ __forceinline__ void quantize32(const float (&x)[32], int m, int b, u
   *z_out = mn;
 }
 
-// V: one thread per (retained token j of head g, 32-channel group).
+// One block per (group of 32 retained tokens j, head g), 2*D threads: thread c < D quantises
+// K channel c over the 32 tokens (group-major words), thread D + i quantises V group
+// i % (D/32) of token i / (D/32).  Every thread handles one 32-element group.
 template <int D>
-__global__ void __launch_bounds__(256)
-pack_v(const uint16_t* __restrict__ v, int64_t N, const int64_t* __restrict__ header,
-       const int32_t* __restrict__ k_keep, const int32_t* __restrict__ k_vloc,
-       uint32_t* __restrict__ v_words, float* __restrict__ v_par) {
+__global__ void __launch_bounds__(2 * D)
+pack_kv(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t N,
+        const int64_t* __restrict__ header, const uint8_t* __restrict__ bits_k,
+        const int32_t* __restrict__ k_keep, const int32_t* __restrict__ k_vloc,
+        uint32_t* __restrict__ k_words, float* __restrict__ k_par, uint32_t* __restrict__ v_words,
+        float* __restrict__ v_par) {
   constexpr int GPR = D / 32;
-  const int g = blockIdx.y;
-  const int64_t* hp = header + KVC_HDR_GLOBAL + g * KVC_HDR_PER_HEAD;
-  const int64_t R = hp[4];
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t j = gid / GPR;
-  const int grp = (int)(gid % GPR);
-  if (j >= R) return;
-  const int32_t t = k_keep[hp[17] + j];
-  const int32_t loc = k_vloc[hp[17] + j];
-  const int z = loc >> 29;
-  const int64_t pos = loc & ((1 << 29) - 1);
-  const int b = 2 << z;    // 2,4,8,16
-  const uint16_t* src = v + ((int64_t)g * N + t) * D + grp * 32;
-  uint32_t raw[16];
-#pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) {
-    uint4 w = *reinterpret_cast<const uint4*>(src + q4 * 8);
-    raw[4 * q4 + 0] = w.x;
-    raw[4 * q4 + 1] = w.y;
-    raw[4 * q4 + 2] = w.z;
-    raw[4 * q4 + 3] = w.w;
-  }
-  uint32_t* dst = v_words + hp[9 + z] + (pos * GPR + grp) * b;
-  if (b == 16) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) dst[i] = raw[i];
-    return;
-  }
-  float x[32];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    x[2 * i] = bf16_bits_to_f32(raw[i] & 0xFFFFu);
-    x[2 * i + 1] = bf16_bits_to_f32(raw[i] >> 16);
-  }
-  uint32_t w[8];
-  float s, zz;
-  quantize32(x, 32, b, w, &s, &zz);
-  for (int i = 0; i < b; ++i) dst[i] = w[i];
-  float* par = v_par + 2 * (hp[13 + z] + pos * GPR + grp);
-  par[0] = s;
-  par[1] = zz;
-}
-
-// K: one block per (group of 32 retained tokens, head); thread c handles channel c.
-template <int D>
-__global__ void __launch_bounds__(128)
-pack_k(const uint16_t* __restrict__ k, int64_t N, const int64_t* __restrict__ header,
-       const uint8_t* __restrict__ bits_k, const int32_t* __restrict__ k_keep,
-       uint32_t* __restrict__ k_words, float* __restrict__ k_par) {
   const int g = blockIdx.y;
   const int64_t jg = blockIdx.x;
   const int64_t* hp = header + KVC_HDR_GLOBAL + g * KVC_HDR_PER_HEAD;
@@ -276,23 +237,13 @@ pack_k(const uint16_t* __restrict__ k, int64_t N, const int64_t* __restrict__ he
   if (jg * 32 >= R) return;
   const int m = (int)((R - jg * 32) < 32 ? (R - jg * 32) : 32);
   __shared__ uint16_t tile[32][D + 2];
-  __shared__ int32_t woff[D], qslot[D];
-  // stage the 32 retained rows (16-byte loads)
-  for (int e = threadIdx.x; e < 32 * (D / 8); e += blockDim.x) {
-    const int r = e / (D / 8), c8 = e % (D / 8);
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (r < m) {
-      const int32_t t = k_keep[hp[17] + jg * 32 + r];
-      val = *reinterpret_cast<const uint4*>(k + ((int64_t)g * N + t) * D + c8 * 8);
-    }
-    uint32_t vv[4] = {val.x, val.y, val.z, val.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      tile[r][c8 * 8 + 2 * i] = (uint16_t)(vv[i] & 0xFFFFu);
-      tile[r][c8 * 8 + 2 * i + 1] = (uint16_t)(vv[i] >> 16);
-    }
+  __shared__ int32_t woff[D], qslot[D], tok[32], vloc[32];
+  const int tid = threadIdx.x;
+  if (tid < 32) {
+    tok[tid] = tid < m ? k_keep[hp[17] + jg * 32 + tid] : 0;
+    vloc[tid] = tid < m ? k_vloc[hp[17] + jg * 32 + tid] : 0;
   }
-  if (threadIdx.x == 0) {
+  if (tid == 32) {
     int32_t wo = 0, qs = 0;
     for (int c = 0; c < D; ++c) {
       const int b = bits_k[(int64_t)g * D + c];
@@ -303,28 +254,76 @@ pack_k(const uint16_t* __restrict__ k, int64_t N, const int64_t* __restrict__ he
     }
   }
   __syncthreads();
-  const int c = threadIdx.x;
-  if (c >= D) return;
-  const int b = bits_k[(int64_t)g * D + c];
-  if (b == 0 || !valid_width(b)) return;
-  uint32_t* dst = k_words + hp[18] + jg * hp[20] + woff[c];
-  if (b == 16) {
-    for (int i = 0; i < 16; ++i) {
-      uint32_t lo16 = (2 * i < m) ? tile[2 * i][c] : 0u;
-      uint32_t hi16 = (2 * i + 1 < m) ? tile[2 * i + 1][c] : 0u;
-      dst[i] = lo16 | (hi16 << 16);
+  // stage the retained K rows (16-byte loads)
+  for (int e = tid; e < 32 * (D / 8); e += 2 * D) {
+    const int r = e / (D / 8), c8 = e % (D / 8);
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (r < m) val = *reinterpret_cast<const uint4*>(k + ((int64_t)g * N + tok[r]) * D + c8 * 8);
+    const uint32_t vv[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tile[r][c8 * 8 + 2 * i] = (uint16_t)(vv[i] & 0xFFFFu);
+      tile[r][c8 * 8 + 2 * i + 1] = (uint16_t)(vv[i] >> 16);
     }
+  }
+  __syncthreads();
+  float x[32];
+  uint32_t w[8];
+  float sc, zz;
+  if (tid < D) {
+    const int c = tid;
+    const int b = bits_k[(int64_t)g * D + c];
+    if (b == 0 || !valid_width(b)) return;
+    uint32_t* dst = k_words + hp[18] + jg * hp[20] + woff[c];
+    if (b == 16) {
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t lo16 = (2 * i < m) ? tile[2 * i][c] : 0u;
+        const uint32_t hi16 = (2 * i + 1 < m) ? tile[2 * i + 1][c] : 0u;
+        dst[i] = lo16 | (hi16 << 16);
+      }
+      return;
+    }
+#pragma unroll
+    for (int e = 0; e < 32; ++e) x[e] = bf16_bits_to_f32(tile[e][c]);
+    quantize32(x, m, b, w, &sc, &zz);
+    for (int i = 0; i < b; ++i) dst[i] = w[i];
+    float* par = k_par + 2 * (hp[19] + jg * hp[21] + qslot[c]);
+    par[0] = sc;
+    par[1] = zz;
     return;
   }
-  float x[32];
+  const int task = tid - D;
+  const int e = task / GPR, grp = task % GPR;
+  if (task >= 32 * GPR || e >= m) return;
+  const int32_t loc = vloc[e];
+  const int z = loc >> 29;
+  const int64_t pos = loc & ((1 << 29) - 1);
+  const int b = 2 << z;    // 2,4,8,16
+  const uint16_t* src = v + ((int64_t)g * N + tok[e]) * D + grp * 32;
+  uint32_t raw[16];
 #pragma unroll
-  for (int e = 0; e < 32; ++e) x[e] = bf16_bits_to_f32(tile[e][c]);
-  uint32_t w[8];
-  float s, zz;
-  quantize32(x, m, b, w, &s, &zz);
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const uint4 wv = *reinterpret_cast<const uint4*>(src + q4 * 8);
+    raw[4 * q4 + 0] = wv.x;
+    raw[4 * q4 + 1] = wv.y;
+    raw[4 * q4 + 2] = wv.z;
+    raw[4 * q4 + 3] = wv.w;
+  }
+  uint32_t* dst = v_words + hp[9 + z] + (pos * GPR + grp) * b;
+  if (b == 16) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dst[i] = raw[i];
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    x[2 * i] = bf16_bits_to_f32(raw[i] & 0xFFFFu);
+    x[2 * i + 1] = bf16_bits_to_f32(raw[i] >> 16);
+  }
+  quantize32(x, 32, b, w, &sc, &zz);
   for (int i = 0; i < b; ++i) dst[i] = w[i];
-  float* par = k_par + 2 * (hp[19] + jg * hp[21] + qslot[c]);
-  par[0] = s;
+  float* par = v_par + 2 * (hp[13 + z] + pos * GPR + grp);
+  par[0] = sc;
   par[1] = zz;
 }
 
@@ -380,16 +379,13 @@ hipError_t launch_pack(const Layer& L, const uint16_t* k, const uint16_t* v,
                                  out.header, out.k_width);
   pack_index<<<gc, 256, 0, s>>>(bits_v, L.n, nchunk, w.base, w.rbase, out.header, out.v_idx,
                                 out.k_keep, out.k_vloc);
-  const int gpr = L.d / 32;
-  dim3 gv((unsigned)((L.n * gpr + 255) / 256), (unsigned)L.hkv);
   dim3 gk((unsigned)((L.n + 31) / 32), (unsigned)L.hkv);
-  if (L.d == 128) {
-    pack_v<128><<<gv, 256, 0, s>>>(v, L.n, out.header, out.k_keep, out.k_vloc, out.v_words, out.v_par);
-    pack_k<128><<<gk, 128, 0, s>>>(k, L.n, out.header, bits_k, out.k_keep, out.k_words, out.k_par);
-  } else {
-    pack_v<64><<<gv, 256, 0, s>>>(v, L.n, out.header, out.k_keep, out.k_vloc, out.v_words, out.v_par);
-    pack_k<64><<<gk, 128, 0, s>>>(k, L.n, out.header, bits_k, out.k_keep, out.k_words, out.k_par);
-  }
+  if (L.d == 128)
+    pack_kv<128><<<gk, 256, 0, s>>>(k, v, L.n, out.header, bits_k, out.k_keep, out.k_vloc,
+                                    out.k_words, out.k_par, out.v_words, out.v_par);
+  else
+    pack_kv<64><<<gk, 128, 0, s>>>(k, v, L.n, out.header, bits_k, out.k_keep, out.k_vloc,
+                                   out.k_words, out.k_par, out.v_words, out.v_par);
   return hipGetLastError();
 }
 

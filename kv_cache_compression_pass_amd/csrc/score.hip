@@ -383,25 +383,37 @@ score_partial(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   }
 }
 
-// SUM: w[g][t] = sum over the group's heads, then over the row tiles that see t (ascending).
-__global__ void score_reduce_sum(const float* __restrict__ part, float* __restrict__ scores,
-                                 int Hkv, int G, int nRT, int64_t N, int64_t Nq, int causal,
-                                 int64_t Npad) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)Hkv * N) return;
-  const int g = (int)(idx / N);
-  const int64_t t = idx % N;
+// SUM: w[g][t] = sum over the group's (head, row tile) pairs that see t.  Four lanes share a
+// key: lane r sums the pairs j = r, r+4, ... (head-major, row tiles ascending), then the four
+// sums are combined as (s0 + s1) + (s2 + s3): a fixed order.
+__global__ void __launch_bounds__(256)
+score_reduce_sum(const float* __restrict__ part, float* __restrict__ scores, int Hkv, int G,
+                 int nRT, int64_t N, int64_t Nq, int causal, int64_t Npad) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t idx = gid >> 2;
+  const int r = (int)(gid & 3);
+  const bool ok = idx < (int64_t)Hkv * N;
+  const int g = ok ? (int)(idx / N) : 0;
+  const int64_t t = ok ? idx % N : 0;
   int rt0 = 0;
   if (causal) {
     const int64_t rel = t - (N - Nq);                 // first row index that sees t
     rt0 = rel > 0 ? (int)(rel / kRowsPerBlock) : 0;
   }
+  const int nrt = nRT - rt0;
+  const int terms = G * nrt;
   float s = 0.f;
-  for (int hl = 0; hl < G; ++hl) {
-    const float* p = part + ((int64_t)(g * G + hl) * nRT) * Npad + t;
-    for (int rt = rt0; rt < nRT; ++rt) s += p[(int64_t)rt * Npad];
+  if (ok) {
+    for (int j = r; j < terms; j += 4) {
+      const int hl = j / nrt, rt = rt0 + j % nrt;
+      s += part[((int64_t)(g * G + hl) * nRT + rt) * Npad + t];
+    }
   }
-  scores[idx] = s;
+  const float s1 = __shfl_xor(s, 1, 64);
+  const float pair = (r & 1) ? s1 + s : s + s1;       // lanes 0/1 -> s0+s1, lanes 2/3 -> s2+s3
+  const float other = __shfl_xor(pair, 2, 64);
+  const float tot = (r & 2) ? other + pair : pair + other;
+  if (ok && r == 0) scores[idx] = tot;
 }
 
 // MAX: s+[g][t] = max over the group's heads h of 2^(max over row tiles of part) / ||W_O^h v_t||.
@@ -680,7 +692,7 @@ hipError_t launch_score(const Layer& L, int mode, const uint16_t* q, const uint1
   if (mx)
     score_reduce_max<<<rb, 256, 0, s>>>(part, won, scores, L.hkv, L.G, p.nRT, L.n, L.nq, L.causal, p.Npad);
   else
-    score_reduce_sum<<<rb, 256, 0, s>>>(part, scores, L.hkv, L.G, p.nRT, L.n, L.nq, L.causal, p.Npad);
+    score_reduce_sum<<<(unsigned)((4 * total + 255) / 256), 256, 0, s>>>(part, scores, L.hkv, L.G, p.nRT, L.n, L.nq, L.causal, p.Npad);
   return hipGetLastError();
 }
 
