@@ -26,7 +26,6 @@ namespace {
 
 constexpr int kThreads = 256;   // 4 waves per block in both passes
 constexpr int kRowsPerBlock = 256;
-constexpr int kPad = 8;         // bf16 elements of padding per LDS row (16 bytes)
 constexpr int kXcds = 8;        // MI355X: blocks are dealt round-robin to 8 XCDs
 
 struct Decomp {
@@ -59,32 +58,95 @@ __device__ __forceinline__ int64_t tile_kend(int rt, int64_t N, int64_t Nq, int 
   return e < N ? e : N;
 }
 
-// 64 rows x D bf16 from global into registers (D/32 16-byte chunks per thread); rows at or
-// beyond `limit` read as zero.
-template <int D>
-__device__ __forceinline__ void load_tile_regs(uint4 (&r)[D / 32], const uint16_t* base,
-                                               int64_t row0, int64_t limit) {
-  constexpr int CPR = D / 8;
-#pragma unroll
-  for (int j = 0; j < D / 32; ++j) {
-    const int chunk = threadIdx.x + j * kThreads;
-    const int rr = chunk / CPR, cc = chunk % CPR;
-    const int64_t row = row0 + rr;
-    r[j] = (row < limit) ? *reinterpret_cast<const uint4*>(base + row * D + cc * 8)
-                         : make_uint4(0, 0, 0, 0);
-  }
+// ---- K tile ring: 4 LDS slots of 64 keys x D bf16, filled by direct global->LDS loads -----
+// Each slot is its own LDS object, so the compiler can tell an in-flight fill of one slot from
+// reads of another and does not serialise them.  A key row occupies 2*D contiguous bytes; its
+// 16-byte chunks are XOR-swizzled (slot s of row r holds chunk s ^ swz(r)) so that the 32 rows
+// read by one matrix-core fragment load hit distinct banks without padding.
+__shared__ __attribute__((aligned(16))) uint16_t g_kslot0[64 * 128];
+__shared__ __attribute__((aligned(16))) uint16_t g_kslot1[64 * 128];
+__shared__ __attribute__((aligned(16))) uint16_t g_kslot2[64 * 128];
+__shared__ __attribute__((aligned(16))) uint16_t g_kslot3[64 * 128];
+
+template <int S>
+__device__ __forceinline__ uint16_t* kslot() {
+  return S == 0 ? g_kslot0 : S == 1 ? g_kslot1 : S == 2 ? g_kslot2 : g_kslot3;
 }
 
 template <int D>
-__device__ __forceinline__ void store_tile_lds(const uint4 (&r)[D / 32], uint16_t* lds) {
-  constexpr int CPR = D / 8;
-  constexpr int RS = D + kPad;
+__device__ __forceinline__ int swz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
+// Global->LDS load instructions per wave for one 64-key tile (each moves 1 KB).
+template <int D>
+constexpr int tile_loads_per_wave() { return (64 * D * 2) / 1024 / 4; }
+
+// Byte offset, inside a tile, of the 16 bytes lane `lane` of wave `wave` moves with its j-th
+// load of every tile (constant across tiles).
+template <int D>
+__device__ __forceinline__ void tile_offsets(int (&voff)[4], int wave, int lane) {
+  constexpr int CPR = D / 8;             // 16-byte chunks per key row
+  constexpr int RPI = 64 / CPR;          // rows per load instruction
+  constexpr int L = tile_loads_per_wave<D>();
 #pragma unroll
-  for (int j = 0; j < D / 32; ++j) {
-    const int chunk = threadIdx.x + j * kThreads;
-    const int rr = chunk / CPR, cc = chunk % CPR;
-    *reinterpret_cast<uint4*>(lds + rr * RS + cc * 8) = r[j];
+  for (int j = 0; j < 4; ++j) {
+    const int row = (wave * L + j) * RPI + lane / CPR;
+    voff[j] = j < L ? (row * D + 8 * ((lane % CPR) ^ swz<D>(row))) * 2 : 0;
   }
+}
+
+// Fill slot S with keys t0 .. t0+63 of head kh.  Buffer loads whose resource ends at key N:
+// rows past the end read as zeros (their logits are masked), so a tile that starts at or past
+// N issues its loads all the same and touches no memory.
+template <int D, int S>
+__device__ __forceinline__ void issue_tile(const uint16_t* kh, int t0, int N,
+                                           const int (&voff)[4], int wave) {
+  constexpr int L = tile_loads_per_wave<D>();
+  constexpr int RPI = 64 / (D / 8);
+  t0 = __builtin_amdgcn_readfirstlane(t0);   // block-uniform; keeps the resource scalar
+  int rows = N - t0;
+  rows = rows < 0 ? 0 : (rows > 64 ? 64 : rows);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(kh + (int64_t)t0 * D), (short)0, __builtin_amdgcn_readfirstlane(rows * D * 2),
+      0x00020000);
+#pragma unroll
+  for (int j = 0; j < L; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(kslot<S>() + (wave * L + j) * RPI * D), 16,
+        voff[j], 0, 0, 0);
+}
+
+// Fragment of key row r, logical 16-byte chunk c, from slot S.
+template <int D, int S>
+__device__ __forceinline__ bf16x8 kfrag(int r, int c) {
+  return as_bf16x8(*reinterpret_cast<const uint4*>(kslot<S>() + r * D + 8 * (c ^ swz<D>(r))));
+}
+
+// Wait until at most `ahead` tiles of this wave's loads are in flight and every LDS operation
+// has finished, then meet the other waves.  The empty asm statements keep the compiler from
+// moving memory operations across the barrier.
+template <int D>
+__device__ __forceinline__ void ring_barrier(int ahead) {
+  constexpr int L = tile_loads_per_wave<D>();
+  asm volatile("" ::: "memory");
+  // s_waitcnt immediate: vmcnt in [3:0] and [15:14], expcnt [6:4] (7 = no wait), lgkmcnt [11:8]
+  if (ahead >= 2)
+    __builtin_amdgcn_s_waitcnt(((2 * L) & 15) | (((2 * L) >> 4) << 14) | (7 << 4));
+  else if (ahead == 1)
+    __builtin_amdgcn_s_waitcnt((L & 15) | ((L >> 4) << 14) | (7 << 4));
+  else
+    __builtin_amdgcn_s_waitcnt(7 << 4);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Barrier for ordinary LDS traffic that leaves the ring's loads in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0); vmcnt and expcnt left alone
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // bf16 fragments of this wave's 64 query rows: qf[nb][ks] holds row 32*nb + lane%32,
@@ -103,118 +165,149 @@ __device__ __forceinline__ void load_q_frags(bf16x8 (&qf)[2][D / 16], const uint
   }
 }
 
+// Per-block geometry shared by both passes.
+struct Geo {
+  int g, rt, ch, hl, h, wave, lane, hi, lo;
+  int off, i_block, i_wave, kend_wave, k0, k1;   // key / row positions (< 2^29)
+  int ntiles;
+};
+
+// Decode the block's work item and key range; false for an empty item (uniform).
+__device__ __forceinline__ bool geo_of(const Decomp& dc, int64_t N, int64_t Nq, int causal, Geo& o) {
+  if (!decode_work(dc, o.g, o.rt, o.ch, o.hl)) return false;
+  const int kend = (int)tile_kend(o.rt, N, Nq, causal);
+  o.k0 = o.ch * dc.KC;
+  if (o.k0 >= kend) return false;
+  o.k1 = (o.k0 + dc.KC < kend) ? o.k0 + dc.KC : kend;
+  o.lane = threadIdx.x & 63;
+  o.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: keeps LDS bases scalar
+  o.hi = o.lane >> 5;
+  o.lo = o.lane & 31;
+  o.h = o.g * dc.G + o.hl;
+  o.off = (int)(N - Nq);
+  o.i_block = o.rt * kRowsPerBlock;
+  o.i_wave = o.i_block + 64 * o.wave;
+  o.kend_wave = 0;
+  if (o.i_wave < Nq) {
+    const int lr = (o.i_wave + 63 < Nq) ? o.i_wave + 63 : (int)Nq - 1;
+    o.kend_wave = causal ? ((o.off + lr + 1 < N) ? o.off + lr + 1 : (int)N) : (int)N;
+  }
+  o.ntiles = (int)((o.k1 - o.k0 + 63) / 64);
+  return true;
+}
+
 // ---------------------------------------------------------------------------------------
 // Pass 1: per chunk, m = max_t x and l = sum_t 2^(x - m) for every row, x = c * q.k.
 // D[m = key][n = row]: a lane holds one row and 16 keys of each 32-key block.
 // ---------------------------------------------------------------------------------------
+template <int D, int S>
+__device__ __forceinline__ void lse_tile(const Geo& G, const bf16x8 (&qf)[2][D / 16],
+                                         float (&m_run)[2], float (&l_run)[2], int t0,
+                                         int N, int causal, float c) {
+  if (t0 >= G.kend_wave) return;
+  constexpr int KS = D / 16;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 a = kfrag<D, S>(kb * 32 + G.lo, 2 * ks + G.hi);
+      acc[kb][0] = mfma32(a, qf[0][ks], acc[kb][0]);
+      acc[kb][1] = mfma32(a, qf[1][ks], acc[kb][1]);
+    }
+  }
+  const bool full = (!causal || t0 + 63 <= G.off + G.i_wave) && (t0 + 64 <= N);
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    if (!full) {
+      const int pos = G.off + G.i_wave + 32 * nb + G.lo;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int t = t0 + 32 * kb + acc_row(i, G.hi);
+          if (t >= N || (causal && t > pos)) acc[kb][nb][i] = -INFINITY;
+        }
+    }
+    float tmax = acc[0][nb][0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, acc[0][nb][i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, acc[1][nb][i]);
+    tmax = fmaxf(tmax, swap_half(tmax));
+    const float mnew = fmaxf(m_run[nb], tmax * c);
+    if (mnew > -INFINITY) {
+      const float nm = -mnew;
+      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        s0 += fast_exp2(fmaf(acc[0][nb][i], c, nm));
+        s1 += fast_exp2(fmaf(acc[0][nb][i + 1], c, nm));
+        s2 += fast_exp2(fmaf(acc[1][nb][i], c, nm));
+        s3 += fast_exp2(fmaf(acc[1][nb][i + 1], c, nm));
+      }
+      l_run[nb] = fmaf(l_run[nb], fast_exp2(m_run[nb] - mnew), (s0 + s1) + (s2 + s3));
+      m_run[nb] = mnew;
+    }
+  }
+}
+
+// One ring step: wait for tile J (two younger tiles may stay in flight), refill the slot the
+// previous step freed with tile J + 3 (always issued: rows past the end are clamped and the
+// slot is never read), then process tile J.  Issuing unconditionally keeps the compiler's view
+// of the in-flight fills exact, so it adds no waits of its own.
+#define KVC_LSE_STEP(S, J)                                                                  \
+  {                                                                                         \
+    ring_barrier<D>(2);                                                                     \
+    issue_tile<D, ((S) + 3) & 3>(kh, G.k0 + 64 * ((J) + 3), n, voff, G.wave);    \
+    lse_tile<D, S>(G, qf, m_run, l_run, G.k0 + 64 * (J), n, causal, c);           \
+  }
+
 template <int D>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 lse_partial(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             float2* __restrict__ part, float* __restrict__ lse, Decomp dc, int64_t N, int64_t Nq,
             int causal, float c) {
-  constexpr int RS = D + kPad;
-  constexpr int KS = D / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t kt[2][64 * RS];
-  int g, rt, ch, hl;
-  if (!decode_work(dc, g, rt, ch, hl)) return;
-  const int64_t kend = tile_kend(rt, N, Nq, causal);
-  const int64_t k0 = (int64_t)ch * dc.KC;
-  if (k0 >= kend) return;                       // empty item: uniform for the block
-  const int64_t k1 = (k0 + dc.KC < kend) ? k0 + dc.KC : kend;
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int hi = lane >> 5, lo = lane & 31;
-  const int h = g * dc.G + hl;
-  const int64_t off = N - Nq;
-  const int64_t i_wave = (int64_t)rt * kRowsPerBlock + 64 * wave;
-  int64_t kend_wave = 0;
-  if (i_wave < Nq) {
-    const int64_t lr = (i_wave + 63 < Nq) ? i_wave + 63 : Nq - 1;
-    kend_wave = causal ? ((off + lr + 1 < N) ? off + lr + 1 : N) : N;
-  }
-  const uint16_t* kh = k + (int64_t)g * N * D;
-
-  bf16x8 qf[2][KS];
-  load_q_frags<D>(qf, q, h, Nq, i_wave, hi, lo);
-
+  Geo G;
+  if (!geo_of(dc, N, Nq, causal, G)) return;   // empty item: uniform for the block
+  const uint16_t* kh = k + (int64_t)G.g * N * D;
+  const int n = (int)N;
+  bf16x8 qf[2][D / 16];
+  load_q_frags<D>(qf, q, G.h, Nq, G.i_wave, G.hi, G.lo);
+  int voff[4];
+  tile_offsets<D>(voff, G.wave, G.lane);
+  __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);    // vmcnt(0): Q fragments resident before the ring starts
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
-  const int ntiles = (int)((k1 - k0 + 63) / 64);
-
-  uint4 pre[D / 32];
-  load_tile_regs<D>(pre, kh, k0, N);
-  store_tile_lds<D>(pre, kt[0]);
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int64_t t0 = k0 + (int64_t)j * 64;
-    if (j + 1 < ntiles) load_tile_regs<D>(pre, kh, t0 + 64, N);
-    if (t0 < kend_wave) {
-      const uint16_t* kl = kt[j & 1];
-      f32x16 acc[2][2];
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(kl + (kb * 32 + lo) * RS + ks * 16 + 8 * hi));
-          acc[kb][0] = mfma32(a, qf[0][ks], acc[kb][0]);
-          acc[kb][1] = mfma32(a, qf[1][ks], acc[kb][1]);
-        }
-      }
-      const bool full = (!causal || t0 + 63 <= off + i_wave) && (t0 + 64 <= N);
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        if (!full) {
-          const int64_t pos = off + i_wave + 32 * nb + lo;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int64_t t = t0 + 32 * kb + acc_row(i, hi);
-              if (t >= N || (causal && t > pos)) acc[kb][nb][i] = -INFINITY;
-            }
-        }
-        float tmax = acc[0][nb][0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, acc[0][nb][i]);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, acc[1][nb][i]);
-        tmax = fmaxf(tmax, swap_half(tmax));
-        const float mnew = fmaxf(m_run[nb], tmax * c);
-        if (mnew > -INFINITY) {
-          const float nm = -mnew;
-          float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; i += 2) {
-            s0 += fast_exp2(fmaf(acc[0][nb][i], c, nm));
-            s1 += fast_exp2(fmaf(acc[0][nb][i + 1], c, nm));
-            s2 += fast_exp2(fmaf(acc[1][nb][i], c, nm));
-            s3 += fast_exp2(fmaf(acc[1][nb][i + 1], c, nm));
-          }
-          l_run[nb] = fmaf(l_run[nb], fast_exp2(m_run[nb] - mnew), (s0 + s1) + (s2 + s3));
-          m_run[nb] = mnew;
-        }
-      }
-    }
-    if (j + 1 < ntiles) store_tile_lds<D>(pre, kt[(j + 1) & 1]);
-    __syncthreads();
+  issue_tile<D, 0>(kh, G.k0, n, voff, G.wave);
+  issue_tile<D, 1>(kh, G.k0 + 64, n, voff, G.wave);
+  issue_tile<D, 2>(kh, G.k0 + 128, n, voff, G.wave);
+  int j0 = 0;
+  for (; j0 + 4 <= G.ntiles; j0 += 4) {
+    KVC_LSE_STEP(0, j0)
+    KVC_LSE_STEP(1, j0 + 1)
+    KVC_LSE_STEP(2, j0 + 2)
+    KVC_LSE_STEP(3, j0 + 3)
   }
-
+  if (j0 < G.ntiles) KVC_LSE_STEP(0, j0)
+  if (j0 + 1 < G.ntiles) KVC_LSE_STEP(1, j0 + 1)
+  if (j0 + 2 < G.ntiles) KVC_LSE_STEP(2, j0 + 2)
+  __builtin_amdgcn_s_waitcnt(7 << 4);       // no LDS fill may outlive the block
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const float lt = l_run[nb] + swap_half(l_run[nb]);
-    const int64_t row = i_wave + 32 * nb + lo;
-    if (hi == 0 && row < Nq) {
+    const int64_t row = G.i_wave + 32 * nb + G.lo;
+    if (G.hi == 0 && row < Nq) {
       if (dc.maxCh == 1)   // one chunk covers the row: write l itself
-        lse[(int64_t)h * Nq + row] = (m_run[nb] > -INFINITY) ? (m_run[nb] + log2f(lt)) * kLn2 : -INFINITY;
+        lse[(int64_t)G.h * Nq + row] = (m_run[nb] > -INFINITY) ? (m_run[nb] + log2f(lt)) * kLn2 : -INFINITY;
       else
-        part[((int64_t)h * Nq + row) * dc.maxCh + ch] = make_float2(m_run[nb], lt);
+        part[((int64_t)G.h * Nq + row) * dc.maxCh + G.ch] = make_float2(m_run[nb], lt);
     }
   }
 }
@@ -242,145 +335,140 @@ __global__ void lse_combine(const float2* __restrict__ part, float* __restrict__
 // MAX: partial = max_rows (x - l'), l' = l*log2(e) - log2||h||.  One partial per
 // (query head, row tile, key), the four waves' rows summed (or maxed) in a fixed order.
 // ---------------------------------------------------------------------------------------
+template <int D, bool MAXMODE, int S>
+__device__ __forceinline__ void score_tile(const Geo& G, const bf16x8 (&qf)[2][D / 16],
+                                           const float (&lv)[2][16], int t0, int N,
+                                           int causal, float c, float (&cbw)[64]) {
+  constexpr int KS = D / 16;
+  const bool any = t0 < G.kend_wave;
+  const bool full = (!causal || t0 + 63 <= G.off + G.i_wave) && (t0 + 64 <= N);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    float colv = MAXMODE ? -INFINITY : 0.f;
+    if (any) {
+      f32x16 acc[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[a][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 b = kfrag<D, S>(kb * 32 + G.lo, 2 * ks + G.hi);
+        acc[0] = mfma32(qf[0][ks], b, acc[0]);
+        acc[1] = mfma32(qf[1][ks], b, acc[1]);
+      }
+      const int t = t0 + 32 * kb + G.lo;
+      if (MAXMODE) {
+        float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) {
+            float x0 = fmaf(acc[mb][i], c, -lv[mb][i]);
+            float x1 = fmaf(acc[mb][i + 1], c, -lv[mb][i + 1]);
+            if (!full) {
+              const int p0 = G.off + G.i_wave + 32 * mb + acc_row(i, G.hi);
+              if (t >= N || (causal && t > p0)) x0 = -INFINITY;
+              if (t >= N || (causal && t > p0 + 1)) x1 = -INFINITY;
+            }
+            mx0 = fmaxf(mx0, x0);
+            mx1 = fmaxf(mx1, x1);
+          }
+        colv = fmaxf(mx0, mx1);
+        colv = fmaxf(colv, swap_half(colv));
+      } else {
+        float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          float x0 = fmaf(acc[0][i], c, -lv[0][i]);
+          float x1 = fmaf(acc[0][i + 1], c, -lv[0][i + 1]);
+          float x2 = fmaf(acc[1][i], c, -lv[1][i]);
+          float x3 = fmaf(acc[1][i + 1], c, -lv[1][i + 1]);
+          if (!full) {
+            const int p0 = G.off + G.i_wave + acc_row(i, G.hi);
+            if (t >= N || (causal && t > p0)) x0 = -INFINITY;
+            if (t >= N || (causal && t > p0 + 1)) x1 = -INFINITY;
+            if (t >= N || (causal && t > p0 + 32)) x2 = -INFINITY;
+            if (t >= N || (causal && t > p0 + 33)) x3 = -INFINITY;
+          }
+          s0 += fast_exp2(x0);
+          s1 += fast_exp2(x1);
+          s2 += fast_exp2(x2);
+          s3 += fast_exp2(x3);
+        }
+        colv = (s0 + s1) + (s2 + s3);
+        colv = colv + swap_half(colv);
+      }
+    }
+    if (G.hi == 0) cbw[32 * kb + G.lo] = colv;
+  }
+}
+
+// Four waves' partials of one 64-key tile, combined in a fixed order.
+template <bool MAXMODE>
+__device__ __forceinline__ float combine4(const float* cp) {
+  if (MAXMODE) return fmaxf(fmaxf(cp[0], cp[64]), fmaxf(cp[128], cp[192]));
+  return (cp[0] + cp[64]) + (cp[128] + cp[192]);
+}
+
+#define KVC_SCORE_STEP(S, J)                                                                \
+  {                                                                                         \
+    ring_barrier<D>(2);                                                                     \
+    if ((J) > 0 && threadIdx.x < 64)                                                        \
+      out[G.k0 + 64 * ((J) - 1) + (int)threadIdx.x] = combine4<MAXMODE>(&cb[((J) - 1) & 1][0][threadIdx.x]); \
+    issue_tile<D, ((S) + 3) & 3>(kh, G.k0 + 64 * ((J) + 3), n, voff, G.wave);    \
+    score_tile<D, MAXMODE, S>(G, qf, lv, G.k0 + 64 * (J), n, causal, c, cb[(J) & 1][G.wave]); \
+  }
+
 template <int D, bool MAXMODE>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 score_partial(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
               const float* __restrict__ lse, const float* __restrict__ hlog2,
               float* __restrict__ part, Decomp dc, int64_t N, int64_t Nq, int causal, float c,
               int64_t Npad) {
-  constexpr int RS = D + kPad;
-  constexpr int KS = D / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t kt[2][64 * RS];
   __shared__ float cb[2][4][64];
   __shared__ float lrow[kRowsPerBlock];
-  int g, rt, ch, hl;
-  if (!decode_work(dc, g, rt, ch, hl)) return;
-  const int64_t kend = tile_kend(rt, N, Nq, causal);
-  const int64_t k0 = (int64_t)ch * dc.KC;
-  if (k0 >= kend) return;
-  const int64_t k1 = (k0 + dc.KC < kend) ? k0 + dc.KC : kend;
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int hi = lane >> 5, lo = lane & 31;
-  const int h = g * dc.G + hl;
-  const int64_t off = N - Nq;
-  const int64_t i_block = (int64_t)rt * kRowsPerBlock;
-  const int64_t i_wave = i_block + 64 * wave;
-  int64_t kend_wave = 0;
-  if (i_wave < Nq) {
-    const int64_t lr = (i_wave + 63 < Nq) ? i_wave + 63 : Nq - 1;
-    kend_wave = causal ? ((off + lr + 1 < N) ? off + lr + 1 : N) : N;
-  }
-  const uint16_t* kh = k + (int64_t)g * N * D;
-  float* out = part + ((int64_t)h * dc.nRT + rt) * Npad;
-
+  Geo G;
+  if (!geo_of(dc, N, Nq, causal, G)) return;
+  const uint16_t* kh = k + (int64_t)G.g * N * D;
+  const int n = (int)N;
+  float* out = part + ((int64_t)G.h * dc.nRT + G.rt) * Npad;
   {
-    const int64_t row = i_block + threadIdx.x;
+    const int64_t row = G.i_block + threadIdx.x;
     float v = INFINITY;                            // rows beyond Nq contribute nothing
     if (row < Nq) {
-      v = lse[(int64_t)h * Nq + row] * kLog2e;
+      v = lse[(int64_t)G.h * Nq + row] * kLog2e;
       if (MAXMODE) v -= hlog2[row];
     }
     lrow[threadIdx.x] = v;
   }
-  bf16x8 qf[2][KS];
-  load_q_frags<D>(qf, q, h, Nq, i_wave, hi, lo);
-
-  uint4 pre[D / 32];
-  load_tile_regs<D>(pre, kh, k0, N);
-  store_tile_lds<D>(pre, kt[0]);
-  __syncthreads();
+  bf16x8 qf[2][D / 16];
+  load_q_frags<D>(qf, q, G.h, Nq, G.i_wave, G.hi, G.lo);
+  int voff[4];
+  tile_offsets<D>(voff, G.wave, G.lane);
+  __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);    // vmcnt(0): Q fragments and l' resident before the ring starts
+  issue_tile<D, 0>(kh, G.k0, n, voff, G.wave);
+  issue_tile<D, 1>(kh, G.k0 + 64, n, voff, G.wave);
+  issue_tile<D, 2>(kh, G.k0 + 128, n, voff, G.wave);
+  lds_barrier();
   float lv[2][16];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) lv[mb][i] = lrow[64 * wave + 32 * mb + acc_row(i, hi)];
-
-  const int ntiles = (int)((k1 - k0 + 63) / 64);
-  for (int j = 0; j < ntiles; ++j) {
-    const int64_t t0 = k0 + (int64_t)j * 64;
-    if (j + 1 < ntiles) load_tile_regs<D>(pre, kh, t0 + 64, N);
-    // the previous tile's wave partials are complete (barrier at the end of j-1)
-    if (j > 0 && threadIdx.x < 64) {
-      const float* cp = &cb[(j - 1) & 1][0][threadIdx.x];
-      float r;
-      if (MAXMODE) r = fmaxf(fmaxf(cp[0], cp[64]), fmaxf(cp[128], cp[192]));
-      else r = (cp[0] + cp[64]) + (cp[128] + cp[192]);
-      out[t0 - 64 + threadIdx.x] = r;
-    }
-    const uint16_t* kl = kt[j & 1];
-    const bool any = t0 < kend_wave;
-    const bool full = (!causal || t0 + 63 <= off + i_wave) && (t0 + 64 <= N);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float colv = MAXMODE ? -INFINITY : 0.f;
-      if (any) {
-        f32x16 acc[2];
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[a][i] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4*>(kl + (kb * 32 + lo) * RS + ks * 16 + 8 * hi));
-          acc[0] = mfma32(qf[0][ks], b, acc[0]);
-          acc[1] = mfma32(qf[1][ks], b, acc[1]);
-        }
-        const int64_t t = t0 + 32 * kb + lo;
-        if (MAXMODE) {
-          float mx0 = -INFINITY, mx1 = -INFINITY;
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int i = 0; i < 16; i += 2) {
-              float x0 = fmaf(acc[mb][i], c, -lv[mb][i]);
-              float x1 = fmaf(acc[mb][i + 1], c, -lv[mb][i + 1]);
-              if (!full) {
-                const int64_t p0 = off + i_wave + 32 * mb + acc_row(i, hi);
-                if (t >= N || (causal && t > p0)) x0 = -INFINITY;
-                if (t >= N || (causal && t > p0 + 1)) x1 = -INFINITY;
-              }
-              mx0 = fmaxf(mx0, x0);
-              mx1 = fmaxf(mx1, x1);
-            }
-          colv = fmaxf(mx0, mx1);
-          colv = fmaxf(colv, swap_half(colv));
-        } else {
-          float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; i += 2) {
-            float x0 = fmaf(acc[0][i], c, -lv[0][i]);
-            float x1 = fmaf(acc[0][i + 1], c, -lv[0][i + 1]);
-            float x2 = fmaf(acc[1][i], c, -lv[1][i]);
-            float x3 = fmaf(acc[1][i + 1], c, -lv[1][i + 1]);
-            if (!full) {
-              const int64_t p0 = off + i_wave + acc_row(i, hi);
-              if (t >= N || (causal && t > p0)) x0 = -INFINITY;
-              if (t >= N || (causal && t > p0 + 1)) x1 = -INFINITY;
-              if (t >= N || (causal && t > p0 + 32)) x2 = -INFINITY;
-              if (t >= N || (causal && t > p0 + 33)) x3 = -INFINITY;
-            }
-            s0 += fast_exp2(x0);
-            s1 += fast_exp2(x1);
-            s2 += fast_exp2(x2);
-            s3 += fast_exp2(x3);
-          }
-          colv = (s0 + s1) + (s2 + s3);
-          colv = colv + swap_half(colv);
-        }
-      }
-      if (hi == 0) cb[j & 1][wave][32 * kb + lo] = colv;
-    }
-    if (j + 1 < ntiles) store_tile_lds<D>(pre, kt[(j + 1) & 1]);
-    __syncthreads();
+    for (int i = 0; i < 16; ++i) lv[mb][i] = lrow[64 * G.wave + 32 * mb + acc_row(i, G.hi)];
+  int j0 = 0;
+  for (; j0 + 4 <= G.ntiles; j0 += 4) {
+    KVC_SCORE_STEP(0, j0)
+    KVC_SCORE_STEP(1, j0 + 1)
+    KVC_SCORE_STEP(2, j0 + 2)
+    KVC_SCORE_STEP(3, j0 + 3)
   }
-  if (threadIdx.x < 64) {
-    const float* cp = &cb[(ntiles - 1) & 1][0][threadIdx.x];
-    float r;
-    if (MAXMODE) r = fmaxf(fmaxf(cp[0], cp[64]), fmaxf(cp[128], cp[192]));
-    else r = (cp[0] + cp[64]) + (cp[128] + cp[192]);
-    out[k0 + (int64_t)(ntiles - 1) * 64 + threadIdx.x] = r;
-  }
+  if (j0 < G.ntiles) KVC_SCORE_STEP(0, j0)
+  if (j0 + 1 < G.ntiles) KVC_SCORE_STEP(1, j0 + 1)
+  if (j0 + 2 < G.ntiles) KVC_SCORE_STEP(2, j0 + 2)
+  ring_barrier<D>(0);                        // also: no LDS fill may outlive the block
+  if (threadIdx.x < 64)
+    out[G.k0 + 64 * (G.ntiles - 1) + (int)threadIdx.x] = combine4<MAXMODE>(&cb[(G.ntiles - 1) & 1][0][threadIdx.x]);
 }
 
 // SUM: w[g][t] = sum over the group's (head, row tile) pairs that see t.  Four lanes share a
