@@ -1,14 +1,22 @@
 """Benchmark: scored+compressed KV tokens/s per layer on one MI355X.
 
 One step is one pass of the whole path over one layer's cache already resident in HBM:
-kvc_row_lse -> kvc_score_tokens(SUM) -> kvc_channel_weights -> kvc_allocate_bits(V tokens)
--> kvc_allocate_bits(K channels) -> kvc_quantize_pack.  The workload is the Llama-3-8B-like
-prefill layer (32 query heads / 8 KV heads, d = 128, N = Nq = 8192, causal, bf16, 4 outlier
-K channels per head, 3 bits/element).  value = N / (mean step time).
+  sum configs (0, 1, 2, 4): kvc_row_lse -> kvc_score_tokens(SUM) -> kvc_channel_weights
+                            -> kvc_allocate_bits(V tokens) -> kvc_allocate_bits(K channels)
+                            -> kvc_quantize_pack
+  max config (3):           kvc_row_lse -> kvc_score_tokens(MAX) -> kvc_allocate_bits(TOPK)
+                            -> kvc_quantize_pack
+The default workload is the Llama-3-8B-like prefill layer (32 query heads / 8 KV heads,
+d = 128, N = Nq = 8192, causal, bf16, 4 outlier K channels per KV head, 3 bits/element).
+value = N / (mean step time over the timed steps).
 
-Prints ONE JSON line.  `roofline` is for the dominant kernel, timed with events on the stream
-its call is enqueued on; `cpu_baseline` times the float64 oracle on a bounded sample on the
-host cores.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1]
+Prints ONE JSON line.  `roofline` is for the dominant kernel (pass 1 of the scorer,
+lse_partial), timed with HIP events recorded on the stream its call is enqueued on, inside
+the timed region.  The fidelity attend is timed after the timed region and reported apart
+(`attend`), together with a single-decode-row slice whose HBM traffic is the packed cache.
+`cpu_baseline` times the float64 oracle on a bounded sample on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1] [--no-cpu-baseline]
 """
 
 import argparse
@@ -23,48 +31,68 @@ sys.path.insert(0, ROOT)
 METRIC = "scored+compressed KV tokens/s per layer; % bf16 MFMA peak & % HBM BW"
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak (published)
+CPU_SAMPLE_SECONDS = 12.0      # oracle sample: KV heads are added until this much CPU time
 
 
 def visible_elements(N, Nq, causal=True):
+    """Visible (query row, key) pairs of one query head, row i at position N - Nq + i."""
     if not causal:
         return N * Nq
     return Nq * (N - Nq) + Nq * (Nq + 1) // 2
 
 
-def cpu_baseline(cfg_index):
-    """The oracle as it stands on one KV head of the layer (its G query heads, all rows),
-    every step of the path; the layer takes H_kv times as long."""
+def cpu_baseline(cfg):
+    """The oracle as it stands, every step of the timed path, on whole KV heads (each with
+    its G query heads and all rows) until about CPU_SAMPLE_SECONDS have passed; the layer
+    time is the per-head time times H_kv."""
     import numpy as np
     import oracle
-    from workloads import get_config, make_config_inputs
+    from workloads import make_config_inputs
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=0)
     except Exception:
         blas_threads = 0
-    cfg = get_config(cfg_index)
     x = make_config_inputs(cfg)
     G = cfg.gqa
-    q1 = np.ascontiguousarray(x["q"][:G])
-    k1 = np.ascontiguousarray(x["k"][:1])
-    v1 = np.ascontiguousarray(x["v"][:1])
-    t0 = time.perf_counter()
-    lse = oracle.row_lse(q1, k1)
-    w = oracle.token_scores_sum(q1, k1, lse)
-    wc = oracle.channel_weights(q1, k1)
-    bv, _ = oracle.allocate_v_tokens(w.astype(np.float32), cfg.avg_bits, cfg.head_dim)
-    bk, _ = oracle.allocate_k_channels(wc.astype(np.float32), bv, cfg.avg_bits)
-    oracle.pack_cache(k1, v1, bv, bk)
-    dt = time.perf_counter() - t0
-    layer_s = dt * cfg.n_kv_heads
-    cores = len(os.sched_getaffinity(0))
+    heads = 0
+    dt = 0.0
+    for g in range(cfg.n_kv_heads):
+        q1 = np.ascontiguousarray(x["q"][g * G:(g + 1) * G])
+        k1 = np.ascontiguousarray(x["k"][g:g + 1])
+        v1 = np.ascontiguousarray(x["v"][g:g + 1])
+        t0 = time.perf_counter()
+        lse = oracle.row_lse(q1, k1)
+        if cfg.mode == "sum":
+            w = oracle.token_scores_sum(q1, k1, lse)
+            wc = oracle.channel_weights(q1, k1)
+            bv, _ = oracle.allocate_v_tokens(w.astype(np.float32), cfg.avg_bits, cfg.head_dim)
+            bk, _ = oracle.allocate_k_channels(wc.astype(np.float32), bv, cfg.avg_bits)
+        else:
+            w_o = x["w_o"][:, g * G * cfg.head_dim:(g + 1) * G * cfg.head_dim]
+            s = oracle.token_scores_max(q1, k1, lse, x["hidden"], np.ascontiguousarray(w_o), v1)
+            bv = oracle.topk_keep(s.astype(np.float32), cfg.keep_fraction, 16)
+            bk = np.full((1, cfg.head_dim), 16, dtype=np.uint8)
+        oracle.pack_cache(k1, v1, bv, bk)
+        dt += time.perf_counter() - t0
+        heads += 1
+        if dt >= CPU_SAMPLE_SECONDS:
+            break
+    layer_s = dt / heads * cfg.n_kv_heads
     return {
-        "value": cfg.n_keys / layer_s, "unit": "tokens/s", "cores": cores,
-        "blas_threads": blas_threads, "kind": "oracle",
-        "sample": (f"1 of {cfg.n_kv_heads} KV heads ({G} query heads x {cfg.n_queries} rows x "
-                   f"{cfg.n_keys} keys), all six steps, float64 numpy: {dt:.2f} s; layer time "
-                   f"taken as {cfg.n_kv_heads} x sample"),
+        "value": round(cfg.n_keys / layer_s, 1), "unit": "tokens/s",
+        "cores": max(1, blas_threads), "kind": "oracle",
+        "sample": (f"{heads} of {cfg.n_kv_heads} KV heads of {cfg.name} (each: {G} query heads x "
+                   f"{cfg.n_queries} rows x {cfg.n_keys} keys), every step of the timed path in "
+                   f"float64 numpy, {dt:.2f} s; layer time = per-head time x {cfg.n_kv_heads}; "
+                   f"BLAS threads {blas_threads}, host cpus {len(os.sched_getaffinity(0))}"),
     }
+
+
+def packed_bytes_read_by_attend(hdr):
+    """Bytes of the packed cache one attend launch streams: value words and (scale, zero)
+    pairs, key words and pairs, the retained-token list and its value locations."""
+    return int(4 * hdr[5] + 8 * hdr[6] + 8 * hdr[7] + 4 * hdr[8] + 8 * hdr[9])
 
 
 def main():
@@ -76,8 +104,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(this path runs on a single GPU; see DESIGN.md for how it would shard)",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the path runs "
+              "on a single GPU (sharding by KV head or key range is a design note only)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -87,15 +115,16 @@ def main():
     from workloads import get_config, make_config_inputs
 
     cfg = get_config(args.config)
-    if cfg.mode != "sum":
-        print("bench.py times the sum-score path (configs 0, 1, 2, 4)", file=sys.stderr)
-        sys.exit(2)
     kvc.load()
     dev = "cuda:0"
     torch.cuda.set_device(0)
     hq, hkv, d, N, Nq = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_keys, cfg.n_queries
     x = make_config_inputs(cfg)
     q, k, v = (kvc.bf16_tensor(x[n], dev) for n in ("q", "k", "v"))
+    hidden = w_o = None
+    if cfg.mode == "max":
+        hidden = kvc.bf16_tensor(x["hidden"], dev)
+        w_o = kvc.bf16_tensor(x["w_o"], dev)
     del x
     desc = kvc.make_desc(hq, hkv, d, N, Nq, True)
     lse = torch.empty(hq, Nq, dtype=torch.float32, device=dev)
@@ -103,76 +132,122 @@ def main():
     wc = torch.empty(hkv, d, dtype=torch.float32, device=dev)
     bv = torch.empty(hkv, N, dtype=torch.uint8, device=dev)
     bk = torch.empty(hkv, d, dtype=torch.uint8, device=dev)
+    mode = kvc.SCORE_SUM if cfg.mode == "sum" else kvc.SCORE_MAX
     ws_l = kvc.workspace(kvc.OP_ROW_LSE, desc, 0, dev)
-    ws_s = kvc.workspace(kvc.OP_SCORE_TOKENS, desc, kvc.SCORE_SUM, dev)
-    ws_c = kvc.workspace(kvc.OP_CHANNEL_WEIGHTS, desc, 0, dev)
-    ws_v = kvc.workspace(kvc.OP_ALLOCATE_BITS, desc, kvc.ALLOC_V_TOKENS, dev)
-    ws_k = kvc.workspace(kvc.OP_ALLOCATE_BITS, desc, kvc.ALLOC_K_CHANNELS, dev)
+    ws_s = kvc.workspace(kvc.OP_SCORE_TOKENS, desc, mode, dev)
     ws_p = kvc.workspace(kvc.OP_QUANTIZE_PACK, desc, 0, dev)
     res_v = kvc.alloc_result_buffer(dev)
     res_k = kvc.alloc_result_buffer(dev)
     cache = kvc.PackedCache(desc, dev)
     stream = torch.cuda.current_stream()
 
-    calls = [
-        ("row_lse", lambda: kvc.kvc_row_lse(desc, q, k, lse, ws_l, stream=stream)),
-        ("score_tokens", lambda: kvc.kvc_score_tokens(desc, kvc.SCORE_SUM, q, k, lse, w, ws_s, stream=stream)),
-        ("channel_weights", lambda: kvc.kvc_channel_weights(desc, q, k, wc, ws_c, stream=stream)),
-        ("allocate_v", lambda: kvc.kvc_allocate_bits(desc, kvc.ALLOC_V_TOKENS, w, bv, ws_v,
-                                                     avg_bits=cfg.avg_bits, result=res_v, stream=stream)),
-        ("allocate_k", lambda: kvc.kvc_allocate_bits(desc, kvc.ALLOC_K_CHANNELS, wc, bk, ws_k, bits_v=bv,
-                                                     avg_bits=cfg.avg_bits, result=res_k, stream=stream)),
-        ("quantize_pack", lambda: kvc.kvc_quantize_pack(desc, k, v, bv, bk, cache, ws_p, stream=stream)),
-    ]
+    calls = [("row_lse", lambda: kvc.kvc_row_lse(desc, q, k, lse, ws_l, stream=stream))]
+    if cfg.mode == "sum":
+        ws_c = kvc.workspace(kvc.OP_CHANNEL_WEIGHTS, desc, 0, dev)
+        ws_v = kvc.workspace(kvc.OP_ALLOCATE_BITS, desc, kvc.ALLOC_V_TOKENS, dev)
+        ws_k = kvc.workspace(kvc.OP_ALLOCATE_BITS, desc, kvc.ALLOC_K_CHANNELS, dev)
+        calls += [
+            ("score_tokens", lambda: kvc.kvc_score_tokens(desc, mode, q, k, lse, w, ws_s, stream=stream)),
+            ("channel_weights", lambda: kvc.kvc_channel_weights(desc, q, k, wc, ws_c, stream=stream)),
+            ("allocate_v", lambda: kvc.kvc_allocate_bits(desc, kvc.ALLOC_V_TOKENS, w, bv, ws_v,
+                                                         avg_bits=cfg.avg_bits, result=res_v, stream=stream)),
+            ("allocate_k", lambda: kvc.kvc_allocate_bits(desc, kvc.ALLOC_K_CHANNELS, wc, bk, ws_k, bits_v=bv,
+                                                         avg_bits=cfg.avg_bits, result=res_k, stream=stream)),
+        ]
+    else:
+        ws_t = kvc.workspace(kvc.OP_ALLOCATE_BITS, desc, kvc.ALLOC_TOPK, dev)
+        bk.fill_(16)
+        calls += [
+            ("score_tokens", lambda: kvc.kvc_score_tokens(desc, mode, q, k, lse, w, ws_s, hidden=hidden,
+                                                          w_o=w_o, v=v, stream=stream)),
+            ("allocate_topk", lambda: kvc.kvc_allocate_bits(desc, kvc.ALLOC_TOPK, w, bv, ws_t,
+                                                            keep_fraction=cfg.keep_fraction, keep_bits=16,
+                                                            result=res_v, stream=stream)),
+        ]
+    calls.append(("quantize_pack", lambda: kvc.kvc_quantize_pack(desc, k, v, bv, bk, cache, ws_p, stream=stream)))
 
     def step(events=None):
         for i, (_, fn) in enumerate(calls):
-            if events is not None:
+            if events is not None and events[i] is not None:
                 events[i][0].record(stream)
             fn()
-            if events is not None:
+            if events is not None and events[i] is not None:
                 events[i][1].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region: whole steps only
+    # timed region: K whole steps; events around the dominant call (row_lse) of every step
+    ev_dom = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
-    for _ in range(args.steps):
-        step()
+    for s in range(args.steps):
+        step([ev_dom[s]] + [None] * (len(calls) - 1))
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    lse_ms = sum(a.elapsed_time(b) for a, b in ev_dom) / args.steps
 
-    # per-call durations over the same number of steps (events around each call's launches)
-    per_call = {name: 0.0 for name, _ in calls}
+    # per-call breakdown and per-step median over the same number of steps (not timed above)
+    per_call = {name: [] for name, _ in calls}
+    step_ms = []
     for _ in range(args.steps):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
         step(ev)
         torch.cuda.synchronize()
         for (name, _), (a, b) in zip(calls, ev):
-            per_call[name] += a.elapsed_time(b) / args.steps
+            per_call[name].append(a.elapsed_time(b))
+        step_ms.append(ev[0][0].elapsed_time(ev[-1][1]))
 
-    alloc_v = kvc.decode_alloc_result(res_v)
-    alloc_k = kvc.decode_alloc_result(res_k)
     hdr = cache.header()
-
-    # dominant kernel: pass 1.  For this workload (1024 head x row-tile blocks) kvc_row_lse
-    # is a single launch of lse_partial, so events around the call time that kernel.
     flops = 2.0 * d * visible_elements(N, Nq) * hq
-    lse_ms = per_call["row_lse"]
     achieved = flops / (lse_ms * 1e-3) / 1e12
     roofline = {
-        "kernel": "lse_partial", "bound": "mfma", "achieved": round(achieved, 2),
-        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-        "traffic": None,
-        "flops_per_launch": flops, "avg_launch_ms": round(lse_ms, 5),
+        "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+        "kernel": "lse_partial", "flops_per_launch": flops, "avg_launch_ms": round(lse_ms, 5),
     }
-    score_flops = flops
+
+    # fidelity attend on the configuration's fidelity rows (the last rows of Q), and a
+    # single-decode-row slice: one row per query head over the whole packed cache
+    bv_h = bv.cpu().numpy()
+    attend = {}
+    for label, rows in (("fidelity", cfg.fidelity_rows), ("decode_row", 1)):
+        rows = min(rows, Nq)
+        desc_f = kvc.make_desc(hq, hkv, d, N, rows, True)
+        q_f = q[:, Nq - rows:, :].contiguous()
+        out_f = torch.empty(hq, rows, d, dtype=torch.float32, device=dev)
+        lse_f = torch.empty(hq, rows, dtype=torch.float32, device=dev)
+        ws_a = kvc.workspace(kvc.OP_COMPRESSED_ATTEND, desc_f, 0, dev)
+        fn = lambda: kvc.kvc_compressed_attend(desc_f, q_f, cache, out_f, lse_f, ws_a, stream=stream)
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        reps = max(args.steps, 10)
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(reps):
+            fn()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        ms = a0.elapsed_time(a1) / reps
+        # retained keys visible to each row, per KV head: rows at positions N - rows + i
+        ret = np.cumsum(bv_h > 0, axis=1)
+        pos = np.arange(N - rows, N)
+        vis = int(ret[:, pos].sum()) * (hq // hkv)
+        a_flops = 4.0 * d * vis
+        a_bytes = packed_bytes_read_by_attend(hdr) + 2 * q_f.numel() + 4 * (out_f.numel() + lse_f.numel())
+        attend[label] = {"rows": rows, "ms": round(ms, 5),
+                         "tflops": round(a_flops / (ms * 1e-3) / 1e12, 2),
+                         "gbs": round(a_bytes / (ms * 1e-3) / 1e9, 1),
+                         "hbm_frac": round(a_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                         "bytes": a_bytes, "flops": a_flops}
+
     out = {
         "metric": METRIC,
         "value": round(N / (ms_per_step * 1e-3), 1),
@@ -187,16 +262,21 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": cfg.name, "n_q_heads": hq, "n_kv_heads": hkv, "head_dim": d,
-                   "n_keys": N, "n_queries": Nq, "causal": True, "avg_bits": cfg.avg_bits},
+                   "n_keys": N, "n_queries": Nq, "causal": True, "score": cfg.mode,
+                   "avg_bits": cfg.avg_bits, "keep_fraction": cfg.keep_fraction},
         "roofline": roofline,
-        "per_call_ms": {n: round(t, 5) for n, t in per_call.items()},
-        "score_pass2_call_tflops": round(score_flops / (per_call["score_tokens"] * 1e-3) / 1e12, 2),
-        "alloc": {"v_lambda": alloc_v["lam"], "v_used_bits": alloc_v["used"], "v_budget": alloc_v["budget"],
-                  "k_lambda": alloc_k["lam"], "k_used_bits": alloc_k["used"], "k_budget": alloc_k["budget"],
-                  "retained_tokens": int(hdr[7])},
+        "ms_per_step_median": round(float(np.median(step_ms)), 5),
+        "per_call_ms": {n: round(float(np.mean(t)), 5) for n, t in per_call.items()},
+        "score_pass2_call_tflops": round(flops / (np.mean(per_call["score_tokens"]) * 1e-3) / 1e12, 2),
+        "attend": attend,
+        "retained_tokens": int(hdr[7]),
     }
+    if cfg.mode == "sum":
+        av, ak = kvc.decode_alloc_result(res_v), kvc.decode_alloc_result(res_k)
+        out["alloc"] = {"v_lambda": av["lam"], "v_used_bits": av["used"], "v_budget": av["budget"],
+                        "k_lambda": ak["lam"], "k_used_bits": ak["used"], "k_budget": ak["budget"]}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.config)
+        out["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(out), flush=True)
 
 

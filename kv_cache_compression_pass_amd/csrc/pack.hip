@@ -2,15 +2,19 @@
 // allocated width from {0,2,4,8,16}, width 0 evicts; §2.3: rows grouped by width so each
 // width has one dequantisation path).  The byte layout is documented in kvc.h.
 //
-// Kernels, all on one stream:
+// Kernels, all on one stream (kernel boundaries order every step):
 //   pack_count   per (1024-token chunk, head): tokens per width zone; width validation
-//   pack_layout  one block: per-chunk zone bases, the header, the k_width copy
+//   pack_layout  per head: chunk bases (block scan), K-channel word/param offsets and the
+//                channels sorted by width, per-head totals
+//   pack_header  one block: head offsets (scans over heads), the header, the status word
 //   pack_index   per chunk: ordered ranks -> v_idx, k_keep, k_vloc
-//   pack_kv      one block per (32 retained tokens, head): quantise every K channel and
-//                every V group of those tokens
-// The quantiser does its division in float64 exactly as the definition reads
-// (z = min, s = float32(float64(max - min) / (2^b - 1)), code = rint(float64(x - z) / s)), so
-// codes, scales and zeros are bit-exact against a float64 reference.
+//   pack_units   z = 0: one block per (32 retained tokens, head) quantises every K channel;
+//                z = 1: one block per 32 tokens of one width zone quantises their V groups
+// Codes follow the definition z = min, s = float32(float64(max - min) / (2^b - 1)),
+// code = clamp(rint(float64(x - z) / s)).  The kernel evaluates v = (x - z) / s in fp32, whose
+// error is below 5e-5 for every v <= 255.5; only where v lies within 1e-4 of a rounding
+// boundary (k + 1/2) can fp32 and fp64 round differently, and there the code is recomputed
+// with the fp64 division.  Codes, scales and zeros are therefore bit-exact.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -21,126 +25,244 @@ namespace {
 constexpr int kChunk = 1024;      // tokens per index chunk (256 threads x 4)
 
 struct PackWs {
-  int32_t* status;
+  int32_t* status;     // word 0 of the workspace
   int32_t* cnt;        // [Hkv][nchunk][4]  tokens per zone in each chunk
+  int32_t* cbad;       // [Hkv][nchunk]     invalid token widths seen in the chunk
   int64_t* base;       // [Hkv][nchunk][4]  zone position of each chunk's first token
-  int64_t* rbase;      // [Hkv][nchunk]     retained index of each chunk's first token
+  int64_t* rbase;      // [Hkv][nchunk]     retained rank of each chunk's first token
+  int64_t* htot;       // [Hkv][8]          tokens per zone (4), R, K words per group, K params per group, bad
+  int32_t* kch;        // [Hkv][D][4]       channels of nonzero width sorted by width:
+                       //                   {channel, word offset, param slot, width}
 };
 
 __device__ __forceinline__ int zone_of(uint32_t b) {
   return b == 2 ? 0 : b == 4 ? 1 : b == 8 ? 2 : b == 16 ? 3 : -1;
 }
 
+// Exclusive prefix sum of one uint64 per thread over a block of NT threads (NT % 64 == 0);
+// *total receives the block total.  sh holds NT / 64 entries.  Every thread must call it.
+template <int NT>
+__device__ __forceinline__ uint64_t block_excl_scan(uint64_t v, uint64_t* total, uint64_t* sh) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint64_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t lo = __shfl_up((uint32_t)x, o, 64), hi = __shfl_up((uint32_t)(x >> 32), o, 64);
+    if (lane >= o) x += ((uint64_t)hi << 32) | lo;
+  }
+  if (lane == 63) sh[wid] = x;
+  __syncthreads();
+  if (wid == 0) {
+    uint64_t y = lane < NW ? sh[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < NW; o <<= 1) {
+      const uint32_t lo = __shfl_up((uint32_t)y, o, 64), hi = __shfl_up((uint32_t)(y >> 32), o, 64);
+      if (lane >= o) y += ((uint64_t)hi << 32) | lo;
+    }
+    if (lane < NW) sh[lane] = y;       // inclusive wave totals
+  }
+  __syncthreads();
+  const uint64_t r = (wid > 0 ? sh[wid - 1] : 0) + x - v;
+  *total = sh[NW - 1];
+  __syncthreads();                     // sh may be reused by the caller's next scan
+  return r;
+}
+
 __global__ void __launch_bounds__(256)
-pack_count(const uint8_t* __restrict__ bits_v, const uint8_t* __restrict__ bits_k, int64_t N,
-           int d, int nchunk, int32_t* __restrict__ cnt, int32_t* status) {
+pack_count(const uint8_t* __restrict__ bits_v, int64_t N, int nchunk, int32_t* __restrict__ cnt,
+           int32_t* __restrict__ cbad) {
   const int ch = blockIdx.x, g = blockIdx.y;
   __shared__ int32_t c4[4];
+  __shared__ int32_t bad_s;
   if (threadIdx.x < 4) c4[threadIdx.x] = 0;
+  if (threadIdx.x == 0) bad_s = 0;
   __syncthreads();
   int my[4] = {0, 0, 0, 0};
   bool bad = false;
-  const int64_t t0 = (int64_t)ch * kChunk;
+  const int64_t t0 = (int64_t)ch * kChunk + threadIdx.x * 4;
+  uint32_t b4 = 0;
+  if (t0 + 3 < N && (reinterpret_cast<uintptr_t>(bits_v + (int64_t)g * N + t0) & 3) == 0) {
+    b4 = *reinterpret_cast<const uint32_t*>(bits_v + (int64_t)g * N + t0);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (t0 + j < N) b4 |= (uint32_t)bits_v[(int64_t)g * N + t0 + j] << (8 * j);
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    int64_t t = t0 + threadIdx.x * 4 + j;
-    if (t < N) {
-      uint32_t b = bits_v[(int64_t)g * N + t];
+    if (t0 + j < N) {
+      const uint32_t b = (b4 >> (8 * j)) & 0xFFu;
       bad |= !valid_width(b);
-      int z = zone_of(b);
+      const int z = zone_of(b);
       if (z >= 0) my[z]++;
     }
   }
-  if (ch == 0 && (int)threadIdx.x < d) bad |= !valid_width(bits_k[(int64_t)g * d + threadIdx.x]);
-  if (bad) set_status(status, KVC_DEV_BAD_WIDTH);
+  if (bad) bad_s = 1;                  // benign race: every writer stores 1
 #pragma unroll
   for (int z = 0; z < 4; ++z)
     if (my[z]) atomicAdd(&c4[z], my[z]);     // integer: order-independent
   __syncthreads();
   if (threadIdx.x < 4) cnt[((int64_t)g * nchunk + ch) * 4 + threadIdx.x] = c4[threadIdx.x];
+  if (threadIdx.x == 0) cbad[(int64_t)g * nchunk + ch] = bad_s;
 }
 
-// Header and per-chunk bases.  One block: threads (g, z) scan their chunks, the K-channel
-// widths are summed per head in parallel, then thread 0 lays the heads out in order.
+// One block of 1024 threads per KV head.
+//  1. chunk bases: the four zone counts travel as two uint64 words with 32-bit fields (a field
+//     never exceeds N < 2^29), so one block scan per word gives every zone's prefix;
+//  2. K channels: one uint64 per channel packs {words (16 bits), params (16 bits), one 8-bit
+//     count per width class}; one scan gives each channel's word offset, param slot and rank
+//     in its width class, hence its place in the width-sorted channel list.
+template <int D>
 __global__ void __launch_bounds__(1024)
-pack_layout(const int32_t* __restrict__ cnt, const uint8_t* __restrict__ bits_k, int Hkv, int d,
-            int64_t N, int nchunk, int64_t* __restrict__ base, int64_t* __restrict__ rbase,
-            int64_t* __restrict__ header, uint8_t* __restrict__ k_width) {
-  __shared__ int64_t tot[1024];      // tokens per (g, z)
-  __shared__ int32_t wk_s[256], qk_s[256];
-  const int tid = threadIdx.x;
-  for (int g = tid; g < Hkv; g += blockDim.x) {
-    wk_s[g] = 0;
-    qk_s[g] = 0;
-  }
-  for (int gz = tid; gz < Hkv * 4; gz += blockDim.x) {
-    const int g = gz / 4, z = gz % 4;
-    int64_t run = 0;
-    for (int ch = 0; ch < nchunk; ++ch) {
-      base[((int64_t)g * nchunk + ch) * 4 + z] = run;
-      run += cnt[((int64_t)g * nchunk + ch) * 4 + z];
+pack_layout(const int32_t* __restrict__ cnt, const int32_t* __restrict__ cbad,
+            const uint8_t* __restrict__ bits_k, int64_t N, int nchunk, int64_t* __restrict__ base,
+            int64_t* __restrict__ rbase, int64_t* __restrict__ htot, int32_t* __restrict__ kch,
+            uint8_t* __restrict__ k_width) {
+  __shared__ uint64_t sh[16];
+  __shared__ int32_t bad_s;
+  const int g = blockIdx.x, tid = threadIdx.x;
+  if (tid == 0) bad_s = 0;
+  uint64_t carry01 = 0, carry23 = 0;
+  bool bad = false;
+  for (int c0 = 0; c0 < nchunk; c0 += 1024) {
+    const int ch = c0 + tid;
+    int4 c = make_int4(0, 0, 0, 0);
+    if (ch < nchunk) {
+      c = *reinterpret_cast<const int4*>(cnt + ((int64_t)g * nchunk + ch) * 4);
+      bad |= cbad[(int64_t)g * nchunk + ch] != 0;
     }
-    tot[gz] = run;
+    const uint64_t a = (uint32_t)c.x | ((uint64_t)(uint32_t)c.y << 32);
+    const uint64_t b = (uint32_t)c.z | ((uint64_t)(uint32_t)c.w << 32);
+    uint64_t ta, tb;
+    const uint64_t ea = block_excl_scan<1024>(a, &ta, sh) + carry01;
+    const uint64_t eb = block_excl_scan<1024>(b, &tb, sh) + carry23;
+    if (ch < nchunk) {
+      const int64_t z0 = (int64_t)(ea & 0xFFFFFFFFu), z1 = (int64_t)(ea >> 32);
+      const int64_t z2 = (int64_t)(eb & 0xFFFFFFFFu), z3 = (int64_t)(eb >> 32);
+      int64_t* bp = base + ((int64_t)g * nchunk + ch) * 4;
+      bp[0] = z0;
+      bp[1] = z1;
+      bp[2] = z2;
+      bp[3] = z3;
+      rbase[(int64_t)g * nchunk + ch] = z0 + z1 + z2 + z3;
+    }
+    carry01 += ta;
+    carry23 += tb;
   }
-  for (int g = tid; g < Hkv; g += blockDim.x) {
-    int64_t run = 0;
-    for (int ch = 0; ch < nchunk; ++ch) {
-      rbase[(int64_t)g * nchunk + ch] = run;
-      const int32_t* cc = cnt + ((int64_t)g * nchunk + ch) * 4;
-      run += (int64_t)cc[0] + cc[1] + cc[2] + cc[3];
+  // K channels
+  uint32_t bk = 0;
+  int cls = 4;
+  uint64_t f = 0;
+  if (tid < D) {
+    bk = bits_k[(int64_t)g * D + tid];
+    k_width[(int64_t)g * D + tid] = (uint8_t)bk;
+    bad |= !valid_width(bk);
+    cls = zone_of(bk);
+    if (cls < 0) cls = 4;                              // width 0 (or invalid): not stored
+    if (cls < 4) {
+      f = (uint64_t)bk | ((uint64_t)(cls < 3) << 16) | (1ull << (32 + 8 * cls));
     }
   }
-  __syncthreads();
-  for (int e = tid; e < Hkv * d; e += blockDim.x) {
-    const uint32_t b = bits_k[e];
-    k_width[e] = (uint8_t)b;
-    if (valid_width(b) && b) atomicAdd(&wk_s[e / d], (int32_t)b);   // integer sums: order-free
-    if (b == 2 || b == 4 || b == 8) atomicAdd(&qk_s[e / d], 1);
+  uint64_t tf;
+  const uint64_t ef = block_excl_scan<1024>(f, &tf, sh);
+  if (tid < D) {
+    // place: channels of smaller width classes first, then rank inside the class; channels
+    // of width 0 (or an invalid width) follow all the others
+    int pos = 0, before = 0, nnz = 0;
+    for (int k2 = 0; k2 < 4; ++k2) {
+      const int tk = (int)((tf >> (32 + 8 * k2)) & 0xFF);
+      if (k2 < cls) pos += tk;
+      before += (int)((ef >> (32 + 8 * k2)) & 0xFF);
+      nnz += tk;
+    }
+    pos = cls < 4 ? pos + (int)((ef >> (32 + 8 * cls)) & 0xFF) : nnz + (tid - before);
+    int32_t* e = kch + ((int64_t)g * D + pos) * 4;
+    e[0] = tid;
+    e[1] = (int32_t)(ef & 0xFFFF);
+    e[2] = (int32_t)((ef >> 16) & 0xFFFF);
+    e[3] = cls < 4 ? (int32_t)bk : 0;
   }
-  for (int i = tid; i < KVC_HDR_GLOBAL + Hkv * KVC_HDR_PER_HEAD; i += blockDim.x) header[i] = 0;
+  if (bad) bad_s = 1;
   __syncthreads();
   if (tid == 0) {
-    const int gpr = d / 32;
-    const int widths[4] = {2, 4, 8, 16};
-    int64_t o_vi = 0, o_vw = 0, o_vp = 0, o_kk = 0, o_kw = 0, o_kp = 0;
+    int64_t* h = htot + (int64_t)g * 8;
+    h[0] = (int64_t)(carry01 & 0xFFFFFFFFu);
+    h[1] = (int64_t)(carry01 >> 32);
+    h[2] = (int64_t)(carry23 & 0xFFFFFFFFu);
+    h[3] = (int64_t)(carry23 >> 32);
+    h[4] = h[0] + h[1] + h[2] + h[3];
+    h[5] = (int64_t)(tf & 0xFFFF);                        // K words per 32-token group
+    h[6] = (int64_t)((tf >> 16) & 0xFFFF);                // quantised K channels
+    h[7] = bad_s;
+  }
+}
+
+// One block of 256 threads: thread g lays out head g (heads in order, zones in order inside a
+// head), by exclusive scans over heads of each head's sizes.
+__global__ void __launch_bounds__(256)
+pack_header(const int64_t* __restrict__ htot, int Hkv, int d, int64_t N,
+            int64_t* __restrict__ header, int32_t* __restrict__ status) {
+  __shared__ uint64_t sh[4];
+  __shared__ int32_t bad_s;
+  const int g = threadIdx.x;
+  const int gpr = d / 32;
+  if (g == 0) bad_s = 0;
+  __syncthreads();
+  int64_t nv[4] = {0, 0, 0, 0}, R = 0, wk = 0, qk = 0, ng = 0;
+  if (g < Hkv) {
+    const int64_t* h = htot + (int64_t)g * 8;
+    for (int z = 0; z < 4; ++z) nv[z] = h[z];
+    R = h[4];
+    wk = h[5];
+    qk = h[6];
+    ng = (R + 31) / 32;
+    if (h[7]) bad_s = 1;
+  }
+  const int64_t vw[4] = {nv[0] * gpr * 2, nv[1] * gpr * 4, nv[2] * gpr * 8, nv[3] * gpr * 16};
+  const int64_t vp[3] = {nv[0] * gpr, nv[1] * gpr, nv[2] * gpr};
+  uint64_t t_vi, t_vw, t_vp, t_kw, t_kp;
+  const int64_t o_vi = (int64_t)block_excl_scan<256>((uint64_t)R, &t_vi, sh);
+  const int64_t o_vw = (int64_t)block_excl_scan<256>((uint64_t)(vw[0] + vw[1] + vw[2] + vw[3]), &t_vw, sh);
+  const int64_t o_vp = (int64_t)block_excl_scan<256>((uint64_t)(vp[0] + vp[1] + vp[2]), &t_vp, sh);
+  const int64_t o_kw = (int64_t)block_excl_scan<256>((uint64_t)(ng * wk), &t_kw, sh);
+  const int64_t o_kp = (int64_t)block_excl_scan<256>((uint64_t)(ng * qk), &t_kp, sh);
+  if (g < Hkv) {
+    int64_t* hp = header + KVC_HDR_GLOBAL + g * KVC_HDR_PER_HEAD;
+    int64_t a = o_vi, b = o_vw, c = o_vp;
+    for (int z = 0; z < 4; ++z) {
+      hp[z] = nv[z];
+      hp[5 + z] = a;
+      hp[9 + z] = b;
+      hp[13 + z] = c;
+      a += nv[z];
+      b += vw[z];
+      c += (z < 3) ? vp[z] : 0;
+    }
+    hp[4] = R;
+    hp[17] = o_vi;          // k_keep lists the same R tokens per head, in the same head order
+    hp[18] = o_kw;
+    hp[19] = o_kp;
+    hp[20] = wk;
+    hp[21] = qk;
+    hp[22] = ng;
+    hp[23] = 0;
+  }
+  if (g == 0) {
     header[0] = Hkv;
     header[1] = d;
     header[2] = N;
     header[3] = 32;
-    for (int g = 0; g < Hkv; ++g) {
-      int64_t* hp = header + KVC_HDR_GLOBAL + g * KVC_HDR_PER_HEAD;
-      int64_t R = 0;
-      for (int z = 0; z < 4; ++z) {
-        const int64_t nv = tot[g * 4 + z];
-        hp[z] = nv;
-        hp[5 + z] = o_vi;
-        hp[9 + z] = o_vw;
-        hp[13 + z] = o_vp;
-        o_vi += nv;
-        o_vw += nv * gpr * widths[z];
-        o_vp += (z < 3) ? nv * gpr : 0;
-        R += nv;
-      }
-      const int64_t wk = wk_s[g], qk = qk_s[g];
-      const int64_t ng = (R + 31) / 32;
-      hp[4] = R;
-      hp[17] = o_kk;
-      hp[18] = o_kw;
-      hp[19] = o_kp;
-      hp[20] = wk;
-      hp[21] = qk;
-      hp[22] = ng;
-      o_kk += R;
-      o_kw += ng * wk;
-      o_kp += ng * qk;
-    }
-    header[4] = o_vi;
-    header[5] = o_vw;
-    header[6] = o_vp;
-    header[7] = o_kk;
-    header[8] = o_kw;
-    header[9] = o_kp;
+    header[4] = (int64_t)t_vi;
+    header[5] = (int64_t)t_vw;
+    header[6] = (int64_t)t_vp;
+    header[7] = (int64_t)t_vi;
+    header[8] = (int64_t)t_kw;
+    header[9] = (int64_t)t_kp;
+    for (int i = 10; i < KVC_HDR_GLOBAL; ++i) header[i] = 0;
   }
+  __syncthreads();
+  if (g == 0) *status = bad_s ? KVC_DEV_BAD_WIDTH : 0;
 }
 
 // Ordered ranks inside each chunk: the four zone counters of a thread's 4 tokens are packed
@@ -160,17 +282,9 @@ pack_index(const uint8_t* __restrict__ bits_v, int64_t N, int nchunk,
     z4[j] = (t < N) ? zone_of(bits_v[(int64_t)g * N + t]) : -1;
     if (z4[j] >= 0) mine += 1ull << (16 * z4[j]);
   }
-  __shared__ uint64_t sc[256];
-  const int i = threadIdx.x;
-  sc[i] = mine;
-  __syncthreads();
-  for (int w = 1; w < 256; w <<= 1) {
-    uint64_t add = (i >= w) ? sc[i - w] : 0;
-    __syncthreads();
-    sc[i] += add;
-    __syncthreads();
-  }
-  uint64_t run = sc[i] - mine;        // exclusive
+  __shared__ uint64_t sh[4];
+  uint64_t total;
+  uint64_t run = block_excl_scan<256>(mine, &total, sh);
   const int64_t* hp = header + KVC_HDR_GLOBAL + g * KVC_HDR_PER_HEAD;
   const int64_t* bz = base + ((int64_t)g * nchunk + ch) * 4;
   const int64_t kbase = hp[17] + rbase[(int64_t)g * nchunk + ch];
@@ -189,117 +303,116 @@ pack_index(const uint8_t* __restrict__ bits_v, int64_t N, int nchunk,
   }
 }
 
-// Quantise one group held as 32 float32 bf16 values (m of them valid) at width b in {2,4,8}.
-__device__ __forceinline__ void quantize32(const float (&x)[32], int m, int b, uint32_t (&w)[8],
-                                           float* s_out, float* z_out) {
+// Quantise one group of 32 values (the first m valid; the rest code 0) at width B and store
+// its B words and its (scale, zero) pair.
+template <int B>
+__device__ __forceinline__ void quantize_store(const float (&x)[32], int m, uint32_t* __restrict__ dst,
+                                               float* __restrict__ par) {
+  constexpr float maxc = (float)((1 << B) - 1);
   float mn = x[0], mx = x[0];
-  for (int e = 1; e < m; ++e) {
-    mn = fminf(mn, x[e]);
-    mx = fmaxf(mx, x[e]);
-  }
-  const double range = (double)mx - (double)mn;
-  const float s = (float)(range / (double)((1 << b) - 1));
-  const double sd = (double)s;
-  const double maxc = (double)((1 << b) - 1);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) w[i] = 0u;
-  const int per = 32 / b;
-#pragma unroll
-  for (int e = 0; e < 32; ++e) {
-    uint32_t code = 0;
-    if (e < m && s != 0.f) {
-      double v = ((double)x[e] - (double)mn) / sd;
-      double r = rint(v);
-      r = r < 0.0 ? 0.0 : (r > maxc ? maxc : r);
-      code = (uint32_t)r;
+  for (int e = 1; e < 32; ++e) {
+    if (e < m) {
+      mn = fminf(mn, x[e]);
+      mx = fmaxf(mx, x[e]);
     }
-    w[e / per] |= code << ((e % per) * b);
   }
-  *s_out = s;
-  *z_out = mn;
+  const float s = (float)(((double)mx - (double)mn) / (double)((1 << B) - 1));
+  uint32_t w[B];
+#pragma unroll
+  for (int i = 0; i < B; ++i) w[i] = 0u;
+  if (s != 0.f) {
+    const float rs = 1.0f / s;
+    const bool fast = __builtin_isfinite(rs);
+    const double sd = (double)s;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const float v = (x[e] - mn) * rs;
+      float r = rintf(v);
+      if (!fast || fabsf(fabsf(v - r) - 0.5f) < 1e-4f) {
+        // near a rounding boundary: decide with the defining fp64 division
+        const double vd = rint(((double)x[e] - (double)mn) / sd);
+        r = (float)(vd < 0.0 ? 0.0 : (vd > (double)maxc ? (double)maxc : vd));
+      }
+      r = __builtin_amdgcn_fmed3f(r, 0.f, maxc);
+      const uint32_t code = (e < m) ? (uint32_t)r : 0u;
+      w[(e * B) / 32] |= code << ((e * B) % 32);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < B; ++i) dst[i] = w[i];
+  *reinterpret_cast<float2*>(par) = make_float2(s, mn);
 }
 
-// One block per (group of 32 retained tokens j, head g), 2*D threads: thread c < D quantises
-// K channel c over the 32 tokens (group-major words), thread D + i quantises V group
-// i % (D/32) of token i / (D/32).  Every thread handles one 32-element group.
+// K: block (group j of 32 retained tokens, head g) with D threads; thread i takes the i-th
+// channel of nonzero width in width order, so a wave's lanes mostly share one width.
 template <int D>
-__global__ void __launch_bounds__(2 * D)
-pack_kv(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t N,
-        const int64_t* __restrict__ header, const uint8_t* __restrict__ bits_k,
-        const int32_t* __restrict__ k_keep, const int32_t* __restrict__ k_vloc,
-        uint32_t* __restrict__ k_words, float* __restrict__ k_par, uint32_t* __restrict__ v_words,
-        float* __restrict__ v_par) {
-  constexpr int GPR = D / 32;
-  const int g = blockIdx.y;
-  const int64_t jg = blockIdx.x;
-  const int64_t* hp = header + KVC_HDR_GLOBAL + g * KVC_HDR_PER_HEAD;
+__device__ __forceinline__ void pack_k_group(const uint16_t* __restrict__ k, int64_t N, int g, int64_t j,
+                                             const int64_t* __restrict__ hp, const int32_t* __restrict__ kch,
+                                             const int32_t* __restrict__ k_keep,
+                                             uint32_t* __restrict__ k_words, float* __restrict__ k_par) {
   const int64_t R = hp[4];
-  if (jg * 32 >= R) return;
-  const int m = (int)((R - jg * 32) < 32 ? (R - jg * 32) : 32);
+  if (j * 32 >= R) return;
+  const int m = (int)((R - j * 32) < 32 ? (R - j * 32) : 32);
   __shared__ uint16_t tile[32][D + 2];
-  __shared__ int32_t woff[D], qslot[D], tok[32], vloc[32];
+  __shared__ int32_t tok[32];
   const int tid = threadIdx.x;
-  if (tid < 32) {
-    tok[tid] = tid < m ? k_keep[hp[17] + jg * 32 + tid] : 0;
-    vloc[tid] = tid < m ? k_vloc[hp[17] + jg * 32 + tid] : 0;
-  }
-  if (tid == 32) {
-    int32_t wo = 0, qs = 0;
-    for (int c = 0; c < D; ++c) {
-      const int b = bits_k[(int64_t)g * D + c];
-      woff[c] = wo;
-      qslot[c] = qs;
-      wo += valid_width(b) ? b : 0;
-      qs += (b == 2 || b == 4 || b == 8);
-    }
-  }
+  if (tid < 32) tok[tid] = tid < m ? k_keep[hp[17] + j * 32 + tid] : 0;
   __syncthreads();
-  // stage the retained K rows (16-byte loads)
-  for (int e = tid; e < 32 * (D / 8); e += 2 * D) {
+  for (int e = tid; e < 32 * (D / 8); e += D) {
     const int r = e / (D / 8), c8 = e % (D / 8);
     uint4 val = make_uint4(0, 0, 0, 0);
     if (r < m) val = *reinterpret_cast<const uint4*>(k + ((int64_t)g * N + tok[r]) * D + c8 * 8);
-    const uint32_t vv[4] = {val.x, val.y, val.z, val.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      tile[r][c8 * 8 + 2 * i] = (uint16_t)(vv[i] & 0xFFFFu);
-      tile[r][c8 * 8 + 2 * i + 1] = (uint16_t)(vv[i] >> 16);
-    }
+    uint32_t* tw = reinterpret_cast<uint32_t*>(&tile[r][c8 * 8]);
+    tw[0] = val.x;
+    tw[1] = val.y;
+    tw[2] = val.z;
+    tw[3] = val.w;
   }
   __syncthreads();
-  float x[32];
-  uint32_t w[8];
-  float sc, zz;
-  if (tid < D) {
-    const int c = tid;
-    const int b = bits_k[(int64_t)g * D + c];
-    if (b == 0 || !valid_width(b)) return;
-    uint32_t* dst = k_words + hp[18] + jg * hp[20] + woff[c];
-    if (b == 16) {
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t lo16 = (2 * i < m) ? tile[2 * i][c] : 0u;
-        const uint32_t hi16 = (2 * i + 1 < m) ? tile[2 * i + 1][c] : 0u;
-        dst[i] = lo16 | (hi16 << 16);
-      }
-      return;
-    }
+  const int4 info = *reinterpret_cast<const int4*>(kch + ((int64_t)g * D + tid) * 4);
+  const int c = info.x, b = info.w;
+  if (b == 0) return;                                     // width 0: nothing stored
+  uint32_t* dst = k_words + hp[18] + j * hp[20] + info.y;
+  if (b == 16) {
 #pragma unroll
-    for (int e = 0; e < 32; ++e) x[e] = bf16_bits_to_f32(tile[e][c]);
-    quantize32(x, m, b, w, &sc, &zz);
-    for (int i = 0; i < b; ++i) dst[i] = w[i];
-    float* par = k_par + 2 * (hp[19] + jg * hp[21] + qslot[c]);
-    par[0] = sc;
-    par[1] = zz;
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t lo16 = (2 * i < m) ? tile[2 * i][c] : 0u;
+      const uint32_t hi16 = (2 * i + 1 < m) ? tile[2 * i + 1][c] : 0u;
+      dst[i] = lo16 | (hi16 << 16);
+    }
     return;
   }
-  const int task = tid - D;
-  const int e = task / GPR, grp = task % GPR;
-  if (task >= 32 * GPR || e >= m) return;
-  const int32_t loc = vloc[e];
-  const int z = loc >> 29;
-  const int64_t pos = loc & ((1 << 29) - 1);
-  const int b = 2 << z;    // 2,4,8,16
-  const uint16_t* src = v + ((int64_t)g * N + tok[e]) * D + grp * 32;
+  float x[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) x[e] = bf16_bits_to_f32(tile[e][c]);
+  float* par = k_par + 2 * (hp[19] + j * hp[21] + info.z);
+  if (b == 2) quantize_store<2>(x, m, dst, par);
+  else if (b == 4) quantize_store<4>(x, m, dst, par);
+  else quantize_store<8>(x, m, dst, par);
+}
+
+// V: block (slab x of 32 tokens of one width zone, head g) with D threads = 32 tokens x
+// (D / 32) groups; the width is uniform over the block.
+template <int D>
+__device__ __forceinline__ void pack_v_slab(const uint16_t* __restrict__ v, int64_t N, int g, int64_t x,
+                                            const int64_t* __restrict__ hp, const int32_t* __restrict__ v_idx,
+                                            uint32_t* __restrict__ v_words, float* __restrict__ v_par) {
+  constexpr int GPR = D / 32;
+  int z = 0;
+  int64_t slab = x;
+  for (; z < 4; ++z) {
+    const int64_t ns = (hp[z] + 31) / 32;
+    if (slab < ns) break;
+    slab -= ns;
+  }
+  if (z == 4) return;
+  const int tid = threadIdx.x;
+  const int e = tid / GPR, grp = tid % GPR;
+  const int64_t pos = slab * 32 + e;
+  if (pos >= hp[z]) return;
+  const int32_t t = v_idx[hp[5 + z] + pos];
+  const uint16_t* src = v + ((int64_t)g * N + t) * D + grp * 32;
   uint32_t raw[16];
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
@@ -309,37 +422,59 @@ pack_kv(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t 
     raw[4 * q4 + 2] = wv.z;
     raw[4 * q4 + 3] = wv.w;
   }
+  const int b = 2 << z;
   uint32_t* dst = v_words + hp[9 + z] + (pos * GPR + grp) * b;
-  if (b == 16) {
+  if (z == 3) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) dst[i] = raw[i];
     return;
   }
+  float xv[32];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    x[2 * i] = bf16_bits_to_f32(raw[i] & 0xFFFFu);
-    x[2 * i + 1] = bf16_bits_to_f32(raw[i] >> 16);
+    xv[2 * i] = bf16_bits_to_f32(raw[i] & 0xFFFFu);
+    xv[2 * i + 1] = bf16_bits_to_f32(raw[i] >> 16);
   }
-  quantize32(x, 32, b, w, &sc, &zz);
-  for (int i = 0; i < b; ++i) dst[i] = w[i];
   float* par = v_par + 2 * (hp[13 + z] + pos * GPR + grp);
-  par[0] = sc;
-  par[1] = zz;
+  if (z == 0) quantize_store<2>(xv, 32, dst, par);
+  else if (z == 1) quantize_store<4>(xv, 32, dst, par);
+  else quantize_store<8>(xv, 32, dst, par);
+}
+
+template <int D>
+__global__ void __launch_bounds__(D)
+pack_units(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t N,
+           const int64_t* __restrict__ header, const int32_t* __restrict__ kch,
+           const int32_t* __restrict__ k_keep, const int32_t* __restrict__ v_idx,
+           uint32_t* __restrict__ k_words, float* __restrict__ k_par, uint32_t* __restrict__ v_words,
+           float* __restrict__ v_par) {
+  const int g = blockIdx.y;
+  const int64_t* hp = header + KVC_HDR_GLOBAL + g * KVC_HDR_PER_HEAD;
+  if (blockIdx.z == 0)
+    pack_k_group<D>(k, N, g, blockIdx.x, hp, kch, k_keep, k_words, k_par);
+  else
+    pack_v_slab<D>(v, N, g, blockIdx.x, hp, v_idx, v_words, v_par);
 }
 
 PackWs carve(const Layer& L, char* ws, size_t* total) {
   const int nchunk = (int)((L.n + kChunk - 1) / kChunk);
   WsPlan p;
   size_t oc = p.take(sizeof(int32_t) * L.hkv * nchunk * 4);
+  size_t obad = p.take(sizeof(int32_t) * L.hkv * nchunk);
   size_t ob = p.take(sizeof(int64_t) * L.hkv * nchunk * 4);
   size_t orb = p.take(sizeof(int64_t) * L.hkv * nchunk);
+  size_t oh = p.take(sizeof(int64_t) * L.hkv * 8);
+  size_t ok = p.take(sizeof(int32_t) * L.hkv * L.d * 4);
   if (total) *total = p.off;
   PackWs w{};
   if (ws) {
     w.status = reinterpret_cast<int32_t*>(ws);
     w.cnt = reinterpret_cast<int32_t*>(ws + oc);
+    w.cbad = reinterpret_cast<int32_t*>(ws + obad);
     w.base = reinterpret_cast<int64_t*>(ws + ob);
     w.rbase = reinterpret_cast<int64_t*>(ws + orb);
+    w.htot = reinterpret_cast<int64_t*>(ws + oh);
+    w.kch = reinterpret_cast<int32_t*>(ws + ok);
   }
   return w;
 }
@@ -372,20 +507,24 @@ hipError_t launch_pack(const Layer& L, const uint16_t* k, const uint16_t* v,
                        const kvc_packed_cache& out, char* ws, hipStream_t s) {
   const int nchunk = (int)((L.n + kChunk - 1) / kChunk);
   PackWs w = carve(L, ws, nullptr);
-  (void)launch_reset_status(ws, s);
   dim3 gc((unsigned)nchunk, (unsigned)L.hkv);
-  pack_count<<<gc, 256, 0, s>>>(bits_v, bits_k, L.n, L.d, nchunk, w.cnt, w.status);
-  pack_layout<<<1, 1024, 0, s>>>(w.cnt, bits_k, L.hkv, L.d, L.n, nchunk, w.base, w.rbase,
-                                 out.header, out.k_width);
+  pack_count<<<gc, 256, 0, s>>>(bits_v, L.n, nchunk, w.cnt, w.cbad);
+  if (L.d == 128)
+    pack_layout<128><<<(unsigned)L.hkv, 1024, 0, s>>>(w.cnt, w.cbad, bits_k, L.n, nchunk, w.base,
+                                                      w.rbase, w.htot, w.kch, out.k_width);
+  else
+    pack_layout<64><<<(unsigned)L.hkv, 1024, 0, s>>>(w.cnt, w.cbad, bits_k, L.n, nchunk, w.base,
+                                                     w.rbase, w.htot, w.kch, out.k_width);
+  pack_header<<<1, 256, 0, s>>>(w.htot, L.hkv, L.d, L.n, out.header, w.status);
   pack_index<<<gc, 256, 0, s>>>(bits_v, L.n, nchunk, w.base, w.rbase, out.header, out.v_idx,
                                 out.k_keep, out.k_vloc);
-  dim3 gk((unsigned)((L.n + 31) / 32), (unsigned)L.hkv);
+  dim3 gu((unsigned)((L.n + 31) / 32 + 4), (unsigned)L.hkv, 2);
   if (L.d == 128)
-    pack_kv<128><<<gk, 256, 0, s>>>(k, v, L.n, out.header, bits_k, out.k_keep, out.k_vloc,
-                                    out.k_words, out.k_par, out.v_words, out.v_par);
+    pack_units<128><<<gu, 128, 0, s>>>(k, v, L.n, out.header, w.kch, out.k_keep, out.v_idx,
+                                       out.k_words, out.k_par, out.v_words, out.v_par);
   else
-    pack_kv<64><<<gk, 128, 0, s>>>(k, v, L.n, out.header, bits_k, out.k_keep, out.k_vloc,
-                                   out.k_words, out.k_par, out.v_words, out.v_par);
+    pack_units<64><<<gu, 64, 0, s>>>(k, v, L.n, out.header, w.kch, out.k_keep, out.v_idx,
+                                     out.k_words, out.k_par, out.v_words, out.v_par);
   return hipGetLastError();
 }
 
