@@ -55,8 +55,9 @@ struct AllocWs {
   int64_t* hist;        // [nseg][kBins]  (the current pass)
   uint64_t* hmin;       // [nseg][kBins]
   uint64_t* hmax;       // [nseg][kBins]
-  uint64_t* keys;       // [U][4] (V/K)
-  int64_t* rcount;      // [Hkv]
+  int32_t* rpart;       // [Hkv][ncb]  retained tokens per 4096-token block (K stage)
+  int32_t* rbad;        // [Hkv][ncb]  invalid token widths seen in the block
+  int64_t* rcount;      // [Hkv]      R_g (K stage)
   int64_t* bsum;        // [nseg][nblk]
   int64_t* bexcl;       // [nseg][nblk]
   int64_t* used_part;   // [nseg][nblk]
@@ -177,10 +178,74 @@ __device__ void select_digit(SelState* st, const int64_t* hist, const uint64_t* 
   }
 }
 
+constexpr int kCountBlock = 4096;      // tokens per block of alloc_count (256 threads x 16)
+
+// K stage: retained tokens (bits_v > 0) of each head, per 4096-token block, and invalid widths.
+__global__ void __launch_bounds__(256)
+alloc_count(const uint8_t* __restrict__ bits_v, int64_t N, int ncb, int32_t* __restrict__ rpart,
+            int32_t* __restrict__ rbad) {
+  __shared__ int32_t wsum[4], wbad[4];
+  const int blk = blockIdx.x, g = blockIdx.y;
+  const int64_t t0 = (int64_t)blk * kCountBlock + threadIdx.x * 16;
+  const uint8_t* src = bits_v + (int64_t)g * N + t0;
+  int cnt = 0;
+  bool bad = false;
+  if (t0 + 15 < N && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+    const uint4 w = *reinterpret_cast<const uint4*>(src);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t b = (ww[i] >> (8 * j)) & 0xFFu;
+        cnt += (b > 0);
+        bad |= !valid_width(b);
+      }
+  } else {
+    for (int j = 0; j < 16; ++j) {
+      if (t0 + j < N) {
+        const uint32_t b = src[j];
+        cnt += (b > 0);
+        bad |= !valid_width(b);
+      }
+    }
+  }
+  int bi = bad ? 1 : 0;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    cnt += __shfl_xor(cnt, o, 64);
+    bi |= __shfl_xor(bi, o, 64);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    wsum[wave] = cnt;
+    wbad[wave] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    rpart[(int64_t)g * ncb + blk] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+    rbad[(int64_t)g * ncb + blk] = wbad[0] | wbad[1] | wbad[2] | wbad[3];
+  }
+}
+
+// R_g = sum of the head's block counts (integer: order-free), computed by a whole block of NT
+// threads into rc[Hkv] (LDS, zeroed by the caller); returns whether any width was invalid.
+template <typename T>
+__device__ __forceinline__ void sum_counts(const int32_t* rpart, const int32_t* rbad, int Hkv,
+                                           int ncb, T* rc, int32_t* bad) {
+  for (int64_t i = threadIdx.x; i < (int64_t)Hkv * ncb; i += blockDim.x) {
+    const int g = (int)(i / ncb);
+    const int32_t v = rpart[i];
+    if (v) atomicAdd(&rc[g], (T)v);
+    if (rbad[i]) *bad = 1;
+  }
+}
+
 // ======================= single-block path (V/K stages, <= 2048 units) ===================
 __global__ void __launch_bounds__(1024)
 alloc_small(const float* __restrict__ weight, const float* __restrict__ sigma,
-            const uint8_t* __restrict__ bits_v, int stage, int Hkv, int64_t N, int d, double avg,
+            const int32_t* __restrict__ rpart, const int32_t* __restrict__ rbad, int ncb,
+            int stage, int Hkv, int64_t N, int d, double avg,
             uint8_t* __restrict__ bits_out, kvc_alloc_result* result, int32_t* status) {
   __shared__ uint64_t keys[kSmallUnits * 4];
   __shared__ int64_t hist[kBins];
@@ -196,26 +261,7 @@ alloc_small(const float* __restrict__ weight, const float* __restrict__ sigma,
   if (tid == 0) bad = 0;
   for (int g = tid; g < Hkv; g += 1024) rc[g] = 0;
   __syncthreads();
-  if (stage == KVC_ALLOC_K_CHANNELS) {        // R_g from bits_v: per-thread counts, LDS sums
-    bool b_bad = false;
-    for (int g = 0; g < Hkv; ++g) {
-      int cnt = 0;
-      for (int64_t t = tid * 4; t < N; t += 4096) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (t + j < N) {
-            const uint32_t b = bits_v[(int64_t)g * N + t + j];
-            cnt += (b > 0);
-            b_bad |= !valid_width(b);
-          }
-        }
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
-      if (lane == 0 && cnt) atomicAdd(&rc[g], cnt);
-    }
-    if (b_bad) bad = 1;
-  }
+  if (stage == KVC_ALLOC_K_CHANNELS) sum_counts(rpart, rbad, Hkv, ncb, rc, &bad);
   __syncthreads();
   if (tid == 0) {
     int64_t E;
@@ -336,41 +382,30 @@ alloc_small(const float* __restrict__ weight, const float* __restrict__ sigma,
 
 // Count R_g (K stage), set the budgets, clear the first pass's histogram.  One block.
 __global__ void __launch_bounds__(1024)
-alloc_begin(AllocWs a, int stage, int nseg, int Hkv, int64_t N, int d,
-            const uint8_t* __restrict__ bits_v, double avg, double keep_fraction) {
+alloc_begin(AllocWs a, int stage, int nseg, int Hkv, int64_t N, int d, int ncb, double avg,
+            double keep_fraction) {
   __shared__ int64_t rsum;
   __shared__ int32_t bad;
-  const int tid = threadIdx.x, lane = tid & 63;
+  __shared__ unsigned long long rc[256];
+  const int tid = threadIdx.x;
   if (tid == 0) {
     rsum = 0;
     bad = 0;
   }
+  if (tid < 256) rc[tid] = 0;
   for (int64_t i = tid; i < (int64_t)nseg * kBins; i += 1024) {
     a.hist[i] = 0;
     a.hmin[i] = ~0ull;
     a.hmax[i] = 0;
   }
   __syncthreads();
-  if (stage == KVC_ALLOC_K_CHANNELS) {
-    bool b_bad = false;
-    for (int g = 0; g < Hkv; ++g) {
-      unsigned long long cnt = 0;
-      for (int64_t t = tid; t < N; t += 1024) {
-        const uint32_t b = bits_v[(int64_t)g * N + t];
-        cnt += (b > 0);
-        b_bad |= !valid_width(b);
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
-      if (lane == 0 && cnt) atomicAdd((unsigned long long*)&a.rcount[g], cnt);
-    }
-    if (b_bad) bad = 1;
-  }
+  if (stage == KVC_ALLOC_K_CHANNELS) sum_counts(a.rpart, a.rbad, Hkv, ncb, rc, &bad);
   __syncthreads();
+  if (stage == KVC_ALLOC_K_CHANNELS && tid < Hkv) a.rcount[tid] = (int64_t)rc[tid];
   if (tid == 0) {
     *a.status = bad ? KVC_DEV_BAD_WIDTH : 0;
     if (stage == KVC_ALLOC_K_CHANNELS)
-      for (int g = 0; g < Hkv; ++g) rsum += a.rcount[g];
+      for (int g = 0; g < Hkv; ++g) rsum += (int64_t)rc[g];
   }
   __syncthreads();
   for (int sgi = tid; sgi < nseg; sgi += 1024) {
@@ -394,21 +429,17 @@ alloc_begin(AllocWs a, int stage, int nseg, int Hkv, int64_t N, int d,
   }
 }
 
-__global__ void zero_counts(int64_t* rcount, int Hkv) {
-  if ((int)threadIdx.x < Hkv) rcount[threadIdx.x] = 0;
-}
-
 __device__ __forceinline__ int64_t unit_size(int stage, int d, int64_t u, const int64_t* rcount) {
   return stage == KVC_ALLOC_V_TOKENS ? (int64_t)d : rcount[u / d];
 }
 
-__device__ __forceinline__ void load_keys(const uint64_t* keys, int64_t u, uint64_t (&kk)[4]) {
-  const uint4* kp = reinterpret_cast<const uint4*>(keys + u * 4);
-  const uint4 x = kp[0], y = kp[1];
-  kk[0] = (uint64_t)x.x | ((uint64_t)x.y << 32);
-  kk[1] = (uint64_t)x.z | ((uint64_t)x.w << 32);
-  kk[2] = (uint64_t)y.x | ((uint64_t)y.y << 32);
-  kk[3] = (uint64_t)y.z | ((uint64_t)y.w << 32);
+// The four step keys of unit u, recomputed from its weight on every pass (the same float64
+// operations each time, so the same bits): cheaper than storing and re-reading 32 bytes.
+__device__ __forceinline__ void keys_of(const float* weight, const float* sigma, int stage, int d,
+                                        int64_t u, const int64_t* rcount, uint64_t (&kk)[4]) {
+  float c = weight[u];
+  if (sigma) c = c * sigma[u];
+  unit_keys(c, unit_size(stage, d, u, rcount), kk);
 }
 
 // Histogram of one pass.  V/K: keys computed on pass 0 (and stored), 4 per unit, weight =
@@ -421,9 +452,7 @@ alloc_hist(AllocWs a, const float* __restrict__ weight, const float* __restrict_
   __shared__ uint64_t hmn[kBins], hmx[kBins];
   const int seg = blockIdx.y;
   const SelState s = a.st[seg];
-  const bool active = !(s.done || s.none);
-  const bool make_keys = !TOPK && pass == 0;
-  if (!active && !make_keys) return;           // uniform for the block
+  if (s.done || s.none) return;                // uniform for the block
   for (int b = threadIdx.x; b < kBins; b += 256) {
     h[b] = 0;
     hmn[b] = ~0ull;
@@ -449,31 +478,19 @@ alloc_hist(AllocWs a, const float* __restrict__ weight, const float* __restrict_
     } else {
       const int64_t sz = unit_size(stage, d, ul, a.rcount);
       uint64_t kk[4];
-      if (make_keys) {
-        float c = weight[ul];
-        if (sigma) c = c * sigma[ul];
-        unit_keys(c, sz, kk);
-        uint4* o = reinterpret_cast<uint4*>(a.keys + ul * 4);
-        o[0] = make_uint4((uint32_t)kk[0], (uint32_t)(kk[0] >> 32), (uint32_t)kk[1], (uint32_t)(kk[1] >> 32));
-        o[1] = make_uint4((uint32_t)kk[2], (uint32_t)(kk[2] >> 32), (uint32_t)kk[3], (uint32_t)(kk[3] >> 32));
-      } else {
-        load_keys(a.keys, ul, kk);
-      }
-      if (active) {
+      keys_of(weight, sigma, stage, d, ul, a.rcount, kk);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          if (kk[k] != 0 && (kk[k] & dg.himask) == pre) {
-            const int b = (int)((kk[k] >> dg.lo) & dmask);
-            atomicAdd((unsigned long long*)&h[b], (unsigned long long)step_rate(sz, k));
-            atomicMin((unsigned long long*)&hmn[b], (unsigned long long)kk[k]);
-            atomicMax((unsigned long long*)&hmx[b], (unsigned long long)kk[k]);
-          }
+      for (int k = 0; k < 4; ++k) {
+        if (kk[k] != 0 && (kk[k] & dg.himask) == pre) {
+          const int b = (int)((kk[k] >> dg.lo) & dmask);
+          atomicAdd((unsigned long long*)&h[b], (unsigned long long)step_rate(sz, k));
+          atomicMin((unsigned long long*)&hmn[b], (unsigned long long)kk[k]);
+          atomicMax((unsigned long long*)&hmx[b], (unsigned long long)kk[k]);
         }
       }
     }
   }
   __syncthreads();
-  if (!active) return;
   for (int b = threadIdx.x; b < kBins; b += 256) {
     if (h[b]) {
       const int64_t gi = (int64_t)seg * kBins + b;
@@ -504,8 +521,8 @@ alloc_select(AllocWs a, int pass, int nb) {
 }
 
 template <bool TOPK>
-__device__ __forceinline__ int64_t unit_tie(const AllocWs& a, const float* weight, int64_t u,
-                                            int64_t seg, int64_t seg_len, int stage, int d,
+__device__ __forceinline__ int64_t unit_tie(const AllocWs& a, const float* weight, const float* sigma,
+                                            int64_t u, int64_t seg, int64_t seg_len, int stage, int d,
                                             const SelState& s, int* n) {
   if (u >= seg_len) {
     *n = 0;
@@ -521,14 +538,15 @@ __device__ __forceinline__ int64_t unit_tie(const AllocWs& a, const float* weigh
     return key == s.prefix ? 1 : 0;
   }
   uint64_t kk[4];
-  load_keys(a.keys, u, kk);
+  keys_of(weight, sigma, stage, d, u, a.rcount, kk);
   return steps_and_tie(kk, unit_size(stage, d, u, a.rcount), s.prefix, s.all_fit != 0, n);
 }
 
 // Block sums of the tie rates (units in index order, 4 per thread).
 template <bool TOPK>
 __global__ void __launch_bounds__(256)
-alloc_ties(AllocWs a, const float* __restrict__ weight, int64_t seg_len, int stage, int d) {
+alloc_ties(AllocWs a, const float* __restrict__ weight, const float* __restrict__ sigma,
+           int64_t seg_len, int stage, int d) {
   __shared__ int64_t wave_tot[4];
   const int seg = blockIdx.y;
   const SelState s = a.st[seg];
@@ -537,7 +555,7 @@ alloc_ties(AllocWs a, const float* __restrict__ weight, int64_t seg_len, int sta
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     int n;
-    t += unit_tie<TOPK>(a, weight, base + j, seg, seg_len, stage, d, s, &n);
+    t += unit_tie<TOPK>(a, weight, sigma, base + j, seg, seg_len, stage, d, s, &n);
   }
   const int64_t tot = block_scan_incl(t, wave_tot);
   if (threadIdx.x == 255) a.bsum[(int64_t)seg * gridDim.x + blockIdx.x] = tot;
@@ -579,7 +597,7 @@ alloc_assign(AllocWs a, const float* __restrict__ weight, const float* __restric
   int64_t tsum = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    tie[j] = unit_tie<TOPK>(a, weight, base + j, seg, seg_len, stage, d, s, &n[j]);
+    tie[j] = unit_tie<TOPK>(a, weight, sigma, base + j, seg, seg_len, stage, d, s, &n[j]);
     tsum += tie[j];
   }
   const int64_t incl = block_scan_incl(tsum, wave_tot);
@@ -621,27 +639,44 @@ alloc_assign(AllocWs a, const float* __restrict__ weight, const float* __restric
   }
 }
 
-// Sum the per-block used rate and distortion in block order and write the result.
-__global__ void alloc_finalize(const AllocWs a, int nparts, int topk, kvc_alloc_result* result) {
-  if (threadIdx.x != 0 || result == nullptr) return;
+// Sum the per-block used rate and distortion and write the result.  256 threads each sum a
+// contiguous range of parts in order; the 256 sums are combined by a fixed tree.
+__global__ void __launch_bounds__(256)
+alloc_finalize(const AllocWs a, int nparts, int topk, kvc_alloc_result* result) {
+  __shared__ int64_t us[256];
+  __shared__ double ds[256];
+  if (result == nullptr) return;
+  const int tid = threadIdx.x;
+  const int per = (nparts + 255) / 256;
   int64_t ut = 0;
   double dt = 0.0;
-  for (int i = 0; i < nparts; ++i) {
+  for (int i = tid * per; i < (tid + 1) * per && i < nparts; ++i) {
     ut += a.used_part[i];
     dt += a.dist_part[i];
   }
+  us[tid] = ut;
+  ds[tid] = dt;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (tid < w) {
+      us[tid] += us[tid + w];
+      ds[tid] += ds[tid + w];
+    }
+    __syncthreads();
+  }
+  if (tid != 0) return;
   kvc_alloc_result r;
   if (topk) {
     r.lambda = 0.0;
-    r.budget_bits = ut;
-    r.used_bits = ut;
+    r.budget_bits = us[0];
+    r.used_bits = us[0];
     r.distortion = 0.0;
   } else {
     const SelState s0 = a.st[0];
     r.lambda = s0.all_fit ? 0.0 : __longlong_as_double((long long)s0.prefix);
     r.budget_bits = s0.budget;
-    r.used_bits = ut;
-    r.distortion = dt;
+    r.used_bits = us[0];
+    r.distortion = ds[0];
   }
   *result = r;
 }
@@ -679,7 +714,10 @@ AllocWs carve(const Layer& L, int stage, char* ws, size_t* total) {
   const size_t o_h = w.take(sizeof(int64_t) * hn);
   const size_t o_mn = w.take(sizeof(uint64_t) * hn);
   const size_t o_mx = w.take(sizeof(uint64_t) * hn);
-  const size_t o_k = w.take(stage == KVC_ALLOC_TOPK ? 0 : sizeof(uint64_t) * 4 * p.U);
+  const int ncb = (int)((L.n + kCountBlock - 1) / kCountBlock);
+  const bool kst = (stage == KVC_ALLOC_K_CHANNELS);
+  const size_t o_rp = w.take(kst ? sizeof(int32_t) * L.hkv * ncb : 0);
+  const size_t o_rb = w.take(kst ? sizeof(int32_t) * L.hkv * ncb : 0);
   const size_t o_r = w.take(sizeof(int64_t) * L.hkv);
   const size_t o_b = w.take(sizeof(int64_t) * p.nseg * p.nblk);
   const size_t o_e = w.take(sizeof(int64_t) * p.nseg * p.nblk);
@@ -692,7 +730,8 @@ AllocWs carve(const Layer& L, int stage, char* ws, size_t* total) {
     a.hist = reinterpret_cast<int64_t*>(ws + o_h);
     a.hmin = reinterpret_cast<uint64_t*>(ws + o_mn);
     a.hmax = reinterpret_cast<uint64_t*>(ws + o_mx);
-    a.keys = reinterpret_cast<uint64_t*>(ws + o_k);
+    a.rpart = reinterpret_cast<int32_t*>(ws + o_rp);
+    a.rbad = reinterpret_cast<int32_t*>(ws + o_rb);
     a.rcount = reinterpret_cast<int64_t*>(ws + o_r);
     a.bsum = reinterpret_cast<int64_t*>(ws + o_b);
     a.bexcl = reinterpret_cast<int64_t*>(ws + o_e);
@@ -717,14 +756,16 @@ hipError_t launch_allocate(const Layer& L, int stage, const float* weight, const
   const Plan p = plan_of(L, stage);
   if (p.nseg > kMaxSeg) return hipErrorInvalidValue;
   AllocWs a = carve(L, stage, ws, nullptr);
+  const int ncb = (int)((L.n + kCountBlock - 1) / kCountBlock);
+  if (stage == KVC_ALLOC_K_CHANNELS)
+    alloc_count<<<dim3((unsigned)ncb, (unsigned)L.hkv), 256, 0, s>>>(bits_v, L.n, ncb, a.rpart, a.rbad);
   if (p.small) {
-    alloc_small<<<1, 1024, 0, s>>>(weight, sigma, bits_v, stage, L.hkv, L.n, L.d, avg_bits,
-                                   bits_out, result, a.status);
+    alloc_small<<<1, 1024, 0, s>>>(weight, sigma, a.rpart, a.rbad, ncb, stage, L.hkv, L.n, L.d,
+                                   avg_bits, bits_out, result, a.status);
     return hipGetLastError();
   }
   const bool topk = (stage == KVC_ALLOC_TOPK);
-  if (stage == KVC_ALLOC_K_CHANNELS) zero_counts<<<1, 256, 0, s>>>(a.rcount, L.hkv);
-  alloc_begin<<<1, 1024, 0, s>>>(a, stage, p.nseg, L.hkv, L.n, L.d, bits_v, avg_bits, keep_fraction);
+  alloc_begin<<<1, 1024, 0, s>>>(a, stage, p.nseg, L.hkv, L.n, L.d, ncb, avg_bits, keep_fraction);
   const dim3 g2((unsigned)p.nblk, (unsigned)p.nseg);
   const int npass = passes_of(p.nb);
   for (int pass = 0; pass < npass; ++pass) {
@@ -735,15 +776,15 @@ hipError_t launch_allocate(const Layer& L, int stage, const float* weight, const
     alloc_select<<<p.nseg, 256, 0, s>>>(a, pass, p.nb);
   }
   if (topk) {
-    alloc_ties<true><<<g2, 256, 0, s>>>(a, weight, p.seg_len, stage, L.d);
+    alloc_ties<true><<<g2, 256, 0, s>>>(a, weight, nullptr, p.seg_len, stage, L.d);
     alloc_tie_scan<<<p.nseg, 256, 0, s>>>(a, p.nblk);
     alloc_assign<true><<<g2, 256, 0, s>>>(a, weight, nullptr, p.seg_len, stage, L.d, keep_bits, bits_out);
   } else {
-    alloc_ties<false><<<g2, 256, 0, s>>>(a, weight, p.seg_len, stage, L.d);
+    alloc_ties<false><<<g2, 256, 0, s>>>(a, weight, sigma, p.seg_len, stage, L.d);
     alloc_tie_scan<<<p.nseg, 256, 0, s>>>(a, p.nblk);
     alloc_assign<false><<<g2, 256, 0, s>>>(a, weight, sigma, p.seg_len, stage, L.d, keep_bits, bits_out);
   }
-  alloc_finalize<<<1, 64, 0, s>>>(a, p.nblk * p.nseg, topk ? 1 : 0, result);
+  alloc_finalize<<<1, 256, 0, s>>>(a, p.nblk * p.nseg, topk ? 1 : 0, result);
   return hipGetLastError();
 }
 
