@@ -33,6 +33,14 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak (published)
 CPU_SAMPLE_SECONDS = 12.0      # oracle sample: KV heads are added until this much CPU time
 
+# HBM bytes per launch of the dominant kernel, from rocprofv3 FETCH_SIZE and WRITE_SIZE runs
+# scaled by the same counters on a plain copy of known size (profiles/hbm_counters_*.md).
+# A figure holds only for the scorer source it was measured on; otherwise traffic is null.
+MEASURED_TRAFFIC = {
+    "llama8b_prefill_n8192": {"bytes": 92609408,
+                              "score_src_sha256": "d22249bc8fbb3a8dee485057d747a53de09c35d9894f19e3fc5a31710b29f354"},
+}
+
 
 def visible_elements(N, Nq, causal=True):
     """Visible (query row, key) pairs of one query head, row i at position N - Nq + i."""
@@ -89,6 +97,18 @@ def cpu_baseline(cfg):
     }
 
 
+def measured_traffic(workload):
+    import hashlib
+    m = MEASURED_TRAFFIC.get(workload)
+    if m is None:
+        return None
+    src = os.path.join(ROOT, "kv_cache_compression_pass_amd", "csrc", "score.hip")
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != m["score_src_sha256"]:
+            return None
+    return m["bytes"]
+
+
 def packed_bytes_read_by_attend(hdr):
     """Bytes of the packed cache one attend launch streams: value words and (scale, zero)
     pairs, key words and pairs, the retained-token list and its value locations."""
@@ -102,6 +122,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="instead of the bench: run a plain elementwise copy of MIB MiB (read MIB, "
+                         "write MIB) five times, the reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the path runs "
@@ -111,6 +134,23 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(5):
+            torch.neg(src, out=dst)
+        a1.record()
+        torch.cuda.synchronize()
+        ms = a0.elapsed_time(a1) / 5
+        print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n,
+                          "ms": round(ms, 5), "gbs": round(8 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+        return
+
     import kv_cache_compression_pass_amd as kvc
     from workloads import get_config, make_config_inputs
 
@@ -208,7 +248,8 @@ def main():
     achieved = flops / (lse_ms * 1e-3) / 1e12
     roofline = {
         "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-        "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+        "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": measured_traffic(cfg.name),
         "kernel": "lse_partial", "flops_per_launch": flops, "avg_launch_ms": round(lse_ms, 5),
     }
 

@@ -7,6 +7,8 @@ identical float32 weights / widths; compressed attention output 2e-2 abs and LSE
 
 import math
 
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -101,7 +103,7 @@ def _pipeline(name, hq, hkv, d, N, Nq, causal, avg, seed, x=None, n_fid=64):
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_small_pipeline(case):
     name, hq, hkv, d, N, Nq, causal, avg = case
-    _pipeline(name, hq, hkv, d, N, Nq, causal, avg, seed=abs(hash(name)) % 1000)
+    _pipeline(name, hq, hkv, d, N, Nq, causal, avg, seed=zlib.crc32(name.encode()) % 1000)
 
 
 def test_config0_tiny_full_parity():
