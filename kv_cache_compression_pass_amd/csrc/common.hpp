@@ -39,6 +39,17 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Exchange with the lane 32 apart (the other half of a 32x32 accumulator column).
 __device__ __forceinline__ float swap_half(float x) { return __shfl_xor(x, 32, 64); }
 
+// max / sum of a value and the one held 32 lanes away, on the VALU (v_permlane32_swap): lane
+// l < 32 sees (x[l], x[l + 32]), lane l >= 32 sees (x[l - 32], x[l]); both get the same result.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Record a device-side data error in the workspace status word.
 __device__ __forceinline__ void set_status(int32_t* status, int32_t code) {
   if (status) atomicOr(status, code);

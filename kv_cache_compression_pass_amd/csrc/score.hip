@@ -197,77 +197,134 @@ __device__ __forceinline__ bool geo_of(const Decomp& dc, int64_t N, int64_t Nq, 
 }
 
 // ---------------------------------------------------------------------------------------
+// Both passes run a software pipeline over 32-key half tiles: while the matrix cores compute
+// the products of one half, the VALU finishes the softmax work of the previous half.  Two
+// accumulator sets (A, B) alternate; a half whose keys are not all visible to every row of
+// the wave (the causal diagonal, the end of the cache, rows past Nq) is masked between the
+// phases, outside the interleaved code.
+// ---------------------------------------------------------------------------------------
+
+// Scheduling fence between pipeline phases: the compiler interleaves matrix-core and VALU
+// work inside a phase but moves nothing across, which bounds the registers live at once.
+#define KVC_PHASE_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// True if every key of the half [t0h, t0h + 32) is visible to every row of the wave.
+__device__ __forceinline__ bool half_full(const Geo& G, int t0h, int N, int causal) {
+  return (!causal || t0h + 31 <= G.off + G.i_wave) && (t0h + 32 <= N);
+}
+
+// ---------------------------------------------------------------------------------------
 // Pass 1: per chunk, m = max_t x and l = sum_t 2^(x - m) for every row, x = c * q.k.
-// D[m = key][n = row]: a lane holds one row and 16 keys of each 32-key block.
+// h[nb] = K_half x Q^T block nb: element i of a lane is key 32kb + acc_row(i, hi), row
+// 32nb + lo, so a lane holds one row and its softmax statistics stay in-lane.
 // ---------------------------------------------------------------------------------------
 template <int D, int S>
-__device__ __forceinline__ void lse_tile(const Geo& G, const bf16x8 (&qf)[2][D / 16],
-                                         float (&m_run)[2], float (&l_run)[2], int t0,
-                                         int N, int causal, float c) {
-  if (t0 >= G.kend_wave) return;
-  constexpr int KS = D / 16;
-  f32x16 acc[2][2];
+__device__ __forceinline__ void lse_mfma_half(f32x16 (&h)[2], const bf16x8 (&qf)[2][D / 16], int kb,
+                                              int lo, int hi) {
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int i = 0; i < 16; ++i) h[nb][i] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8 a = kfrag<D, S>(kb * 32 + G.lo, 2 * ks + G.hi);
-      acc[kb][0] = mfma32(a, qf[0][ks], acc[kb][0]);
-      acc[kb][1] = mfma32(a, qf[1][ks], acc[kb][1]);
-    }
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const bf16x8 a = kfrag<D, S>(kb * 32 + lo, 2 * ks + hi);
+    h[0] = mfma32(a, qf[0][ks], h[0]);
+    h[1] = mfma32(a, qf[1][ks], h[1]);
   }
-  const bool full = (!causal || t0 + 63 <= G.off + G.i_wave) && (t0 + 64 <= N);
+}
+
+// Key t0h + acc_row(i, hi) is invisible to row pos iff it lies past min(pos, N - 1) (past
+// N - 1 without the causal mask).  With acc_row(i, hi) = 4 hi + r_i, r_i = 8 (i / 4) + i % 4, the
+// test is one compare of the constant r_i per element.
+__device__ __forceinline__ void lse_mask_half(f32x16 (&h)[2], const Geo& G, int t0h, int N, int causal) {
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    if (!full) {
-      const int pos = G.off + G.i_wave + 32 * nb + G.lo;
+    const int pos = G.off + G.i_wave + 32 * nb + G.lo;
+    const int lim = (causal && pos < N - 1) ? pos : N - 1;
+    const int L = lim - t0h - 4 * G.hi;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int t = t0 + 32 * kb + acc_row(i, G.hi);
-          if (t >= N || (causal && t > pos)) acc[kb][nb][i] = -INFINITY;
-        }
-    }
-    float tmax = acc[0][nb][0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, acc[0][nb][i]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, acc[1][nb][i]);
-    tmax = fmaxf(tmax, swap_half(tmax));
-    const float mnew = fmaxf(m_run[nb], tmax * c);
-    if (mnew > -INFINITY) {
-      const float nm = -mnew;
-      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        s0 += fast_exp2(fmaf(acc[0][nb][i], c, nm));
-        s1 += fast_exp2(fmaf(acc[0][nb][i + 1], c, nm));
-        s2 += fast_exp2(fmaf(acc[1][nb][i], c, nm));
-        s3 += fast_exp2(fmaf(acc[1][nb][i + 1], c, nm));
-      }
-      l_run[nb] = fmaf(l_run[nb], fast_exp2(m_run[nb] - mnew), (s0 + s1) + (s2 + s3));
-      m_run[nb] = mnew;
+    for (int i = 0; i < 16; ++i) {
+      const int r = 8 * (i >> 2) + (i & 3);
+      h[nb][i] = (r > L) ? -INFINITY : h[nb][i];
     }
   }
 }
 
+// Online update of (m, l) with one half tile; no branches (an all-masked half leaves m, l).
+__device__ __forceinline__ void lse_update_half(const f32x16 (&h)[2], float (&m_run)[2],
+                                                float (&l_run)[2], float c) {
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    float t0 = fmaxf(h[nb][0], h[nb][1]), t1 = fmaxf(h[nb][2], h[nb][3]);
+#pragma unroll
+    for (int i = 4; i < 16; i += 4) {
+      t0 = fmaxf(t0, fmaxf(h[nb][i], h[nb][i + 1]));
+      t1 = fmaxf(t1, fmaxf(h[nb][i + 2], h[nb][i + 3]));
+    }
+    const float tmax = half_max(fmaxf(t0, t1));
+    const float mnew = fmaxf(m_run[nb], tmax * c);
+    const float nm = (mnew == -INFINITY) ? 0.f : -mnew;
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+      s0 += fast_exp2(fmaf(h[nb][i], c, nm));
+      s1 += fast_exp2(fmaf(h[nb][i + 1], c, nm));
+      s2 += fast_exp2(fmaf(h[nb][i + 2], c, nm));
+      s3 += fast_exp2(fmaf(h[nb][i + 3], c, nm));
+    }
+    l_run[nb] = fmaf(l_run[nb], fast_exp2(m_run[nb] + nm), (s0 + s1) + (s2 + s3));
+    m_run[nb] = mnew;
+  }
+}
+
+// Tiles [0, nfull) are visible in full to every row of the block; they run the pipelined
+// step.  The rest (the causal diagonal band and a partial last tile: at most 5 tiles of an
+// item) run a masked step without pipelining.
+__device__ __forceinline__ int full_tiles(const Geo& G, int N, int causal) {
+  int lim = N;                                   // keys [k0, lim) fully visible to all rows
+  if (causal) {
+    const int e = G.off + G.i_block + 1;         // keys <= first row's position
+    lim = e < lim ? e : lim;
+  }
+  int nf = (lim - G.k0) / 64;
+  nf = nf < 0 ? 0 : nf;
+  return nf < G.ntiles ? nf : G.ntiles;
+}
+
 // One ring step: wait for tile J (two younger tiles may stay in flight), refill the slot the
-// previous step freed with tile J + 3 (always issued: rows past the end are clamped and the
-// slot is never read), then process tile J.  Issuing unconditionally keeps the compiler's view
-// of the in-flight fills exact, so it adds no waits of its own.
+// previous step freed with tile J + 3 (always issued: rows past the end read as zero and the
+// slot is never read), then the two phases of tile J: the first half's products with the
+// previous half's softmax update, then the second half's products with the first half's
+// update.
 #define KVC_LSE_STEP(S, J)                                                                  \
   {                                                                                         \
     ring_barrier<D>(2);                                                                     \
-    issue_tile<D, ((S) + 3) & 3>(kh, G.k0 + 64 * ((J) + 3), n, voff, G.wave);    \
-    lse_tile<D, S>(G, qf, m_run, l_run, G.k0 + 64 * (J), n, causal, c);           \
+    issue_tile<D, ((S) + 3) & 3>(kh, G.k0 + 64 * ((J) + 3), n, voff, G.wave);               \
+    KVC_PHASE_FENCE();                                                                      \
+    lse_mfma_half<D, S>(A, qf, 0, G.lo, G.hi);                                              \
+    lse_update_half(B, m_run, l_run, c);                                                    \
+    KVC_PHASE_FENCE();                                                                      \
+    lse_mfma_half<D, S>(B, qf, 1, G.lo, G.hi);                                              \
+    lse_update_half(A, m_run, l_run, c);                                                    \
+    KVC_PHASE_FENCE();                                                                      \
   }
+
+// Masked step (no pipelining): both halves of tile J are masked and folded in.
+template <int D, int S>
+__device__ __forceinline__ void lse_masked_step(const Geo& G, const uint16_t* kh, int J, int n, int causal,
+                                                const int (&voff)[4], const bf16x8 (&qf)[2][D / 16],
+                                                float (&m_run)[2], float (&l_run)[2], float c) {
+  ring_barrier<D>(2);
+  issue_tile<D, (S + 3) & 3>(kh, G.k0 + 64 * (J + 3), n, voff, G.wave);
+  const int t0 = G.k0 + 64 * J;
+  f32x16 h[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    lse_mfma_half<D, S>(h, qf, kb, G.lo, G.hi);
+    lse_mask_half(h, G, t0 + 32 * kb, n, causal);
+    lse_update_half(h, m_run, l_run, c);
+  }
+}
 
 template <int D>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -288,20 +345,37 @@ lse_partial(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   issue_tile<D, 0>(kh, G.k0, n, voff, G.wave);
   issue_tile<D, 1>(kh, G.k0 + 64, n, voff, G.wave);
   issue_tile<D, 2>(kh, G.k0 + 128, n, voff, G.wave);
+  const int nfull = full_tiles(G, n, causal);
   int j0 = 0;
-  for (; j0 + 4 <= G.ntiles; j0 += 4) {
-    KVC_LSE_STEP(0, j0)
-    KVC_LSE_STEP(1, j0 + 1)
-    KVC_LSE_STEP(2, j0 + 2)
-    KVC_LSE_STEP(3, j0 + 3)
+  {
+    f32x16 A[2], B[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) B[nb][i] = -INFINITY;   // "previous half" of the first step
+    for (; j0 + 4 <= nfull; j0 += 4) {
+      KVC_LSE_STEP(0, j0)
+      KVC_LSE_STEP(1, j0 + 1)
+      KVC_LSE_STEP(2, j0 + 2)
+      KVC_LSE_STEP(3, j0 + 3)
+    }
+    if (j0 < nfull) KVC_LSE_STEP(0, j0)
+    if (j0 + 1 < nfull) KVC_LSE_STEP(1, j0 + 1)
+    if (j0 + 2 < nfull) KVC_LSE_STEP(2, j0 + 2)
+    lse_update_half(B, m_run, l_run, c);        // second half of the last pipelined tile
   }
-  if (j0 < G.ntiles) KVC_LSE_STEP(0, j0)
-  if (j0 + 1 < G.ntiles) KVC_LSE_STEP(1, j0 + 1)
-  if (j0 + 2 < G.ntiles) KVC_LSE_STEP(2, j0 + 2)
+  for (int j = nfull; j < G.ntiles; ++j) {
+    switch (j & 3) {
+      case 0: lse_masked_step<D, 0>(G, kh, j, n, causal, voff, qf, m_run, l_run, c); break;
+      case 1: lse_masked_step<D, 1>(G, kh, j, n, causal, voff, qf, m_run, l_run, c); break;
+      case 2: lse_masked_step<D, 2>(G, kh, j, n, causal, voff, qf, m_run, l_run, c); break;
+      default: lse_masked_step<D, 3>(G, kh, j, n, causal, voff, qf, m_run, l_run, c); break;
+    }
+  }
   __builtin_amdgcn_s_waitcnt(7 << 4);       // no LDS fill may outlive the block
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const float lt = l_run[nb] + swap_half(l_run[nb]);
+    const float lt = half_sum(l_run[nb]);
     const int64_t row = G.i_wave + 32 * nb + G.lo;
     if (G.hi == 0 && row < Nq) {
       if (dc.maxCh == 1)   // one chunk covers the row: write l itself
@@ -330,78 +404,70 @@ __global__ void lse_combine(const float2* __restrict__ part, float* __restrict__
 }
 
 // ---------------------------------------------------------------------------------------
-// Pass 2: column reductions.  D[m = row][n = key] (operands swapped): a lane holds one key
-// and 16 rows of each 32-row block.  SUM: partial = sum_rows 2^(x - l'), l' = l*log2(e);
-// MAX: partial = max_rows (x - l'), l' = l*log2(e) - log2||h||.  One partial per
-// (query head, row tile, key), the four waves' rows summed (or maxed) in a fixed order.
+// Pass 2: column reductions.  h[mb] = Q block mb x K_half^T (operands swapped): element i of a
+// lane is row 32mb + acc_row(i, hi), key 32kb + lo, so a lane holds one key and 16 rows of
+// each 32-row block.  SUM: partial = sum_rows 2^(x - l'), l' = l*log2(e); MAX: partial =
+// max_rows (x - l'), l' = l*log2(e) - log2||h||.  One partial per (query head, row tile,
+// key), the four waves' rows combined in a fixed order.
 // ---------------------------------------------------------------------------------------
-template <int D, bool MAXMODE, int S>
-__device__ __forceinline__ void score_tile(const Geo& G, const bf16x8 (&qf)[2][D / 16],
-                                           const float (&lv)[2][16], int t0, int N,
-                                           int causal, float c, float (&cbw)[64]) {
-  constexpr int KS = D / 16;
-  const bool any = t0 < G.kend_wave;
-  const bool full = (!causal || t0 + 63 <= G.off + G.i_wave) && (t0 + 64 <= N);
+template <int D, int S>
+__device__ __forceinline__ void score_mfma_half(f32x16 (&h)[2], const bf16x8 (&qf)[2][D / 16], int kb,
+                                                int lo, int hi) {
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    float colv = MAXMODE ? -INFINITY : 0.f;
-    if (any) {
-      f32x16 acc[2];
+  for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+    for (int i = 0; i < 16; ++i) h[mb][i] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[a][i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 b = kfrag<D, S>(kb * 32 + G.lo, 2 * ks + G.hi);
-        acc[0] = mfma32(qf[0][ks], b, acc[0]);
-        acc[1] = mfma32(qf[1][ks], b, acc[1]);
-      }
-      const int t = t0 + 32 * kb + G.lo;
-      if (MAXMODE) {
-        float mx0 = -INFINITY, mx1 = -INFINITY;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; i += 2) {
-            float x0 = fmaf(acc[mb][i], c, -lv[mb][i]);
-            float x1 = fmaf(acc[mb][i + 1], c, -lv[mb][i + 1]);
-            if (!full) {
-              const int p0 = G.off + G.i_wave + 32 * mb + acc_row(i, G.hi);
-              if (t >= N || (causal && t > p0)) x0 = -INFINITY;
-              if (t >= N || (causal && t > p0 + 1)) x1 = -INFINITY;
-            }
-            mx0 = fmaxf(mx0, x0);
-            mx1 = fmaxf(mx1, x1);
-          }
-        colv = fmaxf(mx0, mx1);
-        colv = fmaxf(colv, swap_half(colv));
-      } else {
-        float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          float x0 = fmaf(acc[0][i], c, -lv[0][i]);
-          float x1 = fmaf(acc[0][i + 1], c, -lv[0][i + 1]);
-          float x2 = fmaf(acc[1][i], c, -lv[1][i]);
-          float x3 = fmaf(acc[1][i + 1], c, -lv[1][i + 1]);
-          if (!full) {
-            const int p0 = G.off + G.i_wave + acc_row(i, G.hi);
-            if (t >= N || (causal && t > p0)) x0 = -INFINITY;
-            if (t >= N || (causal && t > p0 + 1)) x1 = -INFINITY;
-            if (t >= N || (causal && t > p0 + 32)) x2 = -INFINITY;
-            if (t >= N || (causal && t > p0 + 33)) x3 = -INFINITY;
-          }
-          s0 += fast_exp2(x0);
-          s1 += fast_exp2(x1);
-          s2 += fast_exp2(x2);
-          s3 += fast_exp2(x3);
-        }
-        colv = (s0 + s1) + (s2 + s3);
-        colv = colv + swap_half(colv);
-      }
-    }
-    if (G.hi == 0) cbw[32 * kb + G.lo] = colv;
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const bf16x8 b = kfrag<D, S>(kb * 32 + lo, 2 * ks + hi);
+    h[0] = mfma32(qf[0][ks], b, h[0]);
+    h[1] = mfma32(qf[1][ks], b, h[1]);
   }
+}
+
+// Row off + i_wave + 32 mb + 4 hi + r_i does not see key t = t0h + lo iff r_i < t - (off +
+// i_wave + 32 mb + 4 hi) (causal), and no row sees a key t > N - 1: one compare per element.
+__device__ __forceinline__ void score_mask_half(f32x16 (&h)[2], const Geo& G, int t0h, int N, int causal) {
+  const int t = t0h + G.lo;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    int M = causal ? t - (G.off + G.i_wave + 32 * mb + 4 * G.hi) : -1;
+    if (t > N - 1) M = 64;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 8 * (i >> 2) + (i & 3);
+      h[mb][i] = (r < M) ? -INFINITY : h[mb][i];
+    }
+  }
+}
+
+// Column value of one half tile for this wave's 64 rows, written to cbw[32 kb + lo].
+template <bool MAXMODE>
+__device__ __forceinline__ void score_reduce_half(const f32x16 (&h)[2], const float (&lv)[2][16],
+                                                  float c, int hi, int lo, float* cbw) {
+  float colv;
+  if (MAXMODE) {
+    float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        m0 = fmaxf(m0, fmaf(h[mb][i], c, -lv[mb][i]));
+        m1 = fmaxf(m1, fmaf(h[mb][i + 1], c, -lv[mb][i + 1]));
+      }
+    colv = half_max(fmaxf(m0, m1));
+  } else {
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      s0 += fast_exp2(fmaf(h[0][i], c, -lv[0][i]));
+      s1 += fast_exp2(fmaf(h[0][i + 1], c, -lv[0][i + 1]));
+      s2 += fast_exp2(fmaf(h[1][i], c, -lv[1][i]));
+      s3 += fast_exp2(fmaf(h[1][i + 1], c, -lv[1][i + 1]));
+    }
+    colv = half_sum((s0 + s1) + (s2 + s3));
+  }
+  if (hi == 0) cbw[lo] = colv;
 }
 
 // Four waves' partials of one 64-key tile, combined in a fixed order.
@@ -411,14 +477,46 @@ __device__ __forceinline__ float combine4(const float* cp) {
   return (cp[0] + cp[64]) + (cp[128] + cp[192]);
 }
 
+// Ring step J (pipelined, tile J fully visible): tile J's halves are reduced in step J
+// (first half) and step J + 1 (second half), so the LDS partials of tile J are complete at
+// the barrier of step J + 2, where the first wave combines and stores them (three partial
+// buffers rotate).  B holds the previous tile's second half (all -inf before the first step,
+// which then writes zeros into a buffer that is rewritten before it is read).
 #define KVC_SCORE_STEP(S, J)                                                                \
   {                                                                                         \
     ring_barrier<D>(2);                                                                     \
-    if ((J) > 0 && threadIdx.x < 64)                                                        \
-      out[G.k0 + 64 * ((J) - 1) + (int)threadIdx.x] = combine4<MAXMODE>(&cb[((J) - 1) & 1][0][threadIdx.x]); \
-    issue_tile<D, ((S) + 3) & 3>(kh, G.k0 + 64 * ((J) + 3), n, voff, G.wave);    \
-    score_tile<D, MAXMODE, S>(G, qf, lv, G.k0 + 64 * (J), n, causal, c, cb[(J) & 1][G.wave]); \
+    if ((J) > 1 && threadIdx.x < 64)                                                        \
+      out[G.k0 + 64 * ((J) - 2) + (int)threadIdx.x] = combine4<MAXMODE>(&cb[((J) + 1) % 3][0][threadIdx.x]); \
+    issue_tile<D, ((S) + 3) & 3>(kh, G.k0 + 64 * ((J) + 3), n, voff, G.wave);               \
+    KVC_PHASE_FENCE();                                                                      \
+    score_mfma_half<D, S>(A, qf, 0, G.lo, G.hi);                                            \
+    score_reduce_half<MAXMODE>(B, lv, c, G.hi, G.lo, &cb[((J) + 2) % 3][G.wave][32]);        \
+    KVC_PHASE_FENCE();                                                                      \
+    score_mfma_half<D, S>(B, qf, 1, G.lo, G.hi);                                            \
+    score_reduce_half<MAXMODE>(A, lv, c, G.hi, G.lo, &cb[(J) % 3][G.wave][0]);               \
+    KVC_PHASE_FENCE();                                                                      \
   }
+
+// Masked step (no pipelining) for tiles that cross the causal diagonal or the end of the
+// cache: both halves of tile J are masked and reduced in this step.
+template <int D, bool MAXMODE, int S>
+__device__ __forceinline__ void score_masked_step(const Geo& G, const uint16_t* kh, int J, int n, int causal,
+                                                  const int (&voff)[4], const bf16x8 (&qf)[2][D / 16],
+                                                  const float (&lv)[2][16], float c, float (&cb)[3][4][64],
+                                                  float* out) {
+  ring_barrier<D>(2);
+  if (J > 1 && threadIdx.x < 64)
+    out[G.k0 + 64 * (J - 2) + (int)threadIdx.x] = combine4<MAXMODE>(&cb[(J + 1) % 3][0][threadIdx.x]);
+  issue_tile<D, (S + 3) & 3>(kh, G.k0 + 64 * (J + 3), n, voff, G.wave);
+  const int t0 = G.k0 + 64 * J;
+  f32x16 h[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    score_mfma_half<D, S>(h, qf, kb, G.lo, G.hi);
+    score_mask_half(h, G, t0 + 32 * kb, n, causal);
+    score_reduce_half<MAXMODE>(h, lv, c, G.hi, G.lo, &cb[J % 3][G.wave][32 * kb]);
+  }
+}
 
 template <int D, bool MAXMODE>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -426,7 +524,7 @@ score_partial(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
               const float* __restrict__ lse, const float* __restrict__ hlog2,
               float* __restrict__ part, Decomp dc, int64_t N, int64_t Nq, int causal, float c,
               int64_t Npad) {
-  __shared__ float cb[2][4][64];
+  __shared__ float cb[3][4][64];
   __shared__ float lrow[kRowsPerBlock];
   Geo G;
   if (!geo_of(dc, N, Nq, causal, G)) return;
@@ -456,19 +554,40 @@ score_partial(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) lv[mb][i] = lrow[64 * G.wave + 32 * mb + acc_row(i, G.hi)];
+  const int nfull = full_tiles(G, n, causal);
   int j0 = 0;
-  for (; j0 + 4 <= G.ntiles; j0 += 4) {
-    KVC_SCORE_STEP(0, j0)
-    KVC_SCORE_STEP(1, j0 + 1)
-    KVC_SCORE_STEP(2, j0 + 2)
-    KVC_SCORE_STEP(3, j0 + 3)
+  {
+    f32x16 A[2], B[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) B[mb][i] = -INFINITY;
+    for (; j0 + 4 <= nfull; j0 += 4) {
+      KVC_SCORE_STEP(0, j0)
+      KVC_SCORE_STEP(1, j0 + 1)
+      KVC_SCORE_STEP(2, j0 + 2)
+      KVC_SCORE_STEP(3, j0 + 3)
+    }
+    if (j0 < nfull) KVC_SCORE_STEP(0, j0)
+    if (j0 + 1 < nfull) KVC_SCORE_STEP(1, j0 + 1)
+    if (j0 + 2 < nfull) KVC_SCORE_STEP(2, j0 + 2)
+    if (nfull > 0) score_reduce_half<MAXMODE>(B, lv, c, G.hi, G.lo, &cb[(nfull - 1) % 3][G.wave][32]);
   }
-  if (j0 < G.ntiles) KVC_SCORE_STEP(0, j0)
-  if (j0 + 1 < G.ntiles) KVC_SCORE_STEP(1, j0 + 1)
-  if (j0 + 2 < G.ntiles) KVC_SCORE_STEP(2, j0 + 2)
+  for (int j = nfull; j < G.ntiles; ++j) {
+    switch (j & 3) {
+      case 0: score_masked_step<D, MAXMODE, 0>(G, kh, j, n, causal, voff, qf, lv, c, cb, out); break;
+      case 1: score_masked_step<D, MAXMODE, 1>(G, kh, j, n, causal, voff, qf, lv, c, cb, out); break;
+      case 2: score_masked_step<D, MAXMODE, 2>(G, kh, j, n, causal, voff, qf, lv, c, cb, out); break;
+      default: score_masked_step<D, MAXMODE, 3>(G, kh, j, n, causal, voff, qf, lv, c, cb, out); break;
+    }
+  }
+  const int nt = G.ntiles;
   ring_barrier<D>(0);                        // also: no LDS fill may outlive the block
-  if (threadIdx.x < 64)
-    out[G.k0 + 64 * (G.ntiles - 1) + (int)threadIdx.x] = combine4<MAXMODE>(&cb[(G.ntiles - 1) & 1][0][threadIdx.x]);
+  if (threadIdx.x < 64) {
+    if (nt > 1)
+      out[G.k0 + 64 * (nt - 2) + (int)threadIdx.x] = combine4<MAXMODE>(&cb[(nt - 2) % 3][0][threadIdx.x]);
+    out[G.k0 + 64 * (nt - 1) + (int)threadIdx.x] = combine4<MAXMODE>(&cb[(nt - 1) % 3][0][threadIdx.x]);
+  }
 }
 
 // SUM: w[g][t] = sum over the group's (head, row tile) pairs that see t.  Four lanes share a
