@@ -39,11 +39,26 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Exchange with the lane 32 apart (the other half of a 32x32 accumulator column).
 __device__ __forceinline__ float swap_half(float x) { return __shfl_xor(x, 32, 64); }
 
+// max of three values with one v_max3_f32.  fmaxf() on matrix-core results makes the compiler
+// quiet possible signalling NaNs first (an extra instruction per operand); the values here are
+// never NaN, so the raw instruction gives the same result.
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // max / sum of a value and the one held 32 lanes away, on the VALU (v_permlane32_swap): lane
 // l < 32 sees (x[l], x[l + 32]), lane l >= 32 sees (x[l - 32], x[l]); both get the same result.
+// (max: values are never NaN here, see max3_raw.)
 __device__ __forceinline__ float half_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float half_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
