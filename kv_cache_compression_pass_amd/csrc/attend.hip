@@ -3,13 +3,17 @@
 // output Y_hat and the row LSE l_hat whose errors against the full cache are the two terms of
 // KVSculpt's loss (KVSculpt summary §2).
 //
-// Block = (4 waves, key split, KV head g); wave = one query head of the group x 32 query
-// rows.  For each group of 32 retained tokens (the K packing unit) the block decodes
+// Block = (8 waves, key split, KV head g); wave = one query head of the group x 32 query
+// rows.  The block first lays out the head's K channel table once (block scan over the
+// channel widths: word offset and parameter slot per channel, channels ordered by width).
+// Then for each group of 32 retained tokens (the K packing unit) it decodes
 //   K_hat -> LDS as a bf16 hi/lo pair (K_hat = hi + lo to ~2^-17; the bf16 query is exact, so
 //            q.K_hat = q.hi + q.lo is two bf16 matrix-core products with fp32 accumulation),
 //   V_hat -> LDS transposed as fp16 [channel][token],
-// then S = K_hat Q^T (32x32x16 bf16), an online base-2 softmax per row, and
-// O^T += V_hat^T P^T (32x32x16 f16).  In both products a lane owns one query row, so the
+// each thread unpacking a run of codes of one channel (K) or one token's group (V) from a
+// 64-bit window with shifts (no divisions); the channel order by width keeps the lanes of a
+// wave on one width.  Then S = K_hat Q^T (32x32x16 bf16), an online base-2 softmax per row,
+// and O^T += V_hat^T P^T (32x32x16 f16).  In both products a lane owns one query row, so the
 // softmax statistics and the output rescale stay in-lane.  P^T is taken straight from the S
 // accumulator: lane l holds keys 8(i/4) + 4(l/32) + i%4, and the V_hat^T operand is read with
 // the same key order, which is a valid ordering of the contraction index.
@@ -21,7 +25,8 @@ namespace kvc {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
+constexpr int kThreadsA = 64 * kWaves;
 constexpr int kRows = 32;   // query rows per wave
 
 template <int D>
@@ -29,27 +34,38 @@ struct AttnSmem {
   uint16_t khi[32][D + 8];
   uint16_t klo[32][D + 8];
   _Float16 vt[D][32 + 8];
-  int32_t woff[D];
-  int32_t qslot[D];
-  int32_t width[D];
+  int32_t kinfo[D][4];     // channels in width order: {channel, word offset, param slot, width}
   int32_t tok[32];
   int32_t vloc[32];
+  uint64_t scan[kWaves];
 };
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// bf16 hi/lo split of x (hardware round-to-nearest-even conversions): low 16 bits hi, high lo.
+__device__ __forceinline__ uint32_t bf16_hilo(float x) {
+  const __bf16 h = (__bf16)x;
+  const __bf16 l = (__bf16)(x - (float)h);
+  return (uint32_t)__builtin_bit_cast(uint16_t, h) | ((uint32_t)__builtin_bit_cast(uint16_t, l) << 16);
+}
+
+// 64 bits of a word stream starting at word wi (the second word only if `two`).
+__device__ __forceinline__ uint64_t load_window(const uint32_t* w, int64_t wi, bool two) {
+  const uint64_t lo = w[wi];
+  const uint64_t hi = two ? w[wi + 1] : 0u;
+  return lo | (hi << 32);
 }
 
 template <int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kThreadsA)
 attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __restrict__ part,
              int G, int Hkv, int64_t N, int64_t Nq, int causal, float c, int nsplit,
              int32_t* status) {
   constexpr int KS = D / 16;
   constexpr int GPR = D / 32;
   constexpr int PSTRIDE = D + 2;
+  constexpr int KP = kThreadsA / D;        // K decode: threads per channel
+  constexpr int KE = 32 / KP;              // K decode: tokens per thread (8 or 4)
+  constexpr int VP = kThreadsA / (32 * GPR);   // V decode: threads per (token, group)
+  constexpr int VE = 32 / VP;              // V decode: channels per thread (8)
   __shared__ AttnSmem<D> sm;
 
   const int lane = threadIdx.x & 63;
@@ -80,17 +96,33 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
   const int64_t j_begin = (int64_t)split * gps;
   const int64_t j_end_raw = j_begin + gps < ngroups ? j_begin + gps : ngroups;
 
-  // channel tables of this head's K packing
-  if (threadIdx.x == 0) {
-    int32_t wo = 0, qs = 0;
-    for (int cc = 0; cc < D; ++cc) {
-      int b = cache.k_width[(int64_t)g * D + cc];
-      if (!valid_width((uint32_t)b)) b = 0;
-      sm.width[cc] = b;
-      sm.woff[cc] = wo;
-      sm.qslot[cc] = qs;
-      wo += b;
-      qs += (b == 2 || b == 4 || b == 8);
+  // channel table of this head's K packing: one uint64 per channel packs {words (16 bits),
+  // params (16 bits), an 8-bit count per width class}; one block scan places every channel
+  {
+    uint32_t b = 0;
+    int cls = 4;
+    uint64_t f = 0;
+    const int t = threadIdx.x;
+    if (t < D) {
+      b = cache.k_width[(int64_t)g * D + t];
+      cls = b == 2 ? 0 : b == 4 ? 1 : b == 8 ? 2 : b == 16 ? 3 : 4;
+      if (cls < 4) f = (uint64_t)b | ((uint64_t)(cls < 3) << 16) | (1ull << (32 + 8 * cls));
+    }
+    uint64_t tf;
+    const uint64_t ef = block_excl_scan<kThreadsA>(f, &tf, sm.scan);
+    if (t < D) {
+      int pos = 0, before = 0, nnz = 0;
+      for (int k2 = 0; k2 < 4; ++k2) {
+        const int tk = (int)((tf >> (32 + 8 * k2)) & 0xFF);
+        if (k2 < cls) pos += tk;
+        before += (int)((ef >> (32 + 8 * k2)) & 0xFF);
+        nnz += tk;
+      }
+      pos = cls < 4 ? pos + (int)((ef >> (32 + 8 * cls)) & 0xFF) : nnz + (t - before);
+      sm.kinfo[pos][0] = t;
+      sm.kinfo[pos][1] = (int32_t)(ef & 0xFFFF);
+      sm.kinfo[pos][2] = (int32_t)((ef >> 16) & 0xFFFF);
+      sm.kinfo[pos][3] = cls < 4 ? (int32_t)b : 0;
     }
   }
 
@@ -123,6 +155,7 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
     for (int i = 0; i < 16; ++i) o[mb][i] = 0.f;
 
   __syncthreads();
+  const int4 kinf = *reinterpret_cast<const int4*>(sm.kinfo[threadIdx.x % D]);   // this thread's K channel
   for (int64_t j = j_begin; j < j_end_raw; ++j) {
     const int m_valid = (int)((R - j * 32) < 32 ? (R - j * 32) : 32);
     if (threadIdx.x < 32) {
@@ -132,68 +165,76 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
     }
     __syncthreads();
     if (sm.tok[0] > pmax_block) break;      // retained tokens ascend: nothing visible later
-    // ---- decode K_hat: thread -> (channel, quarter of the 32 tokens)
+    // ---- decode K_hat: thread -> (channel in width order, run of KE tokens)
     {
-      constexpr int TPC = 256 / D;         // threads per channel (2 or 4)
-      constexpr int EPT = 32 / TPC;        // tokens per thread
-      const int cc = threadIdx.x % D;
-      const int e0 = (threadIdx.x / D) * EPT;
-      const int b = sm.width[cc];
-      const uint32_t* wp = cache.k_words + hp[18] + j * Wk + sm.woff[cc];
-      float s = 0.f, z = 0.f;
-      if (b == 2 || b == 4 || b == 8) {
-        const float* pp = cache.k_par + 2 * (hp[19] + j * Qk + sm.qslot[cc]);
-        s = pp[0];
-        z = pp[1];
-      }
-      for (int e = e0; e < e0 + EPT; ++e) {
-        uint16_t vh = 0, vl = 0;
-        if (b == 16) {
-          vh = (uint16_t)((wp[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
-        } else if (b != 0) {
-          const int per = 32 / b;
-          const uint32_t code = (wp[e / per] >> ((e % per) * b)) & ((1u << b) - 1u);
-          const float x = fmaf(s, (float)code, z);
-          vh = f32_to_bf16_rne(x);
-          vl = f32_to_bf16_rne(x - bf16_bits_to_f32(vh));
+      const int cc = kinf.x, b = kinf.w;
+      const int e0 = (threadIdx.x / D) * KE;
+      uint32_t hl2[KE];
+      if (b == 0) {
+#pragma unroll
+        for (int k = 0; k < KE; ++k) hl2[k] = 0u;
+      } else {
+        const uint32_t* wp = cache.k_words + hp[18] + j * Wk + kinf.y;
+        if (b == 16) {                       // raw bf16 (lo = 0): KE / 2 words
+#pragma unroll
+          for (int k = 0; k < KE; k += 2) {
+            const uint32_t w = wp[(e0 + k) >> 1];
+            hl2[k] = w & 0xFFFFu;
+            hl2[k + 1] = w >> 16;
+          }
+        } else {
+          const int bit0 = e0 * b;             // KE * b <= 64 bits from bit0
+          const uint64_t win = load_window(wp, bit0 >> 5, (bit0 & 31) + KE * b > 32) >> (bit0 & 31);
+          const float2 sz = *reinterpret_cast<const float2*>(cache.k_par + 2 * (hp[19] + j * Qk + kinf.z));
+          const uint32_t mask = (1u << b) - 1u;
+#pragma unroll
+          for (int k = 0; k < KE; ++k) {
+            const uint32_t code = (uint32_t)(win >> (k * b)) & mask;
+            hl2[k] = bf16_hilo(fmaf(sz.x, (float)code, sz.y));
+          }
         }
-        sm.khi[e][cc] = vh;
-        sm.klo[e][cc] = vl;
+      }
+#pragma unroll
+      for (int k = 0; k < KE; ++k) {
+        sm.khi[e0 + k][cc] = (uint16_t)(hl2[k] & 0xFFFFu);
+        sm.klo[e0 + k][cc] = (uint16_t)(hl2[k] >> 16);
       }
     }
-    // ---- decode V_hat^T: thread -> (token, 32-channel group, half of the group)
+    // ---- decode V_hat^T: thread -> (token e, 32-channel group, run of VE channels)
     {
-      for (int task = threadIdx.x; task < 32 * GPR * 2; task += 256) {
-        const int e = task / (GPR * 2);
-        const int rem = task % (GPR * 2);
-        const int grp = rem / 2;
-        const int half = rem % 2;
-        if (e >= m_valid) {
-          for (int cc = 0; cc < 16; ++cc) sm.vt[grp * 32 + half * 16 + cc][e] = (_Float16)0.f;
-          continue;
-        }
+      const int task = threadIdx.x;
+      const int e = task / (GPR * VP);
+      const int grp = (task / VP) % GPR;
+      const int c0 = (task % VP) * VE;
+      _Float16 vv[VE];
+      if (e >= m_valid) {
+#pragma unroll
+        for (int k = 0; k < VE; ++k) vv[k] = (_Float16)0.f;
+      } else {
         const int32_t loc = sm.vloc[e];
         const int z = loc >> 29;
         const int64_t vpos = loc & ((1 << 29) - 1);
         const int b = 2 << z;
         const uint32_t* wp = cache.v_words + hp[9 + z] + (vpos * GPR + grp) * b;
-        if (b == 16) {
-          for (int cc = 0; cc < 16; ++cc) {
-            const int el = half * 16 + cc;
-            float x = bf16_bits_to_f32((wp[el >> 1] >> ((el & 1) * 16)) & 0xFFFFu);
-            sm.vt[grp * 32 + el][e] = (_Float16)x;
+        if (b == 16) {                       // raw bf16: VE / 2 words
+#pragma unroll
+          for (int k = 0; k < VE; k += 2) {
+            const uint32_t w = wp[(c0 + k) >> 1];
+            vv[k] = (_Float16)bf16_bits_to_f32(w & 0xFFFFu);
+            vv[k + 1] = (_Float16)bf16_bits_to_f32(w >> 16);
           }
         } else {
-          const float* pp = cache.v_par + 2 * (hp[13 + z] + vpos * GPR + grp);
-          const float s = pp[0], zz = pp[1];
-          const int per = 32 / b;
-          for (int cc = 0; cc < 16; ++cc) {
-            const int el = half * 16 + cc;
-            const uint32_t code = (wp[el / per] >> ((el % per) * b)) & ((1u << b) - 1u);
-            sm.vt[grp * 32 + el][e] = (_Float16)fmaf(s, (float)code, zz);
-          }
+          const int bit0 = c0 * b;             // VE * b <= 64 bits from bit0
+          const uint64_t win = load_window(wp, bit0 >> 5, (bit0 & 31) + VE * b > 32) >> (bit0 & 31);
+          const float2 sz = *reinterpret_cast<const float2*>(cache.v_par + 2 * (hp[13 + z] + vpos * GPR + grp));
+          const uint32_t mask = (1u << b) - 1u;
+#pragma unroll
+          for (int k = 0; k < VE; ++k)
+            vv[k] = (_Float16)fmaf(sz.x, (float)((uint32_t)(win >> (k * b)) & mask), sz.y);
         }
       }
+#pragma unroll
+      for (int k = 0; k < VE; ++k) sm.vt[grp * 32 + c0 + k][e] = vv[k];
     }
     __syncthreads();
     const int64_t t_first = sm.tok[0];
@@ -210,16 +251,18 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
       }
       float x[16];
       float tmax = -INFINITY;
+      const bool full = m_valid == 32 && (!causal || sm.tok[31] <= off + r0);   // uniform per wave
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int e = acc_row(i, hi);
-        const int64_t t = sm.tok[e];
-        float v = acc[i] * c;
-        if (e >= m_valid || (causal && t > pos)) v = -INFINITY;
-        x[i] = v;
-        tmax = fmaxf(tmax, v);
+      for (int i = 0; i < 16; ++i) x[i] = acc[i] * c;
+      if (!full) {
+        // slots past m_valid hold the sentinel 0x7FFFFFFF, so one compare covers both masks
+        const int lim = causal ? (int)pos : 0x7FFFFFFE;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = (sm.tok[acc_row(i, hi)] <= lim) ? x[i] : -INFINITY;
       }
-      tmax = fmaxf(tmax, swap_half(tmax));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, x[i]);
+      tmax = half_max(tmax);
       const float mnew = fmaxf(m_run, tmax);
       float p[16];
       float alpha = 1.f;
@@ -334,9 +377,9 @@ hipError_t launch_attend(const Layer& L, const uint16_t* q, const kvc_packed_cac
   dim3 grid((unsigned)((L.G * nRT + kWaves - 1) / kWaves), (unsigned)nsplit, (unsigned)L.hkv);
   int32_t* status = reinterpret_cast<int32_t*>(ws);
   if (L.d == 128)
-    attend_split<128><<<grid, 256, 0, s>>>(q, cache, part, L.G, L.hkv, L.n, L.nq, L.causal, L.c_log2, nsplit, status);
+    attend_split<128><<<grid, kThreadsA, 0, s>>>(q, cache, part, L.G, L.hkv, L.n, L.nq, L.causal, L.c_log2, nsplit, status);
   else
-    attend_split<64><<<grid, 256, 0, s>>>(q, cache, part, L.G, L.hkv, L.n, L.nq, L.causal, L.c_log2, nsplit, status);
+    attend_split<64><<<grid, kThreadsA, 0, s>>>(q, cache, part, L.G, L.hkv, L.n, L.nq, L.causal, L.c_log2, nsplit, status);
   attend_merge<<<(unsigned)((int64_t)L.hq * L.nq), 128, 0, s>>>(part, out, lse, L.d, nsplit);
   return hipGetLastError();
 }

@@ -74,4 +74,34 @@ __device__ __forceinline__ bool valid_width(uint32_t b) {
   return b == 0 || b == 2 || b == 4 || b == 8 || b == 16;
 }
 
+// Exclusive prefix sum of one uint64 per thread over a block of NT threads (NT % 64 == 0);
+// *total receives the block total.  sh holds NT / 64 entries.  Every thread must call it.
+template <int NT>
+__device__ __forceinline__ uint64_t block_excl_scan(uint64_t v, uint64_t* total, uint64_t* sh) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint64_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t lo = __shfl_up((uint32_t)x, o, 64), hi = __shfl_up((uint32_t)(x >> 32), o, 64);
+    if (lane >= o) x += ((uint64_t)hi << 32) | lo;
+  }
+  if (lane == 63) sh[wid] = x;
+  __syncthreads();
+  if (wid == 0) {
+    uint64_t y = lane < NW ? sh[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < NW; o <<= 1) {
+      const uint32_t lo = __shfl_up((uint32_t)y, o, 64), hi = __shfl_up((uint32_t)(y >> 32), o, 64);
+      if (lane >= o) y += ((uint64_t)hi << 32) | lo;
+    }
+    if (lane < NW) sh[lane] = y;       // inclusive wave totals
+  }
+  __syncthreads();
+  const uint64_t r = (wid > 0 ? sh[wid - 1] : 0) + x - v;
+  *total = sh[NW - 1];
+  __syncthreads();                     // sh may be reused by the caller's next scan
+  return r;
+}
+
 }  // namespace kvc

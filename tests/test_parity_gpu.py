@@ -236,3 +236,24 @@ def test_determinism_bitwise():
     for g, t in mism:
         ks = oracle.step_keys(np.array([w_r[g, t]], np.float32), np.array([d]))[0]
         assert np.min(np.abs(ks - lam)) <= 2e-3 * lam
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("bvv,bkk", [(16, 16), (16, 8), (8, 16), (4, 4), (2, 2)])
+def test_attend_group_aligned_uniform_widths(bvv, bkk):
+    """Every K group full (N a multiple of 32, nothing evicted): the causal mask must act inside
+    full groups too, at every width."""
+    hq, hkv, d, N, Nq, nf = 4, 1, 128, 64, 64, 64
+    x = make_inputs(hq, hkv, d, N, Nq, seed=5)
+    desc = H.desc_of(hq, hkv, d, N, Nq, True)
+    k, v = H.dev_bf16(x["k"]), H.dev_bf16(x["v"])
+    bv = np.full((hkv, N), bvv, np.uint8)
+    bk = np.full((hkv, d), bkk, np.uint8)
+    cache, st = H.pack(desc, k, v, H.dev_u8(bv), H.dev_u8(bk))
+    assert st == 0
+    qf = np.ascontiguousarray(x["q"][:, Nq - nf:, :])
+    y_g, l_g, st2 = H.attend(H.desc_of(hq, hkv, d, N, nf, True), H.dev_bf16(qf), cache)
+    assert st2 == 0
+    y_r, l_r = oracle.compressed_attend(qf, x["k"], x["v"], bv, bk)
+    H.assert_abs(y_g.cpu().numpy(), y_r, 2e-2, "attend output")
+    H.assert_abs(l_g.cpu().numpy(), l_r, 1e-3, "attend lse")
