@@ -650,13 +650,18 @@ score_reduce_sum(const float* __restrict__ part, float* __restrict__ scores, int
 }
 
 // MAX: s+[g][t] = max over the group's heads h of 2^(max over row tiles of part) / ||W_O^h v_t||.
-__global__ void score_reduce_max(const float* __restrict__ part, const float* __restrict__ won,
-                                 float* __restrict__ scores, int Hkv, int G, int nRT, int64_t N,
-                                 int64_t Nq, int causal, int64_t Npad) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)Hkv * N) return;
-  const int g = (int)(idx / N);
-  const int64_t t = idx % N;
+// Four lanes share a key: lane r takes the row tiles rt = rt0 + r, rt0 + r + 4, ...; the maxima
+// are combined across the four lanes (max is exact in any order).
+__global__ void __launch_bounds__(256)
+score_reduce_max(const float* __restrict__ part, const float* __restrict__ won,
+                 float* __restrict__ scores, int Hkv, int G, int nRT, int64_t N,
+                 int64_t Nq, int causal, int64_t Npad) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t idx = gid >> 2;
+  const int r = (int)(gid & 3);
+  const bool ok = idx < (int64_t)Hkv * N;
+  const int g = ok ? (int)(idx / N) : 0;
+  const int64_t t = ok ? idx % N : 0;
   int rt0 = 0;
   if (causal) {
     const int64_t rel = t - (N - Nq);
@@ -666,81 +671,112 @@ __global__ void score_reduce_max(const float* __restrict__ part, const float* __
   for (int hl = 0; hl < G; ++hl) {
     const int hh = g * G + hl;
     const float* p = part + ((int64_t)hh * nRT) * Npad + t;
-    float m = -INFINITY;
-    for (int rt = rt0; rt < nRT; ++rt) m = fmaxf(m, p[(int64_t)rt * Npad]);
+    float m0 = -INFINITY, m1 = -INFINITY;
+    int rt = rt0 + r;
+    for (; rt + 4 < nRT; rt += 8) {
+      m0 = fmaxf(m0, p[(int64_t)rt * Npad]);
+      m1 = fmaxf(m1, p[(int64_t)(rt + 4) * Npad]);
+    }
+    if (ok && rt < nRT) m0 = fmaxf(m0, p[(int64_t)rt * Npad]);
+    float m = fmaxf(m0, m1);
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    m = fmaxf(m, __shfl_xor(m, 2, 64));
     const float num = exp2f(m);
-    const float den = won[(int64_t)hh * N + t];
-    const float r = (num == 0.f && den == 0.f) ? 0.f : num / den;
-    best = fmaxf(best, r);
+    const float den = ok ? won[(int64_t)hh * N + t] : 1.f;
+    const float q = (num == 0.f && den == 0.f) ? 0.f : num / den;
+    best = fmaxf(best, q);
   }
-  scores[idx] = best;
+  if (ok && r == 0) scores[idx] = best;
 }
 
-// log2 ||h_j||_2 per query row (float64 accumulation of the squares).
+// log2 ||h_j||_2 per query row: one wave per row, 16-byte loads, float64 sums of the squares
+// (bf16 squares are exact in fp32), a fixed-order wave reduction.
 __global__ void __launch_bounds__(256)
-hidden_log2_norm(const uint16_t* __restrict__ hidden, float* __restrict__ hlog2, int Dh) {
-  const int64_t row = blockIdx.x;
+hidden_log2_norm(const uint16_t* __restrict__ hidden, float* __restrict__ hlog2, int Dh, int64_t Nq) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= Nq) return;
   const uint16_t* hp = hidden + row * Dh;
   double ss = 0.0;
-  for (int i = threadIdx.x; i < Dh; i += blockDim.x) {
-    double v = (double)bf16_bits_to_f32(hp[i]);
-    ss += v * v;
+  if ((Dh & 7) == 0) {
+    for (int i = 8 * lane; i < Dh; i += 512) {
+      const uint4 w = *reinterpret_cast<const uint4*>(hp + i);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a = bf16_bits_to_f32(ww[j] & 0xFFFFu), b = bf16_bits_to_f32(ww[j] >> 16);
+        ss += (double)(a * a) + (double)(b * b);
+      }
+    }
+  } else {
+    for (int i = lane; i < Dh; i += 64) {
+      const float a = bf16_bits_to_f32(hp[i]);
+      ss += (double)(a * a);
+    }
   }
-  __shared__ double red[256];
-  red[threadIdx.x] = ss;
-  __syncthreads();
-  for (int w = 128; w >= 1; w >>= 1) {
-    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) hlog2[row] = (float)(0.5 * log2(red[0]));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  if (lane == 0) hlog2[row] = (float)(0.5 * log2(ss));
 }
 
-// Partial Gram matrices of each head's W_O slice: gp[h][s][c1][c2] = sum over rows r of
-// split s of W[r][h*d + c1] * W[r][h*d + c2]  (products of bf16 are exact in fp32).
+// Partial Gram matrices of each head's W_O slice on the matrix cores: gp[h][s][c1][c2] = sum over
+// rows r of split s of S[r][c1] S[r][c2], S[r][c] = W_O[r][h*d + c] (bf16 products are exact;
+// fp32 accumulation).  Rows are staged 64 at a time in LDS transposed, T[c][r], so both operands
+// of D[m = c1][n = c2] read 8 consecutive rows of one column with one 16-byte load.  Wave w
+// owns output row block c1 in [32w, 32w + 32) (D = 128; for D = 64 waves 2, 3 idle).
 template <int D>
 __global__ void __launch_bounds__(256)
 wo_gram_partial(const uint16_t* __restrict__ w_o, float* __restrict__ gp, int Hq, int Dh,
                 int rows_per_split) {
-  constexpr int RB = 32;   // rows staged per step
-  __shared__ float ws[RB][D + 1];
+  constexpr int RB = 64;          // rows staged per step
+  constexpr int NB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t T[D][RB + 8];
   const int h = blockIdx.x;
   const int s = blockIdx.y;
   const int r0 = s * rows_per_split;
   const int r1 = (r0 + rows_per_split < Dh) ? r0 + rows_per_split : Dh;
-  constexpr int T = D / 16;     // entries per thread per dimension
-  const int ty = threadIdx.x / 16, tx = threadIdx.x % 16;
-  float acc[T][T];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hi = lane >> 5, lo = lane & 31;
+  const bool owner = wave < NB;
+  f32x16 acc[NB];
 #pragma unroll
-  for (int a = 0; a < T; ++a)
+  for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int b = 0; b < T; ++b) acc[a][b] = 0.f;
+    for (int i = 0; i < 16; ++i) acc[nb][i] = 0.f;
   const int64_t ld = (int64_t)Hq * D;
   for (int rb = r0; rb < r1; rb += RB) {
     __syncthreads();
-    for (int e = threadIdx.x; e < RB * D; e += 256) {
-      int rr = e / D, cc = e % D;
-      int r = rb + rr;
-      ws[rr][cc] = (r < r1) ? bf16_bits_to_f32(w_o[(int64_t)r * ld + (int64_t)h * D + cc]) : 0.f;
+    for (int e = threadIdx.x; e < RB * (D / 8); e += 256) {   // 16-byte loads along a row
+      const int rr = e / (D / 8), c8 = e % (D / 8);
+      const int r = rb + rr;
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (r < r1) w = *reinterpret_cast<const uint4*>(w_o + (int64_t)r * ld + (int64_t)h * D + 8 * c8);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        T[8 * c8 + 2 * j][rr] = (uint16_t)(ww[j] & 0xFFFFu);
+        T[8 * c8 + 2 * j + 1][rr] = (uint16_t)(ww[j] >> 16);
+      }
     }
     __syncthreads();
-    for (int rr = 0; rr < RB; ++rr) {
-      float x[T], y[T];
+    if (owner) {
 #pragma unroll
-      for (int a = 0; a < T; ++a) x[a] = ws[rr][ty * T + a];
+      for (int ks = 0; ks < RB / 16; ++ks) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&T[32 * wave + lo][16 * ks + 8 * hi]));
 #pragma unroll
-      for (int b = 0; b < T; ++b) y[b] = ws[rr][tx * T + b];
-#pragma unroll
-      for (int a = 0; a < T; ++a)
-#pragma unroll
-        for (int b = 0; b < T; ++b) acc[a][b] = fmaf(x[a], y[b], acc[a][b]);
+        for (int nb = 0; nb < NB; ++nb) {
+          const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4*>(&T[32 * nb + lo][16 * ks + 8 * hi]));
+          acc[nb] = mfma32(a, b, acc[nb]);
+        }
+      }
     }
   }
+  if (!owner) return;
   float* out = gp + ((int64_t)h * gridDim.y + s) * D * D;
 #pragma unroll
-  for (int a = 0; a < T; ++a)
+  for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int b = 0; b < T; ++b) out[(ty * T + a) * D + tx * T + b] = acc[a][b];
+    for (int i = 0; i < 16; ++i) out[(32 * wave + acc_row(i, hi)) * D + 32 * nb + lo] = acc[nb][i];
 }
 
 // Sum the Gram partials over splits in order: gram[h] = sum_s gp[h][s].
@@ -755,39 +791,70 @@ __global__ void wo_gram_reduce(const float* __restrict__ gp, float* __restrict__
   gram[idx] = s;
 }
 
-// ||W_O^h v_t||_2 = sqrt(v_t^T (W_O^h^T W_O^h) v_t): one token per thread, the Gram matrix of
-// head h in LDS (every lane reads the same entry: broadcast).
+// ||W_O^h v_t||_2 = sqrt(v_t^T G_h v_t), G_h = W_O^h^T W_O^h, on the matrix cores: for 32 tokens
+// at a time Y = G_h V^T (D[m = channel][n = token]; G_h split into bf16 hi + lo, so G_h = hi + lo
+// to ~2^-17 and the bf16 values are exact operands), then each lane forms sum_c V[t][c] Y[c][t]
+// for its token over its 16 channels per 32-channel block and the two lane halves are added.
+// Block = (4 waves x kVnTiles token blocks of 32, query head h); G_h is staged in LDS once.
+constexpr int kVnTiles = 4;
 template <int D>
 __global__ void __launch_bounds__(256)
 value_out_norm(const uint16_t* __restrict__ v, const float* __restrict__ gram,
                float* __restrict__ won, int G, int64_t N) {
-  __shared__ float gm[D * D];
+  constexpr int KS = D / 16, MB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t ghi[D][D + 8];
+  __shared__ __attribute__((aligned(16))) uint16_t glo[D][D + 8];
   const int h = blockIdx.y;
   const int g = h / G;
-  for (int e = threadIdx.x; e < D * D; e += 256) gm[e] = gram[(int64_t)h * D * D + e];
+  const float* gh = gram + (int64_t)h * D * D;
+  for (int e = threadIdx.x; e < D * D; e += 256) {
+    const float x = gh[e];
+    const __bf16 hb = (__bf16)x;
+    const __bf16 lb = (__bf16)(x - (float)hb);
+    ghi[e / D][e % D] = __builtin_bit_cast(uint16_t, hb);
+    glo[e / D][e % D] = __builtin_bit_cast(uint16_t, lb);
+  }
   __syncthreads();
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= N) return;
-  const uint16_t* vp = v + ((int64_t)g * N + t) * D;
-  float x[D];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hi = lane >> 5, lo = lane & 31;
+  const uint16_t* vh = v + (int64_t)g * N * D;
+  for (int tb = 0; tb < kVnTiles; ++tb) {
+    const int64_t t0 = ((int64_t)blockIdx.x * kVnTiles + tb) * 128 + 32 * wave;
+    if (t0 >= N) break;                       // uniform per wave
+    const int64_t t = t0 + lo;
+    const bool ok = t < N;
+    const uint16_t* vr = vh + (ok ? t : 0) * D;
+    f32x16 acc[MB];
 #pragma unroll
-  for (int c8 = 0; c8 < D / 8; ++c8) {
-    uint4 w = *reinterpret_cast<const uint4*>(vp + c8 * 8);
-    uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[c8 * 8 + 2 * j] = bf16_bits_to_f32(ww[j] & 0xFFFFu);
-      x[c8 * 8 + 2 * j + 1] = bf16_bits_to_f32(ww[j] >> 16);
+      for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 b = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(vr + 16 * ks + 8 * hi) : make_uint4(0, 0, 0, 0));
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const bf16x8 ah = as_bf16x8(*reinterpret_cast<const uint4*>(&ghi[32 * mb + lo][16 * ks + 8 * hi]));
+        const bf16x8 al = as_bf16x8(*reinterpret_cast<const uint4*>(&glo[32 * mb + lo][16 * ks + 8 * hi]));
+        acc[mb] = mfma32(ah, b, acc[mb]);
+        acc[mb] = mfma32(al, b, acc[mb]);
+      }
     }
-  }
-  float qf = 0.f;
-  for (int c1 = 0; c1 < D; ++c1) {
-    float y = 0.f;
+    float qf = 0.f;
 #pragma unroll
-    for (int c2 = 0; c2 < D; ++c2) y = fmaf(gm[c1 * D + c2], x[c2], y);
-    qf = fmaf(x[c1], y, qf);
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        // channels 32 mb + 8 q4 + 4 hi + (0..3) of this lane's token
+        const uint2 w = ok ? *reinterpret_cast<const uint2*>(vr + 32 * mb + 8 * q4 + 4 * hi) : make_uint2(0, 0);
+        qf = fmaf(bf16_bits_to_f32(w.x & 0xFFFFu), acc[mb][4 * q4 + 0], qf);
+        qf = fmaf(bf16_bits_to_f32(w.x >> 16), acc[mb][4 * q4 + 1], qf);
+        qf = fmaf(bf16_bits_to_f32(w.y & 0xFFFFu), acc[mb][4 * q4 + 2], qf);
+        qf = fmaf(bf16_bits_to_f32(w.y >> 16), acc[mb][4 * q4 + 3], qf);
+      }
+    qf = half_sum(qf);
+    if (hi == 0 && ok) won[(int64_t)h * N + t] = sqrtf(fmaxf(qf, 0.f));
   }
-  won[(int64_t)h * N + t] = sqrtf(fmaxf(qf, 0.f));
 }
 
 }  // namespace
@@ -893,7 +960,7 @@ hipError_t launch_score(const Layer& L, int mode, const uint16_t* q, const uint1
     float* gp = reinterpret_cast<float*>(ws + w.take((size_t)L.hq * kGramSplits * L.d * L.d * sizeof(float)));
     float* gram = reinterpret_cast<float*>(ws + w.take((size_t)L.hq * L.d * L.d * sizeof(float)));
     won = reinterpret_cast<float*>(ws + w.take((size_t)L.hq * L.n * sizeof(float)));
-    hidden_log2_norm<<<(unsigned)L.nq, 256, 0, s>>>(hidden, hlog2, hidden_dim);
+    hidden_log2_norm<<<(unsigned)((L.nq + 3) / 4), 256, 0, s>>>(hidden, hlog2, hidden_dim, L.nq);
     const int rps = (hidden_dim + kGramSplits - 1) / kGramSplits;
     dim3 gg((unsigned)L.hq, kGramSplits);
     if (L.d == 128)
@@ -902,7 +969,7 @@ hipError_t launch_score(const Layer& L, int mode, const uint16_t* q, const uint1
       wo_gram_partial<64><<<gg, 256, 0, s>>>(w_o, gp, L.hq, hidden_dim, rps);
     const int64_t ng = (int64_t)L.hq * L.d * L.d;
     wo_gram_reduce<<<(unsigned)((ng + 255) / 256), 256, 0, s>>>(gp, gram, L.hq, kGramSplits, L.d * L.d);
-    dim3 gv((unsigned)((L.n + 255) / 256), (unsigned)L.hq);
+    dim3 gv((unsigned)((L.n + 128 * kVnTiles - 1) / (128 * kVnTiles)), (unsigned)L.hq);
     if (L.d == 128)
       value_out_norm<128><<<gv, 256, 0, s>>>(v, gram, won, L.G, L.n);
     else
@@ -921,9 +988,8 @@ hipError_t launch_score(const Layer& L, int mode, const uint16_t* q, const uint1
       score_partial<64, false><<<grid, kThreads, 0, s>>>(q, k, lse, nullptr, part, dc, L.n, L.nq, L.causal, L.c_log2, p.Npad);
   }
   const int64_t total = (int64_t)L.hkv * L.n;
-  const unsigned rb = (unsigned)((total + 255) / 256);
   if (mx)
-    score_reduce_max<<<rb, 256, 0, s>>>(part, won, scores, L.hkv, L.G, p.nRT, L.n, L.nq, L.causal, p.Npad);
+    score_reduce_max<<<(unsigned)((4 * total + 255) / 256), 256, 0, s>>>(part, won, scores, L.hkv, L.G, p.nRT, L.n, L.nq, L.causal, p.Npad);
   else
     score_reduce_sum<<<(unsigned)((4 * total + 255) / 256), 256, 0, s>>>(part, scores, L.hkv, L.G, p.nRT, L.n, L.nq, L.causal, p.Npad);
   return hipGetLastError();
