@@ -273,19 +273,38 @@ pack_index(const uint8_t* __restrict__ bits_v, int64_t N, int nchunk,
   }
 }
 
-// Quantise one group of 32 values (the first m valid; the rest code 0) at width B and store
-// its B words and its (scale, zero) pair.
-template <int B>
-__device__ __forceinline__ void quantize_store(const float (&x)[32], int m, uint32_t* __restrict__ dst,
+// Quantise one group of 32 bf16 values, held as 16 packed pairs (element 2i in the low half of
+// raw[i]), at width B and store its B words and its (scale, zero) pair.  FULL: all 32 valid;
+// otherwise only the first m (>= 1) are, and the rest code 0.
+//  * min / max with v_min3 / v_max3 (values are finite; fminf would first quiet NaNs);
+//  * v = (x - z) * (1 / s) in fp32: 0 <= v < maxc + 2^-16, so rint(v) needs no clamp; where v is
+//    within 1e-4 of a half-integer the code is recomputed with the defining fp64 division.
+__device__ __forceinline__ float min3_raw(float a, float b, float c) {
+  float r;
+  asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float elem_of(const uint32_t (&raw)[16], int e) {
+  return (e & 1) ? __uint_as_float(raw[e >> 1] & 0xFFFF0000u) : __uint_as_float(raw[e >> 1] << 16);
+}
+
+template <int B, bool FULL>
+__device__ __forceinline__ void quantize_store(const uint32_t (&raw)[16], int m, uint32_t* __restrict__ dst,
                                                float* __restrict__ par) {
   constexpr float maxc = (float)((1 << B) - 1);
-  float mn = x[0], mx = x[0];
+  const float x0 = elem_of(raw, 0);
+  float mn = x0, mx = x0;
 #pragma unroll
-  for (int e = 1; e < 32; ++e) {
-    if (e < m) {
-      mn = fminf(mn, x[e]);
-      mx = fmaxf(mx, x[e]);
-    }
+  for (int e = 1; e < 31; e += 2) {
+    const float a = (FULL || e < m) ? elem_of(raw, e) : x0;
+    const float b = (FULL || e + 1 < m) ? elem_of(raw, e + 1) : x0;
+    mn = min3_raw(mn, a, b);
+    mx = max3_raw(mx, a, b);
+  }
+  {
+    const float a = (FULL || 31 < m) ? elem_of(raw, 31) : x0;
+    mn = min3_raw(mn, a, a);
+    mx = max3_raw(mx, a, a);
   }
   const float s = (float)(((double)mx - (double)mn) / (double)((1 << B) - 1));
   uint32_t w[B];
@@ -297,21 +316,28 @@ __device__ __forceinline__ void quantize_store(const float (&x)[32], int m, uint
     const double sd = (double)s;
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
-      const float v = (x[e] - mn) * rs;
+      const float x = elem_of(raw, e);
+      const float v = (x - mn) * rs;
       float r = rintf(v);
       if (!fast || fabsf(fabsf(v - r) - 0.5f) < 1e-4f) {
         // near a rounding boundary: decide with the defining fp64 division
-        const double vd = rint(((double)x[e] - (double)mn) / sd);
+        const double vd = rint(((double)x - (double)mn) / sd);
         r = (float)(vd < 0.0 ? 0.0 : (vd > (double)maxc ? (double)maxc : vd));
       }
-      r = __builtin_amdgcn_fmed3f(r, 0.f, maxc);
-      const uint32_t code = (e < m) ? (uint32_t)r : 0u;
+      const uint32_t code = (FULL || e < m) ? (uint32_t)r : 0u;
       w[(e * B) / 32] |= code << ((e * B) % 32);
     }
   }
 #pragma unroll
   for (int i = 0; i < B; ++i) dst[i] = w[i];
   *reinterpret_cast<float2*>(par) = make_float2(s, mn);
+}
+
+template <int B>
+__device__ __forceinline__ void quantize_store_m(const uint32_t (&raw)[16], int m, uint32_t* __restrict__ dst,
+                                                 float* __restrict__ par) {
+  if (m == 32) quantize_store<B, true>(raw, 32, dst, par);
+  else quantize_store<B, false>(raw, m, dst, par);
 }
 
 // K: block (group j of 32 retained tokens, head g) with D threads; thread i takes the i-th
@@ -353,13 +379,13 @@ __device__ __forceinline__ void pack_k_group(const uint16_t* __restrict__ k, int
     }
     return;
   }
-  float x[32];
+  uint32_t raw[16];
 #pragma unroll
-  for (int e = 0; e < 32; ++e) x[e] = bf16_bits_to_f32(tile[e][c]);
+  for (int i = 0; i < 16; ++i) raw[i] = (uint32_t)tile[2 * i][c] | ((uint32_t)tile[2 * i + 1][c] << 16);
   float* par = k_par + 2 * (hp[19] + j * hp[21] + info.z);
-  if (b == 2) quantize_store<2>(x, m, dst, par);
-  else if (b == 4) quantize_store<4>(x, m, dst, par);
-  else quantize_store<8>(x, m, dst, par);
+  if (b == 2) quantize_store_m<2>(raw, m, dst, par);
+  else if (b == 4) quantize_store_m<4>(raw, m, dst, par);
+  else quantize_store_m<8>(raw, m, dst, par);
 }
 
 // V: block (slab x of 32 tokens of one width zone, head g) with D threads = 32 tokens x
@@ -399,16 +425,10 @@ __device__ __forceinline__ void pack_v_slab(const uint16_t* __restrict__ v, int6
     for (int i = 0; i < 16; ++i) dst[i] = raw[i];
     return;
   }
-  float xv[32];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    xv[2 * i] = bf16_bits_to_f32(raw[i] & 0xFFFFu);
-    xv[2 * i + 1] = bf16_bits_to_f32(raw[i] >> 16);
-  }
   float* par = v_par + 2 * (hp[13 + z] + pos * GPR + grp);
-  if (z == 0) quantize_store<2>(xv, 32, dst, par);
-  else if (z == 1) quantize_store<4>(xv, 32, dst, par);
-  else quantize_store<8>(xv, 32, dst, par);
+  if (z == 0) quantize_store<2, true>(raw, 32, dst, par);
+  else if (z == 1) quantize_store<4, true>(raw, 32, dst, par);
+  else quantize_store<8, true>(raw, 32, dst, par);
 }
 
 template <int D>
