@@ -8,8 +8,8 @@
 //                channels sorted by width, per-head totals
 //   pack_header  one block: head offsets (scans over heads), the header, the status word
 //   pack_index   per chunk: ordered ranks -> v_idx, k_keep, k_vloc
-//   pack_units   z = 0: one block per (32 retained tokens, head) quantises every K channel;
-//                z = 1: one block per 32 tokens of one width zone quantises their V groups
+//   pack_k       one block per (32 retained tokens, head) quantises every K channel
+//   pack_v       one block per 32 tokens of one width zone quantises their V groups
 // Codes follow the definition z = min, s = float32(float64(max - min) / (2^b - 1)),
 // code = clamp(rint(float64(x - z) / s)).  The kernel evaluates v = (x - z) / s in fp32, whose
 // error is below 5e-5 for every v <= 255.5; only where v lies within 1e-4 of a rounding
@@ -433,17 +433,21 @@ __device__ __forceinline__ void pack_v_slab(const uint16_t* __restrict__ v, int6
 
 template <int D>
 __global__ void __launch_bounds__(D)
-pack_units(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t N,
-           const int64_t* __restrict__ header, const int32_t* __restrict__ kch,
-           const int32_t* __restrict__ k_keep, const int32_t* __restrict__ v_idx,
-           uint32_t* __restrict__ k_words, float* __restrict__ k_par, uint32_t* __restrict__ v_words,
-           float* __restrict__ v_par) {
+pack_k(const uint16_t* __restrict__ k, int64_t N, const int64_t* __restrict__ header,
+       const int32_t* __restrict__ kch, const int32_t* __restrict__ k_keep,
+       uint32_t* __restrict__ k_words, float* __restrict__ k_par) {
   const int g = blockIdx.y;
   const int64_t* hp = header + KVC_HDR_GLOBAL + g * KVC_HDR_PER_HEAD;
-  if (blockIdx.z == 0)
-    pack_k_group<D>(k, N, g, blockIdx.x, hp, kch, k_keep, k_words, k_par);
-  else
-    pack_v_slab<D>(v, N, g, blockIdx.x, hp, v_idx, v_words, v_par);
+  pack_k_group<D>(k, N, g, blockIdx.x, hp, kch, k_keep, k_words, k_par);
+}
+
+template <int D>
+__global__ void __launch_bounds__(D)
+pack_v(const uint16_t* __restrict__ v, int64_t N, const int64_t* __restrict__ header,
+       const int32_t* __restrict__ v_idx, uint32_t* __restrict__ v_words, float* __restrict__ v_par) {
+  const int g = blockIdx.y;
+  const int64_t* hp = header + KVC_HDR_GLOBAL + g * KVC_HDR_PER_HEAD;
+  pack_v_slab<D>(v, N, g, blockIdx.x, hp, v_idx, v_words, v_par);
 }
 
 PackWs carve(const Layer& L, char* ws, size_t* total) {
@@ -508,13 +512,15 @@ hipError_t launch_pack(const Layer& L, const uint16_t* k, const uint16_t* v,
   pack_header<<<1, 256, 0, s>>>(w.htot, L.hkv, L.d, L.n, out.header, w.status);
   pack_index<<<gc, 256, 0, s>>>(bits_v, L.n, nchunk, w.base, w.rbase, out.header, out.v_idx,
                                 out.k_keep, out.k_vloc);
-  dim3 gu((unsigned)((L.n + 31) / 32 + 4), (unsigned)L.hkv, 2);
-  if (L.d == 128)
-    pack_units<128><<<gu, 128, 0, s>>>(k, v, L.n, out.header, w.kch, out.k_keep, out.v_idx,
-                                       out.k_words, out.k_par, out.v_words, out.v_par);
-  else
-    pack_units<64><<<gu, 64, 0, s>>>(k, v, L.n, out.header, w.kch, out.k_keep, out.v_idx,
-                                     out.k_words, out.k_par, out.v_words, out.v_par);
+  dim3 gk((unsigned)((L.n + 31) / 32), (unsigned)L.hkv);
+  dim3 gv((unsigned)((L.n + 31) / 32 + 4), (unsigned)L.hkv);
+  if (L.d == 128) {
+    pack_k<128><<<gk, 128, 0, s>>>(k, L.n, out.header, w.kch, out.k_keep, out.k_words, out.k_par);
+    pack_v<128><<<gv, 128, 0, s>>>(v, L.n, out.header, out.v_idx, out.v_words, out.v_par);
+  } else {
+    pack_k<64><<<gk, 64, 0, s>>>(k, L.n, out.header, w.kch, out.k_keep, out.k_words, out.k_par);
+    pack_v<64><<<gv, 64, 0, s>>>(v, L.n, out.header, out.v_idx, out.v_words, out.v_par);
+  }
   return hipGetLastError();
 }
 
