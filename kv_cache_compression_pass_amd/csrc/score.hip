@@ -205,28 +205,9 @@ __device__ __forceinline__ bool geo_of(const Decomp& dc, int64_t N, int64_t Nq, 
 // ---------------------------------------------------------------------------------------
 
 // Scheduling fence between pipeline phases: the compiler interleaves matrix-core and VALU
-// work inside a phase but moves nothing across, which bounds the registers live at once.
+// work inside a phase but moves nothing across except LDS reads (fragment prefetch), which
+// bounds the registers live at once.
 #define KVC_PHASE_FENCE() __builtin_amdgcn_sched_barrier(0x100)   // LDS reads may cross (prefetch)
-
-// Issue order inside a phase.  Transcendentals (v_exp_f32) run beside the matrix cores, other
-// VALU work competes with them for issue, so each product is paired with a share of the
-// exponentials; the fragment reads go first.  Masks: 0x8 matrix core, 0x2 VALU (not
-// transcendental), 0x400 transcendental, 0x100 LDS read.
-#define KVC_SG(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
-#define KVC_LSE_PHASE_ORDER()                                                               \
-  {                                                                                         \
-    KVC_SG(0x100, 4);                                                                       \
-    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) { KVC_SG(0x8, 1); KVC_SG(0x2, 5); }     \
-    KVC_SG(0x100, 4);                                                                       \
-    _Pragma("unroll") for (int i_ = 0; i_ < 12; ++i_) { KVC_SG(0x8, 1); KVC_SG(0x400, 3); KVC_SG(0x2, 6); } \
-  }
-#define KVC_SCORE_PHASE_ORDER()                                                             \
-  {                                                                                         \
-    KVC_SG(0x100, 4);                                                                       \
-    _Pragma("unroll") for (int i_ = 0; i_ < 2; ++i_) { KVC_SG(0x8, 1); KVC_SG(0x2, 6); }     \
-    KVC_SG(0x100, 4);                                                                       \
-    _Pragma("unroll") for (int i_ = 0; i_ < 14; ++i_) { KVC_SG(0x8, 1); KVC_SG(0x400, 3); KVC_SG(0x2, 5); } \
-  }
 
 // True if every key of the half [t0h, t0h + 32) is visible to every row of the wave.
 __device__ __forceinline__ bool half_full(const Geo& G, int t0h, int N, int causal) {
@@ -325,11 +306,9 @@ __device__ __forceinline__ int full_tiles(const Geo& G, int N, int causal) {
     KVC_PHASE_FENCE();                                                                      \
     lse_mfma_half<D, S>(A, qf, 0, G.lo, G.hi);                                              \
     lse_update_half(B, m_run, l_run, c);                                                    \
-    KVC_LSE_PHASE_ORDER();                                                                  \
     KVC_PHASE_FENCE();                                                                      \
     lse_mfma_half<D, S>(B, qf, 1, G.lo, G.hi);                                              \
     lse_update_half(A, m_run, l_run, c);                                                    \
-    KVC_LSE_PHASE_ORDER();                                                                  \
     KVC_PHASE_FENCE();                                                                      \
   }
 
@@ -515,11 +494,9 @@ __device__ __forceinline__ float combine4(const float* cp) {
     KVC_PHASE_FENCE();                                                                      \
     score_mfma_half<D, S>(A, qf, 0, G.lo, G.hi);                                            \
     score_reduce_half<MAXMODE>(B, lv, c, G.hi, G.lo, &cb[((J) + 2) % 3][G.wave][32]);        \
-    KVC_SCORE_PHASE_ORDER();                                                                \
     KVC_PHASE_FENCE();                                                                      \
     score_mfma_half<D, S>(B, qf, 1, G.lo, G.hi);                                            \
     score_reduce_half<MAXMODE>(A, lv, c, G.hi, G.lo, &cb[(J) % 3][G.wave][0]);               \
-    KVC_SCORE_PHASE_ORDER();                                                                \
     KVC_PHASE_FENCE();                                                                      \
   }
 
