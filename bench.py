@@ -37,8 +37,8 @@ CPU_SAMPLE_SECONDS = 12.0      # oracle sample: KV heads are added until this mu
 # scaled by the same counters on a plain copy of known size (profiles/hbm_counters_*.md).
 # A figure holds only for the scorer source it was measured on; otherwise traffic is null.
 MEASURED_TRAFFIC = {
-    "llama8b_prefill_n8192": {"bytes": 93603763,
-                              "score_src_sha256": "1c8046e8c717a2c110075a450edbf158fb4dbbfa1cac4af7e729b3f53c6fa8c1"},
+    "llama8b_prefill_n8192": {"bytes": 90502758,
+                              "score_src_sha256": "98635c6b2702d71b9c3e98b9505f1d4f8f9ec4ce1b57d3e19f6227db6af9dc27"},
 }
 
 

@@ -280,6 +280,39 @@ __device__ __forceinline__ void lse_update_half(const f32x16 (&h)[2], float (&m_
   }
 }
 
+// Update for a half tile that every row sees in full.  The shift m is kept as it is while
+// every term 2^(x - m) of the half stays small: the half's sums are added as they stand
+// when both are at most 2^64 (so no term can overflow and l stays far below the float
+// range), and the exact update above runs for the whole wave otherwise.  That covers the
+// first tile (m = -inf makes every sum +inf, or NaN for the all -inf placeholder half,
+// which the exact update folds in as zero) and a row whose maximum jumps by more than 60
+// in the base-2 domain.  The log-sum-exp m + log2(l) is the same up to rounding for any m
+// at or below the running maximum, so only the row max tree and the rescale are saved.
+__device__ __forceinline__ void lse_update_half_lazy(const f32x16 (&h)[2], float (&m_run)[2],
+                                                     float (&l_run)[2], float c) {
+  float s[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const float nm = -m_run[nb];
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+      s0 += fast_exp2(fmaf(h[nb][i], c, nm));
+      s1 += fast_exp2(fmaf(h[nb][i + 1], c, nm));
+      s2 += fast_exp2(fmaf(h[nb][i + 2], c, nm));
+      s3 += fast_exp2(fmaf(h[nb][i + 3], c, nm));
+    }
+    s[nb] = (s0 + s1) + (s2 + s3);
+  }
+  const bool redo = !(s[0] <= 0x1p64f) || !(s[1] <= 0x1p64f);   // also true for NaN
+  if (__builtin_amdgcn_ballot_w64(redo) != 0) {
+    lse_update_half(h, m_run, l_run, c);
+  } else {
+    l_run[0] += s[0];
+    l_run[1] += s[1];
+  }
+}
+
 // Tiles [0, nfull) are visible in full to every row of the block; they run the pipelined
 // step.  The rest (the causal diagonal band and a partial last tile: at most 5 tiles of an
 // item) run a masked step without pipelining.
@@ -305,10 +338,10 @@ __device__ __forceinline__ int full_tiles(const Geo& G, int N, int causal) {
     issue_tile<D, ((S) + 3) & 3>(kh, G.k0 + 64 * ((J) + 3), n, voff, G.wave);               \
     KVC_PHASE_FENCE();                                                                      \
     lse_mfma_half<D, S>(A, qf, 0, G.lo, G.hi);                                              \
-    lse_update_half(B, m_run, l_run, c);                                                    \
+    lse_update_half_lazy(B, m_run, l_run, c);                                               \
     KVC_PHASE_FENCE();                                                                      \
     lse_mfma_half<D, S>(B, qf, 1, G.lo, G.hi);                                              \
-    lse_update_half(A, m_run, l_run, c);                                                    \
+    lse_update_half_lazy(A, m_run, l_run, c);                                               \
     KVC_PHASE_FENCE();                                                                      \
   }
 
@@ -365,7 +398,7 @@ lse_partial(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     if (j0 < nfull) KVC_LSE_STEP(0, j0)
     if (j0 + 1 < nfull) KVC_LSE_STEP(1, j0 + 1)
     if (j0 + 2 < nfull) KVC_LSE_STEP(2, j0 + 2)
-    lse_update_half(B, m_run, l_run, c);        // second half of the last pipelined tile
+    lse_update_half_lazy(B, m_run, l_run, c);   // second half of the last pipelined tile
   }
   for (int j = nfull; j < G.ntiles; ++j) {
     switch (j & 3) {

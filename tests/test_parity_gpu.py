@@ -100,6 +100,31 @@ def _pipeline(name, hq, hkv, d, N, Nq, causal, avg, seed, x=None, n_fid=64):
     return x
 
 
+@pytest.mark.parametrize("step,causal", [(24.0, False), (24.0, True), (10.0, False)])
+def test_row_lse_rising_maxima(step, causal):
+    """Row maxima that rise by about 73 (step 24) or 31 (step 10) in the base-2 domain every
+    160 keys, so the pipelined LSE must re-take its shift mid-row (a sum past 2^64) or carry
+    terms up to 2^62 until it does.  Logits reach about 3.5e3 before scaling, so the bound
+    adds the float32 accumulation error of a d-term dot product at that size."""
+    from workloads import f32_to_bf16_bits
+    d, N = 128, 1024
+    print(f"case rising maxima: step={step} causal={causal} d={d} N={N}", flush=True)
+    rng = np.random.default_rng(int(step) + 2 * causal)
+    u = np.zeros(d, np.float32)
+    u[:16] = 1.0
+    level = (np.arange(N) // 160).astype(np.float32) * step
+    kf = rng.standard_normal((1, N, d), dtype=np.float32) + level[None, :, None] * u
+    qf = rng.standard_normal((1, N, d), dtype=np.float32) + 1.5 * u
+    qb, kb = f32_to_bf16_bits(qf), f32_to_bf16_bits(kf)
+    desc = H.desc_of(1, 1, d, N, N, causal)
+    got = H.row_lse(desc, H.dev_bf16(qb), H.dev_bf16(kb)).cpu().numpy()
+    want = oracle.row_lse(qb, kb, causal=causal)
+    raw = float(np.max(np.abs(qf)) * np.max(np.abs(kf)) * 16 + 2 * d)
+    tol = 1e-4 + d * 2.0 ** -24 * raw / math.sqrt(d)
+    assert np.all(np.isfinite(got))
+    H.assert_abs(got, want, tol, "row_lse with rising maxima")
+
+
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_small_pipeline(case):
     name, hq, hkv, d, N, Nq, causal, avg = case
