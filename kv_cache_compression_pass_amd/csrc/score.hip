@@ -375,9 +375,11 @@ lse_partial(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   load_q_frags<D>(qf, q, G.h, Nq, G.i_wave, G.hi, G.lo);
   int voff[4];
   tile_offsets<D>(voff, G.wave, G.lane);
-  __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);    // vmcnt(0): Q fragments resident before the ring starts
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
+  // The first tiles are requested while the Q fragments are still in flight, so the two
+  // latencies overlap.  Loads complete in issue order: the first ring wait (at most 2L loads
+  // outstanding) also covers Q.
   issue_tile<D, 0>(kh, G.k0, n, voff, G.wave);
   issue_tile<D, 1>(kh, G.k0 + 64, n, voff, G.wave);
   issue_tile<D, 2>(kh, G.k0 + 128, n, voff, G.wave);
@@ -580,7 +582,8 @@ score_partial(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   load_q_frags<D>(qf, q, G.h, Nq, G.i_wave, G.hi, G.lo);
   int voff[4];
   tile_offsets<D>(voff, G.wave, G.lane);
-  __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);    // vmcnt(0): Q fragments and l' resident before the ring starts
+  // The first tiles are requested while Q is in flight (loads complete in issue order, so the
+  // first ring wait covers Q too).
   issue_tile<D, 0>(kh, G.k0, n, voff, G.wave);
   issue_tile<D, 1>(kh, G.k0 + 64, n, voff, G.wave);
   issue_tile<D, 2>(kh, G.k0 + 128, n, voff, G.wave);
