@@ -29,7 +29,8 @@ namespace kvc {
 
 namespace {
 
-constexpr int kUnitsPerBlock = 1024;   // multi-block path: 256 threads x 4 units
+constexpr int kMaxBlocks = 512;       // multi-block path: units per thread (1..16) chosen so that
+                                       // the blocks of all segments stay within this
 constexpr int kSmallUnits = 2048;      // single-block path: up to 8192 keys in LDS
 constexpr int kMaxSeg = 1024;
 constexpr int kDigitBits = 11;
@@ -444,7 +445,7 @@ __device__ __forceinline__ void keys_of(const float* weight, const float* sigma,
 
 // Histogram of one pass.  V/K: keys computed on pass 0 (and stored), 4 per unit, weight =
 // step rate.  Top-k: 32-bit score keys, 1 per token, weight 1, one segment per KV head.
-template <bool TOPK>
+template <bool TOPK, int UPT>
 __global__ void __launch_bounds__(256)
 alloc_hist(AllocWs a, const float* __restrict__ weight, const float* __restrict__ sigma,
            int64_t seg_len, int stage, int d, int pass, int nb) {
@@ -462,9 +463,9 @@ alloc_hist(AllocWs a, const float* __restrict__ weight, const float* __restrict_
   const Digit dg = digit_of(pass, nb);
   const uint64_t pre = s.prefix & dg.himask;
   const uint64_t dmask = (1ull << (dg.hi - dg.lo)) - 1;
-  const int64_t base = (int64_t)blockIdx.x * kUnitsPerBlock;
+  const int64_t base = (int64_t)blockIdx.x * (256 * UPT);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < UPT; ++j) {
     const int64_t ul = base + threadIdx.x + j * 256;
     if (ul >= seg_len) continue;
     if (TOPK) {
@@ -542,18 +543,18 @@ __device__ __forceinline__ int64_t unit_tie(const AllocWs& a, const float* weigh
   return steps_and_tie(kk, unit_size(stage, d, u, a.rcount), s.prefix, s.all_fit != 0, n);
 }
 
-// Block sums of the tie rates (units in index order, 4 per thread).
-template <bool TOPK>
+// Block sums of the tie rates (units in index order, UPT per thread).
+template <bool TOPK, int UPT>
 __global__ void __launch_bounds__(256)
 alloc_ties(AllocWs a, const float* __restrict__ weight, const float* __restrict__ sigma,
            int64_t seg_len, int stage, int d) {
   __shared__ int64_t wave_tot[4];
   const int seg = blockIdx.y;
   const SelState s = a.st[seg];
-  const int64_t base = (int64_t)blockIdx.x * kUnitsPerBlock + threadIdx.x * 4;
+  const int64_t base = (int64_t)blockIdx.x * (256 * UPT) + threadIdx.x * UPT;
   int64_t t = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < UPT; ++j) {
     int n;
     t += unit_tie<TOPK>(a, weight, sigma, base + j, seg, seg_len, stage, d, s, &n);
   }
@@ -582,7 +583,7 @@ alloc_tie_scan(AllocWs a, int nblk) {
 
 // Final widths: steps with key > lambda*, plus the tied step while the inclusive prefix of tie
 // rates fits the remaining budget; per-block used rate and distortion.
-template <bool TOPK>
+template <bool TOPK, int UPT>
 __global__ void __launch_bounds__(256)
 alloc_assign(AllocWs a, const float* __restrict__ weight, const float* __restrict__ sigma,
              int64_t seg_len, int stage, int d, int keep_bits, uint8_t* __restrict__ bits_out) {
@@ -590,13 +591,13 @@ alloc_assign(AllocWs a, const float* __restrict__ weight, const float* __restric
   __shared__ double dbuf[4];
   const int seg = blockIdx.y;
   const SelState s = a.st[seg];
-  const int64_t base = (int64_t)blockIdx.x * kUnitsPerBlock + threadIdx.x * 4;
+  const int64_t base = (int64_t)blockIdx.x * (256 * UPT) + threadIdx.x * UPT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int64_t tie[4];
-  int n[4];
+  int64_t tie[UPT];
+  int n[UPT];
   int64_t tsum = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < UPT; ++j) {
     tie[j] = unit_tie<TOPK>(a, weight, sigma, base + j, seg, seg_len, stage, d, s, &n[j]);
     tsum += tie[j];
   }
@@ -606,7 +607,7 @@ alloc_assign(AllocWs a, const float* __restrict__ weight, const float* __restric
   int64_t used = 0;
   double dist = 0.0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < UPT; ++j) {
     const int64_t u = base + j;
     if (u >= seg_len) continue;
     int nn = n[j];
@@ -682,7 +683,7 @@ alloc_finalize(const AllocWs a, int nparts, int topk, kvc_alloc_result* result) 
 }
 
 struct Plan {
-  int nseg, nblk, nb;
+  int nseg, nblk, nb, upt;
   int64_t U, seg_len;
   bool small;
 };
@@ -701,7 +702,10 @@ Plan plan_of(const Layer& L, int stage) {
     p.nb = 64;
   }
   p.small = (stage != KVC_ALLOC_TOPK) && p.U <= kSmallUnits;
-  p.nblk = (int)((p.seg_len + kUnitsPerBlock - 1) / kUnitsPerBlock);
+  p.upt = 1;
+  while (p.upt < 16 && (int64_t)p.nseg * ((p.seg_len + 256 * p.upt - 1) / (256 * p.upt)) > kMaxBlocks)
+    p.upt *= 2;
+  p.nblk = (int)((p.seg_len + 256 * p.upt - 1) / (256 * p.upt));
   return p;
 }
 
@@ -741,6 +745,31 @@ AllocWs carve(const Layer& L, int stage, char* ws, size_t* total) {
   return a;
 }
 
+// The selection passes, tie sums and assignment at UPT units per thread.
+template <int UPT>
+void launch_passes(const AllocWs& a, const Plan& p, const Layer& L, int stage, const float* weight,
+                   const float* sigma, int keep_bits, uint8_t* bits_out, hipStream_t s) {
+  const bool topk = (stage == KVC_ALLOC_TOPK);
+  const dim3 g2((unsigned)p.nblk, (unsigned)p.nseg);
+  const int npass = passes_of(p.nb);
+  for (int pass = 0; pass < npass; ++pass) {
+    if (topk)
+      alloc_hist<true, UPT><<<g2, 256, 0, s>>>(a, weight, nullptr, p.seg_len, stage, L.d, pass, p.nb);
+    else
+      alloc_hist<false, UPT><<<g2, 256, 0, s>>>(a, weight, sigma, p.seg_len, stage, L.d, pass, p.nb);
+    alloc_select<<<p.nseg, 256, 0, s>>>(a, pass, p.nb);
+  }
+  if (topk) {
+    alloc_ties<true, UPT><<<g2, 256, 0, s>>>(a, weight, nullptr, p.seg_len, stage, L.d);
+    alloc_tie_scan<<<p.nseg, 256, 0, s>>>(a, p.nblk);
+    alloc_assign<true, UPT><<<g2, 256, 0, s>>>(a, weight, nullptr, p.seg_len, stage, L.d, keep_bits, bits_out);
+  } else {
+    alloc_ties<false, UPT><<<g2, 256, 0, s>>>(a, weight, sigma, p.seg_len, stage, L.d);
+    alloc_tie_scan<<<p.nseg, 256, 0, s>>>(a, p.nblk);
+    alloc_assign<false, UPT><<<g2, 256, 0, s>>>(a, weight, sigma, p.seg_len, stage, L.d, keep_bits, bits_out);
+  }
+}
+
 }  // namespace
 
 size_t alloc_ws_bytes(const Layer& L, int stage) {
@@ -766,23 +795,12 @@ hipError_t launch_allocate(const Layer& L, int stage, const float* weight, const
   }
   const bool topk = (stage == KVC_ALLOC_TOPK);
   alloc_begin<<<1, 1024, 0, s>>>(a, stage, p.nseg, L.hkv, L.n, L.d, ncb, avg_bits, keep_fraction);
-  const dim3 g2((unsigned)p.nblk, (unsigned)p.nseg);
-  const int npass = passes_of(p.nb);
-  for (int pass = 0; pass < npass; ++pass) {
-    if (topk)
-      alloc_hist<true><<<g2, 256, 0, s>>>(a, weight, nullptr, p.seg_len, stage, L.d, pass, p.nb);
-    else
-      alloc_hist<false><<<g2, 256, 0, s>>>(a, weight, sigma, p.seg_len, stage, L.d, pass, p.nb);
-    alloc_select<<<p.nseg, 256, 0, s>>>(a, pass, p.nb);
-  }
-  if (topk) {
-    alloc_ties<true><<<g2, 256, 0, s>>>(a, weight, nullptr, p.seg_len, stage, L.d);
-    alloc_tie_scan<<<p.nseg, 256, 0, s>>>(a, p.nblk);
-    alloc_assign<true><<<g2, 256, 0, s>>>(a, weight, nullptr, p.seg_len, stage, L.d, keep_bits, bits_out);
-  } else {
-    alloc_ties<false><<<g2, 256, 0, s>>>(a, weight, sigma, p.seg_len, stage, L.d);
-    alloc_tie_scan<<<p.nseg, 256, 0, s>>>(a, p.nblk);
-    alloc_assign<false><<<g2, 256, 0, s>>>(a, weight, sigma, p.seg_len, stage, L.d, keep_bits, bits_out);
+  switch (p.upt) {
+    case 1: launch_passes<1>(a, p, L, stage, weight, sigma, keep_bits, bits_out, s); break;
+    case 2: launch_passes<2>(a, p, L, stage, weight, sigma, keep_bits, bits_out, s); break;
+    case 4: launch_passes<4>(a, p, L, stage, weight, sigma, keep_bits, bits_out, s); break;
+    case 8: launch_passes<8>(a, p, L, stage, weight, sigma, keep_bits, bits_out, s); break;
+    default: launch_passes<16>(a, p, L, stage, weight, sigma, keep_bits, bits_out, s); break;
   }
   alloc_finalize<<<1, 256, 0, s>>>(a, p.nblk * p.nseg, topk ? 1 : 0, result);
   return hipGetLastError();
