@@ -37,8 +37,8 @@ CPU_SAMPLE_SECONDS = 12.0      # oracle sample: KV heads are added until this mu
 # scaled by the same counters on a plain copy of known size (profiles/hbm_counters_*.md).
 # A figure holds only for the scorer source it was measured on; otherwise traffic is null.
 MEASURED_TRAFFIC = {
-    "llama8b_prefill_n8192": {"bytes": 90502758,
-                              "score_src_sha256": "98635c6b2702d71b9c3e98b9505f1d4f8f9ec4ce1b57d3e19f6227db6af9dc27"},
+    "llama8b_prefill_n8192": {"bytes": 91935642,
+                              "score_src_sha256": "318ad9cee6273be0500b29de459da82f0afba10b57b99f20798bd6c90be1718a"},
 }
 
 
@@ -113,6 +113,21 @@ def packed_bytes_read_by_attend(hdr):
     """Bytes of the packed cache one attend launch streams: value words and (scale, zero)
     pairs, key words and pairs, the retained-token list and its value locations."""
     return int(4 * hdr[5] + 8 * hdr[6] + 8 * hdr[7] + 4 * hdr[8] + 8 * hdr[9])
+
+
+def pack_algorithmic_bytes(hdr, k_width, d):
+    """Bytes kvc_quantize_pack must move: bf16 elements of retained V tokens and of retained
+    tokens in K channels of nonzero width (read), codes, (scale, zero) pairs and the index
+    lists (written).  Returns the K part (pack_k) and the V part (pack_v)."""
+    hkv = int(hdr[0])
+    k_read = 0
+    for g in range(hkv):
+        r_g = int(hdr[16 + 24 * g + 4])
+        k_read += 2 * r_g * int((k_width[g] > 0).sum())
+    v_read = 2 * d * int(hdr[4])
+    v_write = 4 * int(hdr[5]) + 8 * int(hdr[6]) + 4 * int(hdr[4])
+    k_write = 4 * int(hdr[8]) + 8 * int(hdr[9]) + 8 * int(hdr[7])
+    return {"k": k_read + k_write, "v": v_read + v_write}
 
 
 def main():
@@ -289,6 +304,12 @@ def main():
                          "hbm_frac": round(a_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                          "bytes": a_bytes, "flops": a_flops}
 
+    pb = pack_algorithmic_bytes(hdr, bk.cpu().numpy(), d)
+    pack_ms = float(np.mean(per_call["quantize_pack"]))
+    pack = {"ms": round(pack_ms, 5), "bytes_k": pb["k"], "bytes_v": pb["v"],
+            "gbs": round((pb["k"] + pb["v"]) / (pack_ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round((pb["k"] + pb["v"]) / (pack_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
     out = {
         "metric": METRIC,
         "value": round(N / (ms_per_step * 1e-3), 1),
@@ -310,6 +331,7 @@ def main():
         "per_call_ms": {n: round(float(np.mean(t)), 5) for n, t in per_call.items()},
         "score_pass2_call_tflops": round(flops / (np.mean(per_call["score_tokens"]) * 1e-3) / 1e12, 2),
         "attend": attend,
+        "pack": pack,
         "retained_tokens": int(hdr[7]),
     }
     if cfg.mode == "sum":

@@ -41,6 +41,7 @@ from .allocation import (
     allocate_k_channels,
     retained_counts,
     topk_keep,
+    threshold_keep,
 )
 from .quantize import quantize_group, pack_group_words, pack_cache, HDR_GLOBAL, HDR_PER_HEAD
 from .fidelity import dequantized_head, attend, full_attend, compressed_attend, fidelity_terms
@@ -50,7 +51,7 @@ __all__ = [
     "row_lse", "token_scores_sum", "token_scores_max", "hidden_row_norms", "value_out_norms",
     "channel_weights",
     "LEVELS", "step_ratios", "step_keys", "lagrangian_allocate", "stage_costs",
-    "allocate_v_tokens", "allocate_k_channels", "retained_counts", "topk_keep",
+    "allocate_v_tokens", "allocate_k_channels", "retained_counts", "topk_keep", "threshold_keep",
     "quantize_group", "pack_group_words", "pack_cache", "HDR_GLOBAL", "HDR_PER_HEAD",
     "dequantized_head", "attend", "full_attend", "compressed_attend", "fidelity_terms",
 ]

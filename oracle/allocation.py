@@ -1,4 +1,5 @@
-"""Rate-distortion bit allocation over the widths {0, 2, 4, 8, 16}, and top-k keep.
+"""Rate-distortion bit allocation over the widths {0, 2, 4, 8, 16}, top-k keep, and the
+threshold-and-window keep.
 
 Test infrastructure only (see the package docstring).
 
@@ -155,3 +156,26 @@ def topk_keep(scores, keep_fraction, keep_bits=16):
         order = sorted(range(n), key=lambda t: (-float(s[g, t]), t))
         bits[g, order[:kkeep]] = keep_bits
     return bits
+
+
+def threshold_keep(scores, threshold, window=128, keep_bits=16):
+    """Adaptive keep per KV head (KVzap summary, §2.3: thresholding and the sliding window).
+
+    Token t of head g keeps width keep_bits when its score is at or above the threshold, or
+    when it is one of the head's last `window` tokens (t >= N - window); every other token
+    gets width 0.  Scores and threshold are compared as float32.
+
+    Readings: the pages threshold predicted log-scores against tau, and log is increasing,
+    so the threshold here is on the score's own scale (a caller holding tau passes exp(tau)
+    rounded to float32); a score equal to the threshold is kept (only scores below it are
+    dropped); a NaN score is never at or above the threshold.
+    """
+    s = np.asarray(scores, dtype=np.float32)
+    if s.ndim != 2:
+        raise ValueError("scores must be [H_kv, N]")
+    thr = np.float32(threshold)
+    hkv, n = s.shape
+    in_window = np.arange(n) >= n - int(window)
+    with np.errstate(invalid="ignore"):
+        keep = (s >= thr) | in_window[None, :]
+    return np.where(keep, np.uint8(keep_bits), np.uint8(0)).astype(np.uint8)

@@ -147,3 +147,63 @@ def test_topk_keep_properties(seed):
         eq_drop = drop[s[g, drop] == thr]
         if eq_kept.size and eq_drop.size:
             assert eq_kept.max() < eq_drop.min()
+
+
+def test_threshold_keep_worked_examples(golden_dir):
+    path = os.path.join(golden_dir, "threshold_keep_example.txt")
+    with open(path) as f:
+        rows = [l for l in f if l.strip() and not l.startswith("#")]
+    assert len(rows) == 4
+    for r in rows:
+        head, sc, want = (part.split() for part in r.split("|"))
+        thr, win = float(head[0]), int(head[1])
+        s = np.array([[float(x) for x in sc]], dtype=np.float32)
+        got = oracle.threshold_keep(s, thr, win)
+        assert got.tolist() == [[int(x) for x in want]]
+
+
+def test_threshold_keep_extremes_and_nan():
+    rng = np.random.default_rng(5)
+    s = rng.standard_normal((3, 300)).astype(np.float32)
+    n = s.shape[1]
+    # threshold +inf: exactly the window; -inf: everything
+    only_win = oracle.threshold_keep(s, np.inf, 128)
+    assert (only_win[:, : n - 128] == 0).all() and (only_win[:, n - 128:] == 16).all()
+    assert (oracle.threshold_keep(s, -np.inf, 0) == 16).all()
+    # a NaN score is dropped outside the window and kept inside it
+    s2 = s.copy()
+    s2[0, 5] = np.nan
+    s2[0, n - 1] = np.nan
+    b = oracle.threshold_keep(s2, -np.inf, 1)
+    assert b[0, 5] == 0 and b[0, n - 1] == 16
+    # keep_bits is the width of every kept token
+    assert set(np.unique(oracle.threshold_keep(s, 0.0, 10, keep_bits=8))) <= {0, 8}
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_threshold_keep_matches_topk_at_the_kth_score(seed):
+    """With distinct scores, no window and the threshold at each head's k-th largest score,
+    the threshold rule keeps exactly the k highest scores: the sort-based top-k keep."""
+    rng = np.random.default_rng(100 + seed)
+    n = 211
+    s = rng.permutation(np.arange(3 * n, dtype=np.float32)).reshape(3, n) * np.float32(0.37)
+    k = math.floor(0.3 * n)
+    want = oracle.topk_keep(s, 0.3)
+    for g in range(3):
+        thr = np.sort(s[g])[::-1][k - 1]
+        got = oracle.threshold_keep(s[g : g + 1], thr, 0)
+        assert got[0].tolist() == want[g].tolist()
+
+
+def test_threshold_keep_monotone_in_threshold_and_window():
+    rng = np.random.default_rng(9)
+    s = rng.standard_normal((2, 500)).astype(np.float32)
+    prev = None
+    for thr in (-1.0, -0.2, 0.0, 0.7, 2.0):
+        b = oracle.threshold_keep(s, thr, 64)
+        if prev is not None:
+            assert ((b > 0) <= (prev > 0)).all()     # a higher threshold never keeps more
+        prev = b
+    small = oracle.threshold_keep(s, 1.0, 16)
+    large = oracle.threshold_keep(s, 1.0, 200)
+    assert ((small > 0) <= (large > 0)).all()
