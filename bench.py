@@ -37,7 +37,7 @@ CPU_SAMPLE_SECONDS = 12.0      # oracle sample: KV heads are added until this mu
 # scaled by the same counters on a plain copy of known size (profiles/hbm_counters_*.md).
 # A figure holds only for the scorer source it was measured on; otherwise traffic is null.
 MEASURED_TRAFFIC = {
-    "llama8b_prefill_n8192": {"bytes": 91935642,
+    "llama8b_prefill_n8192": {"bytes": 91933904,
                               "score_src_sha256": "318ad9cee6273be0500b29de459da82f0afba10b57b99f20798bd6c90be1718a"},
 }
 
@@ -304,6 +304,30 @@ def main():
                          "hbm_frac": round(a_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                          "bytes": a_bytes, "flops": a_flops}
 
+    # threshold-and-window keep over this step's token scores (reported apart): the threshold is
+    # the 75th percentile of the scores, the window the pages' 128 tokens
+    w_h = w.cpu().numpy()
+    thr = float(np.percentile(w_h[np.isfinite(w_h)], 75.0))
+    bits_t = torch.empty(hkv, N, dtype=torch.uint8, device=dev)
+    kept_t = torch.empty(hkv, dtype=torch.int64, device=dev)
+    kfn = lambda: kvc.kvc_keep_threshold(desc, w, thr, bits_t, window=128, keep_bits=16, kept=kept_t,
+                                         stream=stream)
+    for _ in range(3):
+        kfn()
+    torch.cuda.synchronize()
+    reps = max(args.steps, 10)
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record(stream)
+    for _ in range(reps):
+        kfn()
+    k1.record(stream)
+    torch.cuda.synchronize()
+    k_ms = k0.elapsed_time(k1) / reps
+    k_bytes = 5 * hkv * N + 8 * hkv
+    keep_thr = {"ms": round(k_ms, 5), "bytes": k_bytes, "gbs": round(k_bytes / (k_ms * 1e-3) / 1e9, 1),
+                "hbm_frac": round(k_bytes / (k_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "kept_fraction": round(float(kept_t.sum().item()) / (hkv * N), 4)}
+
     pb = pack_algorithmic_bytes(hdr, bk.cpu().numpy(), d)
     pack_ms = float(np.mean(per_call["quantize_pack"]))
     pack = {"ms": round(pack_ms, 5), "bytes_k": pb["k"], "bytes_v": pb["v"],
@@ -332,6 +356,7 @@ def main():
         "score_pass2_call_tflops": round(flops / (np.mean(per_call["score_tokens"]) * 1e-3) / 1e12, 2),
         "attend": attend,
         "pack": pack,
+        "keep_threshold": keep_thr,
         "retained_tokens": int(hdr[7]),
     }
     if cfg.mode == "sum":

@@ -161,6 +161,21 @@ kvc_status kvc_allocate_bits(const kvc_layer_desc* desc, kvc_alloc_stage stage,
                              uint8_t* bits_out, kvc_alloc_result* result_dev, void* ws,
                              size_t ws_bytes, void* hip_stream);
 
+/* KVzap §2.3 adaptive keep: per KV head, token t keeps width keep_bits when
+ * scores[g][t] >= threshold (a float32 compare; a NaN score never passes) or when it is one
+ * of the head's last `window` tokens (t >= N - window; the pages keep w = 128); every other
+ * token gets width 0.  The pages threshold predicted log-scores against tau and log is
+ * increasing, so a caller holding tau passes threshold = float32(exp(tau)).  The ratio kept
+ * follows the scores, unlike the fixed top-k stage of kvc_allocate_bits.
+ * scores: f32 [H_kv][N] (device).  bits_out: u8 [H_kv][N] (device; the widths the pack step
+ * takes as bits_v).  kept_dev: i64 [H_kv] (device), tokens kept per head, or NULL.  No
+ * workspace; asynchronous on hip_stream.  Uses desc's n_kv_heads and n_keys only.
+ * Errors: NULL scores or bits_out, misaligned scores or kept_dev, NaN threshold, window < 0,
+ * keep_bits not in {2,4,8,16}. */
+kvc_status kvc_keep_threshold(const kvc_layer_desc* desc, const float* scores, float threshold,
+                              int64_t window, uint8_t keep_bits, uint8_t* bits_out,
+                              int64_t* kept_dev, void* hip_stream);
+
 /* ---- Packed cache ------------------------------------------------------------------------
  * RDKV §2.3 stores retained rows grouped by width so each width has one dequantisation
  * path.  This library's layout (its own format; a token is retained iff bits_v > 0; zone z

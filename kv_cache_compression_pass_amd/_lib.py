@@ -29,7 +29,8 @@ DEV_BAD_CACHE = 2
 
 EXPORTED = (
     "kvc_workspace_size", "kvc_row_lse", "kvc_score_tokens", "kvc_channel_weights",
-    "kvc_allocate_bits", "kvc_packed_capacity", "kvc_quantize_pack", "kvc_compressed_attend",
+    "kvc_allocate_bits", "kvc_keep_threshold", "kvc_packed_capacity", "kvc_quantize_pack",
+    "kvc_compressed_attend",
     "kvc_get_device_status", "kvc_status_string", "kvc_last_error", "kvc_version",
 )
 
@@ -94,11 +95,12 @@ def load():
     lib.kvc_channel_weights.argtypes = [D, P, P, P, P, S, P]
     lib.kvc_allocate_bits.argtypes = [D, I32, P, P, P, ctypes.c_double, ctypes.c_double,
                                       ctypes.c_uint8, P, P, P, S, P]
+    lib.kvc_keep_threshold.argtypes = [D, P, ctypes.c_float, ctypes.c_int64, ctypes.c_uint8, P, P, P]
     lib.kvc_packed_capacity.argtypes = [D, I32, ctypes.POINTER(ctypes.c_size_t)]
     lib.kvc_quantize_pack.argtypes = [D, P, P, P, P, I32, ctypes.POINTER(PackedCacheC), P, S, P]
     lib.kvc_compressed_attend.argtypes = [D, P, ctypes.POINTER(PackedCacheC), P, P, P, S, P]
     lib.kvc_get_device_status.argtypes = [P, ctypes.POINTER(I32), P]
-    for name in ("kvc_row_lse", "kvc_score_tokens", "kvc_channel_weights", "kvc_allocate_bits",
+    for name in ("kvc_row_lse", "kvc_score_tokens", "kvc_channel_weights", "kvc_allocate_bits", "kvc_keep_threshold",
                  "kvc_packed_capacity", "kvc_quantize_pack", "kvc_compressed_attend",
                  "kvc_get_device_status"):
         getattr(lib, name).restype = I32

@@ -104,6 +104,12 @@ def kvc_allocate_bits(desc, stage, weight, bits_out, ws, sigma=None, bits_v=None
                                       _stream(stream)))
 
 
+def kvc_keep_threshold(desc, scores, threshold, bits_out, window=128, keep_bits=16, kept=None,
+                       stream=None):
+    _check(C.load().kvc_keep_threshold(ctypes.byref(desc), _ptr(scores), float(threshold), int(window),
+                                       int(keep_bits), _ptr(bits_out), _ptr(kept), _stream(stream)))
+
+
 def alloc_result_buffer(device="cuda"):
     return torch.zeros(32, dtype=torch.uint8, device=device)
 

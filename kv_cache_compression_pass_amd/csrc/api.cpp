@@ -254,6 +254,24 @@ kvc_status kvc_allocate_bits(const kvc_layer_desc* desc, kvc_alloc_stage stage,
                 "kvc_allocate_bits launch");
 }
 
+kvc_status kvc_keep_threshold(const kvc_layer_desc* desc, const float* scores, float threshold,
+                              int64_t window, uint8_t keep_bits, uint8_t* bits_out,
+                              int64_t* kept_dev, void* hip_stream) {
+  Layer L;
+  KVC_TRY(make_layer(desc, &L));
+  KVC_TRY(need_ptr(scores, 4, "scores"));
+  if (!bits_out) return fail(KVC_ERR_INVALID_ARG, "bits_out is NULL");
+  if (kept_dev && !aligned(kept_dev, 8)) return fail(KVC_ERR_INVALID_ARG, "kept is not 8-byte aligned");
+  if (std::isnan(threshold)) return fail(KVC_ERR_INVALID_ARG, "threshold is NaN");
+  if (window < 0) return fail(KVC_ERR_INVALID_ARG, "window must be >= 0");
+  if (keep_bits != 2 && keep_bits != 4 && keep_bits != 8 && keep_bits != 16)
+    return fail(KVC_ERR_INVALID_ARG, "keep_bits must be 2, 4, 8 or 16");
+  KVC_TRY(need_device());
+  return finish(launch_keep_threshold(L, scores, threshold, window, keep_bits, bits_out, kept_dev,
+                                      (hipStream_t)hip_stream),
+                "kvc_keep_threshold launch");
+}
+
 kvc_status kvc_packed_capacity(const kvc_layer_desc* desc, int32_t group_size,
                                size_t bytes_per_buffer[KVC_PK_NBUF]) {
   Layer L;

@@ -145,3 +145,17 @@ def test_valid_request_without_device_reports_no_device(lib):
     assert st == 3, lib.kvc_last_error()
     st = lib.kvc_row_lse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, need, None)
     assert st == 4, lib.kvc_last_error()
+
+
+def test_keep_threshold_argument_errors(lib):
+    d = _desc()
+    f = ctypes.c_float
+    assert lib.kvc_keep_threshold(ctypes.byref(d), None, f(0.5), 128, 16, FAKE, None, None) == 1
+    assert lib.kvc_keep_threshold(ctypes.byref(d), FAKE, f(0.5), 128, 16, None, None, None) == 1
+    assert lib.kvc_keep_threshold(ctypes.byref(d), FAKE, f(float("nan")), 128, 16, FAKE, None, None) == 1
+    assert lib.kvc_keep_threshold(ctypes.byref(d), FAKE, f(0.5), -1, 16, FAKE, None, None) == 1
+    assert lib.kvc_keep_threshold(ctypes.byref(d), FAKE, f(0.5), 128, 3, FAKE, None, None) == 1
+    assert lib.kvc_keep_threshold(ctypes.byref(d), FAKE, f(0.5), 128, 16, FAKE, FAKE + 4, None) == 1
+    # +-inf thresholds are valid; without a GPU the call stops at the device check
+    st = lib.kvc_keep_threshold(ctypes.byref(d), FAKE, f(float("inf")), 0, 16, FAKE, None, None)
+    assert st != 1

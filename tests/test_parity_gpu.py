@@ -282,3 +282,42 @@ def test_attend_group_aligned_uniform_widths(bvv, bkk):
     y_r, l_r = oracle.compressed_attend(qf, x["k"], x["v"], bv, bk)
     H.assert_abs(y_g.cpu().numpy(), y_r, 2e-2, "attend output")
     H.assert_abs(l_g.cpu().numpy(), l_r, 1e-3, "attend lse")
+
+
+KEEP_CASES = [
+    # name, H_kv, N, threshold (None: the head-0 median score), window, keep_bits
+    ("ragged_median_w128", 3, 1000, None, 128, 16),
+    ("ragged_inf_window_only", 3, 1000, float("inf"), 128, 16),
+    ("ragged_neg_inf_all", 2, 777, float("-inf"), 0, 8),
+    ("window_past_n", 2, 100, 5.0, 1000, 4),
+    ("no_window_bits2", 4, 4096 + 17, 0.25, 0, 2),
+    ("large_8x131072", 8, 131072, None, 128, 16),
+]
+
+
+@pytest.mark.parametrize("case", KEEP_CASES, ids=[c[0] for c in KEEP_CASES])
+def test_keep_threshold(case):
+    """Threshold-and-window keep against the oracle, bit-exact, with planted NaN scores and
+    scores equal to the threshold, rows both 16-byte aligned and not."""
+    name, hkv, n, thr, window, kb = case
+    print(f"case keep_threshold {name}: H_kv={hkv} N={n}", flush=True)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    s = rng.standard_normal((hkv, n)).astype(np.float32)
+    if thr is None:
+        thr = float(np.median(s[0]))
+    if np.isfinite(thr):
+        s.flat[rng.choice(s.size, 5, replace=False)] = np.float32(thr)    # ties at the threshold
+    s.flat[rng.choice(s.size, 3, replace=False)] = np.nan
+    desc = H.desc_of(hkv, hkv, 64, n, 1, True)
+    bits = torch.full((hkv, n), 255, dtype=torch.uint8, device=H.DEV)
+    kept = torch.full((hkv,), -1, dtype=torch.int64, device=H.DEV)
+    kvc.kvc_keep_threshold(desc, H.dev_f32(s), thr, bits, window=window, keep_bits=kb, kept=kept)
+    torch.cuda.synchronize()
+    want = oracle.threshold_keep(s, thr, window, keep_bits=kb)
+    np.testing.assert_array_equal(bits.cpu().numpy(), want)
+    np.testing.assert_array_equal(kept.cpu().numpy(), (want > 0).sum(axis=1))
+    # without the count buffer the widths are the same
+    bits2 = torch.zeros((hkv, n), dtype=torch.uint8, device=H.DEV)
+    kvc.kvc_keep_threshold(desc, H.dev_f32(s), thr, bits2, window=window, keep_bits=kb)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits2.cpu().numpy(), want)
