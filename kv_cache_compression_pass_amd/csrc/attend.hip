@@ -323,29 +323,438 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
 }
 
 // Combine the splits of each (head, row): M = max m_s, L = sum l_s 2^(m_s - M),
-// out = sum O_s 2^(m_s - M) / L, lse = (M + log2 L) ln 2.
-__global__ void __launch_bounds__(128)
+// out = sum O_s 2^(m_s - M) / L, lse = (M + log2 L) ln 2.  One block per (head, row): the
+// splits' (m, l) are read in parallel into LDS, M and L come from fixed-order trees, and
+// each output channel is summed by 256 / D threads over interleaved splits (independent
+// loads), whose partials are then added in thread order.  Deterministic for a given nsplit.
+constexpr int kMergeThreads = 256;
+constexpr int kMaxSplit = 256;
+
+__global__ void __launch_bounds__(kMergeThreads)
 attend_merge(const float* __restrict__ part, float* __restrict__ out, float* __restrict__ lse,
              int D, int nsplit) {
+  __shared__ float sc[kMaxSplit], red[kMergeThreads];
   const int64_t hr = blockIdx.x;             // h * Nq + row
   const int PSTRIDE = D + 2;
   const float* pr = part + hr * nsplit * PSTRIDE;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pr[s * PSTRIDE]);
-  float L = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float ms = pr[s * PSTRIDE];
-    if (ms > -INFINITY) L += pr[s * PSTRIDE + 1] * exp2f(ms - M);
+  const int t = threadIdx.x;
+  float mv = -INFINITY, lv = 0.f;
+  if (t < nsplit) {
+    mv = pr[(int64_t)t * PSTRIDE];
+    lv = pr[(int64_t)t * PSTRIDE + 1];
   }
-  for (int cc = threadIdx.x; cc < D; cc += blockDim.x) {
-    float acc = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float ms = pr[s * PSTRIDE];
-      if (ms > -INFINITY) acc += pr[s * PSTRIDE + 2 + cc] * exp2f(ms - M);
+  red[t] = mv;
+  __syncthreads();
+  for (int w = kMergeThreads / 2; w >= 1; w >>= 1) {
+    if (t < w) red[t] = fmaxf(red[t], red[t + w]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  __syncthreads();
+  float scale = 0.f;
+  if (t < nsplit && mv > -INFINITY) scale = exp2f(mv - M);
+  sc[t] = scale;                             // kMergeThreads == kMaxSplit
+  red[t] = lv * scale;
+  __syncthreads();
+  for (int w = kMergeThreads / 2; w >= 1; w >>= 1) {
+    if (t < w) red[t] += red[t + w];
+    __syncthreads();
+  }
+  const float L = red[0];
+  __syncthreads();
+  const int per = kMergeThreads / D;         // threads per channel (2 or 4)
+  const int cc = t % D, q = t / D;
+  float acc = 0.f;
+#pragma unroll 4
+  for (int s2 = q; s2 < nsplit; s2 += per) acc += pr[(int64_t)s2 * PSTRIDE + 2 + cc] * sc[s2];
+  red[t] = acc;
+  __syncthreads();
+  if (q == 0) {
+    float o = 0.f;
+    for (int k = 0; k < per; ++k) o += red[k * D + cc];
+    out[hr * D + cc] = (L > 0.f) ? o / L : 0.f;
+  }
+  if (t == 0) lse[hr] = (L > 0.f) ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------------------
+// Decode-shaped calls (G * Nq <= 16 query rows per KV head, e.g. one new token per query
+// head).  A 32-row matrix-core tile would be almost all padding, so the rows' dot products
+// run on the VALU in float32, and the packed cache is streamed by many small independent
+// waves, each with one round of loads:
+//   attend_dec_logits: one wave per K group of 32 retained tokens.  The group's code words
+//     and (scale, zero) pairs are staged in LDS by coalesced loads; lane = (token, half of
+//     the channel list); the halves are added with a lane swap.  Writes x = s * q.K_hat (base
+//     2, -inf where the causal mask hides the token) to a scratch row indexed by token.
+//   attend_dec_values: one wave per 64 consecutive V rows of one width zone (contiguous, one
+//     width).  Lane = row: gathers the rows' logits, online softmax per query row (wave max,
+//     per-lane sums); then lane = channels: O[r][c] += p * V_hat, 16 rows' words in flight at
+//     a time.  The block's four waves merge in LDS into one split partial (attend_merge).
+// ---------------------------------------------------------------------------------------
+constexpr int kDecWaves = 4;
+constexpr int kDecThreads = 64 * kDecWaves;
+constexpr int kDecMaxRows = 16;
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// Copy n consecutive elements (n < 2^31) from global memory to LDS with the 64 lanes of a wave:
+// batches of 16 independent loads per lane, then their stores, so a batch costs one latency.
+template <typename T>
+__device__ __forceinline__ void wave_stage(T* __restrict__ dst, const T* __restrict__ src, int n, int lane) {
+  constexpr int B = 16;
+  for (int w0 = 0; w0 < n; w0 += 64 * B) {
+    T t[B];
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      const int w = w0 + k * 64 + lane;
+      if (w < n) t[k] = src[w];
     }
-    out[hr * D + cc] = (L > 0.f) ? acc / L : 0.f;
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      const int w = w0 + k * 64 + lane;
+      if (w < n) dst[w] = t[k];
+    }
   }
-  if (threadIdx.x == 0) lse[hr] = (L > 0.f) ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
+// Nonzero-width K channels of head g grouped by width (2, 4, 8, then 16 bits), each group in
+// channel order: {channel, word offset, param slot, width}, by one block scan.  cnt[k] is the
+// first position of width class k (cnt[4] = all nonzero channels).  Widths outside
+// {2,4,8,16} count as 0.
+template <int D, int NT>
+__device__ void dec_channel_table(const kvc_packed_cache& cache, int g, int32_t (*kch)[4], uint64_t* scan,
+                                  int* cnt) {
+  const int t = threadIdx.x;
+  uint32_t b = 0;
+  int cls = 4;
+  uint64_t f = 0;
+  if (t < D) {
+    b = cache.k_width[(int64_t)g * D + t];
+    cls = b == 2 ? 0 : b == 4 ? 1 : b == 8 ? 2 : b == 16 ? 3 : 4;
+    // word offset [0,16), param slot [16,24), one 8-bit count per width class from bit 24
+    if (cls < 4) f = (uint64_t)b | ((uint64_t)(cls < 3) << 16) | (1ull << (24 + 8 * cls));
+  }
+  uint64_t tf;
+  const uint64_t ef = block_excl_scan<NT>(f, &tf, scan);
+  if (t < D && cls < 4) {
+    int pos = (int)((ef >> (24 + 8 * cls)) & 0xFF);
+    for (int k = 0; k < cls; ++k) pos += (int)((tf >> (24 + 8 * k)) & 0xFF);
+    kch[pos][0] = t;
+    kch[pos][1] = (int32_t)(ef & 0xFFFF);
+    kch[pos][2] = (int32_t)((ef >> 16) & 0xFF);
+    kch[pos][3] = (int32_t)b;
+  }
+  if (t == 0) {
+    int acc = 0;
+    for (int k = 0; k < 4; ++k) {
+      cnt[k] = acc;
+      acc += (int)((tf >> (24 + 8 * k)) & 0xFF);
+    }
+    cnt[4] = acc;
+  }
+  __syncthreads();
+}
+
+// s[r] += code * a[pos][r] over the positions [p0, p1) of one width class B in {2,4,8}, for
+// this lane's token lo and channel half hi (positions p0 + hi, p0 + hi + 2, ...).
+template <int B, int R>
+__device__ __forceinline__ void dec_dot_class(float (&s)[R], const int32_t (*kch)[4], const uint32_t* kw,
+                                              const float (*a)[R], int p0, int p1, int lo, int hi) {
+  const int wo = (lo * B) >> 5, sh = (lo * B) & 31;
+#pragma unroll 4
+  for (int pos = p0 + hi; pos < p1; pos += 2) {
+    const float cf = (float)((kw[kch[pos][1] + wo] >> sh) & ((1u << B) - 1u));
+#pragma unroll
+    for (int r = 0; r < R; ++r) s[r] = fmaf(cf, a[pos][r], s[r]);
+  }
+}
+
+// Per row r < G * Nq of KV head g: query head g*G + r/Nq, query row r%Nq.  Row-indexed tables
+// once per block (no divisions in the loops): the row's index in [H_q][Nq] and its last
+// visible token.
+__device__ __forceinline__ void dec_row_tables(int g, int G, int64_t N, int64_t Nq, int causal, int nr,
+                                               int64_t* rowi, int64_t* lim) {
+  const int r = threadIdx.x;
+  if (r < kDecMaxRows) {
+    const int nqi = (int)Nq;
+    rowi[r] = r < nr ? (int64_t)(g * G + r / nqi) * Nq + r % nqi : 0;
+    lim[r] = r < nr ? (causal ? N - Nq + r % nqi : N - 1) : -1;
+  }
+}
+
+template <int D, int R>
+struct DecLogitSmem {
+  float qt[D][R];                        // query rows, channel-major
+  float a[kDecWaves][D][R];              // a group's scale * q, by quantised channel position
+  int32_t kch[D][4];
+  uint32_t kw[kDecWaves][16 * D];        // a group's code words (at most 16 per channel)
+  float2 kp[kDecWaves][D];               // a group's (scale, zero) pairs
+  int64_t rowi[kDecMaxRows], lim[kDecMaxRows];
+  uint64_t scan[kDecWaves];
+  int cnt[5];
+};
+
+template <int D, int R>
+__global__ void __launch_bounds__(kDecThreads)
+attend_dec_logits(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __restrict__ xl,
+                  int G, int Hkv, int64_t N, int64_t Nq, int causal, float c, int32_t* status) {
+  __shared__ DecLogitSmem<D, R> sm;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hi = lane >> 5, lo = lane & 31;
+  const int g = blockIdx.y;
+  const int nr = G * (int)Nq;
+  const int64_t* H = cache.header;
+  if (H[0] != Hkv || H[1] != D || H[2] != N) {
+    if (threadIdx.x == 0 && blockIdx.x == 0 && g == 0) set_status(status, KVC_DEV_BAD_CACHE);
+    return;
+  }
+  const int64_t* hp = H + KVC_HDR_GLOBAL + g * KVC_HDR_PER_HEAD;
+  const int64_t Rg = hp[4], ngroups = hp[22], Wk = hp[20], Qk = hp[21];
+  if ((int64_t)blockIdx.x * kDecWaves >= ngroups) return;   // uniform for the block
+  dec_row_tables(g, G, N, Nq, causal, nr, sm.rowi, sm.lim);
+  dec_channel_table<D, kDecThreads>(cache, g, sm.kch, sm.scan, sm.cnt);
+  const int nq = sm.cnt[3], nnz = sm.cnt[4];
+  for (int idx = threadIdx.x; idx < R * D; idx += kDecThreads) {
+    const int r = idx / D, cc = idx % D;
+    sm.qt[cc][r] = r < nr ? bf16_bits_to_f32(q[sm.rowi[r] * D + cc]) : 0.f;
+  }
+  __syncthreads();
+  // groups blockIdx.x * 4 + wave, then every gridDim.x * 4 further (no block barrier follows)
+  for (int64_t j = (int64_t)blockIdx.x * kDecWaves + wave; j < ngroups; j += (int64_t)gridDim.x * kDecWaves) {
+    const uint32_t* gw = cache.k_words + hp[18] + j * Wk;
+    wave_stage(sm.kw[wave], gw, (int)Wk, lane);
+    wave_stage(sm.kp[wave], reinterpret_cast<const float2*>(cache.k_par) + hp[19] + j * Qk, (int)Qk, lane);
+    const int64_t tix = j * 32 + lo;
+    const bool tok_ok = tix < Rg;
+    const int64_t tok = tok_ok ? (int64_t)cache.k_keep[hp[17] + tix] : 0;
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    // quantised channels: K_hat = scale * code + zero, so q . K_hat = sum code * (scale q) + sum zero q
+    float bias[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) bias[r] = 0.f;
+    for (int pos = lane; pos < nq; pos += 64) {
+      const int4 ch = *reinterpret_cast<const int4*>(sm.kch[pos]);
+      const float2 sz = sm.kp[wave][ch.z];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float qv = sm.qt[ch.x][r];
+        sm.a[wave][pos][r] = sz.x * qv;
+        bias[r] = fmaf(sz.y, qv, bias[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) bias[r] = wave_sum(bias[r]);
+    __builtin_amdgcn_wave_barrier();
+
+    float s[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) s[r] = 0.f;
+    dec_dot_class<2, R>(s, sm.kch, sm.kw[wave], sm.a[wave], sm.cnt[0], sm.cnt[1], lo, hi);
+    dec_dot_class<4, R>(s, sm.kch, sm.kw[wave], sm.a[wave], sm.cnt[1], sm.cnt[2], lo, hi);
+    dec_dot_class<8, R>(s, sm.kch, sm.kw[wave], sm.a[wave], sm.cnt[2], sm.cnt[3], lo, hi);
+    {                                                        // 16-bit channels: raw bf16
+      const int wo = lo >> 1;
+      const uint32_t s16 = (lo & 1) ? 0u : 16u;
+#pragma unroll 4
+      for (int pos = nq + hi; pos < nnz; pos += 2) {
+        const float kv = __uint_as_float((sm.kw[wave][sm.kch[pos][1] + wo] << s16) & 0xFFFF0000u);
+        const float* qr = sm.qt[sm.kch[pos][0]];
+#pragma unroll
+        for (int r = 0; r < R; ++r) s[r] = fmaf(kv, qr[r], s[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) s[r] += swap_half(s[r]) + bias[r];
+    if (hi == 0 && tok_ok) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (r < nr) xl[sm.rowi[r] * N + tok] = tok <= sm.lim[r] ? s[r] * c : -INFINITY;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+constexpr int kVRows = 64;              // V rows per chunk of the value pass (one per lane)
+
+template <int D, int R>
+struct DecValueSmem {
+  int64_t rowi[kDecMaxRows], lim[kDecMaxRows];
+  float pv[kDecWaves][kVRows][R];        // per V row of the chunk: the query rows' weights
+  float wml[kDecWaves][2][R];
+  float wo[kDecWaves][R][D];
+};
+
+template <int D, int R>
+__global__ void __launch_bounds__(kDecThreads)
+attend_dec_values(kvc_packed_cache cache, const float* __restrict__ xl, float* __restrict__ part,
+                  int G, int Hkv, int64_t N, int64_t Nq, int nsplit) {
+  constexpr int CPL = D / 64;            // channels per lane
+  constexpr int GPR = D / 32;
+  constexpr int PSTRIDE = D + 2;
+  constexpr int NB = 16;                 // V rows whose words are in flight together
+  __shared__ DecValueSmem<D, R> sm;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int split = blockIdx.x, g = blockIdx.y;
+  const int nr = G * (int)Nq;
+  const int64_t* H = cache.header;
+  if (H[0] != Hkv || H[1] != D || H[2] != N) return;         // reported by attend_dec_logits
+  const int64_t* hp = H + KVC_HDR_GLOBAL + g * KVC_HDR_PER_HEAD;
+  dec_row_tables(g, G, N, Nq, 0, nr, sm.rowi, sm.lim);
+  __syncthreads();
+  int64_t nch[4], ctot = 0;
+#pragma unroll
+  for (int z = 0; z < 4; ++z) {
+    nch[z] = (hp[z] + kVRows - 1) / kVRows;
+    ctot += nch[z];
+  }
+  const int64_t cps = (ctot + nsplit - 1) / nsplit;
+  const int64_t cb = (int64_t)split * cps;
+  const int64_t ce = cb + cps < ctot ? cb + cps : ctot;
+
+  float m[R], l[R], o[R][CPL];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    m[r] = -INFINITY;
+    l[r] = 0.f;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) o[r][k] = 0.f;
+  }
+  const int c0 = lane * CPL, grp = c0 / 32, e2 = c0 % 32;
+  for (int64_t ck = cb + wave; ck < ce; ck += kDecWaves) {
+    int z = 0;
+    int64_t cz = ck;
+    while (z < 3 && cz >= nch[z]) {
+      cz -= nch[z];
+      ++z;
+    }
+    const int b = 2 << z;
+    const int64_t r0 = cz * kVRows;
+    const int nrows = (int)(hp[z] - r0 < kVRows ? hp[z] - r0 : kVRows);
+    // lane = row: the query rows' logits of this V row's token, then the online softmax
+    const bool rok = lane < nrows;
+    const int64_t tok = rok ? (int64_t)cache.v_idx[hp[5 + z] + r0 + lane] : 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float x = -INFINITY;
+      if (rok && r < nr) x = xl[sm.rowi[r] * N + tok];
+      const float mn = fmaxf(m[r], wave_max(x));
+      float p = 0.f;
+      if (mn > -INFINITY) {                                  // uniform
+        const float alpha = fast_exp2(m[r] - mn);
+        p = fast_exp2(x - mn);
+        l[r] = fmaf(l[r], alpha, p);
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) o[r][k] *= alpha;
+        m[r] = mn;
+      }
+      if (lane < kVRows) sm.pv[wave][lane][r] = p;
+    }
+    __builtin_amdgcn_wave_barrier();
+    // lane = channels: O += p * V_hat over the chunk's rows (width b for all of them), the
+    // words (and pairs) of 16 rows in flight at a time; rows past nrows repeat the last and
+    // contribute 0
+    const int vstride = GPR * b;                             // words per V row
+    const uint32_t* vw = cache.v_words + hp[9 + z] + r0 * vstride + grp * b + ((e2 * b) >> 5);
+    const float2* vp = reinterpret_cast<const float2*>(cache.v_par) + hp[13 + z] + r0 * GPR + grp;
+    const uint32_t mask = b == 16 ? 0xFFFFu : (1u << b) - 1u;
+    const int shift = (e2 * b) & 31;
+#pragma unroll 1
+    for (int t0 = 0; t0 < nrows; t0 += NB) {
+      uint32_t w[NB];
+      float2 sz[NB];
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const int tp = t0 + k < nrows ? t0 + k : nrows - 1;
+        w[k] = vw[tp * vstride];
+        sz[k] = make_float2(0.f, 0.f);
+      }
+      if (b < 16) {                                          // uniform: zones 2/4/8 have pairs
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+          const int tp = t0 + k < nrows ? t0 + k : nrows - 1;
+          sz[k] = vp[tp * GPR];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const int tp = t0 + k;
+        const float* pr = sm.pv[wave][tp < kVRows ? tp : kVRows - 1];
+        float v[CPL];
+#pragma unroll
+        for (int kk = 0; kk < CPL; ++kk) {
+          const uint32_t code = (w[k] >> (shift + kk * b)) & mask;
+          const float vv = b == 16 ? bf16_bits_to_f32(code) : fmaf(sz[k].x, (float)code, sz[k].y);
+          v[kk] = tp < nrows ? vv : 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int kk = 0; kk < CPL; ++kk) o[r][kk] = fmaf(pr[r], v[kk], o[r][kk]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // merge the four waves' (m, l, O) and write this split's partial for every row
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float lt = wave_sum(l[r]);
+    if (lane == 0) {
+      sm.wml[wave][0][r] = m[r];
+      sm.wml[wave][1][r] = lt;
+    }
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) sm.wo[wave][r][lane * CPL + k] = o[r][k];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < nr * D; idx += kDecThreads) {
+    const int r = idx / D, cc = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, sm.wml[w][0][r]);
+    float Lr = 0.f, Or = 0.f;
+    if (M > -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) {
+        const float mw = sm.wml[w][0][r];
+        const float sc = mw > -INFINITY ? fast_exp2(mw - M) : 0.f;
+        Lr = fmaf(sm.wml[w][1][r], sc, Lr);
+        Or = fmaf(sm.wo[w][r][cc], sc, Or);
+      }
+    }
+    float* pr = part + (sm.rowi[r] * nsplit + split) * PSTRIDE;
+    if (cc == 0) {
+      pr[0] = M;
+      pr[1] = Lr;
+    }
+    pr[2 + cc] = Or;
+  }
+}
+
+// The decode path addresses a head's V words with 32-bit offsets: N * d / 2 (the words of a
+// head whose every token is kept at 16 bits) must stay below 2^32.
+bool use_decode(const Layer& L) {
+  return (int64_t)L.G * L.nq <= kDecMaxRows && L.n * (int64_t)L.d / 2 < (int64_t(1) << 32);
+}
+
+int nsplit_decode(const Layer& L) {
+  const int64_t cmax = (L.n + kVRows - 1) / kVRows + 4;  // V chunks per head, at most
+  int64_t want = (1024 + L.hkv - 1) / L.hkv;
+  const int64_t cap = (cmax + 3) / 4;                    // at least 4 chunks (one per wave) per split
+  if (want > cap) want = cap;
+  if (want > kMaxSplit) want = kMaxSplit;
+  if (want < 1) want = 1;
+  return (int)want;
 }
 
 int nsplit_of(const Layer& L) {
@@ -355,7 +764,7 @@ int nsplit_of(const Layer& L) {
   const int64_t maxs = (L.n + 32 * 8 - 1) / (32 * 8);   // at least 8 groups per split
   if (want > maxs) want = maxs;
   if (want < 1) want = 1;
-  if (want > 256) want = 256;
+  if (want > kMaxSplit) want = kMaxSplit;
   return (int)want;
 }
 
@@ -363,16 +772,52 @@ int nsplit_of(const Layer& L) {
 
 size_t attend_ws_bytes(const Layer& L) {
   WsPlan p;
-  p.take((size_t)L.hq * L.nq * nsplit_of(L) * (L.d + 2) * sizeof(float));
+  const bool dec = use_decode(L);
+  const int nsplit = dec ? nsplit_decode(L) : nsplit_of(L);
+  p.take((size_t)L.hq * L.nq * nsplit * (L.d + 2) * sizeof(float));
+  if (dec) p.take((size_t)L.hq * L.nq * L.n * sizeof(float));     // logits by token
   return p.off;
 }
 
 hipError_t launch_attend(const Layer& L, const uint16_t* q, const kvc_packed_cache& cache,
                          float* out, float* lse, char* ws, hipStream_t s) {
-  const int nsplit = nsplit_of(L);
+  const bool dec = use_decode(L);
+  const int nsplit = dec ? nsplit_decode(L) : nsplit_of(L);
   WsPlan p;
   float* part = reinterpret_cast<float*>(ws + p.take((size_t)L.hq * L.nq * nsplit * (L.d + 2) * sizeof(float)));
   (void)launch_reset_status(ws, s);
+  if (dec) {
+    int32_t* status = reinterpret_cast<int32_t*>(ws);
+    float* xl = reinterpret_cast<float*>(ws + p.take((size_t)L.hq * L.nq * L.n * sizeof(float)));
+    int64_t nb1 = ((L.n + 31) / 32 + kDecWaves - 1) / kDecWaves;   // blocks of 4 groups per head, at most
+    const int64_t cap1 = (1024 + L.hkv - 1) / L.hkv;                 // the blocks loop over the rest
+    if (nb1 > cap1) nb1 = cap1;
+    const dim3 g1((unsigned)nb1, (unsigned)L.hkv);
+    const dim3 g3((unsigned)nsplit, (unsigned)L.hkv);
+    const int rows = L.G * (int)L.nq;
+#define KVC_DEC(DD, RR)                                                                                   \
+  do {                                                                                                    \
+    attend_dec_logits<DD, RR><<<g1, kDecThreads, 0, s>>>(q, cache, xl, L.G, L.hkv, L.n, L.nq, L.causal,  \
+                                                         L.c_log2, status);                              \
+    attend_dec_values<DD, RR><<<g3, kDecThreads, 0, s>>>(cache, xl, part, L.G, L.hkv, L.n, L.nq, nsplit); \
+  } while (0)
+    if (L.d == 128) {
+      if (rows <= 1) KVC_DEC(128, 1);
+      else if (rows <= 2) KVC_DEC(128, 2);
+      else if (rows <= 4) KVC_DEC(128, 4);
+      else if (rows <= 8) KVC_DEC(128, 8);
+      else KVC_DEC(128, 16);
+    } else {
+      if (rows <= 1) KVC_DEC(64, 1);
+      else if (rows <= 2) KVC_DEC(64, 2);
+      else if (rows <= 4) KVC_DEC(64, 4);
+      else if (rows <= 8) KVC_DEC(64, 8);
+      else KVC_DEC(64, 16);
+    }
+#undef KVC_DEC
+    attend_merge<<<(unsigned)((int64_t)L.hq * L.nq), kMergeThreads, 0, s>>>(part, out, lse, L.d, nsplit);
+    return hipGetLastError();
+  }
   const int nRT = (int)((L.nq + kRows - 1) / kRows);
   dim3 grid((unsigned)((L.G * nRT + kWaves - 1) / kWaves), (unsigned)nsplit, (unsigned)L.hkv);
   int32_t* status = reinterpret_cast<int32_t*>(ws);
@@ -380,7 +825,7 @@ hipError_t launch_attend(const Layer& L, const uint16_t* q, const kvc_packed_cac
     attend_split<128><<<grid, kThreadsA, 0, s>>>(q, cache, part, L.G, L.hkv, L.n, L.nq, L.causal, L.c_log2, nsplit, status);
   else
     attend_split<64><<<grid, kThreadsA, 0, s>>>(q, cache, part, L.G, L.hkv, L.n, L.nq, L.causal, L.c_log2, nsplit, status);
-  attend_merge<<<(unsigned)((int64_t)L.hq * L.nq), 128, 0, s>>>(part, out, lse, L.d, nsplit);
+  attend_merge<<<(unsigned)((int64_t)L.hq * L.nq), kMergeThreads, 0, s>>>(part, out, lse, L.d, nsplit);
   return hipGetLastError();
 }
 

@@ -321,3 +321,72 @@ def test_keep_threshold(case):
     kvc.kvc_keep_threshold(desc, H.dev_f32(s), thr, bits2, window=window, keep_bits=kb)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(bits2.cpu().numpy(), want)
+
+
+DECODE_CASES = [
+    # name, H_q, H_kv, d, N, rows per query head, causal
+    ("dec_g4_d128_n3000_r1", 8, 2, 128, 3000, 1, True),
+    ("dec_g7_d128_n1000_r2", 7, 1, 128, 1000, 2, True),
+    ("dec_g8_d64_n777_r2", 8, 1, 64, 777, 2, True),
+    ("dec_g1_d64_n64_r1", 1, 1, 64, 64, 1, False),
+    ("dec_g2_d128_n513_noncausal", 4, 2, 128, 513, 1, False),
+    ("dec_g3_d128_n2049_r1", 6, 2, 128, 2049, 1, True),
+]
+
+
+def _random_widths(rng, hkv, n, d):
+    bv = rng.choice(np.array([0, 2, 4, 8, 16], np.uint8), size=(hkv, n), p=[0.3, 0.2, 0.2, 0.2, 0.1])
+    bk = rng.choice(np.array([0, 2, 4, 8, 16], np.uint8), size=(hkv, d), p=[0.1, 0.3, 0.3, 0.2, 0.1])
+    return bv.astype(np.uint8), bk.astype(np.uint8)
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_attend_decode_rows(case):
+    """Decode-shaped attend (G * rows <= 16 query rows per KV head: the VALU path) against the
+    oracle, on random widths with evictions, then on the all-16 cache against full attention."""
+    name, hq, hkv, d, N, rows, causal = case
+    print(f"case {name}: H_q={hq} H_kv={hkv} d={d} N={N} rows={rows} causal={causal}", flush=True)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    x = make_inputs(hq, hkv, d, N, N, seed=zlib.crc32(name.encode()) % 1000, k_outliers=True)
+    bv, bk = _random_widths(rng, hkv, N, d)
+    desc = H.desc_of(hq, hkv, d, N, N, causal)
+    k, v = H.dev_bf16(x["k"]), H.dev_bf16(x["v"])
+    cache, st = H.pack(desc, k, v, H.dev_u8(bv), H.dev_u8(bk))
+    assert st == 0
+    qf_bits = np.ascontiguousarray(x["q"][:, N - rows:, :])
+    desc_f = H.desc_of(hq, hkv, d, N, rows, causal)
+    out_g, lh_g, st = H.attend(desc_f, H.dev_bf16(qf_bits), cache)
+    assert st == 0
+    out_r, lh_r = oracle.compressed_attend(qf_bits, x["k"], x["v"], bv, bk, causal=causal)
+    H.assert_abs(out_g.cpu().numpy(), out_r, 2e-2, "decode attend output")
+    H.assert_abs(lh_g.cpu().numpy(), lh_r, 1e-3, "decode attend lse")
+    cache16, st = H.pack(desc, k, v, H.dev_u8(np.full((hkv, N), 16, np.uint8)),
+                         H.dev_u8(np.full((hkv, d), 16, np.uint8)))
+    y_g, l_g, st2 = H.attend(desc_f, H.dev_bf16(qf_bits), cache16)
+    assert st == 0 and st2 == 0
+    y_r, l_r = oracle.full_attend(qf_bits, x["k"], x["v"], causal=causal)
+    H.assert_abs(y_g.cpu().numpy(), y_r, 2e-2, "decode attend output, all-16 cache")
+    H.assert_abs(l_g.cpu().numpy(), l_r, 1e-3, "decode attend lse, all-16 cache")
+
+
+def test_attend_decode_row_that_sees_nothing():
+    """Two rows per query head, only the last token retained: the first row (one position
+    earlier) sees no retained token (output 0, LSE -inf); the second sees exactly one."""
+    hq, hkv, d, N, rows = 4, 1, 128, 300, 2
+    print("case decode row that sees nothing", flush=True)
+    x = make_inputs(hq, hkv, d, N, N, seed=77)
+    bv = np.zeros((hkv, N), np.uint8)
+    bv[:, N - 1] = 8
+    bk = np.full((hkv, d), 4, np.uint8)
+    desc = H.desc_of(hq, hkv, d, N, N, True)
+    cache, st = H.pack(desc, H.dev_bf16(x["k"]), H.dev_bf16(x["v"]), H.dev_u8(bv), H.dev_u8(bk))
+    assert st == 0
+    qf_bits = np.ascontiguousarray(x["q"][:, N - rows:, :])
+    out_g, lh_g, st = H.attend(H.desc_of(hq, hkv, d, N, rows, True), H.dev_bf16(qf_bits), cache)
+    assert st == 0
+    out_r, lh_r = oracle.compressed_attend(qf_bits, x["k"], x["v"], bv, bk, causal=True)
+    og, lg = out_g.cpu().numpy(), lh_g.cpu().numpy()
+    assert np.all(og[:, 0, :] == 0.0) and np.all(np.isneginf(lg[:, 0]))
+    assert np.all(np.isneginf(lh_r[:, 0]))
+    H.assert_abs(og, out_r, 2e-2, "decode attend output")
+    H.assert_abs(lg[:, 1], lh_r[:, 1], 1e-3, "decode attend lse")
