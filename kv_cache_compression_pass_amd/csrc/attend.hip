@@ -465,14 +465,16 @@ __device__ void dec_channel_table(const kvc_packed_cache& cache, int g, int32_t 
 }
 
 // s[r] += code * a[pos][r] over the positions [p0, p1) of one width class B in {2,4,8}, for
-// this lane's token lo and channel half hi (positions p0 + hi, p0 + hi + 2, ...).
+// this lane's token lo and channel half hi (positions p0 + hi, p0 + hi + 2, ...).  The
+// group's words are staged in width-class order, so position pos's words start at
+// wbase + B * (pos - p0): no table lookup between the loads.
 template <int B, int R>
-__device__ __forceinline__ void dec_dot_class(float (&s)[R], const int32_t (*kch)[4], const uint32_t* kw,
-                                              const float (*a)[R], int p0, int p1, int lo, int hi) {
+__device__ __forceinline__ void dec_dot_class(float (&s)[R], const uint32_t* kw, const float (*a)[R], int p0,
+                                              int p1, int wbase, int lo, int hi) {
   const int wo = (lo * B) >> 5, sh = (lo * B) & 31;
 #pragma unroll 4
   for (int pos = p0 + hi; pos < p1; pos += 2) {
-    const float cf = (float)((kw[kch[pos][1] + wo] >> sh) & ((1u << B) - 1u));
+    const float cf = (float)((kw[wbase + B * (pos - p0) + wo] >> sh) & ((1u << B) - 1u));
 #pragma unroll
     for (int r = 0; r < R; ++r) s[r] = fmaf(cf, a[pos][r], s[r]);
   }
@@ -494,13 +496,15 @@ __device__ __forceinline__ void dec_row_tables(int g, int G, int64_t N, int64_t 
 template <int D, int R>
 struct DecLogitSmem {
   float qt[D][R];                        // query rows, channel-major
-  float a[kDecWaves][D][R];              // a group's scale * q, by quantised channel position
+  float a[kDecWaves][D][R];              // a group's scale * q (quantised positions), q (16-bit ones)
+  uint16_t wmap[16 * D];                 // a group's word w goes to LDS word wmap[w] (width-class order)
   int32_t kch[D][4];
   uint32_t kw[kDecWaves][16 * D];        // a group's code words (at most 16 per channel)
   float2 kp[kDecWaves][D];               // a group's (scale, zero) pairs
   int64_t rowi[kDecMaxRows], lim[kDecMaxRows];
   uint64_t scan[kDecWaves];
   int cnt[5];
+  int wb[5];                             // first staged word of each width class
 };
 
 template <int D, int R>
@@ -523,6 +527,20 @@ attend_dec_logits(const uint16_t* __restrict__ q, kvc_packed_cache cache, float*
   dec_row_tables(g, G, N, Nq, causal, nr, sm.rowi, sm.lim);
   dec_channel_table<D, kDecThreads>(cache, g, sm.kch, sm.scan, sm.cnt);
   const int nq = sm.cnt[3], nnz = sm.cnt[4];
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int k = 0; k < 4; ++k) {
+      sm.wb[k] = acc;
+      acc += (sm.cnt[k + 1] - sm.cnt[k]) * (2 << k);
+    }
+    sm.wb[4] = acc;
+  }
+  __syncthreads();
+  for (int pos = threadIdx.x; pos < nnz; pos += kDecThreads) {   // the word map (the same for every group)
+    const int b = sm.kch[pos][3], cls = b == 2 ? 0 : b == 4 ? 1 : b == 8 ? 2 : 3;
+    const int dst = sm.wb[cls] + b * (pos - sm.cnt[cls]);
+    for (int i = 0; i < b; ++i) sm.wmap[sm.kch[pos][1] + i] = (uint16_t)(dst + i);
+  }
   for (int idx = threadIdx.x; idx < R * D; idx += kDecThreads) {
     const int r = idx / D, cc = idx % D;
     sm.qt[cc][r] = r < nr ? bf16_bits_to_f32(q[sm.rowi[r] * D + cc]) : 0.f;
@@ -531,7 +549,22 @@ attend_dec_logits(const uint16_t* __restrict__ q, kvc_packed_cache cache, float*
   // groups blockIdx.x * 4 + wave, then every gridDim.x * 4 further (no block barrier follows)
   for (int64_t j = (int64_t)blockIdx.x * kDecWaves + wave; j < ngroups; j += (int64_t)gridDim.x * kDecWaves) {
     const uint32_t* gw = cache.k_words + hp[18] + j * Wk;
-    wave_stage(sm.kw[wave], gw, (int)Wk, lane);
+    {
+      constexpr int SB = 16;
+      for (int w0 = 0; w0 < (int)Wk; w0 += 64 * SB) {
+        uint32_t t[SB];
+#pragma unroll
+        for (int k = 0; k < SB; ++k) {
+          const int w = w0 + k * 64 + lane;
+          if (w < (int)Wk) t[k] = gw[w];
+        }
+#pragma unroll
+        for (int k = 0; k < SB; ++k) {
+          const int w = w0 + k * 64 + lane;
+          if (w < (int)Wk) sm.kw[wave][sm.wmap[w]] = t[k];
+        }
+      }
+    }
     wave_stage(sm.kp[wave], reinterpret_cast<const float2*>(cache.k_par) + hp[19] + j * Qk, (int)Qk, lane);
     const int64_t tix = j * 32 + lo;
     const bool tok_ok = tix < Rg;
@@ -542,9 +575,9 @@ attend_dec_logits(const uint16_t* __restrict__ q, kvc_packed_cache cache, float*
     float bias[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) bias[r] = 0.f;
-    for (int pos = lane; pos < nq; pos += 64) {
+    for (int pos = lane; pos < nnz; pos += 64) {
       const int4 ch = *reinterpret_cast<const int4*>(sm.kch[pos]);
-      const float2 sz = sm.kp[wave][ch.z];
+      const float2 sz = pos < nq ? sm.kp[wave][ch.z] : make_float2(1.f, 0.f);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const float qv = sm.qt[ch.x][r];
@@ -559,18 +592,17 @@ attend_dec_logits(const uint16_t* __restrict__ q, kvc_packed_cache cache, float*
     float s[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) s[r] = 0.f;
-    dec_dot_class<2, R>(s, sm.kch, sm.kw[wave], sm.a[wave], sm.cnt[0], sm.cnt[1], lo, hi);
-    dec_dot_class<4, R>(s, sm.kch, sm.kw[wave], sm.a[wave], sm.cnt[1], sm.cnt[2], lo, hi);
-    dec_dot_class<8, R>(s, sm.kch, sm.kw[wave], sm.a[wave], sm.cnt[2], sm.cnt[3], lo, hi);
+    dec_dot_class<2, R>(s, sm.kw[wave], sm.a[wave], sm.cnt[0], sm.cnt[1], sm.wb[0], lo, hi);
+    dec_dot_class<4, R>(s, sm.kw[wave], sm.a[wave], sm.cnt[1], sm.cnt[2], sm.wb[1], lo, hi);
+    dec_dot_class<8, R>(s, sm.kw[wave], sm.a[wave], sm.cnt[2], sm.cnt[3], sm.wb[2], lo, hi);
     {                                                        // 16-bit channels: raw bf16
-      const int wo = lo >> 1;
+      const int wo = sm.wb[3] + (lo >> 1);
       const uint32_t s16 = (lo & 1) ? 0u : 16u;
 #pragma unroll 4
       for (int pos = nq + hi; pos < nnz; pos += 2) {
-        const float kv = __uint_as_float((sm.kw[wave][sm.kch[pos][1] + wo] << s16) & 0xFFFF0000u);
-        const float* qr = sm.qt[sm.kch[pos][0]];
+        const float kv = __uint_as_float((sm.kw[wave][wo + 16 * (pos - nq)] << s16) & 0xFFFF0000u);
 #pragma unroll
-        for (int r = 0; r < R; ++r) s[r] = fmaf(kv, qr[r], s[r]);
+        for (int r = 0; r < R; ++r) s[r] = fmaf(kv, sm.a[wave][pos][r], s[r]);
       }
     }
 #pragma unroll
