@@ -44,7 +44,8 @@ from .allocation import (
     threshold_keep,
 )
 from .quantize import quantize_group, pack_group_words, pack_cache, HDR_GLOBAL, HDR_PER_HEAD
-from .fidelity import dequantized_head, attend, full_attend, compressed_attend, fidelity_terms
+from .fidelity import (dequantized_head, attend, full_attend, compressed_attend, compressed_attend_append,
+                       fidelity_terms)
 
 __all__ = [
     "as_f64", "query_positions", "default_scale",
@@ -53,5 +54,5 @@ __all__ = [
     "LEVELS", "step_ratios", "step_keys", "lagrangian_allocate", "stage_costs",
     "allocate_v_tokens", "allocate_k_channels", "retained_counts", "topk_keep", "threshold_keep",
     "quantize_group", "pack_group_words", "pack_cache", "HDR_GLOBAL", "HDR_PER_HEAD",
-    "dequantized_head", "attend", "full_attend", "compressed_attend", "fidelity_terms",
+    "dequantized_head", "attend", "full_attend", "compressed_attend", "compressed_attend_append", "fidelity_terms",
 ]

@@ -110,6 +110,30 @@ def compressed_attend(q, k, v, bits_v, bits_k, scale=None, causal=True, group_si
     return attend(q, heads, n, scale, causal)
 
 
+def compressed_attend_append(q, k, v, bits_v, bits_k, k_new, v_new, scale=None, causal=True, group_size=32):
+    """Attention over the compressed cache followed by an uncompressed append buffer.
+
+    RDKV summary, §2.3: decode reads the packed width zones of the compressed cache, and the
+    tokens generated since compression sit beside them in full precision; attention spans
+    both.  Here that is written out plainly: the retained, dequantised tokens of the cache
+    (positions < N) and the new tokens k_new, v_new [H_kv][n_new][d] at positions N .. N+n_new-1
+    form one token list per KV head, and the query rows are the last Nq positions of the
+    N + n_new.  Reading: the buffer holds the raw bf16 values (no quantisation), and the rows'
+    positions count the new tokens.
+    """
+    K = np.asarray(k)
+    hkv, n, d = K.shape
+    kn, vn = as_f64(k_new), as_f64(v_new)
+    n_new = kn.shape[1]
+    heads = []
+    for g in range(hkv):
+        toks, kh, vh = dequantized_head(K[g], np.asarray(v)[g], np.asarray(bits_v)[g],
+                                        np.asarray(bits_k)[g], group_size)
+        heads.append((np.concatenate([toks, n + np.arange(n_new)]),
+                      np.concatenate([kh, kn[g]]), np.concatenate([vh, vn[g]])))
+    return attend(q, heads, n + n_new, scale, causal)
+
+
 def fidelity_terms(y_hat, y, lse_hat, lse):
     """(||Y_hat - Y||_F^2, ||l_hat - l||_F^2), the two terms of KVSculpt's loss (§2)."""
     dy = np.asarray(y_hat, dtype=np.float64) - np.asarray(y, dtype=np.float64)

@@ -98,3 +98,53 @@ def test_key_channel_width_zero_drops_the_channel():
     y2, l2 = oracle.full_attend(Q, x["k"], x["v"])
     np.testing.assert_allclose(yh, y2, rtol=1e-13, atol=1e-13)
     np.testing.assert_allclose(lh, l2, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_append_buffer_all_sixteen_is_full_attention(causal):
+    """An all-16, no-eviction cache followed by the append buffer is full attention over the
+    concatenated raw keys and values (rows are the last Nq of the N + n_new positions)."""
+    hq, hkv, d, N, n_new, Nq = 4, 2, 64, 40, 7, 5
+    x = make_inputs(hq, hkv, d, N + n_new, N + n_new, seed=31)
+    k, v = x["k"][:, :N], x["v"][:, :N]
+    kn, vn = x["k"][:, N:], x["v"][:, N:]
+    q = x["q"][:, -Nq:]
+    bv = np.full((hkv, N), 16, np.uint8)
+    bk = np.full((hkv, d), 16, np.uint8)
+    y, l = oracle.compressed_attend_append(q, k, v, bv, bk, kn, vn, causal=causal)
+    yr, lr = oracle.full_attend(q, x["k"], x["v"], causal=causal)
+    np.testing.assert_allclose(y, yr, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l, lr, rtol=0, atol=1e-12)
+
+
+def test_append_buffer_is_the_lse_merge_of_the_two_zones():
+    """For a decode row (it sees every cached and every new token) the result is the
+    log-sum-exp merge of attention over the compressed cache alone and over the buffer
+    alone: l = logaddexp(l1, l2), Y = e^(l1 - l) Y1 + e^(l2 - l) Y2."""
+    hq, hkv, d, N, n_new = 6, 2, 32, 70, 9
+    x = make_inputs(hq, hkv, d, N + n_new, N + n_new, seed=32)
+    rng = np.random.default_rng(3)
+    bv = rng.choice(np.array([0, 2, 4, 8, 16], np.uint8), size=(hkv, N)).astype(np.uint8)
+    bk = rng.choice(np.array([0, 2, 4, 8, 16], np.uint8), size=(hkv, d)).astype(np.uint8)
+    k, v, kn, vn = x["k"][:, :N], x["v"][:, :N], x["k"][:, N:], x["v"][:, N:]
+    q = x["q"][:, -1:]
+    y, l = oracle.compressed_attend_append(q, k, v, bv, bk, kn, vn, causal=True)
+    y1, l1 = oracle.compressed_attend(q, k, v, bv, bk, causal=False)
+    y2, l2 = oracle.full_attend(q, kn, vn, causal=False)
+    lm = np.logaddexp(l1, l2)
+    ym = np.exp(l1 - lm)[..., None] * y1 + np.exp(l2 - lm)[..., None] * y2
+    np.testing.assert_allclose(l, lm, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(y, ym, rtol=0, atol=1e-12)
+
+
+def test_append_buffer_empty_is_the_cache_alone():
+    hq, hkv, d, N, Nq = 4, 1, 32, 50, 3
+    x = make_inputs(hq, hkv, d, N, N, seed=33)
+    bv = np.full((hkv, N), 4, np.uint8)
+    bv[:, ::3] = 0
+    bk = np.full((hkv, d), 8, np.uint8)
+    q = x["q"][:, -Nq:]
+    empty = np.zeros((hkv, 0, d), np.uint16)
+    y, l = oracle.compressed_attend_append(q, x["k"], x["v"], bv, bk, empty, empty, causal=True)
+    yc, lc = oracle.compressed_attend(q, x["k"], x["v"], bv, bk, causal=True)
+    assert np.array_equal(y, yc) and np.array_equal(l, lc)
