@@ -304,6 +304,34 @@ def main():
                          "hbm_frac": round(a_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                          "bytes": a_bytes, "flops": a_flops}
 
+    # one decode row per query head over the packed cache plus an append buffer of 128 new
+    # tokens (raw bf16; the last 128 keys and values stand in for them)
+    n_new = min(128, N)
+    kn = k[:, N - n_new:, :].contiguous()
+    vn = v[:, N - n_new:, :].contiguous()
+    desc_a = kvc.make_desc(hq, hkv, d, N, 1, True)
+    q_a = q[:, Nq - 1:, :].contiguous()
+    out_a = torch.empty(hq, 1, d, dtype=torch.float32, device=dev)
+    lse_a = torch.empty(hq, 1, dtype=torch.float32, device=dev)
+    ws_aa = kvc.workspace(kvc.OP_COMPRESSED_ATTEND, desc_a, 0, dev)
+    afn = lambda: kvc.kvc_compressed_attend_append(desc_a, q_a, cache, kn, vn, out_a, lse_a, ws_aa, stream=stream)
+    for _ in range(3):
+        afn()
+    torch.cuda.synchronize()
+    reps = max(args.steps, 10)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        afn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ap_ms = e0.elapsed_time(e1) / reps
+    ap_bytes = packed_bytes_read_by_attend(hdr) + 2 * kn.numel() * 2 + 2 * q_a.numel() + 4 * (out_a.numel() + lse_a.numel())
+    attend["decode_row_append128"] = {"rows": 1, "n_new": n_new, "ms": round(ap_ms, 5),
+                                      "gbs": round(ap_bytes / (ap_ms * 1e-3) / 1e9, 1),
+                                      "hbm_frac": round(ap_bytes / (ap_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                      "bytes": ap_bytes}
+
     # threshold-and-window keep over this step's token scores (reported apart): the threshold is
     # the 75th percentile of the scores, the window the pages' 128 tokens
     w_h = w.cpu().numpy()

@@ -11,6 +11,7 @@
  *   kvc_allocate_bits      Lagrangian width allocation over {0,2,4,8,16}, or top-k keep
  *   kvc_quantize_pack      group quantisation and packing into the width zones
  *   kvc_compressed_attend  attention output and LSE over a packed cache
+ *   kvc_compressed_attend_append  the same, over the packed cache and a bf16 buffer of new tokens
  *
  * Sources (summary pages of the papers; section numbers are the pages' own):
  *   "RDKV - rate-distortion bit allocation for joint eviction and quantization of the KV
@@ -241,6 +242,20 @@ kvc_status kvc_quantize_pack(const kvc_layer_desc* desc, const void* k, const vo
 kvc_status kvc_compressed_attend(const kvc_layer_desc* desc, const void* q,
                                  const kvc_packed_cache* cache, float* out, float* lse,
                                  void* ws, size_t ws_bytes, void* hip_stream);
+
+/* kvc_compressed_attend over the packed cache followed by an append buffer: the n_new tokens
+ * generated since compression, kept as raw bf16 beside the packed zones (RDKV §2.3), at
+ * positions N .. N+n_new-1.  The query rows are the last Nq of the N + n_new positions (row i
+ * at N + n_new - Nq + i; with the causal flag it sees the new tokens up to its own position).
+ * The buffer's keys and values are attended exactly; its log-sum-exp part is merged with the
+ * packed cache's.  k_new, v_new: bf16 [H_kv][n_new][d] (device, 16-byte aligned; NULL allowed
+ * when n_new == 0, which gives kvc_compressed_attend).  ws: as kvc_compressed_attend
+ * (KVC_OP_COMPRESSED_ATTEND sizes both).  Errors: n_new < 0, a NULL or misaligned buffer when
+ * n_new > 0, and every error of kvc_compressed_attend. */
+kvc_status kvc_compressed_attend_append(const kvc_layer_desc* desc, const void* q,
+                                        const kvc_packed_cache* cache, const void* k_new,
+                                        const void* v_new, int64_t n_new, float* out, float* lse,
+                                        void* ws, size_t ws_bytes, void* hip_stream);
 
 /* Device status codes (bit set). */
 #define KVC_DEV_BAD_WIDTH 1

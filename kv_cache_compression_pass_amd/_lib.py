@@ -30,7 +30,7 @@ DEV_BAD_CACHE = 2
 EXPORTED = (
     "kvc_workspace_size", "kvc_row_lse", "kvc_score_tokens", "kvc_channel_weights",
     "kvc_allocate_bits", "kvc_keep_threshold", "kvc_packed_capacity", "kvc_quantize_pack",
-    "kvc_compressed_attend",
+    "kvc_compressed_attend", "kvc_compressed_attend_append",
     "kvc_get_device_status", "kvc_status_string", "kvc_last_error", "kvc_version",
 )
 
@@ -99,9 +99,12 @@ def load():
     lib.kvc_packed_capacity.argtypes = [D, I32, ctypes.POINTER(ctypes.c_size_t)]
     lib.kvc_quantize_pack.argtypes = [D, P, P, P, P, I32, ctypes.POINTER(PackedCacheC), P, S, P]
     lib.kvc_compressed_attend.argtypes = [D, P, ctypes.POINTER(PackedCacheC), P, P, P, S, P]
+    lib.kvc_compressed_attend_append.argtypes = [D, P, ctypes.POINTER(PackedCacheC), P, P, ctypes.c_int64,
+                                                 P, P, P, S, P]
     lib.kvc_get_device_status.argtypes = [P, ctypes.POINTER(I32), P]
     for name in ("kvc_row_lse", "kvc_score_tokens", "kvc_channel_weights", "kvc_allocate_bits", "kvc_keep_threshold",
                  "kvc_packed_capacity", "kvc_quantize_pack", "kvc_compressed_attend",
+                 "kvc_compressed_attend_append",
                  "kvc_get_device_status"):
         getattr(lib, name).restype = I32
     lib.kvc_status_string.argtypes = [I32]

@@ -175,6 +175,16 @@ def kvc_compressed_attend(desc, q, cache, out, lse, ws, stream=None):
                                           _ptr(out), _ptr(lse), wp, wn, _stream(stream)))
 
 
+def kvc_compressed_attend_append(desc, q, cache, k_new, v_new, out, lse, ws, stream=None):
+    """k_new, v_new: bf16 tensors [H_kv][n_new][d] of the tokens generated after compression."""
+    cs = cache.c_struct()
+    wp, wn = _ws(ws)
+    n_new = 0 if k_new is None else int(k_new.shape[-2])
+    _check(C.load().kvc_compressed_attend_append(ctypes.byref(desc), _ptr(q), ctypes.byref(cs), _ptr(k_new),
+                                                 _ptr(v_new), n_new, _ptr(out), _ptr(lse), wp, wn,
+                                                 _stream(stream)))
+
+
 def kvc_get_device_status(ws, stream=None):
     code = ctypes.c_int32(0)
     _check(C.load().kvc_get_device_status(_ptr(ws), ctypes.byref(code), _stream(stream)))

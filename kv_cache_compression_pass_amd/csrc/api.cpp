@@ -329,6 +329,28 @@ kvc_status kvc_compressed_attend(const kvc_layer_desc* desc, const void* q,
                 "kvc_compressed_attend launch");
 }
 
+kvc_status kvc_compressed_attend_append(const kvc_layer_desc* desc, const void* q,
+                                        const kvc_packed_cache* cache, const void* k_new,
+                                        const void* v_new, int64_t n_new, float* out, float* lse,
+                                        void* ws, size_t ws_bytes, void* hip_stream) {
+  Layer L;
+  KVC_TRY(make_layer(desc, &L));
+  KVC_TRY(need_bf16(q, "q"));
+  KVC_TRY(check_cache(cache));
+  KVC_TRY(need_ptr(out, 4, "out"));
+  KVC_TRY(need_ptr(lse, 4, "lse"));
+  if (n_new < 0) return fail(KVC_ERR_INVALID_ARG, "n_new must be >= 0");
+  if (n_new > 0) {
+    KVC_TRY(need_bf16(k_new, "k_new"));
+    KVC_TRY(need_bf16(v_new, "v_new"));
+  }
+  KVC_TRY(need_ws(ws, ws_bytes, attend_ws_bytes(L)));
+  KVC_TRY(need_device());
+  return finish(launch_attend(L, (const uint16_t*)q, *cache, out, lse, (char*)ws, (hipStream_t)hip_stream,
+                              (const uint16_t*)k_new, (const uint16_t*)v_new, n_new),
+                "kvc_compressed_attend_append launch");
+}
+
 kvc_status kvc_get_device_status(const void* ws, int32_t* code, void* hip_stream) {
   if (!ws || !code) return fail(KVC_ERR_INVALID_ARG, "ws / code is NULL");
   KVC_TRY(need_device());

@@ -58,7 +58,7 @@ template <int D>
 __global__ void __launch_bounds__(kThreadsA)
 attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __restrict__ part,
              int G, int Hkv, int64_t N, int64_t Nq, int causal, float c, int nsplit,
-             int32_t* status) {
+             int64_t shift, int pstride, int32_t* status) {
   constexpr int KS = D / 16;
   constexpr int GPR = D / 32;
   constexpr int PSTRIDE = D + 2;
@@ -80,7 +80,7 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
   const int rt = active ? pair / G : 0;
   const int h = g * G + hl;
   const int64_t r0 = (int64_t)rt * kRows;
-  const int64_t off = N - Nq;
+  const int64_t off = N - Nq + shift;         // row r sits at position off + r
 
   const int64_t* H = cache.header;
   if (H[0] != Hkv || H[1] != D || H[2] != N) {
@@ -311,7 +311,7 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
   const float lt = l_run + swap_half(l_run);
   const int64_t row = r0 + lo;
   if (row >= Nq) return;
-  float* pr = part + (((int64_t)h * Nq + row) * nsplit + split) * PSTRIDE;
+  float* pr = part + (((int64_t)h * Nq + row) * pstride + split) * PSTRIDE;
   if (hi == 0) {
     pr[0] = m_run;
     pr[1] = lt;
@@ -483,13 +483,13 @@ __device__ __forceinline__ void dec_dot_class(float (&s)[R], const uint32_t* kw,
 // Per row r < G * Nq of KV head g: query head g*G + r/Nq, query row r%Nq.  Row-indexed tables
 // once per block (no divisions in the loops): the row's index in [H_q][Nq] and its last
 // visible token.
-__device__ __forceinline__ void dec_row_tables(int g, int G, int64_t N, int64_t Nq, int causal, int nr,
-                                               int64_t* rowi, int64_t* lim) {
+__device__ __forceinline__ void dec_row_tables(int g, int G, int64_t N, int64_t Nq, int64_t shift, int causal,
+                                               int nr, int64_t* rowi, int64_t* lim) {
   const int r = threadIdx.x;
   if (r < kDecMaxRows) {
     const int nqi = (int)Nq;
     rowi[r] = r < nr ? (int64_t)(g * G + r / nqi) * Nq + r % nqi : 0;
-    lim[r] = r < nr ? (causal ? N - Nq + r % nqi : N - 1) : -1;
+    lim[r] = r < nr ? (causal ? N - Nq + shift + r % nqi : N - 1) : -1;
   }
 }
 
@@ -510,7 +510,7 @@ struct DecLogitSmem {
 template <int D, int R>
 __global__ void __launch_bounds__(kDecThreads)
 attend_dec_logits(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __restrict__ xl,
-                  int G, int Hkv, int64_t N, int64_t Nq, int causal, float c, int32_t* status) {
+                  int G, int Hkv, int64_t N, int64_t Nq, int64_t shift, int causal, float c, int32_t* status) {
   __shared__ DecLogitSmem<D, R> sm;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hi = lane >> 5, lo = lane & 31;
@@ -524,7 +524,7 @@ attend_dec_logits(const uint16_t* __restrict__ q, kvc_packed_cache cache, float*
   const int64_t* hp = H + KVC_HDR_GLOBAL + g * KVC_HDR_PER_HEAD;
   const int64_t Rg = hp[4], ngroups = hp[22], Wk = hp[20], Qk = hp[21];
   if ((int64_t)blockIdx.x * kDecWaves >= ngroups) return;   // uniform for the block
-  dec_row_tables(g, G, N, Nq, causal, nr, sm.rowi, sm.lim);
+  dec_row_tables(g, G, N, Nq, shift, causal, nr, sm.rowi, sm.lim);
   dec_channel_table<D, kDecThreads>(cache, g, sm.kch, sm.scan, sm.cnt);
   const int nq = sm.cnt[3], nnz = sm.cnt[4];
   if (threadIdx.x == 0) {
@@ -629,7 +629,7 @@ struct DecValueSmem {
 template <int D, int R>
 __global__ void __launch_bounds__(kDecThreads)
 attend_dec_values(kvc_packed_cache cache, const float* __restrict__ xl, float* __restrict__ part,
-                  int G, int Hkv, int64_t N, int64_t Nq, int nsplit) {
+                  int G, int Hkv, int64_t N, int64_t Nq, int nsplit, int pstride) {
   constexpr int CPL = D / 64;            // channels per lane
   constexpr int GPR = D / 32;
   constexpr int PSTRIDE = D + 2;
@@ -641,7 +641,7 @@ attend_dec_values(kvc_packed_cache cache, const float* __restrict__ xl, float* _
   const int64_t* H = cache.header;
   if (H[0] != Hkv || H[1] != D || H[2] != N) return;         // reported by attend_dec_logits
   const int64_t* hp = H + KVC_HDR_GLOBAL + g * KVC_HDR_PER_HEAD;
-  dec_row_tables(g, G, N, Nq, 0, nr, sm.rowi, sm.lim);
+  dec_row_tables(g, G, N, Nq, 0, 0, nr, sm.rowi, sm.lim);
   __syncthreads();
   int64_t nch[4], ctot = 0;
 #pragma unroll
@@ -764,13 +764,99 @@ attend_dec_values(kvc_packed_cache cache, const float* __restrict__ xl, float* _
         Or = fmaf(sm.wo[w][r][cc], sc, Or);
       }
     }
-    float* pr = part + (sm.rowi[r] * nsplit + split) * PSTRIDE;
+    float* pr = part + (sm.rowi[r] * pstride + split) * PSTRIDE;
     if (cc == 0) {
       pr[0] = M;
       pr[1] = Lr;
     }
     pr[2 + cc] = Or;
   }
+}
+
+// ---------------------------------------------------------------------------------------
+// The append buffer: tokens generated after compression, raw bf16 [H_kv][n_new][d] at positions
+// N .. N+n_new-1 (RDKV summary §2.3 keeps new tokens beside the packed zones).  One wave per
+// query row: lanes = 64 new tokens at a time for the logits (the row in LDS, each lane reading
+// its token's key row as 16-byte loads), an exact online softmax, then lanes = channels for
+// O += p * v.  The row's (m, l, O) is one more split for attend_merge.
+// ---------------------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256)
+attend_append(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
+              float* __restrict__ part, int G, int Hq, int64_t Nq, int64_t n_new, int causal, float c,
+              int split, int pstride) {
+  constexpr int CPL = D / 64;
+  constexpr int PSTRIDE = D + 2;
+  __shared__ float qs[4][D];
+  __shared__ float pv[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t hr = (int64_t)blockIdx.x * 4 + wave;          // h * Nq + i
+  if (hr >= (int64_t)Hq * Nq) return;                         // uniform per wave; no block barrier follows
+  const int h = (int)(hr / Nq);
+  const int64_t i = hr % Nq;
+  const int g = h / G;
+  for (int cc = lane; cc < D; cc += 64) qs[wave][cc] = bf16_bits_to_f32(q[hr * D + cc]);
+  // the row sits at position N + n_new - Nq + i: it sees new tokens t <= n_new - Nq + i
+  int64_t nt = n_new;
+  if (causal) {
+    const int64_t lim = n_new - Nq + i + 1;
+    nt = lim < nt ? lim : nt;
+    if (nt < 0) nt = 0;
+  }
+  const uint16_t* kg = kn + (int64_t)g * n_new * D;
+  const uint16_t* vg = vn + (int64_t)g * n_new * D;
+  float m = -INFINITY, l = 0.f, o[CPL];
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) o[k] = 0.f;
+  __builtin_amdgcn_wave_barrier();
+  for (int64_t t0 = 0; t0 < nt; t0 += 64) {
+    const int64_t t = t0 + lane;
+    float x = -INFINITY;
+    if (t < nt) {
+      const uint4* kr = reinterpret_cast<const uint4*>(kg + t * D);
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < D / 8; ++j) {
+        const uint4 w = kr[j];
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc = fmaf(qs[wave][8 * j + 2 * e], __uint_as_float(ww[e] << 16), acc);
+          acc = fmaf(qs[wave][8 * j + 2 * e + 1], __uint_as_float(ww[e] & 0xFFFF0000u), acc);
+        }
+      }
+      x = acc * c;
+    }
+    const float mn = fmaxf(m, wave_max(x));
+    float p = 0.f;
+    if (mn > -INFINITY) {                                    // uniform
+      const float alpha = fast_exp2(m - mn);
+      p = fast_exp2(x - mn);
+      l = fmaf(l, alpha, p);
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) o[k] *= alpha;
+      m = mn;
+    }
+    pv[wave][lane] = p;
+    __builtin_amdgcn_wave_barrier();
+    const int cnt = (int)(nt - t0 < 64 ? nt - t0 : 64);
+#pragma unroll 8
+    for (int tp = 0; tp < cnt; ++tp) {
+      const float pp = pv[wave][tp];
+      const uint16_t* vr = vg + (t0 + tp) * D + lane * CPL;
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) o[k] = fmaf(pp, bf16_bits_to_f32(vr[k]), o[k]);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  const float lt = wave_sum(l);
+  float* pr = part + (hr * pstride + split) * PSTRIDE;
+  if (lane == 0) {
+    pr[0] = m;
+    pr[1] = lt;
+  }
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) pr[2 + lane * CPL + k] = o[k];
 }
 
 // The decode path addresses a head's V words with 32-bit offsets: N * d / 2 (the words of a
@@ -784,7 +870,7 @@ int nsplit_decode(const Layer& L) {
   int64_t want = (1024 + L.hkv - 1) / L.hkv;
   const int64_t cap = (cmax + 3) / 4;                    // at least 4 chunks (one per wave) per split
   if (want > cap) want = cap;
-  if (want > kMaxSplit) want = kMaxSplit;
+  if (want > kMaxSplit - 1) want = kMaxSplit - 1;   // one more for the append buffer
   if (want < 1) want = 1;
   return (int)want;
 }
@@ -796,7 +882,7 @@ int nsplit_of(const Layer& L) {
   const int64_t maxs = (L.n + 32 * 8 - 1) / (32 * 8);   // at least 8 groups per split
   if (want > maxs) want = maxs;
   if (want < 1) want = 1;
-  if (want > kMaxSplit) want = kMaxSplit;
+  if (want > kMaxSplit - 1) want = kMaxSplit - 1;   // one more for the append buffer
   return (int)want;
 }
 
@@ -806,20 +892,22 @@ size_t attend_ws_bytes(const Layer& L) {
   WsPlan p;
   const bool dec = use_decode(L);
   const int nsplit = dec ? nsplit_decode(L) : nsplit_of(L);
-  p.take((size_t)L.hq * L.nq * nsplit * (L.d + 2) * sizeof(float));
+  p.take((size_t)L.hq * L.nq * (nsplit + 1) * (L.d + 2) * sizeof(float));   // + the append buffer's split
   if (dec) p.take((size_t)L.hq * L.nq * L.n * sizeof(float));     // logits by token
   return p.off;
 }
 
 hipError_t launch_attend(const Layer& L, const uint16_t* q, const kvc_packed_cache& cache,
-                         float* out, float* lse, char* ws, hipStream_t s) {
+                         float* out, float* lse, char* ws, hipStream_t s, const uint16_t* k_new,
+                         const uint16_t* v_new, int64_t n_new) {
   const bool dec = use_decode(L);
   const int nsplit = dec ? nsplit_decode(L) : nsplit_of(L);
+  const int pstride = n_new > 0 ? nsplit + 1 : nsplit;      // partials per row
   WsPlan p;
-  float* part = reinterpret_cast<float*>(ws + p.take((size_t)L.hq * L.nq * nsplit * (L.d + 2) * sizeof(float)));
+  float* part = reinterpret_cast<float*>(ws + p.take((size_t)L.hq * L.nq * (nsplit + 1) * (L.d + 2) * sizeof(float)));
   (void)launch_reset_status(ws, s);
+  int32_t* status = reinterpret_cast<int32_t*>(ws);
   if (dec) {
-    int32_t* status = reinterpret_cast<int32_t*>(ws);
     float* xl = reinterpret_cast<float*>(ws + p.take((size_t)L.hq * L.nq * L.n * sizeof(float)));
     int64_t nb1 = ((L.n + 31) / 32 + kDecWaves - 1) / kDecWaves;   // blocks of 4 groups per head, at most
     const int64_t cap1 = (1024 + L.hkv - 1) / L.hkv;                 // the blocks loop over the rest
@@ -829,9 +917,10 @@ hipError_t launch_attend(const Layer& L, const uint16_t* q, const kvc_packed_cac
     const int rows = L.G * (int)L.nq;
 #define KVC_DEC(DD, RR)                                                                                   \
   do {                                                                                                    \
-    attend_dec_logits<DD, RR><<<g1, kDecThreads, 0, s>>>(q, cache, xl, L.G, L.hkv, L.n, L.nq, L.causal,  \
-                                                         L.c_log2, status);                              \
-    attend_dec_values<DD, RR><<<g3, kDecThreads, 0, s>>>(cache, xl, part, L.G, L.hkv, L.n, L.nq, nsplit); \
+    attend_dec_logits<DD, RR><<<g1, kDecThreads, 0, s>>>(q, cache, xl, L.G, L.hkv, L.n, L.nq, n_new,      \
+                                                         L.causal, L.c_log2, status);                    \
+    attend_dec_values<DD, RR><<<g3, kDecThreads, 0, s>>>(cache, xl, part, L.G, L.hkv, L.n, L.nq, nsplit,  \
+                                                         pstride);                                       \
   } while (0)
     if (L.d == 128) {
       if (rows <= 1) KVC_DEC(128, 1);
@@ -847,17 +936,26 @@ hipError_t launch_attend(const Layer& L, const uint16_t* q, const kvc_packed_cac
       else KVC_DEC(64, 16);
     }
 #undef KVC_DEC
-    attend_merge<<<(unsigned)((int64_t)L.hq * L.nq), kMergeThreads, 0, s>>>(part, out, lse, L.d, nsplit);
-    return hipGetLastError();
+  } else {
+    const int nRT = (int)((L.nq + kRows - 1) / kRows);
+    dim3 grid((unsigned)((L.G * nRT + kWaves - 1) / kWaves), (unsigned)nsplit, (unsigned)L.hkv);
+    if (L.d == 128)
+      attend_split<128><<<grid, kThreadsA, 0, s>>>(q, cache, part, L.G, L.hkv, L.n, L.nq, L.causal, L.c_log2, nsplit,
+                                                   n_new, pstride, status);
+    else
+      attend_split<64><<<grid, kThreadsA, 0, s>>>(q, cache, part, L.G, L.hkv, L.n, L.nq, L.causal, L.c_log2, nsplit,
+                                                  n_new, pstride, status);
   }
-  const int nRT = (int)((L.nq + kRows - 1) / kRows);
-  dim3 grid((unsigned)((L.G * nRT + kWaves - 1) / kWaves), (unsigned)nsplit, (unsigned)L.hkv);
-  int32_t* status = reinterpret_cast<int32_t*>(ws);
-  if (L.d == 128)
-    attend_split<128><<<grid, kThreadsA, 0, s>>>(q, cache, part, L.G, L.hkv, L.n, L.nq, L.causal, L.c_log2, nsplit, status);
-  else
-    attend_split<64><<<grid, kThreadsA, 0, s>>>(q, cache, part, L.G, L.hkv, L.n, L.nq, L.causal, L.c_log2, nsplit, status);
-  attend_merge<<<(unsigned)((int64_t)L.hq * L.nq), kMergeThreads, 0, s>>>(part, out, lse, L.d, nsplit);
+  if (n_new > 0) {
+    const unsigned nb = (unsigned)(((int64_t)L.hq * L.nq + 3) / 4);
+    if (L.d == 128)
+      attend_append<128><<<nb, 256, 0, s>>>(q, k_new, v_new, part, L.G, L.hq, L.nq, n_new, L.causal, L.c_log2,
+                                            nsplit, pstride);
+    else
+      attend_append<64><<<nb, 256, 0, s>>>(q, k_new, v_new, part, L.G, L.hq, L.nq, n_new, L.causal, L.c_log2,
+                                           nsplit, pstride);
+  }
+  attend_merge<<<(unsigned)((int64_t)L.hq * L.nq), kMergeThreads, 0, s>>>(part, out, lse, L.d, pstride);
   return hipGetLastError();
 }
 

@@ -73,7 +73,8 @@ hipError_t launch_pack(const Layer& L, const uint16_t* k, const uint16_t* v,
 // ---- compressed attend ------------------------------------------------------------------
 size_t attend_ws_bytes(const Layer& L);
 hipError_t launch_attend(const Layer& L, const uint16_t* q, const kvc_packed_cache& cache,
-                         float* out, float* lse, char* ws, hipStream_t s);
+                         float* out, float* lse, char* ws, hipStream_t s, const uint16_t* k_new = nullptr,
+                         const uint16_t* v_new = nullptr, int64_t n_new = 0);
 
 // ---- misc ------------------------------------------------------------------------------
 hipError_t launch_reset_status(char* ws, hipStream_t s);

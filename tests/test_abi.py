@@ -159,3 +159,22 @@ def test_keep_threshold_argument_errors(lib):
     # +-inf thresholds are valid; without a GPU the call stops at the device check
     st = lib.kvc_keep_threshold(ctypes.byref(d), FAKE, f(float("inf")), 0, 16, FAKE, None, None)
     assert st != 1
+
+
+def test_attend_append_argument_errors(lib):
+    d = _desc()
+    cs = C.PackedCacheC(*([FAKE] * C.PK_NBUF))
+    big = 1 << 30
+    st = lib.kvc_compressed_attend_append(ctypes.byref(d), FAKE, ctypes.byref(cs), FAKE, FAKE, -1,
+                                          FAKE, FAKE, FAKE, big, None)
+    assert st == 1
+    st = lib.kvc_compressed_attend_append(ctypes.byref(d), FAKE, ctypes.byref(cs), None, FAKE, 5,
+                                          FAKE, FAKE, FAKE, big, None)
+    assert st == 1
+    st = lib.kvc_compressed_attend_append(ctypes.byref(d), FAKE, ctypes.byref(cs), FAKE, FAKE + 2, 5,
+                                          FAKE, FAKE, FAKE, big, None)
+    assert st == 1
+    # n_new == 0 with NULL buffers is valid; without a GPU the call stops at the device check
+    st = lib.kvc_compressed_attend_append(ctypes.byref(d), FAKE, ctypes.byref(cs), None, None, 0,
+                                          FAKE, FAKE, FAKE, big, None)
+    assert st != 1

@@ -390,3 +390,48 @@ def test_attend_decode_row_that_sees_nothing():
     assert np.all(np.isneginf(lh_r[:, 0]))
     H.assert_abs(og, out_r, 2e-2, "decode attend output")
     H.assert_abs(lg[:, 1], lh_r[:, 1], 1e-3, "decode attend lse")
+
+
+APPEND_CASES = [
+    # name, H_q, H_kv, d, N (packed), n_new, rows per query head, causal
+    ("app_dec_g4_d128", 8, 2, 128, 1500, 37, 1, True),
+    ("app_dec_g8_d64_r2", 8, 1, 64, 700, 130, 2, True),
+    ("app_mfma_g4_d128_r64", 8, 2, 128, 1200, 100, 64, True),
+    ("app_mfma_rows_before_buffer", 4, 1, 128, 900, 20, 48, True),
+    ("app_dec_noncausal", 4, 2, 128, 600, 50, 1, False),
+]
+
+
+@pytest.mark.parametrize("case", APPEND_CASES, ids=[c[0] for c in APPEND_CASES])
+def test_attend_with_append_buffer(case):
+    """Packed cache + raw bf16 buffer of new tokens against the oracle, on the decode path
+    (few rows) and the matrix-core path (many rows, some of them before the buffer)."""
+    name, hq, hkv, d, N, n_new, rows, causal = case
+    print(f"case {name}: H_q={hq} H_kv={hkv} d={d} N={N} n_new={n_new} rows={rows} causal={causal}", flush=True)
+    seed = zlib.crc32(name.encode())
+    rng = np.random.default_rng(seed)
+    x = make_inputs(hq, hkv, d, N + n_new, N + n_new, seed=seed % 1000, k_outliers=True)
+    k, v = np.ascontiguousarray(x["k"][:, :N]), np.ascontiguousarray(x["v"][:, :N])
+    kn, vn = np.ascontiguousarray(x["k"][:, N:]), np.ascontiguousarray(x["v"][:, N:])
+    bv, bk = _random_widths(rng, hkv, N, d)
+    desc = H.desc_of(hq, hkv, d, N, N, causal)
+    cache, st = H.pack(desc, H.dev_bf16(k), H.dev_bf16(v), H.dev_u8(bv), H.dev_u8(bk))
+    assert st == 0
+    qf_bits = np.ascontiguousarray(x["q"][:, N + n_new - rows:, :])
+    desc_f = H.desc_of(hq, hkv, d, N, rows, causal)
+    out = torch.empty(hq, rows, d, dtype=torch.float32, device=H.DEV)
+    lse = torch.empty(hq, rows, dtype=torch.float32, device=H.DEV)
+    ws = kvc.workspace(kvc.OP_COMPRESSED_ATTEND, desc_f, 0, H.DEV)
+    kvc.kvc_compressed_attend_append(desc_f, H.dev_bf16(qf_bits), cache, H.dev_bf16(kn), H.dev_bf16(vn),
+                                     out, lse, ws)
+    torch.cuda.synchronize()
+    assert kvc.kvc_get_device_status(ws) == 0
+    out_r, lh_r = oracle.compressed_attend_append(qf_bits, k, v, bv, bk, kn, vn, causal=causal)
+    H.assert_abs(out.cpu().numpy(), out_r, 2e-2, "append attend output")
+    H.assert_abs(lse.cpu().numpy(), lh_r, 1e-3, "append attend lse")
+    # no new tokens: the same call is the packed cache alone
+    kvc.kvc_compressed_attend_append(desc_f, H.dev_bf16(qf_bits), cache, None, None, out, lse, ws)
+    torch.cuda.synchronize()
+    out0, l0 = oracle.compressed_attend(qf_bits, k, v, bv, bk, causal=causal)
+    H.assert_abs(out.cpu().numpy(), out0, 2e-2, "attend output, empty buffer")
+    H.assert_abs(lse.cpu().numpy(), l0, 1e-3, "attend lse, empty buffer")
