@@ -42,17 +42,18 @@ from .allocation import (
     retained_counts,
     topk_keep,
     threshold_keep,
+    pilot_budgets,
 )
 from .quantize import quantize_group, pack_group_words, pack_cache, HDR_GLOBAL, HDR_PER_HEAD
 from .fidelity import (dequantized_head, attend, full_attend, compressed_attend, compressed_attend_append,
-                       fidelity_terms)
+                       fidelity_terms, fidelity_terms_per_head)
 
 __all__ = [
     "as_f64", "query_positions", "default_scale",
     "row_lse", "token_scores_sum", "token_scores_max", "hidden_row_norms", "value_out_norms",
     "channel_weights",
     "LEVELS", "step_ratios", "step_keys", "lagrangian_allocate", "stage_costs",
-    "allocate_v_tokens", "allocate_k_channels", "retained_counts", "topk_keep", "threshold_keep",
+    "allocate_v_tokens", "allocate_k_channels", "retained_counts", "topk_keep", "threshold_keep", "pilot_budgets",
     "quantize_group", "pack_group_words", "pack_cache", "HDR_GLOBAL", "HDR_PER_HEAD",
-    "dequantized_head", "attend", "full_attend", "compressed_attend", "compressed_attend_append", "fidelity_terms",
+    "dequantized_head", "attend", "full_attend", "compressed_attend", "compressed_attend_append", "fidelity_terms", "fidelity_terms_per_head",
 ]

@@ -179,3 +179,29 @@ def threshold_keep(scores, threshold, window=128, keep_bits=16):
     with np.errstate(invalid="ignore"):
         keep = (s >= thr) | in_window[None, :]
     return np.where(keep, np.uint8(keep_bits), np.uint8(0)).astype(np.uint8)
+
+
+def pilot_budgets(mse, total, floor_each=0):
+    """KVSculpt summary, §2 (adaptive budget): after a pilot run at a uniform budget, give
+    each head a share of the total budget in proportion to the square root of its pilot MSE.
+
+    Readings: every head first gets floor_each; the rest, R = total - n * floor_each, is split
+    as R * sqrt(mse_i) / sum_j sqrt(mse_j), rounded down, and the units left over go one each
+    to the largest fractional parts (ties to the lower index).  If every MSE is 0, the shares
+    are equal.  Shares are computed in float64.
+    """
+    m = np.asarray(mse, dtype=np.float64)
+    n = m.size
+    rest = int(total) - n * int(floor_each)
+    if rest < 0:
+        raise ValueError("total is below n * floor_each")
+    r = np.sqrt(m)
+    tot = float(r.sum())
+    share = np.full(n, rest / n) if tot == 0.0 else rest * (r / tot)
+    base = np.floor(share).astype(np.int64)
+    left = rest - int(base.sum())
+    frac = share - base
+    order = sorted(range(n), key=lambda i: (-frac[i], i))
+    for i in order[:left]:
+        base[i] += 1
+    return base + int(floor_each)

@@ -139,3 +139,25 @@ def fidelity_terms(y_hat, y, lse_hat, lse):
     dy = np.asarray(y_hat, dtype=np.float64) - np.asarray(y, dtype=np.float64)
     dl = np.asarray(lse_hat, dtype=np.float64) - np.asarray(lse, dtype=np.float64)
     return float((dy * dy).sum()), float((dl * dl).sum())
+
+
+def fidelity_terms_per_head(y_hat, y, lse_hat, lse):
+    """Per query head h: (sum over rows and channels of (Y_hat - Y)^2, sum over rows of
+    (l_hat - l)^2), the two terms of KVSculpt's loss (§2) split by head.  Reading: a row with
+    no visible token in both caches (l_hat = l = -inf, outputs 0) contributes 0 to the LSE
+    term; one empty and one not contributes +inf.
+    """
+    dy = np.asarray(y_hat, dtype=np.float64) - np.asarray(y, dtype=np.float64)
+    lh = np.asarray(lse_hat, dtype=np.float64)
+    lr = np.asarray(lse, dtype=np.float64)
+    hq = dy.shape[0]
+    out = np.zeros((hq, 2))
+    for h in range(hq):
+        out[h, 0] = float((dy[h] * dy[h]).sum())
+        acc = 0.0
+        for a, b in zip(lh[h].ravel(), lr[h].ravel()):
+            if a == b:                       # equal values, both -inf included
+                continue
+            acc += (a - b) ** 2
+        out[h, 1] = acc
+    return out

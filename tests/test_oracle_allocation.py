@@ -207,3 +207,30 @@ def test_threshold_keep_monotone_in_threshold_and_window():
     small = oracle.threshold_keep(s, 1.0, 16)
     large = oracle.threshold_keep(s, 1.0, 200)
     assert ((small > 0) <= (large > 0)).all()
+
+
+def test_pilot_budget_worked_examples(golden_dir):
+    with open(os.path.join(golden_dir, "pilot_budget_example.txt")) as f:
+        rows = [l for l in f if l.strip() and not l.startswith("#")]
+    assert len(rows) == 4
+    for r in rows:
+        head, mse, want = (part.split() for part in r.split("|"))
+        got = oracle.pilot_budgets([float(x) for x in mse], int(head[0]), int(head[1]))
+        assert got.tolist() == [int(x) for x in want]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_pilot_budget_properties(seed):
+    rng = np.random.default_rng(seed)
+    n = 9
+    mse = rng.random(n) ** 3
+    total = 1000 + seed
+    b = oracle.pilot_budgets(mse, total)
+    assert int(b.sum()) == total                                  # the whole budget, no more
+    share = total * np.sqrt(mse) / np.sqrt(mse).sum()
+    assert np.all(np.abs(b - share) < 1.0)                        # within one unit of the exact share
+    order = np.argsort(mse)
+    assert np.all(np.diff(b[order]) >= 0)                         # more pilot error, no smaller budget
+    assert b.tolist() == oracle.pilot_budgets(mse * 37.0, total).tolist()   # only ratios matter
+    bf = oracle.pilot_budgets(mse, total, floor_each=50)
+    assert bf.min() >= 50 and int(bf.sum()) == total

@@ -148,3 +148,24 @@ def test_append_buffer_empty_is_the_cache_alone():
     y, l = oracle.compressed_attend_append(q, x["k"], x["v"], bv, bk, empty, empty, causal=True)
     yc, lc = oracle.compressed_attend(q, x["k"], x["v"], bv, bk, causal=True)
     assert np.array_equal(y, yc) and np.array_equal(l, lc)
+
+
+def test_fidelity_terms_per_head_closed_forms():
+    rng = np.random.default_rng(4)
+    hq, nq, d = 3, 5, 8
+    y = rng.standard_normal((hq, nq, d))
+    l = rng.standard_normal((hq, nq))
+    c = np.array([0.5, -2.0, 0.0])
+    yh = y + c[:, None, None]                                     # a constant offset per head
+    lh = l + np.array([1.0, 0.0, 3.0])[:, None]
+    t = oracle.fidelity_terms_per_head(yh, y, lh, l)
+    np.testing.assert_allclose(t[:, 0], nq * d * c ** 2, rtol=1e-12)
+    np.testing.assert_allclose(t[:, 1], nq * np.array([1.0, 0.0, 9.0]), rtol=1e-12)
+    tot = oracle.fidelity_terms(yh, y, lh, l)
+    assert t[:, 0].sum() == pytest.approx(tot[0], rel=1e-12) and t[:, 1].sum() == pytest.approx(tot[1], rel=1e-12)
+    # rows empty in both caches add 0; empty in one only adds +inf
+    l2, lh2 = l.copy(), lh.copy()
+    l2[0, 1] = lh2[0, 1] = -np.inf
+    assert np.isfinite(oracle.fidelity_terms_per_head(yh, y, lh2, l2)[0, 1])
+    lh2[1, 2] = -np.inf
+    assert np.isinf(oracle.fidelity_terms_per_head(yh, y, lh2, l2)[1, 1])
