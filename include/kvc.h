@@ -12,6 +12,9 @@
  *   kvc_quantize_pack      group quantisation and packing into the width zones
  *   kvc_compressed_attend  attention output and LSE over a packed cache
  *   kvc_compressed_attend_append  the same, over the packed cache and a bf16 buffer of new tokens
+ *   kvc_keep_threshold     KVzap threshold keep plus a recent-token window
+ *   kvc_fidelity_terms     per-head output and LSE errors of a compressed attend (KVSculpt loss)
+ *   kvc_pilot_budgets      per-head budgets in proportion to sqrt(pilot MSE) (host only)
  *
  * Sources (summary pages of the papers; section numbers are the pages' own):
  *   "RDKV - rate-distortion bit allocation for joint eviction and quantization of the KV
@@ -20,7 +23,7 @@
  *   "KVzap - fast, adaptive and faithful KV cache pruning": §2.1 KVzip+ score, §2.2 one score
  *    per KV head, §2.3 fixed-budget keep of KVzip.
  *   "KVSculpt: KV Cache Compression as Distillation": §2 loss terms (output error and LSE
- *    error) that the fidelity attend measures.
+ *    error) that the fidelity attend measures, and §2's adaptive per-head budget.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -256,6 +259,32 @@ kvc_status kvc_compressed_attend_append(const kvc_layer_desc* desc, const void* 
                                         const kvc_packed_cache* cache, const void* k_new,
                                         const void* v_new, int64_t n_new, float* out, float* lse,
                                         void* ws, size_t ws_bytes, void* hip_stream);
+
+/* The two terms of KVSculpt's distillation loss (KVSculpt §2), split by query head: for head h,
+ * terms[h][0] = sum over rows i and channels c of (y_hat - y)^2 and terms[h][1] = sum over rows
+ * of (lse_hat - lse)^2, both accumulated in float64 from the float32 inputs.  A row whose two
+ * LSE values are equal adds 0 (this covers a row that sees no token in either attend, both
+ * -inf); -inf against a finite value adds +inf.  The summation order is fixed (a strided
+ * split over 256 lanes, then a fixed tree), so repeated calls give identical bits.
+ * y_hat, y: f32 [H_q][Nq][d] (device, 16-byte aligned), the outputs of kvc_compressed_attend
+ * over the compressed and the uncompressed cache.  lse_hat, lse: f32 [H_q][Nq] (device).
+ * terms: f64 [H_q][2] (device).  No workspace; asynchronous on hip_stream.  Uses desc's
+ * n_q_heads, head_dim and n_queries.  Errors: a NULL or misaligned pointer. */
+kvc_status kvc_fidelity_terms(const kvc_layer_desc* desc, const float* y_hat, const float* lse_hat,
+                              const float* y, const float* lse, double* terms, void* hip_stream);
+
+/* KVSculpt §2 adaptive budget: after a pilot at a uniform budget, head i's share of `total` is
+ * proportional to sqrt(mse[i]).  Each head first gets floor_each; the rest R = total -
+ * n*floor_each is split as R * sqrt(mse[i]) / sum_j sqrt(mse[j]) (float64, the sum taken in
+ * index order), rounded down, and the units left go one each to the largest fractional parts,
+ * ties to the lower index.  All MSE zero gives equal shares.  If rounding ever made the floors
+ * exceed R, the excess is taken back from the smallest fractional parts among heads holding a
+ * unit, ties to the higher index.  The budgets always add up to `total`.
+ * mse: f64 [n] and budgets: i64 [n] are HOST memory (this call runs on the host and touches
+ * no device).  Errors: NULL pointer, n < 1, total or floor_each < 0, total >= 2^53, an MSE that
+ * is negative or not finite, total < n * floor_each. */
+kvc_status kvc_pilot_budgets(const double* mse, int32_t n, int64_t total, int64_t floor_each,
+                             int64_t* budgets);
 
 /* Device status codes (bit set). */
 #define KVC_DEV_BAD_WIDTH 1

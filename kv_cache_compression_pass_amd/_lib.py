@@ -30,7 +30,7 @@ DEV_BAD_CACHE = 2
 EXPORTED = (
     "kvc_workspace_size", "kvc_row_lse", "kvc_score_tokens", "kvc_channel_weights",
     "kvc_allocate_bits", "kvc_keep_threshold", "kvc_packed_capacity", "kvc_quantize_pack",
-    "kvc_compressed_attend", "kvc_compressed_attend_append",
+    "kvc_compressed_attend", "kvc_compressed_attend_append", "kvc_fidelity_terms", "kvc_pilot_budgets",
     "kvc_get_device_status", "kvc_status_string", "kvc_last_error", "kvc_version",
 )
 
@@ -101,10 +101,13 @@ def load():
     lib.kvc_compressed_attend.argtypes = [D, P, ctypes.POINTER(PackedCacheC), P, P, P, S, P]
     lib.kvc_compressed_attend_append.argtypes = [D, P, ctypes.POINTER(PackedCacheC), P, P, ctypes.c_int64,
                                                  P, P, P, S, P]
+    lib.kvc_fidelity_terms.argtypes = [D, P, P, P, P, P, P]
+    lib.kvc_pilot_budgets.argtypes = [ctypes.POINTER(ctypes.c_double), I32, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.POINTER(ctypes.c_int64)]
     lib.kvc_get_device_status.argtypes = [P, ctypes.POINTER(I32), P]
     for name in ("kvc_row_lse", "kvc_score_tokens", "kvc_channel_weights", "kvc_allocate_bits", "kvc_keep_threshold",
                  "kvc_packed_capacity", "kvc_quantize_pack", "kvc_compressed_attend",
-                 "kvc_compressed_attend_append",
+                 "kvc_compressed_attend_append", "kvc_fidelity_terms", "kvc_pilot_budgets",
                  "kvc_get_device_status"):
         getattr(lib, name).restype = I32
     lib.kvc_status_string.argtypes = [I32]

@@ -185,6 +185,21 @@ def kvc_compressed_attend_append(desc, q, cache, k_new, v_new, out, lse, ws, str
                                                  _stream(stream)))
 
 
+def kvc_fidelity_terms(desc, y_hat, lse_hat, y, lse, terms, stream=None):
+    """terms: float64 tensor [H_q][2] on the device (output)."""
+    _check(C.load().kvc_fidelity_terms(ctypes.byref(desc), _ptr(y_hat), _ptr(lse_hat), _ptr(y), _ptr(lse),
+                                       _ptr(terms), _stream(stream)))
+
+
+def kvc_pilot_budgets(mse, total, floor_each=0):
+    """Host call: mse is a sequence of per-head pilot MSE values; returns int64 numpy budgets."""
+    m = np.ascontiguousarray(np.asarray(mse, dtype=np.float64).ravel())
+    out = np.zeros(m.size, dtype=np.int64)
+    _check(C.load().kvc_pilot_budgets(m.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), int(m.size), int(total),
+                                      int(floor_each), out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
+    return out
+
+
 def kvc_get_device_status(ws, stream=None):
     code = ctypes.c_int32(0)
     _check(C.load().kvc_get_device_status(_ptr(ws), ctypes.byref(code), _stream(stream)))

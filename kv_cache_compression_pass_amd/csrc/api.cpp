@@ -2,12 +2,14 @@
 // kernel launchers.  Every argument error is detected here, before anything is enqueued.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "internal.hpp"
 #include "kvc.h"
@@ -349,6 +351,63 @@ kvc_status kvc_compressed_attend_append(const kvc_layer_desc* desc, const void* 
   return finish(launch_attend(L, (const uint16_t*)q, *cache, out, lse, (char*)ws, (hipStream_t)hip_stream,
                               (const uint16_t*)k_new, (const uint16_t*)v_new, n_new),
                 "kvc_compressed_attend_append launch");
+}
+
+kvc_status kvc_fidelity_terms(const kvc_layer_desc* desc, const float* y_hat, const float* lse_hat,
+                              const float* y, const float* lse, double* terms, void* hip_stream) {
+  Layer L;
+  KVC_TRY(make_layer(desc, &L));
+  KVC_TRY(need_ptr(y_hat, 16, "y_hat"));
+  KVC_TRY(need_ptr(y, 16, "y"));
+  KVC_TRY(need_ptr(lse_hat, 4, "lse_hat"));
+  KVC_TRY(need_ptr(lse, 4, "lse"));
+  KVC_TRY(need_ptr(terms, 8, "terms"));
+  KVC_TRY(need_device());
+  return finish(launch_fidelity_terms(L, y_hat, lse_hat, y, lse, terms, (hipStream_t)hip_stream),
+                "kvc_fidelity_terms launch");
+}
+
+kvc_status kvc_pilot_budgets(const double* mse, int32_t n, int64_t total, int64_t floor_each,
+                             int64_t* budgets) {
+  if (!mse || !budgets) return fail(KVC_ERR_INVALID_ARG, "mse / budgets is NULL");
+  if (n < 1) return fail(KVC_ERR_INVALID_ARG, "n must be >= 1");
+  if (total < 0 || floor_each < 0) return fail(KVC_ERR_INVALID_ARG, "total and floor_each must be >= 0");
+  if (total >= (int64_t(1) << 53)) return fail(KVC_ERR_UNSUPPORTED, "total >= 2^53");
+  for (int32_t i = 0; i < n; ++i)
+    if (!std::isfinite(mse[i]) || mse[i] < 0.0)
+      return fail(KVC_ERR_INVALID_ARG, "mse[%d] must be finite and >= 0", (int)i);
+  if (floor_each > total / n) return fail(KVC_ERR_INVALID_ARG, "total is below n * floor_each");
+  const int64_t rest = total - (int64_t)n * floor_each;
+  std::vector<double> r(n), share(n), frac(n);
+  double tot = 0.0;
+  for (int32_t i = 0; i < n; ++i) {
+    r[i] = std::sqrt(mse[i]);
+    tot += r[i];
+  }
+  for (int32_t i = 0; i < n; ++i) share[i] = tot == 0.0 ? (double)rest / (double)n : (double)rest * (r[i] / tot);
+  int64_t used = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const double b = std::floor(share[i]);
+    budgets[i] = (int64_t)b;
+    frac[i] = share[i] - b;
+    used += budgets[i];
+  }
+  int64_t left = rest - used;
+  std::vector<int32_t> order;
+  order.reserve(n);
+  if (left >= 0) {
+    for (int32_t i = 0; i < n; ++i) order.push_back(i);
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return frac[a] > frac[b]; });
+    for (int64_t j = 0; j < left && j < n; ++j) budgets[order[j]] += 1;
+  } else {
+    // rounding left the floors above the rest: take units back from the smallest fractions
+    for (int32_t i = n - 1; i >= 0; --i)
+      if (budgets[i] > 0) order.push_back(i);
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return frac[a] < frac[b]; });
+    for (int64_t j = 0; j < -left && j < (int64_t)order.size(); ++j) budgets[order[j]] -= 1;
+  }
+  for (int32_t i = 0; i < n; ++i) budgets[i] += floor_each;
+  return ok();
 }
 
 kvc_status kvc_get_device_status(const void* ws, int32_t* code, void* hip_stream) {

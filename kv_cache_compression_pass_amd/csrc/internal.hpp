@@ -63,6 +63,10 @@ hipError_t launch_allocate(const Layer& L, int stage, const float* weight, const
 hipError_t launch_keep_threshold(const Layer& L, const float* scores, float threshold, int64_t window,
                                  int keep_bits, uint8_t* bits_out, int64_t* kept, hipStream_t s);
 
+// ---- fidelity terms ---------------------------------------------------------------------
+hipError_t launch_fidelity_terms(const Layer& L, const float* y_hat, const float* lse_hat, const float* y,
+                                 const float* lse, double* terms, hipStream_t s);
+
 // ---- quantise / pack --------------------------------------------------------------------
 void packed_capacity(const Layer& L, size_t bytes[KVC_PK_NBUF]);
 size_t pack_ws_bytes(const Layer& L);

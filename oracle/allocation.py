@@ -188,20 +188,35 @@ def pilot_budgets(mse, total, floor_each=0):
     Readings: every head first gets floor_each; the rest, R = total - n * floor_each, is split
     as R * sqrt(mse_i) / sum_j sqrt(mse_j), rounded down, and the units left over go one each
     to the largest fractional parts (ties to the lower index).  If every MSE is 0, the shares
-    are equal.  Shares are computed in float64.
+    are equal.  Shares are computed in float64.  Should rounding ever make the floors add up to
+    more than R, the excess is taken back one unit each from the smallest fractional parts among
+    heads that still hold a unit (ties to the higher index).
     """
-    m = np.asarray(mse, dtype=np.float64)
+    m = np.asarray(mse, dtype=np.float64).ravel()
     n = m.size
+    if n < 1:
+        raise ValueError("no heads")
+    if not np.all(np.isfinite(m)) or np.any(m < 0):
+        raise ValueError("MSE values must be finite and >= 0")
+    if int(floor_each) < 0 or int(total) < 0:
+        raise ValueError("total and floor_each must be >= 0")
     rest = int(total) - n * int(floor_each)
     if rest < 0:
         raise ValueError("total is below n * floor_each")
     r = np.sqrt(m)
-    tot = float(r.sum())
+    tot = 0.0
+    for x in r:                              # left to right
+        tot += float(x)
     share = np.full(n, rest / n) if tot == 0.0 else rest * (r / tot)
     base = np.floor(share).astype(np.int64)
     left = rest - int(base.sum())
     frac = share - base
-    order = sorted(range(n), key=lambda i: (-frac[i], i))
-    for i in order[:left]:
-        base[i] += 1
+    if left >= 0:
+        order = sorted(range(n), key=lambda i: (-frac[i], i))
+        for i in order[:left]:
+            base[i] += 1
+    else:
+        order = sorted((i for i in range(n) if base[i] > 0), key=lambda i: (frac[i], -i))
+        for i in order[:-left]:
+            base[i] -= 1
     return base + int(floor_each)

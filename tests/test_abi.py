@@ -178,3 +178,31 @@ def test_attend_append_argument_errors(lib):
     st = lib.kvc_compressed_attend_append(ctypes.byref(d), FAKE, ctypes.byref(cs), None, None, 0,
                                           FAKE, FAKE, FAKE, big, None)
     assert st != 1
+
+
+def test_fidelity_terms_argument_errors(lib):
+    d = _desc()
+    assert lib.kvc_fidelity_terms(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.kvc_fidelity_terms(ctypes.byref(d), FAKE, FAKE, FAKE + 4, FAKE, FAKE, None) == 1
+    assert lib.kvc_fidelity_terms(ctypes.byref(d), FAKE, FAKE + 2, FAKE, FAKE, FAKE, None) == 1
+    assert lib.kvc_fidelity_terms(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE + 4, None) == 1
+    bad = _desc(head_dim=96)
+    assert lib.kvc_fidelity_terms(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, None) == 2
+
+
+def test_pilot_budget_argument_errors(lib):
+    D = ctypes.c_double * 3
+    I = ctypes.c_int64 * 3
+    out = I()
+    assert lib.kvc_pilot_budgets(None, 3, 10, 0, out) == 1
+    assert lib.kvc_pilot_budgets(D(1, 2, 3), 3, 10, 0, None) == 1
+    assert lib.kvc_pilot_budgets(D(1, 2, 3), 0, 10, 0, out) == 1
+    assert lib.kvc_pilot_budgets(D(1, 2, 3), 3, -1, 0, out) == 1
+    assert lib.kvc_pilot_budgets(D(1, 2, 3), 3, 10, -1, out) == 1
+    assert lib.kvc_pilot_budgets(D(1, -2, 3), 3, 10, 0, out) == 1
+    assert lib.kvc_pilot_budgets(D(1, float("nan"), 3), 3, 10, 0, out) == 1
+    assert lib.kvc_pilot_budgets(D(1, float("inf"), 3), 3, 10, 0, out) == 1
+    assert lib.kvc_pilot_budgets(D(1, 2, 3), 3, 10, 4, out) == 1          # 3 * 4 > 10
+    assert lib.kvc_pilot_budgets(D(1, 2, 3), 3, 1 << 53, 0, out) == 2
+    assert lib.kvc_pilot_budgets(D(1, 2, 3), 3, 12, 4, out) == 0          # rest 0
+    assert list(out) == [4, 4, 4]

@@ -97,6 +97,13 @@ def _pipeline(name, hq, hkv, d, N, Nq, causal, avg, seed, x=None, n_fid=64):
     y_r, l_r = oracle.full_attend(qf_bits, x["k"], x["v"], causal=causal)
     H.assert_abs(y_g.cpu().numpy(), y_r, 2e-2, "full attend output")
     H.assert_abs(l_g.cpu().numpy(), l_r, 1e-3, "full attend lse")
+
+    # KVSculpt's loss terms per query head, from the two attends above
+    terms = torch.empty(hq, 2, dtype=torch.float64, device=H.DEV)
+    kvc.kvc_fidelity_terms(desc_f, out_g, lh_g, y_g, l_g, terms)
+    t_r = oracle.fidelity_terms_per_head(out_g.cpu().numpy(), y_g.cpu().numpy(), lh_g.cpu().numpy(),
+                                         l_g.cpu().numpy())
+    np.testing.assert_allclose(terms.cpu().numpy(), t_r, rtol=1e-10, atol=0)
     return x
 
 
@@ -435,3 +442,44 @@ def test_attend_with_append_buffer(case):
     out0, l0 = oracle.compressed_attend(qf_bits, k, v, bv, bk, causal=causal)
     H.assert_abs(out.cpu().numpy(), out0, 2e-2, "attend output, empty buffer")
     H.assert_abs(lse.cpu().numpy(), l0, 1e-3, "attend lse, empty buffer")
+
+
+FID_CASES = [
+    # name, H_q, Nq, d
+    ("fid_one_row_d128", 4, 1, 128),
+    ("fid_ragged_d64", 6, 1001, 64),
+    ("fid_many_rows_d128", 32, 2048, 128),
+    ("fid_short_d64", 2, 3, 64),
+]
+
+
+@pytest.mark.parametrize("case", FID_CASES, ids=[c[0] for c in FID_CASES])
+def test_fidelity_terms(case):
+    """Per-head output and LSE error sums against the oracle on the same float32 arrays, with
+    rows that see nothing in both attends (0), in one of them (+inf) and equal finite LSEs."""
+    name, hq, nq, d = case
+    print(f"case {name}: H_q={hq} Nq={nq} d={d}", flush=True)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    y = rng.normal(0.0, 1.0, (hq, nq, d)).astype(np.float32)
+    y_hat = (y + rng.normal(0.0, 0.05, y.shape)).astype(np.float32)
+    lse = rng.normal(5.0, 2.0, (hq, nq)).astype(np.float32)
+    lse_hat = (lse + rng.normal(0.0, 0.01, lse.shape)).astype(np.float32)
+    lse_hat[0, 0] = lse[0, 0]                               # equal: adds 0
+    if nq > 1:
+        lse[1 % hq, 1] = lse_hat[1 % hq, 1] = -np.inf       # sees nothing in both: adds 0
+        y[1 % hq, 1] = y_hat[1 % hq, 1] = 0.0
+    if hq > 2:
+        lse_hat[2, nq - 1] = -np.inf                        # sees nothing only after compression
+    desc = H.desc_of(hq, hq, d, nq, nq, True)
+    terms = torch.empty(hq, 2, dtype=torch.float64, device=H.DEV)
+    kvc.kvc_fidelity_terms(desc, H.dev_f32(y_hat), H.dev_f32(lse_hat), H.dev_f32(y), H.dev_f32(lse), terms)
+    got = terms.cpu().numpy()
+    want = oracle.fidelity_terms_per_head(y_hat, y, lse_hat, lse)
+    fin = np.isfinite(want)
+    np.testing.assert_array_equal(np.isfinite(got), fin)
+    np.testing.assert_array_equal(got[~fin], want[~fin])
+    np.testing.assert_allclose(got[fin], want[fin], rtol=1e-10, atol=0)
+    # fixed summation order: a second call gives the same bits
+    again = torch.empty_like(terms)
+    kvc.kvc_fidelity_terms(desc, H.dev_f32(y_hat), H.dev_f32(lse_hat), H.dev_f32(y), H.dev_f32(lse), again)
+    assert torch.equal(terms, again)
