@@ -4,17 +4,18 @@
 //
 // Kernels, all on one stream (kernel boundaries order every step):
 //   pack_count   per (1024-token chunk, head): tokens per width zone; width validation
-//   pack_layout  per head: chunk bases (block scan), K-channel word/param offsets and the
-//                channels sorted by width, per-head totals
+//   pack_layout  per head: chunk bases (block scan), K-channel word/param offsets, per-head
+//                totals
 //   pack_header  one block: head offsets (scans over heads), the header, the status word
 //   pack_index   per chunk: ordered ranks -> v_idx, k_keep, k_vloc
-//   pack_k       one block per (32 retained tokens, head) quantises every K channel
+//   pack_k       one wave per (group of 32 retained tokens, head) quantises every K channel
 //   pack_v       one block per 32 tokens of one width zone quantises their V groups
 // Codes follow the definition z = min, s = float32(float64(max - min) / (2^b - 1)),
-// code = clamp(rint(float64(x - z) / s)).  The kernel evaluates v = (x - z) / s in fp32, whose
-// error is below 5e-5 for every v <= 255.5; only where v lies within 1e-4 of a rounding
-// boundary (k + 1/2) can fp32 and fp64 round differently, and there the code is recomputed
-// with the fp64 division.  Codes, scales and zeros are therefore bit-exact.
+// code = clamp(rint(float64(x - z) / s)).  The kernels evaluate v = (x - z) / s in fp32, whose
+// error is at most about 3 * 2^-24 * v; only where v lies within 2^(b-21) (over 2.6 times that
+// error for every v < 2^b) of a rounding boundary (k + 1/2) can fp32 and fp64 round
+// differently, and there the code is recomputed with the fp64 division.  Codes, scales and
+// zeros are therefore bit-exact.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -31,8 +32,7 @@ struct PackWs {
   int64_t* base;       // [Hkv][nchunk][4]  zone position of each chunk's first token
   int64_t* rbase;      // [Hkv][nchunk]     retained rank of each chunk's first token
   int64_t* htot;       // [Hkv][8]          tokens per zone (4), R, K words per group, K params per group, bad
-  int32_t* kch;        // [Hkv][D][4]       channels of nonzero width sorted by width:
-                       //                   {channel, word offset, param slot, width}
+  int32_t* kchc;       // [Hkv][D][4]       per K channel: {word offset, param slot, width, 0}
 };
 
 __device__ __forceinline__ int zone_of(uint32_t b) {
@@ -80,14 +80,13 @@ pack_count(const uint8_t* __restrict__ bits_v, int64_t N, int nchunk, int32_t* _
 // One block of 1024 threads per KV head.
 //  1. chunk bases: the four zone counts travel as two uint64 words with 32-bit fields (a field
 //     never exceeds N < 2^29), so one block scan per word gives every zone's prefix;
-//  2. K channels: one uint64 per channel packs {words (16 bits), params (16 bits), one 8-bit
-//     count per width class}; one scan gives each channel's word offset, param slot and rank
-//     in its width class, hence its place in the width-sorted channel list.
+//  2. K channels: one uint64 per channel packs {words (16 bits), params (16 bits)}; one scan
+//     gives each channel's word offset and parameter slot inside a group.
 template <int D>
 __global__ void __launch_bounds__(1024)
 pack_layout(const int32_t* __restrict__ cnt, const int32_t* __restrict__ cbad,
             const uint8_t* __restrict__ bits_k, int64_t N, int nchunk, int64_t* __restrict__ base,
-            int64_t* __restrict__ rbase, int64_t* __restrict__ htot, int32_t* __restrict__ kch,
+            int64_t* __restrict__ rbase, int64_t* __restrict__ htot, int32_t* __restrict__ kchc,
             uint8_t* __restrict__ k_width) {
   __shared__ uint64_t sh[16];
   __shared__ int32_t bad_s;
@@ -131,27 +130,14 @@ pack_layout(const int32_t* __restrict__ cnt, const int32_t* __restrict__ cbad,
     cls = zone_of(bk);
     if (cls < 0) cls = 4;                              // width 0 (or invalid): not stored
     if (cls < 4) {
-      f = (uint64_t)bk | ((uint64_t)(cls < 3) << 16) | (1ull << (32 + 8 * cls));
+      f = (uint64_t)bk | ((uint64_t)(cls < 3) << 16);
     }
   }
   uint64_t tf;
   const uint64_t ef = block_excl_scan<1024>(f, &tf, sh);
   if (tid < D) {
-    // place: channels of smaller width classes first, then rank inside the class; channels
-    // of width 0 (or an invalid width) follow all the others
-    int pos = 0, before = 0, nnz = 0;
-    for (int k2 = 0; k2 < 4; ++k2) {
-      const int tk = (int)((tf >> (32 + 8 * k2)) & 0xFF);
-      if (k2 < cls) pos += tk;
-      before += (int)((ef >> (32 + 8 * k2)) & 0xFF);
-      nnz += tk;
-    }
-    pos = cls < 4 ? pos + (int)((ef >> (32 + 8 * cls)) & 0xFF) : nnz + (tid - before);
-    int32_t* e = kch + ((int64_t)g * D + pos) * 4;
-    e[0] = tid;
-    e[1] = (int32_t)(ef & 0xFFFF);
-    e[2] = (int32_t)((ef >> 16) & 0xFFFF);
-    e[3] = cls < 4 ? (int32_t)bk : 0;
+    *reinterpret_cast<int4*>(kchc + ((int64_t)g * D + tid) * 4) =
+        make_int4((int32_t)(ef & 0xFFFF), (int32_t)((ef >> 16) & 0xFFFF), cls < 4 ? (int32_t)bk : 0, 0);
   }
   if (bad) bad_s = 1;
   __syncthreads();
@@ -273,119 +259,188 @@ pack_index(const uint8_t* __restrict__ bits_v, int64_t N, int nchunk,
   }
 }
 
-// Quantise one group of 32 bf16 values, held as 16 packed pairs (element 2i in the low half of
-// raw[i]), at width B and store its B words and its (scale, zero) pair.  FULL: all 32 valid;
-// otherwise only the first m (>= 1) are, and the rest code 0.
-//  * min / max with v_min3 / v_max3 (values are finite; fminf would first quiet NaNs);
-//  * v = (x - z) * (1 / s) in fp32: 0 <= v < maxc + 2^-16, so rint(v) needs no clamp; where v is
-//    within 1e-4 of a half-integer the code is recomputed with the defining fp64 division.
+// Group quantiser.  min / max use v_min3 / v_max3 (values are finite; fminf would first quiet
+// NaNs).  quantize_rt quantises the NE values a lane holds of one group (NE = 32: the whole
+// group; NE = 16: one half, the other half on lane ^ 32, XCH = true) at width b in {2, 4, 8},
+// stores the lane's NE*b/32 code words and, if asked, the group's (scale, zero) pair.  Only the
+// first m_own (0..NE) of the lane's values are valid; the rest code 0.  b is a runtime value
+// (the K channels of one wave have mixed widths) and every lane runs the same instructions:
+// codes are first placed one per byte, then the bytes are compacted to b bits.
+//  * v = (x - z) * (1 / s) in fp32: 0 <= v < maxc + 2^-16, so rint(v) needs no clamp;
+//  * a value whose fp32 v lies within 2^(b-21) of a half-integer (over 2.6 times the error
+//    bound 3 * 2^-24 * v for v < 2^b) is decided again with the defining fp64 division,
+//    reading the value back through src.fetch().  The codes equal those of that definition.
+// Src provides elem(e) (value e as float), refresh() (makes the held registers opaque, so
+// that a later pass unpacks them afresh instead of keeping every unpacked value alive) and
+// fetch(e) (value e read back from memory).
 __device__ __forceinline__ float min3_raw(float a, float b, float c) {
   float r;
   asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
 }
-__device__ __forceinline__ float elem_of(const uint32_t (&raw)[16], int e) {
-  return (e & 1) ? __uint_as_float(raw[e >> 1] & 0xFFFF0000u) : __uint_as_float(raw[e >> 1] << 16);
+
+__device__ __forceinline__ uint32_t nibbles_of(uint32_t lo, uint32_t hi) {
+  // 8 byte codes < 16 (4 in lo, 4 in hi) -> 8 nibbles, code k in bits 4k .. 4k+3
+  const uint32_t a = lo | (lo >> 4), c = hi | (hi >> 4);   // bytes 0 and 2 hold code pairs
+  return (a & 0xFFu) | ((a >> 8) & 0xFF00u) | ((c & 0xFFu) << 16) | ((c << 8) & 0xFF000000u);
+}
+__device__ __forceinline__ uint32_t crumbs_of(uint32_t w) {
+  // 4 byte codes < 4 -> one byte, code k in bits 2k .. 2k+1
+  const uint32_t t = w | (w >> 6);                          // bytes 0 and 2 hold code pairs
+  return (t | (t >> 12)) & 0xFFu;
 }
 
-template <int B, bool FULL>
-__device__ __forceinline__ void quantize_store(const uint32_t (&raw)[16], int m, uint32_t* __restrict__ dst,
-                                               float* __restrict__ par) {
-  constexpr float maxc = (float)((1 << B) - 1);
-  const float x0 = elem_of(raw, 0);
-  float mn = x0, mx = x0;
+template <int NE, bool XCH, bool FULL, class Src>
+__device__ __forceinline__ void quantize_rt(Src& src, int m_own, int b, uint32_t* __restrict__ dst,
+                                            float* __restrict__ par, bool write_par) {
+  static_assert(NE == 16 || NE == 32, "NE");
+  float mn, mx;
+  if (FULL) {
+    mn = src.elem(0);
+    mx = mn;
+  } else {
+    mn = m_own > 0 ? src.elem(0) : __builtin_inff();
+    mx = m_own > 0 ? src.elem(0) : -__builtin_inff();
+  }
 #pragma unroll
-  for (int e = 1; e < 31; e += 2) {
-    const float a = (FULL || e < m) ? elem_of(raw, e) : x0;
-    const float b = (FULL || e + 1 < m) ? elem_of(raw, e + 1) : x0;
-    mn = min3_raw(mn, a, b);
-    mx = max3_raw(mx, a, b);
+  for (int e = 1; e < NE - 1; e += 2) {
+    const float a = (FULL || e < m_own) ? src.elem(e) : mn;
+    const float c = (FULL || e + 1 < m_own) ? src.elem(e + 1) : mn;
+    const float a2 = (FULL || e < m_own) ? a : mx;
+    const float c2 = (FULL || e + 1 < m_own) ? c : mx;
+    mn = min3_raw(mn, a, c);
+    mx = max3_raw(mx, a2, c2);
   }
   {
-    const float a = (FULL || 31 < m) ? elem_of(raw, 31) : x0;
+    const float a = (FULL || NE - 1 < m_own) ? src.elem(NE - 1) : mn;
+    const float a2 = (FULL || NE - 1 < m_own) ? a : mx;
     mn = min3_raw(mn, a, a);
-    mx = max3_raw(mx, a, a);
+    mx = max3_raw(mx, a2, a2);
   }
-  const float s = (float)(((double)mx - (double)mn) / (double)((1 << B) - 1));
-  uint32_t w[B];
+  if (XCH) {
+    mn = min3_raw(mn, __shfl_xor(mn, 32), mn);
+    mx = max3_raw(mx, __shfl_xor(mx, 32), mx);
+  }
+  const int maxi = (1 << b) - 1;
+  const float s = (float)(((double)mx - (double)mn) / (double)maxi);
+  const float lim = 0.5f - __uint_as_float((uint32_t)(b - 21 + 127) << 23);   // 1/2 - 2^(b-21)
+  constexpr int NW = NE / 4;                       // byte-code words
+  uint32_t w8[NW];
 #pragma unroll
-  for (int i = 0; i < B; ++i) w[i] = 0u;
+  for (int i = 0; i < NW; ++i) w8[i] = 0u;
   if (s != 0.f) {
+    src.refresh();
     const float rs = 1.0f / s;
-    const bool fast = __builtin_isfinite(rs);
-    const double sd = (double)s;
+    const bool fin = __builtin_isfinite(rs);
+    const float rsf = fin ? rs : 0.f;
+    uint32_t near = fin ? 0u : 0xFFFFFFFFu;        // an infinite 1/s sends every value to fp64
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const float x = elem_of(raw, e);
-      const float v = (x - mn) * rs;
-      float r = rintf(v);
-      if (!fast || fabsf(fabsf(v - r) - 0.5f) < 1e-4f) {
-        // near a rounding boundary: decide with the defining fp64 division
-        const double vd = rint(((double)x - (double)mn) / sd);
-        r = (float)(vd < 0.0 ? 0.0 : (vd > (double)maxc ? (double)maxc : vd));
-      }
-      const uint32_t code = (FULL || e < m) ? (uint32_t)r : 0u;
-      w[(e * B) / 32] |= code << ((e * B) % 32);
+    for (int e = 0; e < NE; ++e) {
+      const float v = (src.elem(e) - mn) * rsf;
+      const float r = rintf(v);
+      if (FULL || e < m_own) near |= (fabsf(v - r) > lim) ? (1u << e) : 0u;
+      const float code = (FULL || e < m_own) ? r : 0.f;
+      w8[e >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(code, e & 3, w8[e >> 2]);
+    }
+    if (!FULL) near &= (m_own >= 32) ? 0xFFFFFFFFu : ((1u << m_own) - 1u);
+    // values near a rounding boundary (rare): decide them with the defining fp64 division
+    const double sd = (double)s;
+    while (near != 0u) {
+      const int e = __builtin_ctz(near);
+      near &= near - 1u;
+      const double vd = rint(((double)src.fetch(e) - (double)mn) / sd);
+      const float code = (float)(vd < 0.0 ? 0.0 : (vd > (double)maxi ? (double)maxi : vd));
+#pragma unroll
+      for (int i = 0; i < NW; ++i)
+        if (i == (e >> 2)) w8[i] = __builtin_amdgcn_cvt_pk_u8_f32(code, e & 3, w8[i]);
     }
   }
+  uint32_t o[NW];
 #pragma unroll
-  for (int i = 0; i < B; ++i) dst[i] = w[i];
-  *reinterpret_cast<float2*>(par) = make_float2(s, mn);
-}
-
-template <int B>
-__device__ __forceinline__ void quantize_store_m(const uint32_t (&raw)[16], int m, uint32_t* __restrict__ dst,
-                                                 float* __restrict__ par) {
-  if (m == 32) quantize_store<B, true>(raw, 32, dst, par);
-  else quantize_store<B, false>(raw, m, dst, par);
-}
-
-// K: block (group j of 32 retained tokens, head g) with D threads; thread i takes the i-th
-// channel of nonzero width in width order, so a wave's lanes mostly share one width.
-template <int D>
-__device__ __forceinline__ void pack_k_group(const uint16_t* __restrict__ k, int64_t N, int g, int64_t j,
-                                             const int64_t* __restrict__ hp, const int32_t* __restrict__ kch,
-                                             const int32_t* __restrict__ k_keep,
-                                             uint32_t* __restrict__ k_words, float* __restrict__ k_par) {
-  const int64_t R = hp[4];
-  if (j * 32 >= R) return;
-  const int m = (int)((R - j * 32) < 32 ? (R - j * 32) : 32);
-  __shared__ uint16_t tile[32][D + 2];
-  __shared__ int32_t tok[32];
-  const int tid = threadIdx.x;
-  if (tid < 32) tok[tid] = tid < m ? k_keep[hp[17] + j * 32 + tid] : 0;
-  __syncthreads();
-  for (int e = tid; e < 32 * (D / 8); e += D) {
-    const int r = e / (D / 8), c8 = e % (D / 8);
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (r < m) val = *reinterpret_cast<const uint4*>(k + ((int64_t)g * N + tok[r]) * D + c8 * 8);
-    uint32_t* tw = reinterpret_cast<uint32_t*>(&tile[r][c8 * 8]);
-    tw[0] = val.x;
-    tw[1] = val.y;
-    tw[2] = val.z;
-    tw[3] = val.w;
+  for (int i = 0; i < NW; ++i) o[i] = w8[i];
+  if (b == 4) {
+#pragma unroll
+    for (int i = 0; i < NW / 2; ++i) o[i] = nibbles_of(w8[2 * i], w8[2 * i + 1]);
+  } else if (b == 2) {
+#pragma unroll
+    for (int i = 0; i < NW / 4; ++i)
+      o[i] = crumbs_of(w8[4 * i]) | (crumbs_of(w8[4 * i + 1]) << 8) | (crumbs_of(w8[4 * i + 2]) << 16) |
+             (crumbs_of(w8[4 * i + 3]) << 24);
   }
-  __syncthreads();
-  const int4 info = *reinterpret_cast<const int4*>(kch + ((int64_t)g * D + tid) * 4);
-  const int c = info.x, b = info.w;
-  if (b == 0) return;                                     // width 0: nothing stored
-  uint32_t* dst = k_words + hp[18] + j * hp[20] + info.y;
-  if (b == 16) {
+  const int nw = (NE * b) >> 5;
+#pragma unroll
+  for (int i = 0; i < NW; ++i)
+    if (i < nw) dst[i] = o[i];
+  if (write_par) *reinterpret_cast<float2*>(par) = make_float2(s, mn);
+}
+
+// A lane's 32 values of one group as 16 packed bf16 pairs (element 2i in the low half of
+// w[i]); Fetch reads value e back from memory.
+template <class Fetch>
+struct PairSrc {
+  uint32_t w[16];
+  Fetch fetch_fn;
+  __device__ __forceinline__ float elem(int e) const {
+    return (e & 1) ? __uint_as_float(w[e >> 1] & 0xFFFF0000u) : __uint_as_float(w[e >> 1] << 16);
+  }
+  __device__ __forceinline__ void refresh() {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(w[i]));
+  }
+  __device__ __forceinline__ float fetch(int e) const { return fetch_fn(e); }
+};
+
+// K: one wave per (group j of 32 retained tokens, head g).  Lane l < D/2 holds channels 2l and
+// 2l+1, so each load instruction reads one retained token's whole K row (D*2 bytes, coalesced)
+// with no staging or transposition; the group's token indices are wave-uniform.
+template <int D, bool FULL>
+__device__ __forceinline__ void pack_k_group(const uint16_t* __restrict__ k, int64_t N, int g, int64_t j, int m,
+                                             const int64_t* __restrict__ hp, const int32_t* __restrict__ kchc,
+                                             const int32_t* __restrict__ k_keep, uint32_t* __restrict__ k_words,
+                                             float* __restrict__ k_par) {
+  const int lane = threadIdx.x & 63;
+  const int32_t* tk = k_keep + hp[17] + j * 32;              // wave-uniform
+  const uint16_t* kh = k + (int64_t)g * N * D;
+  const uint32_t* rows = reinterpret_cast<const uint32_t*>(kh) + lane;
+  uint32_t ld[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) ld[i] = (FULL || i < m) ? rows[(int64_t)tk[i] * (D / 2)] : 0u;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int c = 2 * lane + q;
+    const int4 info = *reinterpret_cast<const int4*>(kchc + ((int64_t)g * D + c) * 4);
+    const int b = info.z;
+    uint32_t* dst = k_words + hp[18] + j * hp[20] + info.x;
+    auto fetch = [&](int e) { return __uint_as_float((uint32_t)kh[(int64_t)tk[e] * D + c] << 16); };
+    PairSrc<decltype(fetch)> src{{}, fetch};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const uint32_t lo16 = (2 * i < m) ? tile[2 * i][c] : 0u;
-      const uint32_t hi16 = (2 * i + 1 < m) ? tile[2 * i + 1][c] : 0u;
-      dst[i] = lo16 | (hi16 << 16);
+      const uint32_t lo = ld[2 * i], hi = ld[2 * i + 1];
+      src.w[i] = q ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
     }
-    return;
-  }
-  uint32_t raw[16];
+    if (b == 16) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) raw[i] = (uint32_t)tile[2 * i][c] | ((uint32_t)tile[2 * i + 1][c] << 16);
-  float* par = k_par + 2 * (hp[19] + j * hp[21] + info.z);
-  if (b == 2) quantize_store_m<2>(raw, m, dst, par);
-  else if (b == 4) quantize_store_m<4>(raw, m, dst, par);
-  else quantize_store_m<8>(raw, m, dst, par);
+      for (int i = 0; i < 16; ++i) dst[i] = src.w[i];
+    } else if (b != 0) {
+      float* par = k_par + 2 * (hp[19] + j * hp[21] + info.y);
+      quantize_rt<32, false, FULL>(src, m, b, dst, par, true);
+    }
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256)
+pack_k(const uint16_t* __restrict__ k, int64_t N, const int64_t* __restrict__ header,
+       const int32_t* __restrict__ kchc, const int32_t* __restrict__ k_keep,
+       uint32_t* __restrict__ k_words, float* __restrict__ k_par) {
+  const int g = blockIdx.y;
+  const int64_t* hp = header + KVC_HDR_GLOBAL + g * KVC_HDR_PER_HEAD;
+  const int64_t j = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t R = hp[4];
+  if (j * 32 >= R || (threadIdx.x & 63) >= D / 2) return;
+  const int m = (int)((R - j * 32) < 32 ? (R - j * 32) : 32);
+  if (m == 32) pack_k_group<D, true>(k, N, g, j, 32, hp, kchc, k_keep, k_words, k_par);
+  else pack_k_group<D, false>(k, N, g, j, m, hp, kchc, k_keep, k_words, k_par);
 }
 
 // V: block (slab x of 32 tokens of one width zone, head g) with D threads = 32 tokens x
@@ -404,41 +459,30 @@ __device__ __forceinline__ void pack_v_slab(const uint16_t* __restrict__ v, int6
   }
   if (z == 4) return;
   const int tid = threadIdx.x;
-  const int e = tid / GPR, grp = tid % GPR;
-  const int64_t pos = slab * 32 + e;
+  const int row = tid / GPR, grp = tid % GPR;
+  const int64_t pos = slab * 32 + row;
   if (pos >= hp[z]) return;
   const int32_t t = v_idx[hp[5 + z] + pos];
-  const uint16_t* src = v + ((int64_t)g * N + t) * D + grp * 32;
-  uint32_t raw[16];
+  const uint16_t* vrow = v + ((int64_t)g * N + t) * D + grp * 32;
+  auto fetch = [=](int e) { return __uint_as_float((uint32_t)vrow[e] << 16); };
+  PairSrc<decltype(fetch)> src{{}, fetch};
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
-    const uint4 wv = *reinterpret_cast<const uint4*>(src + q4 * 8);
-    raw[4 * q4 + 0] = wv.x;
-    raw[4 * q4 + 1] = wv.y;
-    raw[4 * q4 + 2] = wv.z;
-    raw[4 * q4 + 3] = wv.w;
+    const uint4 wv = *reinterpret_cast<const uint4*>(vrow + q4 * 8);
+    src.w[4 * q4 + 0] = wv.x;
+    src.w[4 * q4 + 1] = wv.y;
+    src.w[4 * q4 + 2] = wv.z;
+    src.w[4 * q4 + 3] = wv.w;
   }
   const int b = 2 << z;
   uint32_t* dst = v_words + hp[9 + z] + (pos * GPR + grp) * b;
   if (z == 3) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) dst[i] = raw[i];
+    for (int i = 0; i < 16; ++i) dst[i] = src.w[i];
     return;
   }
   float* par = v_par + 2 * (hp[13 + z] + pos * GPR + grp);
-  if (z == 0) quantize_store<2, true>(raw, 32, dst, par);
-  else if (z == 1) quantize_store<4, true>(raw, 32, dst, par);
-  else quantize_store<8, true>(raw, 32, dst, par);
-}
-
-template <int D>
-__global__ void __launch_bounds__(D)
-pack_k(const uint16_t* __restrict__ k, int64_t N, const int64_t* __restrict__ header,
-       const int32_t* __restrict__ kch, const int32_t* __restrict__ k_keep,
-       uint32_t* __restrict__ k_words, float* __restrict__ k_par) {
-  const int g = blockIdx.y;
-  const int64_t* hp = header + KVC_HDR_GLOBAL + g * KVC_HDR_PER_HEAD;
-  pack_k_group<D>(k, N, g, blockIdx.x, hp, kch, k_keep, k_words, k_par);
+  quantize_rt<32, false, true>(src, 32, b, dst, par, true);
 }
 
 template <int D>
@@ -458,7 +502,7 @@ PackWs carve(const Layer& L, char* ws, size_t* total) {
   size_t ob = p.take(sizeof(int64_t) * L.hkv * nchunk * 4);
   size_t orb = p.take(sizeof(int64_t) * L.hkv * nchunk);
   size_t oh = p.take(sizeof(int64_t) * L.hkv * 8);
-  size_t ok = p.take(sizeof(int32_t) * L.hkv * L.d * 4);
+  size_t okc = p.take(sizeof(int32_t) * L.hkv * L.d * 4);
   if (total) *total = p.off;
   PackWs w{};
   if (ws) {
@@ -468,7 +512,7 @@ PackWs carve(const Layer& L, char* ws, size_t* total) {
     w.base = reinterpret_cast<int64_t*>(ws + ob);
     w.rbase = reinterpret_cast<int64_t*>(ws + orb);
     w.htot = reinterpret_cast<int64_t*>(ws + oh);
-    w.kch = reinterpret_cast<int32_t*>(ws + ok);
+    w.kchc = reinterpret_cast<int32_t*>(ws + okc);
   }
   return w;
 }
@@ -505,20 +549,20 @@ hipError_t launch_pack(const Layer& L, const uint16_t* k, const uint16_t* v,
   pack_count<<<gc, 256, 0, s>>>(bits_v, L.n, nchunk, w.cnt, w.cbad);
   if (L.d == 128)
     pack_layout<128><<<(unsigned)L.hkv, 1024, 0, s>>>(w.cnt, w.cbad, bits_k, L.n, nchunk, w.base,
-                                                      w.rbase, w.htot, w.kch, out.k_width);
+                                                      w.rbase, w.htot, w.kchc, out.k_width);
   else
     pack_layout<64><<<(unsigned)L.hkv, 1024, 0, s>>>(w.cnt, w.cbad, bits_k, L.n, nchunk, w.base,
-                                                     w.rbase, w.htot, w.kch, out.k_width);
+                                                     w.rbase, w.htot, w.kchc, out.k_width);
   pack_header<<<1, 256, 0, s>>>(w.htot, L.hkv, L.d, L.n, out.header, w.status);
   pack_index<<<gc, 256, 0, s>>>(bits_v, L.n, nchunk, w.base, w.rbase, out.header, out.v_idx,
                                 out.k_keep, out.k_vloc);
-  dim3 gk((unsigned)((L.n + 31) / 32), (unsigned)L.hkv);
   dim3 gv((unsigned)((L.n + 31) / 32 + 4), (unsigned)L.hkv);
+  dim3 gk2((unsigned)(((L.n + 31) / 32 + 3) / 4), (unsigned)L.hkv);
   if (L.d == 128) {
-    pack_k<128><<<gk, 128, 0, s>>>(k, L.n, out.header, w.kch, out.k_keep, out.k_words, out.k_par);
+    pack_k<128><<<gk2, 256, 0, s>>>(k, L.n, out.header, w.kchc, out.k_keep, out.k_words, out.k_par);
     pack_v<128><<<gv, 128, 0, s>>>(v, L.n, out.header, out.v_idx, out.v_words, out.v_par);
   } else {
-    pack_k<64><<<gk, 64, 0, s>>>(k, L.n, out.header, w.kch, out.k_keep, out.k_words, out.k_par);
+    pack_k<64><<<gk2, 256, 0, s>>>(k, L.n, out.header, w.kchc, out.k_keep, out.k_words, out.k_par);
     pack_v<64><<<gv, 64, 0, s>>>(v, L.n, out.header, out.v_idx, out.v_words, out.v_par);
   }
   return hipGetLastError();
