@@ -4,10 +4,9 @@
 //
 // Kernels, all on one stream (kernel boundaries order every step):
 //   pack_count   per (1024-token chunk, head): tokens per width zone; width validation
-//   pack_layout  per head: chunk bases (block scan), K-channel word/param offsets, per-head
-//                totals
-//   pack_header  one block: head offsets (scans over heads), the header, the status word
-//   pack_index   per chunk: ordered ranks -> v_idx, k_keep, k_vloc
+//   pack_place   per (chunk, head): head totals and offsets (the header, the status word, the
+//                K-channel table), the chunk's zone bases, ordered ranks -> v_idx, k_keep,
+//                k_vloc
 //   pack_k       one wave per (group of 32 retained tokens, head) quantises every K channel
 //   pack_v       one block per 32 tokens of one width zone quantises their V groups
 // Codes follow the definition z = min, s = float32(float64(max - min) / (2^b - 1)),
@@ -29,9 +28,6 @@ struct PackWs {
   int32_t* status;     // word 0 of the workspace
   int32_t* cnt;        // [Hkv][nchunk][4]  tokens per zone in each chunk
   int32_t* cbad;       // [Hkv][nchunk]     invalid token widths seen in the chunk
-  int64_t* base;       // [Hkv][nchunk][4]  zone position of each chunk's first token
-  int64_t* rbase;      // [Hkv][nchunk]     retained rank of each chunk's first token
-  int64_t* htot;       // [Hkv][8]          tokens per zone (4), R, K words per group, K params per group, bad
   int32_t* kchc;       // [Hkv][D][4]       per K channel: {word offset, param slot, width, 0}
 };
 
@@ -43,13 +39,9 @@ __global__ void __launch_bounds__(256)
 pack_count(const uint8_t* __restrict__ bits_v, int64_t N, int nchunk, int32_t* __restrict__ cnt,
            int32_t* __restrict__ cbad) {
   const int ch = blockIdx.x, g = blockIdx.y;
-  __shared__ int32_t c4[4];
-  __shared__ int32_t bad_s;
-  if (threadIdx.x < 4) c4[threadIdx.x] = 0;
-  if (threadIdx.x == 0) bad_s = 0;
-  __syncthreads();
-  int my[4] = {0, 0, 0, 0};
-  bool bad = false;
+  __shared__ uint64_t part[4];
+  __shared__ int32_t badw[4];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int64_t t0 = (int64_t)ch * kChunk + threadIdx.x * 4;
   uint32_t b4 = 0;
   if (t0 + 3 < N && (reinterpret_cast<uintptr_t>(bits_v + (int64_t)g * N + t0) & 3) == 0) {
@@ -59,121 +51,109 @@ pack_count(const uint8_t* __restrict__ bits_v, int64_t N, int nchunk, int32_t* _
     for (int j = 0; j < 4; ++j)
       if (t0 + j < N) b4 |= (uint32_t)bits_v[(int64_t)g * N + t0 + j] << (8 * j);
   }
+  // the thread's four zone counts as 16-bit fields (a block counts at most 1024 tokens)
+  uint64_t mine = 0;
+  bool bad = false;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     if (t0 + j < N) {
       const uint32_t b = (b4 >> (8 * j)) & 0xFFu;
       bad |= !valid_width(b);
       const int z = zone_of(b);
-      if (z >= 0) my[z]++;
+      if (z >= 0) mine += 1ull << (16 * z);
     }
   }
-  if (bad) bad_s = 1;                  // benign race: every writer stores 1
 #pragma unroll
-  for (int z = 0; z < 4; ++z)
-    if (my[z]) atomicAdd(&c4[z], my[z]);     // integer: order-independent
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)mine, o, 64), hi = __shfl_xor((uint32_t)(mine >> 32), o, 64);
+    mine += ((uint64_t)hi << 32) | lo;
+  }
+  const bool wbad = __builtin_amdgcn_ballot_w64(bad) != 0;
+  if (lane == 0) {
+    part[wid] = mine;
+    badw[wid] = wbad ? 1 : 0;
+  }
   __syncthreads();
-  if (threadIdx.x < 4) cnt[((int64_t)g * nchunk + ch) * 4 + threadIdx.x] = c4[threadIdx.x];
-  if (threadIdx.x == 0) cbad[(int64_t)g * nchunk + ch] = bad_s;
+  if (threadIdx.x < 4) {
+    const uint64_t s = part[0] + part[1] + part[2] + part[3];
+    cnt[((int64_t)g * nchunk + ch) * 4 + threadIdx.x] = (int32_t)((s >> (16 * threadIdx.x)) & 0xFFFF);
+  }
+  if (threadIdx.x == 0) cbad[(int64_t)g * nchunk + ch] = badw[0] | badw[1] | badw[2] | badw[3];
 }
 
-// One block of 1024 threads per KV head.
-//  1. chunk bases: the four zone counts travel as two uint64 words with 32-bit fields (a field
-//     never exceeds N < 2^29), so one block scan per word gives every zone's prefix;
-//  2. K channels: one uint64 per channel packs {words (16 bits), params (16 bits)}; one scan
-//     gives each channel's word offset and parameter slot inside a group.
+// Placement, one block per (1024-token chunk ch, head g).  Every block first rebuilds, in LDS,
+// the zone totals of every head (from the chunk counts) and the K words / parameters per group
+// of every head (from bits_k); scans over heads then give the head offsets of the header.  The
+// chunk's own zone bases are the sums over the head's earlier chunks.  Finally the chunk's
+// tokens get their ordered ranks: the four zone counters of a thread's 4 tokens are packed into
+// one 64-bit word (16 bits per zone) and scanned.  Block (0, g) also writes head g's header
+// entries, its channel table and k_width; block (0, 0) the global header and the status word.
 template <int D>
-__global__ void __launch_bounds__(1024)
-pack_layout(const int32_t* __restrict__ cnt, const int32_t* __restrict__ cbad,
-            const uint8_t* __restrict__ bits_k, int64_t N, int nchunk, int64_t* __restrict__ base,
-            int64_t* __restrict__ rbase, int64_t* __restrict__ htot, int32_t* __restrict__ kchc,
-            uint8_t* __restrict__ k_width) {
-  __shared__ uint64_t sh[16];
-  __shared__ int32_t bad_s;
-  const int g = blockIdx.x, tid = threadIdx.x;
-  if (tid == 0) bad_s = 0;
-  uint64_t carry01 = 0, carry23 = 0;
-  bool bad = false;
-  for (int c0 = 0; c0 < nchunk; c0 += 1024) {
-    const int ch = c0 + tid;
-    int4 c = make_int4(0, 0, 0, 0);
-    if (ch < nchunk) {
-      c = *reinterpret_cast<const int4*>(cnt + ((int64_t)g * nchunk + ch) * 4);
-      bad |= cbad[(int64_t)g * nchunk + ch] != 0;
-    }
-    const uint64_t a = (uint32_t)c.x | ((uint64_t)(uint32_t)c.y << 32);
-    const uint64_t b = (uint32_t)c.z | ((uint64_t)(uint32_t)c.w << 32);
-    uint64_t ta, tb;
-    const uint64_t ea = block_excl_scan<1024>(a, &ta, sh) + carry01;
-    const uint64_t eb = block_excl_scan<1024>(b, &tb, sh) + carry23;
-    if (ch < nchunk) {
-      const int64_t z0 = (int64_t)(ea & 0xFFFFFFFFu), z1 = (int64_t)(ea >> 32);
-      const int64_t z2 = (int64_t)(eb & 0xFFFFFFFFu), z3 = (int64_t)(eb >> 32);
-      int64_t* bp = base + ((int64_t)g * nchunk + ch) * 4;
-      bp[0] = z0;
-      bp[1] = z1;
-      bp[2] = z2;
-      bp[3] = z3;
-      rbase[(int64_t)g * nchunk + ch] = z0 + z1 + z2 + z3;
-    }
-    carry01 += ta;
-    carry23 += tb;
-  }
-  // K channels
-  uint32_t bk = 0;
-  int cls = 4;
-  uint64_t f = 0;
-  if (tid < D) {
-    bk = bits_k[(int64_t)g * D + tid];
-    k_width[(int64_t)g * D + tid] = (uint8_t)bk;
-    bad |= !valid_width(bk);
-    cls = zone_of(bk);
-    if (cls < 0) cls = 4;                              // width 0 (or invalid): not stored
-    if (cls < 4) {
-      f = (uint64_t)bk | ((uint64_t)(cls < 3) << 16);
-    }
-  }
-  uint64_t tf;
-  const uint64_t ef = block_excl_scan<1024>(f, &tf, sh);
-  if (tid < D) {
-    *reinterpret_cast<int4*>(kchc + ((int64_t)g * D + tid) * 4) =
-        make_int4((int32_t)(ef & 0xFFFF), (int32_t)((ef >> 16) & 0xFFFF), cls < 4 ? (int32_t)bk : 0, 0);
-  }
-  if (bad) bad_s = 1;
-  __syncthreads();
-  if (tid == 0) {
-    int64_t* h = htot + (int64_t)g * 8;
-    h[0] = (int64_t)(carry01 & 0xFFFFFFFFu);
-    h[1] = (int64_t)(carry01 >> 32);
-    h[2] = (int64_t)(carry23 & 0xFFFFFFFFu);
-    h[3] = (int64_t)(carry23 >> 32);
-    h[4] = h[0] + h[1] + h[2] + h[3];
-    h[5] = (int64_t)(tf & 0xFFFF);                        // K words per 32-token group
-    h[6] = (int64_t)((tf >> 16) & 0xFFFF);                // quantised K channels
-    h[7] = bad_s;
-  }
-}
-
-// One block of 256 threads: thread g lays out head g (heads in order, zones in order inside a
-// head), by exclusive scans over heads of each head's sizes.
 __global__ void __launch_bounds__(256)
-pack_header(const int64_t* __restrict__ htot, int Hkv, int d, int64_t N,
-            int64_t* __restrict__ header, int32_t* __restrict__ status) {
+pack_place(const uint8_t* __restrict__ bits_v, const uint8_t* __restrict__ bits_k, int64_t N, int Hkv,
+           int nchunk, const int32_t* __restrict__ cnt, const int32_t* __restrict__ cbad,
+           int64_t* __restrict__ header, int32_t* __restrict__ status, int32_t* __restrict__ kchc,
+           uint8_t* __restrict__ k_width, int32_t* __restrict__ v_idx, int32_t* __restrict__ k_keep,
+           int32_t* __restrict__ k_vloc) {
+  __shared__ int32_t tot[256][4];
+  __shared__ int32_t kw_s[256], kq_s[256];
+  __shared__ int64_t hv[24];
   __shared__ uint64_t sh[4];
   __shared__ int32_t bad_s;
-  const int g = threadIdx.x;
-  const int gpr = d / 32;
-  if (g == 0) bad_s = 0;
+  const int ch = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
+  const int gpr = D / 32;
+  if (tid == 0) bad_s = 0;
   __syncthreads();
+  // per-head totals, one wave per head: lanes stride over the head's chunks and channels, then
+  // a butterfly sum (integer: order-independent)
+  bool bad = false;
+  for (int h = wid; h < Hkv; h += 4) {
+    uint64_t a = 0, b = 0;
+    uint32_t kwv = 0, kqv = 0;
+    for (int c2 = lane; c2 < nchunk; c2 += 64) {
+      const int4 c = *reinterpret_cast<const int4*>(cnt + ((int64_t)h * nchunk + c2) * 4);
+      a += (uint32_t)c.x | ((uint64_t)(uint32_t)c.y << 32);
+      b += (uint32_t)c.z | ((uint64_t)(uint32_t)c.w << 32);
+      bad |= cbad[(int64_t)h * nchunk + c2] != 0;
+    }
+    for (int c = lane; c < D; c += 64) {
+      const uint32_t bk = bits_k[(int64_t)h * D + c];
+      bad |= !valid_width(bk);
+      if (zone_of(bk) >= 0) {
+        kwv += bk;
+        kqv += bk != 16 ? 1u : 0u;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const uint32_t a0 = __shfl_xor((uint32_t)a, o, 64), a1 = __shfl_xor((uint32_t)(a >> 32), o, 64);
+      const uint32_t b0 = __shfl_xor((uint32_t)b, o, 64), b1 = __shfl_xor((uint32_t)(b >> 32), o, 64);
+      a += ((uint64_t)a1 << 32) | a0;
+      b += ((uint64_t)b1 << 32) | b0;
+      kwv += __shfl_xor(kwv, o, 64);
+      kqv += __shfl_xor(kqv, o, 64);
+    }
+    if (lane == 0) {
+      tot[h][0] = (int32_t)(a & 0xFFFFFFFFu);
+      tot[h][1] = (int32_t)(a >> 32);
+      tot[h][2] = (int32_t)(b & 0xFFFFFFFFu);
+      tot[h][3] = (int32_t)(b >> 32);
+      kw_s[h] = (int32_t)kwv;
+      kq_s[h] = (int32_t)kqv;
+    }
+  }
+  if (bad) bad_s = 1;                               // benign race: every writer stores 1
+  __syncthreads();
+
+  // head offsets: thread h handles head h (Hkv <= 256)
   int64_t nv[4] = {0, 0, 0, 0}, R = 0, wk = 0, qk = 0, ng = 0;
-  if (g < Hkv) {
-    const int64_t* h = htot + (int64_t)g * 8;
-    for (int z = 0; z < 4; ++z) nv[z] = h[z];
-    R = h[4];
-    wk = h[5];
-    qk = h[6];
+  if (tid < Hkv) {
+    for (int z = 0; z < 4; ++z) nv[z] = tot[tid][z];
+    R = nv[0] + nv[1] + nv[2] + nv[3];
+    wk = kw_s[tid];
+    qk = kq_s[tid];
     ng = (R + 31) / 32;
-    if (h[7]) bad_s = 1;
   }
   const int64_t vw[4] = {nv[0] * gpr * 2, nv[1] * gpr * 4, nv[2] * gpr * 8, nv[3] * gpr * 16};
   const int64_t vp[3] = {nv[0] * gpr, nv[1] * gpr, nv[2] * gpr};
@@ -183,30 +163,29 @@ pack_header(const int64_t* __restrict__ htot, int Hkv, int d, int64_t N,
   const int64_t o_vp = (int64_t)block_excl_scan<256>((uint64_t)(vp[0] + vp[1] + vp[2]), &t_vp, sh);
   const int64_t o_kw = (int64_t)block_excl_scan<256>((uint64_t)(ng * wk), &t_kw, sh);
   const int64_t o_kp = (int64_t)block_excl_scan<256>((uint64_t)(ng * qk), &t_kp, sh);
-  if (g < Hkv) {
-    int64_t* hp = header + KVC_HDR_GLOBAL + g * KVC_HDR_PER_HEAD;
+  if (tid == g) {
     int64_t a = o_vi, b = o_vw, c = o_vp;
     for (int z = 0; z < 4; ++z) {
-      hp[z] = nv[z];
-      hp[5 + z] = a;
-      hp[9 + z] = b;
-      hp[13 + z] = c;
+      hv[z] = nv[z];
+      hv[5 + z] = a;
+      hv[9 + z] = b;
+      hv[13 + z] = c;
       a += nv[z];
       b += vw[z];
       c += (z < 3) ? vp[z] : 0;
     }
-    hp[4] = R;
-    hp[17] = o_vi;          // k_keep lists the same R tokens per head, in the same head order
-    hp[18] = o_kw;
-    hp[19] = o_kp;
-    hp[20] = wk;
-    hp[21] = qk;
-    hp[22] = ng;
-    hp[23] = 0;
+    hv[4] = R;
+    hv[17] = o_vi;          // k_keep lists the same R tokens per head, in the same head order
+    hv[18] = o_kw;
+    hv[19] = o_kp;
+    hv[20] = wk;
+    hv[21] = qk;
+    hv[22] = ng;
+    hv[23] = 0;
   }
-  if (g == 0) {
+  if (ch == 0 && g == 0 && tid == 0) {
     header[0] = Hkv;
-    header[1] = d;
+    header[1] = D;
     header[2] = N;
     header[3] = 32;
     header[4] = (int64_t)t_vi;
@@ -216,34 +195,53 @@ pack_header(const int64_t* __restrict__ htot, int Hkv, int d, int64_t N,
     header[8] = (int64_t)t_kw;
     header[9] = (int64_t)t_kp;
     for (int i = 10; i < KVC_HDR_GLOBAL; ++i) header[i] = 0;
+    *status = bad_s ? KVC_DEV_BAD_WIDTH : 0;
   }
   __syncthreads();
-  if (g == 0) *status = bad_s ? KVC_DEV_BAD_WIDTH : 0;
-}
+  if (ch == 0) {
+    if (tid < KVC_HDR_PER_HEAD) header[KVC_HDR_GLOBAL + g * KVC_HDR_PER_HEAD + tid] = hv[tid];
+    // head g's K channels: word offset and parameter slot inside a group (scan in channel order)
+    uint32_t bk = 0;
+    uint64_t f = 0;
+    if (tid < D) {
+      bk = bits_k[(int64_t)g * D + tid];
+      k_width[(int64_t)g * D + tid] = (uint8_t)bk;
+      const int cls = zone_of(bk);
+      if (cls >= 0) f = (uint64_t)bk | ((uint64_t)(cls < 3) << 16);
+    }
+    uint64_t tf;
+    const uint64_t ef = block_excl_scan<256>(f, &tf, sh);
+    if (tid < D)
+      *reinterpret_cast<int4*>(kchc + ((int64_t)g * D + tid) * 4) =
+          make_int4((int32_t)(ef & 0xFFFF), (int32_t)((ef >> 16) & 0xFFFF), f ? (int32_t)bk : 0, 0);
+  }
 
-// Ordered ranks inside each chunk: the four zone counters of a thread's 4 tokens are packed
-// into one 64-bit word (16 bits per zone; a chunk holds at most 1024 tokens) and scanned.
-__global__ void __launch_bounds__(256)
-pack_index(const uint8_t* __restrict__ bits_v, int64_t N, int nchunk,
-           const int64_t* __restrict__ base, const int64_t* __restrict__ rbase,
-           const int64_t* __restrict__ header, int32_t* __restrict__ v_idx,
-           int32_t* __restrict__ k_keep, int32_t* __restrict__ k_vloc) {
-  const int ch = blockIdx.x, g = blockIdx.y;
-  const int64_t t0 = (int64_t)ch * kChunk + threadIdx.x * 4;
+  // zone bases of this chunk: sums over the head's earlier chunks (32-bit fields)
+  uint64_t pa = 0, pb = 0;
+  for (int c2 = tid; c2 < ch; c2 += 256) {
+    const int4 c = *reinterpret_cast<const int4*>(cnt + ((int64_t)g * nchunk + c2) * 4);
+    pa += (uint32_t)c.x | ((uint64_t)(uint32_t)c.y << 32);
+    pb += (uint32_t)c.z | ((uint64_t)(uint32_t)c.w << 32);
+  }
+  uint64_t sa, sb;
+  block_excl_scan<256>(pa, &sa, sh);
+  block_excl_scan<256>(pb, &sb, sh);
+  const int64_t bz[4] = {(int64_t)(sa & 0xFFFFFFFFu), (int64_t)(sa >> 32), (int64_t)(sb & 0xFFFFFFFFu),
+                         (int64_t)(sb >> 32)};
+
+  // ordered ranks of the chunk's tokens
+  const int64_t t0 = (int64_t)ch * kChunk + tid * 4;
   int z4[4];
   uint64_t mine = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    int64_t t = t0 + j;
+    const int64_t t = t0 + j;
     z4[j] = (t < N) ? zone_of(bits_v[(int64_t)g * N + t]) : -1;
     if (z4[j] >= 0) mine += 1ull << (16 * z4[j]);
   }
-  __shared__ uint64_t sh[4];
   uint64_t total;
   uint64_t run = block_excl_scan<256>(mine, &total, sh);
-  const int64_t* hp = header + KVC_HDR_GLOBAL + g * KVC_HDR_PER_HEAD;
-  const int64_t* bz = base + ((int64_t)g * nchunk + ch) * 4;
-  const int64_t kbase = hp[17] + rbase[(int64_t)g * nchunk + ch];
+  const int64_t kbase = hv[17] + bz[0] + bz[1] + bz[2] + bz[3];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int z = z4[j];
@@ -252,7 +250,7 @@ pack_index(const uint8_t* __restrict__ bits_v, int64_t N, int nchunk,
     const int64_t rall = (int64_t)((run & 0xFFFF) + ((run >> 16) & 0xFFFF) + ((run >> 32) & 0xFFFF) + ((run >> 48) & 0xFFFF));
     const int64_t pos = bz[z] + rz;
     const int32_t t = (int32_t)(t0 + j);
-    v_idx[hp[5 + z] + pos] = t;
+    v_idx[hv[5 + z] + pos] = t;
     k_keep[kbase + rall] = t;
     k_vloc[kbase + rall] = (int32_t)(((int64_t)z << 29) | pos);
     run += 1ull << (16 * z);
@@ -499,9 +497,6 @@ PackWs carve(const Layer& L, char* ws, size_t* total) {
   WsPlan p;
   size_t oc = p.take(sizeof(int32_t) * L.hkv * nchunk * 4);
   size_t obad = p.take(sizeof(int32_t) * L.hkv * nchunk);
-  size_t ob = p.take(sizeof(int64_t) * L.hkv * nchunk * 4);
-  size_t orb = p.take(sizeof(int64_t) * L.hkv * nchunk);
-  size_t oh = p.take(sizeof(int64_t) * L.hkv * 8);
   size_t okc = p.take(sizeof(int32_t) * L.hkv * L.d * 4);
   if (total) *total = p.off;
   PackWs w{};
@@ -509,9 +504,6 @@ PackWs carve(const Layer& L, char* ws, size_t* total) {
     w.status = reinterpret_cast<int32_t*>(ws);
     w.cnt = reinterpret_cast<int32_t*>(ws + oc);
     w.cbad = reinterpret_cast<int32_t*>(ws + obad);
-    w.base = reinterpret_cast<int64_t*>(ws + ob);
-    w.rbase = reinterpret_cast<int64_t*>(ws + orb);
-    w.htot = reinterpret_cast<int64_t*>(ws + oh);
     w.kchc = reinterpret_cast<int32_t*>(ws + okc);
   }
   return w;
@@ -548,14 +540,11 @@ hipError_t launch_pack(const Layer& L, const uint16_t* k, const uint16_t* v,
   dim3 gc((unsigned)nchunk, (unsigned)L.hkv);
   pack_count<<<gc, 256, 0, s>>>(bits_v, L.n, nchunk, w.cnt, w.cbad);
   if (L.d == 128)
-    pack_layout<128><<<(unsigned)L.hkv, 1024, 0, s>>>(w.cnt, w.cbad, bits_k, L.n, nchunk, w.base,
-                                                      w.rbase, w.htot, w.kchc, out.k_width);
+    pack_place<128><<<gc, 256, 0, s>>>(bits_v, bits_k, L.n, L.hkv, nchunk, w.cnt, w.cbad, out.header,
+                                       w.status, w.kchc, out.k_width, out.v_idx, out.k_keep, out.k_vloc);
   else
-    pack_layout<64><<<(unsigned)L.hkv, 1024, 0, s>>>(w.cnt, w.cbad, bits_k, L.n, nchunk, w.base,
-                                                     w.rbase, w.htot, w.kchc, out.k_width);
-  pack_header<<<1, 256, 0, s>>>(w.htot, L.hkv, L.d, L.n, out.header, w.status);
-  pack_index<<<gc, 256, 0, s>>>(bits_v, L.n, nchunk, w.base, w.rbase, out.header, out.v_idx,
-                                out.k_keep, out.k_vloc);
+    pack_place<64><<<gc, 256, 0, s>>>(bits_v, bits_k, L.n, L.hkv, nchunk, w.cnt, w.cbad, out.header,
+                                      w.status, w.kchc, out.k_width, out.v_idx, out.k_keep, out.k_vloc);
   dim3 gv((unsigned)((L.n + 31) / 32 + 4), (unsigned)L.hkv);
   dim3 gk2((unsigned)(((L.n + 31) / 32 + 3) / 4), (unsigned)L.hkv);
   if (L.d == 128) {
