@@ -8,7 +8,7 @@ Every function here is the plainest reading of the definition it cites, computed
 float64 from the exact bf16 inputs (bf16 -> float64 widening is exact).  Sources cited:
 
 * "KVSculpt: KV Cache Compression as Distillation" summary page, §2 (loss: output MSE and
-  log-sum-exp matching terms).
+  log-sum-exp matching terms; the closed-form ridge value solve; the pilot budget split).
 * "RDKV - rate-distortion bit allocation for joint eviction and quantization of the KV
   cache" summary page, §2.1 (token weight w_t, channel weight w_c, rate-distortion
   objective), §2.2 (allocation over the widths {0,2,4,8,16} in three stages), §2.3 (packed
@@ -47,6 +47,7 @@ from .allocation import (
 from .quantize import quantize_group, pack_group_words, pack_cache, HDR_GLOBAL, HDR_PER_HEAD
 from .fidelity import (dequantized_head, attend, full_attend, compressed_attend, compressed_attend_append,
                        fidelity_terms, fidelity_terms_per_head)
+from .ridge import ridge_normal_equations, ridge_value_fit
 
 __all__ = [
     "as_f64", "query_positions", "default_scale",
@@ -56,4 +57,5 @@ __all__ = [
     "allocate_v_tokens", "allocate_k_channels", "retained_counts", "topk_keep", "threshold_keep", "pilot_budgets",
     "quantize_group", "pack_group_words", "pack_cache", "HDR_GLOBAL", "HDR_PER_HEAD",
     "dequantized_head", "attend", "full_attend", "compressed_attend", "compressed_attend_append", "fidelity_terms", "fidelity_terms_per_head",
+    "ridge_normal_equations", "ridge_value_fit",
 ]
