@@ -15,6 +15,7 @@
  *   kvc_keep_threshold     KVzap threshold keep plus a recent-token window
  *   kvc_fidelity_terms     per-head output and LSE errors of a compressed attend (KVSculpt loss)
  *   kvc_pilot_budgets      per-head budgets in proportion to sqrt(pilot MSE) (host only)
+ *   kvc_ridge_value_fit    KVSculpt's closed-form ridge fit of compressed values to given keys
  *
  * Sources (summary pages of the papers; section numbers are the pages' own):
  *   "RDKV - rate-distortion bit allocation for joint eviction and quantization of the KV
@@ -23,7 +24,8 @@
  *   "KVzap - fast, adaptive and faithful KV cache pruning": §2.1 KVzip+ score, §2.2 one score
  *    per KV head, §2.3 fixed-budget keep of KVzip.
  *   "KVSculpt: KV Cache Compression as Distillation": §2 loss terms (output error and LSE
- *    error) that the fidelity attend measures, and §2's adaptive per-head budget.
+ *    error) that the fidelity attend measures, §2's closed-form value solve and its adaptive
+ *    per-head budget.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -86,11 +88,12 @@ enum {
   KVC_OP_CHANNEL_WEIGHTS = 2,
   KVC_OP_ALLOCATE_BITS = 3,
   KVC_OP_QUANTIZE_PACK = 4,
-  KVC_OP_COMPRESSED_ATTEND = 5
+  KVC_OP_COMPRESSED_ATTEND = 5,
+  KVC_OP_RIDGE_FIT = 6
 };
 
-/* Bytes of device workspace `op` needs for `desc` (`mode` = score mode or allocation stage,
- * ignored otherwise).  Returns 0 for an invalid descriptor.  A larger workspace is fine. */
+/* Bytes of device workspace `op` needs for `desc` (`mode` = score mode, allocation stage, or
+ * for KVC_OP_RIDGE_FIT the number of compressed pairs n_c; ignored otherwise).  Returns 0 for an invalid descriptor.  A larger workspace is fine. */
 size_t kvc_workspace_size(int32_t op, const kvc_layer_desc* desc, int32_t mode);
 
 /* Pass 1.  lse[h][i] = ln sum_{t visible} exp(scale * q_{h,i} . k_{g(h),t}) (natural log, the
@@ -286,9 +289,30 @@ kvc_status kvc_fidelity_terms(const kvc_layer_desc* desc, const float* y_hat, co
 kvc_status kvc_pilot_budgets(const double* mse, int32_t n, int64_t total, int64_t floor_each,
                              int64_t* budgets);
 
+/* KVSculpt §2 value step (also §4's Select+Fit): the cache is n_c free pairs (K_c, V_c)
+ * followed by the m = n_keys - n_c most recent tokens kept as they are (K_r, V_r).  With the
+ * keys fixed the attention weights A = softmax(scale Q [K_c; K_r]^T) do not depend on the
+ * values, and this call returns the V_c minimising ||A_c V_c + A_r V_r - Y||_F^2 +
+ * lambda ||V_c||_F^2, i.e. the solution of (A_c^T A_c + lambda I) V_c = A_c^T (Y - A_r V_r).
+ * The G query heads of a KV head share its V_c: their rows are stacked into one problem.
+ * desc: n_keys = n_c + m, n_queries = Nq training query rows per query head (the layer's
+ * causal convention applies, bottom-right over the n_keys keys; causal = 0 for queries that
+ * see every key, and then Nq may exceed n_keys).  q: bf16 [H_q][Nq][d]; k: bf16 [H_kv][n_keys][d], compressed keys first;
+ * v_r: bf16 [H_kv][m][d] (NULL allowed when m = 0); y: f32 [H_q][Nq][d] target outputs
+ * (16-byte aligned); v_c: f32 [H_kv][n_c][d] (output).  A is float32 (exp of float32 logits
+ * from bf16 products); the normal equations are summed and solved (blocked Cholesky) in
+ * float64, in a fixed order.  Workspace: kvc_workspace_size(KVC_OP_RIDGE_FIT, desc, n_c).
+ * Errors: n_c outside [1, n_keys], n_c > 8192, lambda < 0 or not finite, G * Nq > 2^22 rows, a
+ * NULL or misaligned pointer.  A normal matrix that is not positive definite (lambda = 0 with
+ * too few independent rows) sets KVC_DEV_NOT_SPD in the status word. */
+kvc_status kvc_ridge_value_fit(const kvc_layer_desc* desc, int64_t n_compressed, const void* q, const void* k,
+                               const void* v_r, const float* y, double lambda, float* v_c, void* ws,
+                               size_t ws_bytes, void* hip_stream);
+
 /* Device status codes (bit set). */
 #define KVC_DEV_BAD_WIDTH 1
 #define KVC_DEV_BAD_CACHE 2
+#define KVC_DEV_NOT_SPD 4      /* kvc_ridge_value_fit: the normal matrix is not positive definite */
 
 /* Copy the device status word at the start of `ws` to *code (synchronises `hip_stream`). */
 kvc_status kvc_get_device_status(const void* ws, int32_t* code, void* hip_stream);

@@ -16,7 +16,7 @@ STATUS_NAMES = {
 }
 
 OP_ROW_LSE, OP_SCORE_TOKENS, OP_CHANNEL_WEIGHTS, OP_ALLOCATE_BITS, OP_QUANTIZE_PACK, \
-    OP_COMPRESSED_ATTEND = range(6)
+    OP_COMPRESSED_ATTEND, OP_RIDGE_FIT = range(7)
 SCORE_SUM, SCORE_MAX = 0, 1
 ALLOC_V_TOKENS, ALLOC_K_CHANNELS, ALLOC_TOPK = 0, 1, 2
 PK_NBUF = 9
@@ -26,12 +26,13 @@ HDR_GLOBAL = 16
 HDR_PER_HEAD = 24
 DEV_BAD_WIDTH = 1
 DEV_BAD_CACHE = 2
+DEV_NOT_SPD = 4
 
 EXPORTED = (
     "kvc_workspace_size", "kvc_row_lse", "kvc_score_tokens", "kvc_channel_weights",
     "kvc_allocate_bits", "kvc_keep_threshold", "kvc_packed_capacity", "kvc_quantize_pack",
     "kvc_compressed_attend", "kvc_compressed_attend_append", "kvc_fidelity_terms", "kvc_pilot_budgets",
-    "kvc_get_device_status", "kvc_status_string", "kvc_last_error", "kvc_version",
+    "kvc_ridge_value_fit", "kvc_get_device_status", "kvc_status_string", "kvc_last_error", "kvc_version",
 )
 
 
@@ -104,11 +105,12 @@ def load():
     lib.kvc_fidelity_terms.argtypes = [D, P, P, P, P, P, P]
     lib.kvc_pilot_budgets.argtypes = [ctypes.POINTER(ctypes.c_double), I32, ctypes.c_int64, ctypes.c_int64,
                                       ctypes.POINTER(ctypes.c_int64)]
+    lib.kvc_ridge_value_fit.argtypes = [D, ctypes.c_int64, P, P, P, P, ctypes.c_double, P, P, S, P]
     lib.kvc_get_device_status.argtypes = [P, ctypes.POINTER(I32), P]
     for name in ("kvc_row_lse", "kvc_score_tokens", "kvc_channel_weights", "kvc_allocate_bits", "kvc_keep_threshold",
                  "kvc_packed_capacity", "kvc_quantize_pack", "kvc_compressed_attend",
                  "kvc_compressed_attend_append", "kvc_fidelity_terms", "kvc_pilot_budgets",
-                 "kvc_get_device_status"):
+                 "kvc_ridge_value_fit", "kvc_get_device_status"):
         getattr(lib, name).restype = I32
     lib.kvc_status_string.argtypes = [I32]
     lib.kvc_status_string.restype = ctypes.c_char_p

@@ -200,6 +200,14 @@ def kvc_pilot_budgets(mse, total, floor_each=0):
     return out
 
 
+def kvc_ridge_value_fit(desc, n_compressed, q, k, v_r, y, lam, v_c, ws, stream=None):
+    """k: bf16 [H_kv][n_c + m][d] (compressed keys first); v_r: bf16 [H_kv][m][d] or None when
+    m = 0; y: float32 [H_q][Nq][d]; v_c: float32 [H_kv][n_c][d] (output)."""
+    wp, wn = _ws(ws)
+    _check(C.load().kvc_ridge_value_fit(ctypes.byref(desc), int(n_compressed), _ptr(q), _ptr(k), _ptr(v_r), _ptr(y),
+                                        float(lam), _ptr(v_c), wp, wn, _stream(stream)))
+
+
 def kvc_get_device_status(ws, stream=None):
     code = ctypes.c_int32(0)
     _check(C.load().kvc_get_device_status(_ptr(ws), ctypes.byref(code), _stream(stream)))

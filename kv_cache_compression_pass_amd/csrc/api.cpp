@@ -39,10 +39,13 @@ kvc_status hip_fail(hipError_t e, const char* where) {
   return fail(KVC_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
 }
 
+constexpr int kMaxRidgePairs = 8192;
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Validate and convert a layer descriptor.
-kvc_status make_layer(const kvc_layer_desc* d, Layer* L) {
+// Validate and convert a layer descriptor.  more_queries: Nq > N is allowed when the layer
+// is not causal (query rows that see every key; used by the ridge fit's training queries).
+kvc_status make_layer(const kvc_layer_desc* d, Layer* L, bool more_queries = false) {
   if (!d) return fail(KVC_ERR_INVALID_ARG, "desc is NULL");
   if (d->reserved != 0) return fail(KVC_ERR_INVALID_ARG, "desc.reserved must be 0");
   if (d->n_q_heads < 1 || d->n_kv_heads < 1)
@@ -58,8 +61,9 @@ kvc_status make_layer(const kvc_layer_desc* d, Layer* L) {
   if (d->causal != 0 && d->causal != 1) return fail(KVC_ERR_INVALID_ARG, "causal must be 0 or 1");
   if (d->n_keys < 1 || d->n_queries < 1)
     return fail(KVC_ERR_INVALID_ARG, "N and Nq must be >= 1 (N=%lld, Nq=%lld)", (long long)d->n_keys, (long long)d->n_queries);
-  if (d->n_queries > d->n_keys)
+  if (d->n_queries > d->n_keys && !(more_queries && d->causal == 0))
     return fail(KVC_ERR_INVALID_ARG, "Nq > N (Nq=%lld, N=%lld)", (long long)d->n_queries, (long long)d->n_keys);
+  if (d->n_queries >= (int64_t(1) << 29)) return fail(KVC_ERR_UNSUPPORTED, "Nq >= 2^29");
   if (d->n_keys >= (int64_t(1) << 29)) return fail(KVC_ERR_UNSUPPORTED, "N >= 2^29");
   if (!std::isfinite(d->softmax_scale) || d->softmax_scale < 0.f)
     return fail(KVC_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
@@ -150,7 +154,7 @@ extern "C" {
 size_t kvc_workspace_size(int32_t op, const kvc_layer_desc* desc, int32_t mode) {
   Layer L;
   std::string saved = g_last_error;
-  if (make_layer(desc, &L) != KVC_OK) return 0;
+  if (make_layer(desc, &L, op == KVC_OP_RIDGE_FIT) != KVC_OK) return 0;
   g_last_error = saved;
   switch (op) {
     case KVC_OP_ROW_LSE: return lse_ws_bytes(L);
@@ -163,6 +167,9 @@ size_t kvc_workspace_size(int32_t op, const kvc_layer_desc* desc, int32_t mode) 
       return alloc_ws_bytes(L, mode);
     case KVC_OP_QUANTIZE_PACK: return pack_ws_bytes(L);
     case KVC_OP_COMPRESSED_ATTEND: return attend_ws_bytes(L);
+    case KVC_OP_RIDGE_FIT:
+      if (mode < 1 || mode > L.n || mode > kMaxRidgePairs) return 0;
+      return ridge_ws_bytes(L, mode);
     default: return 0;
   }
 }
@@ -408,6 +415,28 @@ kvc_status kvc_pilot_budgets(const double* mse, int32_t n, int64_t total, int64_
   }
   for (int32_t i = 0; i < n; ++i) budgets[i] += floor_each;
   return ok();
+}
+
+kvc_status kvc_ridge_value_fit(const kvc_layer_desc* desc, int64_t n_compressed, const void* q, const void* k,
+                               const void* v_r, const float* y, double lambda, float* v_c, void* ws,
+                               size_t ws_bytes, void* hip_stream) {
+  Layer L;
+  KVC_TRY(make_layer(desc, &L, true));
+  if (n_compressed < 1 || n_compressed > L.n)
+    return fail(KVC_ERR_INVALID_ARG, "n_compressed %lld outside [1, n_keys]", (long long)n_compressed);
+  if (n_compressed > kMaxRidgePairs) return fail(KVC_ERR_UNSUPPORTED, "n_compressed > %d", kMaxRidgePairs);
+  if (!std::isfinite(lambda) || lambda < 0.0) return fail(KVC_ERR_INVALID_ARG, "lambda must be finite and >= 0");
+  if ((int64_t)L.G * L.nq > (int64_t(1) << 22)) return fail(KVC_ERR_UNSUPPORTED, "G * Nq > 2^22 rows");
+  KVC_TRY(need_bf16(q, "q"));
+  KVC_TRY(need_bf16(k, "k"));
+  if (n_compressed < L.n) KVC_TRY(need_bf16(v_r, "v_r"));
+  KVC_TRY(need_ptr(y, 16, "y"));
+  KVC_TRY(need_ptr(v_c, 16, "v_c"));
+  KVC_TRY(need_ws(ws, ws_bytes, ridge_ws_bytes(L, n_compressed)));
+  KVC_TRY(need_device());
+  return finish(launch_ridge_fit(L, n_compressed, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v_r, y,
+                                 lambda, v_c, (char*)ws, (hipStream_t)hip_stream),
+                "kvc_ridge_value_fit launch");
 }
 
 kvc_status kvc_get_device_status(const void* ws, int32_t* code, void* hip_stream) {

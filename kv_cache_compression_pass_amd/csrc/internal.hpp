@@ -80,6 +80,12 @@ hipError_t launch_attend(const Layer& L, const uint16_t* q, const kvc_packed_cac
                          float* out, float* lse, char* ws, hipStream_t s, const uint16_t* k_new = nullptr,
                          const uint16_t* v_new = nullptr, int64_t n_new = 0);
 
+// ---- ridge value fit ----------------------------------------------------------------------
+size_t ridge_ws_bytes(const Layer& L, int64_t nc);
+hipError_t launch_ridge_fit(const Layer& L, int64_t nc, const uint16_t* q, const uint16_t* k,
+                            const uint16_t* v_r, const float* y, double lambda, float* v_c, char* ws,
+                            hipStream_t s);
+
 // ---- misc ------------------------------------------------------------------------------
 hipError_t launch_reset_status(char* ws, hipStream_t s);
 

@@ -206,3 +206,26 @@ def test_pilot_budget_argument_errors(lib):
     assert lib.kvc_pilot_budgets(D(1, 2, 3), 3, 1 << 53, 0, out) == 2
     assert lib.kvc_pilot_budgets(D(1, 2, 3), 3, 12, 4, out) == 0          # rest 0
     assert list(out) == [4, 4, 4]
+
+
+def test_ridge_fit_argument_errors(lib):
+    d = _desc(n_keys=128, n_queries=64)
+    big = 1 << 34
+    f = lib.kvc_ridge_value_fit
+    assert f(ctypes.byref(d), 0, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, big, None) == 1      # n_c < 1
+    assert f(ctypes.byref(d), 129, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, big, None) == 1    # n_c > n_keys
+    assert f(ctypes.byref(d), 64, FAKE, FAKE, FAKE, FAKE, -1.0, FAKE, FAKE, big, None) == 1    # lambda < 0
+    assert f(ctypes.byref(d), 64, FAKE, FAKE, FAKE, FAKE, float("nan"), FAKE, FAKE, big, None) == 1
+    assert f(ctypes.byref(d), 64, FAKE, FAKE, None, FAKE, 0.1, FAKE, FAKE, big, None) == 1     # m > 0 needs v_r
+    assert f(ctypes.byref(d), 64, FAKE, FAKE, FAKE, FAKE + 4, 0.1, FAKE, FAKE, big, None) == 1  # y alignment
+    assert f(ctypes.byref(d), 64, FAKE, FAKE, FAKE, FAKE, 0.1, None, FAKE, big, None) == 1     # v_c NULL
+    need = lib.kvc_workspace_size(6, ctypes.byref(d), 64)
+    assert need > 0
+    assert lib.kvc_workspace_size(6, ctypes.byref(d), 0) == 0
+    assert lib.kvc_workspace_size(6, ctypes.byref(d), 129) == 0
+    assert f(ctypes.byref(d), 64, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, need - 1, None) == 3
+    dl = _desc(n_keys=10000, n_queries=64)
+    assert f(ctypes.byref(dl), 8193, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, big, None) == 2
+    # n_c == n_keys: no retained zone, v_r may be NULL; without a GPU the call stops at the device check
+    st = f(ctypes.byref(d), 128, FAKE, FAKE, None, FAKE, 0.0, FAKE, FAKE, big, None)
+    assert st not in (1, 2, 3)

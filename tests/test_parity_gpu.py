@@ -483,3 +483,68 @@ def test_fidelity_terms(case):
     again = torch.empty_like(terms)
     kvc.kvc_fidelity_terms(desc, H.dev_f32(y_hat), H.dev_f32(lse_hat), H.dev_f32(y), H.dev_f32(lse), again)
     assert torch.equal(terms, again)
+
+
+RIDGE_CASES = [
+    # name, H_q, H_kv, d, n_c, m, Nq, causal, lambda
+    ("ridge_d64_small", 4, 2, 64, 40, 24, 100, False, 0.1),
+    ("ridge_d128_ragged_causal", 8, 2, 128, 130, 70, 200, True, 0.01),
+    ("ridge_d128_one_block_no_zone", 2, 1, 128, 64, 0, 64, False, 1.0),
+    ("ridge_d128_five_blocks", 6, 2, 128, 300, 100, 128, False, 0.05),
+    ("ridge_g1_d64_tiny_lambda", 1, 1, 64, 33, 7, 90, False, 1e-4),
+]
+
+
+@pytest.mark.parametrize("case", RIDGE_CASES, ids=[c[0] for c in RIDGE_CASES])
+def test_ridge_value_fit(case):
+    """KVSculpt's value solve against the oracle.  The GPU forms A in float32, so its V_c solves
+    the normal equations up to a relative perturbation of about 1e-5: the residual
+    M V - B of the oracle's own (M, B) must be small relative to |M| |V| + |B| (a bound that
+    does not depend on the conditioning), and V itself must agree within cond(M) times that."""
+    name, hq, hkv, d, nc, m, nq, causal, lam = case
+    print(f"case {name}: H_q={hq} H_kv={hkv} d={d} n_c={nc} m={m} Nq={nq} causal={causal} lambda={lam}", flush=True)
+    seed = zlib.crc32(name.encode()) % 1000
+    x = make_inputs(hq, hkv, d, nc + m, nq, seed=seed)
+    rng = np.random.default_rng(seed)
+    y = rng.standard_normal((hq, nq, d)).astype(np.float32)
+    v_r = np.ascontiguousarray(x["v"][:, nc:])
+    desc = H.desc_of(hq, hkv, d, nc + m, nq, causal)
+    ws = kvc.workspace(kvc.OP_RIDGE_FIT, desc, nc, H.DEV)
+    v_c = torch.empty(hkv, nc, d, dtype=torch.float32, device=H.DEV)
+    kvc.kvc_ridge_value_fit(desc, nc, H.dev_bf16(x["q"]), H.dev_bf16(x["k"]), H.dev_bf16(v_r) if m else None,
+                            H.dev_f32(y), lam, v_c, ws)
+    torch.cuda.synchronize()
+    assert kvc.kvc_get_device_status(ws) == 0
+    got = v_c.cpu().numpy().astype(np.float64)
+    Ms, Bs = oracle.ridge_normal_equations(x["q"], x["k"], v_r, y, nc, lam, causal=causal)
+    want = np.stack([np.linalg.solve(M, B) for M, B in zip(Ms, Bs)])
+    for g in range(hkv):
+        M, B = Ms[g], Bs[g]
+        scale = np.abs(M).sum(axis=1).max() * np.abs(got[g]).max() + np.abs(B).max()
+        res = np.abs(M @ got[g] - B).max()
+        assert res <= 1e-4 * scale, (g, res, scale)
+        cond = np.linalg.cond(M)
+        err = np.abs(got[g] - want[g]).max()
+        assert err <= 1e-4 * cond * np.abs(want[g]).max() + 1e-6, (g, err, cond)
+    # fixed summation order: a second call gives the same bits
+    v2 = torch.empty_like(v_c)
+    kvc.kvc_ridge_value_fit(desc, nc, H.dev_bf16(x["q"]), H.dev_bf16(x["k"]), H.dev_bf16(v_r) if m else None,
+                            H.dev_f32(y), lam, v2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(v_c, v2)
+
+
+def test_ridge_single_key_closed_form():
+    """One compressed key and no retained zone: every weight is 1, so V_c = sum(Y rows) / (R + lambda)."""
+    hq, hkv, d, lam = 4, 1, 128, 3.0
+    print(f"case ridge_single_key: H_q={hq} d={d} lambda={lam}", flush=True)
+    x = make_inputs(hq, hkv, d, 1, 1, seed=3)
+    y = np.random.default_rng(5).standard_normal((hq, 1, d)).astype(np.float32)
+    desc = H.desc_of(hq, hkv, d, 1, 1, False)
+    ws = kvc.workspace(kvc.OP_RIDGE_FIT, desc, 1, H.DEV)
+    v_c = torch.empty(hkv, 1, d, dtype=torch.float32, device=H.DEV)
+    kvc.kvc_ridge_value_fit(desc, 1, H.dev_bf16(x["q"]), H.dev_bf16(x["k"]), None, H.dev_f32(y), lam, v_c, ws)
+    torch.cuda.synchronize()
+    assert kvc.kvc_get_device_status(ws) == 0
+    want = y.astype(np.float64).reshape(-1, d).sum(axis=0) / (hq + lam)
+    np.testing.assert_allclose(v_c.cpu().numpy()[0, 0], want, rtol=1e-5, atol=1e-6)
