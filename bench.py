@@ -130,6 +130,56 @@ def pack_algorithmic_bytes(hdr, k_width, d):
     return {"k": k_read + k_write, "v": v_read + v_write}
 
 
+# KVSculpt's setting (Qwen2.5-1.5B-like layer, 2048-token context): 12 query heads, 2 KV heads,
+# d = 128; the 512 most recent tokens are kept, the older 1536 are fitted by n_c = 768 pairs
+# (ratio 0.5), with 1024 training query rows per query head that see every key.
+RIDGE_SHAPE = {"n_q_heads": 12, "n_kv_heads": 2, "head_dim": 128, "n_compressed": 768, "n_retained": 512,
+               "n_queries": 1024, "lambda": 1e-3}
+
+
+def ridge_algorithmic_flops(hq, hkv, d, nc, m, nq):
+    """Per call: logits 2 R n d, retained product 2 R m d, the normal matrix by symmetry
+    R n_c (n_c + 1), its right side 2 R n_c d, Cholesky n_c^3 / 3, two solves 2 n_c^2 d (per KV
+    head, R = G Nq stacked rows, n = n_c + m keys)."""
+    R = (hq // hkv) * nq
+    n = nc + m
+    per = 2 * R * n * d + 2 * R * m * d + R * nc * (nc + 1) + 2 * R * nc * d + nc ** 3 / 3 + 2 * nc * nc * d
+    return hkv * per
+
+
+def ridge_figure(args, stream, dev):
+    import numpy as np
+    import torch
+    import kv_cache_compression_pass_amd as kvc
+    from workloads import make_inputs
+    sh = RIDGE_SHAPE
+    hq, hkv, d, nc, m, nq = (sh["n_q_heads"], sh["n_kv_heads"], sh["head_dim"], sh["n_compressed"],
+                             sh["n_retained"], sh["n_queries"])
+    x = make_inputs(hq, hkv, d, nc + m, nq, seed=4321)
+    q = kvc.bf16_tensor(x["q"], dev)
+    k = kvc.bf16_tensor(x["k"], dev)
+    v_r = kvc.bf16_tensor(np.ascontiguousarray(x["v"][:, nc:]), dev)
+    y = torch.randn(hq, nq, d, dtype=torch.float32, device=dev, generator=torch.Generator(device=dev).manual_seed(7))
+    desc = kvc.make_desc(hq, hkv, d, nc + m, nq, False)
+    ws = kvc.workspace(kvc.OP_RIDGE_FIT, desc, nc, dev)
+    v_c = torch.empty(hkv, nc, d, dtype=torch.float32, device=dev)
+    fn = lambda: kvc.kvc_ridge_value_fit(desc, nc, q, k, v_r, y, sh["lambda"], v_c, ws, stream=stream)
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    reps = max(min(args.steps, 20), 5)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    fl = ridge_algorithmic_flops(hq, hkv, d, nc, m, nq)
+    return {"shape": dict(sh), "ms": round(ms, 4), "flops": fl, "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+            "status": kvc.kvc_get_device_status(ws)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -356,6 +406,8 @@ def main():
                 "hbm_frac": round(k_bytes / (k_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                 "kept_fraction": round(float(kept_t.sum().item()) / (hkv * N), 4)}
 
+    ridge = ridge_figure(args, stream, dev)
+
     pb = pack_algorithmic_bytes(hdr, bk.cpu().numpy(), d)
     pack_ms = float(np.mean(per_call["quantize_pack"]))
     pack = {"ms": round(pack_ms, 5), "bytes_k": pb["k"], "bytes_v": pb["v"],
@@ -385,6 +437,7 @@ def main():
         "attend": attend,
         "pack": pack,
         "keep_threshold": keep_thr,
+        "ridge_fit": ridge,
         "retained_tokens": int(hdr[7]),
     }
     if cfg.mode == "sum":

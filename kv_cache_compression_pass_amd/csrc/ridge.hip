@@ -10,10 +10,13 @@
 //   ridge_gram     M = P_c^T P_c and B = P_c^T T, fp64 sums of fp32 products (exact), the row
 //                  sum split in kSplit fixed parts
 //   ridge_sum      M += lambda I (identity on the padding), the parts added in fixed order
-//   ridge_chol     blocked Cholesky, one launch per block column kb: every tile (i, j) of the
-//                  trailing matrix computes L_ik = A_ik L_kk^-T itself, subtracts L_ik L_jk^T,
-//                  and the tile (kb+1, kb+1) then factors itself and inverts its L (look-ahead)
-//   ridge_solve    forward and backward substitution by blocks, one block per 16 columns
+//   ridge_chol     blocked Cholesky (32-wide blocks), one launch per block column kb: every tile
+//                  (i, j) of the trailing matrix computes L_ik = A_ik L_kk^-T itself, subtracts
+//                  L_ik L_jk^T, and the tile (kb+1, kb+1) then factors itself and inverts its L
+//                  (look-ahead); in the same launch the forward solve moves one block: Y_k =
+//                  L_kk^-1 B_k, and B_i -= L_ik Y_k for every i > k
+//   ridge_back     the backward solve, one launch per block row k from the last: X_k =
+//                  L_kk^-T Y_k, Y_i -= L_ki^T X_k for every i < k; X_k is V_c's rows
 // Every sum has a fixed order, so results are deterministic.  The matrix is padded to a
 // multiple of 64 with an identity block, which leaves the solution unchanged.
 #include "common.hpp"
@@ -23,14 +26,15 @@ namespace kvc {
 
 namespace {
 
-constexpr int kT = 64;          // tile edge
+constexpr int kT = 64;          // tile edge of the probability, residual and Gram kernels
+constexpr int kNB = 32;         // block edge of the Cholesky factorisation and the solves
 constexpr int kSplit = 4;       // parts of the row sum in the Gram products
-constexpr int kSolveCols = 16;  // right-hand-side columns per solve block
 
 struct RidgeDims {
   int hq, hkv, d, G, causal;
   int64_t n, nq, nc, m, R, npad;
-  int nb;
+  int nt;         // 64-wide tiles of npad (Gram)
+  int nb;         // 32-wide blocks of npad (Cholesky, solves)
 };
 
 RidgeDims dims_of(const Layer& L, int64_t nc) {
@@ -46,7 +50,8 @@ RidgeDims dims_of(const Layer& L, int64_t nc) {
   r.m = L.n - nc;
   r.R = (int64_t)L.G * L.nq;
   r.npad = (nc + kT - 1) / kT * kT;
-  r.nb = (int)(r.npad / kT);
+  r.nt = (int)(r.npad / kT);
+  r.nb = (int)(r.npad / kNB);
   return r;
 }
 
@@ -59,9 +64,9 @@ struct RidgeWs {
   double* Bp;     // [kSplit][Hkv][npad][d]
   double* M;      // [Hkv][npad][npad]          (lower tiles; updated in place)
   double* Lm;     // [Hkv][npad][npad]          (lower tiles of L)
-  double* Li;     // [Hkv][nb][64][64]          inverse of each diagonal block of L
-  double* Bm;     // [Hkv][npad][d]
-  double* Yf;     // [Hkv][npad][d]             forward-substitution result
+  double* Li;     // [Hkv][nb][32][32]          inverse of each diagonal block of L
+  double* Bm;     // [Hkv][npad][d]             right side, updated by the forward solve
+  double* Yf;     // [Hkv][npad][d]             forward result, updated by the backward solve
 };
 
 RidgeWs carve(const Layer& L, const RidgeDims& r, char* ws, size_t* total) {
@@ -74,7 +79,7 @@ RidgeWs carve(const Layer& L, const RidgeDims& r, char* ws, size_t* total) {
   const size_t o_Bp = p.take(sizeof(double) * kSplit * r.hkv * r.npad * r.d);
   const size_t o_M = p.take(sizeof(double) * r.hkv * r.npad * r.npad);
   const size_t o_L = p.take(sizeof(double) * r.hkv * r.npad * r.npad);
-  const size_t o_Li = p.take(sizeof(double) * r.hkv * r.nb * kT * kT);
+  const size_t o_Li = p.take(sizeof(double) * r.hkv * r.nb * kNB * kNB);
   const size_t o_Bm = p.take(sizeof(double) * r.hkv * r.npad * r.d);
   const size_t o_Y = p.take(sizeof(double) * r.hkv * r.npad * r.d);
   if (total) *total = p.off;
@@ -222,7 +227,7 @@ ridge_gram(const float* __restrict__ P, const float* __restrict__ T, double* __r
   __shared__ double xs[32][kT];
   __shared__ double zs[32][kT];
   const int s = blockIdx.y, g = blockIdx.z;
-  const int nt = r.nb;
+  const int nt = r.nt;
   const int nlow = nt * (nt + 1) / 2;
   int tile = blockIdx.x;
   bool isB;
@@ -314,227 +319,282 @@ ridge_sum(const double* __restrict__ Mp, const double* __restrict__ Bp, double* 
   }
 }
 
-// Cholesky of the 64 x 64 tile in LDS (lower part) by wave 0, then the inverse of that L;
-// writes L (lower, zeros above) to Ld (row stride ld) and L^-1 to Li (64 x 64).  A pivot that
-// is not positive sets the status bit.
-__device__ void potrf_tile(double (*A)[kT + 1], double (*X)[kT + 1], double* __restrict__ Ld, int64_t ld,
-                           double* __restrict__ Li, int32_t* __restrict__ status) {
+// Cholesky of the 32 x 32 tile in LDS (lower part), right-looking with all threads.  Thread t
+// owns the fixed elements e = t + 256 u (u < 3) of the 528-element lower triangle.  Step j: every
+// thread reads the pivot, its owned elements (i, c), j < c <= i, drop l_ij l_cj with
+// l = a * (1 / sqrt(pivot)); after the barrier column j is scaled (it is not read by later
+// steps' updates, and the next pivot is final).  The inverse of L follows, one column per lane
+// held in registers.  Writes L (lower, zeros above) to Ld (row stride ld) and L^-1 to Li
+// (32 x 32).  A pivot that is not positive sets the status bit.
+__device__ __forceinline__ void potrf_tile(double (*A)[kNB + 1], double (*X)[kNB + 1], double* __restrict__ Ld,
+                                           int64_t ld, double* __restrict__ Li, int32_t* __restrict__ status) {
+  constexpr int kTri = kNB * (kNB + 1) / 2;          // 528
+  constexpr int kPer = (kTri + 255) / 256;           // 3
   const int tid = threadIdx.x;
-  if (tid < 64) {
-    const int i = tid;
-    bool bad = false;
-    for (int j = 0; j < kT; ++j) {
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-      const double piv = A[j][j];
-      bad |= !(piv > 0.0);
-      const double dj = sqrt(piv);
-      if (i == j) A[j][j] = dj;
-      if (i > j) A[i][j] = A[i][j] / dj;
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-      if (i > j) {
-        const double lij = A[i][j];
-        for (int c = j + 1; c <= i; ++c) A[i][c] -= lij * A[c][j];
-      }
+  int ei[kPer], ec[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {                   // element e -> (i, c), e = i (i + 1) / 2 + c
+    const int e = tid + 256 * u;
+    int i = 0;
+    while ((i + 1) * (i + 2) / 2 <= e && i < kNB) ++i;
+    ei[u] = e < kTri ? i : -1;
+    ec[u] = e < kTri ? e - i * (i + 1) / 2 : kNB;
+  }
+  bool bad = false;
+  __syncthreads();
+  for (int j = 0; j < kNB; ++j) {
+    const double piv = A[j][j];
+    bad |= !(piv > 0.0);
+    const double rd = 1.0 / sqrt(piv);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = ei[u], c = ec[u];
+      if (c > j && i >= c) A[i][c] -= (A[i][j] * rd) * (A[c][j] * rd);
     }
-    if (bad && i == 0) atomicOr(status, KVC_DEV_NOT_SPD);
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    // column i of L^-1 by forward substitution: X[r][i] for r >= i
-    for (int rr = 0; rr < kT; ++rr) {
-      double v;
-      if (rr < i) {
-        v = 0.0;
-      } else {
-        v = rr == i ? 1.0 : 0.0;
-        for (int p = i; p < rr; ++p) v -= A[rr][p] * X[p][i];
-        v /= A[rr][rr];
-      }
-      X[rr][i] = v;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = ei[u], c = ec[u];
+      if (c == j) A[i][j] = (i == j) ? piv * rd : A[i][j] * rd;
     }
   }
+  if (bad && tid == 0) atomicOr(status, KVC_DEV_NOT_SPD);
   __syncthreads();
-  for (int e = tid; e < kT * kT; e += blockDim.x) {
-    const int rr = e / kT, c = e % kT;
+  if (tid < kNB) {
+    const int c = tid;
+    double x[kNB];
+#pragma unroll
+    for (int rr = 0; rr < kNB; ++rr) {
+      double s0 = rr == c ? 1.0 : 0.0, s1 = 0.0;
+#pragma unroll
+      for (int p = 0; p + 1 < rr; p += 2) {
+        s0 -= A[rr][p] * x[p];
+        s1 -= A[rr][p + 1] * x[p + 1];
+      }
+      if (rr & 1) s0 -= A[rr][rr - 1] * x[rr - 1];
+      x[rr] = (s0 + s1) / A[rr][rr];                 // 0 above the diagonal (rr < c)
+    }
+#pragma unroll
+    for (int rr = 0; rr < kNB; ++rr) X[rr][c] = x[rr];
+  }
+  __syncthreads();
+  for (int e = tid; e < kNB * kNB; e += blockDim.x) {
+    const int rr = e / kNB, c = e % kNB;
     Ld[rr * ld + c] = c <= rr ? A[rr][c] : 0.0;
     Li[e] = X[rr][c];
   }
 }
 
-// One block column kb of the blocked Cholesky (kb = -1: factor tile (0, 0) only).  Block
-// (tile index) covers tile (ib, jb), kb < jb <= ib < nb, of head g.
+// 32 x 32 products with 256 threads as 16 x 16, each 2 x 2 outputs:
+//   mm_abT: C[r][c] = sum_p A[r][p] B[c][p];   mm_ab: C[r][c] = sum_p A[r][p] B[p][c];
+//   mm_aTb: C[r][c] = sum_p A[p][r] B[p][c].
+typedef double Tile[kNB][kNB + 1];
+__device__ __forceinline__ void mm_abT(const Tile& A, const Tile& B, double (&c)[2][2]) {
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  for (int p = 0; p < kNB; ++p) {
+    const double a0 = A[2 * ty][p], a1 = A[2 * ty + 1][p], b0 = B[2 * tx][p], b1 = B[2 * tx + 1][p];
+    c[0][0] = fma(a0, b0, c[0][0]);
+    c[0][1] = fma(a0, b1, c[0][1]);
+    c[1][0] = fma(a1, b0, c[1][0]);
+    c[1][1] = fma(a1, b1, c[1][1]);
+  }
+}
+__device__ __forceinline__ void mm_ab(const Tile& A, const Tile& B, double (&c)[2][2]) {
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  for (int p = 0; p < kNB; ++p) {
+    const double a0 = A[2 * ty][p], a1 = A[2 * ty + 1][p], b0 = B[p][2 * tx], b1 = B[p][2 * tx + 1];
+    c[0][0] = fma(a0, b0, c[0][0]);
+    c[0][1] = fma(a0, b1, c[0][1]);
+    c[1][0] = fma(a1, b0, c[1][0]);
+    c[1][1] = fma(a1, b1, c[1][1]);
+  }
+}
+__device__ __forceinline__ void mm_aTb(const Tile& A, const Tile& B, double (&c)[2][2]) {
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  for (int p = 0; p < kNB; ++p) {
+    const double a0 = A[p][2 * ty], a1 = A[p][2 * ty + 1], b0 = B[p][2 * tx], b1 = B[p][2 * tx + 1];
+    c[0][0] = fma(a0, b0, c[0][0]);
+    c[0][1] = fma(a0, b1, c[0][1]);
+    c[1][0] = fma(a1, b0, c[1][0]);
+    c[1][1] = fma(a1, b1, c[1][1]);
+  }
+}
+__device__ __forceinline__ void tile_load(Tile& T, const double* __restrict__ src, int64_t ld) {
+  for (int e = threadIdx.x; e < kNB * kNB; e += 256) T[e / kNB][e % kNB] = src[(e / kNB) * ld + e % kNB];
+}
+__device__ __forceinline__ void tile_put(Tile& T, const double (&c)[2][2]) {
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  T[2 * ty][2 * tx] = c[0][0];
+  T[2 * ty][2 * tx + 1] = c[0][1];
+  T[2 * ty + 1][2 * tx] = c[1][0];
+  T[2 * ty + 1][2 * tx + 1] = c[1][1];
+}
+__device__ __forceinline__ void zero2(double (&c)[2][2]) { c[0][0] = c[0][1] = c[1][0] = c[1][1] = 0.0; }
+
+// One block column kb of the blocked Cholesky and one block of the forward solve (kb = -1:
+// factor tile (0, 0) only).  Blocks [0, ntile) cover the trailing tiles (ib, jb),
+// kb < jb <= ib < nb; the next blocks the right-side tiles (ib, column block cb), ib > kb.
 __global__ void __launch_bounds__(256)
-ridge_chol(double* __restrict__ M, double* __restrict__ Lm, double* __restrict__ Li, RidgeDims r, int kb,
-           int32_t* __restrict__ status) {
-  __shared__ double Ls[kT][kT + 1];     // L_kk^-1, then the tile to factor
-  __shared__ double Xi[kT][kT + 1];
-  __shared__ double Xj[kT][kT + 1];
-  const int g = blockIdx.y, tid = threadIdx.x;
-  const int64_t np = r.npad;
+ridge_chol(double* __restrict__ M, double* __restrict__ Lm, double* __restrict__ Li, double* __restrict__ Bm,
+           double* __restrict__ Yf, RidgeDims r, int kb, int32_t* __restrict__ status) {
+  __shared__ Tile Ls, Xi, Xj;
+  const int g = blockIdx.y;
+  const int64_t np = r.npad, D = r.d;
   double* Mg = M + (int64_t)g * np * np;
   double* Lg = Lm + (int64_t)g * np * np;
-  double* Lig = Li + (int64_t)g * r.nb * kT * kT;
+  double* Lig = Li + (int64_t)g * r.nb * kNB * kNB;
   if (kb < 0) {
-    for (int e = tid; e < kT * kT; e += 256) Ls[e / kT][e % kT] = Mg[(e / kT) * np + e % kT];
-    __syncthreads();
+    tile_load(Ls, Mg, np);
     potrf_tile(Ls, Xi, Lg, np, Lig, status);
     return;
   }
-  // tile index -> (ib, jb) with kb < jb <= ib < nb: t = u (u + 1) / 2 + v, ib = kb + 1 + u, jb = kb + 1 + v
+  const int rem = r.nb - 1 - kb;
+  const int ntile = rem * (rem + 1) / 2;
+  const int64_t k0 = (int64_t)kb * kNB;
+  double c[2][2];
+  tile_load(Ls, Lig + k0 * kNB, kNB);                             // L_kk^-1
+  if ((int)blockIdx.x >= ntile) {
+    // forward solve: Y_k = L_kk^-1 B_k, B_ib -= L_ib,k Y_k
+    const int t = blockIdx.x - ntile;
+    const int ib = kb + 1 + t / (int)(D / kNB), cb = t % (int)(D / kNB);
+    double* Bg = Bm + (int64_t)g * np * D;
+    tile_load(Xj, Mg + (int64_t)ib * kNB * np + k0, np);          // A_ib,k
+    tile_load(Xi, Bg + k0 * D + (int64_t)cb * kNB, D);            // B_k
+    __syncthreads();
+    zero2(c);
+    mm_ab(Ls, Xi, c);                                             // Y_k = L_kk^-1 B_k
+    double y[2][2] = {{c[0][0], c[0][1]}, {c[1][0], c[1][1]}};
+    zero2(c);
+    mm_abT(Xj, Ls, c);                                            // L_ib,k = A_ib,k L_kk^-T
+    __syncthreads();
+    tile_put(Xi, y);
+    tile_put(Xj, c);
+    __syncthreads();
+    if (ib == kb + 1) {
+      const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+      double* Yt = Yf + (int64_t)g * np * D + k0 * D + (int64_t)cb * kNB;
+      Yt[(2 * ty) * D + 2 * tx] = y[0][0];
+      Yt[(2 * ty) * D + 2 * tx + 1] = y[0][1];
+      Yt[(2 * ty + 1) * D + 2 * tx] = y[1][0];
+      Yt[(2 * ty + 1) * D + 2 * tx + 1] = y[1][1];
+    }
+    double* Bt = Bg + (int64_t)ib * kNB * D + (int64_t)cb * kNB;
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    c[0][0] = -Bt[(2 * ty) * D + 2 * tx];
+    c[0][1] = -Bt[(2 * ty) * D + 2 * tx + 1];
+    c[1][0] = -Bt[(2 * ty + 1) * D + 2 * tx];
+    c[1][1] = -Bt[(2 * ty + 1) * D + 2 * tx + 1];
+    mm_ab(Xj, Xi, c);                                             // L_ib,k Y_k - B_ib
+    Bt[(2 * ty) * D + 2 * tx] = -c[0][0];
+    Bt[(2 * ty) * D + 2 * tx + 1] = -c[0][1];
+    Bt[(2 * ty + 1) * D + 2 * tx] = -c[1][0];
+    Bt[(2 * ty + 1) * D + 2 * tx + 1] = -c[1][1];
+    return;
+  }
+  // trailing tile index -> (ib, jb): t = u (u + 1) / 2 + v, ib = kb + 1 + u, jb = kb + 1 + v
   const int t = blockIdx.x;
   int u = 0;
   while ((u + 1) * (u + 2) / 2 <= t) ++u;
   const int v = t - u * (u + 1) / 2;
   const int ib = kb + 1 + u, jb = kb + 1 + v;
-  for (int e = tid; e < kT * kT; e += 256) {
-    const int rr = e / kT, c = e % kT;
-    Ls[rr][c] = Lig[(int64_t)kb * kT * kT + e];
-    Xj[rr][c] = Mg[((int64_t)ib * kT + rr) * np + (int64_t)kb * kT + c];      // A_ib,kb
-  }
+  tile_load(Xj, Mg + (int64_t)ib * kNB * np + k0, np);            // A_ib,k
   __syncthreads();
-  const int tx = tid & 15, ty = tid >> 4;
-  // X_i = A_ib,kb L_kk^-T: X[r][c] = sum_{p <= c} A[r][p] Linv[c][p]
-  double acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-  for (int p = 0; p < kT; ++p) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const double a = Xj[ty * 4 + i][p];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = fma(a, Ls[tx * 4 + j][p], acc[i][j]);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) Xi[ty * 4 + i][tx * 4 + j] = acc[i][j];
+  zero2(c);
+  mm_abT(Xj, Ls, c);                                              // X_i = A_ib,k L_kk^-T
+  double xi[2][2] = {{c[0][0], c[0][1]}, {c[1][0], c[1][1]}};
   __syncthreads();
+  tile_put(Xi, xi);
   if (jb != ib) {
-    for (int e = tid; e < kT * kT; e += 256)
-      Xj[e / kT][e % kT] = Mg[((int64_t)jb * kT + e / kT) * np + (int64_t)kb * kT + e % kT];   // A_jb,kb
+    tile_load(Xj, Mg + (int64_t)jb * kNB * np + k0, np);          // A_jb,k
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-    for (int p = 0; p < kT; ++p) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const double a = Xj[ty * 4 + i][p];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a, Ls[tx * 4 + j][p], acc[i][j]);
-      }
-    }
+    zero2(c);
+    mm_abT(Xj, Ls, c);                                            // X_j
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) Xj[ty * 4 + i][tx * 4 + j] = acc[i][j];
-    __syncthreads();
+    tile_put(Xj, c);
   } else {
-    for (int e = tid; e < kT * kT; e += 256) Xj[e / kT][e % kT] = Xi[e / kT][e % kT];
-    __syncthreads();
+    tile_put(Xj, xi);
   }
+  __syncthreads();
   // A_ib,jb -= X_i X_j^T
-  double* tileA = Mg + (int64_t)ib * kT * np + (int64_t)jb * kT;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = tileA[(ty * 4 + i) * np + tx * 4 + j];
-  for (int p = 0; p < kT; ++p) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const double a = Xi[ty * 4 + i][p];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = fma(-a, Xj[tx * 4 + j][p], acc[i][j]);
-    }
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  double* tileA = Mg + (int64_t)ib * kNB * np + (int64_t)jb * kNB;
+  c[0][0] = -tileA[(2 * ty) * np + 2 * tx];
+  c[0][1] = -tileA[(2 * ty) * np + 2 * tx + 1];
+  c[1][0] = -tileA[(2 * ty + 1) * np + 2 * tx];
+  c[1][1] = -tileA[(2 * ty + 1) * np + 2 * tx + 1];
+  mm_abT(Xi, Xj, c);
+  c[0][0] = -c[0][0];
+  c[0][1] = -c[0][1];
+  c[1][0] = -c[1][0];
+  c[1][1] = -c[1][1];
+  tileA[(2 * ty) * np + 2 * tx] = c[0][0];
+  tileA[(2 * ty) * np + 2 * tx + 1] = c[0][1];
+  tileA[(2 * ty + 1) * np + 2 * tx] = c[1][0];
+  tileA[(2 * ty + 1) * np + 2 * tx + 1] = c[1][1];
+  if (jb == kb + 1) {                                             // this tile publishes L_ib,k
+    double* Lt = Lg + (int64_t)ib * kNB * np + k0;
+    for (int e = threadIdx.x; e < kNB * kNB; e += 256) Lt[(e / kNB) * np + e % kNB] = Xi[e / kNB][e % kNB];
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) tileA[(ty * 4 + i) * np + tx * 4 + j] = acc[i][j];
-  if (jb == kb + 1) {                                  // this tile publishes L_ib,kb
-    double* Lt = Lg + (int64_t)ib * kT * np + (int64_t)kb * kT;
-    for (int e = tid; e < kT * kT; e += 256) Lt[(e / kT) * np + e % kT] = Xi[e / kT][e % kT];
-  }
-  if (ib == kb + 1 && jb == kb + 1) {                 // look-ahead: factor the next diagonal tile
+  if (ib == kb + 1 && jb == kb + 1) {                             // look-ahead: factor the next diagonal tile
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) Ls[ty * 4 + i][tx * 4 + j] = acc[i][j];
-    __syncthreads();
-    potrf_tile(Ls, Xi, Lg + (int64_t)ib * kT * np + (int64_t)ib * kT, np, Lig + (int64_t)ib * kT * kT, status);
+    tile_put(Ls, c);
+    potrf_tile(Ls, Xi, Lg + (int64_t)ib * kNB * np + (int64_t)ib * kNB, np, Lig + (int64_t)ib * kNB * kNB, status);
   }
 }
 
-// Solve L L^T X = B for kSolveCols columns of head g: forward Y_k = L_kk^-1 (B_k - sum_{j<k}
-// L_kj Y_j), backward X_k = L_kk^-T (Y_k - sum_{j>k} L_jk^T X_j); writes V_c = X[:n_c] (fp32).
+// Backward solve, block row kb (from the last): every block computes X_k = L_kk^-T Y_k
+// (Y_{nb-1} = L^-1 B_{nb-1}, the last forward step, for the first launch); block (ib, cb),
+// ib < kb, then does Y_ib -= L_k,ib^T X_k.  Block ib = 0 (the only one when kb = 0) writes
+// X_k's rows below n_c to V_c.
 __global__ void __launch_bounds__(256)
-ridge_solve(const double* __restrict__ Lm, const double* __restrict__ Li, const double* __restrict__ Bm,
-            double* __restrict__ Yf, float* __restrict__ v_c, RidgeDims r) {
-  __shared__ double acc_s[kT][kSolveCols];
-  const int g = blockIdx.y, c0 = blockIdx.x * kSolveCols;
-  const int tid = threadIdx.x, row = tid >> 2, cq = (tid & 3) * 4;
+ridge_back(const double* __restrict__ Lm, const double* __restrict__ Li, const double* __restrict__ Bm,
+           double* __restrict__ Yf, float* __restrict__ v_c, RidgeDims r, int kb) {
+  __shared__ Tile Ls, Ys, Lt;
+  const int g = blockIdx.y;
   const int64_t np = r.npad, D = r.d;
-  const double* Lg = Lm + (int64_t)g * np * np;
-  const double* Lig = Li + (int64_t)g * r.nb * kT * kT;
-  const double* Bg = Bm + (int64_t)g * np * D;
+  const int nib = kb > 0 ? kb : 1;
+  const int ib = blockIdx.x % nib, cb = blockIdx.x / nib;
+  const int64_t k0 = (int64_t)kb * kNB;
+  const double* Lig = Li + (int64_t)g * r.nb * kNB * kNB;
   double* Yg = Yf + (int64_t)g * np * D;
-  for (int kb = 0; kb < r.nb; ++kb) {
-    const int64_t a = (int64_t)kb * kT + row;
-    double acc[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = Bg[a * D + c0 + cq + j];
-    for (int64_t p = 0; p < (int64_t)kb * kT; ++p) {
-      const double l = Lg[a * np + p];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = fma(-l, Yg[p * D + c0 + cq + j], acc[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc_s[row][cq + j] = acc[j];
+  tile_load(Ls, Lig + k0 * kNB, kNB);
+  double c[2][2];
+  if (kb == r.nb - 1) {
+    tile_load(Ys, Bm + (int64_t)g * np * D + k0 * D + (int64_t)cb * kNB, D);
     __syncthreads();
-    const double* Lik = Lig + (int64_t)kb * kT * kT;
-    double y[4] = {0.0, 0.0, 0.0, 0.0};
-    for (int p = 0; p <= row; ++p) {
-      const double l = Lik[row * kT + p];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) y[j] = fma(l, acc_s[p][cq + j], y[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) Yg[a * D + c0 + cq + j] = y[j];
+    zero2(c);
+    mm_ab(Ls, Ys, c);                                             // Y_k = L_kk^-1 B_k
     __syncthreads();
+    tile_put(Ys, c);
+  } else {
+    tile_load(Ys, Yg + k0 * D + (int64_t)cb * kNB, D);
   }
-  for (int kb = r.nb - 1; kb >= 0; --kb) {
-    const int64_t a = (int64_t)kb * kT + row;
-    double acc[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = Yg[a * D + c0 + cq + j];
-    for (int64_t p = (int64_t)(kb + 1) * kT; p < np; ++p) {
-      const double l = Lg[p * np + a];                 // (L^T)[a][p] = L[p][a]
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = fma(-l, Yg[p * D + c0 + cq + j], acc[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc_s[row][cq + j] = acc[j];
-    __syncthreads();
-    const double* Lik = Lig + (int64_t)kb * kT * kT;
-    double x[4] = {0.0, 0.0, 0.0, 0.0};
-    for (int p = row; p < kT; ++p) {
-      const double l = Lik[p * kT + row];              // (L_kk^-T)[row][p] = L_kk^-1[p][row]
-#pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] = fma(l, acc_s[p][cq + j], x[j]);
-    }
-    __syncthreads();                                   // every thread has read Y_k's rows
-#pragma unroll
-    for (int j = 0; j < 4; ++j) Yg[a * D + c0 + cq + j] = x[j];   // X_k replaces Y_k
-    if (a < r.nc) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v_c[((int64_t)g * r.nc + a) * D + c0 + cq + j] = (float)x[j];
-    }
-    __syncthreads();
+  __syncthreads();
+  zero2(c);
+  mm_aTb(Ls, Ys, c);                                              // X_k = L_kk^-T Y_k
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  if (ib == 0) {
+    for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 2; ++j) {
+        const int64_t a = k0 + 2 * ty + i;
+        if (a < r.nc) v_c[((int64_t)g * r.nc + a) * D + (int64_t)cb * kNB + 2 * tx + j] = (float)c[i][j];
+      }
   }
+  if (kb == 0) return;
+  __syncthreads();
+  tile_put(Ys, c);                                                // Ys = X_k
+  tile_load(Lt, Lm + (int64_t)g * np * np + k0 * np + (int64_t)ib * kNB, np);   // L_k,ib
+  __syncthreads();
+  double* Yt = Yg + (int64_t)ib * kNB * D + (int64_t)cb * kNB;
+  c[0][0] = -Yt[(2 * ty) * D + 2 * tx];
+  c[0][1] = -Yt[(2 * ty) * D + 2 * tx + 1];
+  c[1][0] = -Yt[(2 * ty + 1) * D + 2 * tx];
+  c[1][1] = -Yt[(2 * ty + 1) * D + 2 * tx + 1];
+  mm_aTb(Lt, Ys, c);                                              // L_k,ib^T X_k - Y_ib
+  Yt[(2 * ty) * D + 2 * tx] = -c[0][0];
+  Yt[(2 * ty) * D + 2 * tx + 1] = -c[0][1];
+  Yt[(2 * ty + 1) * D + 2 * tx] = -c[1][0];
+  Yt[(2 * ty + 1) * D + 2 * tx + 1] = -c[1][1];
 }
 
 __global__ void ridge_reset_status(int32_t* status) {
@@ -560,8 +620,8 @@ hipError_t launch_ridge_fit(const Layer& L, int64_t nc, const uint16_t* q, const
   if (e != hipSuccess) return e;
   const dim3 gp((unsigned)((r.n + kT - 1) / kT), (unsigned)((r.R + kT - 1) / kT), (unsigned)r.hkv);
   const dim3 gr((unsigned)(r.d / kT), (unsigned)((r.R + kT - 1) / kT), (unsigned)r.hkv);
-  const int nlow = r.nb * (r.nb + 1) / 2;
-  const dim3 gg((unsigned)(nlow + r.nb * (r.d / kT)), (unsigned)kSplit, (unsigned)r.hkv);
+  const int nlow = r.nt * (r.nt + 1) / 2;
+  const dim3 gg((unsigned)(nlow + r.nt * (r.d / kT)), (unsigned)kSplit, (unsigned)r.hkv);
   if (r.d == 128) {
     ridge_probs<128><<<gp, 256, 0, s>>>(q, k, w.lse, w.P, r, L.c_log2);
     ridge_resid<128><<<gr, 256, 0, s>>>(w.P, v_r, y, w.T, r);
@@ -575,13 +635,17 @@ hipError_t launch_ridge_fit(const Layer& L, int64_t nc, const uint16_t* q, const
   unsigned bs = (unsigned)((nsum + 255) / 256);
   if (bs > 4096) bs = 4096;
   ridge_sum<<<dim3(bs, (unsigned)r.hkv), 256, 0, s>>>(w.Mp, w.Bp, w.M, w.Bm, r, lambda);
-  ridge_chol<<<dim3(1, (unsigned)r.hkv), 256, 0, s>>>(w.M, w.Lm, w.Li, r, -1, status);
+  ridge_chol<<<dim3(1, (unsigned)r.hkv), 256, 0, s>>>(w.M, w.Lm, w.Li, w.Bm, w.Yf, r, -1, status);
+  const int ncb = r.d / kNB;
   for (int kb = 0; kb + 1 < r.nb; ++kb) {
     const int rem = r.nb - 1 - kb;
-    ridge_chol<<<dim3((unsigned)(rem * (rem + 1) / 2), (unsigned)r.hkv), 256, 0, s>>>(w.M, w.Lm, w.Li, r, kb,
-                                                                                        status);
+    const unsigned nblk = (unsigned)(rem * (rem + 1) / 2 + rem * ncb);
+    ridge_chol<<<dim3(nblk, (unsigned)r.hkv), 256, 0, s>>>(w.M, w.Lm, w.Li, w.Bm, w.Yf, r, kb, status);
   }
-  ridge_solve<<<dim3((unsigned)(r.d / kSolveCols), (unsigned)r.hkv), 256, 0, s>>>(w.Lm, w.Li, w.Bm, w.Yf, v_c, r);
+  for (int kb = r.nb - 1; kb >= 0; --kb) {
+    const unsigned nblk = (unsigned)((kb > 0 ? kb : 1) * ncb);
+    ridge_back<<<dim3(nblk, (unsigned)r.hkv), 256, 0, s>>>(w.Lm, w.Li, w.Bm, w.Yf, v_c, r, kb);
+  }
   return hipGetLastError();
 }
 
