@@ -37,8 +37,8 @@ CPU_SAMPLE_SECONDS = 12.0      # oracle sample: KV heads are added until this mu
 # scaled by the same counters on a plain copy of known size (profiles/hbm_counters_*.md).
 # A figure holds only for the scorer source it was measured on; otherwise traffic is null.
 MEASURED_TRAFFIC = {
-    "llama8b_prefill_n8192": {"bytes": 91933904,
-                              "score_src_sha256": "318ad9cee6273be0500b29de459da82f0afba10b57b99f20798bd6c90be1718a"},
+    "llama8b_prefill_n8192": {"bytes": 91862810,
+                              "score_src_sha256": "f82d8658e023da47f0f53c8db3dfa35dff47f0f18eb9391ee25f11d30fc29b8d"},
 }
 
 
@@ -315,7 +315,7 @@ def main():
         "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
         "traffic": measured_traffic(cfg.name),
-        "kernel": "lse_partial", "flops_per_launch": flops, "avg_launch_ms": round(lse_ms, 5),
+        "kernel": "lse_partial<128, 0>", "flops_per_launch": flops, "avg_launch_ms": round(lse_ms, 5),
     }
 
     # fidelity attend on the configuration's fidelity rows (the last rows of Q), and a

@@ -616,7 +616,7 @@ hipError_t launch_ridge_fit(const Layer& L, int64_t nc, const uint16_t* q, const
   RidgeWs w = carve(L, r, ws, nullptr);
   int32_t* status = reinterpret_cast<int32_t*>(ws);
   ridge_reset_status<<<1, 64, 0, s>>>(status);
-  hipError_t e = launch_row_lse(L, q, k, w.lse, w.lse_ws, s);
+  hipError_t e = launch_row_lse(L, q, k, w.lse, w.lse_ws, s, 1);
   if (e != hipSuccess) return e;
   const dim3 gp((unsigned)((r.n + kT - 1) / kT), (unsigned)((r.R + kT - 1) / kT), (unsigned)r.hkv);
   const dim3 gr((unsigned)(r.d / kT), (unsigned)((r.R + kT - 1) / kT), (unsigned)r.hkv);

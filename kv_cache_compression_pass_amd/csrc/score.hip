@@ -362,7 +362,9 @@ __device__ __forceinline__ void lse_masked_step(const Geo& G, const uint16_t* kh
   }
 }
 
-template <int D>
+// TAG does not change the code: it gives the launches made for another caller (the ridge
+// fit's weights) their own kernel name, so that profiles keep the two apart.
+template <int D, int TAG>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 lse_partial(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             float2* __restrict__ part, float* __restrict__ lse, Decomp dc, int64_t N, int64_t Nq,
@@ -941,15 +943,19 @@ size_t score_ws_bytes(const Layer& L, int mode, int hidden_dim) {
 }
 
 hipError_t launch_row_lse(const Layer& L, const uint16_t* q, const uint16_t* k, float* lse,
-                          char* ws, hipStream_t s) {
+                          char* ws, hipStream_t s, int tag) {
   const ScorePlan p = score_plan(L);
   const Decomp dc = decomp_of(L, p);
   WsPlan w;
   float2* part = reinterpret_cast<float2*>(ws + w.take((size_t)L.hq * L.nq * p.maxCh * sizeof(float2)));
-  if (L.d == 128)
-    lse_partial<128><<<grid_of(p), kThreads, 0, s>>>(q, k, part, lse, dc, L.n, L.nq, L.causal, L.c_log2);
+  if (L.d == 128 && tag == 0)
+    lse_partial<128, 0><<<grid_of(p), kThreads, 0, s>>>(q, k, part, lse, dc, L.n, L.nq, L.causal, L.c_log2);
+  else if (L.d == 128)
+    lse_partial<128, 1><<<grid_of(p), kThreads, 0, s>>>(q, k, part, lse, dc, L.n, L.nq, L.causal, L.c_log2);
+  else if (tag == 0)
+    lse_partial<64, 0><<<grid_of(p), kThreads, 0, s>>>(q, k, part, lse, dc, L.n, L.nq, L.causal, L.c_log2);
   else
-    lse_partial<64><<<grid_of(p), kThreads, 0, s>>>(q, k, part, lse, dc, L.n, L.nq, L.causal, L.c_log2);
+    lse_partial<64, 1><<<grid_of(p), kThreads, 0, s>>>(q, k, part, lse, dc, L.n, L.nq, L.causal, L.c_log2);
   if (p.maxCh > 1) {
     const int64_t rows = (int64_t)L.hq * L.nq;
     lse_combine<<<(unsigned)((rows + 255) / 256), 256, 0, s>>>(part, lse, L.hq, L.n, L.nq, L.causal, p.KC, p.maxCh);
