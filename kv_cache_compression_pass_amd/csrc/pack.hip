@@ -258,12 +258,11 @@ pack_place(const uint8_t* __restrict__ bits_v, const uint8_t* __restrict__ bits_
 }
 
 // Group quantiser.  min / max use v_min3 / v_max3 (values are finite; fminf would first quiet
-// NaNs).  quantize_rt quantises the NE values a lane holds of one group (NE = 32: the whole
-// group; NE = 16: one half, the other half on lane ^ 32, XCH = true) at width b in {2, 4, 8},
-// stores the lane's NE*b/32 code words and, if asked, the group's (scale, zero) pair.  Only the
-// first m_own (0..NE) of the lane's values are valid; the rest code 0.  b is a runtime value
-// (the K channels of one wave have mixed widths) and every lane runs the same instructions:
-// codes are first placed one per byte, then the bytes are compacted to b bits.
+// NaNs).  quantize_rt quantises the 32 values of one group a lane holds at width b in {2, 4, 8}
+// and stores the group's b code words and its (scale, zero) pair.  Only the first m_own (1..32)
+// values are valid; the rest code 0.  b is a runtime value (the K channels of one wave have mixed
+// widths) and every lane runs the same instructions: codes are first placed one per byte, then
+// the bytes are compacted to b bits.
 //  * v = (x - z) * (1 / s) in fp32: 0 <= v < maxc + 2^-16, so rint(v) needs no clamp;
 //  * a value whose fp32 v lies within 2^(b-21) of a half-integer (over 2.6 times the error
 //    bound 3 * 2^-24 * v for v < 2^b) is decided again with the defining fp64 division,
@@ -288,18 +287,11 @@ __device__ __forceinline__ uint32_t crumbs_of(uint32_t w) {
   return (t | (t >> 12)) & 0xFFu;
 }
 
-template <int NE, bool XCH, bool FULL, class Src>
+template <bool FULL, class Src>
 __device__ __forceinline__ void quantize_rt(Src& src, int m_own, int b, uint32_t* __restrict__ dst,
-                                            float* __restrict__ par, bool write_par) {
-  static_assert(NE == 16 || NE == 32, "NE");
-  float mn, mx;
-  if (FULL) {
-    mn = src.elem(0);
-    mx = mn;
-  } else {
-    mn = m_own > 0 ? src.elem(0) : __builtin_inff();
-    mx = m_own > 0 ? src.elem(0) : -__builtin_inff();
-  }
+                                            float* __restrict__ par) {
+  constexpr int NE = 32;
+  float mn = src.elem(0), mx = mn;
 #pragma unroll
   for (int e = 1; e < NE - 1; e += 2) {
     const float a = (FULL || e < m_own) ? src.elem(e) : mn;
@@ -314,10 +306,6 @@ __device__ __forceinline__ void quantize_rt(Src& src, int m_own, int b, uint32_t
     const float a2 = (FULL || NE - 1 < m_own) ? a : mx;
     mn = min3_raw(mn, a, a);
     mx = max3_raw(mx, a2, a2);
-  }
-  if (XCH) {
-    mn = min3_raw(mn, __shfl_xor(mn, 32), mn);
-    mx = max3_raw(mx, __shfl_xor(mx, 32), mx);
   }
   const int maxi = (1 << b) - 1;
   const float s = (float)(((double)mx - (double)mn) / (double)maxi);
@@ -369,7 +357,7 @@ __device__ __forceinline__ void quantize_rt(Src& src, int m_own, int b, uint32_t
 #pragma unroll
   for (int i = 0; i < NW; ++i)
     if (i < nw) dst[i] = o[i];
-  if (write_par) *reinterpret_cast<float2*>(par) = make_float2(s, mn);
+  *reinterpret_cast<float2*>(par) = make_float2(s, mn);
 }
 
 // A lane's 32 values of one group as 16 packed bf16 pairs (element 2i in the low half of
@@ -421,7 +409,7 @@ __device__ __forceinline__ void pack_k_group(const uint16_t* __restrict__ k, int
       for (int i = 0; i < 16; ++i) dst[i] = src.w[i];
     } else if (b != 0) {
       float* par = k_par + 2 * (hp[19] + j * hp[21] + info.y);
-      quantize_rt<32, false, FULL>(src, m, b, dst, par, true);
+      quantize_rt<FULL>(src, m, b, dst, par);
     }
   }
 }
@@ -480,7 +468,7 @@ __device__ __forceinline__ void pack_v_slab(const uint16_t* __restrict__ v, int6
     return;
   }
   float* par = v_par + 2 * (hp[13 + z] + pos * GPR + grp);
-  quantize_rt<32, false, true>(src, 32, b, dst, par, true);
+  quantize_rt<true>(src, 32, b, dst, par);
 }
 
 template <int D>

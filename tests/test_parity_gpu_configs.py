@@ -143,3 +143,93 @@ def test_config3_kvzip_full_size():
     bk = np.full((hkv, d), 16, np.uint8)
     cache, st = H.pack(desc, k, v, H.dev_u8(b_r), H.dev_u8(bk))
     H.compare_packed(cache.to_numpy(), oracle.pack_cache(x["k"], x["v"], b_r, bk))
+
+
+def test_ridge_fit_at_the_bench_shape():
+    """The ridge value fit at the shape bench.py times (KVSculpt's layer: 12/2 heads, 768 pairs, 512
+    retained tokens, 1024 training rows), against the oracle's normal equations: the residual bound
+    that does not depend on the conditioning, and V itself within cond(M) times it."""
+    import bench
+    sh = bench.RIDGE_SHAPE
+    hq, hkv, d, nc, m, nq, lam = (sh["n_q_heads"], sh["n_kv_heads"], sh["head_dim"], sh["n_compressed"],
+                                  sh["n_retained"], sh["n_queries"], sh["lambda"])
+    print(f"case ridge bench shape: H_q={hq} H_kv={hkv} d={d} n_c={nc} m={m} Nq={nq} lambda={lam}", flush=True)
+    from workloads import make_inputs
+    x = make_inputs(hq, hkv, d, nc + m, nq, seed=4321)
+    y = np.random.default_rng(7).standard_normal((hq, nq, d)).astype(np.float32)
+    v_r = np.ascontiguousarray(x["v"][:, nc:])
+    desc = H.desc_of(hq, hkv, d, nc + m, nq, False)
+    ws = kvc.workspace(kvc.OP_RIDGE_FIT, desc, nc, H.DEV)
+    v_c = torch.empty(hkv, nc, d, dtype=torch.float32, device=H.DEV)
+    kvc.kvc_ridge_value_fit(desc, nc, H.dev_bf16(x["q"]), H.dev_bf16(x["k"]), H.dev_bf16(v_r), H.dev_f32(y), lam,
+                            v_c, ws)
+    torch.cuda.synchronize()
+    assert kvc.kvc_get_device_status(ws) == 0
+    got = v_c.cpu().numpy().astype(np.float64)
+    Ms, Bs = oracle.ridge_normal_equations(x["q"], x["k"], v_r, y, nc, lam, causal=False)
+    for g in range(hkv):
+        M, B = Ms[g], Bs[g]
+        want = np.linalg.solve(M, B)
+        scale = np.abs(M).sum(axis=1).max() * np.abs(got[g]).max() + np.abs(B).max()
+        assert np.abs(M @ got[g] - B).max() <= 1e-4 * scale
+        assert np.abs(got[g] - want).max() <= 1e-4 * np.linalg.cond(M) * np.abs(want).max() + 1e-6
+
+
+def test_step_replays_in_a_graph():
+    """Every call of the step only enqueues kernels on its stream (no allocation, no memset, no host
+    synchronisation), so the whole step can be captured in a HIP graph.  Replays, with eager work
+    between them that clobbers the outputs, give results bitwise equal to the eager step."""
+    cfg = get_config(1)
+    print("case graph replay: llama8b_prefill_n8192 step", flush=True)
+    hq, hkv, d, N, Nq = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_keys, cfg.n_queries
+    x = make_config_inputs(cfg)
+    q, k, v = (H.dev_bf16(x[n]) for n in ("q", "k", "v"))
+    desc = H.desc_of(hq, hkv, d, N, Nq, True)
+    lse = torch.empty(hq, Nq, dtype=torch.float32, device=H.DEV)
+    w = torch.empty(hkv, N, dtype=torch.float32, device=H.DEV)
+    wc = torch.empty(hkv, d, dtype=torch.float32, device=H.DEV)
+    bv = torch.empty(hkv, N, dtype=torch.uint8, device=H.DEV)
+    bk = torch.empty(hkv, d, dtype=torch.uint8, device=H.DEV)
+    ws = {op: kvc.workspace(op, desc, mode, H.DEV) for op, mode in
+          ((kvc.OP_ROW_LSE, 0), (kvc.OP_SCORE_TOKENS, 0), (kvc.OP_CHANNEL_WEIGHTS, 0), (kvc.OP_QUANTIZE_PACK, 0))}
+    ws_v = kvc.workspace(kvc.OP_ALLOCATE_BITS, desc, kvc.ALLOC_V_TOKENS, H.DEV)
+    ws_k = kvc.workspace(kvc.OP_ALLOCATE_BITS, desc, kvc.ALLOC_K_CHANNELS, H.DEV)
+    res_v, res_k = kvc.alloc_result_buffer(H.DEV), kvc.alloc_result_buffer(H.DEV)
+    cache = kvc.PackedCache(desc, H.DEV)
+
+    def step(s):
+        kvc.kvc_row_lse(desc, q, k, lse, ws[kvc.OP_ROW_LSE], stream=s)
+        kvc.kvc_score_tokens(desc, kvc.SCORE_SUM, q, k, lse, w, ws[kvc.OP_SCORE_TOKENS], stream=s)
+        kvc.kvc_channel_weights(desc, q, k, wc, ws[kvc.OP_CHANNEL_WEIGHTS], stream=s)
+        kvc.kvc_allocate_bits(desc, kvc.ALLOC_V_TOKENS, w, bv, ws_v, avg_bits=cfg.avg_bits, result=res_v, stream=s)
+        kvc.kvc_allocate_bits(desc, kvc.ALLOC_K_CHANNELS, wc, bk, ws_k, bits_v=bv, avg_bits=cfg.avg_bits,
+                              result=res_k, stream=s)
+        kvc.kvc_quantize_pack(desc, k, v, bv, bk, cache, ws[kvc.OP_QUANTIZE_PACK], stream=s)
+
+    def outputs():
+        torch.cuda.synchronize()
+        packed = cache.to_numpy()                      # the buffers trimmed to the lengths the header records
+        return [t.cpu().numpy() for t in (lse, w, wc, bv, bk, res_v, res_k)] + [packed[n] for n in sorted(packed)]
+
+    main = torch.cuda.current_stream()
+    step(main)
+    ref = outputs()
+    side = torch.cuda.Stream()
+    side.wait_stream(main)
+    with torch.cuda.stream(side):
+        step(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step(side)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        w.fill_(0)
+        bv.fill_(0)
+        lse.fill_(0)
+        cache.buffers["k_words"].fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        now = outputs()
+        for a, b in zip(ref, now):
+            np.testing.assert_array_equal(a, b)
