@@ -81,13 +81,34 @@ pack_count(const uint8_t* __restrict__ bits_v, int64_t N, int nchunk, int32_t* _
   if (threadIdx.x == 0) cbad[(int64_t)g * nchunk + ch] = badw[0] | badw[1] | badw[2] | badw[3];
 }
 
-// Placement, one block per (1024-token chunk ch, head g).  Every block first rebuilds, in LDS,
-// the zone totals of every head (from the chunk counts) and the K words / parameters per group
-// of every head (from bits_k); scans over heads then give the head offsets of the header.  The
-// chunk's own zone bases are the sums over the head's earlier chunks.  Finally the chunk's
-// tokens get their ordered ranks: the four zone counters of a thread's 4 tokens are packed into
-// one 64-bit word (16 bits per zone) and scanned.  Block (0, g) also writes head g's header
-// entries, its channel table and k_width; block (0, 0) the global header and the status word.
+// Placement, one block per (1024-token chunk ch, head g).  The chunk's own width bytes are
+// loaded first.  One wave per head then rebuilds, in LDS, the zone totals of every head (from
+// the chunk counts) and the K words / parameters per group (from bits_k).  Next, three waves
+// work side by side: wave 0 sums the sizes of the heads before g (the header offsets of head g;
+// for block (0, 0) also the totals), wave 1 the zone counts of the head's earlier chunks (the
+// chunk's zone bases), and in blocks (0, g) wave 2 scans head g's channels (its channel table
+// and k_width).  Finally the chunk's tokens get their ordered ranks: the four zone counters of a
+// thread's 4 tokens are packed into one 64-bit word (16 bits per zone) and scanned.  Block
+// (0, g) writes head g's header entries; block (0, 0) the global header and the status word.
+// All sums are of integers, so their order does not matter.
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)x, o, 64), hi = __shfl_xor((uint32_t)(x >> 32), o, 64);
+    x += ((uint64_t)hi << 32) | lo;
+  }
+  return x;
+}
+
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t lo = __shfl_up((uint32_t)x, o, 64), hi = __shfl_up((uint32_t)(x >> 32), o, 64);
+    if (lane >= o) x += ((uint64_t)hi << 32) | lo;
+  }
+  return x;
+}
+
 template <int D>
 __global__ void __launch_bounds__(256)
 pack_place(const uint8_t* __restrict__ bits_v, const uint8_t* __restrict__ bits_k, int64_t N, int Hkv,
@@ -98,15 +119,27 @@ pack_place(const uint8_t* __restrict__ bits_v, const uint8_t* __restrict__ bits_
   __shared__ int32_t tot[256][4];
   __shared__ int32_t kw_s[256], kq_s[256];
   __shared__ int64_t hv[24];
+  __shared__ int64_t bzs[4];
   __shared__ uint64_t sh[4];
   __shared__ int32_t bad_s;
   const int ch = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
   const int gpr = D / 32;
+
+  // the chunk's own tokens: loads that depend on nothing below
+  const int64_t t0 = (int64_t)ch * kChunk + tid * 4;
+  uint32_t b4 = 0;
+  if (t0 + 3 < N && (reinterpret_cast<uintptr_t>(bits_v + (int64_t)g * N + t0) & 3) == 0) {
+    b4 = *reinterpret_cast<const uint32_t*>(bits_v + (int64_t)g * N + t0);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (t0 + j < N) b4 |= (uint32_t)bits_v[(int64_t)g * N + t0 + j] << (8 * j);
+  }
   if (tid == 0) bad_s = 0;
   __syncthreads();
-  // per-head totals, one wave per head: lanes stride over the head's chunks and channels, then
-  // a butterfly sum (integer: order-independent)
+
+  // per-head totals, one wave per head
   bool bad = false;
   for (int h = wid; h < Hkv; h += 4) {
     uint64_t a = 0, b = 0;
@@ -125,122 +158,124 @@ pack_place(const uint8_t* __restrict__ bits_v, const uint8_t* __restrict__ bits_
         kqv += bk != 16 ? 1u : 0u;
       }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const uint32_t a0 = __shfl_xor((uint32_t)a, o, 64), a1 = __shfl_xor((uint32_t)(a >> 32), o, 64);
-      const uint32_t b0 = __shfl_xor((uint32_t)b, o, 64), b1 = __shfl_xor((uint32_t)(b >> 32), o, 64);
-      a += ((uint64_t)a1 << 32) | a0;
-      b += ((uint64_t)b1 << 32) | b0;
-      kwv += __shfl_xor(kwv, o, 64);
-      kqv += __shfl_xor(kqv, o, 64);
-    }
+    a = wave_sum_u64(a);
+    b = wave_sum_u64(b);
+    const uint64_t kk = wave_sum_u64((uint64_t)kwv | ((uint64_t)kqv << 32));
     if (lane == 0) {
       tot[h][0] = (int32_t)(a & 0xFFFFFFFFu);
       tot[h][1] = (int32_t)(a >> 32);
       tot[h][2] = (int32_t)(b & 0xFFFFFFFFu);
       tot[h][3] = (int32_t)(b >> 32);
-      kw_s[h] = (int32_t)kwv;
-      kq_s[h] = (int32_t)kqv;
+      kw_s[h] = (int32_t)(kk & 0xFFFFFFFFu);
+      kq_s[h] = (int32_t)(kk >> 32);
     }
   }
   if (bad) bad_s = 1;                               // benign race: every writer stores 1
   __syncthreads();
 
-  // head offsets: thread h handles head h (Hkv <= 256)
-  int64_t nv[4] = {0, 0, 0, 0}, R = 0, wk = 0, qk = 0, ng = 0;
-  if (tid < Hkv) {
-    for (int z = 0; z < 4; ++z) nv[z] = tot[tid][z];
-    R = nv[0] + nv[1] + nv[2] + nv[3];
-    wk = kw_s[tid];
-    qk = kq_s[tid];
-    ng = (R + 31) / 32;
-  }
-  const int64_t vw[4] = {nv[0] * gpr * 2, nv[1] * gpr * 4, nv[2] * gpr * 8, nv[3] * gpr * 16};
-  const int64_t vp[3] = {nv[0] * gpr, nv[1] * gpr, nv[2] * gpr};
-  uint64_t t_vi, t_vw, t_vp, t_kw, t_kp;
-  const int64_t o_vi = (int64_t)block_excl_scan<256>((uint64_t)R, &t_vi, sh);
-  const int64_t o_vw = (int64_t)block_excl_scan<256>((uint64_t)(vw[0] + vw[1] + vw[2] + vw[3]), &t_vw, sh);
-  const int64_t o_vp = (int64_t)block_excl_scan<256>((uint64_t)(vp[0] + vp[1] + vp[2]), &t_vp, sh);
-  const int64_t o_kw = (int64_t)block_excl_scan<256>((uint64_t)(ng * wk), &t_kw, sh);
-  const int64_t o_kp = (int64_t)block_excl_scan<256>((uint64_t)(ng * qk), &t_kp, sh);
-  if (tid == g) {
-    int64_t a = o_vi, b = o_vw, c = o_vp;
-    for (int z = 0; z < 4; ++z) {
-      hv[z] = nv[z];
-      hv[5 + z] = a;
-      hv[9 + z] = b;
-      hv[13 + z] = c;
-      a += nv[z];
-      b += vw[z];
-      c += (z < 3) ? vp[z] : 0;
+  if (wid == 0) {
+    // sizes of heads h < g (head g's offsets), and of all heads (the global header)
+    const bool all = ch == 0 && g == 0;
+    uint64_t s[5] = {0, 0, 0, 0, 0}, t[5] = {0, 0, 0, 0, 0};
+    for (int h = lane; h < Hkv; h += 64) {
+      const int64_t n0 = tot[h][0], n1 = tot[h][1], n2 = tot[h][2], n3 = tot[h][3];
+      const int64_t R = n0 + n1 + n2 + n3, ng = (R + 31) / 32;
+      const uint64_t v[5] = {(uint64_t)R, (uint64_t)((n0 * 2 + n1 * 4 + n2 * 8 + n3 * 16) * gpr),
+                             (uint64_t)((n0 + n1 + n2) * gpr), (uint64_t)(ng * kw_s[h]), (uint64_t)(ng * kq_s[h])};
+#pragma unroll
+      for (int u = 0; u < 5; ++u) {
+        if (h < g) s[u] += v[u];
+        t[u] += v[u];
+      }
     }
-    hv[4] = R;
-    hv[17] = o_vi;          // k_keep lists the same R tokens per head, in the same head order
-    hv[18] = o_kw;
-    hv[19] = o_kp;
-    hv[20] = wk;
-    hv[21] = qk;
-    hv[22] = ng;
-    hv[23] = 0;
-  }
-  if (ch == 0 && g == 0 && tid == 0) {
-    header[0] = Hkv;
-    header[1] = D;
-    header[2] = N;
-    header[3] = 32;
-    header[4] = (int64_t)t_vi;
-    header[5] = (int64_t)t_vw;
-    header[6] = (int64_t)t_vp;
-    header[7] = (int64_t)t_vi;
-    header[8] = (int64_t)t_kw;
-    header[9] = (int64_t)t_kp;
-    for (int i = 10; i < KVC_HDR_GLOBAL; ++i) header[i] = 0;
-    *status = bad_s ? KVC_DEV_BAD_WIDTH : 0;
+#pragma unroll
+    for (int u = 0; u < 5; ++u) s[u] = wave_sum_u64(s[u]);
+    if (all) {
+#pragma unroll
+      for (int u = 0; u < 5; ++u) t[u] = wave_sum_u64(t[u]);
+    }
+    if (lane == 0) {
+      const int64_t nv[4] = {tot[g][0], tot[g][1], tot[g][2], tot[g][3]};
+      const int64_t R = nv[0] + nv[1] + nv[2] + nv[3];
+      int64_t a = (int64_t)s[0], b = (int64_t)s[1], c = (int64_t)s[2];
+      for (int z = 0; z < 4; ++z) {
+        hv[z] = nv[z];
+        hv[5 + z] = a;
+        hv[9 + z] = b;
+        hv[13 + z] = c;
+        a += nv[z];
+        b += nv[z] * gpr * (2 << z);
+        c += (z < 3) ? nv[z] * gpr : 0;
+      }
+      hv[4] = R;
+      hv[17] = (int64_t)s[0];   // k_keep lists the same R tokens per head, in the same head order
+      hv[18] = (int64_t)s[3];
+      hv[19] = (int64_t)s[4];
+      hv[20] = kw_s[g];
+      hv[21] = kq_s[g];
+      hv[22] = (R + 31) / 32;
+      hv[23] = 0;
+      if (all) {
+        header[0] = Hkv;
+        header[1] = D;
+        header[2] = N;
+        header[3] = 32;
+        header[4] = (int64_t)t[0];
+        header[5] = (int64_t)t[1];
+        header[6] = (int64_t)t[2];
+        header[7] = (int64_t)t[0];
+        header[8] = (int64_t)t[3];
+        header[9] = (int64_t)t[4];
+        for (int i = 10; i < KVC_HDR_GLOBAL; ++i) header[i] = 0;
+        *status = bad_s ? KVC_DEV_BAD_WIDTH : 0;
+      }
+    }
+  } else if (wid == 1) {
+    // zone bases of this chunk: sums over the head's earlier chunks (32-bit fields)
+    uint64_t pa = 0, pb = 0;
+    for (int c2 = lane; c2 < ch; c2 += 64) {
+      const int4 c = *reinterpret_cast<const int4*>(cnt + ((int64_t)g * nchunk + c2) * 4);
+      pa += (uint32_t)c.x | ((uint64_t)(uint32_t)c.y << 32);
+      pb += (uint32_t)c.z | ((uint64_t)(uint32_t)c.w << 32);
+    }
+    pa = wave_sum_u64(pa);
+    pb = wave_sum_u64(pb);
+    if (lane == 0) {
+      bzs[0] = (int64_t)(pa & 0xFFFFFFFFu);
+      bzs[1] = (int64_t)(pa >> 32);
+      bzs[2] = (int64_t)(pb & 0xFFFFFFFFu);
+      bzs[3] = (int64_t)(pb >> 32);
+    }
+  } else if (wid == 2 && ch == 0) {
+    // head g's K channels: word offset and parameter slot inside a group (scan in channel order)
+    uint64_t carry = 0;
+    for (int c0 = 0; c0 < D; c0 += 64) {
+      const int c = c0 + lane;
+      const uint32_t bk = bits_k[(int64_t)g * D + c];
+      k_width[(int64_t)g * D + c] = (uint8_t)bk;
+      const int cls = zone_of(bk);
+      const uint64_t f = cls >= 0 ? ((uint64_t)bk | ((uint64_t)(cls < 3) << 16)) : 0;
+      const uint64_t inc = wave_incl_scan_u64(f, lane);
+      const uint64_t ef = carry + inc - f;
+      *reinterpret_cast<int4*>(kchc + ((int64_t)g * D + c) * 4) =
+          make_int4((int32_t)(ef & 0xFFFF), (int32_t)((ef >> 16) & 0xFFFF), f ? (int32_t)bk : 0, 0);
+      carry += __shfl(inc, 63, 64);
+    }
   }
   __syncthreads();
-  if (ch == 0) {
-    if (tid < KVC_HDR_PER_HEAD) header[KVC_HDR_GLOBAL + g * KVC_HDR_PER_HEAD + tid] = hv[tid];
-    // head g's K channels: word offset and parameter slot inside a group (scan in channel order)
-    uint32_t bk = 0;
-    uint64_t f = 0;
-    if (tid < D) {
-      bk = bits_k[(int64_t)g * D + tid];
-      k_width[(int64_t)g * D + tid] = (uint8_t)bk;
-      const int cls = zone_of(bk);
-      if (cls >= 0) f = (uint64_t)bk | ((uint64_t)(cls < 3) << 16);
-    }
-    uint64_t tf;
-    const uint64_t ef = block_excl_scan<256>(f, &tf, sh);
-    if (tid < D)
-      *reinterpret_cast<int4*>(kchc + ((int64_t)g * D + tid) * 4) =
-          make_int4((int32_t)(ef & 0xFFFF), (int32_t)((ef >> 16) & 0xFFFF), f ? (int32_t)bk : 0, 0);
-  }
-
-  // zone bases of this chunk: sums over the head's earlier chunks (32-bit fields)
-  uint64_t pa = 0, pb = 0;
-  for (int c2 = tid; c2 < ch; c2 += 256) {
-    const int4 c = *reinterpret_cast<const int4*>(cnt + ((int64_t)g * nchunk + c2) * 4);
-    pa += (uint32_t)c.x | ((uint64_t)(uint32_t)c.y << 32);
-    pb += (uint32_t)c.z | ((uint64_t)(uint32_t)c.w << 32);
-  }
-  uint64_t sa, sb;
-  block_excl_scan<256>(pa, &sa, sh);
-  block_excl_scan<256>(pb, &sb, sh);
-  const int64_t bz[4] = {(int64_t)(sa & 0xFFFFFFFFu), (int64_t)(sa >> 32), (int64_t)(sb & 0xFFFFFFFFu),
-                         (int64_t)(sb >> 32)};
+  if (ch == 0 && tid < KVC_HDR_PER_HEAD) header[KVC_HDR_GLOBAL + g * KVC_HDR_PER_HEAD + tid] = hv[tid];
 
   // ordered ranks of the chunk's tokens
-  const int64_t t0 = (int64_t)ch * kChunk + tid * 4;
   int z4[4];
   uint64_t mine = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int64_t t = t0 + j;
-    z4[j] = (t < N) ? zone_of(bits_v[(int64_t)g * N + t]) : -1;
+    z4[j] = (t0 + j < N) ? zone_of((b4 >> (8 * j)) & 0xFFu) : -1;
     if (z4[j] >= 0) mine += 1ull << (16 * z4[j]);
   }
   uint64_t total;
   uint64_t run = block_excl_scan<256>(mine, &total, sh);
+  const int64_t bz[4] = {bzs[0], bzs[1], bzs[2], bzs[3]};
   const int64_t kbase = hv[17] + bz[0] + bz[1] + bz[2] + bz[3];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
