@@ -7,8 +7,8 @@
 //   row LSE        the scorer's pass 1 over the n keys                          (score.hip)
 //   ridge_probs    P[r][t] = exp(s q_r . k_t - l_r), fp32, 64 x 64 tiles, VALU dot products
 //   ridge_resid    T = Y - P_r V_r (fp32), 64 x 64 tiles over (rows, channels)
-//   ridge_gram     M = P_c^T P_c and B = P_c^T T, fp64 sums of fp32 products (exact), the row
-//                  sum split in kSplit fixed parts
+//   ridge_gram     M = P_c^T P_c and B = P_c^T T on the fp64 matrix cores (each product of two
+//                  fp32 values is exact in fp64), the row sum split in kSplit fixed parts
 //   ridge_sum      M += lambda I (identity on the padding), the parts added in fixed order
 //   ridge_chol     blocked Cholesky (32-wide blocks), one launch per block column kb: every tile
 //                  (i, j) of the trailing matrix computes L_ik = A_ik L_kk^-T itself, subtracts
@@ -219,13 +219,19 @@ ridge_resid(const float* __restrict__ P, const uint16_t* __restrict__ v_r, const
 }
 
 // Gram products over the rows of part s: tile (a-tile, b-tile) of M = P_c^T P_c (lower tiles),
-// or tile (a-tile, channel tile) of B = P_c^T T.  fp32 inputs, fp64 products and sums.
+// or tile (a-tile, channel tile) of B = P_c^T T.  fp32 inputs staged in LDS as fp64, products and
+// sums on the fp64 matrix cores (v_mfma_f64_16x16x4f64: A[i][k] from lane i + 16k, B[k][j] from
+// lane j + 16k, D[i][j] in lane j + 16 (i % 4), register i / 4).  Wave w owns the 16 tile rows
+// 16w .. 16w+15 and all 64 columns (four 16 x 16 accumulators); each step of 4 staged rows is
+// one A fragment, four B fragments and four MFMAs per wave, in a fixed order.
+typedef double v4d __attribute__((ext_vector_type(4)));
+
 template <int D>
 __global__ void __launch_bounds__(256)
 ridge_gram(const float* __restrict__ P, const float* __restrict__ T, double* __restrict__ Mp,
            double* __restrict__ Bp, RidgeDims r) {
-  __shared__ double xs[32][kT];
-  __shared__ double zs[32][kT];
+  __shared__ double xs[32][kT + 1];
+  __shared__ double zs[32][kT + 1];
   const int s = blockIdx.y, g = blockIdx.z;
   const int nt = r.nt;
   const int nlow = nt * (nt + 1) / 2;
@@ -246,54 +252,65 @@ ridge_gram(const float* __restrict__ P, const float* __restrict__ T, double* __r
   const int64_t a0 = (int64_t)ia * kT, b0 = (int64_t)ib * kT;
   const int64_t rs = (r.R + kSplit - 1) / kSplit;
   const int64_t rbeg = s * rs, rend = (s + 1) * rs < r.R ? (s + 1) * rs : r.R;
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  double acc[4][4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int li = lane & 15, lk = lane >> 4;
+  v4d acc[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+  for (int q = 0; q < 4; ++q) acc[q] = (v4d){0.0, 0.0, 0.0, 0.0};
   const float* Pg = P + (int64_t)g * r.R * r.n;
   const float* Tg = T + (int64_t)g * r.R * D;
-  for (int64_t q0 = rbeg; q0 < rend; q0 += 32) {
-    for (int e = tid; e < 32 * kT; e += 256) {
+  // the next chunk's values are loaded into registers while the matrix cores work on this one
+  constexpr int kPer = 32 * kT / 256;               // values per thread per chunk and array
+  float px[kPer], pz[kPer];
+  auto fetch = [&](int64_t q0) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = tid + 256 * u;
       const int rr = e / kT, col = e % kT;
       const int64_t row = q0 + rr;
       const bool rv = row < rend;
-      const int64_t a = a0 + col;
-      xs[rr][col] = (rv && a < r.nc) ? (double)Pg[row * r.n + a] : 0.0;
-      const int64_t b = b0 + col;
-      double z = 0.0;
-      if (rv) z = isB ? (double)Tg[row * D + b] : (b < r.nc ? (double)Pg[row * r.n + b] : 0.0);
-      zs[rr][col] = z;
+      const int64_t a = a0 + col, b = b0 + col;
+      px[u] = (rv && a < r.nc) ? Pg[row * r.n + a] : 0.f;
+      pz[u] = rv ? (isB ? Tg[row * D + b] : (b < r.nc ? Pg[row * r.n + b] : 0.f)) : 0.f;
+    }
+  };
+  if (rbeg < rend) fetch(rbeg);
+  for (int64_t q0 = rbeg; q0 < rend; q0 += 32) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = tid + 256 * u;
+      xs[e / kT][e % kT] = (double)px[u];
+      zs[e / kT][e % kT] = (double)pz[u];
     }
     __syncthreads();
-#pragma unroll 4
-    for (int rr = 0; rr < 32; ++rr) {
-      double av[4], bv[4];
+    if (q0 + 32 < rend) fetch(q0 + 32);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = xs[rr][ty * 4 + i];
+    for (int k0 = 0; k0 < 32; k0 += 4) {
+      const double av = xs[k0 + lk][16 * w + li];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bv[j] = zs[rr][tx * 4 + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(av[i], bv[j], acc[i][j]);
+      for (int q = 0; q < 4; ++q) {
+        const double bv = zs[k0 + lk][16 * q + li];
+        acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[q], 0, 0, 0);
+      }
     }
     __syncthreads();
   }
+  double* dst;
+  int64_t ld;
   if (!isB) {
-    double* dst = Mp + ((int64_t)s * r.hkv + g) * r.npad * r.npad;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dst[(a0 + ty * 4 + i) * r.npad + b0 + tx * 4 + j] = acc[i][j];
+    dst = Mp + ((int64_t)s * r.hkv + g) * r.npad * r.npad + a0 * r.npad + b0;
+    ld = r.npad;
   } else {
-    double* dst = Bp + ((int64_t)s * r.hkv + g) * r.npad * D;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dst[(a0 + ty * 4 + i) * D + b0 + tx * 4 + j] = acc[i][j];
+    dst = Bp + ((int64_t)s * r.hkv + g) * r.npad * D + a0 * D + b0;
+    ld = D;
   }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int reg = 0; reg < 4; ++reg) {
+      const int i = 16 * w + 4 * reg + lk, j = 16 * q + li;
+      dst[(int64_t)i * ld + j] = acc[q][reg];
+    }
 }
 
 // M = sum of the parts + lambda I (1 on the padded diagonal) over the lower tiles; B likewise.
