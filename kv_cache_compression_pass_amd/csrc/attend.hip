@@ -31,12 +31,12 @@ constexpr int kRows = 32;   // query rows per wave
 
 template <int D>
 struct AttnSmem {
-  uint16_t khi[32][D + 8];
-  uint16_t klo[32][D + 8];
-  _Float16 vt[D][32 + 8];
+  uint16_t khi[2][32][D + 8];   // two buffers: group j is decoded into buffer j & 1
+  uint16_t klo[2][32][D + 8];
+  _Float16 vt[2][D][32 + 8];
+  int32_t tok[2][32];
   int32_t kinfo[D][4];     // channels in width order: {channel, word offset, param slot, width}
-  int32_t tok[32];
-  int32_t vloc[32];
+  int64_t vzone[4][2];     // V zones by width class: first word, first (scale, zero) pair
   uint64_t scan[kWaves];
 };
 
@@ -124,6 +124,10 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
       sm.kinfo[pos][2] = (int32_t)((ef >> 16) & 0xFFFF);
       sm.kinfo[pos][3] = cls < 4 ? (int32_t)b : 0;
     }
+    if (t < 4) {
+      sm.vzone[t][0] = hp[9 + t];
+      sm.vzone[t][1] = hp[13 + t];
+    }
   }
 
   // Q^T operand of this wave's rows
@@ -156,109 +160,169 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
 
   __syncthreads();
   const int4 kinf = *reinterpret_cast<const int4*>(sm.kinfo[threadIdx.x % D]);   // this thread's K channel
-  for (int64_t j = j_begin; j < j_end_raw; ++j) {
-    const int m_valid = (int)((R - j * 32) < 32 ? (R - j * 32) : 32);
-    if (threadIdx.x < 32) {
-      const int e = threadIdx.x;
-      sm.tok[e] = e < m_valid ? cache.k_keep[hp[17] + j * 32 + e] : 0x7FFFFFFF;
-      sm.vloc[e] = e < m_valid ? cache.k_vloc[hp[17] + j * 32 + e] : 0;
+  // K decode task: channel kinf.x (width kb), tokens ke0 .. ke0 + KE - 1 of the group
+  const int kb = kinf.w;
+  const int ke0 = (threadIdx.x / D) * KE;
+  const int kbit0 = ke0 * kb;                  // KE * kb <= 64 bits from kbit0
+  const bool ktwo = (kbit0 & 31) + KE * kb > 32;
+  // V decode task: token ve, 32-channel group vgrp, channels vc0 .. vc0 + VE - 1
+  const int ve = threadIdx.x / (GPR * VP);
+  const int vgrp = (threadIdx.x / VP) % GPR;
+  const int vc0 = (threadIdx.x % VP) * VE;
+  // header fields used in the loop, read once (the zone bases sit in LDS)
+  const int64_t slot0 = hp[17];                // the head's first retained-token slot
+  const int64_t kword0 = hp[18], kpar0 = hp[19];
+
+  // The global words of group j+1 (and the V locations of group j+2) are requested while
+  // group j is in LDS, so their latency overlaps the products of group j.
+  auto m_valid_of = [&](int64_t j) { return (int)((R - j * 32) < 32 ? (R - j * 32) : 32); };
+  auto load_k = [&](int64_t j, uint32_t (&w)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = 0u;
+    if (kb == 0) return;
+    const uint32_t* wp = cache.k_words + kword0 + j * Wk + kinf.y;
+    if (kb == 16) {                            // raw bf16: KE / 2 words
+#pragma unroll
+      for (int k = 0; k < KE / 2; ++k) w[k] = wp[(ke0 >> 1) + k];
+    } else {
+      w[0] = wp[kbit0 >> 5];
+      if (ktwo) w[1] = wp[(kbit0 >> 5) + 1];
+      const float2 sz = *reinterpret_cast<const float2*>(cache.k_par + 2 * (kpar0 + j * Qk + kinf.z));
+      w[2] = __float_as_uint(sz.x);
+      w[3] = __float_as_uint(sz.y);
     }
-    __syncthreads();
-    if (sm.tok[0] > pmax_block) break;      // retained tokens ascend: nothing visible later
-    // ---- decode K_hat: thread -> (channel in width order, run of KE tokens)
+  };
+  auto load_vloc = [&](int64_t j) -> int32_t {   // -1 past the retained tokens
+    return (j * 32 + ve < R) ? cache.k_vloc[slot0 + j * 32 + ve] : -1;
+  };
+  auto load_v = [&](int32_t loc, uint32_t (&w)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = 0u;
+    if (loc < 0) return;
+    const int z = loc >> 29;
+    const int64_t vpos = loc & ((1 << 29) - 1);
+    const int b = 2 << z;
+    const uint32_t* wp = cache.v_words + sm.vzone[z][0] + (vpos * GPR + vgrp) * b;
+    if (b == 16) {                             // raw bf16: VE / 2 words
+#pragma unroll
+      for (int k = 0; k < VE / 2; ++k) w[k] = wp[(vc0 >> 1) + k];
+    } else {
+      const int bit0 = vc0 * b;                // VE * b <= 64 bits from bit0
+      w[0] = wp[bit0 >> 5];
+      if ((bit0 & 31) + VE * b > 32) w[1] = wp[(bit0 >> 5) + 1];
+      const float2 sz = *reinterpret_cast<const float2*>(cache.v_par + 2 * (sm.vzone[z][1] + vpos * GPR + vgrp));
+      w[2] = __float_as_uint(sz.x);
+      w[3] = __float_as_uint(sz.y);
+    }
+  };
+  auto load_tok = [&](int64_t j) -> int32_t {    // slots past the group's end hold the sentinel
+    const int e = threadIdx.x & 31;
+    return (threadIdx.x < 32 && e < m_valid_of(j)) ? cache.k_keep[slot0 + j * 32 + e] : 0x7FFFFFFF;
+  };
+
+  uint32_t kw[4] = {0u, 0u, 0u, 0u}, vw[4] = {0u, 0u, 0u, 0u};
+  int32_t vl = -1, vl_next = -1, tok = 0x7FFFFFFF;
+  int32_t tfirst = 0;                          // the group's first token (32-bit, as stored)
+  if (j_begin < j_end_raw) {
+    vl = load_vloc(j_begin);
+    load_k(j_begin, kw);
+    tok = load_tok(j_begin);
+    tfirst = cache.k_keep[slot0 + j_begin * 32];
+    load_v(vl, vw);
+    vl_next = load_vloc(j_begin + 1);
+  }
+  for (int64_t j = j_begin; j < j_end_raw; ++j) {
+    if ((int64_t)tfirst > pmax_block) break;   // retained tokens ascend: nothing visible later
+    const int buf = (int)(j & 1);
+    const int m_valid = m_valid_of(j);
+    // ---- decode K_hat of group j into buffer buf
     {
-      const int cc = kinf.x, b = kinf.w;
-      const int e0 = (threadIdx.x / D) * KE;
       uint32_t hl2[KE];
-      if (b == 0) {
+      if (kb == 0) {
 #pragma unroll
         for (int k = 0; k < KE; ++k) hl2[k] = 0u;
+      } else if (kb == 16) {                   // lo = 0
+#pragma unroll
+        for (int k = 0; k < KE; ++k) hl2[k] = (kw[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
       } else {
-        const uint32_t* wp = cache.k_words + hp[18] + j * Wk + kinf.y;
-        if (b == 16) {                       // raw bf16 (lo = 0): KE / 2 words
+        const uint64_t win = ((uint64_t)kw[0] | ((uint64_t)kw[1] << 32)) >> (kbit0 & 31);
+        const float sc = __uint_as_float(kw[2]), zp = __uint_as_float(kw[3]);
+        const uint32_t mask = (1u << kb) - 1u;
 #pragma unroll
-          for (int k = 0; k < KE; k += 2) {
-            const uint32_t w = wp[(e0 + k) >> 1];
-            hl2[k] = w & 0xFFFFu;
-            hl2[k + 1] = w >> 16;
-          }
-        } else {
-          const int bit0 = e0 * b;             // KE * b <= 64 bits from bit0
-          const uint64_t win = load_window(wp, bit0 >> 5, (bit0 & 31) + KE * b > 32) >> (bit0 & 31);
-          const float2 sz = *reinterpret_cast<const float2*>(cache.k_par + 2 * (hp[19] + j * Qk + kinf.z));
-          const uint32_t mask = (1u << b) - 1u;
-#pragma unroll
-          for (int k = 0; k < KE; ++k) {
-            const uint32_t code = (uint32_t)(win >> (k * b)) & mask;
-            hl2[k] = bf16_hilo(fmaf(sz.x, (float)code, sz.y));
-          }
+        for (int k = 0; k < KE; ++k) {
+          const uint32_t code = (uint32_t)(win >> (k * kb)) & mask;
+          hl2[k] = bf16_hilo(fmaf(sc, (float)code, zp));
         }
       }
+      const int cc = kinf.x;
 #pragma unroll
       for (int k = 0; k < KE; ++k) {
-        sm.khi[e0 + k][cc] = (uint16_t)(hl2[k] & 0xFFFFu);
-        sm.klo[e0 + k][cc] = (uint16_t)(hl2[k] >> 16);
+        sm.khi[buf][ke0 + k][cc] = (uint16_t)(hl2[k] & 0xFFFFu);
+        sm.klo[buf][ke0 + k][cc] = (uint16_t)(hl2[k] >> 16);
       }
     }
-    // ---- decode V_hat^T: thread -> (token e, 32-channel group, run of VE channels)
+    // ---- decode V_hat^T of group j into buffer buf
     {
-      const int task = threadIdx.x;
-      const int e = task / (GPR * VP);
-      const int grp = (task / VP) % GPR;
-      const int c0 = (task % VP) * VE;
       _Float16 vv[VE];
-      if (e >= m_valid) {
+      if (vl < 0) {
 #pragma unroll
         for (int k = 0; k < VE; ++k) vv[k] = (_Float16)0.f;
       } else {
-        const int32_t loc = sm.vloc[e];
-        const int z = loc >> 29;
-        const int64_t vpos = loc & ((1 << 29) - 1);
-        const int b = 2 << z;
-        const uint32_t* wp = cache.v_words + hp[9 + z] + (vpos * GPR + grp) * b;
-        if (b == 16) {                       // raw bf16: VE / 2 words
+        const int b = 2 << (vl >> 29);
+        if (b == 16) {
 #pragma unroll
           for (int k = 0; k < VE; k += 2) {
-            const uint32_t w = wp[(c0 + k) >> 1];
-            vv[k] = (_Float16)bf16_bits_to_f32(w & 0xFFFFu);
-            vv[k + 1] = (_Float16)bf16_bits_to_f32(w >> 16);
+            vv[k] = (_Float16)bf16_bits_to_f32(vw[k >> 1] & 0xFFFFu);
+            vv[k + 1] = (_Float16)bf16_bits_to_f32(vw[k >> 1] >> 16);
           }
         } else {
-          const int bit0 = c0 * b;             // VE * b <= 64 bits from bit0
-          const uint64_t win = load_window(wp, bit0 >> 5, (bit0 & 31) + VE * b > 32) >> (bit0 & 31);
-          const float2 sz = *reinterpret_cast<const float2*>(cache.v_par + 2 * (hp[13 + z] + vpos * GPR + grp));
+          const int bit0 = vc0 * b;
+          const uint64_t win = ((uint64_t)vw[0] | ((uint64_t)vw[1] << 32)) >> (bit0 & 31);
+          const float sc = __uint_as_float(vw[2]), zp = __uint_as_float(vw[3]);
           const uint32_t mask = (1u << b) - 1u;
 #pragma unroll
-          for (int k = 0; k < VE; ++k)
-            vv[k] = (_Float16)fmaf(sz.x, (float)((uint32_t)(win >> (k * b)) & mask), sz.y);
+          for (int k = 0; k < VE; ++k) vv[k] = (_Float16)fmaf(sc, (float)((uint32_t)(win >> (k * b)) & mask), zp);
         }
       }
 #pragma unroll
-      for (int k = 0; k < VE; ++k) sm.vt[grp * 32 + c0 + k][e] = vv[k];
+      for (int k = 0; k < VE; ++k) sm.vt[buf][vgrp * 32 + vc0 + k][ve] = vv[k];
     }
+    if (threadIdx.x < 32) sm.tok[buf][threadIdx.x] = tok;
+    // ---- requests for group j + 1, issued after the decode of group j so that they stay in
+    // flight through the barrier and the products of group j
+    uint32_t kw_n[4] = {0u, 0u, 0u, 0u}, vw_n[4] = {0u, 0u, 0u, 0u};
+    int32_t vl_nn = -1, tok_n = 0x7FFFFFFF, tfirst_n = 0;
+    if (j + 1 < j_end_raw) {
+      load_k(j + 1, kw_n);
+      tok_n = load_tok(j + 1);
+      tfirst_n = cache.k_keep[slot0 + (j + 1) * 32];
+      load_v(vl_next, vw_n);
+      vl_nn = load_vloc(j + 2);
+    }
+    // One barrier per group: a wave that reaches it has finished the products of group j-1,
+    // the last reader of the buffer that group j+1 will be decoded into.
     __syncthreads();
-    const int64_t t_first = sm.tok[0];
-    if (active && (!causal || t_first <= off + r0 + kRows - 1)) {
+    if (active && (!causal || (int64_t)tfirst <= off + r0 + kRows - 1)) {
       f32x16 acc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 ah = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.khi[lo][ks * 16 + 8 * hi]));
-        bf16x8 al = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.klo[lo][ks * 16 + 8 * hi]));
+        bf16x8 ah = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.khi[buf][lo][ks * 16 + 8 * hi]));
+        bf16x8 al = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.klo[buf][lo][ks * 16 + 8 * hi]));
         acc = mfma32(ah, qb[ks], acc);
         acc = mfma32(al, qb[ks], acc);
       }
       float x[16];
       float tmax = -INFINITY;
-      const bool full = m_valid == 32 && (!causal || sm.tok[31] <= off + r0);   // uniform per wave
+      const bool full = m_valid == 32 && (!causal || sm.tok[buf][31] <= off + r0);   // uniform per wave
 #pragma unroll
       for (int i = 0; i < 16; ++i) x[i] = acc[i] * c;
       if (!full) {
         // slots past m_valid hold the sentinel 0x7FFFFFFF, so one compare covers both masks
         const int lim = causal ? (int)pos : 0x7FFFFFFE;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = (sm.tok[acc_row(i, hi)] <= lim) ? x[i] : -INFINITY;
+        for (int i = 0; i < 16; ++i) x[i] = (sm.tok[buf][acc_row(i, hi)] <= lim) ? x[i] : -INFINITY;
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, x[i]);
@@ -280,10 +344,12 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
 #pragma unroll
         for (int i = 0; i < 16; ++i) p[i] = 0.f;
       }
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {   // no row of the wave moved its max: skip
 #pragma unroll
-      for (int mb = 0; mb < GPR; ++mb)
+        for (int mb = 0; mb < GPR; ++mb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[mb][i] *= alpha;
+          for (int i = 0; i < 16; ++i) o[mb][i] *= alpha;
+      }
       // O^T[ch][row] += sum_key V^T[ch][key] P^T[key][row], keys in the accumulator's order
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2) {
@@ -293,7 +359,7 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
         const int kbase = 16 * ks2 + 4 * hi;
 #pragma unroll
         for (int mb = 0; mb < GPR; ++mb) {
-          const _Float16* vr = &sm.vt[mb * 32 + lo][0];
+          const _Float16* vr = &sm.vt[buf][mb * 32 + lo][0];
           f16x8 va;
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
@@ -304,7 +370,15 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
         }
       }
     }
-    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      kw[k] = kw_n[k];
+      vw[k] = vw_n[k];
+    }
+    vl = vl_next;
+    vl_next = vl_nn;
+    tok = tok_n;
+    tfirst = tfirst_n;
   }
 
   if (!active) return;
