@@ -64,8 +64,8 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
   constexpr int PSTRIDE = D + 2;
   constexpr int KP = kThreadsA / D;        // K decode: threads per channel
   constexpr int KE = 32 / KP;              // K decode: tokens per thread (8 or 4)
-  constexpr int VP = kThreadsA / (32 * GPR);   // V decode: threads per (token, group)
-  constexpr int VE = 32 / VP;              // V decode: channels per thread (8)
+  constexpr int VC = GPR;                  // V decode: channels per thread, for 2 tokens
+  constexpr int VRUNS = 32 / VC;           // V decode: channel runs per 32-channel group
   __shared__ AttnSmem<D> sm;
 
   const int lane = threadIdx.x & 63;
@@ -165,10 +165,13 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
   const int ke0 = (threadIdx.x / D) * KE;
   const int kbit0 = ke0 * kb;                  // KE * kb <= 64 bits from kbit0
   const bool ktwo = (kbit0 & 31) + KE * kb > 32;
-  // V decode task: token ve, 32-channel group vgrp, channels vc0 .. vc0 + VE - 1
-  const int ve = threadIdx.x / (GPR * VP);
-  const int vgrp = (threadIdx.x / VP) % GPR;
-  const int vc0 = (threadIdx.x % VP) * VE;
+  // V decode task: tokens 2 vtp and 2 vtp + 1, 32-channel group vgrp, channels vc0 .. vc0 + VC - 1.
+  // The four 16-lane quarters of a wave take consecutive runs of one group, so a wave's
+  // 32-bit stores of a token pair into V_hat^T land in distinct LDS banks.
+  const int vtp = threadIdx.x & 15;
+  const int vr = threadIdx.x >> 4;
+  const int vgrp = vr / VRUNS;
+  const int vc0 = (vr % VRUNS) * VC;
   // header fields used in the loop, read once (the zone bases sit in LDS)
   const int64_t slot0 = hp[17];                // the head's first retained-token slot
   const int64_t kword0 = hp[18], kpar0 = hp[19];
@@ -192,9 +195,15 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
       w[3] = __float_as_uint(sz.y);
     }
   };
-  auto load_vloc = [&](int64_t j) -> int32_t {   // -1 past the retained tokens
-    return (j * 32 + ve < R) ? cache.k_vloc[slot0 + j * 32 + ve] : -1;
+  auto load_vloc = [&](int64_t j, int32_t (&vl)[2]) {   // -1 past the retained tokens
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t e = j * 32 + 2 * vtp + u;
+      vl[u] = (e < R) ? cache.k_vloc[slot0 + e] : -1;
+    }
   };
+  // One token's VC channels: VC * b bits, aligned to their own size, so one word (two at
+  // 16 bits, VC = 4), and the row's (scale, zero) pair.
   auto load_v = [&](int32_t loc, uint32_t (&w)[4]) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) w[k] = 0u;
@@ -202,14 +211,11 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
     const int z = loc >> 29;
     const int64_t vpos = loc & ((1 << 29) - 1);
     const int b = 2 << z;
-    const uint32_t* wp = cache.v_words + sm.vzone[z][0] + (vpos * GPR + vgrp) * b;
-    if (b == 16) {                             // raw bf16: VE / 2 words
-#pragma unroll
-      for (int k = 0; k < VE / 2; ++k) w[k] = wp[(vc0 >> 1) + k];
-    } else {
-      const int bit0 = vc0 * b;                // VE * b <= 64 bits from bit0
-      w[0] = wp[bit0 >> 5];
-      if ((bit0 & 31) + VE * b > 32) w[1] = wp[(bit0 >> 5) + 1];
+    const uint32_t* wp = cache.v_words + sm.vzone[z][0] + (vpos * GPR + vgrp) * b + ((vc0 * b) >> 5);
+    w[0] = wp[0];
+    if (VC * b > 32) {
+      w[1] = wp[1];
+    } else if (b != 16) {
       const float2 sz = *reinterpret_cast<const float2*>(cache.v_par + 2 * (sm.vzone[z][1] + vpos * GPR + vgrp));
       w[2] = __float_as_uint(sz.x);
       w[3] = __float_as_uint(sz.y);
@@ -220,16 +226,17 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
     return (threadIdx.x < 32 && e < m_valid_of(j)) ? cache.k_keep[slot0 + j * 32 + e] : 0x7FFFFFFF;
   };
 
-  uint32_t kw[4] = {0u, 0u, 0u, 0u}, vw[4] = {0u, 0u, 0u, 0u};
-  int32_t vl = -1, vl_next = -1, tok = 0x7FFFFFFF;
+  uint32_t kw[4] = {0u, 0u, 0u, 0u}, vw[2][4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+  int32_t vl[2] = {-1, -1}, vl_next[2] = {-1, -1}, tok = 0x7FFFFFFF;
   int32_t tfirst = 0;                          // the group's first token (32-bit, as stored)
   if (j_begin < j_end_raw) {
-    vl = load_vloc(j_begin);
+    load_vloc(j_begin, vl);
     load_k(j_begin, kw);
     tok = load_tok(j_begin);
     tfirst = cache.k_keep[slot0 + j_begin * 32];
-    load_v(vl, vw);
-    vl_next = load_vloc(j_begin + 1);
+    load_v(vl[0], vw[0]);
+    load_v(vl[1], vw[1]);
+    load_vloc(j_begin + 1, vl_next);
   }
   for (int64_t j = j_begin; j < j_end_raw; ++j) {
     if ((int64_t)tfirst > pmax_block) break;   // retained tokens ascend: nothing visible later
@@ -261,58 +268,67 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
         sm.klo[buf][ke0 + k][cc] = (uint16_t)(hl2[k] >> 16);
       }
     }
-    // ---- decode V_hat^T of group j into buffer buf
+    // ---- decode V_hat^T of group j into buffer buf (tokens 2 vtp and 2 vtp + 1 side by side)
     {
-      _Float16 vv[VE];
-      if (vl < 0) {
+      uint32_t vv[2][VC];                      // fp16 bits
 #pragma unroll
-        for (int k = 0; k < VE; ++k) vv[k] = (_Float16)0.f;
-      } else {
-        const int b = 2 << (vl >> 29);
-        if (b == 16) {
+      for (int u = 0; u < 2; ++u) {
+        if (vl[u] < 0) {
 #pragma unroll
-          for (int k = 0; k < VE; k += 2) {
-            vv[k] = (_Float16)bf16_bits_to_f32(vw[k >> 1] & 0xFFFFu);
-            vv[k + 1] = (_Float16)bf16_bits_to_f32(vw[k >> 1] >> 16);
-          }
+          for (int k = 0; k < VC; ++k) vv[u][k] = 0u;
         } else {
-          const int bit0 = vc0 * b;
-          const uint64_t win = ((uint64_t)vw[0] | ((uint64_t)vw[1] << 32)) >> (bit0 & 31);
-          const float sc = __uint_as_float(vw[2]), zp = __uint_as_float(vw[3]);
-          const uint32_t mask = (1u << b) - 1u;
+          const int b = 2 << (vl[u] >> 29);
+          if (b == 16) {
 #pragma unroll
-          for (int k = 0; k < VE; ++k) vv[k] = (_Float16)fmaf(sc, (float)((uint32_t)(win >> (k * b)) & mask), zp);
+            for (int k = 0; k < VC; ++k) {
+              const _Float16 h = (_Float16)bf16_bits_to_f32((vw[u][k >> 1] >> (16 * (k & 1))) & 0xFFFFu);
+              vv[u][k] = __builtin_bit_cast(uint16_t, h);
+            }
+          } else {
+            const uint32_t win = vw[u][0] >> ((vc0 * b) & 31);
+            const float sc = __uint_as_float(vw[u][2]), zp = __uint_as_float(vw[u][3]);
+            const uint32_t mask = (1u << b) - 1u;
+#pragma unroll
+            for (int k = 0; k < VC; ++k) {
+              const _Float16 h = (_Float16)fmaf(sc, (float)((win >> (k * b)) & mask), zp);
+              vv[u][k] = __builtin_bit_cast(uint16_t, h);
+            }
+          }
         }
       }
 #pragma unroll
-      for (int k = 0; k < VE; ++k) sm.vt[buf][vgrp * 32 + vc0 + k][ve] = vv[k];
+      for (int k = 0; k < VC; ++k)
+        *reinterpret_cast<uint32_t*>(&sm.vt[buf][vgrp * 32 + vc0 + k][2 * vtp]) = vv[0][k] | (vv[1][k] << 16);
     }
     if (threadIdx.x < 32) sm.tok[buf][threadIdx.x] = tok;
     // ---- requests for group j + 1, issued after the decode of group j so that they stay in
     // flight through the barrier and the products of group j
-    uint32_t kw_n[4] = {0u, 0u, 0u, 0u}, vw_n[4] = {0u, 0u, 0u, 0u};
-    int32_t vl_nn = -1, tok_n = 0x7FFFFFFF, tfirst_n = 0;
+    uint32_t kw_n[4] = {0u, 0u, 0u, 0u}, vw_n[2][4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    int32_t vl_nn[2] = {-1, -1}, tok_n = 0x7FFFFFFF, tfirst_n = 0;
     if (j + 1 < j_end_raw) {
       load_k(j + 1, kw_n);
       tok_n = load_tok(j + 1);
       tfirst_n = cache.k_keep[slot0 + (j + 1) * 32];
-      load_v(vl_next, vw_n);
-      vl_nn = load_vloc(j + 2);
+      load_v(vl_next[0], vw_n[0]);
+      load_v(vl_next[1], vw_n[1]);
+      load_vloc(j + 2, vl_nn);
     }
     // One barrier per group: a wave that reaches it has finished the products of group j-1,
     // the last reader of the buffer that group j+1 will be decoded into.
     __syncthreads();
     if (active && (!causal || (int64_t)tfirst <= off + r0 + kRows - 1)) {
-      f32x16 acc;
+      f32x16 acc, acc_lo;                      // q.hi and q.lo in two chains, added at the end
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+      for (int i = 0; i < 16; ++i) acc[i] = acc_lo[i] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         bf16x8 ah = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.khi[buf][lo][ks * 16 + 8 * hi]));
         bf16x8 al = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.klo[buf][lo][ks * 16 + 8 * hi]));
         acc = mfma32(ah, qb[ks], acc);
-        acc = mfma32(al, qb[ks], acc);
+        acc_lo = mfma32(al, qb[ks], acc_lo);
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] += acc_lo[i];
       float x[16];
       float tmax = -INFINITY;
       const bool full = m_valid == 32 && (!causal || sm.tok[buf][31] <= off + r0);   // uniform per wave
@@ -373,10 +389,14 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       kw[k] = kw_n[k];
-      vw[k] = vw_n[k];
+      vw[0][k] = vw_n[0][k];
+      vw[1][k] = vw_n[1][k];
     }
-    vl = vl_next;
-    vl_next = vl_nn;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      vl[u] = vl_next[u];
+      vl_next[u] = vl_nn[u];
+    }
     tok = tok_n;
     tfirst = tfirst_n;
   }
