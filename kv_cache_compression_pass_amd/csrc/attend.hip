@@ -226,97 +226,101 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
     return (threadIdx.x < 32 && e < m_valid_of(j)) ? cache.k_keep[slot0 + j * 32 + e] : 0x7FFFFFFF;
   };
 
-  uint32_t kw[4] = {0u, 0u, 0u, 0u}, vw[2][4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-  int32_t vl[2] = {-1, -1}, vl_next[2] = {-1, -1}, tok = 0x7FFFFFFF;
-  int32_t tfirst = 0;                          // the group's first token (32-bit, as stored)
+  // Decode of one group from its raw words into LDS buffer `bf`, without branches (every lane
+  // runs the same instructions, so the products of the previous group can interleave).
+  auto decode_k = [&](const uint32_t (&w)[4], int bf) {
+    const int kq = kb < 16 ? kb : 0;           // quantised width (0 for raw and evicted channels)
+    const uint64_t win = ((uint64_t)w[0] | ((uint64_t)w[1] << 32)) >> (kbit0 & 31);
+    const float sc = __uint_as_float(w[2]), zp = __uint_as_float(w[3]);
+    const uint32_t mask = (1u << kq) - 1u;
+    const int cc = kinf.x;
+    // both forms are computed and blended with bit masks (a select would become a branch)
+    const uint32_t mq = kq != 0 ? 0xFFFFFFFFu : 0u, mr = kb == 16 ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+    for (int k = 0; k < KE; ++k) {
+      const uint32_t code = (uint32_t)(win >> (k * kq)) & mask;
+      const uint32_t q = bf16_hilo(fmaf(sc, (float)code, zp));
+      const uint32_t raw = (w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;   // lo = 0
+      const uint32_t hl = (q & mq) | (raw & mr);
+      sm.khi[bf][ke0 + k][cc] = (uint16_t)(hl & 0xFFFFu);
+      sm.klo[bf][ke0 + k][cc] = (uint16_t)(hl >> 16);
+    }
+  };
+  auto decode_v = [&](const uint32_t (&w)[2][4], const int32_t (&vl)[2], int bf) {
+    uint32_t vv[2][VC];                        // fp16 bits
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int b = 2 << ((vl[u] >> 29) & 3);
+      const int bq = b < 16 ? b : 0;
+      const uint32_t win = w[u][0] >> ((vc0 * bq) & 31);
+      const float sc = __uint_as_float(w[u][2]), zp = __uint_as_float(w[u][3]);
+      const uint32_t mask = (1u << bq) - 1u;
+      const uint32_t mq = (vl[u] >= 0 && bq != 0) ? 0xFFFFu : 0u, mr = (vl[u] >= 0 && bq == 0) ? 0xFFFFu : 0u;
+#pragma unroll
+      for (int k = 0; k < VC; ++k) {
+        const _Float16 hq = (_Float16)fmaf(sc, (float)((win >> (k * bq)) & mask), zp);
+        const _Float16 hr = (_Float16)bf16_bits_to_f32((w[u][k >> 1] >> (16 * (k & 1))) & 0xFFFFu);
+        vv[u][k] = ((uint32_t)__builtin_bit_cast(uint16_t, hq) & mq) | ((uint32_t)__builtin_bit_cast(uint16_t, hr) & mr);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < VC; ++k)
+      *reinterpret_cast<uint32_t*>(&sm.vt[bf][vgrp * 32 + vc0 + k][2 * vtp]) = vv[0][k] | (vv[1][k] << 16);
+  };
+
+  // Pipeline: at the top of iteration j, LDS buffer j & 1 holds group j decoded, the registers
+  // hold group j+1's raw words (set 1) and group j+2's V locations.  Iteration j requests group
+  // j+2's words (set 2), multiplies group j while decoding group j+1 into the other buffer,
+  // then moves set 2 into set 1.
+  uint32_t kw1[4] = {0u, 0u, 0u, 0u}, vw1[2][4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+  int32_t vl1[2] = {-1, -1}, vl2[2] = {-1, -1}, tok1 = 0x7FFFFFFF, tf0 = 0, tf1 = 0;
   if (j_begin < j_end_raw) {
-    load_vloc(j_begin, vl);
-    load_k(j_begin, kw);
-    tok = load_tok(j_begin);
-    tfirst = cache.k_keep[slot0 + j_begin * 32];
-    load_v(vl[0], vw[0]);
-    load_v(vl[1], vw[1]);
-    load_vloc(j_begin + 1, vl_next);
+    uint32_t kw0[4], vw0[2][4];
+    int32_t vl0[2];
+    load_vloc(j_begin, vl0);
+    load_k(j_begin, kw0);
+    const int32_t tok0 = load_tok(j_begin);
+    tf0 = cache.k_keep[slot0 + j_begin * 32];
+    load_v(vl0[0], vw0[0]);
+    load_v(vl0[1], vw0[1]);
+    load_vloc(j_begin + 1, vl1);
+    decode_k(kw0, (int)(j_begin & 1));
+    decode_v(vw0, vl0, (int)(j_begin & 1));
+    if (threadIdx.x < 32) sm.tok[j_begin & 1][threadIdx.x] = tok0;
+    if (j_begin + 1 < j_end_raw) {
+      load_k(j_begin + 1, kw1);
+      tok1 = load_tok(j_begin + 1);
+      tf1 = cache.k_keep[slot0 + (j_begin + 1) * 32];
+      load_v(vl1[0], vw1[0]);
+      load_v(vl1[1], vw1[1]);
+    }
+    load_vloc(j_begin + 2, vl2);
   }
   for (int64_t j = j_begin; j < j_end_raw; ++j) {
-    if ((int64_t)tfirst > pmax_block) break;   // retained tokens ascend: nothing visible later
+    if ((int64_t)tf0 > pmax_block) break;      // retained tokens ascend: nothing visible later
     const int buf = (int)(j & 1);
     const int m_valid = m_valid_of(j);
-    // ---- decode K_hat of group j into buffer buf
-    {
-      uint32_t hl2[KE];
-      if (kb == 0) {
-#pragma unroll
-        for (int k = 0; k < KE; ++k) hl2[k] = 0u;
-      } else if (kb == 16) {                   // lo = 0
-#pragma unroll
-        for (int k = 0; k < KE; ++k) hl2[k] = (kw[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
-      } else {
-        const uint64_t win = ((uint64_t)kw[0] | ((uint64_t)kw[1] << 32)) >> (kbit0 & 31);
-        const float sc = __uint_as_float(kw[2]), zp = __uint_as_float(kw[3]);
-        const uint32_t mask = (1u << kb) - 1u;
-#pragma unroll
-        for (int k = 0; k < KE; ++k) {
-          const uint32_t code = (uint32_t)(win >> (k * kb)) & mask;
-          hl2[k] = bf16_hilo(fmaf(sc, (float)code, zp));
-        }
-      }
-      const int cc = kinf.x;
-#pragma unroll
-      for (int k = 0; k < KE; ++k) {
-        sm.khi[buf][ke0 + k][cc] = (uint16_t)(hl2[k] & 0xFFFFu);
-        sm.klo[buf][ke0 + k][cc] = (uint16_t)(hl2[k] >> 16);
-      }
-    }
-    // ---- decode V_hat^T of group j into buffer buf (tokens 2 vtp and 2 vtp + 1 side by side)
-    {
-      uint32_t vv[2][VC];                      // fp16 bits
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        if (vl[u] < 0) {
-#pragma unroll
-          for (int k = 0; k < VC; ++k) vv[u][k] = 0u;
-        } else {
-          const int b = 2 << (vl[u] >> 29);
-          if (b == 16) {
-#pragma unroll
-            for (int k = 0; k < VC; ++k) {
-              const _Float16 h = (_Float16)bf16_bits_to_f32((vw[u][k >> 1] >> (16 * (k & 1))) & 0xFFFFu);
-              vv[u][k] = __builtin_bit_cast(uint16_t, h);
-            }
-          } else {
-            const uint32_t win = vw[u][0] >> ((vc0 * b) & 31);
-            const float sc = __uint_as_float(vw[u][2]), zp = __uint_as_float(vw[u][3]);
-            const uint32_t mask = (1u << b) - 1u;
-#pragma unroll
-            for (int k = 0; k < VC; ++k) {
-              const _Float16 h = (_Float16)fmaf(sc, (float)((win >> (k * b)) & mask), zp);
-              vv[u][k] = __builtin_bit_cast(uint16_t, h);
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < VC; ++k)
-        *reinterpret_cast<uint32_t*>(&sm.vt[buf][vgrp * 32 + vc0 + k][2 * vtp]) = vv[0][k] | (vv[1][k] << 16);
-    }
-    if (threadIdx.x < 32) sm.tok[buf][threadIdx.x] = tok;
-    // ---- requests for group j + 1, issued after the decode of group j so that they stay in
-    // flight through the barrier and the products of group j
-    uint32_t kw_n[4] = {0u, 0u, 0u, 0u}, vw_n[2][4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-    int32_t vl_nn[2] = {-1, -1}, tok_n = 0x7FFFFFFF, tfirst_n = 0;
-    if (j + 1 < j_end_raw) {
-      load_k(j + 1, kw_n);
-      tok_n = load_tok(j + 1);
-      tfirst_n = cache.k_keep[slot0 + (j + 1) * 32];
-      load_v(vl_next[0], vw_n[0]);
-      load_v(vl_next[1], vw_n[1]);
-      load_vloc(j + 2, vl_nn);
-    }
-    // One barrier per group: a wave that reaches it has finished the products of group j-1,
-    // the last reader of the buffer that group j+1 will be decoded into.
+    // One barrier per group: group j is in LDS, and every wave has finished group j-1, the
+    // last reader of the buffer that group j+1 is decoded into below.
     __syncthreads();
-    if (active && (!causal || (int64_t)tfirst <= off + r0 + kRows - 1)) {
+    // ---- requests for group j + 2 (set 2), in flight while group j is multiplied
+    uint32_t kw2[4] = {0u, 0u, 0u, 0u}, vw2[2][4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    int32_t vl3[2] = {-1, -1}, tok2 = 0x7FFFFFFF, tf2 = 0;
+    if (j + 2 < j_end_raw) {
+      load_k(j + 2, kw2);
+      tok2 = load_tok(j + 2);
+      tf2 = cache.k_keep[slot0 + (j + 2) * 32];
+      load_v(vl2[0], vw2[0]);
+      load_v(vl2[1], vw2[1]);
+      load_vloc(j + 3, vl3);
+    }
+    // Group j+1 is decoded unconditionally (past the split's end the words are zeros and the
+    // buffer is not read again), so the decode has no branch to keep it apart from the products.
+    const int nbuf = buf ^ 1;
+    // Every wave multiplies every group, so the decode sits in the same straight-line code as
+    // the products: an inactive wave has zero queries and writes nothing, and a group that
+    // lies past all of a wave's rows is masked to -inf, which leaves (m, l, O) unchanged.
+    {
       f32x16 acc, acc_lo;                      // q.hi and q.lo in two chains, added at the end
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] = acc_lo[i] = 0.f;
@@ -327,13 +331,21 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
         acc = mfma32(ah, qb[ks], acc);
         acc_lo = mfma32(al, qb[ks], acc_lo);
       }
+      decode_k(kw1, nbuf);                     // VALU work beside the matrix products
+      // issue order: each product of the two chains followed by a share of the decode
+#pragma unroll
+      for (int i = 0; i < 2 * KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read (K operand)
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // matrix product
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU (decode)
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] += acc_lo[i];
       float x[16];
       float tmax = -INFINITY;
       const bool full = m_valid == 32 && (!causal || sm.tok[buf][31] <= off + r0);   // uniform per wave
 #pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = acc[i] * c;
+      for (int i = 0; i < 16; ++i) x[i] = acc[i];   // raw products; the scale c > 0 is applied below
       if (!full) {
         // slots past m_valid hold the sentinel 0x7FFFFFFF, so one compare covers both masks
         const int lim = causal ? (int)pos : 0x7FFFFFFE;
@@ -343,23 +355,19 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
 #pragma unroll
       for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, x[i]);
       tmax = half_max(tmax);
-      const float mnew = fmaxf(m_run, tmax);
+      const float mnew = fmaxf(m_run, tmax * c);   // max(c x) = c max(x) for c > 0
+      // an all-masked row so far (mnew = -inf) keeps l = 0 and adds p = 0
+      const float msafe = mnew > -INFINITY ? mnew : 0.f;
+      const float alpha = mnew > -INFINITY ? fast_exp2(m_run - mnew) : 1.f;
       float p[16];
-      float alpha = 1.f;
-      if (mnew > -INFINITY) {
-        alpha = fast_exp2(m_run - mnew);
-        float ps = 0.f;
+      float ps = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          p[i] = fast_exp2(x[i] - mnew);
-          ps += p[i];
-        }
-        l_run = l_run * alpha + ps;
-        m_run = mnew;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) p[i] = 0.f;
+      for (int i = 0; i < 16; ++i) {
+        p[i] = fast_exp2(fmaf(x[i], c, -msafe));
+        ps += p[i];
       }
+      l_run = l_run * alpha + ps;
+      m_run = mnew;
       if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {   // no row of the wave moved its max: skip
 #pragma unroll
         for (int mb = 0; mb < GPR; ++mb)
@@ -385,20 +393,30 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
           o[mb] = mfma32h(va, pb, o[mb]);
         }
       }
+      decode_v(vw1, vl1, nbuf);
+#pragma unroll
+      for (int i = 0; i < 2 * GPR; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read (V operand)
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // matrix product
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU (decode)
+      }
     }
+    if (threadIdx.x < 32) sm.tok[nbuf][threadIdx.x] = tok1;
+    // set 2 becomes set 1
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      kw[k] = kw_n[k];
-      vw[0][k] = vw_n[0][k];
-      vw[1][k] = vw_n[1][k];
+      kw1[k] = kw2[k];
+      vw1[0][k] = vw2[0][k];
+      vw1[1][k] = vw2[1][k];
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      vl[u] = vl_next[u];
-      vl_next[u] = vl_nn[u];
+      vl1[u] = vl2[u];
+      vl2[u] = vl3[u];
     }
-    tok = tok_n;
-    tfirst = tfirst_n;
+    tok1 = tok2;
+    tf0 = tf1;
+    tf1 = tf2;
   }
 
   if (!active) return;
