@@ -336,13 +336,23 @@ ridge_sum(const double* __restrict__ Mp, const double* __restrict__ Bp, double* 
   }
 }
 
-// Cholesky of the 32 x 32 tile in LDS (lower part), right-looking with all threads.  Thread t
-// owns the fixed elements e = t + 256 u (u < 3) of the 528-element lower triangle.  Step j: every
-// thread reads the pivot, its owned elements (i, c), j < c <= i, drop l_ij l_cj with
-// l = a * (1 / sqrt(pivot)); after the barrier column j is scaled (it is not read by later
-// steps' updates, and the next pivot is final).  The inverse of L follows, one column per lane
-// held in registers.  Writes L (lower, zeros above) to Ld (row stride ld) and L^-1 to Li
-// (32 x 32).  A pivot that is not positive sets the status bit.
+// 1 / sqrt(a): the hardware estimate and two Newton steps y <- y (3 - a y^2) / 2.
+__device__ __forceinline__ double rsqrt_newton(double a) {
+  const double h = 0.5 * a;
+  double y = __builtin_amdgcn_rsq(a);
+  y = y * fma(-h * y, y, 1.5);
+  y = y * fma(-h * y, y, 1.5);
+  return y;
+}
+
+// Cholesky of the 32 x 32 tile in LDS (lower part) and the inverse of its factor, both
+// right-looking with all threads.  Thread t owns the fixed positions e = t + 256 u (u < 3) of
+// the 528-element lower triangle, in A and in X (X starts as I and ends as L^-1).  Step j, with
+// rd = 1 / sqrt(a_jj) and l_ij = a_ij rd: every owned A(i, c), j < c <= i, drops l_ij l_cj, and
+// every owned X(i, c), c <= j < i, drops l_ij (x_jc rd), x_jc rd being row j of L^-1.  After the
+// barrier column j of A and row j of X are scaled by rd; step j+1 neither reads nor writes
+// them, and its pivot and its row of X are final.  Writes L (lower, zeros above) to Ld (row
+// stride ld) and L^-1 to Li (32 x 32).  A pivot that is not positive sets the status bit.
 __device__ __forceinline__ void potrf_tile(double (*A)[kNB + 1], double (*X)[kNB + 1], double* __restrict__ Ld,
                                            int64_t ld, double* __restrict__ Li, int32_t* __restrict__ status) {
   constexpr int kTri = kNB * (kNB + 1) / 2;          // 528
@@ -357,43 +367,31 @@ __device__ __forceinline__ void potrf_tile(double (*A)[kNB + 1], double (*X)[kNB
     ei[u] = e < kTri ? i : -1;
     ec[u] = e < kTri ? e - i * (i + 1) / 2 : kNB;
   }
+  for (int e = tid; e < kNB * kNB; e += blockDim.x) X[e / kNB][e % kNB] = (e / kNB == e % kNB) ? 1.0 : 0.0;
   bool bad = false;
   __syncthreads();
   for (int j = 0; j < kNB; ++j) {
     const double piv = A[j][j];
     bad |= !(piv > 0.0);
-    const double rd = 1.0 / sqrt(piv);
+    const double rd = rsqrt_newton(piv);
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int i = ei[u], c = ec[u];
-      if (c > j && i >= c) A[i][c] -= (A[i][j] * rd) * (A[c][j] * rd);
+      if (i > j) {
+        const double lij = A[i][j] * rd;
+        if (c > j) A[i][c] -= lij * (A[c][j] * rd);
+        else X[i][c] -= lij * (X[j][c] * rd);
+      }
     }
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int i = ei[u], c = ec[u];
       if (c == j) A[i][j] = (i == j) ? piv * rd : A[i][j] * rd;
+      if (i == j) X[j][c] *= rd;
     }
   }
   if (bad && tid == 0) atomicOr(status, KVC_DEV_NOT_SPD);
-  __syncthreads();
-  if (tid < kNB) {
-    const int c = tid;
-    double x[kNB];
-#pragma unroll
-    for (int rr = 0; rr < kNB; ++rr) {
-      double s0 = rr == c ? 1.0 : 0.0, s1 = 0.0;
-#pragma unroll
-      for (int p = 0; p + 1 < rr; p += 2) {
-        s0 -= A[rr][p] * x[p];
-        s1 -= A[rr][p + 1] * x[p + 1];
-      }
-      if (rr & 1) s0 -= A[rr][rr - 1] * x[rr - 1];
-      x[rr] = (s0 + s1) / A[rr][rr];                 // 0 above the diagonal (rr < c)
-    }
-#pragma unroll
-    for (int rr = 0; rr < kNB; ++rr) X[rr][c] = x[rr];
-  }
   __syncthreads();
   for (int e = tid; e < kNB * kNB; e += blockDim.x) {
     const int rr = e / kNB, c = e % kNB;
@@ -454,7 +452,7 @@ __device__ __forceinline__ void zero2(double (&c)[2][2]) { c[0][0] = c[0][1] = c
 __global__ void __launch_bounds__(256)
 ridge_chol(double* __restrict__ M, double* __restrict__ Lm, double* __restrict__ Li, double* __restrict__ Bm,
            double* __restrict__ Yf, RidgeDims r, int kb, int32_t* __restrict__ status) {
-  __shared__ Tile Ls, Xi, Xj;
+  __shared__ Tile Ls, Xi, Xj, Xk;
   const int g = blockIdx.y;
   const int64_t np = r.npad, D = r.d;
   double* Mg = M + (int64_t)g * np * np;
@@ -514,31 +512,26 @@ ridge_chol(double* __restrict__ M, double* __restrict__ Lm, double* __restrict__
   while ((u + 1) * (u + 2) / 2 <= t) ++u;
   const int v = t - u * (u + 1) / 2;
   const int ib = kb + 1 + u, jb = kb + 1 + v;
-  tile_load(Xj, Mg + (int64_t)ib * kNB * np + k0, np);            // A_ib,k
-  __syncthreads();
-  zero2(c);
-  mm_abT(Xj, Ls, c);                                              // X_i = A_ib,k L_kk^-T
-  double xi[2][2] = {{c[0][0], c[0][1]}, {c[1][0], c[1][1]}};
-  __syncthreads();
-  tile_put(Xi, xi);
-  if (jb != ib) {
-    tile_load(Xj, Mg + (int64_t)jb * kNB * np + k0, np);          // A_jb,k
-    __syncthreads();
-    zero2(c);
-    mm_abT(Xj, Ls, c);                                            // X_j
-    __syncthreads();
-    tile_put(Xj, c);
-  } else {
-    tile_put(Xj, xi);
-  }
-  __syncthreads();
-  // A_ib,jb -= X_i X_j^T
+  // every global read of the block is issued before the first barrier
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   double* tileA = Mg + (int64_t)ib * kNB * np + (int64_t)jb * kNB;
   c[0][0] = -tileA[(2 * ty) * np + 2 * tx];
   c[0][1] = -tileA[(2 * ty) * np + 2 * tx + 1];
   c[1][0] = -tileA[(2 * ty + 1) * np + 2 * tx];
   c[1][1] = -tileA[(2 * ty + 1) * np + 2 * tx + 1];
+  tile_load(Xj, Mg + (int64_t)ib * kNB * np + k0, np);            // A_ib,k
+  tile_load(Xk, Mg + (int64_t)jb * kNB * np + k0, np);            // A_jb,k (= A_ib,k on the diagonal)
+  __syncthreads();
+  double xi[2][2], xj[2][2];
+  zero2(xi);
+  mm_abT(Xj, Ls, xi);                                             // X_i = A_ib,k L_kk^-T
+  zero2(xj);
+  mm_abT(Xk, Ls, xj);                                             // X_j (the same on the diagonal)
+  __syncthreads();
+  tile_put(Xi, xi);
+  tile_put(Xj, xj);
+  __syncthreads();
+  // A_ib,jb -= X_i X_j^T
   mm_abT(Xi, Xj, c);
   c[0][0] = -c[0][0];
   c[0][1] = -c[0][1];
