@@ -347,56 +347,64 @@ __device__ __forceinline__ double rsqrt_newton(double a) {
 
 // Cholesky of the 32 x 32 tile in LDS (lower part) and the inverse of its factor, both
 // right-looking with all threads.  Thread t owns the fixed positions e = t + 256 u (u < 3) of
-// the 528-element lower triangle, in A and in X (X starts as I and ends as L^-1).  Step j, with
-// rd = 1 / sqrt(a_jj) and l_ij = a_ij rd: every owned A(i, c), j < c <= i, drops l_ij l_cj, and
-// every owned X(i, c), c <= j < i, drops l_ij (x_jc rd), x_jc rd being row j of L^-1.  After the
-// barrier column j of A and row j of X are scaled by rd; step j+1 neither reads nor writes
-// them, and its pivot and its row of X are final.  Writes L (lower, zeros above) to Ld (row
-// stride ld) and L^-1 to Li (32 x 32).  A pivot that is not positive sets the status bit.
+// the 528-element lower triangle, in A and in X (X starts as I).  Column j of A and row j of X
+// are left unscaled in LDS: with rd_j = 1 / sqrt(a_jj) and l_ij = a_ij rd_j, step j makes every
+// owned A(i, c), j < c <= i, drop l_ij (a_cj rd_j) and every owned X(i, c), c <= j < i, drop
+// l_ij (x_jc rd_j).  A step writes neither column j of A nor row j of X nor the next pivot's
+// inputs that other threads read, so each step is one batch of LDS reads, one batch of writes
+// and one barrier.  At the end L(i, j) = a_ij rd_j (a_jj rd_j on the diagonal) and
+// L^-1(i, c) = x_ic rd_i.  Writes L (lower, zeros above) to Ld (row stride ld) and L^-1 to Li
+// (32 x 32).  A pivot that is not positive sets the status bit.
 __device__ __forceinline__ void potrf_tile(double (*A)[kNB + 1], double (*X)[kNB + 1], double* __restrict__ Ld,
                                            int64_t ld, double* __restrict__ Li, int32_t* __restrict__ status) {
   constexpr int kTri = kNB * (kNB + 1) / 2;          // 528
   constexpr int kPer = (kTri + 255) / 256;           // 3
+  __shared__ double rdv[kNB];
   const int tid = threadIdx.x;
-  int ei[kPer], ec[kPer];
+  int ei[kPer], ec[kPer], ri[kPer], rc[kPer];        // owned position (-1: none), and a readable one
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {                   // element e -> (i, c), e = i (i + 1) / 2 + c
     const int e = tid + 256 * u;
     int i = 0;
     while ((i + 1) * (i + 2) / 2 <= e && i < kNB) ++i;
     ei[u] = e < kTri ? i : -1;
-    ec[u] = e < kTri ? e - i * (i + 1) / 2 : kNB;
+    ec[u] = e < kTri ? e - i * (i + 1) / 2 : 0;
+    ri[u] = e < kTri ? ei[u] : 0;
+    rc[u] = ec[u];
   }
   for (int e = tid; e < kNB * kNB; e += blockDim.x) X[e / kNB][e % kNB] = (e / kNB == e % kNB) ? 1.0 : 0.0;
   bool bad = false;
   __syncthreads();
   for (int j = 0; j < kNB; ++j) {
     const double piv = A[j][j];
+    double aij[kPer], acj[kPer], xjc[kPer], aic[kPer], xic[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {                 // every read of the step, issued together
+      aij[u] = A[ri[u]][j];
+      acj[u] = A[rc[u]][j];
+      xjc[u] = X[j][rc[u]];
+      aic[u] = A[ri[u]][rc[u]];
+      xic[u] = X[ri[u]][rc[u]];
+    }
     bad |= !(piv > 0.0);
     const double rd = rsqrt_newton(piv);
+    if (tid == 0) rdv[j] = rd;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int i = ei[u], c = ec[u];
       if (i > j) {
-        const double lij = A[i][j] * rd;
-        if (c > j) A[i][c] -= lij * (A[c][j] * rd);
-        else X[i][c] -= lij * (X[j][c] * rd);
+        const double lij = aij[u] * rd;
+        if (c > j) A[i][c] = aic[u] - lij * (acj[u] * rd);
+        else X[i][c] = xic[u] - lij * (xjc[u] * rd);
       }
     }
     __syncthreads();
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int i = ei[u], c = ec[u];
-      if (c == j) A[i][j] = (i == j) ? piv * rd : A[i][j] * rd;
-      if (i == j) X[j][c] *= rd;
-    }
   }
   if (bad && tid == 0) atomicOr(status, KVC_DEV_NOT_SPD);
-  __syncthreads();
   for (int e = tid; e < kNB * kNB; e += blockDim.x) {
     const int rr = e / kNB, c = e % kNB;
-    Ld[rr * ld + c] = c <= rr ? A[rr][c] : 0.0;
-    Li[e] = X[rr][c];
+    Ld[rr * ld + c] = c < rr ? A[rr][c] * rdv[c] : (c == rr ? A[rr][rr] * rdv[rr] : 0.0);
+    Li[e] = c <= rr ? X[rr][c] * rdv[rr] : 0.0;
   }
 }
 
