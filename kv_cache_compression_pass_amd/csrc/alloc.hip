@@ -256,10 +256,16 @@ alloc_small(const float* __restrict__ weight, const float* __restrict__ sigma,
   __shared__ SelState st;
   __shared__ int32_t bad;
   __shared__ double dbuf[16];
+  __shared__ unsigned long long kmin, kmax;
+  __shared__ int nbits;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int U = (stage == KVC_ALLOC_V_TOKENS) ? (int)(Hkv * N) : Hkv * d;
-  if (tid == 0) bad = 0;
+  if (tid == 0) {
+    bad = 0;
+    kmin = ~0ull;
+    kmax = 0;
+  }
   for (int g = tid; g < Hkv; g += 1024) rc[g] = 0;
   __syncthreads();
   if (stage == KVC_ALLOC_K_CHANNELS) sum_counts(rpart, rbad, Hkv, ncb, rc, &bad);
@@ -282,6 +288,7 @@ alloc_small(const float* __restrict__ weight, const float* __restrict__ sigma,
     st.pad = 0;
     *status = bad ? KVC_DEV_BAD_WIDTH : 0;
   }
+  uint64_t tmn = ~0ull, tmx = 0;
   for (int u = tid; u < U; u += 1024) {
     float c = weight[u];
     if (sigma) c = c * sigma[u];
@@ -289,9 +296,41 @@ alloc_small(const float* __restrict__ weight, const float* __restrict__ sigma,
     uint64_t kk[4];
     unit_keys(c, s, kk);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) keys[u * 4 + k] = kk[k];
+    for (int k = 0; k < 4; ++k) {
+      keys[u * 4 + k] = kk[k];
+      if (kk[k] != 0) {
+        tmn = kk[k] < tmn ? kk[k] : tmn;
+        tmx = kk[k] > tmx ? kk[k] : tmx;
+      }
+    }
   }
-  const int npass = passes_of(64);
+  // The radix select starts at the highest bit in which the positive keys differ: the bits
+  // above it are the same for all of them and become the starting prefix, so the first digit
+  // already spreads the keys over many bins (few colliding LDS atomics, earlier single-value
+  // bins).
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint64_t a = __shfl_xor(tmn, o, 64), b = __shfl_xor(tmx, o, 64);
+    tmn = a < tmn ? a : tmn;
+    tmx = b > tmx ? b : tmx;
+  }
+  if (lane == 0) {
+    atomicMin(&kmin, (unsigned long long)tmn);
+    atomicMax(&kmax, (unsigned long long)tmx);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int nb = 64;
+    if (kmax != 0) {
+      const uint64_t x = kmin ^ kmax;
+      nb = x ? 64 - __clzll((long long)x) : 1;
+      if (nb < 64) st.prefix = kmin & (~0ull << nb);
+    }
+    nbits = nb;
+  }
+  __syncthreads();
+  const int nbk = nbits;
+  const int npass = passes_of(nbk);
   for (int pass = 0; pass < npass; ++pass) {
     __syncthreads();
     if (st.done) break;                         // uniform: read after a barrier
@@ -301,7 +340,7 @@ alloc_small(const float* __restrict__ weight, const float* __restrict__ sigma,
       hmax[b] = 0;
     }
     __syncthreads();
-    const Digit dg = digit_of(pass, 64);
+    const Digit dg = digit_of(pass, nbk);
     const uint64_t pre = st.prefix & dg.himask;
     const uint64_t dmask = (1ull << (dg.hi - dg.lo)) - 1;
     for (int e = tid; e < U * 4; e += 1024) {
@@ -316,7 +355,7 @@ alloc_small(const float* __restrict__ weight, const float* __restrict__ sigma,
       }
     }
     __syncthreads();
-    select_digit<1024>(&st, hist, hmin, hmax, pass, 64, wave_tot);
+    select_digit<1024>(&st, hist, hmin, hmax, pass, nbk, wave_tot);
   }
   __syncthreads();
   const SelState S = st;
