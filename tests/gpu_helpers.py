@@ -129,3 +129,36 @@ def compare_packed(gpu, ref):
         if not np.all(eq):
             bad = np.argwhere(~eq)[:5]
             raise AssertionError(f"{name}: {int((~eq).sum())} mismatches, first at {bad.tolist()}")
+
+
+def attend_tols(q_bits, k_bits_list, v_bits_list, lse_ref, scale=None):
+    """Bounds on |Y_hat - Y_ref| and |l_hat - l_ref| for the attend calls.
+
+    Logits: the keys enter the products as bf16 hi + lo (exact to 2^-17 relative) and the d
+    products are summed in fp32 (at most d 2^-24 relative to sum |q_c k_c|), and sum |q_c k_c|
+    <= ||q|| ||k_hat|| with |k_hat_c| <= max_t |k_tc| (a dequantised value stays inside its
+    group's range), so dl = (2^-17 + d 2^-24) max||q|| kcap scale bounds a logit's error and,
+    the LSE being a smooth maximum, the LSE's; the base-2 to natural conversion adds a few
+    float32 roundings of |l|.  Outputs: V_hat and the probabilities enter the matrix products
+    as fp16 (2^-11 relative each; the probabilities of a row sum to 1 and |V_hat| <= max|V|),
+    one more such term covers the fp32 sums, and a logit error dl moves each probability by at
+    most a factor e^dl, i.e. the output by about 2 dl max|V|."""
+    from workloads import bf16_bits_to_f32
+    q = bf16_bits_to_f32(np.asarray(q_bits)).astype(np.float64)
+    d = q.shape[-1]
+    s = scale if scale else 1.0 / np.sqrt(d)
+    qn = float(np.sqrt((q * q).sum(-1)).max()) if q.size else 0.0
+    kcap = 0.0
+    for kb in k_bits_list:
+        k = bf16_bits_to_f32(np.asarray(kb)).astype(np.float64)
+        if k.size:
+            kcap = max(kcap, float(np.sqrt((np.abs(k).max(axis=-2) ** 2).sum(-1)).max()))
+    vmax = 0.0
+    for vb in v_bits_list:
+        v = np.asarray(vb)
+        if v.size:
+            vmax = max(vmax, float(np.abs(bf16_bits_to_f32(v)).max()))
+    dl = (2.0 ** -17 + d * 2.0 ** -24) * qn * kcap * s
+    lr = np.asarray(lse_ref, dtype=np.float64)
+    lmax = float(np.abs(lr[np.isfinite(lr)]).max()) if np.isfinite(lr).any() else 0.0
+    return (3 * 2.0 ** -11 + 2 * dl) * vmax + 1e-5, dl + 4 * 2.0 ** -24 * lmax + 1e-6

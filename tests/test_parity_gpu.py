@@ -1,8 +1,9 @@
 """GPU parity: every C-ABI call against the float64 oracle on the same seeded inputs.
 
-Bars (derived in the design doc from the arithmetic): row LSE 1e-4 abs; token scores rel 1e-3
+Bars (derived from the arithmetic): row LSE 1e-4 abs; token scores rel 1e-3
 (floor 1e-30); channel weights rel 1e-5; widths, results and packed buffers bit-exact from
-identical float32 weights / widths; compressed attention output 2e-2 abs and LSE 1e-3 abs.
+identical float32 weights / widths; attention outputs and LSEs within the bounds that
+gpu_helpers.attend_tols derives from the operand precisions and the inputs' magnitudes.
 """
 
 import math
@@ -87,16 +88,18 @@ def _pipeline(name, hq, hkv, d, N, Nq, causal, avg, seed, x=None, n_fid=64):
     out_g, lh_g, st = H.attend(desc_f, H.dev_bf16(qf_bits), cache)
     assert st == 0
     out_r, lh_r = oracle.compressed_attend(qf_bits, x["k"], x["v"], bv_r, bk_r, causal=causal)
-    H.assert_abs(out_g.cpu().numpy(), out_r, 2e-2, "compressed attend output")
-    H.assert_abs(lh_g.cpu().numpy(), lh_r, 1e-3, "compressed attend lse")
+    ty, tl = H.attend_tols(qf_bits, [x["k"]], [x["v"]], lh_r)
+    H.assert_abs(out_g.cpu().numpy(), out_r, ty, "compressed attend output")
+    H.assert_abs(lh_g.cpu().numpy(), lh_r, tl, "compressed attend lse")
     full_v = np.full((hkv, N), 16, np.uint8)
     full_k = np.full((hkv, d), 16, np.uint8)
     cache16, st = H.pack(desc, k, v, H.dev_u8(full_v), H.dev_u8(full_k))
     y_g, l_g, st2 = H.attend(desc_f, H.dev_bf16(qf_bits), cache16)
     assert st == 0 and st2 == 0
     y_r, l_r = oracle.full_attend(qf_bits, x["k"], x["v"], causal=causal)
-    H.assert_abs(y_g.cpu().numpy(), y_r, 2e-2, "full attend output")
-    H.assert_abs(l_g.cpu().numpy(), l_r, 1e-3, "full attend lse")
+    ty, tl = H.attend_tols(qf_bits, [x["k"]], [x["v"]], l_r)
+    H.assert_abs(y_g.cpu().numpy(), y_r, ty, "full attend output")
+    H.assert_abs(l_g.cpu().numpy(), l_r, tl, "full attend lse")
 
     # KVSculpt's loss terms per query head, from the two attends above
     terms = torch.empty(hq, 2, dtype=torch.float64, device=H.DEV)
@@ -233,8 +236,9 @@ def test_evict_everything_and_empty_rows():
     H.compare_packed(cache.to_numpy(), oracle.pack_cache(x["k"], x["v"], bv, bk))
     out_g, lh_g, st = H.attend(desc, H.dev_bf16(x["q"]), cache)
     out_r, lh_r = oracle.compressed_attend(x["q"], x["k"], x["v"], bv, bk)
-    H.assert_abs(out_g.cpu().numpy(), out_r, 2e-2, "out")
-    H.assert_abs(lh_g.cpu().numpy(), lh_r, 1e-3, "lse")
+    ty, tl = H.attend_tols(x["q"], [x["k"]], [x["v"]], lh_r)
+    H.assert_abs(out_g.cpu().numpy(), out_r, ty, "out")
+    H.assert_abs(lh_g.cpu().numpy(), lh_r, tl, "lse")
     assert np.isneginf(lh_g.cpu().numpy()[:2]).all()
 
 
@@ -287,8 +291,9 @@ def test_attend_group_aligned_uniform_widths(bvv, bkk):
     y_g, l_g, st2 = H.attend(H.desc_of(hq, hkv, d, N, nf, True), H.dev_bf16(qf), cache)
     assert st2 == 0
     y_r, l_r = oracle.compressed_attend(qf, x["k"], x["v"], bv, bk)
-    H.assert_abs(y_g.cpu().numpy(), y_r, 2e-2, "attend output")
-    H.assert_abs(l_g.cpu().numpy(), l_r, 1e-3, "attend lse")
+    ty, tl = H.attend_tols(qf, [x["k"]], [x["v"]], l_r)
+    H.assert_abs(y_g.cpu().numpy(), y_r, ty, "attend output")
+    H.assert_abs(l_g.cpu().numpy(), l_r, tl, "attend lse")
 
 
 KEEP_CASES = [
@@ -365,15 +370,17 @@ def test_attend_decode_rows(case):
     out_g, lh_g, st = H.attend(desc_f, H.dev_bf16(qf_bits), cache)
     assert st == 0
     out_r, lh_r = oracle.compressed_attend(qf_bits, x["k"], x["v"], bv, bk, causal=causal)
-    H.assert_abs(out_g.cpu().numpy(), out_r, 2e-2, "decode attend output")
-    H.assert_abs(lh_g.cpu().numpy(), lh_r, 1e-3, "decode attend lse")
+    ty, tl = H.attend_tols(qf_bits, [x["k"]], [x["v"]], lh_r)
+    H.assert_abs(out_g.cpu().numpy(), out_r, ty, "decode attend output")
+    H.assert_abs(lh_g.cpu().numpy(), lh_r, tl, "decode attend lse")
     cache16, st = H.pack(desc, k, v, H.dev_u8(np.full((hkv, N), 16, np.uint8)),
                          H.dev_u8(np.full((hkv, d), 16, np.uint8)))
     y_g, l_g, st2 = H.attend(desc_f, H.dev_bf16(qf_bits), cache16)
     assert st == 0 and st2 == 0
     y_r, l_r = oracle.full_attend(qf_bits, x["k"], x["v"], causal=causal)
-    H.assert_abs(y_g.cpu().numpy(), y_r, 2e-2, "decode attend output, all-16 cache")
-    H.assert_abs(l_g.cpu().numpy(), l_r, 1e-3, "decode attend lse, all-16 cache")
+    ty, tl = H.attend_tols(qf_bits, [x["k"]], [x["v"]], l_r)
+    H.assert_abs(y_g.cpu().numpy(), y_r, ty, "decode attend output, all-16 cache")
+    H.assert_abs(l_g.cpu().numpy(), l_r, tl, "decode attend lse, all-16 cache")
 
 
 def test_attend_decode_row_that_sees_nothing():
@@ -395,8 +402,9 @@ def test_attend_decode_row_that_sees_nothing():
     og, lg = out_g.cpu().numpy(), lh_g.cpu().numpy()
     assert np.all(og[:, 0, :] == 0.0) and np.all(np.isneginf(lg[:, 0]))
     assert np.all(np.isneginf(lh_r[:, 0]))
-    H.assert_abs(og, out_r, 2e-2, "decode attend output")
-    H.assert_abs(lg[:, 1], lh_r[:, 1], 1e-3, "decode attend lse")
+    ty, tl = H.attend_tols(qf_bits, [x["k"]], [x["v"]], lh_r)
+    H.assert_abs(og, out_r, ty, "decode attend output")
+    H.assert_abs(lg[:, 1], lh_r[:, 1], tl, "decode attend lse")
 
 
 APPEND_CASES = [
@@ -434,14 +442,16 @@ def test_attend_with_append_buffer(case):
     torch.cuda.synchronize()
     assert kvc.kvc_get_device_status(ws) == 0
     out_r, lh_r = oracle.compressed_attend_append(qf_bits, k, v, bv, bk, kn, vn, causal=causal)
-    H.assert_abs(out.cpu().numpy(), out_r, 2e-2, "append attend output")
-    H.assert_abs(lse.cpu().numpy(), lh_r, 1e-3, "append attend lse")
+    ty, tl = H.attend_tols(qf_bits, [k, kn], [v, vn], lh_r)
+    H.assert_abs(out.cpu().numpy(), out_r, ty, "append attend output")
+    H.assert_abs(lse.cpu().numpy(), lh_r, tl, "append attend lse")
     # no new tokens: the same call is the packed cache alone
     kvc.kvc_compressed_attend_append(desc_f, H.dev_bf16(qf_bits), cache, None, None, out, lse, ws)
     torch.cuda.synchronize()
     out0, l0 = oracle.compressed_attend(qf_bits, k, v, bv, bk, causal=causal)
-    H.assert_abs(out.cpu().numpy(), out0, 2e-2, "attend output, empty buffer")
-    H.assert_abs(lse.cpu().numpy(), l0, 1e-3, "attend lse, empty buffer")
+    ty, tl = H.attend_tols(qf_bits, [k], [v], l0)
+    H.assert_abs(out.cpu().numpy(), out0, ty, "attend output, empty buffer")
+    H.assert_abs(lse.cpu().numpy(), l0, tl, "attend lse, empty buffer")
 
 
 FID_CASES = [
@@ -548,3 +558,37 @@ def test_ridge_single_key_closed_form():
     assert kvc.kvc_get_device_status(ws) == 0
     want = y.astype(np.float64).reshape(-1, d).sum(axis=0) / (hq + lam)
     np.testing.assert_allclose(v_c.cpu().numpy()[0, 0], want, rtol=1e-5, atol=1e-6)
+
+
+ALLROW_CASES = [
+    # name, H_q, H_kv, d, N, Nq, causal
+    ("allrows_causal_d128", 8, 2, 128, 777, 777, True),
+    ("allrows_causal_d64", 4, 1, 64, 1000, 1000, True),
+    ("rows_noncausal_d128", 4, 2, 128, 650, 97, False),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", ALLROW_CASES, ids=[c[0] for c in ALLROW_CASES])
+def test_attend_every_row_mixed_widths(case):
+    """The matrix-core attend on every query row of a causal layer (row blocks whose last row
+    comes before a key split's groups stop early, and splits of one or a few groups), with each
+    token's V width and each channel's K width drawn independently from {0, 2, 4, 8, 16}, so
+    the lanes of one wave decode different widths side by side."""
+    name, hq, hkv, d, N, Nq, causal = case
+    print(f"case {name}", flush=True)
+    x = make_inputs(hq, hkv, d, N, Nq, seed=zlib.crc32(name.encode()) % 1000)
+    rng = np.random.default_rng(11)
+    widths = np.array([0, 2, 4, 8, 16], np.uint8)
+    bv = widths[rng.integers(0, 5, size=(hkv, N))]
+    bv[:, 0] = 4                                   # every row sees at least one token
+    bk = widths[rng.integers(0, 5, size=(hkv, d))]
+    desc = H.desc_of(hq, hkv, d, N, Nq, causal)
+    cache, st = H.pack(desc, H.dev_bf16(x["k"]), H.dev_bf16(x["v"]), H.dev_u8(bv), H.dev_u8(bk))
+    assert st == 0
+    y_g, l_g, st2 = H.attend(desc, H.dev_bf16(x["q"]), cache)
+    assert st2 == 0
+    y_r, l_r = oracle.compressed_attend(x["q"], x["k"], x["v"], bv, bk, causal=causal)
+    ty, tl = H.attend_tols(x["q"], [x["k"]], [x["v"]], l_r)
+    H.assert_abs(y_g.cpu().numpy(), y_r, ty, "attend output")
+    H.assert_abs(l_g.cpu().numpy(), l_r, tl, "attend lse")
