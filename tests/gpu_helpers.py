@@ -132,7 +132,8 @@ def compare_packed(gpu, ref):
 
 
 def attend_tols(q_bits, k_bits_list, v_bits_list, lse_ref, scale=None):
-    """Bounds on |Y_hat - Y_ref| and |l_hat - l_ref| for the attend calls.
+    """Bounds on |Y_hat - Y_ref| and |l_hat - l_ref| for the attend calls: the stated bars
+    (2e-2 and 1e-3 abs), tightened to what the arithmetic allows for the test's own inputs.
 
     Logits: the keys enter the products as bf16 hi + lo (exact to 2^-17 relative) and the d
     products are summed in fp32 (at most d 2^-24 relative to sum |q_c k_c|), and sum |q_c k_c|
@@ -161,4 +162,5 @@ def attend_tols(q_bits, k_bits_list, v_bits_list, lse_ref, scale=None):
     dl = (2.0 ** -17 + d * 2.0 ** -24) * qn * kcap * s
     lr = np.asarray(lse_ref, dtype=np.float64)
     lmax = float(np.abs(lr[np.isfinite(lr)]).max()) if np.isfinite(lr).any() else 0.0
-    return (3 * 2.0 ** -11 + 2 * dl) * vmax + 1e-5, dl + 4 * 2.0 ** -24 * lmax + 1e-6
+    # never looser than the stated bars (output 2e-2 abs, LSE 1e-3 abs)
+    return min((3 * 2.0 ** -11 + 2 * dl) * vmax + 1e-5, 2e-2), min(dl + 4 * 2.0 ** -24 * lmax + 1e-6, 1e-3)
