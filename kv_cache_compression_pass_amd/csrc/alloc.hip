@@ -20,7 +20,8 @@
 // Two launch shapes:
 //  * small stages (<= 2048 units, e.g. the K-channel stage): one block does everything in LDS;
 //  * larger stages: per pass a histogram kernel (block-private LDS bins flushed with integer
-//    atomics) and a one-block select kernel; then tie sums, their scan, and the assignment.
+//    atomics) and a one-block select kernel; then per-block tie sums, and the assignment, each
+//    of whose blocks adds up the tie sums of the blocks before it (at most kMaxBlocks).
 //    Kernel boundaries order every step; no cross-block fences are needed.
 #include "common.hpp"
 #include "internal.hpp"
@@ -60,7 +61,6 @@ struct AllocWs {
   int32_t* rbad;        // [Hkv][ncb]  invalid token widths seen in the block
   int64_t* rcount;      // [Hkv]      R_g (K stage)
   int64_t* bsum;        // [nseg][nblk]
-  int64_t* bexcl;       // [nseg][nblk]
   int64_t* used_part;   // [nseg][nblk]
   double* dist_part;    // [nseg][nblk]
 };
@@ -601,25 +601,6 @@ alloc_ties(AllocWs a, const float* __restrict__ weight, const float* __restrict_
   if (threadIdx.x == 255) a.bsum[(int64_t)seg * gridDim.x + blockIdx.x] = tot;
 }
 
-// Exclusive scan of the block sums of each segment, in block order (one block per segment).
-__global__ void __launch_bounds__(256)
-alloc_tie_scan(AllocWs a, int nblk) {
-  __shared__ int64_t wave_tot[4];
-  __shared__ int64_t blk_total;
-  const int seg = blockIdx.x;
-  int64_t carry = 0;
-  for (int b0 = 0; b0 < nblk; b0 += 256) {
-    const int b = b0 + threadIdx.x;
-    const int64_t v = (b < nblk) ? a.bsum[(int64_t)seg * nblk + b] : 0;
-    const int64_t incl = block_scan_incl(v, wave_tot);
-    if (b < nblk) a.bexcl[(int64_t)seg * nblk + b] = carry + incl - v;
-    if (threadIdx.x == 255) blk_total = incl;
-    __syncthreads();
-    carry += blk_total;
-    __syncthreads();
-  }
-}
-
 // Final widths: steps with key > lambda*, plus the tied step while the inclusive prefix of tie
 // rates fits the remaining budget; per-block used rate and distortion.
 template <bool TOPK, int UPT>
@@ -628,6 +609,7 @@ alloc_assign(AllocWs a, const float* __restrict__ weight, const float* __restric
              int64_t seg_len, int stage, int d, int keep_bits, uint8_t* __restrict__ bits_out) {
   __shared__ int64_t wave_tot[4];
   __shared__ double dbuf[4];
+  __shared__ int64_t prefix_sh;
   const int seg = blockIdx.y;
   const SelState s = a.st[seg];
   const int64_t base = (int64_t)blockIdx.x * (256 * UPT) + threadIdx.x * UPT;
@@ -641,7 +623,14 @@ alloc_assign(AllocWs a, const float* __restrict__ weight, const float* __restric
     tsum += tie[j];
   }
   const int64_t incl = block_scan_incl(tsum, wave_tot);
-  int64_t run = a.bexcl[(int64_t)seg * gridDim.x + blockIdx.x] + incl - tsum;
+  // tie rates of the segment's earlier blocks (at most kMaxBlocks sums, read by the whole block;
+  // integers, so the order of the additions does not matter)
+  int64_t before = 0;
+  for (int b = threadIdx.x; b < (int)blockIdx.x; b += 256) before += a.bsum[(int64_t)seg * gridDim.x + b];
+  before = block_scan_incl(before, wave_tot);
+  if (threadIdx.x == 255) prefix_sh = before;
+  __syncthreads();
+  int64_t run = prefix_sh + incl - tsum;
   const int64_t cap = TOPK ? s.brem + 1 : s.brem;
   int64_t used = 0;
   double dist = 0.0;
@@ -763,7 +752,6 @@ AllocWs carve(const Layer& L, int stage, char* ws, size_t* total) {
   const size_t o_rb = w.take(kst ? sizeof(int32_t) * L.hkv * ncb : 0);
   const size_t o_r = w.take(sizeof(int64_t) * L.hkv);
   const size_t o_b = w.take(sizeof(int64_t) * p.nseg * p.nblk);
-  const size_t o_e = w.take(sizeof(int64_t) * p.nseg * p.nblk);
   const size_t o_u = w.take(sizeof(int64_t) * p.nseg * p.nblk);
   const size_t o_d = w.take(sizeof(double) * p.nseg * p.nblk);
   if (total) *total = w.off;
@@ -777,7 +765,6 @@ AllocWs carve(const Layer& L, int stage, char* ws, size_t* total) {
     a.rbad = reinterpret_cast<int32_t*>(ws + o_rb);
     a.rcount = reinterpret_cast<int64_t*>(ws + o_r);
     a.bsum = reinterpret_cast<int64_t*>(ws + o_b);
-    a.bexcl = reinterpret_cast<int64_t*>(ws + o_e);
     a.used_part = reinterpret_cast<int64_t*>(ws + o_u);
     a.dist_part = reinterpret_cast<double*>(ws + o_d);
   }
@@ -800,11 +787,9 @@ void launch_passes(const AllocWs& a, const Plan& p, const Layer& L, int stage, c
   }
   if (topk) {
     alloc_ties<true, UPT><<<g2, 256, 0, s>>>(a, weight, nullptr, p.seg_len, stage, L.d);
-    alloc_tie_scan<<<p.nseg, 256, 0, s>>>(a, p.nblk);
     alloc_assign<true, UPT><<<g2, 256, 0, s>>>(a, weight, nullptr, p.seg_len, stage, L.d, keep_bits, bits_out);
   } else {
     alloc_ties<false, UPT><<<g2, 256, 0, s>>>(a, weight, sigma, p.seg_len, stage, L.d);
-    alloc_tie_scan<<<p.nseg, 256, 0, s>>>(a, p.nblk);
     alloc_assign<false, UPT><<<g2, 256, 0, s>>>(a, weight, sigma, p.seg_len, stage, L.d, keep_bits, bits_out);
   }
 }
