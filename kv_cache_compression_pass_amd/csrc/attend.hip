@@ -10,9 +10,11 @@
 //   K_hat -> LDS as a bf16 hi/lo pair (K_hat = hi + lo to ~2^-17; the bf16 query is exact, so
 //            q.K_hat = q.hi + q.lo is two bf16 matrix-core products with fp32 accumulation),
 //   V_hat -> LDS transposed as fp16 [channel][token],
-// each thread unpacking a run of codes of one channel (K) or one token's group (V) from a
-// 64-bit window with shifts (no divisions); the channel order by width keeps the lanes of a
-// wave on one width.  Then S = K_hat Q^T (32x32x16 bf16), an online base-2 softmax per row,
+// each thread unpacking a run of codes of one channel (K) or two tokens' channel run (V) from
+// a 64-bit window with shifts (no divisions).  Two LDS buffers hold consecutive groups: while
+// the block multiplies group j it decodes group j+1 into the other buffer (one barrier per
+// group), and group j+2's words are in flight in registers.  Then S = K_hat Q^T (32x32x16
+// bf16, the hi and lo products in two chains), an online base-2 softmax per row,
 // and O^T += V_hat^T P^T (32x32x16 f16).  In both products a lane owns one query row, so the
 // softmax statistics and the output rescale stay in-lane.  P^T is taken straight from the S
 // accumulator: lane l holds keys 8(i/4) + 4(l/32) + i%4, and the V_hat^T operand is read with
