@@ -632,8 +632,9 @@ score_partial(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 }
 
 // SUM: w[g][t] = sum over the group's (head, row tile) pairs that see t.  Four lanes share a
-// key: lane r sums the pairs j = r, r+4, ... (head-major, row tiles ascending), then the four
-// sums are combined as (s0 + s1) + (s2 + s3): a fixed order.
+// key: for each head in turn, lane r adds the row tiles rt0 + r, rt0 + r + 4, ... in two
+// interleaved chains (independent loads in flight), then the four lanes' sums are combined as
+// (s0 + s1) + (s2 + s3): a fixed order.
 __global__ void __launch_bounds__(256)
 score_reduce_sum(const float* __restrict__ part, float* __restrict__ scores, int Hkv, int G,
                  int nRT, int64_t N, int64_t Nq, int causal, int64_t Npad) {
@@ -648,13 +649,18 @@ score_reduce_sum(const float* __restrict__ part, float* __restrict__ scores, int
     const int64_t rel = t - (N - Nq);                 // first row index that sees t
     rt0 = rel > 0 ? (int)(rel / kRowsPerBlock) : 0;
   }
-  const int nrt = nRT - rt0;
-  const int terms = G * nrt;
   float s = 0.f;
   if (ok) {
-    for (int j = r; j < terms; j += 4) {
-      const int hl = j / nrt, rt = rt0 + j % nrt;
-      s += part[((int64_t)(g * G + hl) * nRT + rt) * Npad + t];
+    for (int hl = 0; hl < G; ++hl) {
+      const float* p = part + ((int64_t)(g * G + hl) * nRT) * Npad + t;
+      float a0 = 0.f, a1 = 0.f;
+      int rt = rt0 + r;
+      for (; rt + 4 < nRT; rt += 8) {
+        a0 += p[(int64_t)rt * Npad];
+        a1 += p[(int64_t)(rt + 4) * Npad];
+      }
+      if (rt < nRT) a0 += p[(int64_t)rt * Npad];
+      s += a0 + a1;
     }
   }
   const float s1 = __shfl_xor(s, 1, 64);
