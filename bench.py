@@ -37,8 +37,8 @@ CPU_SAMPLE_SECONDS = 12.0      # oracle sample: KV heads are added until this mu
 # scaled by the same counters on a plain copy of known size (profiles/hbm_counters_*.md).
 # A figure holds only for the scorer source it was measured on; otherwise traffic is null.
 MEASURED_TRAFFIC = {
-    "llama8b_prefill_n8192": {"bytes": 91862810,
-                              "score_src_sha256": "f82d8658e023da47f0f53c8db3dfa35dff47f0f18eb9391ee25f11d30fc29b8d"},
+    "llama8b_prefill_n8192": {"bytes": 91862467,
+                              "score_src_sha256": "8a6446159db3b85d56de0cbd9a711eaa8ddd6d510debf9133ff59960e1185e5f"},
 }
 
 
