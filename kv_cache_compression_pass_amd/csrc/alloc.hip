@@ -261,6 +261,19 @@ alloc_small(const float* __restrict__ weight, const float* __restrict__ sigma,
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int U = (stage == KVC_ALLOC_V_TOKENS) ? (int)(Hkv * N) : Hkv * d;
+  // thread tid owns units 2 tid and 2 tid + 1 (U <= 2048) throughout; their costs are read
+  // first, so the load overlaps the count of retained tokens
+  float cw[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int u = 2 * tid + j;
+    float c = 0.f;
+    if (u < U) {
+      c = weight[u];
+      if (sigma) c = c * sigma[u];
+    }
+    cw[j] = c;
+  }
   if (tid == 0) {
     bad = 0;
     kmin = ~0ull;
@@ -289,12 +302,13 @@ alloc_small(const float* __restrict__ weight, const float* __restrict__ sigma,
     *status = bad ? KVC_DEV_BAD_WIDTH : 0;
   }
   uint64_t tmn = ~0ull, tmx = 0;
-  for (int u = tid; u < U; u += 1024) {
-    float c = weight[u];
-    if (sigma) c = c * sigma[u];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int u = 2 * tid + j;
+    if (u >= U) continue;
     const int64_t s = (stage == KVC_ALLOC_V_TOKENS) ? (int64_t)d : (int64_t)rc[u / d];
     uint64_t kk[4];
-    unit_keys(c, s, kk);
+    unit_keys(cw[j], s, kk);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       keys[u * 4 + k] = kk[k];
@@ -393,9 +407,7 @@ alloc_small(const float* __restrict__ weight, const float* __restrict__ sigma,
     bits_out[u] = (uint8_t)b;
     const int64_t s = (stage == KVC_ALLOC_V_TOKENS) ? (int64_t)d : (int64_t)rc[u / d];
     used += s * (int64_t)b;
-    float c = weight[u];
-    if (sigma) c = c * sigma[u];
-    dist += ldexp((double)c, -(int)b);
+    dist += ldexp((double)cw[j], -(int)b);
   }
   const int64_t used_tot = block_scan_incl(used, wave_tot);
   // distortion: fixed-order tree within each wave, then the 16 wave sums in order
