@@ -62,32 +62,38 @@ chanw_partial(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   }
 }
 
-// One block per KV head: thread (src, c) sums its partials in ascending block order.
-__global__ void __launch_bounds__(256)
+// One block per KV head.  Four threads share each (src, c): thread q sums the q-th quarter of
+// the partials in ascending block order, eight independent loads at a time, and the four
+// sums are combined as (s0 + s1) + (s2 + s3): a fixed order.
+__global__ void __launch_bounds__(1024)
 chanw_finish(const double* __restrict__ part, float* __restrict__ w_c, int D, int G, int64_t N,
              int64_t Nq, int nblk, double scale) {
-  __shared__ double sums[2][128];
+  __shared__ double sums[2][4][128];
   const int g = blockIdx.x;
-  const int src = threadIdx.x / D;
   const int c = threadIdx.x % D;
+  const int q = (threadIdx.x / D) & 3;
+  const int src = threadIdx.x / (4 * D);
   if (src < 2) {
     const int64_t rows = src == 0 ? (int64_t)G * Nq : N;
     const int nb = (int)((rows + kRowsPerBlock - 1) / kRowsPerBlock);
+    const int b0 = (int)((int64_t)nb * q / 4), b1 = (int)((int64_t)nb * (q + 1) / 4);
     const double* p = part + (((int64_t)g * 2 + src) * nblk) * D + c;
-    double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
-    int b = 0;
-    for (; b + 4 <= nb; b += 4) {
-      s0 += p[(int64_t)b * D];
-      s1 += p[(int64_t)(b + 1) * D];
-      s2 += p[(int64_t)(b + 2) * D];
-      s3 += p[(int64_t)(b + 3) * D];
+    double a[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    int b = b0;
+    for (; b + 8 <= b1; b += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a[u] += p[(int64_t)(b + u) * D];
     }
-    for (; b < nb; ++b) s0 += p[(int64_t)b * D];
-    sums[src][c] = (s0 + s1) + (s2 + s3);
+    for (; b < b1; ++b) a[0] += p[(int64_t)b * D];
+    sums[src][q][c] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
   }
   __syncthreads();
-  if (threadIdx.x < D)
-    w_c[(int64_t)g * D + threadIdx.x] = (float)(scale * sqrt(sums[0][threadIdx.x]) * sqrt(sums[1][threadIdx.x]));
+  if (threadIdx.x < D) {
+    const int cc = threadIdx.x;
+    const double sq = (sums[0][0][cc] + sums[0][1][cc]) + (sums[0][2][cc] + sums[0][3][cc]);
+    const double sk = (sums[1][0][cc] + sums[1][1][cc]) + (sums[1][2][cc] + sums[1][3][cc]);
+    w_c[(int64_t)g * D + cc] = (float)(scale * sqrt(sq) * sqrt(sk));
+  }
 }
 
 int nblk_of(const Layer& L) {
@@ -114,7 +120,7 @@ hipError_t launch_channel_weights(const Layer& L, const uint16_t* q, const uint1
     chanw_partial<128><<<grid, 256, 0, s>>>(q, k, part, L.G, L.n, L.nq, nblk);
   else
     chanw_partial<64><<<grid, 256, 0, s>>>(q, k, part, L.G, L.n, L.nq, nblk);
-  chanw_finish<<<(unsigned)L.hkv, 256, 0, s>>>(part, w_c, L.d, L.G, L.n, L.nq, nblk, L.scale);
+  chanw_finish<<<(unsigned)L.hkv, 1024, 0, s>>>(part, w_c, L.d, L.G, L.n, L.nq, nblk, L.scale);
   return hipGetLastError();
 }
 
