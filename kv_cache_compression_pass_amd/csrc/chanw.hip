@@ -88,7 +88,7 @@ chanw_finish(const double* __restrict__ part, float* __restrict__ w_c, int D, in
     sums[src][q][c] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
   }
   __syncthreads();
-  if (threadIdx.x < D) {
+  if ((int)threadIdx.x < D) {
     const int cc = threadIdx.x;
     const double sq = (sums[0][0][cc] + sums[0][1][cc]) + (sums[0][2][cc] + sums[0][3][cc]);
     const double sk = (sums[1][0][cc] + sums[1][1][cc]) + (sums[1][2][cc] + sums[1][3][cc]);
