@@ -5,7 +5,7 @@
 //
 // Kernels, one stream, per KV head g (R = G * Nq stacked rows, n = n_c + m keys):
 //   row LSE        the scorer's pass 1 over the n keys                          (score.hip)
-//   ridge_probs    P[r][t] = exp(s q_r . k_t - l_r), fp32, 64 x 64 tiles, VALU dot products
+//   ridge_probs    P[r][t] = exp(s q_r . k_t - l_r), fp32, 64 x 64 tiles, bf16 matrix-core products
 //   ridge_resid    T = Y - P_r V_r (fp32), 64 x 64 tiles over (rows, channels)
 //   ridge_gram     M = P_c^T P_c and B = P_c^T T on the fp64 matrix cores (each product of two
 //                  fp32 values is exact in fp64), the row sum split in kSplit fixed parts
@@ -102,69 +102,65 @@ RidgeWs carve(const Layer& L, const RidgeDims& r, char* ws, size_t* total) {
 
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// P[g][r][t] = exp(s q_r . k_t - l_r) (0 where masked).  Block: 64 rows x 64 keys of head g,
-// 256 threads as 16 x 16, each 4 rows x 4 keys; Q and K tiles staged transposed in LDS as fp32.
+// A[r][t] = exp(s q_r . k_t - l_r) on the bf16 matrix cores (each product exact, fp32 sums,
+// like the scorer's pass 1).  Block = 64 rows x 64 keys; wave w takes the 32 x 32 quarter
+// (w / 2, w % 2) with the query rows as the A operand and the keys as the B operand, so a
+// lane's accumulator holds one key column of 16 rows and the 32 lanes of a row store 32
+// consecutive keys.  The rows' LSE (base 2) and last visible key are laid out once in LDS.
 template <int D>
 __global__ void __launch_bounds__(256)
 ridge_probs(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ lse,
             float* __restrict__ P, RidgeDims r, float c_log2) {
-  __shared__ float qT[D][kT];
-  __shared__ float kT_[D][kT];
+  constexpr int KS = D / 16;
+  constexpr float kLog2e = 1.4426950408889634f;
+  __shared__ float l2s[kT];
+  __shared__ int64_t lasts[kT];
   const int g = blockIdx.z;
-  const int64_t r0 = (int64_t)blockIdx.y * kT, t0 = (int64_t)blockIdx.x * kT;
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  for (int e = tid; e < kT * (D / 8); e += 256) {
-    const int row = e / (D / 8), c8 = e % (D / 8);
-    const int64_t rr = r0 + row;
-    uint4 qv = make_uint4(0, 0, 0, 0), kv = make_uint4(0, 0, 0, 0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lo = lane & 31, hi = lane >> 5;
+  const int64_t r0 = (int64_t)blockIdx.y * kT;
+  if (threadIdx.x < kT) {
+    const int64_t rr = r0 + threadIdx.x;
+    float l2 = -__builtin_inff();
+    int64_t last = -1;
     if (rr < r.R) {
-      const int64_t h = (int64_t)g * r.G + rr / r.nq, i = rr % r.nq;
-      qv = *reinterpret_cast<const uint4*>(q + (h * r.nq + i) * D + c8 * 8);
+      const int64_t h = (int64_t)g * r.G + rr / r.nq, qi = rr % r.nq;
+      const float l = lse[h * r.nq + qi];
+      if (l > -__builtin_inff()) {
+        l2 = l * kLog2e;
+        last = r.causal ? r.n - r.nq + qi : r.n - 1;      // last visible key
+      }
     }
-    const int64_t tt = t0 + row;
-    if (tt < r.n) kv = *reinterpret_cast<const uint4*>(k + ((int64_t)g * r.n + tt) * D + c8 * 8);
-    const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w}, kw[4] = {kv.x, kv.y, kv.z, kv.w};
+    l2s[threadIdx.x] = l2;
+    lasts[threadIdx.x] = last;
+  }
+  const int rw = (wave >> 1) * 32;                          // the wave's rows and keys in the tile
+  const int64_t tcol = (int64_t)blockIdx.x * kT + (wave & 1) * 32 + lo;   // this lane's key
+  const int64_t rr = r0 + rw + lo;                          // this lane's A-operand row
+  const uint16_t* qp = nullptr;
+  if (rr < r.R) {
+    const int64_t h = (int64_t)g * r.G + rr / r.nq, qi = rr % r.nq;
+    qp = q + (h * r.nq + qi) * D;
+  }
+  const uint16_t* kp = tcol < r.n ? k + ((int64_t)g * r.n + tcol) * D : nullptr;
+  f32x16 acc;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      qT[c8 * 8 + 2 * u][row] = __uint_as_float(qw[u] << 16);
-      qT[c8 * 8 + 2 * u + 1][row] = __uint_as_float(qw[u] & 0xFFFF0000u);
-      kT_[c8 * 8 + 2 * u][row] = __uint_as_float(kw[u] << 16);
-      kT_[c8 * 8 + 2 * u + 1][row] = __uint_as_float(kw[u] & 0xFFFF0000u);
-    }
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const uint4 a = qp ? *reinterpret_cast<const uint4*>(qp + ks * 16 + 8 * hi) : make_uint4(0, 0, 0, 0);
+    const uint4 b = kp ? *reinterpret_cast<const uint4*>(kp + ks * 16 + 8 * hi) : make_uint4(0, 0, 0, 0);
+    acc = mfma32(as_bf16x8(a), as_bf16x8(b), acc);
   }
   __syncthreads();
-  float acc[4][4];
+  if (tcol >= r.n) return;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-#pragma unroll 4
-  for (int c = 0; c < D; ++c) {
-    const float4 a = *reinterpret_cast<const float4*>(&qT[c][ty * 4]);
-    const float4 b = *reinterpret_cast<const float4*>(&kT_[c][tx * 4]);
-    const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
-  }
-  constexpr float kLog2e = 1.4426950408889634f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t rr = r0 + ty * 4 + i;
-    if (rr >= r.R) continue;
-    const int64_t h = (int64_t)g * r.G + rr / r.nq, qi = rr % r.nq;
-    const float l = lse[h * r.nq + qi];
-    const float l2 = l * kLog2e;
-    const int64_t last = r.causal ? r.n - r.nq + qi : r.n - 1;      // last visible key
-    float* prow = P + ((int64_t)g * r.R + rr) * r.n;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t tt = t0 + tx * 4 + j;
-      if (tt >= r.n) continue;
-      const bool vis = tt <= last && l > -__builtin_inff();
-      prow[tt] = vis ? exp2f(fmaf(acc[i][j], c_log2, -l2)) : 0.f;
-    }
+  for (int i = 0; i < 16; ++i) {
+    const int rl = rw + acc_row(i, hi);
+    const int64_t row = r0 + rl;
+    if (row >= r.R) continue;
+    const bool vis = tcol <= lasts[rl];
+    P[((int64_t)g * r.R + row) * r.n + tcol] = vis ? exp2f(fmaf(acc[i], c_log2, -l2s[rl])) : 0.f;
   }
 }
 
