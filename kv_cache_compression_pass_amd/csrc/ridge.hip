@@ -6,7 +6,7 @@
 // Kernels, one stream, per KV head g (R = G * Nq stacked rows, n = n_c + m keys):
 //   row LSE        the scorer's pass 1 over the n keys                          (score.hip)
 //   ridge_probs    P[r][t] = exp(s q_r . k_t - l_r), fp32, 64 x 64 tiles, bf16 matrix-core products
-//   ridge_resid    T = Y - P_r V_r (fp32), 64 x 64 tiles over (rows, channels)
+//   ridge_resid    T = Y - P_r V_r (fp32), 64 x 64 tiles over (rows, channels), bf16 matrix cores
 //   ridge_gram     M = P_c^T P_c and B = P_c^T T on the fp64 matrix cores (each product of two
 //                  fp32 values is exact in fp64), the row sum split in kSplit fixed parts
 //   ridge_sum      M += lambda I (identity on the padding), the parts added in fixed order
@@ -100,7 +100,6 @@ RidgeWs carve(const Layer& L, const RidgeDims& r, char* ws, size_t* total) {
   return w;
 }
 
-__device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // A[r][t] = exp(s q_r . k_t - l_r) on the bf16 matrix cores (each product exact, fp32 sums,
 // like the scorer's pass 1).  Block = 64 rows x 64 keys; wave w takes the 32 x 32 quarter
@@ -164,53 +163,62 @@ ridge_probs(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
   }
 }
 
-// T[g][r][c] = Y[h][i][c] - sum_{t < m} P[g][r][n_c + t] V_r[g][t][c].  Block: 64 rows x 64
-// channels; the t sum in chunks of 32 staged in LDS.
+// T = Y - A_r V_r (fp32) on the bf16 matrix cores: A_r's fp32 weights enter as a bf16 hi + lo
+// pair (exact to about 2^-17 of each weight) and V_r is bf16, so each product pair is exact and
+// the sums are fp32.  Block = 64 rows x 64 channels; wave w takes the 32 x 32 quarter (w / 2,
+// w % 2).  Per chunk of 64 retained keys the block stages V_r^T in LDS (channel-major, so a
+// lane's 8 consecutive keys are one 16-byte read); the weights come straight from global.
 template <int D>
 __global__ void __launch_bounds__(256)
 ridge_resid(const float* __restrict__ P, const uint16_t* __restrict__ v_r, const float* __restrict__ y,
             float* __restrict__ T, RidgeDims r) {
-  __shared__ float pT[32][kT];
-  __shared__ float vS[32][kT];
+  __shared__ __attribute__((aligned(16))) uint16_t vT[kT][kT + 8];   // [channel][key]
   const int g = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lo = lane & 31, hi = lane >> 5;
   const int64_t r0 = (int64_t)blockIdx.y * kT;
   const int c0 = blockIdx.x * kT;
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  float acc[4][4];
+  const int rw = (wave >> 1) * 32, cw = (wave & 1) * 32;
+  const int64_t arow = r0 + rw + lo;                        // this lane's A-operand row
+  const float* prow = arow < r.R ? P + ((int64_t)g * r.R + arow) * r.n + r.nc : nullptr;
+  f32x16 acc, acc_lo;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-  for (int64_t s0 = 0; s0 < r.m; s0 += 32) {
-    for (int e = tid; e < 32 * kT; e += 256) {
-      const int row = e / 32, tt = e % 32;               // P: consecutive threads, consecutive keys
-      const int64_t rr = r0 + row, t = s0 + tt;
-      pT[tt][row] = (rr < r.R && t < r.m) ? P[((int64_t)g * r.R + rr) * r.n + r.nc + t] : 0.f;
-      const int vt = e / kT, vc = e % kT;                // V: consecutive threads, consecutive channels
-      const int64_t t2 = s0 + vt;
-      vS[vt][vc] = (t2 < r.m) ? bf16f(v_r[((int64_t)g * r.m + t2) * D + c0 + vc]) : 0.f;
+  for (int i = 0; i < 16; ++i) acc[i] = acc_lo[i] = 0.f;
+  for (int64_t s0 = 0; s0 < r.m; s0 += kT) {
+    __syncthreads();                                        // the previous chunk's reads are done
+    for (int e = threadIdx.x; e < kT * kT; e += 256) {      // V_r rows: consecutive threads, channels
+      const int t = e / kT, ch = e % kT;
+      const int64_t tt = s0 + t;
+      vT[ch][t] = tt < r.m ? v_r[((int64_t)g * r.m + tt) * D + c0 + ch] : (uint16_t)0;
     }
     __syncthreads();
-#pragma unroll 8
-    for (int tt = 0; tt < 32; ++tt) {
-      const float4 a = *reinterpret_cast<const float4*>(&pT[tt][ty * 4]);
-      const float4 b = *reinterpret_cast<const float4*>(&vS[tt][tx * 4]);
-      const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int ks = 0; ks < kT / 16; ++ks) {
+      const int64_t t0 = s0 + ks * 16 + 8 * hi;             // this lane's 8 keys
+      float pv[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+      for (int u = 0; u < 8; ++u) pv[u] = (prow && t0 + u < r.m) ? prow[t0 + u] : 0.f;
+      uint32_t ph[4], pl[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const __bf16 h0 = (__bf16)pv[2 * u], h1 = (__bf16)pv[2 * u + 1];
+        const __bf16 l0 = (__bf16)(pv[2 * u] - (float)h0), l1 = (__bf16)(pv[2 * u + 1] - (float)h1);
+        ph[u] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        pl[u] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+      }
+      const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4*>(&vT[cw + lo][ks * 16 + 8 * hi]));
+      acc = mfma32(as_bf16x8(make_uint4(ph[0], ph[1], ph[2], ph[3])), b, acc);
+      acc_lo = mfma32(as_bf16x8(make_uint4(pl[0], pl[1], pl[2], pl[3])), b, acc_lo);
     }
-    __syncthreads();
   }
+  // acc[i]: row rw + acc_row(i, hi), channel cw + lo
+  const int ch = c0 + cw + lo;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t rr = r0 + ty * 4 + i;
+  for (int i = 0; i < 16; ++i) {
+    const int64_t rr = r0 + rw + acc_row(i, hi);
     if (rr >= r.R) continue;
     const int64_t h = (int64_t)g * r.G + rr / r.nq, qi = rr % r.nq;
-    const float4 yv = *reinterpret_cast<const float4*>(y + (h * r.nq + qi) * D + c0 + tx * 4);
-    *reinterpret_cast<float4*>(T + ((int64_t)g * r.R + rr) * D + c0 + tx * 4) =
-        make_float4(yv.x - acc[i][0], yv.y - acc[i][1], yv.z - acc[i][2], yv.w - acc[i][3]);
+    T[((int64_t)g * r.R + rr) * D + ch] = y[(h * r.nq + qi) * D + ch] - (acc[i] + acc_lo[i]);
   }
 }
 
