@@ -167,7 +167,8 @@ ridge_probs(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
 // pair (exact to about 2^-17 of each weight) and V_r is bf16, so each product pair is exact and
 // the sums are fp32.  Block = 64 rows x 64 channels; wave w takes the 32 x 32 quarter (w / 2,
 // w % 2).  Per chunk of 64 retained keys the block stages V_r^T in LDS (channel-major, so a
-// lane's 8 consecutive keys are one 16-byte read); the weights come straight from global.
+// lane's 8 consecutive keys are one 16-byte read) from registers loaded during the previous
+// chunk; a lane's weights of the chunk are requested before the chunk's barriers.
 template <int D>
 __global__ void __launch_bounds__(256)
 ridge_resid(const float* __restrict__ P, const uint16_t* __restrict__ v_r, const float* __restrict__ y,
@@ -184,25 +185,42 @@ ridge_resid(const float* __restrict__ P, const uint16_t* __restrict__ v_r, const
   f32x16 acc, acc_lo;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = acc_lo[i] = 0.f;
-  for (int64_t s0 = 0; s0 < r.m; s0 += kT) {
-    __syncthreads();                                        // the previous chunk's reads are done
-    for (int e = threadIdx.x; e < kT * kT; e += 256) {      // V_r rows: consecutive threads, channels
-      const int t = e / kT, ch = e % kT;
-      const int64_t tt = s0 + t;
-      vT[ch][t] = tt < r.m ? v_r[((int64_t)g * r.m + tt) * D + c0 + ch] : (uint16_t)0;
+  // V_r of the next chunk waits in registers while the current one is multiplied
+  constexpr int kVPer = kT * kT / 256;                      // 16 values per thread
+  uint16_t vn[kVPer];
+  auto load_v = [&](int64_t s0) {
+#pragma unroll
+    for (int u = 0; u < kVPer; ++u) {
+      const int e = threadIdx.x + 256 * u;                  // V_r rows: consecutive threads, channels
+      const int64_t tt = s0 + e / kT;
+      vn[u] = tt < r.m ? v_r[((int64_t)g * r.m + tt) * D + c0 + e % kT] : (uint16_t)0;
     }
+  };
+  load_v(0);
+  for (int64_t s0 = 0; s0 < r.m; s0 += kT) {
+    float pv[kT / 16][8];                                   // this lane's weights of the chunk
+#pragma unroll
+    for (int ks = 0; ks < kT / 16; ++ks) {
+      const int64_t t0 = s0 + ks * 16 + 8 * hi;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pv[ks][u] = (prow && t0 + u < r.m) ? prow[t0 + u] : 0.f;
+    }
+    __syncthreads();                                        // the previous chunk's reads are done
+#pragma unroll
+    for (int u = 0; u < kVPer; ++u) {
+      const int e = threadIdx.x + 256 * u;
+      vT[e % kT][e / kT] = vn[u];
+    }
+    if (s0 + kT < r.m) load_v(s0 + kT);
     __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < kT / 16; ++ks) {
-      const int64_t t0 = s0 + ks * 16 + 8 * hi;             // this lane's 8 keys
-      float pv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) pv[u] = (prow && t0 + u < r.m) ? prow[t0 + u] : 0.f;
       uint32_t ph[4], pl[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const __bf16 h0 = (__bf16)pv[2 * u], h1 = (__bf16)pv[2 * u + 1];
-        const __bf16 l0 = (__bf16)(pv[2 * u] - (float)h0), l1 = (__bf16)(pv[2 * u + 1] - (float)h1);
+        const float p0 = pv[ks][2 * u], p1 = pv[ks][2 * u + 1];
+        const __bf16 h0 = (__bf16)p0, h1 = (__bf16)p1;
+        const __bf16 l0 = (__bf16)(p0 - (float)h0), l1 = (__bf16)(p1 - (float)h1);
         ph[u] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
         pl[u] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
       }
