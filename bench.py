@@ -6,8 +6,10 @@ One step is one pass of the whole path over one layer's cache already resident i
                             -> kvc_quantize_pack
   max config (3):           kvc_row_lse -> kvc_score_tokens(MAX) -> kvc_allocate_bits(TOPK)
                             -> kvc_quantize_pack
-The default workload is the Llama-3-8B-like prefill layer (32 query heads / 8 KV heads,
-d = 128, N = Nq = 8192, causal, bf16, 4 outlier K channels per KV head, 3 bits/element).
+The default workload is the largest single-GPU one: the decode-time 128k cache (32 query heads /
+8 KV heads, d = 128, N = 131072 cached keys, the last Nq = 512 positions as query rows, causal,
+bf16, 4 outlier K channels per KV head, 2 bits/element), whose 512 MiB of K and V do not fit the
+Infinity Cache, so its pack and attend figures are HBM figures.
 value = N / (mean step time over the timed steps).
 
 Prints ONE JSON line.  `roofline` is for the dominant kernel (pass 1 of the scorer,
@@ -16,7 +18,7 @@ the timed region.  The fidelity attend is timed after the timed region and repor
 (`attend`), together with a single-decode-row slice whose HBM traffic is the packed cache.
 `cpu_baseline` times the float64 oracle on a bounded sample on the host cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4] [--no-cpu-baseline]
 """
 
 import argparse
@@ -185,7 +187,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the bench: run a plain elementwise copy of MIB MiB (read MIB, "

@@ -180,6 +180,45 @@ def test_max_scores_and_topk(case):
     H.compare_packed(cache.to_numpy(), oracle.pack_cache(x["k"], x["v"], b_r, np.full((hkv, d), 16, np.uint8)))
 
 
+UNCHUNKED = [
+    # name, mode, H_q, H_kv, d, N, Nq, causal, D_h
+    ("sum_g16_d128_n2304", "sum", 128, 8, 128, 2304, 2304, True, 0),
+    ("sum_g4_d64_q_lt_n", "sum", 128, 32, 64, 2500, 2100, True, 0),
+    ("sum_g8_d128_noncausal", "sum", 128, 16, 128, 2600, 2304, False, 0),
+    ("max_g4_d64_n2048", "max", 128, 32, 64, 2048, 2048, True, 512),
+]
+
+
+@pytest.mark.parametrize("case", UNCHUNKED, ids=[c[0] for c in UNCHUNKED])
+def test_scorer_one_chunk_per_item(case):
+    """The scorer's launch shape for layers with at least 1024 (query head, 256-row tile) items:
+    each item takes its whole key range as one chunk, pass 1 writes the row LSE directly, and the
+    column reduction adds one partial per row tile (9 here, with a ragged last tile when Nq is not
+    a multiple of 256).  The full-size workloads take this path; here every row LSE and every
+    score column of every head is compared with the oracle."""
+    from tests import oracle_blocks as OB
+    name, mode, hq, hkv, d, N, Nq, causal, Dh = case
+    assert -(-Nq // 256) * hq >= 1024
+    print(f"case {name}: H_q={hq} H_kv={hkv} d={d} N={N} Nq={Nq} causal={causal} mode={mode}", flush=True)
+    x = make_inputs(hq, hkv, d, N, Nq, seed=zlib.crc32(name.encode()) % 1000, hidden_dim=Dh)
+    desc = H.desc_of(hq, hkv, d, N, Nq, causal)
+    q, k, v = H.dev_bf16(x["q"]), H.dev_bf16(x["k"]), H.dev_bf16(x["v"])
+    lse_t = H.row_lse(desc, q, k)
+    lse_r = OB.head_lse(x["q"], x["k"], list(range(hq)), causal=causal)
+    H.assert_abs(lse_t.cpu().numpy(), lse_r, 1e-4, "row_lse")
+    G = hq // hkv
+    if mode == "sum":
+        s_g = H.score_sum(desc, q, k, lse_t).cpu().numpy()
+        s_r = np.stack([OB.group_scores_sum(x["q"], x["k"], lse_r[g * G:(g + 1) * G], g, causal=causal)
+                        for g in range(hkv)])
+        np.testing.assert_allclose(s_g.astype(np.float64).sum(axis=1), G * Nq, rtol=2e-5)
+    else:
+        s_g = H.score_max(desc, q, k, lse_t, H.dev_bf16(x["hidden"]), H.dev_bf16(x["w_o"]), v).cpu().numpy()
+        s_r = np.stack([OB.group_scores_max(x["q"], x["k"], lse_r[g * G:(g + 1) * G], x["hidden"], x["w_o"],
+                                            x["v"], g, causal=causal) for g in range(hkv)])
+    H.assert_rel(s_g, s_r, 1e-3, what=f"token scores ({mode})")
+
+
 def test_allocation_ties_zeros_and_extremes():
     print("case allocation edge cases", flush=True)
     hkv, N, d = 3, 2000, 64

@@ -14,6 +14,7 @@ import kv_cache_compression_pass_amd as kvc
 import oracle
 from workloads import get_config, make_config_inputs
 from tests import gpu_helpers as H
+from tests import oracle_blocks as OB
 
 pytestmark = pytest.mark.gpu
 
@@ -72,12 +73,16 @@ def test_sum_config_full_size(ci):
     w_g = H.score_sum(desc, q, k, lse_t).cpu().numpy()
     np.testing.assert_allclose(w_g.astype(np.float64).sum(axis=1), cfg.gqa * Nq, rtol=2e-5)
     H.assert_rel(w_g[:, -TAIL:], _tail_scores(x, cfg), 1e-3, what="tail token scores")
-    if ci == 4:
-        # config 4 (Nq = 512): one KV head exactly, every column
-        G = cfg.gqa
-        lse_r = oracle.row_lse(x["q"][:G], x["k"][:1])
-        w_r = oracle.token_scores_sum(x["q"][:G], x["k"][:1], lse_r)
-        H.assert_rel(w_g[:1], w_r, 1e-3, what="head-0 token scores")
+    # whole KV heads: the LSE of every row of their query heads and every score column, so the
+    # many-partial column reduction the full-size launch takes is compared element by element
+    G = cfg.gqa
+    for g in ((0, hkv - 1) if ci == 1 else (0,)):
+        print(f"config {ci}: whole KV head {g} against the oracle", flush=True)
+        heads = list(range(g * G, (g + 1) * G))
+        lse_r = OB.head_lse(x["q"], x["k"], heads)
+        H.assert_abs(lse_g[heads], lse_r, 1e-4, f"row LSE of KV head {g}'s query heads")
+        w_r = OB.group_scores_sum(x["q"], x["k"], lse_r, g)
+        H.assert_rel(w_g[g], w_r, 1e-3, what=f"token scores of KV head {g}")
 
     print(f"config {ci}: channel weights", flush=True)
     wc_g = H.channel_weights(desc, q, k).cpu().numpy()
@@ -132,6 +137,13 @@ def test_config3_kvzip_full_size():
     s_r = oracle.token_scores_max(q_sub, x["k"], lse_sub, x["hidden"][r0:], x["w_o"], x["v"], tokens=cols)
     H.assert_rel(s_g[:, -TAIL:], s_r, 1e-3, what="tail KVzip+ scores")
     assert np.isfinite(s_g).all() and (s_g > 0).all()
+    g = hkv - 1
+    print(f"config 3: whole KV head {g} against the oracle", flush=True)
+    heads = list(range(g * cfg.gqa, (g + 1) * cfg.gqa))
+    lse_r = OB.head_lse(x["q"], x["k"], heads)
+    H.assert_abs(lse_t.cpu().numpy()[heads], lse_r, 1e-4, f"row LSE of KV head {g}'s query heads")
+    s_head = OB.group_scores_max(x["q"], x["k"], lse_r, x["hidden"], x["w_o"], x["v"], g)
+    H.assert_rel(s_g[g], s_head, 1e-3, what=f"KVzip+ scores of KV head {g}")
     print("config 3: top-k + pack", flush=True)
     s32 = _synthetic_weights((hkv, N), 1.0, seed=303)
     kk = math.floor(cfg.keep_fraction * N)
