@@ -6,6 +6,7 @@
  * cache to a mixed-width, partly evicted form:
  *
  *   kvc_row_lse            row log-sum-exp of the causal, scaled logits        (pass 1)
+ *   kvc_row_lse_noalloc    the same with the library's static scratch (no workspace)
  *   kvc_score_tokens       per-token scores, RDKV sum or KVzip+ max            (pass 2)
  *   kvc_channel_weights    RDKV K-channel weights
  *   kvc_allocate_bits      Lagrangian width allocation over {0,2,4,8,16}, or top-k keep
@@ -102,6 +103,19 @@ size_t kvc_workspace_size(int32_t op, const kvc_layer_desc* desc, int32_t mode);
  * float32 accumulation.  Workspace: kvc_workspace_size(KVC_OP_ROW_LSE, desc, 0) bytes. */
 kvc_status kvc_row_lse(const kvc_layer_desc* desc, const void* q, const void* k, float* lse,
                        void* ws, size_t ws_bytes, void* hip_stream);
+
+/* kvc_row_lse for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same kernels and the same result,
+ * with no workspace argument.  Its scratch (pass 1's per-chunk partials) is a static device
+ * array inside the library, 16 MiB per device, held from the first call on a device until the
+ * process ends; the call itself allocates nothing.  Layers whose kvc_workspace_size(
+ * KVC_OP_ROW_LSE, desc, 0) exceeds 16 MiB are rejected with KVC_ERR_UNSUPPORTED (the decode
+ * cache of 32 query heads x 512 rows x 131072 keys needs 8 MiB).  Every call on one device
+ * shares that scratch, so calls that overlap on one device (concurrent streams or host threads)
+ * race and must be ordered by the caller; nothing in it needs clearing between calls.
+ * Errors: as kvc_row_lse, plus KVC_ERR_UNSUPPORTED for a layer beyond the scratch. */
+kvc_status kvc_row_lse_noalloc(const kvc_layer_desc* desc, const void* q, const void* k, float* lse,
+                               void* hip_stream);
 
 typedef enum { KVC_SCORE_SUM = 0, KVC_SCORE_MAX = 1 } kvc_score_mode;
 

@@ -14,6 +14,6 @@ from .api import (  # noqa: F401
     KvcError, PackedCache, alloc_result_buffer, bf16_tensor, decode_alloc_result, kvc_allocate_bits,
     kvc_keep_threshold, kvc_channel_weights, kvc_compressed_attend, kvc_compressed_attend_append,
     kvc_fidelity_terms, kvc_get_device_status, kvc_pilot_budgets, kvc_packed_capacity, kvc_ridge_value_fit,
-    kvc_quantize_pack, kvc_row_lse, kvc_score_tokens, kvc_version, kvc_workspace_size, make_desc,
+    kvc_quantize_pack, kvc_row_lse, kvc_row_lse_noalloc, kvc_score_tokens, kvc_version, kvc_workspace_size, make_desc,
     workspace,
 )

@@ -29,7 +29,7 @@ DEV_BAD_CACHE = 2
 DEV_NOT_SPD = 4
 
 EXPORTED = (
-    "kvc_workspace_size", "kvc_row_lse", "kvc_score_tokens", "kvc_channel_weights",
+    "kvc_workspace_size", "kvc_row_lse", "kvc_row_lse_noalloc", "kvc_score_tokens", "kvc_channel_weights",
     "kvc_allocate_bits", "kvc_keep_threshold", "kvc_packed_capacity", "kvc_quantize_pack",
     "kvc_compressed_attend", "kvc_compressed_attend_append", "kvc_fidelity_terms", "kvc_pilot_budgets",
     "kvc_ridge_value_fit", "kvc_get_device_status", "kvc_status_string", "kvc_last_error", "kvc_version",
@@ -92,6 +92,7 @@ def load():
     lib.kvc_workspace_size.argtypes = [I32, D, I32]
     lib.kvc_workspace_size.restype = S
     lib.kvc_row_lse.argtypes = [D, P, P, P, P, S, P]
+    lib.kvc_row_lse_noalloc.argtypes = [D, P, P, P, P]
     lib.kvc_score_tokens.argtypes = [D, I32, P, P, P, ctypes.POINTER(KvzipArgs), P, P, S, P]
     lib.kvc_channel_weights.argtypes = [D, P, P, P, P, S, P]
     lib.kvc_allocate_bits.argtypes = [D, I32, P, P, P, ctypes.c_double, ctypes.c_double,
@@ -107,7 +108,7 @@ def load():
                                       ctypes.POINTER(ctypes.c_int64)]
     lib.kvc_ridge_value_fit.argtypes = [D, ctypes.c_int64, P, P, P, P, ctypes.c_double, P, P, S, P]
     lib.kvc_get_device_status.argtypes = [P, ctypes.POINTER(I32), P]
-    for name in ("kvc_row_lse", "kvc_score_tokens", "kvc_channel_weights", "kvc_allocate_bits", "kvc_keep_threshold",
+    for name in ("kvc_row_lse", "kvc_row_lse_noalloc", "kvc_score_tokens", "kvc_channel_weights", "kvc_allocate_bits", "kvc_keep_threshold",
                  "kvc_packed_capacity", "kvc_quantize_pack", "kvc_compressed_attend",
                  "kvc_compressed_attend_append", "kvc_fidelity_terms", "kvc_pilot_budgets",
                  "kvc_ridge_value_fit", "kvc_get_device_status"):

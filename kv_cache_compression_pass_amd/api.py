@@ -111,6 +111,14 @@ def kvc_row_lse(desc, q, k, lse, ws=None, stream=None):
     _check(C.load().kvc_row_lse(ctypes.byref(desc), qp, kp, lp, wp, _nbytes(ws), _stream(stream)))
 
 
+def kvc_row_lse_noalloc(desc, q, k, lse, stream=None):
+    """kvc_row_lse with the library's static scratch instead of a workspace (allocates nothing)."""
+    hq, hkv, d, n, nq = _dims(desc)
+    a = (_arg(q, "q", BF16, hq * nq * d), _arg(k, "k", BF16, hkv * n * d), _arg(lse, "lse", F32, hq * nq))
+    qp, kp, lp = _addresses(*a)
+    _check(C.load().kvc_row_lse_noalloc(ctypes.byref(desc), qp, kp, lp, _stream(stream)))
+
+
 def kvc_score_tokens(desc, mode, q, k, lse, scores, ws, hidden=None, w_o=None, v=None,
                      hidden_dim=0, stream=None):
     hq, hkv, d, n, nq = _dims(desc)

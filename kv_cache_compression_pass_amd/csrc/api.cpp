@@ -188,6 +188,26 @@ kvc_status kvc_row_lse(const kvc_layer_desc* desc, const void* q, const void* k,
                 "kvc_row_lse launch");
 }
 
+kvc_status kvc_row_lse_noalloc(const kvc_layer_desc* desc, const void* q, const void* k, float* lse,
+                               void* hip_stream) {
+  Layer L;
+  KVC_TRY(make_layer(desc, &L));
+  KVC_TRY(need_bf16(q, "q"));
+  KVC_TRY(need_bf16(k, "k"));
+  KVC_TRY(need_ptr(lse, 4, "lse"));
+  const size_t need = lse_ws_bytes(L);
+  if (need > kLseScratchBytes)
+    return fail(KVC_ERR_UNSUPPORTED,
+                "kvc_row_lse_noalloc: this layer needs %zu bytes of scratch, more than the %zu bytes the library "
+                "holds (call kvc_row_lse with a workspace)", need, kLseScratchBytes);
+  KVC_TRY(need_device());
+  char* scratch_dev = nullptr;
+  hipError_t e = row_lse_scratch(&scratch_dev);
+  if (e != hipSuccess) return hip_fail(e, "kvc_row_lse_noalloc: hipGetSymbolAddress(scratch)");
+  return finish(launch_row_lse(L, (const uint16_t*)q, (const uint16_t*)k, lse, scratch_dev, (hipStream_t)hip_stream),
+                "kvc_row_lse_noalloc launch");
+}
+
 kvc_status kvc_score_tokens(const kvc_layer_desc* desc, kvc_score_mode mode, const void* q,
                             const void* k, const float* lse, const kvc_kvzip_args* zip,
                             float* scores, void* ws, size_t ws_bytes, void* hip_stream) {

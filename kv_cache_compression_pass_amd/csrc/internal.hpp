@@ -42,6 +42,10 @@ size_t lse_ws_bytes(const Layer& L);
 size_t score_ws_bytes(const Layer& L, int mode, int hidden_dim);
 hipError_t launch_row_lse(const Layer& L, const uint16_t* q, const uint16_t* k, float* lse,
                           char* ws, hipStream_t s, int tag = 0);
+// The allocation-free row LSE: the library's static scratch (kLseScratchBytes per device) stands in
+// for the workspace.  row_lse_scratch() gives its address on the current device.
+constexpr size_t kLseScratchBytes = size_t(16) << 20;
+hipError_t row_lse_scratch(char** out);
 hipError_t launch_score(const Layer& L, int mode, const uint16_t* q, const uint16_t* k,
                         const float* lse, const uint16_t* hidden, const uint16_t* w_o,
                         const uint16_t* v, int hidden_dim, float* scores, char* ws,

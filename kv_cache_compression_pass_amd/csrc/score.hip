@@ -17,10 +17,40 @@
 // its keys stay in that XCD's L2.  Pass 1 writes per-chunk (max, sum) partials that a tiny
 // kernel combines into l; pass 2 writes per-(head, row tile) column partials that a second
 // kernel reduces in a fixed order, so every result is bitwise reproducible.
+#include <mutex>
+
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace kvc {
+
+// Scratch of kvc_row_lse_noalloc: the per-chunk (max, sum) partials of pass 1, in a file-scope
+// device array instead of a caller's workspace.  Each device that loads the library holds its
+// own copy until the process ends.  Host code never uses the array's name as an address (on the
+// host it is only a stand-in): row_lse_scratch() asks the runtime for the device address once per
+// device and keeps it.
+static __device__ __align__(256) char scratch[kLseScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+char* g_scratch_dev[64] = {};
+}  // namespace
+
+hipError_t row_lse_scratch(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_dev[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
+}
 
 namespace {
 

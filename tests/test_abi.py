@@ -229,3 +229,17 @@ def test_ridge_fit_argument_errors(lib):
     # n_c == n_keys: no retained zone, v_r may be NULL; without a GPU the call stops at the device check
     st = f(ctypes.byref(d), 128, FAKE, FAKE, None, FAKE, 0.0, FAKE, FAKE, big, None)
     assert st not in (1, 2, 3)
+
+
+def test_row_lse_noalloc_rejects_layers_beyond_its_scratch(lib):
+    """The allocation-free row LSE holds 16 MiB of static scratch: a layer whose workspace would be
+    larger is refused on the host, before any device work (a fitting one reaches the device check)."""
+    big = _desc(n_q_heads=16, n_kv_heads=1, head_dim=128, n_keys=1 << 22, n_queries=1 << 12)
+    assert lib.kvc_workspace_size(0, ctypes.byref(big), 0) > 16 << 20
+    st = lib.kvc_row_lse_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, None)
+    assert st == 2
+    assert "16777216" in lib.kvc_last_error().decode()
+    small = _desc()
+    assert lib.kvc_workspace_size(0, ctypes.byref(small), 0) <= 16 << 20
+    assert lib.kvc_row_lse_noalloc(ctypes.byref(small), FAKE, FAKE, FAKE, None) == 4
+    assert lib.kvc_row_lse_noalloc(ctypes.byref(small), None, FAKE, FAKE, None) == 1
