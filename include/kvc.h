@@ -66,7 +66,9 @@ typedef enum {
   KVC_ERR_WORKSPACE = 3,     /* ws_bytes smaller than kvc_workspace_size()                  */
   KVC_ERR_NO_DEVICE = 4,     /* no HIP device, or the current device is not gfx950          */
   KVC_ERR_HIP = 5,           /* a HIP runtime call failed (detail in kvc_last_error())      */
-  KVC_ERR_DEVICE_DATA = 6    /* device-side data error (see kvc_get_device_status())        */
+  KVC_ERR_DEVICE_DATA = 6,   /* device-side data error (see kvc_get_device_status())        */
+  KVC_STATUS_INT32_MIN_ = -0x7FFFFFFF - 1,  /* (not statuses) these two give the enum the range */
+  KVC_STATUS_INT32_MAX_ = 0x7FFFFFFF        /* of int32_t                                        */
 } kvc_status;
 
 /* One attention layer.  Limits: H_q % H_kv == 0, 1 <= H_kv, H_q / H_kv <= 16,
@@ -117,7 +119,15 @@ kvc_status kvc_row_lse(const kvc_layer_desc* desc, const void* q, const void* k,
 kvc_status kvc_row_lse_noalloc(const kvc_layer_desc* desc, const void* q, const void* k, float* lse,
                                void* hip_stream);
 
-typedef enum { KVC_SCORE_SUM = 0, KVC_SCORE_MAX = 1 } kvc_score_mode;
+/* The enums of this header span the range of int32_t (their last two members), so any int32
+ * value is a valid argument of the enum type, and one outside the listed modes is refused with
+ * KVC_ERR_INVALID_ARG. */
+typedef enum {
+  KVC_SCORE_SUM = 0,
+  KVC_SCORE_MAX = 1,
+  KVC_SCORE_INT32_MIN_ = -0x7FFFFFFF - 1,
+  KVC_SCORE_INT32_MAX_ = 0x7FFFFFFF
+} kvc_score_mode;
 
 /* Extra inputs of the KVzip+ score (KVzap §2.1); required iff mode == KVC_SCORE_MAX. */
 typedef struct {
@@ -149,7 +159,9 @@ kvc_status kvc_channel_weights(const kvc_layer_desc* desc, const void* q, const 
 typedef enum {
   KVC_ALLOC_V_TOKENS = 0,    /* RDKV stage 2: units (g,t), size d                            */
   KVC_ALLOC_K_CHANNELS = 1,  /* RDKV stage 3: units (g,c), size R_g = #tokens with bits_v > 0 */
-  KVC_ALLOC_TOPK = 2         /* KVzip fixed budget: keep floor(rho*N) best tokens per head    */
+  KVC_ALLOC_TOPK = 2,        /* KVzip fixed budget: keep floor(rho*N) best tokens per head    */
+  KVC_ALLOC_INT32_MIN_ = -0x7FFFFFFF - 1,
+  KVC_ALLOC_INT32_MAX_ = 0x7FFFFFFF
 } kvc_alloc_stage;
 
 /* Allocation result, written to DEVICE memory by kvc_allocate_bits. */
@@ -255,10 +267,15 @@ kvc_status kvc_quantize_pack(const kvc_layer_desc* desc, const void* k, const vo
 
 /* Attention of Q (the last Nq = desc->n_queries rows of the sequence, [H_q][Nq][d]) over the
  * retained tokens of a packed cache, dequantised on the fly (x = zero + scale*code; width 0
- * channels are 0; width 16 exact): out f32 [H_q][Nq][d] and lse f32 [H_q][Nq]
+ * channels are 0; width 16 the stored bf16 value): out f32 [H_q][Nq][d] and lse f32 [H_q][Nq]
  * (RDKV §2.3 decode over packed zones; the two outputs whose errors form KVSculpt's loss,
  * §2).  A row with no visible retained token gets lse = -inf and out = 0.  The packed cache's
- * header must match desc (H_kv, d, N); a mismatch sets the device status. */
+ * header must match desc (H_kv, d, N); a mismatch sets the device status.
+ * Precision: logits use keys to 2^-17 relative (bf16 hi + lo) with float32 accumulation.  With
+ * more than 16 query rows per KV head the value products take fp16 operands: the probabilities,
+ * and V_hat scaled per KV head by a power of two that puts the head's largest |V_hat| in
+ * [2^14, 2^15), so any finite bf16 V keeps 11 significant bits (values below 2^-24 of the head's
+ * largest round to that absolute step).  With at most 16 rows they are float32. */
 kvc_status kvc_compressed_attend(const kvc_layer_desc* desc, const void* q,
                                  const kvc_packed_cache* cache, float* out, float* lse,
                                  void* ws, size_t ws_bytes, void* hip_stream);

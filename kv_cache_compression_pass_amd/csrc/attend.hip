@@ -9,7 +9,11 @@
 // Then for each group of 32 retained tokens (the K packing unit) it decodes
 //   K_hat -> LDS as a bf16 hi/lo pair (K_hat = hi + lo to ~2^-17; the bf16 query is exact, so
 //            q.K_hat = q.hi + q.lo is two bf16 matrix-core products with fp32 accumulation),
-//   V_hat -> LDS transposed as fp16 [channel][token],
+//   V_hat -> LDS transposed as fp16 [channel][token], scaled by 2^-E_g: E_g is chosen per KV head
+//            from a bound on |V_hat| over the whole packed head (attend_vbound), so that the
+//            largest value lands in [2^14, 2^15) and every value keeps fp16's 11 bits down to
+//            2^-24 of that bound, whatever the magnitude of V (the partial O is scaled back by
+//            2^E_g when it is written),
 // each thread unpacking a run of codes of one channel (K) or two tokens' channel run (V) from
 // a 64-bit window with shifts (no divisions).  Two LDS buffers hold consecutive groups: while
 // the block multiplies group j it decodes group j+1 into the other buffer (one barrier per
@@ -56,11 +60,69 @@ __device__ __forceinline__ uint64_t load_window(const uint32_t* w, int64_t wi, b
   return lo | (hi << 32);
 }
 
+// ---------------------------------------------------------------------------------------
+// Bound on |V_hat| per KV head, for the fp16 staging of V_hat in attend_split: the largest of
+// |zero| and |zero + scale * (2^b - 1)| over every (scale, zero) pair of the 2/4/8-bit zones (the
+// dequantiser fmaf(scale, code, zero) is monotone in the code, so these are its extremes) and of
+// |v| over the raw bf16 words of the 16-bit zone.  Non-negative floats order as their bit
+// patterns, so the bound is kept as uint32 bits and combined with atomicMax (order-free, so the
+// result does not depend on scheduling).
+// ---------------------------------------------------------------------------------------
+__global__ void attend_vbound_init(uint32_t* vb, int Hkv) {
+  if ((int)threadIdx.x < Hkv) vb[threadIdx.x] = 0u;
+}
+
+template <int D>
+__global__ void __launch_bounds__(256)
+attend_vbound(kvc_packed_cache cache, uint32_t* __restrict__ vb, int Hkv, int64_t N) {
+  constexpr int GPR = D / 32;
+  __shared__ uint32_t red[4];
+  const int64_t* H = cache.header;
+  if (H[0] != Hkv || H[1] != D || H[2] != N) return;   // reported by attend_split
+  const int g = blockIdx.y;
+  const int64_t* hp = H + KVC_HDR_GLOBAL + g * KVC_HDR_PER_HEAD;
+  const int64_t np0 = hp[0] * GPR, np1 = hp[1] * GPR, np2 = hp[2] * GPR;
+  const int64_t nw3 = hp[3] * GPR * 16;
+  const int64_t total = np0 + np1 + np2 + nw3;
+  const float2* par = reinterpret_cast<const float2*>(cache.v_par);
+  uint32_t m = 0u;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    if (i < np0 + np1 + np2) {
+      const int z = i < np0 ? 0 : (i < np0 + np1 ? 1 : 2);
+      const int64_t k = i - (z == 0 ? 0 : (z == 1 ? np0 : np0 + np1));
+      const float2 sz = par[hp[13 + z] + k];
+      const float top = (float)((1 << (2 << z)) - 1);
+      const uint32_t a = __float_as_uint(fabsf(sz.y));
+      const uint32_t b = __float_as_uint(fabsf(fmaf(sz.x, top, sz.y)));
+      m = max(m, max(a, b));
+    } else {
+      const uint32_t w = cache.v_words[hp[12] + (i - np0 - np1 - np2)];
+      m = max(m, max((w & 0x7FFFu) << 16, w & 0x7FFF0000u));
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t r = max(max(red[0], red[1]), max(red[2], red[3]));
+    if (r != 0u) atomicMax(vb + g, r);
+  }
+}
+
+// Power-of-two exponent E for the fp16 staging of a head whose |V_hat| bound has bits vb: the
+// bound times 2^-E lies in [2^14, 2^15) (E is clamped so that 2^E and 2^-E are normal floats).
+__device__ __forceinline__ int vscale_exp(uint32_t vb) {
+  if (vb == 0u) return 0;
+  const int e = (int)((vb >> 23) & 0xFF) - 127 - 14;
+  return e < -100 ? -100 : (e > 110 ? 110 : e);
+}
+
 template <int D>
 __global__ void __launch_bounds__(kThreadsA)
 attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __restrict__ part,
-             int G, int Hkv, int64_t N, int64_t Nq, int causal, float c, int nsplit,
-             int64_t shift, int pstride, int32_t* status) {
+             const uint32_t* __restrict__ vbound, int G, int Hkv, int64_t N, int64_t Nq, int causal, float c,
+             int nsplit, int64_t shift, int pstride, int32_t* status) {
   constexpr int KS = D / 16;
   constexpr int GPR = D / 32;
   constexpr int PSTRIDE = D + 2;
@@ -94,6 +156,8 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
   const int64_t ngroups = hp[22];
   const int64_t Wk = hp[20];
   const int64_t Qk = hp[21];
+  const int vexp = vscale_exp(vbound[g]);
+  const float vscale = __builtin_amdgcn_ldexpf(1.f, -vexp);   // V_hat is staged as fp16(V_hat * 2^-E)
   const int64_t gps = (ngroups + nsplit - 1) / nsplit;
   const int64_t j_begin = (int64_t)split * gps;
   const int64_t j_end_raw = j_begin + gps < ngroups ? j_begin + gps : ngroups;
@@ -260,8 +324,8 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
       const uint32_t mq = (vl[u] >= 0 && bq != 0) ? 0xFFFFu : 0u, mr = (vl[u] >= 0 && bq == 0) ? 0xFFFFu : 0u;
 #pragma unroll
       for (int k = 0; k < VC; ++k) {
-        const _Float16 hq = (_Float16)fmaf(sc, (float)((win >> (k * bq)) & mask), zp);
-        const _Float16 hr = (_Float16)bf16_bits_to_f32((w[u][k >> 1] >> (16 * (k & 1))) & 0xFFFFu);
+        const _Float16 hq = (_Float16)(fmaf(sc, (float)((win >> (k * bq)) & mask), zp) * vscale);
+        const _Float16 hr = (_Float16)(bf16_bits_to_f32((w[u][k >> 1] >> (16 * (k & 1))) & 0xFFFFu) * vscale);
         vv[u][k] = ((uint32_t)__builtin_bit_cast(uint16_t, hq) & mq) | ((uint32_t)__builtin_bit_cast(uint16_t, hr) & mr);
       }
     }
@@ -430,10 +494,11 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
     pr[0] = m_run;
     pr[1] = lt;
   }
+  const float oscale = __builtin_amdgcn_ldexpf(1.f, vexp);   // undo the staging scale (exact)
 #pragma unroll
   for (int mb = 0; mb < GPR; ++mb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) pr[2 + mb * 32 + acc_row(i, hi)] = o[mb][i];
+    for (int i = 0; i < 16; ++i) pr[2 + mb * 32 + acc_row(i, hi)] = o[mb][i] * oscale;
 }
 
 // Combine the splits of each (head, row): M = max m_s, L = sum l_s 2^(m_s - M),
@@ -1008,6 +1073,7 @@ size_t attend_ws_bytes(const Layer& L) {
   const int nsplit = dec ? nsplit_decode(L) : nsplit_of(L);
   p.take((size_t)L.hq * L.nq * (nsplit + 1) * (L.d + 2) * sizeof(float));   // + the append buffer's split
   if (dec) p.take((size_t)L.hq * L.nq * L.n * sizeof(float));     // logits by token
+  else p.take((size_t)L.hkv * sizeof(uint32_t));                  // |V_hat| bound per head
   return p.off;
 }
 
@@ -1051,14 +1117,21 @@ hipError_t launch_attend(const Layer& L, const uint16_t* q, const kvc_packed_cac
     }
 #undef KVC_DEC
   } else {
+    uint32_t* vb = reinterpret_cast<uint32_t*>(ws + p.take((size_t)L.hkv * sizeof(uint32_t)));
+    attend_vbound_init<<<1, 256, 0, s>>>(vb, L.hkv);
+    const dim3 gb(64, (unsigned)L.hkv);
+    if (L.d == 128)
+      attend_vbound<128><<<gb, 256, 0, s>>>(cache, vb, L.hkv, L.n);
+    else
+      attend_vbound<64><<<gb, 256, 0, s>>>(cache, vb, L.hkv, L.n);
     const int nRT = (int)((L.nq + kRows - 1) / kRows);
     dim3 grid((unsigned)((L.G * nRT + kWaves - 1) / kWaves), (unsigned)nsplit, (unsigned)L.hkv);
     if (L.d == 128)
-      attend_split<128><<<grid, kThreadsA, 0, s>>>(q, cache, part, L.G, L.hkv, L.n, L.nq, L.causal, L.c_log2, nsplit,
-                                                   n_new, pstride, status);
+      attend_split<128><<<grid, kThreadsA, 0, s>>>(q, cache, part, vb, L.G, L.hkv, L.n, L.nq, L.causal, L.c_log2,
+                                                   nsplit, n_new, pstride, status);
     else
-      attend_split<64><<<grid, kThreadsA, 0, s>>>(q, cache, part, L.G, L.hkv, L.n, L.nq, L.causal, L.c_log2, nsplit,
-                                                  n_new, pstride, status);
+      attend_split<64><<<grid, kThreadsA, 0, s>>>(q, cache, part, vb, L.G, L.hkv, L.n, L.nq, L.causal, L.c_log2,
+                                                  nsplit, n_new, pstride, status);
   }
   if (n_new > 0) {
     const unsigned nb = (unsigned)(((int64_t)L.hq * L.nq + 3) / 4);

@@ -219,6 +219,86 @@ def test_scorer_one_chunk_per_item(case):
     H.assert_rel(s_g, s_r, 1e-3, what=f"token scores ({mode})")
 
 
+def test_kvsculpt_pilot_flow():
+    """KVSculpt's adaptive budget (KVSculpt summary, §2) as one flow through the C ABI: a pilot at a
+    uniform budget (every KV head allocated alone at the same average, one-head descriptors), pack,
+    compressed and full attends on the last rows, per-head loss terms, budgets in proportion to
+    sqrt(pilot MSE), then every head allocated again alone at its own budget.  Each decision is
+    compared with the oracle's same step on identical inputs: widths, budgets and packed bytes bit
+    for bit, attends within their derived bounds, loss terms at rel 1e-10."""
+    hq, hkv, d, N, Nq, nf, a0 = 8, 2, 128, 1024, 1024, 64, 3.0   # N d = 2^17: budgets map to exact averages
+    print(f"case pilot flow: H_q={hq} H_kv={hkv} d={d} N={N} fidelity rows={nf} pilot avg={a0}", flush=True)
+    G = hq // hkv
+    x = make_inputs(hq, hkv, d, N, Nq, seed=808, k_outliers=True)
+    desc = H.desc_of(hq, hkv, d, N, Nq, True)
+    q, k, v = H.dev_bf16(x["q"]), H.dev_bf16(x["k"]), H.dev_bf16(x["v"])
+    w32 = H.score_sum(desc, q, k, H.row_lse(desc, q, k)).cpu().numpy()
+    wc32 = H.channel_weights(desc, q, k).cpu().numpy()
+    one = H.desc_of(G, 1, d, N, Nq, True)
+
+    def allocate_heads(avgs):
+        bv = np.zeros((hkv, N), np.uint8)
+        bk = np.zeros((hkv, d), np.uint8)
+        for g in range(hkv):
+            bvg, res, st = H.allocate(one, kvc.ALLOC_V_TOKENS, H.dev_f32(w32[g:g + 1]), avgs[g])
+            assert st == 0
+            bv_r, info = oracle.allocate_v_tokens(w32[g:g + 1], avgs[g], d)
+            np.testing.assert_array_equal(bvg.cpu().numpy(), bv_r)
+            assert res["used"] == info["used"] and res["budget"] == info["budget"]
+            bkg, resk, st = H.allocate(one, kvc.ALLOC_K_CHANNELS, H.dev_f32(wc32[g:g + 1]), avgs[g],
+                                       bits_v=H.dev_u8(bv_r))
+            bk_r, infok = oracle.allocate_k_channels(wc32[g:g + 1], bv_r, avgs[g])
+            np.testing.assert_array_equal(bkg.cpu().numpy(), bk_r)
+            bv[g], bk[g] = bv_r[0], bk_r[0]
+        return bv, bk
+
+    qf = np.ascontiguousarray(x["q"][:, Nq - nf:, :])
+    desc_f = H.desc_of(hq, hkv, d, N, nf, True)
+    c16, st = H.pack(desc, k, v, H.dev_u8(np.full((hkv, N), 16, np.uint8)), H.dev_u8(np.full((hkv, d), 16, np.uint8)))
+    y_g, l_g, st2 = H.attend(desc_f, H.dev_bf16(qf), c16)
+    assert st == 0 and st2 == 0
+
+    # pilot: every head at the same average
+    bv, bk = allocate_heads([a0] * hkv)
+    cache, st = H.pack(desc, k, v, H.dev_u8(bv), H.dev_u8(bk))
+    assert st == 0
+    H.compare_packed(cache.to_numpy(), oracle.pack_cache(x["k"], x["v"], bv, bk))
+    yh_g, lh_g, st = H.attend(desc_f, H.dev_bf16(qf), cache)
+    assert st == 0
+    yh_r, lh_r = oracle.compressed_attend(qf, x["k"], x["v"], bv, bk)
+    ty, tl = H.attend_tols(qf, [x["k"]], [x["v"]], lh_r)
+    H.assert_abs(yh_g.cpu().numpy(), yh_r, ty, "pilot attend output")
+    H.assert_abs(lh_g.cpu().numpy(), lh_r, tl, "pilot attend lse")
+    terms = torch.empty(hq, 2, dtype=torch.float64, device=H.DEV)
+    kvc.kvc_fidelity_terms(desc_f, yh_g, lh_g, y_g, l_g, terms)
+    t_g = terms.cpu().numpy()
+    np.testing.assert_allclose(t_g, oracle.fidelity_terms_per_head(yh_g.cpu().numpy(), y_g.cpu().numpy(),
+                                                                   lh_g.cpu().numpy(), l_g.cpu().numpy()),
+                               rtol=1e-10, atol=0)
+    # the pilot MSE of a KV head: output error over its query heads' rows and channels
+    mse = t_g[:, 0].reshape(hkv, G).sum(axis=1) / (G * nf * d)
+    total = int(a0 * hkv * N * d)
+    budgets = kvc.kvc_pilot_budgets(mse, total)
+    np.testing.assert_array_equal(budgets, oracle.pilot_budgets(mse, total))
+    assert int(budgets.sum()) == total
+    # the same decision from the oracle's own attend moves each budget by no more than the change
+    # of its share, times the total, plus one unit of rounding
+    y_r, l_r = oracle.full_attend(qf, x["k"], x["v"])
+    mse_r = oracle.fidelity_terms_per_head(yh_r, y_r, lh_r, l_r)[:, 0].reshape(hkv, G).sum(axis=1) / (G * nf * d)
+    share, share_r = np.sqrt(mse) / np.sqrt(mse).sum(), np.sqrt(mse_r) / np.sqrt(mse_r).sum()
+    assert np.abs(oracle.pilot_budgets(mse_r, total) - budgets).max() <= total * np.abs(share - share_r).max() + 1
+    print(f"pilot MSE per KV head {mse.tolist()}, budgets {budgets.tolist()} bits", flush=True)
+
+    # final allocation: each head alone at its own budget (budget / (N d) is exact, so B = budget)
+    avgs = [float(b) / (N * d) for b in budgets]
+    bv2, bk2 = allocate_heads(avgs)
+    used = [int((bv2[g].astype(np.int64)).sum()) * d for g in range(hkv)]
+    assert all(u <= int(b) for u, b in zip(used, budgets))
+    cache2, st = H.pack(desc, k, v, H.dev_u8(bv2), H.dev_u8(bk2))
+    assert st == 0
+    H.compare_packed(cache2.to_numpy(), oracle.pack_cache(x["k"], x["v"], bv2, bk2))
+
+
 def test_allocation_ties_zeros_and_extremes():
     print("case allocation edge cases", flush=True)
     hkv, N, d = 3, 2000, 64
@@ -445,6 +525,45 @@ def test_attend_decode_row_that_sees_nothing():
     ty, tl = H.attend_tols(qf_bits, [x["k"]], [x["v"]], lh_r)
     H.assert_abs(og, out_r, ty, "decode attend output")
     H.assert_abs(lg[:, 1], lh_r[:, 1], tl, "decode attend lse")
+
+
+RANGE_CASES = [
+    # name, H_q, H_kv, d, N, rows per query head, V scale
+    ("range_mfma_large", 8, 2, 128, 700, 64, 1e5),
+    ("range_mfma_tiny", 8, 2, 128, 700, 64, 1e-6),
+    ("range_mfma_d64_huge", 4, 1, 64, 300, 40, 3e30),
+    ("range_decode_large", 8, 2, 128, 700, 1, 1e5),
+    ("range_decode_tiny", 8, 2, 128, 700, 1, 1e-6),
+]
+
+
+@pytest.mark.parametrize("case", RANGE_CASES, ids=[c[0] for c in RANGE_CASES])
+def test_attend_value_range(case):
+    """Values far outside fp16's range (|V| up to ~5e5 and ~1e31) and far below its normal range
+    (|V| ~ 1e-6), in the 16-bit zone and the quantised zones (random widths), on both attend paths:
+    the output stays within the operand-precision bound relative to max|V|."""
+    from workloads import bf16_bits_to_f32, f32_to_bf16_bits
+    name, hq, hkv, d, N, rows, vs = case
+    print(f"case {name}: H_q={hq} H_kv={hkv} d={d} N={N} rows={rows} V scale={vs}", flush=True)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    x = make_inputs(hq, hkv, d, N, N, seed=zlib.crc32(name.encode()) % 1000)
+    v_bits = f32_to_bf16_bits((bf16_bits_to_f32(x["v"]) * np.float32(vs)).astype(np.float32))
+    bv, bk = _random_widths(rng, hkv, N, d)
+    bv[:, -1] = 16                                   # the last row always sees a 16-bit token
+    desc = H.desc_of(hq, hkv, d, N, N, True)
+    cache, st = H.pack(desc, H.dev_bf16(x["k"]), H.dev_bf16(v_bits), H.dev_u8(bv), H.dev_u8(bk))
+    assert st == 0
+    qf_bits = np.ascontiguousarray(x["q"][:, N - rows:, :])
+    out_g, lh_g, st = H.attend(H.desc_of(hq, hkv, d, N, rows, True), H.dev_bf16(qf_bits), cache)
+    assert st == 0
+    out_r, lh_r = oracle.compressed_attend(qf_bits, x["k"], v_bits, bv, bk)
+    og = out_g.cpu().numpy()
+    assert np.isfinite(og).all()
+    ty, tl = H.attend_tols(qf_bits, [x["k"]], [v_bits], lh_r, capped=False)
+    H.assert_abs(og, out_r, ty, "attend output, scaled V")
+    H.assert_abs(lh_g.cpu().numpy(), lh_r, tl, "attend lse, scaled V")
+    # the outputs are not flushed: a typical row has |Y| of the order of the V scale
+    assert np.abs(out_r).max() > 0.05 * vs
 
 
 APPEND_CASES = [
