@@ -47,7 +47,7 @@ from .allocation import (
 from .quantize import quantize_group, pack_group_words, pack_cache, HDR_GLOBAL, HDR_PER_HEAD
 from .fidelity import (dequantized_head, attend, full_attend, compressed_attend, compressed_attend_append,
                        fidelity_terms, fidelity_terms_per_head)
-from .ridge import ridge_normal_equations, ridge_value_fit
+from .ridge import ridge_normal_equations, ridge_system, ridge_value_fit
 
 __all__ = [
     "as_f64", "query_positions", "default_scale",
@@ -57,5 +57,5 @@ __all__ = [
     "allocate_v_tokens", "allocate_k_channels", "retained_counts", "topk_keep", "threshold_keep", "pilot_budgets",
     "quantize_group", "pack_group_words", "pack_cache", "HDR_GLOBAL", "HDR_PER_HEAD",
     "dequantized_head", "attend", "full_attend", "compressed_attend", "compressed_attend_append", "fidelity_terms", "fidelity_terms_per_head",
-    "ridge_normal_equations", "ridge_value_fit",
+    "ridge_normal_equations", "ridge_system", "ridge_value_fit",
 ]

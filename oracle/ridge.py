@@ -35,9 +35,10 @@ def _weights(q_head, k_head, scale, vis):
     return a
 
 
-def ridge_normal_equations(q, k, v_r, y, n_compressed, lam, scale=None, causal=False):
-    """Per KV head g: (M_g, B_g) with M = A_c^T A_c + lam I [n_c][n_c] and
-    B = A_c^T (Y - A_r V_r) [n_c][d], rows of the group's G query heads stacked in head order.
+def ridge_system(q, k, v_r, y, n_compressed, scale=None, causal=False):
+    """Per KV head g: (A_c, A_r, T) with the rows of the group's G query heads stacked in head
+    order: the attention weights on the n_c compressed keys [R][n_c] and on the m retained keys
+    [R][m], and the target the compressed part must reproduce, T = Y - A_r V_r [R][d].
 
     q: bf16 bits [H_q][Nq][d]; k: bf16 bits [H_kv][n_c + m][d] (compressed keys first);
     v_r: bf16 bits [H_kv][m][d] (ignored when m = 0); y: [H_q][Nq][d] target outputs.
@@ -54,16 +55,25 @@ def ridge_normal_equations(q, k, v_r, y, n_compressed, lam, scale=None, causal=F
     Vr = as_f64(v_r) if m > 0 else np.zeros((hkv, 0, d))
     sc = default_scale(d, scale)
     vis = visible_mask(n, nq, 0, nq, causal)
-    Ms, Bs = [], []
+    out = []
     for g in range(hkv):
-        Ac, T = [], []
+        Ac, Ar, T = [], [], []
         for h in range(g * G, (g + 1) * G):
             a = _weights(Q[h], K[g], sc, vis)
             Ac.append(a[:, :nc])
+            Ar.append(a[:, nc:])
             T.append(Y[h] - a[:, nc:] @ Vr[g])
-        Ac = np.vstack(Ac)
-        T = np.vstack(T)
-        Ms.append(Ac.T @ Ac + float(lam) * np.eye(nc))
+        out.append((np.vstack(Ac), np.vstack(Ar), np.vstack(T)))
+    return out
+
+
+def ridge_normal_equations(q, k, v_r, y, n_compressed, lam, scale=None, causal=False):
+    """Per KV head g: (M_g, B_g) with M = A_c^T A_c + lam I [n_c][n_c] and
+    B = A_c^T (Y - A_r V_r) [n_c][d], from the stacked system of ridge_system.
+    """
+    Ms, Bs = [], []
+    for Ac, _, T in ridge_system(q, k, v_r, y, n_compressed, scale, causal):
+        Ms.append(Ac.T @ Ac + float(lam) * np.eye(Ac.shape[1]))
         Bs.append(Ac.T @ T)
     return Ms, Bs
 

@@ -654,6 +654,24 @@ def test_fidelity_terms(case):
     assert torch.equal(terms, again)
 
 
+def _check_ridge(name, x, v_r, y, nc, lam, causal, got):
+    """V from the GPU against the oracle's exact solve, within the elementwise bounds derived from
+    the GPU's operand precisions (tests/ridge_bounds.py); prints the measured error and residual
+    relative to their bounds."""
+    from tests.ridge_bounds import ridge_error_bounds
+    for g, b in enumerate(ridge_error_bounds(x["q"], x["k"], v_r, y, nc, lam, causal, got)):
+        vmax = np.abs(b["exact"]).max()
+        print(f"ridge {name} head {g}: cond(M) {b['cond']:.3g}; max|dV|/max|V| {b['err'].max() / vmax:.3g} "
+              f"(bound {b['err_bound'].max() / vmax:.3g}); worst error / its bound {(b['err'] / b['err_bound']).max():.3g}; "
+              f"worst residual / its bound {(b['res'] / b['res_bound']).max():.3g}", flush=True)
+        assert (b["res"] <= b["res_bound"]).all(), "residual outside its derived bound"
+        assert (b["err"] <= b["err_bound"]).all(), "V outside its derived bound"
+        # The derived bounds are worst cases (d roundings per logit, absolute values through
+        # M^-1); the measured errors sit far inside them, at most 6.5e-7 of max|V| over every
+        # case, the benchmark shape included.  A regression guard at about 15 times that:
+        assert b["err"].max() <= 1e-5 * vmax, "V error far above every measured one"
+
+
 RIDGE_CASES = [
     # name, H_q, H_kv, d, n_c, m, Nq, causal, lambda
     ("ridge_d64_small", 4, 2, 64, 40, 24, 100, False, 0.1),
@@ -666,10 +684,10 @@ RIDGE_CASES = [
 
 @pytest.mark.parametrize("case", RIDGE_CASES, ids=[c[0] for c in RIDGE_CASES])
 def test_ridge_value_fit(case):
-    """KVSculpt's value solve against the oracle.  The GPU forms A in float32, so its V_c solves
-    the normal equations up to a relative perturbation of about 1e-5: the residual
-    M V - B of the oracle's own (M, B) must be small relative to |M| |V| + |B| (a bound that
-    does not depend on the conditioning), and V itself must agree within cond(M) times that."""
+    """KVSculpt's value solve against the oracle.  The GPU's V solves exactly a system whose float32
+    weights and target carry bounded elementwise perturbations, so the residual of the oracle's
+    (M, B) at the GPU's V and the error of V itself have elementwise bounds derived from those
+    precisions (tests/ridge_bounds.py)."""
     name, hq, hkv, d, nc, m, nq, causal, lam = case
     print(f"case {name}: H_q={hq} H_kv={hkv} d={d} n_c={nc} m={m} Nq={nq} causal={causal} lambda={lam}", flush=True)
     seed = zlib.crc32(name.encode()) % 1000
@@ -685,16 +703,7 @@ def test_ridge_value_fit(case):
     torch.cuda.synchronize()
     assert kvc.kvc_get_device_status(ws) == 0
     got = v_c.cpu().numpy().astype(np.float64)
-    Ms, Bs = oracle.ridge_normal_equations(x["q"], x["k"], v_r, y, nc, lam, causal=causal)
-    want = np.stack([np.linalg.solve(M, B) for M, B in zip(Ms, Bs)])
-    for g in range(hkv):
-        M, B = Ms[g], Bs[g]
-        scale = np.abs(M).sum(axis=1).max() * np.abs(got[g]).max() + np.abs(B).max()
-        res = np.abs(M @ got[g] - B).max()
-        assert res <= 1e-4 * scale, (g, res, scale)
-        cond = np.linalg.cond(M)
-        err = np.abs(got[g] - want[g]).max()
-        assert err <= 1e-4 * cond * np.abs(want[g]).max() + 1e-6, (g, err, cond)
+    _check_ridge(name, x, v_r, y, nc, lam, causal, got)
     # fixed summation order: a second call gives the same bits
     v2 = torch.empty_like(v_c)
     kvc.kvc_ridge_value_fit(desc, nc, H.dev_bf16(x["q"]), H.dev_bf16(x["k"]), H.dev_bf16(v_r) if m else None,

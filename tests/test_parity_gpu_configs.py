@@ -160,8 +160,8 @@ def test_config3_kvzip_full_size():
 
 def test_ridge_fit_at_the_bench_shape():
     """The ridge value fit at the shape bench.py times (KVSculpt's layer: 12/2 heads, 768 pairs, 512
-    retained tokens, 1024 training rows), against the oracle's normal equations: the residual bound
-    that does not depend on the conditioning, and V itself within cond(M) times it."""
+    retained tokens, 1024 training rows), against the oracle's exact solve within the elementwise
+    bounds derived from the GPU's operand precisions."""
     import bench
     sh = bench.RIDGE_SHAPE
     hq, hkv, d, nc, m, nq, lam = (sh["n_q_heads"], sh["n_kv_heads"], sh["head_dim"], sh["n_compressed"],
@@ -179,13 +179,8 @@ def test_ridge_fit_at_the_bench_shape():
     torch.cuda.synchronize()
     assert kvc.kvc_get_device_status(ws) == 0
     got = v_c.cpu().numpy().astype(np.float64)
-    Ms, Bs = oracle.ridge_normal_equations(x["q"], x["k"], v_r, y, nc, lam, causal=False)
-    for g in range(hkv):
-        M, B = Ms[g], Bs[g]
-        want = np.linalg.solve(M, B)
-        scale = np.abs(M).sum(axis=1).max() * np.abs(got[g]).max() + np.abs(B).max()
-        assert np.abs(M @ got[g] - B).max() <= 1e-4 * scale
-        assert np.abs(got[g] - want).max() <= 1e-4 * np.linalg.cond(M) * np.abs(want).max() + 1e-6
+    from tests.test_parity_gpu import _check_ridge
+    _check_ridge("bench shape", x, v_r, y, nc, lam, False, got)
 
 
 def test_step_replays_in_a_graph():
