@@ -456,21 +456,31 @@ lse_partial(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   }
 }
 
-// l = (M + log2 sum_c l_c 2^(m_c - M)) * ln 2 over the chunks of the row's tile.
-__global__ void lse_combine(const float2* __restrict__ part, float* __restrict__ lse, int Hq,
-                            int64_t N, int64_t Nq, int causal, int KC, int maxCh) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)Hq * Nq) return;
+// l = (M + log2 sum_c l_c 2^(m_c - M)) * ln 2 over the chunks of the row's tile.  One wave per
+// row: lane c takes chunks c, c + 64, ... (the row's partials are contiguous, so every load
+// instruction reads 512 consecutive bytes), then fixed butterfly trees give M and the sum.
+__global__ void __launch_bounds__(256)
+lse_combine(const float2* __restrict__ part, float* __restrict__ lse, int Hq, int64_t N, int64_t Nq, int causal,
+            int KC, int maxCh) {
+  const int64_t idx = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // h * Nq + row
+  if (idx >= (int64_t)Hq * Nq) return;                                 // uniform per wave
+  const int lane = threadIdx.x & 63;
   const int64_t row = idx % Nq;
   const int rt = (int)(row / kRowsPerBlock);
   const int nch = (int)((tile_kend(rt, N, Nq, causal) + KC - 1) / KC);
   const float2* p = part + idx * maxCh;
   float M = -INFINITY;
-  for (int ch = 0; ch < nch; ++ch) M = fmaxf(M, p[ch].x);
+  for (int ch = lane; ch < nch; ch += 64) M = fmaxf(M, p[ch].x);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
   float L = 0.f;
-  for (int ch = 0; ch < nch; ++ch)
-    if (p[ch].x > -INFINITY) L += p[ch].y * exp2f(p[ch].x - M);
-  lse[idx] = (M > -INFINITY) ? (M + log2f(L)) * kLn2 : -INFINITY;
+  for (int ch = lane; ch < nch; ch += 64) {
+    const float2 v = p[ch];
+    if (v.x > -INFINITY) L += v.y * fast_exp2(v.x - M);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
+  if (lane == 0) lse[idx] = (M > -INFINITY) ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -661,83 +671,84 @@ score_partial(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   }
 }
 
-// SUM: w[g][t] = sum over the group's (head, row tile) pairs that see t.  Four lanes share a
-// key: for each head in turn, lane r adds the row tiles rt0 + r, rt0 + r + 4, ... in two
-// interleaved chains (independent loads in flight), then the four lanes' sums are combined as
-// (s0 + s1) + (s2 + s3): a fixed order.
+// Column reductions of the pass-2 partials [H_q][nRT][Npad].  A block of 4 waves covers 64
+// consecutive keys of one KV head (lane = key, so each load reads 256 consecutive bytes); wave
+// w adds the row tiles rt = rt0 + w, rt0 + w + 4, ... of every head of the group (rt0 = the
+// first tile whose rows see the key), and the four waves' values are combined in LDS in a fixed
+// order, so every result is bitwise reproducible.
+// SUM: scores[g][t] = sum over the group's heads and row tiles.
 __global__ void __launch_bounds__(256)
 score_reduce_sum(const float* __restrict__ part, float* __restrict__ scores, int Hkv, int G,
                  int nRT, int64_t N, int64_t Nq, int causal, int64_t Npad) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t idx = gid >> 2;
-  const int r = (int)(gid & 3);
-  const bool ok = idx < (int64_t)Hkv * N;
-  const int g = ok ? (int)(idx / N) : 0;
-  const int64_t t = ok ? idx % N : 0;
+  __shared__ float red[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = blockIdx.y;
+  const int64_t t = (int64_t)blockIdx.x * 64 + lane;
+  const bool ok = t < N;
   int rt0 = 0;
-  if (causal) {
+  if (causal && ok) {
     const int64_t rel = t - (N - Nq);                 // first row index that sees t
     rt0 = rel > 0 ? (int)(rel / kRowsPerBlock) : 0;
   }
   float s = 0.f;
   if (ok) {
-    for (int hl = 0; hl < G; ++hl) {
-      const float* p = part + ((int64_t)(g * G + hl) * nRT) * Npad + t;
-      float a0 = 0.f, a1 = 0.f;
-      int rt = rt0 + r;
-      for (; rt + 4 < nRT; rt += 8) {
-        a0 += p[(int64_t)rt * Npad];
-        a1 += p[(int64_t)(rt + 4) * Npad];
-      }
-      if (rt < nRT) a0 += p[(int64_t)rt * Npad];
-      s += a0 + a1;
+    // per row tile, the group's heads (at most 16) as independent loads, then added in head order
+    const float* p = part + (int64_t)g * G * nRT * Npad + t;
+    for (int rt = rt0 + w; rt < nRT; rt += 4) {
+      float v[16];
+#pragma unroll
+      for (int hl = 0; hl < 16; ++hl) v[hl] = hl < G ? p[((int64_t)hl * nRT + rt) * Npad] : 0.f;
+#pragma unroll
+      for (int hl = 0; hl < 16; ++hl) s += v[hl];
     }
   }
-  const float s1 = __shfl_xor(s, 1, 64);
-  const float pair = (r & 1) ? s1 + s : s + s1;       // lanes 0/1 -> s0+s1, lanes 2/3 -> s2+s3
-  const float other = __shfl_xor(pair, 2, 64);
-  const float tot = (r & 2) ? other + pair : pair + other;
-  if (ok && r == 0) scores[idx] = tot;
+  red[w][lane] = s;
+  __syncthreads();
+  if (w == 0 && ok) scores[(int64_t)g * N + t] = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
 }
 
 // MAX: s+[g][t] = max over the group's heads h of 2^(max over row tiles of part) / ||W_O^h v_t||.
-// Four lanes share a key: lane r takes the row tiles rt = rt0 + r, rt0 + r + 4, ...; the maxima
-// are combined across the four lanes (max is exact in any order).
+// The per-head maxima of the four waves are combined in LDS (max is exact in any order).
 __global__ void __launch_bounds__(256)
 score_reduce_max(const float* __restrict__ part, const float* __restrict__ won,
                  float* __restrict__ scores, int Hkv, int G, int nRT, int64_t N,
                  int64_t Nq, int causal, int64_t Npad) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t idx = gid >> 2;
-  const int r = (int)(gid & 3);
-  const bool ok = idx < (int64_t)Hkv * N;
-  const int g = ok ? (int)(idx / N) : 0;
-  const int64_t t = ok ? idx % N : 0;
+  __shared__ float red[4][16][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = blockIdx.y;
+  const int64_t t = (int64_t)blockIdx.x * 64 + lane;
+  const bool ok = t < N;
   int rt0 = 0;
-  if (causal) {
+  if (causal && ok) {
     const int64_t rel = t - (N - Nq);
     rt0 = rel > 0 ? (int)(rel / kRowsPerBlock) : 0;
   }
+  float m[16];
+#pragma unroll
+  for (int hl = 0; hl < 16; ++hl) m[hl] = -INFINITY;
+  if (ok) {
+    const float* p = part + (int64_t)g * G * nRT * Npad + t;
+    for (int rt = rt0 + w; rt < nRT; rt += 4) {
+#pragma unroll
+      for (int hl = 0; hl < 16; ++hl)
+        if (hl < G) m[hl] = fmaxf(m[hl], p[((int64_t)hl * nRT + rt) * Npad]);
+    }
+  }
+#pragma unroll
+  for (int hl = 0; hl < 16; ++hl)
+    if (hl < G) red[w][hl][lane] = m[hl];
+  __syncthreads();
+  if (w != 0 || !ok) return;
   float best = 0.f;
   for (int hl = 0; hl < G; ++hl) {
     const int hh = g * G + hl;
-    const float* p = part + ((int64_t)hh * nRT) * Npad + t;
-    float m0 = -INFINITY, m1 = -INFINITY;
-    int rt = rt0 + r;
-    for (; rt + 4 < nRT; rt += 8) {
-      m0 = fmaxf(m0, p[(int64_t)rt * Npad]);
-      m1 = fmaxf(m1, p[(int64_t)(rt + 4) * Npad]);
-    }
-    if (ok && rt < nRT) m0 = fmaxf(m0, p[(int64_t)rt * Npad]);
-    float m = fmaxf(m0, m1);
-    m = fmaxf(m, __shfl_xor(m, 1, 64));
-    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    const float m = fmaxf(fmaxf(red[0][hl][lane], red[1][hl][lane]), fmaxf(red[2][hl][lane], red[3][hl][lane]));
     const float num = exp2f(m);
-    const float den = ok ? won[(int64_t)hh * N + t] : 1.f;
+    const float den = won[(int64_t)hh * N + t];
     const float q = (num == 0.f && den == 0.f) ? 0.f : num / den;
     best = fmaxf(best, q);
   }
-  if (ok && r == 0) scores[idx] = best;
+  scores[(int64_t)g * N + t] = best;
 }
 
 // log2 ||h_j||_2 per query row: one wave per row, 16-byte loads, float64 sums of the squares
@@ -994,7 +1005,7 @@ hipError_t launch_row_lse(const Layer& L, const uint16_t* q, const uint16_t* k, 
     lse_partial<64, 1><<<grid_of(p), kThreads, 0, s>>>(q, k, part, lse, dc, L.n, L.nq, L.causal, L.c_log2);
   if (p.maxCh > 1) {
     const int64_t rows = (int64_t)L.hq * L.nq;
-    lse_combine<<<(unsigned)((rows + 255) / 256), 256, 0, s>>>(part, lse, L.hq, L.n, L.nq, L.causal, p.KC, p.maxCh);
+    lse_combine<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(part, lse, L.hq, L.n, L.nq, L.causal, p.KC, p.maxCh);
   }
   return hipGetLastError();
 }
@@ -1042,11 +1053,11 @@ hipError_t launch_score(const Layer& L, int mode, const uint16_t* q, const uint1
     else
       score_partial<64, false><<<grid, kThreads, 0, s>>>(q, k, lse, nullptr, part, dc, L.n, L.nq, L.causal, L.c_log2, p.Npad);
   }
-  const int64_t total = (int64_t)L.hkv * L.n;
+  const dim3 gr((unsigned)((L.n + 63) / 64), (unsigned)L.hkv);
   if (mx)
-    score_reduce_max<<<(unsigned)((4 * total + 255) / 256), 256, 0, s>>>(part, won, scores, L.hkv, L.G, p.nRT, L.n, L.nq, L.causal, p.Npad);
+    score_reduce_max<<<gr, 256, 0, s>>>(part, won, scores, L.hkv, L.G, p.nRT, L.n, L.nq, L.causal, p.Npad);
   else
-    score_reduce_sum<<<(unsigned)((4 * total + 255) / 256), 256, 0, s>>>(part, scores, L.hkv, L.G, p.nRT, L.n, L.nq, L.causal, p.Npad);
+    score_reduce_sum<<<gr, 256, 0, s>>>(part, scores, L.hkv, L.G, p.nRT, L.n, L.nq, L.causal, p.Npad);
   return hipGetLastError();
 }
 
