@@ -271,11 +271,14 @@ kvc_status kvc_quantize_pack(const kvc_layer_desc* desc, const void* k, const vo
  * (RDKV §2.3 decode over packed zones; the two outputs whose errors form KVSculpt's loss,
  * §2).  A row with no visible retained token gets lse = -inf and out = 0.  The packed cache's
  * header must match desc (H_kv, d, N); a mismatch sets the device status.
- * Precision: logits use keys to 2^-17 relative (bf16 hi + lo) with float32 accumulation.  With
- * more than 16 query rows per KV head the value products take fp16 operands: the probabilities,
- * and V_hat scaled per KV head by a power of two that puts the head's largest |V_hat| in
- * [2^14, 2^15), so any finite bf16 V keeps 11 significant bits (values below 2^-24 of the head's
- * largest round to that absolute step).  With at most 16 rows they are float32. */
+ * Precision: with more than 16 query rows per KV head, logits use keys to 2^-17 relative (bf16
+ * hi + lo) with float32 accumulation, and the value products take fp16 operands: the
+ * probabilities, and V_hat scaled per KV head by a power of two that puts the head's largest
+ * |V_hat| in [2^14, 2^15), so any finite bf16 V keeps 11 significant bits (values below 2^-24 of
+ * the head's largest round to that absolute step).  With at most 16 rows (decode) the codes and
+ * raw bf16 values enter exactly, q * scale and p * scale_v as bf16 hi + lo pairs (2^-17
+ * relative), zero terms exactly or in float32, all accumulated in float32.  Workspace: the
+ * decode path also holds every retained token's logits (4 * H_kv * N * 16 bytes at most). */
 kvc_status kvc_compressed_attend(const kvc_layer_desc* desc, const void* q,
                                  const kvc_packed_cache* cache, float* out, float* lse,
                                  void* ws, size_t ws_bytes, void* hip_stream);

@@ -17,7 +17,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvc.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "score.hip", "chanw.hip", "alloc.hip", "keep.hip", "pack.hip", "attend.hip", "fidelity.hip", "ridge.hip"]
+SOURCES = ["api.cpp", "score.hip", "chanw.hip", "alloc.hip", "keep.hip", "pack.hip", "attend.hip", "decode.hip", "fidelity.hip", "ridge.hip"]
 
 # -ffp-contract=off: every fused multiply-add is written explicitly, so the exact paths
 # (allocation keys, quantiser) round exactly as written.  Packed fp32 instructions are

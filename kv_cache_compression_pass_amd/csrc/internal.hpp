@@ -80,6 +80,11 @@ hipError_t launch_pack(const Layer& L, const uint16_t* k, const uint16_t* v,
 
 // ---- compressed attend ------------------------------------------------------------------
 size_t attend_ws_bytes(const Layer& L);
+// Decode-shaped attends (at most 16 query rows per KV head): a logits and a values kernel (decode.hip).
+int decode_nsplit(const Layer& L);
+size_t decode_ws_bytes(const Layer& L);   // the logits (by V row) and the logits blocks' maxima
+hipError_t launch_attend_decode(const Layer& L, const uint16_t* q, const kvc_packed_cache& cache, float* part,
+                                int nsplit, int pstride, int64_t shift, int32_t* status, char* dws, hipStream_t s);
 hipError_t launch_attend(const Layer& L, const uint16_t* q, const kvc_packed_cache& cache,
                          float* out, float* lse, char* ws, hipStream_t s, const uint16_t* k_new = nullptr,
                          const uint16_t* v_new = nullptr, int64_t n_new = 0);
