@@ -46,10 +46,10 @@ constexpr int kDcThreads = 64 * kDcWaves;
 constexpr int kPPMax = 160;            // padded K positions: D <= 128 channels + up to 7 per class
 constexpr int kKBMax = kPPMax / 32;    // 32-position blocks
 constexpr int kKSt = 2304;             // >= staged K words of a group (sum_c b_c * padded count)
-constexpr int kKRing = 3072;           // K ring words per wave (group slots: words, pairs, tokens)
+constexpr int kKRing = 2048;           // K ring words per wave (group slots: words, pairs, tokens)
 constexpr int kKMaxSlots = 8;
 constexpr int kVSlotWords = 792;       // V chunk words and pairs: 12 blocks of 64 words, 2 apart
-constexpr int kVSlots = 4;             // V ring slots per wave
+constexpr int kVSlots = 3;             // V ring slots per wave
 
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -300,7 +300,7 @@ struct LgSmem {
 };
 
 template <int D, int RP>
-__global__ void __launch_bounds__(kDcThreads)
+__global__ void __launch_bounds__(kDcThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
 attend_dec_logits(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __restrict__ logit,
                   float* __restrict__ bmax, int G, int Hkv, int64_t N, int64_t Nq, int64_t shift, int causal,
                   float c, int nsplit, int32_t* __restrict__ status) {
@@ -380,7 +380,7 @@ attend_dec_logits(const uint16_t* __restrict__ q, kvc_packed_cache cache, float*
   // this lane's 8-position runs (block kb, positions 32 kb + 8 lg ..) for token t of each half, one
   // word each: staged address of the token's words | path << 12 | bit << 16 | byte (raw: half) << 20
   // | 2-bit << 22 | real positions of a raw run << 24
-  uint32_t kd[2][kKBMax], ksel[2][kKBMax];      // descriptor; byte selector (crumb / nibble / byte / half)
+  uint32_t kd[2][kKBMax];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int tt = 16 * h + ln;
@@ -388,7 +388,6 @@ attend_dec_logits(const uint16_t* __restrict__ q, kvc_packed_cache cache, float*
     for (int kb = 0; kb < kKBMax; ++kb) {
       const int pp = 32 * kb + 8 * lg;
       kd[h][kb] = 0;
-      ksel[h][kb] = 0;
       if (pp < npp) {
         const int cls = pp >= sm.pp0[3] ? 3 : pp >= sm.pp0[2] ? 2 : pp >= sm.pp0[1] ? 1 : 0;
         const int lb = cls + 1;
@@ -400,7 +399,6 @@ attend_dec_logits(const uint16_t* __restrict__ q, kvc_packed_cache cache, float*
         const int nval = min(8, sm.pp0[cls] + sm.ccnt[cls] - pp);
         kd[h][kb] = (uint32_t)a | ((uint32_t)path << 12) | ((uint32_t)(sh & 7) << 16) | ((uint32_t)byte << 20) |
                     ((uint32_t)(cls == 0) << 22) | ((uint32_t)nval << 24);
-        ksel[h][kb] = path == 3 ? (byte ? 0x07060302u : 0x05040100u) : 0x0C0C0400u + (uint32_t)byte * 0x101u;
       }
     }
   }
@@ -414,11 +412,15 @@ attend_dec_logits(const uint16_t* __restrict__ q, kvc_packed_cache cache, float*
 
   // ---- this wave's groups j_begin + w + 4 k through a ring of NBK slots, each a group's staged
   // words, its (scale, zero) pairs, its token ids and V locations; filled NBK - 1 groups ahead
-  const int ssw = (Ws + 3) & ~3, ssp = 2 * Qk, ssp4 = (ssp + 3) & ~3;
+  // a group's staged words beyond what a slot holds (heads whose channels are mostly 16-bit) are
+  // read from global memory where they are used
+  const int ssp = 2 * Qk, ssp4 = (ssp + 3) & ~3;
+  const int cap = Ws < ((kKRing - 64 - ssp4) & ~7) ? Ws : ((kKRing - 64 - ssp4) & ~7);   // staged words
+  const int ssw = (cap + 3) & ~3;
   const int SS = ssw + ssp4 + 64;
   int NBK = kKRing / SS;
   NBK = NBK < kKMaxSlots ? NBK : kKMaxSlots;
-  const int cg = (Ws + 63) / 64 + (ssp + 63) / 64 + 1;   // copies per group
+  const int cg = (cap + 63) / 64 + (ssp + 63) / 64 + 1;  // copies per group
   if (NBK > 2 && (NBK - 2) * cg > 63) NBK = 2 + 63 / cg;  // the wait count field holds 63
   const int64_t nblk = j_end - j_begin;
   const int nw = nblk > w ? (int)((nblk - w + kDcWaves - 1) / kDcWaves) : 0;
@@ -433,7 +435,7 @@ attend_dec_logits(const uint16_t* __restrict__ q, kvc_packed_cache cache, float*
     const int64_t j = j_begin + w + (int64_t)kDcWaves * k;
     lds_u32* dst = ring_l + slot * SS;
     const uint32_t* gw = kwords + j * Wk;
-    for (int i0 = 0; 64 * i0 < Ws; i0 += 4) {     // copy i moves staged words 64 i .. 64 i + 63
+    for (int i0 = 0; 64 * i0 < cap; i0 += 4) {    // copy i moves staged words 64 i .. 64 i + 63
       int src[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
@@ -443,7 +445,7 @@ attend_dec_logits(const uint16_t* __restrict__ q, kvc_packed_cache cache, float*
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int i = i0 + b;
-        if (64 * i < Ws && 64 * i + lane < Ws) stage_dword(gw + src[b], dst + 64 * i);
+        if (64 * i < cap && 64 * i + lane < cap) stage_dword(gw + src[b], dst + 64 * i);
       }
     }
     const float* gp = kparf + j * ssp;
@@ -495,16 +497,29 @@ attend_dec_logits(const uint16_t* __restrict__ q, kvc_packed_cache cache, float*
 #pragma unroll
       for (int kb = 0; kb < kKBMax; ++kb) {
         if (kb < nkb) {
-          const uint32_t dA = kd[h][kb];
+          uint32_t dA = kd[h][kb];
+          asm volatile("" : "+v"(dA));           // derived selectors stay inside the loop
           const int path = (int)((dA >> 12) & 3);
           const int pk = 32 * kb + 8 * lg;
           uint4 w0, w1, bh, bl, az, bq;
-          lds_rd_kblock(sb + 4u * (dA & 0xFFFu), lds_addr(&sm.qah[w][r_col][pk]), lds_addr(&sm.qal[w][r_col][pk]),
-                        lds_addr(&sm.zbv[w][pk]), lds_addr(&sm.qb[r_col][pk]), w0, w1, bh, bl, az, bq);
+          const int ad = (int)(dA & 0xFFFu);
+          const bool staged = ad + 8 <= cap;
+          lds_rd_kblock(sb + 4u * (uint32_t)(staged ? ad : 0), lds_addr(&sm.qah[w][r_col][pk]),
+                        lds_addr(&sm.qal[w][r_col][pk]), lds_addr(&sm.zbv[w][pk]), lds_addr(&sm.qb[r_col][pk]), w0, w1,
+                        bh, bl, az, bq);
+          if (path != 0 && !staged) {              // past the slot: the group's words in global memory
+            const uint32_t* gw = kwords + j * Wk;
+            uint32_t x[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = gw[sm.srcw[ad + i]];
+            w0 = make_uint4(x[0], x[1], x[2], x[3]);
+            w1 = make_uint4(x[4], x[5], x[6], x[7]);
+          }
           uint4 a = make_uint4(0u, 0u, 0u, 0u);
           if (path != 0) {
             const int bit = (int)((dA >> 16) & 7);
-            const uint32_t sel = ksel[h][kb];
+            const uint32_t byte = (dA >> 20) & 3;
+            const uint32_t sel = path == 3 ? (byte ? 0x07060302u : 0x05040100u) : 0x0C0C0400u + byte * 0x101u;
             const uint32_t mask = (dA >> 22) & 1 ? 0x03030303u : 0x0F0F0F0Fu;
             if (path == 1) a = codes8<1>(w0, w1, sel, bit, mask);
             else if (path == 2) a = codes8<2>(w0, w1, sel, bit, mask);
@@ -681,7 +696,7 @@ __device__ __forceinline__ void v_chunk(const float* Ms, uint32_t vb, int crows,
 }
 
 template <int D, int RP>
-__global__ void __launch_bounds__(kDcThreads)
+__global__ void __launch_bounds__(kDcThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
 attend_dec_values(kvc_packed_cache cache, const float* __restrict__ logit, const float* __restrict__ bmax,
                   float* __restrict__ part, int G, int Hkv, int64_t N, int64_t Nq, float c, int nsa, int nsplit,
                   int pstride) {
@@ -826,7 +841,7 @@ attend_dec_values(kvc_packed_cache cache, const float* __restrict__ logit, const
 
 int decode_nsplit(const Layer& L) {
   const int64_t groups = (L.n + 31) / 32;                 // K groups per head, at most
-  int64_t want = (512 + L.hkv - 1) / L.hkv;               // two blocks per compute unit, one round
+  int64_t want = (768 + L.hkv - 1) / L.hkv;               // three blocks per compute unit, one round
   const int64_t cap = (groups + 3) / 4;                   // at least one group per wave
   if (want > cap) want = cap;
   if (want > 255) want = 255;                             // one more split for the append buffer
