@@ -55,8 +55,8 @@ struct AllocWs {
   int32_t* status;
   SelState* st;         // [nseg]
   int64_t* hist;        // [nseg][kBins]  (the current pass)
-  uint64_t* hmin;       // [nseg][kBins]
-  uint64_t* hmax;       // [nseg][kBins]
+  uint64_t* pmin;       // [nseg]  smallest key of the current prefix set (this pass)
+  uint64_t* pmax;       // [nseg]  largest
   int32_t* rpart;       // [Hkv][ncb]  retained tokens per 4096-token block (K stage)
   int32_t* rbad;        // [Hkv][ncb]  invalid token widths seen in the block
   int64_t* rcount;      // [Hkv]      R_g (K stage)
@@ -174,6 +174,61 @@ __device__ void select_digit(SelState* st, const int64_t* hist, const uint64_t* 
       } else if (dg.lo == 0) {
         n.done = 1;
       }
+      *st = n;
+    }
+  }
+}
+
+// The multi-block path's digit choice.  Instead of per-bin extremes it has the smallest and
+// largest key of the current prefix set (the keys of the bin chosen by the previous pass, all
+// positive keys on pass 0): when they are equal that value is lambda* (the same value and budget
+// the per-bin test finds one pass earlier).
+template <int NT>
+__device__ void select_digit_set(SelState* st, const int64_t* hist, uint64_t pmin, uint64_t pmax, int pass,
+                                 int nb, int64_t* wave_tot) {
+  const SelState s = *st;
+  constexpr int PER = kBins / NT;
+  const int i = threadIdx.x;
+  int64_t hv[PER];
+  int64_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    hv[j] = hist[kBins - 1 - (PER * i + j)];
+    mine += hv[j];
+  }
+  const int64_t incl_t = block_scan_incl(mine, wave_tot);
+  int64_t total = 0;                           // the block's wave totals stay in wave_tot
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) total += wave_tot[w];
+  if (s.done || s.none) return;               // uniform
+  if (pass == 0 && total <= s.brem) {          // every positive step fits: lambda* = 0
+    if (i == 0) {
+      st->all_fit = 1;
+      st->done = 1;
+    }
+    return;
+  }
+  if (pmin == pmax) {                          // a single key value in the prefix set: lambda*
+    if (i == 0) {
+      SelState n = s;
+      n.prefix = pmin;
+      n.done = 1;
+      *st = n;
+    }
+    return;
+  }
+  int64_t run = incl_t - mine;                 // cumulative weight of higher digits
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int64_t excl = run;
+    run += hv[j];
+    if (excl <= s.brem && run > s.brem) {      // exactly one bin overall
+      const int digit = kBins - 1 - (PER * i + j);
+      const Digit dg = digit_of(pass, nb);
+      SelState n = s;
+      n.brem = s.brem - excl;
+      n.prefix = s.prefix | ((uint64_t)digit << dg.lo);
+      if (dg.lo == 0) n.done = 1;
       *st = n;
     }
   }
@@ -445,10 +500,10 @@ alloc_begin(AllocWs a, int stage, int nseg, int Hkv, int64_t N, int d, int ncb, 
     bad = 0;
   }
   if (tid < 256) rc[tid] = 0;
-  for (int64_t i = tid; i < (int64_t)nseg * kBins; i += 1024) {
-    a.hist[i] = 0;
-    a.hmin[i] = ~0ull;
-    a.hmax[i] = 0;
+  for (int64_t i = tid; i < (int64_t)nseg * kBins; i += 1024) a.hist[i] = 0;
+  for (int i = tid; i < nseg; i += 1024) {
+    a.pmin[i] = ~0ull;
+    a.pmax[i] = 0;
   }
   __syncthreads();
   if (stage == KVC_ALLOC_K_CHANNELS) sum_counts(a.rpart, a.rbad, Hkv, ncb, rc, &bad);
@@ -494,23 +549,21 @@ __device__ __forceinline__ void keys_of(const float* weight, const float* sigma,
   unit_keys(c, unit_size(stage, d, u, rcount), kk);
 }
 
-// Histogram of one pass.  V/K: keys computed on pass 0 (and stored), 4 per unit, weight =
-// step rate.  Top-k: 32-bit score keys, 1 per token, weight 1, one segment per KV head.
+// Histogram of one pass over the keys of the current prefix set.  V/K: the 4 step keys of each
+// unit, weight = step rate.  Top-k: 32-bit score keys, 1 per token, weight 1, one segment per KV
+// head.  One LDS atomic per key; the set's smallest and largest keys go out once per block.
 template <bool TOPK, int UPT>
 __global__ void __launch_bounds__(256)
 alloc_hist(AllocWs a, const float* __restrict__ weight, const float* __restrict__ sigma,
            int64_t seg_len, int stage, int d, int pass, int nb) {
   __shared__ int64_t h[kBins];
-  __shared__ uint64_t hmn[kBins], hmx[kBins];
+  __shared__ uint64_t wmn[4], wmx[4];
   const int seg = blockIdx.y;
   const SelState s = a.st[seg];
   if (s.done || s.none) return;                // uniform for the block
-  for (int b = threadIdx.x; b < kBins; b += 256) {
-    h[b] = 0;
-    hmn[b] = ~0ull;
-    hmx[b] = 0;
-  }
+  for (int b = threadIdx.x; b < kBins; b += 256) h[b] = 0;
   __syncthreads();
+  uint64_t kmn = ~0ull, kmx = 0;               // extremes of this thread's keys in the prefix set
   const Digit dg = digit_of(pass, nb);
   const uint64_t pre = s.prefix & dg.himask;
   const uint64_t dmask = (1ull << (dg.hi - dg.lo)) - 1;
@@ -524,8 +577,8 @@ alloc_hist(AllocWs a, const float* __restrict__ weight, const float* __restrict_
       if ((key & dg.himask) == pre) {
         const int b = (int)((key >> dg.lo) & dmask);
         atomicAdd((unsigned long long*)&h[b], 1ull);
-        atomicMin((unsigned long long*)&hmn[b], (unsigned long long)key);
-        atomicMax((unsigned long long*)&hmx[b], (unsigned long long)key);
+        kmn = key < kmn ? key : kmn;
+        kmx = key > kmx ? key : kmx;
       }
     } else {
       const int64_t sz = unit_size(stage, d, ul, a.rcount);
@@ -536,19 +589,36 @@ alloc_hist(AllocWs a, const float* __restrict__ weight, const float* __restrict_
         if (kk[k] != 0 && (kk[k] & dg.himask) == pre) {
           const int b = (int)((kk[k] >> dg.lo) & dmask);
           atomicAdd((unsigned long long*)&h[b], (unsigned long long)step_rate(sz, k));
-          atomicMin((unsigned long long*)&hmn[b], (unsigned long long)kk[k]);
-          atomicMax((unsigned long long*)&hmx[b], (unsigned long long)kk[k]);
+          kmn = kk[k] < kmn ? kk[k] : kmn;
+          kmx = kk[k] > kmx ? kk[k] : kmx;
         }
       }
     }
   }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint64_t mo = __shfl_xor(kmn, o, 64), xo = __shfl_xor(kmx, o, 64);
+    kmn = mo < kmn ? mo : kmn;
+    kmx = xo > kmx ? xo : kmx;
+  }
+  if ((threadIdx.x & 63) == 0) {
+    wmn[threadIdx.x >> 6] = kmn;
+    wmx[threadIdx.x >> 6] = kmx;
+  }
   __syncthreads();
   for (int b = threadIdx.x; b < kBins; b += 256) {
-    if (h[b]) {
-      const int64_t gi = (int64_t)seg * kBins + b;
-      atomicAdd((unsigned long long*)&a.hist[gi], (unsigned long long)h[b]);
-      atomicMin((unsigned long long*)&a.hmin[gi], (unsigned long long)hmn[b]);
-      atomicMax((unsigned long long*)&a.hmax[gi], (unsigned long long)hmx[b]);
+    if (h[b]) atomicAdd((unsigned long long*)&a.hist[(int64_t)seg * kBins + b], (unsigned long long)h[b]);
+  }
+  if (threadIdx.x == 0) {
+    uint64_t mn = wmn[0], mx = wmx[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      mn = wmn[w] < mn ? wmn[w] : mn;
+      mx = wmx[w] > mx ? wmx[w] : mx;
+    }
+    if (mn <= mx) {                            // the block saw keys of the prefix set
+      atomicMin((unsigned long long*)&a.pmin[seg], (unsigned long long)mn);
+      atomicMax((unsigned long long*)&a.pmax[seg], (unsigned long long)mx);
     }
   }
 }
@@ -561,14 +631,12 @@ alloc_select(AllocWs a, int pass, int nb) {
   SelState* st = &a.st[seg];
   if (st->done || st->none) return;            // uniform
   int64_t* hist = a.hist + (int64_t)seg * kBins;
-  uint64_t* hmin = a.hmin + (int64_t)seg * kBins;
-  uint64_t* hmax = a.hmax + (int64_t)seg * kBins;
-  select_digit<256>(st, hist, hmin, hmax, pass, nb, wave_tot);
+  select_digit_set<256>(st, hist, a.pmin[seg], a.pmax[seg], pass, nb, wave_tot);
   __syncthreads();
-  for (int b = threadIdx.x; b < kBins; b += 256) {
-    hist[b] = 0;
-    hmin[b] = ~0ull;
-    hmax[b] = 0;
+  for (int b = threadIdx.x; b < kBins; b += 256) hist[b] = 0;
+  if (threadIdx.x == 0) {
+    a.pmin[seg] = ~0ull;
+    a.pmax[seg] = 0;
   }
 }
 
@@ -756,8 +824,8 @@ AllocWs carve(const Layer& L, int stage, char* ws, size_t* total) {
   const size_t hn = (size_t)p.nseg * kBins;
   const size_t o_st = w.take(sizeof(SelState) * p.nseg);
   const size_t o_h = w.take(sizeof(int64_t) * hn);
-  const size_t o_mn = w.take(sizeof(uint64_t) * hn);
-  const size_t o_mx = w.take(sizeof(uint64_t) * hn);
+  const size_t o_mn = w.take(sizeof(uint64_t) * (size_t)p.nseg);
+  const size_t o_mx = w.take(sizeof(uint64_t) * (size_t)p.nseg);
   const int ncb = (int)((L.n + kCountBlock - 1) / kCountBlock);
   const bool kst = (stage == KVC_ALLOC_K_CHANNELS);
   const size_t o_rp = w.take(kst ? sizeof(int32_t) * L.hkv * ncb : 0);
@@ -771,8 +839,8 @@ AllocWs carve(const Layer& L, int stage, char* ws, size_t* total) {
     a.status = reinterpret_cast<int32_t*>(ws);
     a.st = reinterpret_cast<SelState*>(ws + o_st);
     a.hist = reinterpret_cast<int64_t*>(ws + o_h);
-    a.hmin = reinterpret_cast<uint64_t*>(ws + o_mn);
-    a.hmax = reinterpret_cast<uint64_t*>(ws + o_mx);
+    a.pmin = reinterpret_cast<uint64_t*>(ws + o_mn);
+    a.pmax = reinterpret_cast<uint64_t*>(ws + o_mx);
     a.rpart = reinterpret_cast<int32_t*>(ws + o_rp);
     a.rbad = reinterpret_cast<int32_t*>(ws + o_rb);
     a.rcount = reinterpret_cast<int64_t*>(ws + o_r);
