@@ -281,8 +281,24 @@ __device__ __forceinline__ void lse_mask_half(f32x16 (&h)[2], const Geo& G, int 
   }
 }
 
-// Online update of (m, l) with one half tile; no branches (an all-masked half leaves m, l).
-__device__ __forceinline__ void lse_update_half(const f32x16 (&h)[2], float (&m_run)[2],
+// sum_i 2^(c h_i + nm) over the 16 elements of a lane, in four chains that start from their
+// first terms (a chain started from 0 would cost one more add per chain), then a fixed tree.
+__device__ __forceinline__ float sum_exp2_16(const f32x16& h, float c, float nm) {
+  float s0 = fast_exp2(fmaf(h[0], c, nm)), s1 = fast_exp2(fmaf(h[1], c, nm));
+  float s2 = fast_exp2(fmaf(h[2], c, nm)), s3 = fast_exp2(fmaf(h[3], c, nm));
+#pragma unroll
+  for (int i = 4; i < 16; i += 4) {
+    s0 += fast_exp2(fmaf(h[i], c, nm));
+    s1 += fast_exp2(fmaf(h[i + 1], c, nm));
+    s2 += fast_exp2(fmaf(h[i + 2], c, nm));
+    s3 += fast_exp2(fmaf(h[i + 3], c, nm));
+  }
+  return (s0 + s1) + (s2 + s3);
+}
+
+// Online update of (m, l) with one half tile, the running max kept negated (nm_run = -m); no
+// branches (an all-masked half leaves m, l).
+__device__ __forceinline__ void lse_update_half(const f32x16 (&h)[2], float (&nm_run)[2],
                                                 float (&l_run)[2], float c) {
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
@@ -295,18 +311,10 @@ __device__ __forceinline__ void lse_update_half(const f32x16 (&h)[2], float (&m_
     }
     t0 = max3_raw(t0, h[nb][14], h[nb][15]);
     const float tmax = half_max(max_raw(t0, t1));
-    const float mnew = fmaxf(m_run[nb], tmax * c);
-    const float nm = (mnew == -INFINITY) ? 0.f : -mnew;
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; i += 4) {
-      s0 += fast_exp2(fmaf(h[nb][i], c, nm));
-      s1 += fast_exp2(fmaf(h[nb][i + 1], c, nm));
-      s2 += fast_exp2(fmaf(h[nb][i + 2], c, nm));
-      s3 += fast_exp2(fmaf(h[nb][i + 3], c, nm));
-    }
-    l_run[nb] = fmaf(l_run[nb], fast_exp2(m_run[nb] + nm), (s0 + s1) + (s2 + s3));
-    m_run[nb] = mnew;
+    const float nmnew = fminf(nm_run[nb], -(tmax * c));   // -max(m, tmax c)
+    const float nm = (nmnew == INFINITY) ? 0.f : nmnew;
+    l_run[nb] = fmaf(l_run[nb], fast_exp2(nm - nm_run[nb]), sum_exp2_16(h[nb], c, nm));
+    nm_run[nb] = nmnew;
   }
 }
 
@@ -318,25 +326,14 @@ __device__ __forceinline__ void lse_update_half(const f32x16 (&h)[2], float (&m_
 // which the exact update folds in as zero) and a row whose maximum jumps by more than 60
 // in the base-2 domain.  The log-sum-exp m + log2(l) is the same up to rounding for any m
 // at or below the running maximum, so only the row max tree and the rescale are saved.
-__device__ __forceinline__ void lse_update_half_lazy(const f32x16 (&h)[2], float (&m_run)[2],
+__device__ __forceinline__ void lse_update_half_lazy(const f32x16 (&h)[2], float (&nm_run)[2],
                                                      float (&l_run)[2], float c) {
   float s[2];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const float nm = -m_run[nb];
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; i += 4) {
-      s0 += fast_exp2(fmaf(h[nb][i], c, nm));
-      s1 += fast_exp2(fmaf(h[nb][i + 1], c, nm));
-      s2 += fast_exp2(fmaf(h[nb][i + 2], c, nm));
-      s3 += fast_exp2(fmaf(h[nb][i + 3], c, nm));
-    }
-    s[nb] = (s0 + s1) + (s2 + s3);
-  }
+  for (int nb = 0; nb < 2; ++nb) s[nb] = sum_exp2_16(h[nb], c, nm_run[nb]);
   const bool redo = !(s[0] <= 0x1p64f) || !(s[1] <= 0x1p64f);   // also true for NaN
   if (__builtin_amdgcn_ballot_w64(redo) != 0) {
-    lse_update_half(h, m_run, l_run, c);
+    lse_update_half(h, nm_run, l_run, c);
   } else {
     l_run[0] += s[0];
     l_run[1] += s[1];
@@ -368,10 +365,10 @@ __device__ __forceinline__ int full_tiles(const Geo& G, int N, int causal) {
     issue_tile<D, ((S) + 3) & 3>(kh, G.k0 + 64 * ((J) + 3), n, voff, G.wave);               \
     KVC_PHASE_FENCE();                                                                      \
     lse_mfma_half<D, S>(A, qf, 0, G.lo, G.hi);                                              \
-    lse_update_half_lazy(B, m_run, l_run, c);                                               \
+    lse_update_half_lazy(B, nm_run, l_run, c);                                               \
     KVC_PHASE_FENCE();                                                                      \
     lse_mfma_half<D, S>(B, qf, 1, G.lo, G.hi);                                              \
-    lse_update_half_lazy(A, m_run, l_run, c);                                               \
+    lse_update_half_lazy(A, nm_run, l_run, c);                                               \
     KVC_PHASE_FENCE();                                                                      \
   }
 
@@ -379,7 +376,7 @@ __device__ __forceinline__ int full_tiles(const Geo& G, int N, int causal) {
 template <int D, int S>
 __device__ __forceinline__ void lse_masked_step(const Geo& G, const uint16_t* kh, int J, int n, int causal,
                                                 const int (&voff)[4], const bf16x8 (&qf)[2][D / 16],
-                                                float (&m_run)[2], float (&l_run)[2], float c) {
+                                                float (&nm_run)[2], float (&l_run)[2], float c) {
   ring_barrier<D>(2);
   issue_tile<D, (S + 3) & 3>(kh, G.k0 + 64 * (J + 3), n, voff, G.wave);
   const int t0 = G.k0 + 64 * J;
@@ -388,7 +385,7 @@ __device__ __forceinline__ void lse_masked_step(const Geo& G, const uint16_t* kh
   for (int kb = 0; kb < 2; ++kb) {
     lse_mfma_half<D, S>(h, qf, kb, G.lo, G.hi);
     lse_mask_half(h, G, t0 + 32 * kb, n, causal);
-    lse_update_half(h, m_run, l_run, c);
+    lse_update_half(h, nm_run, l_run, c);
   }
 }
 
@@ -407,7 +404,7 @@ lse_partial(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   load_q_frags<D>(qf, q, G.h, Nq, G.i_wave, G.hi, G.lo);
   int voff[4];
   tile_offsets<D>(voff, G.wave, G.lane);
-  float m_run[2] = {-INFINITY, -INFINITY};
+  float nm_run[2] = {INFINITY, INFINITY};      // minus the running maxima
   float l_run[2] = {0.f, 0.f};
   // The first tiles are requested while the Q fragments are still in flight, so the two
   // latencies overlap.  Loads complete in issue order: the first ring wait (at most 2L loads
@@ -432,14 +429,14 @@ lse_partial(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     if (j0 < nfull) KVC_LSE_STEP(0, j0)
     if (j0 + 1 < nfull) KVC_LSE_STEP(1, j0 + 1)
     if (j0 + 2 < nfull) KVC_LSE_STEP(2, j0 + 2)
-    lse_update_half_lazy(B, m_run, l_run, c);   // second half of the last pipelined tile
+    lse_update_half_lazy(B, nm_run, l_run, c);   // second half of the last pipelined tile
   }
   for (int j = nfull; j < G.ntiles; ++j) {
     switch (j & 3) {
-      case 0: lse_masked_step<D, 0>(G, kh, j, n, causal, voff, qf, m_run, l_run, c); break;
-      case 1: lse_masked_step<D, 1>(G, kh, j, n, causal, voff, qf, m_run, l_run, c); break;
-      case 2: lse_masked_step<D, 2>(G, kh, j, n, causal, voff, qf, m_run, l_run, c); break;
-      default: lse_masked_step<D, 3>(G, kh, j, n, causal, voff, qf, m_run, l_run, c); break;
+      case 0: lse_masked_step<D, 0>(G, kh, j, n, causal, voff, qf, nm_run, l_run, c); break;
+      case 1: lse_masked_step<D, 1>(G, kh, j, n, causal, voff, qf, nm_run, l_run, c); break;
+      case 2: lse_masked_step<D, 2>(G, kh, j, n, causal, voff, qf, nm_run, l_run, c); break;
+      default: lse_masked_step<D, 3>(G, kh, j, n, causal, voff, qf, nm_run, l_run, c); break;
     }
   }
   __builtin_amdgcn_s_waitcnt(7 << 4);       // no LDS fill may outlive the block
@@ -449,9 +446,9 @@ lse_partial(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int64_t row = G.i_wave + 32 * nb + G.lo;
     if (G.hi == 0 && row < Nq) {
       if (dc.maxCh == 1)   // one chunk covers the row: write l itself
-        lse[(int64_t)G.h * Nq + row] = (m_run[nb] > -INFINITY) ? (m_run[nb] + log2f(lt)) * kLn2 : -INFINITY;
+        lse[(int64_t)G.h * Nq + row] = (nm_run[nb] < INFINITY) ? (log2f(lt) - nm_run[nb]) * kLn2 : -INFINITY;
       else
-        part[((int64_t)G.h * Nq + row) * dc.maxCh + G.ch] = make_float2(m_run[nb], lt);
+        part[((int64_t)G.h * Nq + row) * dc.maxCh + G.ch] = make_float2(-nm_run[nb], lt);
     }
   }
 }
@@ -537,9 +534,10 @@ __device__ __forceinline__ void score_reduce_half(const f32x16 (&h)[2], const fl
       }
     colv = half_max(fmaxf(m0, m1));
   } else {
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    float s0 = fast_exp2(fmaf(h[0][0], c, -lv[0][0])), s1 = fast_exp2(fmaf(h[0][1], c, -lv[0][1]));
+    float s2 = fast_exp2(fmaf(h[1][0], c, -lv[1][0])), s3 = fast_exp2(fmaf(h[1][1], c, -lv[1][1]));
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) {
+    for (int i = 2; i < 16; i += 2) {
       s0 += fast_exp2(fmaf(h[0][i], c, -lv[0][i]));
       s1 += fast_exp2(fmaf(h[0][i + 1], c, -lv[0][i + 1]));
       s2 += fast_exp2(fmaf(h[1][i], c, -lv[1][i]));
