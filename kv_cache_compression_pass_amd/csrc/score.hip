@@ -65,17 +65,18 @@ struct Decomp {
 
 // Work item of a block.  Items are ordered (g, row tile descending, chunk, head in group),
 // and block b runs on XCD b % 8, so XCD x receives the x-th eighth of the items.
+// W < 2^31 (the launchers check it), so the index arithmetic is 32-bit.
 __device__ __forceinline__ bool decode_work(const Decomp& dc, int& g, int& rt, int& ch, int& hl) {
-  const int64_t b = blockIdx.x;
-  const int64_t per = (dc.W + kXcds - 1) / kXcds;
-  int64_t w = (b % kXcds) * per + b / kXcds;
-  if (w >= dc.W) return false;
-  hl = (int)(w % dc.G);
-  w /= dc.G;
-  ch = (int)(w % dc.maxCh);
-  w /= dc.maxCh;
-  rt = dc.nRT - 1 - (int)(w % dc.nRT);
-  g = (int)(w / dc.nRT);
+  const uint32_t b = blockIdx.x, W = (uint32_t)dc.W;
+  const uint32_t per = (W + kXcds - 1) / kXcds;
+  uint32_t w = (b % kXcds) * per + b / kXcds;
+  if (w >= W) return false;
+  hl = (int)(w % (uint32_t)dc.G);
+  w /= (uint32_t)dc.G;
+  ch = (int)(w % (uint32_t)dc.maxCh);
+  w /= (uint32_t)dc.maxCh;
+  rt = dc.nRT - 1 - (int)(w % (uint32_t)dc.nRT);
+  g = (int)(w / (uint32_t)dc.nRT);
   return true;
 }
 
@@ -990,6 +991,7 @@ size_t score_ws_bytes(const Layer& L, int mode, int hidden_dim) {
 hipError_t launch_row_lse(const Layer& L, const uint16_t* q, const uint16_t* k, float* lse,
                           char* ws, hipStream_t s, int tag) {
   const ScorePlan p = score_plan(L);
+  if (p.W >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   const Decomp dc = decomp_of(L, p);
   WsPlan w;
   float2* part = reinterpret_cast<float2*>(ws + w.take((size_t)L.hq * L.nq * p.maxCh * sizeof(float2)));
@@ -1013,6 +1015,7 @@ hipError_t launch_score(const Layer& L, int mode, const uint16_t* q, const uint1
                         const uint16_t* v, int hidden_dim, float* scores, char* ws,
                         hipStream_t s) {
   const ScorePlan p = score_plan(L);
+  if (p.W >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   const Decomp dc = decomp_of(L, p);
   const bool mx = (mode == KVC_SCORE_MAX);
   WsPlan w;
