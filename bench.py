@@ -39,8 +39,8 @@ CPU_SAMPLE_SECONDS = 12.0      # oracle sample: KV heads are added until this mu
 # scaled by the same counters on a plain copy of known size (profiles/hbm_counters_*.md).
 # A figure holds only for the scorer source it was measured on; otherwise traffic is null.
 MEASURED_TRAFFIC = {
-    "llama8b_prefill_n8192": {"bytes": 91862467,
-                              "score_src_sha256": "8a6446159db3b85d56de0cbd9a711eaa8ddd6d510debf9133ff59960e1185e5f"},
+    "decode_cache_n131072_q512": {"bytes": 309878618,
+                                  "score_src_sha256": "5fc095335bdb6081bf714a3488036e0375c138f3f88d532c6d0332666af39cbf"},
 }
 
 

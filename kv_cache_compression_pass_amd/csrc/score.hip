@@ -63,8 +63,10 @@ struct Decomp {
   int64_t W;
 };
 
-// Work item of a block.  Items are ordered (g, row tile descending, chunk, head in group),
-// and block b runs on XCD b % 8, so XCD x receives the x-th eighth of the items.
+// Work item of a block.  Items are ordered (g, chunk, row tile descending, head in group), and
+// block b runs on XCD b % 8, so XCD x receives the x-th eighth of the items: the items that
+// read one key chunk (every row tile and head of the group) run together on one XCD and share
+// its L2, so each key is fetched from HBM about once.
 // W < 2^31 (the launchers check it), so the index arithmetic is 32-bit.
 __device__ __forceinline__ bool decode_work(const Decomp& dc, int& g, int& rt, int& ch, int& hl) {
   const uint32_t b = blockIdx.x, W = (uint32_t)dc.W;
@@ -73,10 +75,10 @@ __device__ __forceinline__ bool decode_work(const Decomp& dc, int& g, int& rt, i
   if (w >= W) return false;
   hl = (int)(w % (uint32_t)dc.G);
   w /= (uint32_t)dc.G;
-  ch = (int)(w % (uint32_t)dc.maxCh);
-  w /= (uint32_t)dc.maxCh;
   rt = dc.nRT - 1 - (int)(w % (uint32_t)dc.nRT);
-  g = (int)(w / (uint32_t)dc.nRT);
+  w /= (uint32_t)dc.nRT;
+  ch = (int)(w % (uint32_t)dc.maxCh);
+  g = (int)(w / (uint32_t)dc.maxCh);
   return true;
 }
 
@@ -934,11 +936,11 @@ ScorePlan score_plan(const Layer& L) {
   int64_t kmax = 0;
   for (int rt = 0; rt < p.nRT; ++rt) kmax = kend(rt) > kmax ? kend(rt) : kmax;
   // With >= 1024 (head, row tile) items one chunk per item balances well (longest items run
-  // first); otherwise split the keys into chunks (<= 2048, >= 512 keys) until there are
+  // first); otherwise split the keys into chunks (<= 4096, >= 512 keys) until there are
   // >= 2048 non-empty items.
   int KC = (int)(((kmax + 63) / 64) * 64);
   if ((int64_t)p.nRT * L.hq < 1024) {
-    KC = 2048;
+    KC = 4096;
     for (; KC > 512; KC /= 2) {
       int64_t items = 0;
       for (int rt = 0; rt < p.nRT; ++rt) items += (kend(rt) + KC - 1) / KC;
