@@ -8,7 +8,9 @@
 //  16x16x32 bf16 product hold row n % R (the rows are repeated), and per 16-token half
 //      S^T = codes x (q * scale)_hi + codes x (q * scale)_lo + zero x q
 //  over the head's nonzero K channels, since q . k_hat = sum_c q_c zero_c + sum_c (q_c scale_c) code_c
-//  for a quantised channel and q . k for a raw one (code = the raw bf16, scale 1, zero 0).  Codes
+//  for a quantised channel and q . k for a raw one (code = the raw bf16, scale 1, zero 0).  A
+//  32-position block's B operands serve both halves, and its zero term (the same for every token)
+//  is one product.  Codes
 //  and raw bf16 are exact bf16 operands, q * scale enters as a bf16 hi + lo pair (to 2^-17), q and
 //  the zeros (minima of bf16 values) are exact: the logits carry only the float32 accumulation
 //  error.  The channels are ordered by width ("positions"), each width class padded to a multiple
@@ -181,6 +183,31 @@ __device__ __forceinline__ uint4 codes8(uint4 w0, uint4 w1, uint32_t sel_a, int 
   return make_uint4(nib_bf16x2<false>(y0), nib_bf16x2<true>(y0), nib_bf16x2<false>(y1), nib_bf16x2<true>(y1));
 }
 
+// A lane's 8 bf16 A-operand codes of one 32-position block (descriptor dA: path, bit, byte, 2-bit
+// flag, real positions of a raw run); zero for a block past the positions.
+__device__ __forceinline__ uint4 kcodes(uint32_t dA, uint4 w0, uint4 w1) {
+  const int path = (int)((dA >> 12) & 3);
+  uint4 a = make_uint4(0u, 0u, 0u, 0u);
+  if (path != 0) {
+    const int bit = (int)((dA >> 16) & 7);
+    const uint32_t byte = (dA >> 20) & 3;
+    const uint32_t sel = path == 3 ? (byte ? 0x07060302u : 0x05040100u) : 0x0C0C0400u + byte * 0x101u;
+    const uint32_t mask = (dA >> 22) & 1 ? 0x03030303u : 0x0F0F0F0Fu;
+    if (path == 1) a = codes8<1>(w0, w1, sel, bit, mask);
+    else if (path == 2) a = codes8<2>(w0, w1, sel, bit, mask);
+    else {
+      a = codes8<3>(w0, w1, sel, bit, mask);
+      const int nval = (int)((dA >> 24) & 15);   // raw class padding holds copies: zero it
+      uint32_t aa[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        aa[i] &= (2 * i < nval ? 0x0000FFFFu : 0u) | (2 * i + 1 < nval ? 0xFFFF0000u : 0u);
+      a = make_uint4(aa[0], aa[1], aa[2], aa[3]);
+    }
+  }
+  return a;
+}
+
 // bf16 hi / lo words of 8 values (element order), lo = bf16(x - hi).
 __device__ __forceinline__ void hilo8(const float (&x)[8], uint4& hi, uint4& lo) {
   uint32_t h[4], l[4];
@@ -201,23 +228,27 @@ __device__ __forceinline__ void hilo8(const float (&x)[8], uint4& hi, uint4& lo)
 // Reads of the copy buffers.  The compiler would wait for every copy in flight before any read of
 // the array they fill, so these reads are written out (each asm statement waits for its own data
 // before it ends) and the copies are waited for explicitly (wait_vm).  addr: LDS byte address.
-// The operands of one 32-position block: two 16-byte reads at aw (code words) and one each at ah, al,
-// az, aq (q * scale hi, lo, zeros, q).
-__device__ __forceinline__ void lds_rd_kblock(uint32_t aw, uint32_t ah, uint32_t al, uint32_t az, uint32_t aq,
-                                              uint4& w0, uint4& w1, uint4& bh, uint4& bl, uint4& bz, uint4& bq) {
+// The operands of one 32-position block for both token halves: two 16-byte reads each at aw0 and
+// aw1 (the halves' code words) and one each at ah, al, az, aq (q * scale hi, lo, zeros, q).
+__device__ __forceinline__ void lds_rd_kblock(uint32_t aw0, uint32_t aw1, uint32_t ah, uint32_t al, uint32_t az,
+                                               uint32_t aq, uint4& w00, uint4& w01, uint4& w10, uint4& w11,
+                                               uint4& bh, uint4& bl, uint4& bz, uint4& bq) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 x0, x1, x2, x3, x4, x5;
+  u32x4 x0, x1, x2, x3, x4, x5, x6, x7;
   asm volatile(
-      "ds_read_b128 %0, %6\n\tds_read_b128 %1, %6 offset:16\n\tds_read_b128 %2, %7\n\t"
-      "ds_read_b128 %3, %8\n\tds_read_b128 %4, %9\n\tds_read_b128 %5, %10\n\ts_waitcnt lgkmcnt(0)"
-      : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3), "=&v"(x4), "=&v"(x5)
-      : "v"(aw), "v"(ah), "v"(al), "v"(az), "v"(aq));
-  w0 = make_uint4(x0[0], x0[1], x0[2], x0[3]);
-  w1 = make_uint4(x1[0], x1[1], x1[2], x1[3]);
-  bh = make_uint4(x2[0], x2[1], x2[2], x2[3]);
-  bl = make_uint4(x3[0], x3[1], x3[2], x3[3]);
-  bz = make_uint4(x4[0], x4[1], x4[2], x4[3]);
-  bq = make_uint4(x5[0], x5[1], x5[2], x5[3]);
+      "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:16\n\tds_read_b128 %2, %9\n\t"
+      "ds_read_b128 %3, %9 offset:16\n\tds_read_b128 %4, %10\n\tds_read_b128 %5, %11\n\t"
+      "ds_read_b128 %6, %12\n\tds_read_b128 %7, %13\n\ts_waitcnt lgkmcnt(0)"
+      : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3), "=&v"(x4), "=&v"(x5), "=&v"(x6), "=&v"(x7)
+      : "v"(aw0), "v"(aw1), "v"(ah), "v"(al), "v"(az), "v"(aq));
+  w00 = make_uint4(x0[0], x0[1], x0[2], x0[3]);
+  w01 = make_uint4(x1[0], x1[1], x1[2], x1[3]);
+  w10 = make_uint4(x2[0], x2[1], x2[2], x2[3]);
+  w11 = make_uint4(x3[0], x3[1], x3[2], x3[3]);
+  bh = make_uint4(x4[0], x4[1], x4[2], x4[3]);
+  bl = make_uint4(x5[0], x5[1], x5[2], x5[3]);
+  bz = make_uint4(x6[0], x6[1], x6[2], x6[3]);
+  bq = make_uint4(x7[0], x7[1], x7[2], x7[3]);
 }
 __device__ __forceinline__ uint64_t lds_rd_64(uint32_t addr) {
   uint64_t x;
@@ -259,6 +290,31 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F&&
 
 // Staged V words sit in blocks of 64, 66 words apart (copy i of a chunk fills block i).
 __host__ __device__ constexpr int vpad(int u) { return (u >> 6) * 66 + (u & 63); }
+
+// The words of rows 0..7 of two consecutive value tiles (tile CT and CT + 1, HB words per tile per
+// row, RW words per row, padded every 64 words), one wait.
+template <int RW, int CT, int HB>
+__device__ __forceinline__ void lds_rd_tile2(uint32_t addr, uint32_t (&w)[16]) {
+  asm volatile(
+      "ds_read_b32 %0, %16 offset:%17\n\tds_read_b32 %1, %16 offset:%18\n\t"
+      "ds_read_b32 %2, %16 offset:%19\n\tds_read_b32 %3, %16 offset:%20\n\t"
+      "ds_read_b32 %4, %16 offset:%21\n\tds_read_b32 %5, %16 offset:%22\n\t"
+      "ds_read_b32 %6, %16 offset:%23\n\tds_read_b32 %7, %16 offset:%24\n\t"
+      "ds_read_b32 %8, %16 offset:%25\n\tds_read_b32 %9, %16 offset:%26\n\t"
+      "ds_read_b32 %10, %16 offset:%27\n\tds_read_b32 %11, %16 offset:%28\n\t"
+      "ds_read_b32 %12, %16 offset:%29\n\tds_read_b32 %13, %16 offset:%30\n\t"
+      "ds_read_b32 %14, %16 offset:%31\n\tds_read_b32 %15, %16 offset:%32\n\ts_waitcnt lgkmcnt(0)"
+      : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(w[4]), "=&v"(w[5]), "=&v"(w[6]), "=&v"(w[7]),
+        "=&v"(w[8]), "=&v"(w[9]), "=&v"(w[10]), "=&v"(w[11]), "=&v"(w[12]), "=&v"(w[13]), "=&v"(w[14]),
+        "=&v"(w[15])
+      : "v"(addr), "i"(4 * vpad(0 * RW + CT * HB)), "i"(4 * vpad(1 * RW + CT * HB)),
+        "i"(4 * vpad(2 * RW + CT * HB)), "i"(4 * vpad(3 * RW + CT * HB)), "i"(4 * vpad(4 * RW + CT * HB)),
+        "i"(4 * vpad(5 * RW + CT * HB)), "i"(4 * vpad(6 * RW + CT * HB)), "i"(4 * vpad(7 * RW + CT * HB)),
+        "i"(4 * vpad(0 * RW + (CT + 1) * HB)), "i"(4 * vpad(1 * RW + (CT + 1) * HB)),
+        "i"(4 * vpad(2 * RW + (CT + 1) * HB)), "i"(4 * vpad(3 * RW + (CT + 1) * HB)),
+        "i"(4 * vpad(4 * RW + (CT + 1) * HB)), "i"(4 * vpad(5 * RW + (CT + 1) * HB)),
+        "i"(4 * vpad(6 * RW + (CT + 1) * HB)), "i"(4 * vpad(7 * RW + (CT + 1) * HB)));
+}
 
 // Row r < G * Nq of KV head g: query head g * G + r / Nq, query row r % Nq; its index in [H_q][Nq].
 __device__ __forceinline__ int64_t dec_row_index(int g, int G, int64_t Nq, int r) {
@@ -402,12 +458,18 @@ attend_dec_logits(const uint16_t* __restrict__ q, kvc_packed_cache cache, float*
       }
     }
   }
-  int kslot[3];                                   // parameter slots of the positions lane + 64 i
+  // this lane's position pairs 2 lane + 128 i + e: their parameter slots and the query values
+  int kslot[2][2];
+  float qv[2][RP][2];
 #pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    const int pp = lane + 64 * i;
-    kslot[i] = pp < npp ? sm.ppslot[pp] : -1;
-  }
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int pp = 2 * lane + 128 * i + e;
+      kslot[i][e] = pp < npp ? sm.ppslot[pp] : -1;
+#pragma unroll
+      for (int r = 0; r < RP; ++r) qv[i][r][e] = pp < kPPMax ? bf16_bits_to_f32(sm.qb[r][pp]) : 0.f;
+    }
   __syncthreads();
 
   // ---- this wave's groups j_begin + w + 4 k through a ring of NBK slots, each a group's staged
@@ -429,6 +491,7 @@ attend_dec_logits(const uint16_t* __restrict__ q, kvc_packed_cache cache, float*
   lds_u32* ring_l = (lds_u32*)&ring[w * kKRing];
   const uint32_t ring_b = lds_addr(&ring[w * kKRing]);
   const int r_col = ln % RP;
+  constexpr int kIPL = RP >= 4 ? RP / 4 : 1;        // logits a lane stores per token half
   const int64_t lim_col = sm.lim[r_col];
   const uint32_t zrow32[4] = {(uint32_t)sm.zrow[0], (uint32_t)sm.zrow[1], (uint32_t)sm.zrow[2], (uint32_t)sm.zrow[3]};
   auto stage_group = [&](int k, int slot) {
@@ -468,88 +531,100 @@ attend_dec_logits(const uint16_t* __restrict__ q, kvc_packed_cache cache, float*
     if (NBK > 1 && k + NBK - 1 < nw) stage_group(k + NBK - 1, (k + NBK - 1) % NBK);
     const int64_t j = j_begin + w + (int64_t)kDcWaves * k;
     const uint32_t sb = ring_b + 4u * (uint32_t)(slot * SS);
-    // q * scale (hi, lo) and the zeros of this group
+    // q * scale (hi, lo) and the zeros of this group, two positions a lane per 32-bit store
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int pp = lane + 64 * i;
+    for (int i = 0; i < 2; ++i) {
+      const int pp = 2 * lane + 128 * i;
       if (pp < 32 * nkb) {
-        float sc = 1.f, zr = 0.f;
-        if (kslot[i] >= 0) {
-          const uint64_t pv = lds_rd_64(sb + 4u * (uint32_t)(ssw + 2 * kslot[i]));
-          sc = __uint_as_float((uint32_t)pv);
-          zr = __uint_as_float((uint32_t)(pv >> 32));
-        }
-        sm.zbv[w][pp] = kslot[i] >= 0 ? (uint16_t)(__float_as_uint(zr) >> 16) : (uint16_t)0;
+        float sc[2] = {1.f, 1.f};
+        uint32_t zb = 0u;
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          if (kslot[i][e] >= 0) {
+            const uint64_t pv = lds_rd_64(sb + 4u * (uint32_t)(ssw + 2 * kslot[i][e]));
+            sc[e] = __uint_as_float((uint32_t)pv);
+            zb |= ((uint32_t)(pv >> 48)) << (16 * e);   // the zero as bf16 bits (a bf16 value)
+          }
+        *reinterpret_cast<uint32_t*>(&sm.zbv[w][pp]) = zb;
 #pragma unroll
         for (int r = 0; r < RP; ++r) {
-          const float v = bf16_bits_to_f32(sm.qb[r][pp]) * sc;
-          const __bf16 hb = (__bf16)v;
-          const __bf16 lb2 = (__bf16)(v - (float)hb);
-          sm.qah[w][r][pp] = __builtin_bit_cast(uint16_t, hb);
-          sm.qal[w][r][pp] = __builtin_bit_cast(uint16_t, lb2);
+          uint32_t hi = 0u, lo = 0u;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const float v = qv[i][r][e] * sc[e];
+            const __bf16 hb = (__bf16)v;
+            const __bf16 lb2 = (__bf16)(v - (float)hb);
+            hi |= (uint32_t)__builtin_bit_cast(uint16_t, hb) << (16 * e);
+            lo |= (uint32_t)__builtin_bit_cast(uint16_t, lb2) << (16 * e);
+          }
+          *reinterpret_cast<uint32_t*>(&sm.qah[w][r][pp]) = hi;
+          *reinterpret_cast<uint32_t*>(&sm.qal[w][r][pp]) = lo;
         }
       }
     }
     wave_lds_sync();
+    // both token halves per 32-position block: the block's B operands are read once, and the zero
+    // term (the same for every token) is one product per block
+    f32x4 s2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, sz = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < kKBMax; ++kb) {
-        if (kb < nkb) {
-          uint32_t dA = kd[h][kb];
-          asm volatile("" : "+v"(dA));           // derived selectors stay inside the loop
-          const int path = (int)((dA >> 12) & 3);
-          const int pk = 32 * kb + 8 * lg;
-          uint4 w0, w1, bh, bl, az, bq;
-          const int ad = (int)(dA & 0xFFFu);
-          const bool staged = ad + 8 <= cap;
-          lds_rd_kblock(sb + 4u * (uint32_t)(staged ? ad : 0), lds_addr(&sm.qah[w][r_col][pk]),
-                        lds_addr(&sm.qal[w][r_col][pk]), lds_addr(&sm.zbv[w][pk]), lds_addr(&sm.qb[r_col][pk]), w0, w1,
-                        bh, bl, az, bq);
-          if (path != 0 && !staged) {              // past the slot: the group's words in global memory
-            const uint32_t* gw = kwords + j * Wk;
+    for (int kb = 0; kb < kKBMax; ++kb) {
+      if (kb < nkb) {
+        uint32_t dA0 = kd[0][kb], dA1 = kd[1][kb];
+        asm volatile("" : "+v"(dA0), "+v"(dA1));   // derived selectors stay inside the loop
+        const int path = (int)((dA0 >> 12) & 3);
+        const int pk = 32 * kb + 8 * lg;
+        const int ad0 = (int)(dA0 & 0xFFFu), ad1 = (int)(dA1 & 0xFFFu);
+        const bool st0 = ad0 + 8 <= cap, st1 = ad1 + 8 <= cap;
+        uint4 w00, w01, w10, w11, bh, bl, az, bq;
+        lds_rd_kblock(sb + 4u * (uint32_t)(st0 ? ad0 : 0), sb + 4u * (uint32_t)(st1 ? ad1 : 0),
+                       lds_addr(&sm.qah[w][r_col][pk]), lds_addr(&sm.qal[w][r_col][pk]), lds_addr(&sm.zbv[w][pk]),
+                       lds_addr(&sm.qb[r_col][pk]), w00, w01, w10, w11, bh, bl, az, bq);
+        if (path != 0 && (!st0 || !st1)) {       // past the slot: the group's words in global memory
+          const uint32_t* gw = kwords + j * Wk;
+          if (!st0) {
             uint32_t x[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = gw[sm.srcw[ad + i]];
-            w0 = make_uint4(x[0], x[1], x[2], x[3]);
-            w1 = make_uint4(x[4], x[5], x[6], x[7]);
+            for (int i = 0; i < 8; ++i) x[i] = gw[sm.srcw[ad0 + i]];
+            w00 = make_uint4(x[0], x[1], x[2], x[3]);
+            w01 = make_uint4(x[4], x[5], x[6], x[7]);
           }
-          uint4 a = make_uint4(0u, 0u, 0u, 0u);
-          if (path != 0) {
-            const int bit = (int)((dA >> 16) & 7);
-            const uint32_t byte = (dA >> 20) & 3;
-            const uint32_t sel = path == 3 ? (byte ? 0x07060302u : 0x05040100u) : 0x0C0C0400u + byte * 0x101u;
-            const uint32_t mask = (dA >> 22) & 1 ? 0x03030303u : 0x0F0F0F0Fu;
-            if (path == 1) a = codes8<1>(w0, w1, sel, bit, mask);
-            else if (path == 2) a = codes8<2>(w0, w1, sel, bit, mask);
-            else {
-              a = codes8<3>(w0, w1, sel, bit, mask);
-              const int nval = (int)((dA >> 24) & 15);   // raw class padding holds copies: zero it
-              uint32_t aa[4] = {a.x, a.y, a.z, a.w};
+          if (!st1) {
+            uint32_t x[8];
 #pragma unroll
-              for (int i = 0; i < 4; ++i)
-                aa[i] &= (2 * i < nval ? 0x0000FFFFu : 0u) | (2 * i + 1 < nval ? 0xFFFF0000u : 0u);
-              a = make_uint4(aa[0], aa[1], aa[2], aa[3]);
-            }
+            for (int i = 0; i < 8; ++i) x[i] = gw[sm.srcw[ad1 + i]];
+            w10 = make_uint4(x[0], x[1], x[2], x[3]);
+            w11 = make_uint4(x[4], x[5], x[6], x[7]);
           }
-          s = mfma16(a, bh, s);
-          s = mfma16(a, bl, s);
-          s = mfma16(az, bq, s);
         }
+        const uint4 a0 = kcodes(dA0, w00, w01), a1 = kcodes(dA1, w10, w11);
+        s2[0] = mfma16(a0, bh, s2[0]);
+        s2[1] = mfma16(a1, bh, s2[1]);
+        s2[0] = mfma16(a0, bl, s2[0]);
+        s2[1] = mfma16(a1, bl, s2[1]);
+        sz = mfma16(az, bq, sz);
       }
-      // tokens 16 h + 4 lg + i of column ln: the columns of real rows store their logits by V row
-      if (ln < R) {
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x4 s;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] = s2[h][i] + sz[i];
+      // tokens 16 h + 4 lg + i of column ln (row ln % RP): the 16 / RP copies of a row's column share
+      // its four tokens, so a lane stores the logits of IPL of them by V row
+      if (ln % RP < R && (ln / RP) * kIPL < 4) {
         uint4 tk, vl;
         const uint32_t ta = sb + 4u * (uint32_t)(ssw + ssp4 + 16 * h + 4 * lg);
         lds_rd_128_pair(ta, ta + 128u, tk, vl);
-        const uint32_t tks[4] = {tk.x, tk.y, tk.z, tk.w}, vls[4] = {vl.x, vl.y, vl.z, vl.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int ii = 0; ii < kIPL; ++ii) {
+          const int i = (ln / RP) * kIPL + ii;
           if (j * 32 + 16 * h + 4 * lg + i < Rg) {
-            const float v = (int64_t)(int32_t)tks[i] <= lim_col ? s[i] : -INFINITY;
-            const uint32_t row = zrow32[vls[i] >> 29] + (vls[i] & ((1u << 29) - 1u));   // below 2^31
-            logit[row * (uint32_t)RP + (uint32_t)ln] = v;
+            const uint32_t tki = i == 0 ? tk.x : i == 1 ? tk.y : i == 2 ? tk.z : tk.w;
+            const uint32_t vli = i == 0 ? vl.x : i == 1 ? vl.y : i == 2 ? vl.z : vl.w;
+            const float si = i == 0 ? s[0] : i == 1 ? s[1] : i == 2 ? s[2] : s[3];
+            const float v = (int64_t)(int32_t)tki <= lim_col ? si : -INFINITY;
+            const uint32_t row = zrow32[vli >> 29] + (vli & ((1u << 29) - 1u));   // below 2^31
+            logit[row * (uint32_t)RP + (uint32_t)(ln % RP)] = v;
             mx = fmaxf(mx, v);
           }
         }
@@ -559,6 +634,8 @@ attend_dec_logits(const uint16_t* __restrict__ q, kvc_packed_cache cache, float*
     if (NBK == 1 && k + 1 < nw) stage_group(k + 1, 0);
   }
   wave_vm_sync();
+#pragma unroll
+  for (int o = RP; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));   // the copies of a row
   mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
   if (lane < RP) sm.red[w][lane] = mx;
@@ -666,30 +743,34 @@ __device__ __forceinline__ void v_chunk(const float* Ms, uint32_t vb, int crows,
     ozp[ps] += zs;
     uint4 bh, bl;
     hilo8(x, bh, bl);
-    static_for(std::make_integer_sequence<int, NT>{}, [&](auto ctc) {
-      constexpr int ct = decltype(ctc)::value;
+    static_for(std::make_integer_sequence<int, NT / 2>{}, [&](auto cpc) {
+      constexpr int ct = 2 * decltype(cpc)::value;   // tiles ct and ct + 1: one channel group
       if constexpr ((ct / 2) / NGC == ps) {    // the tiles of this pass's channel groups
-        uint4 a = make_uint4(0u, 0u, 0u, 0u);
+        uint4 a0 = make_uint4(0u, 0u, 0u, 0u), a1 = a0;
         if (lane_rows) {
-          uint32_t wv[8];
-          lds_rd_8x32<4 * vpad(0 * RW + ct * (B / 2)), 4 * vpad(1 * RW + ct * (B / 2)),
-                      4 * vpad(2 * RW + ct * (B / 2)), 4 * vpad(3 * RW + ct * (B / 2)),
-                      4 * vpad(4 * RW + ct * (B / 2)), 4 * vpad(5 * RW + ct * (B / 2)),
-                      4 * vpad(6 * RW + ct * (B / 2)), 4 * vpad(7 * RW + ct * (B / 2))>(wbase, wv);
-          a = codes8<PATH>(make_uint4(wv[0], wv[1], wv[2], wv[3]), make_uint4(wv[4], wv[5], wv[6], wv[7]), sel_a,
-                           bit, MASK);
+          uint32_t wv[16];
+          lds_rd_tile2<RW, ct, B / 2>(wbase, wv);
+          a0 = codes8<PATH>(make_uint4(wv[0], wv[1], wv[2], wv[3]), make_uint4(wv[4], wv[5], wv[6], wv[7]), sel_a,
+                            bit, MASK);
+          a1 = codes8<PATH>(make_uint4(wv[8], wv[9], wv[10], wv[11]), make_uint4(wv[12], wv[13], wv[14], wv[15]),
+                            sel_a, bit, MASK);
           if (PATH == 3 && crows < CR) {       // raw rows past the chunk hold stale bit patterns
-            uint32_t aa[4] = {a.x, a.y, a.z, a.w};
+            uint32_t aa[4] = {a0.x, a0.y, a0.z, a0.w}, bb[4] = {a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int k = 8 * lg + 2 * i;
-              aa[i] &= (k < crows ? 0x0000FFFFu : 0u) | (k + 1 < crows ? 0xFFFF0000u : 0u);
+              const uint32_t mk = (k < crows ? 0x0000FFFFu : 0u) | (k + 1 < crows ? 0xFFFF0000u : 0u);
+              aa[i] &= mk;
+              bb[i] &= mk;
             }
-            a = make_uint4(aa[0], aa[1], aa[2], aa[3]);
+            a0 = make_uint4(aa[0], aa[1], aa[2], aa[3]);
+            a1 = make_uint4(bb[0], bb[1], bb[2], bb[3]);
           }
         }
-        o[ct] = mfma16(a, bh, o[ct]);
-        o[ct] = mfma16(a, bl, o[ct]);
+        o[ct] = mfma16(a0, bh, o[ct]);
+        o[ct + 1] = mfma16(a1, bh, o[ct + 1]);
+        o[ct] = mfma16(a0, bl, o[ct]);
+        o[ct + 1] = mfma16(a1, bl, o[ct + 1]);
       }
     });
   });
