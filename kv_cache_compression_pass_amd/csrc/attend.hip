@@ -695,7 +695,7 @@ hipError_t launch_attend(const Layer& L, const uint16_t* q, const kvc_packed_cac
   const int pstride = n_new > 0 ? nsplit + 1 : nsplit;      // partials per row
   WsPlan p;
   float* part = reinterpret_cast<float*>(ws + p.take((size_t)L.hq * L.nq * (nsplit + 1) * (L.d + 2) * sizeof(float)));
-  (void)launch_reset_status(ws, s);
+  if (!dec) (void)launch_reset_status(ws, s);   // the decode path's logits kernel writes the status itself
   int32_t* status = reinterpret_cast<int32_t*>(ws);
   if (dec) {
     char* dws = ws + p.take(decode_ws_bytes(L));

@@ -368,10 +368,10 @@ attend_dec_logits(const uint16_t* __restrict__ q, kvc_packed_cache cache, float*
   const int split = blockIdx.x, g = blockIdx.y;
   const int R = G * (int)Nq;
   const int64_t* H = cache.header;
-  if (H[0] != Hkv || H[1] != D || H[2] != N) {
-    if (t == 0 && split == 0 && g == 0) set_status(status, KVC_DEV_BAD_CACHE);
-    return;
-  }
+  const bool bad = H[0] != Hkv || H[1] != D || H[2] != N;
+  // the call's only status writer (every block sees the same header): no separate reset launch
+  if (t == 0 && split == 0 && g == 0 && status) *status = bad ? KVC_DEV_BAD_CACHE : 0;
+  if (bad) return;
   const int64_t* hp = H + KVC_HDR_GLOBAL + g * KVC_HDR_PER_HEAD;
   const int64_t Rg = hp[4], ngroups = hp[22];
   const int Wk = (int)hp[20], Qk = (int)hp[21];

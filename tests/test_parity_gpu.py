@@ -343,6 +343,39 @@ def test_bad_width_sets_device_status():
     assert st & kvc.DEV_BAD_WIDTH
 
 
+@pytest.mark.parametrize("rows", [1, 40], ids=["decode_path", "matrix_core_path"])
+def test_attend_reports_a_cache_that_does_not_match(rows):
+    """A packed cache whose header does not match the call's descriptor is refused on the device
+    (KVC_DEV_BAD_CACHE; the kernels read nothing past the header), on both attend paths, and the
+    next call with a matching cache and the same workspace clears the status word."""
+    print(f"case bad cache status, {rows} rows per query head", flush=True)
+    hq, hkv, d, N = 4, 2, 64, 300
+    x = make_inputs(hq, hkv, d, N, N, seed=77)
+    desc = H.desc_of(hq, hkv, d, N, N, True)
+    bv = np.full((hkv, N), 4, np.uint8)
+    bk = np.full((hkv, d), 4, np.uint8)
+    cache, st = H.pack(desc, H.dev_bf16(x["k"]), H.dev_bf16(x["v"]), H.dev_u8(bv), H.dev_u8(bk))
+    assert st == 0
+    desc_f = H.desc_of(hq, hkv, d, N, rows, True)
+    qf = H.dev_bf16(np.ascontiguousarray(x["q"][:, N - rows:, :]))
+    ws = kvc.workspace(kvc.OP_COMPRESSED_ATTEND, desc_f, 0, H.DEV)
+    out = torch.empty(hq, rows, d, dtype=torch.float32, device=H.DEV)
+    lse = torch.empty(hq, rows, dtype=torch.float32, device=H.DEV)
+    hdr = cache.buffers["header"]
+    good = hdr[16:24].clone()                       # global header word 2: N
+    hdr[16:24] = torch.from_numpy(np.array([N + 1], np.int64).view(np.uint8)).to(hdr.device)
+    kvc.kvc_compressed_attend(desc_f, qf, cache, out, lse, ws)
+    torch.cuda.synchronize()
+    assert kvc.kvc_get_device_status(ws) == kvc.DEV_BAD_CACHE
+    hdr[16:24] = good
+    kvc.kvc_compressed_attend(desc_f, qf, cache, out, lse, ws)
+    torch.cuda.synchronize()
+    assert kvc.kvc_get_device_status(ws) == 0
+    out_r, lh_r = oracle.compressed_attend(np.ascontiguousarray(x["q"][:, N - rows:, :]), x["k"], x["v"], bv, bk)
+    ty, tl = H.attend_tols(x["q"][:, N - rows:, :], [x["k"]], [x["v"]], lh_r)
+    H.assert_abs(out.cpu().numpy(), out_r, ty, "attend output after a refused call")
+
+
 def test_evict_everything_and_empty_rows():
     print("case evict everything", flush=True)
     hq, hkv, d, N, Nq = 4, 2, 128, 300, 40
