@@ -31,9 +31,11 @@
 //  (16 / R groups per pass, more passes when that is below the number of groups).  Each block
 //  writes (M, l, O) per row as one split; attend_merge combines the splits.
 //
-// Both kernels copy their data straight into per-wave LDS rings (global -> LDS loads) several
+// Both kernels copy their data straight into per-wave LDS rings (global -> LDS loads) one or more
 // groups or chunks ahead and wait for exactly the copies they need; no block barrier runs in the
-// streaming loops.
+// streaming loops.  Both run four waves per SIMD (at most 128 registers; rings sized so that four
+// blocks share a compute unit's LDS): more waves in flight hide the copies and the LDS reads better
+// than deeper rings at three waves.
 #include <utility>
 
 #include "common.hpp"
@@ -48,10 +50,10 @@ constexpr int kDcThreads = 64 * kDcWaves;
 constexpr int kPPMax = 160;            // padded K positions: D <= 128 channels + up to 7 per class
 constexpr int kKBMax = kPPMax / 32;    // 32-position blocks
 constexpr int kKSt = 2304;             // >= staged K words of a group (sum_c b_c * padded count)
-constexpr int kKRing = 2048;           // K ring words per wave (group slots: words, pairs, tokens)
+constexpr int kKRing = 1344;           // K ring words per wave (group slots: words, pairs, tokens)
 constexpr int kKMaxSlots = 8;
 constexpr int kVSlotWords = 792;       // V chunk words and pairs: 12 blocks of 64 words, 2 apart
-constexpr int kVSlots = 3;             // V ring slots per wave
+constexpr int kVSlots = 2;             // V ring slots per wave
 
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -356,7 +358,7 @@ struct LgSmem {
 };
 
 template <int D, int RP>
-__global__ void __launch_bounds__(kDcThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+__global__ void __launch_bounds__(kDcThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 attend_dec_logits(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __restrict__ logit,
                   float* __restrict__ bmax, int G, int Hkv, int64_t N, int64_t Nq, int64_t shift, int causal,
                   float c, int nsplit, int32_t* __restrict__ status) {
@@ -460,15 +462,17 @@ attend_dec_logits(const uint16_t* __restrict__ q, kvc_packed_cache cache, float*
   }
   // this lane's position pairs 2 lane + 128 i + e: their parameter slots and the query values
   int kslot[2][2];
-  float qv[2][RP][2];
-#pragma unroll
+  float qv[RP][2];                                // the query at the first pair (the second, positions
+#pragma unroll                                    // 128.., is read from LDS where it is used)
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int pp = 2 * lane + 128 * i + e;
       kslot[i][e] = pp < npp ? sm.ppslot[pp] : -1;
+      if (i == 0) {
 #pragma unroll
-      for (int r = 0; r < RP; ++r) qv[i][r][e] = pp < kPPMax ? bf16_bits_to_f32(sm.qb[r][pp]) : 0.f;
+        for (int r = 0; r < RP; ++r) qv[r][e] = bf16_bits_to_f32(sm.qb[r][pp]);
+      }
     }
   __syncthreads();
 
@@ -551,7 +555,7 @@ attend_dec_logits(const uint16_t* __restrict__ q, kvc_packed_cache cache, float*
           uint32_t hi = 0u, lo = 0u;
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            const float v = qv[i][r][e] * sc[e];
+            const float v = (i == 0 ? qv[r][e] : bf16_bits_to_f32(sm.qb[r][pp + e])) * sc[e];
             const __bf16 hb = (__bf16)v;
             const __bf16 lb2 = (__bf16)(v - (float)hb);
             hi |= (uint32_t)__builtin_bit_cast(uint16_t, hb) << (16 * e);
@@ -777,7 +781,7 @@ __device__ __forceinline__ void v_chunk(const float* Ms, uint32_t vb, int crows,
 }
 
 template <int D, int RP>
-__global__ void __launch_bounds__(kDcThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+__global__ void __launch_bounds__(kDcThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 attend_dec_values(kvc_packed_cache cache, const float* __restrict__ logit, const float* __restrict__ bmax,
                   float* __restrict__ part, int G, int Hkv, int64_t N, int64_t Nq, float c, int nsa, int nsplit,
                   int pstride) {
@@ -920,13 +924,24 @@ attend_dec_values(kvc_packed_cache cache, const float* __restrict__ logit, const
 
 }  // namespace
 
-int decode_nsplit(const Layer& L) {
+static int logits_nsplit(const Layer& L) {
   const int64_t groups = (L.n + 31) / 32;                 // K groups per head, at most
-  int64_t want = (768 + L.hkv - 1) / L.hkv;               // three blocks per compute unit, one round
+  int64_t want = (1024 + L.hkv - 1) / L.hkv;              // four blocks per compute unit, one round
   const int64_t cap = (groups + 3) / 4;                   // at least one group per wave
   if (want > cap) want = cap;
-  if (want > 255) want = 255;                             // one more split for the append buffer
+  if (want > 255) want = 255;
   if (want < 1) want = 1;
+  return (int)want;
+}
+
+int decode_nsplit(const Layer& L) {                       // the values kernel's splits (partials per row)
+  const int64_t chunks = (L.n + 7) / 8;                   // V chunks per head, at most
+  int64_t want = (1024 + L.hkv - 1) / L.hkv;              // four blocks per compute unit, one round
+  const int64_t cap = (chunks + 3) / 4;
+  if (want > cap) want = cap;
+  if (want > 255) want = 255;                             // one more split for the append buffer
+  const int nsa = logits_nsplit(L);
+  if (want < nsa) want = nsa;                             // the logits blocks' maxima fit the same array
   return (int)want;
 }
 
@@ -943,16 +958,17 @@ size_t decode_ws_bytes(const Layer& L) {
 
 hipError_t launch_attend_decode(const Layer& L, const uint16_t* q, const kvc_packed_cache& cache, float* part,
                                 int nsplit, int pstride, int64_t shift, int32_t* status, char* dws, hipStream_t s) {
-  const dim3 grid((unsigned)nsplit, (unsigned)L.hkv);
+  const int nsa = logits_nsplit(L);
+  const dim3 grid((unsigned)nsa, (unsigned)L.hkv), gridv((unsigned)nsplit, (unsigned)L.hkv);
   const int rp = decode_rows_padded(L);
   float* logit = reinterpret_cast<float*>(dws);
   float* bm = reinterpret_cast<float*>(dws + (((size_t)L.hkv * (size_t)L.n * rp * sizeof(float) + 255) & ~size_t(255)));
 #define KVC_DC(DD, RR)                                                                                          \
   do {                                                                                                          \
     attend_dec_logits<DD, RR><<<grid, kDcThreads, 0, s>>>(q, cache, logit, bm, L.G, L.hkv, L.n, L.nq, shift,     \
-                                                          L.causal, L.c_log2, nsplit, status);                  \
-    attend_dec_values<DD, RR><<<grid, kDcThreads, 0, s>>>(cache, logit, bm, part, L.G, L.hkv, L.n, L.nq,         \
-                                                          L.c_log2, nsplit, nsplit, pstride);                   \
+                                                          L.causal, L.c_log2, nsa, status);                     \
+    attend_dec_values<DD, RR><<<gridv, kDcThreads, 0, s>>>(cache, logit, bm, part, L.G, L.hkv, L.n, L.nq,        \
+                                                           L.c_log2, nsa, nsplit, pstride);                     \
   } while (0)
   if (L.d == 128) {
     if (rp == 1) KVC_DC(128, 1);
