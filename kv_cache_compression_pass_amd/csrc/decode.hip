@@ -935,7 +935,7 @@ static int logits_nsplit(const Layer& L) {
 }
 
 int decode_nsplit(const Layer& L) {                       // the values kernel's splits (partials per row)
-  const int64_t chunks = (L.n + 7) / 8;                   // V chunks per head, at most
+  const int64_t chunks = (L.n + 31) / 32;                 // V chunks per head if most tokens sit below 16 bits
   int64_t want = (1024 + L.hkv - 1) / L.hkv;              // four blocks per compute unit, one round
   const int64_t cap = (chunks + 3) / 4;
   if (want > cap) want = cap;
