@@ -39,7 +39,7 @@ template <int D>
 struct AttnSmem {
   uint16_t khi[2][32][D + 8];   // two buffers: group j is decoded into buffer j & 1
   uint16_t klo[2][32][D + 8];
-  _Float16 vt[2][D][32 + 8];
+  _Float16 vt[2][D][32 + 4];   // rows of 18 words: the operand reads (8 bytes a lane) hit distinct banks
   int32_t tok[2][32];
   int32_t kinfo[D][4];     // channels in width order: {channel, word offset, param slot, width}
   int64_t vzone[4][2];     // V zones by width class: first word, first (scale, zero) pair
