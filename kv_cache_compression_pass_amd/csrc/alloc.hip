@@ -30,6 +30,7 @@ namespace kvc {
 
 namespace {
 
+constexpr int kHistUpt = 4;           // multi-block V/K histograms: units per thread of a 1024-thread block
 constexpr int kMaxBlocks = 512;       // multi-block path: units per thread (1..16) chosen so that
                                        // the blocks of all segments stay within this
 constexpr int kSmallUnits = 2048;      // single-block path: up to 8192 keys in LDS
@@ -549,28 +550,68 @@ __device__ __forceinline__ void keys_of(const float* weight, const float* sigma,
   unit_keys(c, unit_size(stage, d, u, rcount), kk);
 }
 
+// Cheap bounds on the four step keys of a unit (cost c > 0, size s > 0), as float64 bit patterns:
+// the keys in float32 (c * (theta_num / theta_den) * (1 / s), five roundings, within 2^-21.6 of the
+// exact quotient), widened to a float64 pattern.  Positive doubles order like their patterns, and
+// within 2^-21.6 of a value the pattern moves by less than 2^31.5, so the exact key's pattern lies
+// in [ak - kKeyMargin, ak + kKeyMargin].  false when an estimate is not a normal float32 (then only
+// the exact keys may decide).
+constexpr uint64_t kKeyMargin = 1ull << 33;
+__constant__ float kThetaF[4] = {0.375f, 0.09375f, 0.0146484375f, 255.0f / 524288.0f};
+
+__device__ __forceinline__ bool key_bounds(float c, int64_t s, uint64_t (&ak)[4]) {
+  const float inv = 1.0f / (float)s;
+  bool ok = true;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t b = __float_as_uint((c * kThetaF[k]) * inv);
+    const uint32_t e = b >> 23;                // c > 0: the sign bit is clear
+    ok = ok && e > 0u && e < 255u;
+    ak[k] = ((uint64_t)(e + 896u) << 52) | ((uint64_t)(b & 0x7FFFFFu) << 29);
+  }
+  return ok;
+}
+
+// Whether some step key of the unit may carry the prefix `pre` (pattern bits at and above bit hi).
+__device__ __forceinline__ bool may_carry(float c, int64_t s, uint64_t pre, int hi) {
+  if (!(c > 0.f) || s <= 0) return false;     // no positive key
+  if (hi >= 64) return true;                  // the first pass takes every key
+  uint64_t ak[4];
+  if (!key_bounds(c, s, ak)) return true;
+  const uint64_t end = pre + (1ull << hi);     // the prefix set is [pre, end)
+  bool any = false;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint64_t lo = ak[k] > kKeyMargin ? ak[k] - kKeyMargin : 0ull;
+    any = any || (ak[k] + kKeyMargin >= pre && lo < end);
+  }
+  return any;
+}
+
 // Histogram of one pass over the keys of the current prefix set.  V/K: the 4 step keys of each
 // unit, weight = step rate.  Top-k: 32-bit score keys, 1 per token, weight 1, one segment per KV
-// head.  One LDS atomic per key; the set's smallest and largest keys go out once per block.
-template <bool TOPK, int UPT>
-__global__ void __launch_bounds__(256)
+// head.  The set's smallest and largest keys go out once per block.
+template <bool TOPK, int UPT, int NT>
+__global__ void __launch_bounds__(NT)
 alloc_hist(AllocWs a, const float* __restrict__ weight, const float* __restrict__ sigma,
            int64_t seg_len, int stage, int d, int pass, int nb) {
   __shared__ int64_t h[kBins];
-  __shared__ uint64_t wmn[4], wmx[4];
+  __shared__ uint64_t wmn[NT / 64], wmx[NT / 64];
   const int seg = blockIdx.y;
   const SelState s = a.st[seg];
   if (s.done || s.none) return;                // uniform for the block
-  for (int b = threadIdx.x; b < kBins; b += 256) h[b] = 0;
+  for (int b = threadIdx.x; b < kBins; b += NT) h[b] = 0;
   __syncthreads();
   uint64_t kmn = ~0ull, kmx = 0;               // extremes of this thread's keys in the prefix set
+  int rb[4] = {-1, -1, -1, -1};                // V/K: per step, the bin of the current run and its rates
+  int64_t rs[4] = {0, 0, 0, 0};
   const Digit dg = digit_of(pass, nb);
   const uint64_t pre = s.prefix & dg.himask;
   const uint64_t dmask = (1ull << (dg.hi - dg.lo)) - 1;
-  const int64_t base = (int64_t)blockIdx.x * (256 * UPT);
+  const int64_t base = (int64_t)blockIdx.x * (NT * UPT);
 #pragma unroll
   for (int j = 0; j < UPT; ++j) {
-    const int64_t ul = base + threadIdx.x + j * 256;
+    const int64_t ul = base + threadIdx.x + j * NT;
     if (ul >= seg_len) continue;
     if (TOPK) {
       const uint64_t key = score_key(weight[(int64_t)seg * seg_len + ul]);
@@ -581,19 +622,39 @@ alloc_hist(AllocWs a, const float* __restrict__ weight, const float* __restrict_
         kmx = key > kmx ? key : kmx;
       }
     } else {
+      // The float64 keys only where their float32 bounds may reach the prefix set (after the first
+      // pass, few units).  Key k of a thread's units often falls in the same bin as the previous
+      // one (nearly always on the first passes, where the bins are exponent ranges): each k's rates
+      // are summed in registers while the bin repeats, so the LDS atomics, which serialise on a
+      // shared address, come once per run.
       const int64_t sz = unit_size(stage, d, ul, a.rcount);
+      float cu = weight[ul];
+      if (sigma) cu = cu * sigma[ul];
+      if (!may_carry(cu, sz, pre, dg.hi)) continue;
       uint64_t kk[4];
-      keys_of(weight, sigma, stage, d, ul, a.rcount, kk);
+      unit_keys(cu, sz, kk);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         if (kk[k] != 0 && (kk[k] & dg.himask) == pre) {
           const int b = (int)((kk[k] >> dg.lo) & dmask);
-          atomicAdd((unsigned long long*)&h[b], (unsigned long long)step_rate(sz, k));
+          const int64_t r = step_rate(sz, k);
+          if (b != rb[k]) {
+            if (rb[k] >= 0) atomicAdd((unsigned long long*)&h[rb[k]], (unsigned long long)rs[k]);
+            rb[k] = b;
+            rs[k] = r;
+          } else {
+            rs[k] += r;
+          }
           kmn = kk[k] < kmn ? kk[k] : kmn;
           kmx = kk[k] > kmx ? kk[k] : kmx;
         }
       }
     }
+  }
+  if (!TOPK) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (rb[k] >= 0) atomicAdd((unsigned long long*)&h[rb[k]], (unsigned long long)rs[k]);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -606,13 +667,13 @@ alloc_hist(AllocWs a, const float* __restrict__ weight, const float* __restrict_
     wmx[threadIdx.x >> 6] = kmx;
   }
   __syncthreads();
-  for (int b = threadIdx.x; b < kBins; b += 256) {
+  for (int b = threadIdx.x; b < kBins; b += NT) {
     if (h[b]) atomicAdd((unsigned long long*)&a.hist[(int64_t)seg * kBins + b], (unsigned long long)h[b]);
   }
   if (threadIdx.x == 0) {
     uint64_t mn = wmn[0], mx = wmx[0];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) {
+    for (int w = 1; w < NT / 64; ++w) {
       mn = wmn[w] < mn ? wmn[w] : mn;
       mx = wmx[w] > mx ? wmx[w] : mx;
     }
@@ -657,9 +718,35 @@ __device__ __forceinline__ int64_t unit_tie(const AllocWs& a, const float* weigh
     *n = key > s.prefix ? 1 : 0;
     return key == s.prefix ? 1 : 0;
   }
+  float c = weight[u];
+  if (sigma) c = c * sigma[u];
+  const int64_t sz = unit_size(stage, d, u, a.rcount);
+  if (!(c > 0.f) || sz <= 0) {                 // no positive key: no step, no tie
+    *n = 0;
+    return 0;
+  }
+  if (s.all_fit) {                             // every positive step is taken
+    *n = 4;
+    return 0;
+  }
+  uint64_t ak[4];
+  if (key_bounds(c, sz, ak)) {                 // decided by the bounds unless a key may equal lambda*
+    int cnt = 0;
+    bool near = false;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint64_t lo = ak[k] > kKeyMargin ? ak[k] - kKeyMargin : 0ull;
+      cnt += lo > s.prefix ? 1 : 0;
+      near = near || (lo <= s.prefix && ak[k] + kKeyMargin >= s.prefix);
+    }
+    if (!near) {
+      *n = cnt;
+      return 0;
+    }
+  }
   uint64_t kk[4];
-  keys_of(weight, sigma, stage, d, u, a.rcount, kk);
-  return steps_and_tie(kk, unit_size(stage, d, u, a.rcount), s.prefix, s.all_fit != 0, n);
+  unit_keys(c, sz, kk);
+  return steps_and_tie(kk, sz, s.prefix, false, n);
 }
 
 // Block sums of the tie rates (units in index order, UPT per thread).
@@ -857,12 +944,17 @@ void launch_passes(const AllocWs& a, const Plan& p, const Layer& L, int stage, c
                    const float* sigma, int keep_bits, uint8_t* bits_out, hipStream_t s) {
   const bool topk = (stage == KVC_ALLOC_TOPK);
   const dim3 g2((unsigned)p.nblk, (unsigned)p.nseg);
+  const int64_t gh = (p.seg_len + 1024 * kHistUpt - 1) / (1024 * kHistUpt);
   const int npass = passes_of(p.nb);
   for (int pass = 0; pass < npass; ++pass) {
     if (topk)
-      alloc_hist<true, UPT><<<g2, 256, 0, s>>>(a, weight, nullptr, p.seg_len, stage, L.d, pass, p.nb);
+      alloc_hist<true, UPT, 256><<<g2, 256, 0, s>>>(a, weight, nullptr, p.seg_len, stage, L.d, pass, p.nb);
+    else if (gh >= 256)   // a large stage: 1024-thread blocks, one per compute unit, each flushing its
+                          // LDS bins to the global histogram once for four times the units
+      alloc_hist<false, kHistUpt, 1024><<<dim3((unsigned)gh), 1024, 0, s>>>(a, weight, sigma, p.seg_len, stage, L.d,
+                                                                       pass, p.nb);
     else
-      alloc_hist<false, UPT><<<g2, 256, 0, s>>>(a, weight, sigma, p.seg_len, stage, L.d, pass, p.nb);
+      alloc_hist<false, UPT, 256><<<g2, 256, 0, s>>>(a, weight, sigma, p.seg_len, stage, L.d, pass, p.nb);
     alloc_select<<<p.nseg, 256, 0, s>>>(a, pass, p.nb);
   }
   if (topk) {
