@@ -367,66 +367,74 @@ __device__ __forceinline__ double rsqrt_newton(double a) {
   return y;
 }
 
-// Cholesky of the 32 x 32 tile in LDS (lower part) and the inverse of its factor, both
-// right-looking with all threads.  Thread t owns the fixed positions e = t + 256 u (u < 3) of
-// the 528-element lower triangle, in A and in X (X starts as I).  Column j of A and row j of X
-// are left unscaled in LDS: with rd_j = 1 / sqrt(a_jj) and l_ij = a_ij rd_j, step j makes every
-// owned A(i, c), j < c <= i, drop l_ij (a_cj rd_j) and every owned X(i, c), c <= j < i, drop
-// l_ij (x_jc rd_j).  A step writes neither column j of A nor row j of X nor the next pivot's
-// inputs that other threads read, so each step is one batch of LDS reads, one batch of writes
-// and one barrier.  At the end L(i, j) = a_ij rd_j (a_jj rd_j on the diagonal) and
-// L^-1(i, c) = x_ic rd_i.  Writes L (lower, zeros above) to Ld (row stride ld) and L^-1 to Li
-// (32 x 32).  A pivot that is not positive sets the status bit.
-__device__ __forceinline__ void potrf_tile(double (*A)[kNB + 1], double (*X)[kNB + 1], double* __restrict__ Ld,
+__device__ __forceinline__ double readlane_f64(double x, int lane) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Step J of the factorisation below (a template, so that every register index is a constant).
+template <int J>
+__device__ __forceinline__ void potrf_step(double (&r)[kNB], double& piv, bool& bad, double (*B)[kNB], int row,
+                                           bool fac) {
+  bad |= !(piv > 0.0);
+  const double m = r[J] * rsqrt_newton(piv);
+  r[J] = m;
+  if constexpr (J + 1 < kNB) {
+    if (fac) B[J][row] = m;                                       // L(row, J), read back as L(e, J)
+    piv = readlane_f64(fma(-m, m, r[J + 1]), J + 1);              // lane J+1: a_{J+1,J+1} - L(J+1, J)^2
+    __builtin_amdgcn_wave_barrier();
+    if constexpr ((J + 1) & 1) r[J + 1] = fma(-m, B[J][J + 1], r[J + 1]);
+#pragma unroll
+    for (int e = ((J + 1) & 1) ? J + 2 : J + 1; e < kNB; e += 2) {
+      const double2 b = *reinterpret_cast<const double2*>(&B[J][e]);
+      r[e] = fma(-m, b.x, r[e]);
+      r[e + 1] = fma(-m, b.y, r[e + 1]);
+    }
+    // the updated row is materialised here: left to itself the compiler sinks each element's
+    // updates to its own step, keeping every earlier multiplier and column value alive
+#pragma unroll
+    for (int e = J + 1; e < kNB; ++e) asm volatile("" : "+v"(r[e]));
+    potrf_step<J + 1>(r, piv, bad, B, row, fac);
+  }
+}
+
+// Cholesky of the 32 x 32 tile in LDS (lower part) and the inverse of its factor, by the first
+// wave of the block alone, with every row in registers (no block barrier in the 32 steps).
+// Lane i < 32 holds row i of A; lane 32 + c holds column c of the identity, which becomes column
+// c of L^-1 (the elimination form L X = I: row j of X is row j of the reduced right side over
+// L_jj, then every later row drops L_ej times it).  Step j: with rd_j = 1 / sqrt(pivot_j), every
+// lane scales its element j by rd_j (lane i: L(i, j); lane 32 + c: L^-1(j, c)) and subtracts that
+// element times L(e, j) from its elements e > j.  The column L(., j) is passed through LDS (one
+// row of B per step).  The next pivot, lane j+1's element j+1 after the update, is formed by lane
+// j+1 from its own element j and read with readlane, so the chain of pivots never waits on LDS.
+// Elements above the diagonal of A's rows end with values nobody reads; the elements of the
+// inverse's columns above the diagonal keep their zeros (their multipliers are zeros of L^-1).
+// Writes L (lower, zeros above) to Ld (row stride ld) and L^-1 to Li (32 x 32).  A pivot that
+// is not positive sets the status bit.  The caller has written the tile and passed a barrier;
+// B is 31 x 32 doubles of LDS with 16-byte aligned rows.
+__device__ __forceinline__ void potrf_tile(const double (*A)[kNB + 1], double (*B)[kNB], double* __restrict__ Ld,
                                            int64_t ld, double* __restrict__ Li, int32_t* __restrict__ status) {
-  constexpr int kTri = kNB * (kNB + 1) / 2;          // 528
-  constexpr int kPer = (kTri + 255) / 256;           // 3
-  __shared__ double rdv[kNB];
-  const int tid = threadIdx.x;
-  int ei[kPer], ec[kPer], ri[kPer], rc[kPer];        // owned position (-1: none), and a readable one
+  const int lane = threadIdx.x & 63;
+  const int row = lane & 31;
+  const bool fac = lane < 32;
+  double r[kNB];
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) {                   // element e -> (i, c), e = i (i + 1) / 2 + c
-    const int e = tid + 256 * u;
-    int i = 0;
-    while ((i + 1) * (i + 2) / 2 <= e && i < kNB) ++i;
-    ei[u] = e < kTri ? i : -1;
-    ec[u] = e < kTri ? e - i * (i + 1) / 2 : 0;
-    ri[u] = e < kTri ? ei[u] : 0;
-    rc[u] = ec[u];
+  for (int e = 0; e < kNB; ++e) {
+    const double a = A[row][e];
+    r[e] = fac ? a : (e == row ? 1.0 : 0.0);
   }
-  for (int e = tid; e < kNB * kNB; e += blockDim.x) X[e / kNB][e % kNB] = (e / kNB == e % kNB) ? 1.0 : 0.0;
+  double piv = readlane_f64(r[0], 0);
   bool bad = false;
-  __syncthreads();
-  for (int j = 0; j < kNB; ++j) {
-    const double piv = A[j][j];
-    double aij[kPer], acj[kPer], xjc[kPer], aic[kPer], xic[kPer];
+  potrf_step<0>(r, piv, bad, B, row, fac);
+  if (bad && lane == 0) atomicOr(status, KVC_DEV_NOT_SPD);
+  if (fac) {
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {                 // every read of the step, issued together
-      aij[u] = A[ri[u]][j];
-      acj[u] = A[rc[u]][j];
-      xjc[u] = X[j][rc[u]];
-      aic[u] = A[ri[u]][rc[u]];
-      xic[u] = X[ri[u]][rc[u]];
-    }
-    bad |= !(piv > 0.0);
-    const double rd = rsqrt_newton(piv);
-    if (tid == 0) rdv[j] = rd;
+    for (int c = 0; c < kNB; ++c) Ld[row * ld + c] = c <= row ? r[c] : 0.0;
+  } else {
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int i = ei[u], c = ec[u];
-      if (i > j) {
-        const double lij = aij[u] * rd;
-        if (c > j) A[i][c] = aic[u] - lij * (acj[u] * rd);
-        else X[i][c] = xic[u] - lij * (xjc[u] * rd);
-      }
-    }
-    __syncthreads();
-  }
-  if (bad && tid == 0) atomicOr(status, KVC_DEV_NOT_SPD);
-  for (int e = tid; e < kNB * kNB; e += blockDim.x) {
-    const int rr = e / kNB, c = e % kNB;
-    Ld[rr * ld + c] = c < rr ? A[rr][c] * rdv[c] : (c == rr ? A[rr][rr] * rdv[rr] : 0.0);
-    Li[e] = c <= rr ? X[rr][c] * rdv[rr] : 0.0;
+    for (int i = 0; i < kNB; ++i) Li[i * kNB + row] = i >= row ? r[i] : 0.0;
   }
 }
 
@@ -482,7 +490,9 @@ __device__ __forceinline__ void zero2(double (&c)[2][2]) { c[0][0] = c[0][1] = c
 __global__ void __launch_bounds__(256)
 ridge_chol(double* __restrict__ M, double* __restrict__ Lm, double* __restrict__ Li, double* __restrict__ Bm,
            double* __restrict__ Yf, RidgeDims r, int kb, int32_t* __restrict__ status) {
-  __shared__ Tile Ls, Xi, Xj, Xk;
+  __shared__ Tile Ls, Xj, Xk;
+  __shared__ __attribute__((aligned(16))) Tile Xi;                // also the factorisation's column rows
+  double (*const Bc)[kNB] = reinterpret_cast<double (*)[kNB]>(&Xi[0][0]);
   const int g = blockIdx.y;
   const int64_t np = r.npad, D = r.d;
   double* Mg = M + (int64_t)g * np * np;
@@ -490,7 +500,8 @@ ridge_chol(double* __restrict__ M, double* __restrict__ Lm, double* __restrict__
   double* Lig = Li + (int64_t)g * r.nb * kNB * kNB;
   if (kb < 0) {
     tile_load(Ls, Mg, np);
-    potrf_tile(Ls, Xi, Lg, np, Lig, status);
+    __syncthreads();
+    if (threadIdx.x < 64) potrf_tile(Ls, Bc, Lg, np, Lig, status);
     return;
   }
   const int rem = r.nb - 1 - kb;
@@ -578,7 +589,9 @@ ridge_chol(double* __restrict__ M, double* __restrict__ Lm, double* __restrict__
   if (ib == kb + 1 && jb == kb + 1) {                             // look-ahead: factor the next diagonal tile
     __syncthreads();
     tile_put(Ls, c);
-    potrf_tile(Ls, Xi, Lg + (int64_t)ib * kNB * np + (int64_t)ib * kNB, np, Lig + (int64_t)ib * kNB * kNB, status);
+    __syncthreads();
+    if (threadIdx.x < 64)
+      potrf_tile(Ls, Bc, Lg + (int64_t)ib * kNB * np + (int64_t)ib * kNB, np, Lig + (int64_t)ib * kNB * kNB, status);
   }
 }
 
