@@ -28,7 +28,7 @@ namespace {
 
 constexpr int kT = 64;          // tile edge of the probability, residual and Gram kernels
 constexpr int kNB = 32;         // block edge of the Cholesky factorisation and the solves
-constexpr int kSplit = 4;       // parts of the row sum in the Gram products
+constexpr int kSplit = 5;       // parts of the row sum in the Gram products
 
 struct RidgeDims {
   int hq, hkv, d, G, causal;
@@ -245,11 +245,13 @@ ridge_resid(const float* __restrict__ P, const uint16_t* __restrict__ v_r, const
 // sums on the fp64 matrix cores (v_mfma_f64_16x16x4f64: A[i][k] from lane i + 16k, B[k][j] from
 // lane j + 16k, D[i][j] in lane j + 16 (i % 4), register i / 4).  Wave w owns the 16 tile rows
 // 16w .. 16w+15 and all 64 columns (four 16 x 16 accumulators); each step of 4 staged rows is
-// one A fragment, four B fragments and four MFMAs per wave, in a fixed order.
+// one A fragment, four B fragments and four MFMAs per wave, in a fixed order.  Four waves per
+// SIMD (at most 128 registers: the step loop is unrolled twice, not eight times) and five row
+// parts make about four blocks per compute unit, so the whole grid runs in one round.
 typedef double v4d __attribute__((ext_vector_type(4)));
 
 template <int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4)))
 ridge_gram(const float* __restrict__ P, const float* __restrict__ T, double* __restrict__ Mp,
            double* __restrict__ Bp, RidgeDims r) {
   __shared__ double xs[32][kT + 1];
@@ -306,7 +308,7 @@ ridge_gram(const float* __restrict__ P, const float* __restrict__ T, double* __r
     }
     __syncthreads();
     if (q0 + 32 < rend) fetch(q0 + 32);
-#pragma unroll
+#pragma unroll 2
     for (int k0 = 0; k0 < 32; k0 += 4) {
       const double av = xs[k0 + lk][16 * w + li];
 #pragma unroll
@@ -376,27 +378,32 @@ __device__ __forceinline__ double readlane_f64(double x, int lane) {
 
 // Step J of the factorisation below (a template, so that every register index is a constant).
 template <int J>
-__device__ __forceinline__ void potrf_step(double (&r)[kNB], double& piv, bool& bad, double (*B)[kNB], int row,
+__device__ __forceinline__ void potrf_step(double (&r)[kNB], double& rd, bool& bad, double (*B)[kNB], int row,
                                            bool fac) {
-  bad |= !(piv > 0.0);
-  const double m = r[J] * rsqrt_newton(piv);
+  const double m = r[J] * rd;
   r[J] = m;
   if constexpr (J + 1 < kNB) {
     if (fac) B[J][row] = m;                                       // L(row, J), read back as L(e, J)
-    piv = readlane_f64(fma(-m, m, r[J + 1]), J + 1);              // lane J+1: a_{J+1,J+1} - L(J+1, J)^2
+    const double piv = readlane_f64(fma(-m, m, r[J + 1]), J + 1); // lane J+1: a_{J+1,J+1} - L(J+1, J)^2
     __builtin_amdgcn_wave_barrier();
-    if constexpr ((J + 1) & 1) r[J + 1] = fma(-m, B[J][J + 1], r[J + 1]);
+    constexpr int e0 = ((J + 1) & 1) ? J + 2 : J + 1;
+    constexpr int np = (kNB - e0) / 2;
+    double b1 = 0.0;
+    if constexpr ((J + 1) & 1) b1 = B[J][J + 1];
+    double2 b[np > 0 ? np : 1];
 #pragma unroll
-    for (int e = ((J + 1) & 1) ? J + 2 : J + 1; e < kNB; e += 2) {
-      const double2 b = *reinterpret_cast<const double2*>(&B[J][e]);
-      r[e] = fma(-m, b.x, r[e]);
-      r[e + 1] = fma(-m, b.y, r[e + 1]);
+    for (int p = 0; p < np; ++p) b[p] = *reinterpret_cast<const double2*>(&B[J][e0 + 2 * p]);
+    bad |= !(piv > 0.0);
+    rd = rsqrt_newton(piv);
+    if constexpr ((J + 1) & 1) r[J + 1] = fma(-m, b1, r[J + 1]);
+#pragma unroll
+    for (int p = 0; p < np; ++p) {
+      r[e0 + 2 * p] = fma(-m, b[p].x, r[e0 + 2 * p]);
+      r[e0 + 2 * p + 1] = fma(-m, b[p].y, r[e0 + 2 * p + 1]);
     }
-    // the updated row is materialised here: left to itself the compiler sinks each element's
-    // updates to its own step, keeping every earlier multiplier and column value alive
 #pragma unroll
     for (int e = J + 1; e < kNB; ++e) asm volatile("" : "+v"(r[e]));
-    potrf_step<J + 1>(r, piv, bad, B, row, fac);
+    potrf_step<J + 1>(r, rd, bad, B, row, fac);
   }
 }
 
@@ -425,9 +432,10 @@ __device__ __forceinline__ void potrf_tile(const double (*A)[kNB + 1], double (*
     const double a = A[row][e];
     r[e] = fac ? a : (e == row ? 1.0 : 0.0);
   }
-  double piv = readlane_f64(r[0], 0);
-  bool bad = false;
-  potrf_step<0>(r, piv, bad, B, row, fac);
+  const double piv = readlane_f64(r[0], 0);
+  bool bad = !(piv > 0.0);
+  double rd = rsqrt_newton(piv);
+  potrf_step<0>(r, rd, bad, B, row, fac);
   if (bad && lane == 0) atomicOr(status, KVC_DEV_NOT_SPD);
   if (fac) {
 #pragma unroll
