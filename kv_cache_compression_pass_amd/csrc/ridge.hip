@@ -452,6 +452,7 @@ __device__ __forceinline__ void potrf_tile(const double (*A)[kNB + 1], double (*
 typedef double Tile[kNB][kNB + 1];
 __device__ __forceinline__ void mm_abT(const Tile& A, const Tile& B, double (&c)[2][2]) {
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+#pragma unroll 8
   for (int p = 0; p < kNB; ++p) {
     const double a0 = A[2 * ty][p], a1 = A[2 * ty + 1][p], b0 = B[2 * tx][p], b1 = B[2 * tx + 1][p];
     c[0][0] = fma(a0, b0, c[0][0]);
@@ -462,6 +463,7 @@ __device__ __forceinline__ void mm_abT(const Tile& A, const Tile& B, double (&c)
 }
 __device__ __forceinline__ void mm_ab(const Tile& A, const Tile& B, double (&c)[2][2]) {
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+#pragma unroll 8
   for (int p = 0; p < kNB; ++p) {
     const double a0 = A[2 * ty][p], a1 = A[2 * ty + 1][p], b0 = B[p][2 * tx], b1 = B[p][2 * tx + 1];
     c[0][0] = fma(a0, b0, c[0][0]);
@@ -472,6 +474,7 @@ __device__ __forceinline__ void mm_ab(const Tile& A, const Tile& B, double (&c)[
 }
 __device__ __forceinline__ void mm_aTb(const Tile& A, const Tile& B, double (&c)[2][2]) {
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+#pragma unroll 8
   for (int p = 0; p < kNB; ++p) {
     const double a0 = A[p][2 * ty], a1 = A[p][2 * ty + 1], b0 = B[p][2 * tx], b1 = B[p][2 * tx + 1];
     c[0][0] = fma(a0, b0, c[0][0]);
@@ -569,13 +572,17 @@ ridge_chol(double* __restrict__ M, double* __restrict__ Lm, double* __restrict__
   c[1][0] = -tileA[(2 * ty + 1) * np + 2 * tx];
   c[1][1] = -tileA[(2 * ty + 1) * np + 2 * tx + 1];
   tile_load(Xj, Mg + (int64_t)ib * kNB * np + k0, np);            // A_ib,k
-  tile_load(Xk, Mg + (int64_t)jb * kNB * np + k0, np);            // A_jb,k (= A_ib,k on the diagonal)
+  const bool diag = ib == jb;                                     // then X_j = X_i
+  if (!diag) tile_load(Xk, Mg + (int64_t)jb * kNB * np + k0, np); // A_jb,k
   __syncthreads();
-  double xi[2][2], xj[2][2];
+  double xi[2][2];
   zero2(xi);
   mm_abT(Xj, Ls, xi);                                             // X_i = A_ib,k L_kk^-T
-  zero2(xj);
-  mm_abT(Xk, Ls, xj);                                             // X_j (the same on the diagonal)
+  double xj[2][2] = {{xi[0][0], xi[0][1]}, {xi[1][0], xi[1][1]}};
+  if (!diag) {
+    zero2(xj);
+    mm_abT(Xk, Ls, xj);                                           // X_j = A_jb,k L_kk^-T
+  }
   __syncthreads();
   tile_put(Xi, xi);
   tile_put(Xj, xj);
@@ -658,6 +665,98 @@ ridge_back(const double* __restrict__ Lm, const double* __restrict__ Li, const d
   Yt[(2 * ty + 1) * D + 2 * tx + 1] = -c[1][1];
 }
 
+// Backward solve, block rows kb and kb - 1 in one launch (kb >= 1): every block computes X_k =
+// L_kk^-T Y_k (Y_{nb-1} = L^-1 B_{nb-1} at kb = nb - 1), the row above Y_{k-1} - L_k,k-1^T X_k
+// and X_{k-1} = L_{k-1,k-1}^-T of that, the same values in every block; block (ib, cb), ib <
+// kb - 1, then does Y_ib -= L_k,ib^T X_k + L_{k-1},ib^T X_{k-1} (one product chain, so the
+// sums round as two single-row steps would).  Block ib = 0 (the only one when kb = 1) writes
+// both rows of X below n_c to V_c.  Every global read of a block is issued before its first
+// barrier.
+__global__ void __launch_bounds__(256)
+ridge_back2(const double* __restrict__ Lm, const double* __restrict__ Li, const double* __restrict__ Bm,
+            double* __restrict__ Yf, float* __restrict__ v_c, RidgeDims r, int kb) {
+  __shared__ Tile Ls, Ys, Lk1, Y1, Ls1, La, Lb;
+  const int g = blockIdx.y;
+  const int64_t np = r.npad, D = r.d;
+  const int k1 = kb - 1;
+  const int nib = k1 > 0 ? k1 : 1;
+  const int ib = blockIdx.x % nib, cb = blockIdx.x / nib;
+  const int64_t k0 = (int64_t)kb * kNB, j0 = (int64_t)k1 * kNB;
+  const double* Lig = Li + (int64_t)g * r.nb * kNB * kNB;
+  const double* Lg = Lm + (int64_t)g * np * np;
+  double* Yg = Yf + (int64_t)g * np * D;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const bool last = kb == r.nb - 1;
+  tile_load(Ls, Lig + k0 * kNB, kNB);                             // L_kk^-1
+  tile_load(Ys, (last ? Bm + (int64_t)g * np * D : Yg) + k0 * D + (int64_t)cb * kNB, D);   // B_k or Y_k
+  tile_load(Lk1, Lg + k0 * np + j0, np);                          // L_k,k-1
+  tile_load(Y1, Yg + j0 * D + (int64_t)cb * kNB, D);              // Y_{k-1}
+  tile_load(Ls1, Lig + j0 * kNB, kNB);                            // L_{k-1,k-1}^-1
+  double* Yt = Yg + (int64_t)ib * kNB * D + (int64_t)cb * kNB;
+  double yb[2][2] = {{0.0, 0.0}, {0.0, 0.0}};
+  if (k1 > 0) {
+    tile_load(La, Lg + k0 * np + (int64_t)ib * kNB, np);          // L_k,ib
+    tile_load(Lb, Lg + j0 * np + (int64_t)ib * kNB, np);          // L_{k-1},ib
+    yb[0][0] = Yt[(2 * ty) * D + 2 * tx];
+    yb[0][1] = Yt[(2 * ty) * D + 2 * tx + 1];
+    yb[1][0] = Yt[(2 * ty + 1) * D + 2 * tx];
+    yb[1][1] = Yt[(2 * ty + 1) * D + 2 * tx + 1];
+  }
+  __syncthreads();
+  double c[2][2];
+  if (last) {
+    zero2(c);
+    mm_ab(Ls, Ys, c);                                             // Y_k = L_kk^-1 B_k
+    __syncthreads();
+    tile_put(Ys, c);
+    __syncthreads();
+  }
+  double xk[2][2];
+  zero2(xk);
+  mm_aTb(Ls, Ys, xk);                                             // X_k = L_kk^-T Y_k
+  // Y_{k-1} - L_k,k-1^T X_k, as the single-row step forms it: -(L^T X - Y)
+  c[0][0] = -Y1[2 * ty][2 * tx];
+  c[0][1] = -Y1[2 * ty][2 * tx + 1];
+  c[1][0] = -Y1[2 * ty + 1][2 * tx];
+  c[1][1] = -Y1[2 * ty + 1][2 * tx + 1];
+  __syncthreads();
+  tile_put(Ys, xk);                                               // Ys = X_k
+  __syncthreads();
+  mm_aTb(Lk1, Ys, c);
+  c[0][0] = -c[0][0];
+  c[0][1] = -c[0][1];
+  c[1][0] = -c[1][0];
+  c[1][1] = -c[1][1];
+  __syncthreads();
+  tile_put(Y1, c);                                                // Y1 = the updated Y_{k-1}
+  __syncthreads();
+  double xk1[2][2];
+  zero2(xk1);
+  mm_aTb(Ls1, Y1, xk1);                                           // X_{k-1}
+  if (ib == 0) {
+    for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 2; ++j) {
+        const int64_t a = k0 + 2 * ty + i, b = j0 + 2 * ty + i;
+        if (a < r.nc) v_c[((int64_t)g * r.nc + a) * D + (int64_t)cb * kNB + 2 * tx + j] = (float)xk[i][j];
+        if (b < r.nc) v_c[((int64_t)g * r.nc + b) * D + (int64_t)cb * kNB + 2 * tx + j] = (float)xk1[i][j];
+      }
+  }
+  if (k1 == 0) return;
+  __syncthreads();
+  tile_put(Y1, xk1);                                              // Y1 = X_{k-1}
+  __syncthreads();
+  c[0][0] = -yb[0][0];
+  c[0][1] = -yb[0][1];
+  c[1][0] = -yb[1][0];
+  c[1][1] = -yb[1][1];
+  mm_aTb(La, Ys, c);                                              // L_k,ib^T X_k - Y_ib
+  mm_aTb(Lb, Y1, c);                                              //   + L_{k-1},ib^T X_{k-1}
+  Yt[(2 * ty) * D + 2 * tx] = -c[0][0];
+  Yt[(2 * ty) * D + 2 * tx + 1] = -c[0][1];
+  Yt[(2 * ty + 1) * D + 2 * tx] = -c[1][0];
+  Yt[(2 * ty + 1) * D + 2 * tx + 1] = -c[1][1];
+}
+
 __global__ void ridge_reset_status(int32_t* status) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *status = 0;
 }
@@ -703,10 +802,13 @@ hipError_t launch_ridge_fit(const Layer& L, int64_t nc, const uint16_t* q, const
     const unsigned nblk = (unsigned)(rem * (rem + 1) / 2 + rem * ncb);
     ridge_chol<<<dim3(nblk, (unsigned)r.hkv), 256, 0, s>>>(w.M, w.Lm, w.Li, w.Bm, w.Yf, r, kb, status);
   }
-  for (int kb = r.nb - 1; kb >= 0; --kb) {
-    const unsigned nblk = (unsigned)((kb > 0 ? kb : 1) * ncb);
-    ridge_back<<<dim3(nblk, (unsigned)r.hkv), 256, 0, s>>>(w.Lm, w.Li, w.Bm, w.Yf, v_c, r, kb);
+  int kb = r.nb - 1;
+  for (; kb >= 1; kb -= 2) {                                      // block rows kb and kb - 1
+    const unsigned nblk = (unsigned)((kb - 1 > 0 ? kb - 1 : 1) * ncb);
+    ridge_back2<<<dim3(nblk, (unsigned)r.hkv), 256, 0, s>>>(w.Lm, w.Li, w.Bm, w.Yf, v_c, r, kb);
   }
+  if (kb == 0)                                                    // an odd count: row 0 alone
+    ridge_back<<<dim3((unsigned)ncb, (unsigned)r.hkv), 256, 0, s>>>(w.Lm, w.Li, w.Bm, w.Yf, v_c, r, 0);
   return hipGetLastError();
 }
 
