@@ -37,8 +37,10 @@ constexpr int kRows = 32;   // query rows per wave
 
 template <int D>
 struct AttnSmem {
-  uint16_t khi[2][32][D + 8];   // two buffers: group j is decoded into buffer j & 1
-  uint16_t klo[2][32][D + 8];
+  // two buffers: group j is decoded into buffer j & 1.  Rows of D/2 + 2 words: the operand reads
+  // (two 8-byte halves a lane, 32 lanes a pass) start 2 words apart, so every lane has its own banks
+  uint16_t khi[2][32][D + 4];
+  uint16_t klo[2][32][D + 4];
   _Float16 vt[2][D][32 + 4];   // rows of 18 words: the operand reads (8 bytes a lane) hit distinct banks
   int32_t tok[2][32];
   int32_t kinfo[D][4];     // channels in width order: {channel, word offset, param slot, width}
