@@ -24,6 +24,11 @@
 // accumulator: lane l holds keys 8(i/4) + 4(l/32) + i%4, and the V_hat^T operand is read with
 // the same key order, which is a valid ordering of the contraction index.
 // Each block writes (m, l, O) partials per row; a merge kernel combines the splits by LSE.
+// With many query rows, each group would be decoded once per block of 64 rows.  Then a first
+// launch of the same kernel only decodes, one block per key split and head, and writes every
+// group's K_hat hi / lo and V_hat^T to the workspace (192 d bytes a group); the second launch
+// copies those records into its LDS buffers in place of the decode (same values, so the same
+// results), and its loop is left with the products and the softmax.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -34,6 +39,9 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kThreadsA = 64 * kWaves;
 constexpr int kRows = 32;   // query rows per wave
+// attend_split modes: decode each group into LDS and multiply it (one pass); decode only, writing
+// each group's decoded record to the workspace; multiply records decoded by the previous mode
+constexpr int kModeFused = 0, kModeDecodeOut = 1, kModePredecoded = 2;
 
 template <int D>
 struct AttnSmem {
@@ -120,11 +128,11 @@ __device__ __forceinline__ int vscale_exp(uint32_t vb) {
   return e < -100 ? -100 : (e > 110 ? 110 : e);
 }
 
-template <int D>
+template <int D, int MODE>
 __global__ void __launch_bounds__(kThreadsA)
 attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __restrict__ part,
              const uint32_t* __restrict__ vbound, int G, int Hkv, int64_t N, int64_t Nq, int causal, float c,
-             int nsplit, int64_t shift, int pstride, int32_t* status) {
+             int nsplit, int64_t shift, int pstride, int32_t* status, uint16_t* __restrict__ pre) {
   constexpr int KS = D / 16;
   constexpr int GPR = D / 32;
   constexpr int PSTRIDE = D + 2;
@@ -141,7 +149,7 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
   const int split = blockIdx.y;
   const int nRT = (int)((Nq + kRows - 1) / kRows);
   const int pair = blockIdx.x * kWaves + wave;
-  const bool active = pair < G * nRT;
+  const bool active = MODE != kModeDecodeOut && pair < G * nRT;
   const int hl = active ? pair % G : 0;
   const int rt = active ? pair / G : 0;
   const int h = g * G + hl;
@@ -166,7 +174,7 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
 
   // channel table of this head's K packing: one uint64 per channel packs {words (16 bits),
   // params (16 bits), an 8-bit count per width class}; one block scan places every channel
-  {
+  if constexpr (MODE != kModePredecoded) {
     uint32_t b = 0;
     int cls = 4;
     uint64_t f = 0;
@@ -200,7 +208,7 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
 
   // Q^T operand of this wave's rows
   bf16x8 qb[KS];
-  {
+  if constexpr (MODE != kModeDecodeOut) {
     const int64_t row = r0 + lo;
     const bool ok = active && row < Nq;
     const uint16_t* qp = q + ((int64_t)h * Nq + (ok ? row : 0)) * D;
@@ -217,6 +225,7 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
     int64_t lr = (int64_t)(last_pair / G) * kRows + kRows - 1;
     if (lr >= Nq) lr = Nq - 1;
     pmax_block = causal ? off + lr : N - 1;
+    if (MODE == kModeDecodeOut) pmax_block = causal ? off + Nq - 1 : N - 1;
   }
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -294,6 +303,43 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
     return (threadIdx.x < 32 && e < m_valid_of(j)) ? cache.k_keep[slot0 + j * 32 + e] : 0x7FFFFFFF;
   };
 
+  // A group's decoded record in `pre` (written by the decode-only mode, read by the predecoded
+  // mode): K_hat hi [32][D] and lo [32][D] (bf16 bits), then V_hat^T [D][32] (fp16 bits of the
+  // scaled values), 192 D bytes.  Thread t moves the t-th chunk of D / 8 bytes of each array.
+  using Chunk = typename std::conditional<D == 128, uint4, uint2>::type;
+  const int64_t ngmax = (N + 31) / 32;
+  auto rec_ptr = [&](int64_t j, int u) -> Chunk* {
+    return reinterpret_cast<Chunk*>(pre + ((int64_t)g * ngmax + j) * (3 * 32 * D) + (int64_t)u * 32 * D) +
+           threadIdx.x;
+  };
+  auto lds_chunk = [&](int u, int bf) -> uint2* {   // rows are 8-byte aligned: 8-byte accesses
+    const int t = threadIdx.x;
+    if (u < 2) {
+      const int row = t >> 4, col = (t & 15) * (D / 16);
+      return reinterpret_cast<uint2*>(u == 0 ? &sm.khi[bf][row][col] : &sm.klo[bf][row][col]);
+    }
+    constexpr int CPR = kThreadsA / D;          // chunks per V_hat^T row of 32 tokens
+    return reinterpret_cast<uint2*>(&sm.vt[bf][t / CPR][(t % CPR) * (D / 16)]);
+  };
+  auto put_chunk = [&](const Chunk& v, int u, int bf) {
+    uint2* d = lds_chunk(u, bf);
+    if constexpr (D == 128) {
+      d[0] = make_uint2(v.x, v.y);
+      d[1] = make_uint2(v.z, v.w);
+    } else {
+      d[0] = v;
+    }
+  };
+  auto get_chunk = [&](int u, int bf) -> Chunk {
+    const uint2* d = lds_chunk(u, bf);
+    if constexpr (D == 128) {
+      const uint2 a = d[0], b = d[1];
+      return make_uint4(a.x, a.y, b.x, b.y);
+    } else {
+      return d[0];
+    }
+  };
+
   // Decode of one group from its raw words into LDS buffer `bf`, without branches (every lane
   // runs the same instructions, so the products of the previous group can interleave).
   auto decode_k = [&](const uint32_t (&w)[4], int bf) {
@@ -342,7 +388,20 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
   // then moves set 2 into set 1.
   uint32_t kw1[4] = {0u, 0u, 0u, 0u}, vw1[2][4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
   int32_t vl1[2] = {-1, -1}, vl2[2] = {-1, -1}, tok1 = 0x7FFFFFFF, tf0 = 0, tf1 = 0;
-  if (j_begin < j_end_raw) {
+  Chunk ch1[3] = {};                           // the predecoded mode's set 1
+  if (MODE == kModePredecoded && j_begin < j_end_raw) {
+    const int32_t tok0 = load_tok(j_begin);
+    tf0 = cache.k_keep[slot0 + j_begin * 32];
+#pragma unroll
+    for (int u = 0; u < 3; ++u) put_chunk(*rec_ptr(j_begin, u), u, (int)(j_begin & 1));
+    if (threadIdx.x < 32) sm.tok[j_begin & 1][threadIdx.x] = tok0;
+    if (j_begin + 1 < j_end_raw) {
+      tok1 = load_tok(j_begin + 1);
+      tf1 = cache.k_keep[slot0 + (j_begin + 1) * 32];
+#pragma unroll
+      for (int u = 0; u < 3; ++u) ch1[u] = *rec_ptr(j_begin + 1, u);
+    }
+  } else if (j_begin < j_end_raw) {
     uint32_t kw0[4], vw0[2][4];
     int32_t vl0[2];
     load_vloc(j_begin, vl0);
@@ -374,13 +433,19 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
     // ---- requests for group j + 2 (set 2), in flight while group j is multiplied
     uint32_t kw2[4] = {0u, 0u, 0u, 0u}, vw2[2][4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
     int32_t vl3[2] = {-1, -1}, tok2 = 0x7FFFFFFF, tf2 = 0;
+    Chunk ch2[3] = {};
     if (j + 2 < j_end_raw) {
-      load_k(j + 2, kw2);
       tok2 = load_tok(j + 2);
       tf2 = cache.k_keep[slot0 + (j + 2) * 32];
-      load_v(vl2[0], vw2[0]);
-      load_v(vl2[1], vw2[1]);
-      load_vloc(j + 3, vl3);
+      if constexpr (MODE == kModePredecoded) {
+#pragma unroll
+        for (int u = 0; u < 3; ++u) ch2[u] = *rec_ptr(j + 2, u);
+      } else {
+        load_k(j + 2, kw2);
+        load_v(vl2[0], vw2[0]);
+        load_v(vl2[1], vw2[1]);
+        load_vloc(j + 3, vl3);
+      }
     }
     // Group j+1 is decoded unconditionally (past the split's end the words are zeros and the
     // buffer is not read again), so the decode has no branch to keep it apart from the products.
@@ -388,7 +453,12 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
     // Every wave multiplies every group, so the decode sits in the same straight-line code as
     // the products: an inactive wave has zero queries and writes nothing, and a group that
     // lies past all of a wave's rows is masked to -inf, which leaves (m, l, O) unchanged.
-    {
+    if constexpr (MODE == kModeDecodeOut) {
+#pragma unroll
+      for (int u = 0; u < 3; ++u) *rec_ptr(j, u) = get_chunk(u, buf);
+      decode_k(kw1, nbuf);
+      decode_v(vw1, vl1, nbuf);
+    } else {
       f32x16 acc, acc_lo;                      // q.hi and q.lo in two chains, added at the end
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] = acc_lo[i] = 0.f;
@@ -399,13 +469,15 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
         acc = mfma32(ah, qb[ks], acc);
         acc_lo = mfma32(al, qb[ks], acc_lo);
       }
-      decode_k(kw1, nbuf);                     // VALU work beside the matrix products
-      // issue order: each product of the two chains followed by a share of the decode
+      if constexpr (MODE == kModeFused) {
+        decode_k(kw1, nbuf);                   // VALU work beside the matrix products
+        // issue order: each product of the two chains followed by a share of the decode
 #pragma unroll
-      for (int i = 0; i < 2 * KS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read (K operand)
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // matrix product
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU (decode)
+        for (int i = 0; i < 2 * KS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read (K operand)
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // matrix product
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU (decode)
+        }
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] += acc_lo[i];
@@ -461,12 +533,17 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
           o[mb] = mfma32h(va, pb, o[mb]);
         }
       }
-      decode_v(vw1, vl1, nbuf);
+      if constexpr (MODE == kModeFused) {
+        decode_v(vw1, vl1, nbuf);
 #pragma unroll
-      for (int i = 0; i < 2 * GPR; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read (V operand)
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // matrix product
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU (decode)
+        for (int i = 0; i < 2 * GPR; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read (V operand)
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // matrix product
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU (decode)
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 3; ++u) put_chunk(ch1[u], u, nbuf);   // group j+1, decoded once before
       }
     }
     if (threadIdx.x < 32) sm.tok[nbuf][threadIdx.x] = tok1;
@@ -482,6 +559,8 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
       vl1[u] = vl2[u];
       vl2[u] = vl3[u];
     }
+#pragma unroll
+    for (int u = 0; u < 3; ++u) ch1[u] = ch2[u];
     tok1 = tok2;
     tf0 = tf1;
     tf1 = tf2;
@@ -677,6 +756,25 @@ int nsplit_of(const Layer& L) {
   return (int)want;
 }
 
+// The decoded records pay off once several row blocks would each decode every group of a head.
+constexpr int kPredecodeRowBlocks = 4;
+bool use_predecode(const Layer& L) {
+  const int nRT = (int)((L.nq + kRows - 1) / kRows);
+  return (L.G * nRT + kWaves - 1) / kWaves >= kPredecodeRowBlocks;
+}
+size_t predecode_bytes(const Layer& L) {
+  return (size_t)L.hkv * (size_t)((L.n + 31) / 32) * 3 * 32 * (size_t)L.d * sizeof(uint16_t);
+}
+// Blocks per head of the decode-only pass: about 1024 in all, at least 8 groups each.
+int predecode_nsplit(const Layer& L) {
+  int64_t want = (1024 + L.hkv - 1) / L.hkv;
+  const int64_t maxs = (L.n + 32 * 8 - 1) / (32 * 8);
+  if (want > maxs) want = maxs;
+  if (want < 1) want = 1;
+  if (want > 65535) want = 65535;
+  return (int)want;
+}
+
 }  // namespace
 
 size_t attend_ws_bytes(const Layer& L) {
@@ -684,8 +782,12 @@ size_t attend_ws_bytes(const Layer& L) {
   const bool dec = use_decode(L);
   const int nsplit = dec ? decode_nsplit(L) : nsplit_of(L);
   p.take((size_t)L.hq * L.nq * (nsplit + 1) * (L.d + 2) * sizeof(float));   // + the append buffer's split
-  if (!dec) p.take((size_t)L.hkv * sizeof(uint32_t));             // |V_hat| bound per head
-  else p.take(decode_ws_bytes(L));
+  if (!dec) {
+    p.take((size_t)L.hkv * sizeof(uint32_t));                     // |V_hat| bound per head
+    if (use_predecode(L)) p.take(predecode_bytes(L));            // decoded records
+  } else {
+    p.take(decode_ws_bytes(L));
+  }
   return p.off;
 }
 
@@ -713,12 +815,30 @@ hipError_t launch_attend(const Layer& L, const uint16_t* q, const kvc_packed_cac
       attend_vbound<64><<<gb, 256, 0, s>>>(cache, vb, L.hkv, L.n);
     const int nRT = (int)((L.nq + kRows - 1) / kRows);
     dim3 grid((unsigned)((L.G * nRT + kWaves - 1) / kWaves), (unsigned)nsplit, (unsigned)L.hkv);
-    if (L.d == 128)
-      attend_split<128><<<grid, kThreadsA, 0, s>>>(q, cache, part, vb, L.G, L.hkv, L.n, L.nq, L.causal, L.c_log2,
-                                                   nsplit, n_new, pstride, status);
-    else
-      attend_split<64><<<grid, kThreadsA, 0, s>>>(q, cache, part, vb, L.G, L.hkv, L.n, L.nq, L.causal, L.c_log2,
-                                                  nsplit, n_new, pstride, status);
+    if (use_predecode(L)) {
+      uint16_t* pre = reinterpret_cast<uint16_t*>(ws + p.take(predecode_bytes(L)));
+      const int ns1 = predecode_nsplit(L);
+      const dim3 g1(1, (unsigned)ns1, (unsigned)L.hkv);
+      if (L.d == 128) {
+        attend_split<128, kModeDecodeOut><<<g1, kThreadsA, 0, s>>>(q, cache, part, vb, L.G, L.hkv, L.n, L.nq,
+                                                                   L.causal, L.c_log2, ns1, n_new, pstride, status, pre);
+        attend_split<128, kModePredecoded><<<grid, kThreadsA, 0, s>>>(q, cache, part, vb, L.G, L.hkv, L.n, L.nq,
+                                                                      L.causal, L.c_log2, nsplit, n_new, pstride,
+                                                                      status, pre);
+      } else {
+        attend_split<64, kModeDecodeOut><<<g1, kThreadsA, 0, s>>>(q, cache, part, vb, L.G, L.hkv, L.n, L.nq,
+                                                                  L.causal, L.c_log2, ns1, n_new, pstride, status, pre);
+        attend_split<64, kModePredecoded><<<grid, kThreadsA, 0, s>>>(q, cache, part, vb, L.G, L.hkv, L.n, L.nq,
+                                                                     L.causal, L.c_log2, nsplit, n_new, pstride,
+                                                                     status, pre);
+      }
+    } else if (L.d == 128) {
+      attend_split<128, kModeFused><<<grid, kThreadsA, 0, s>>>(q, cache, part, vb, L.G, L.hkv, L.n, L.nq, L.causal,
+                                                               L.c_log2, nsplit, n_new, pstride, status, nullptr);
+    } else {
+      attend_split<64, kModeFused><<<grid, kThreadsA, 0, s>>>(q, cache, part, vb, L.G, L.hkv, L.n, L.nq, L.causal,
+                                                              L.c_log2, nsplit, n_new, pstride, status, nullptr);
+    }
   }
   if (n_new > 0) {
     const unsigned nb = (unsigned)(((int64_t)L.hq * L.nq + 3) / 4);
