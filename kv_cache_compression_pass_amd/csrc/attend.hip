@@ -145,10 +145,20 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int hi = lane >> 5, lo = lane & 31;
-  const int g = blockIdx.z;
-  const int split = blockIdx.y;
   const int nRT = (int)((Nq + kRows - 1) / kRows);
-  const int pair = blockIdx.x * kWaves + wave;
+  int rb = blockIdx.x, split = blockIdx.y, g = blockIdx.z;
+  if constexpr (MODE == kModePredecoded) {
+    // One-dimensional grid.  Blocks are dealt to the eight XCDs in turn, so the row blocks of one
+    // (split, head), which read the same records, are given ids eight apart: one XCD, one L2.
+    const int nrb = (G * nRT + kWaves - 1) / kWaves;
+    const int id = blockIdx.x, chunk = id / (8 * nrb), rem = id % (8 * nrb);
+    const int u = chunk * 8 + rem % 8;
+    if (u >= nsplit * Hkv) return;             // padding of the last eight (split, head) units
+    rb = rem / 8;
+    split = u % nsplit;
+    g = u / nsplit;
+  }
+  const int pair = rb * kWaves + wave;
   const bool active = MODE != kModeDecodeOut && pair < G * nRT;
   const int hl = active ? pair % G : 0;
   const int rt = active ? pair / G : 0;
@@ -158,7 +168,7 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
 
   const int64_t* H = cache.header;
   if (H[0] != Hkv || H[1] != D || H[2] != N) {
-    if (threadIdx.x == 0 && blockIdx.x == 0 && split == 0) set_status(status, KVC_DEV_BAD_CACHE);
+    if (threadIdx.x == 0 && rb == 0 && split == 0) set_status(status, KVC_DEV_BAD_CACHE);
     return;
   }
   const int64_t* hp = H + KVC_HDR_GLOBAL + g * KVC_HDR_PER_HEAD;
@@ -220,7 +230,7 @@ attend_split(const uint16_t* __restrict__ q, kvc_packed_cache cache, float* __re
   // last position among the block's active rows (rows of later pairs are later or equal)
   int64_t pmax_block;
   {
-    int last_pair = blockIdx.x * kWaves + kWaves - 1;
+    int last_pair = rb * kWaves + kWaves - 1;
     if (last_pair >= G * nRT) last_pair = G * nRT - 1;
     int64_t lr = (int64_t)(last_pair / G) * kRows + kRows - 1;
     if (lr >= Nq) lr = Nq - 1;
@@ -819,16 +829,18 @@ hipError_t launch_attend(const Layer& L, const uint16_t* q, const kvc_packed_cac
       uint16_t* pre = reinterpret_cast<uint16_t*>(ws + p.take(predecode_bytes(L)));
       const int ns1 = predecode_nsplit(L);
       const dim3 g1(1, (unsigned)ns1, (unsigned)L.hkv);
+      const int64_t units = (int64_t)nsplit * L.hkv;
+      const dim3 g2((unsigned)((units + 7) / 8 * 8 * grid.x));
       if (L.d == 128) {
         attend_split<128, kModeDecodeOut><<<g1, kThreadsA, 0, s>>>(q, cache, part, vb, L.G, L.hkv, L.n, L.nq,
                                                                    L.causal, L.c_log2, ns1, n_new, pstride, status, pre);
-        attend_split<128, kModePredecoded><<<grid, kThreadsA, 0, s>>>(q, cache, part, vb, L.G, L.hkv, L.n, L.nq,
+        attend_split<128, kModePredecoded><<<g2, kThreadsA, 0, s>>>(q, cache, part, vb, L.G, L.hkv, L.n, L.nq,
                                                                       L.causal, L.c_log2, nsplit, n_new, pstride,
                                                                       status, pre);
       } else {
         attend_split<64, kModeDecodeOut><<<g1, kThreadsA, 0, s>>>(q, cache, part, vb, L.G, L.hkv, L.n, L.nq,
                                                                   L.causal, L.c_log2, ns1, n_new, pstride, status, pre);
-        attend_split<64, kModePredecoded><<<grid, kThreadsA, 0, s>>>(q, cache, part, vb, L.G, L.hkv, L.n, L.nq,
+        attend_split<64, kModePredecoded><<<g2, kThreadsA, 0, s>>>(q, cache, part, vb, L.G, L.hkv, L.n, L.nq,
                                                                      L.causal, L.c_log2, nsplit, n_new, pstride,
                                                                      status, pre);
       }
