@@ -278,7 +278,9 @@ kvc_status kvc_quantize_pack(const kvc_layer_desc* desc, const void* k, const vo
  * the head's largest round to that absolute step).  With at most 16 rows (decode) the codes and
  * raw bf16 values enter exactly, q * scale and p * scale_v as bf16 hi + lo pairs (2^-17
  * relative), zero terms exactly or in float32, all accumulated in float32.  Workspace: the
- * decode path also holds every retained token's logits (4 * H_kv * N * 16 bytes at most). */
+ * decode path also holds every retained token's logits (4 * H_kv * N * 16 bytes at most); with
+ * G * ceil(Nq / 32) > 24 query row tiles per KV head every group of 32 retained tokens is decoded
+ * once into the workspace (192 * d bytes for each of the H_kv * ceil(N / 32) possible groups). */
 kvc_status kvc_compressed_attend(const kvc_layer_desc* desc, const void* q,
                                  const kvc_packed_cache* cache, float* out, float* lse,
                                  void* ws, size_t ws_bytes, void* hip_stream);
