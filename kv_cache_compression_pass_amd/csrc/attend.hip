@@ -758,7 +758,7 @@ bool use_decode(const Layer& L) {
 int nsplit_of(const Layer& L) {
   const int nRT = (int)((L.nq + kRows - 1) / kRows);
   const int64_t bps = (int64_t)L.hkv * ((L.G * nRT + kWaves - 1) / kWaves);   // blocks per split
-  int64_t want = (1024 + bps - 1) / bps;
+  int64_t want = (768 + bps - 1) / bps;                  // about 768 blocks (1024 was 2-10 % slower)
   const int64_t maxs = (L.n + 32 * 8 - 1) / (32 * 8);   // at least 8 groups per split
   if (want > maxs) want = maxs;
   if (want < 1) want = 1;
