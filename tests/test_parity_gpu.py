@@ -766,6 +766,9 @@ ALLROW_CASES = [
     ("allrows_causal_d128", 8, 2, 128, 777, 777, True),
     ("allrows_causal_d64", 4, 1, 64, 1000, 1000, True),
     ("rows_noncausal_d128", 4, 2, 128, 650, 97, False),
+    # more than 24 row tiles per KV head (decoded-record launches), future rows that see every
+    # key, and a grid of 6 (split, head) units padded to 8
+    ("rows_noncausal_many_d128", 8, 2, 128, 700, 300, False),
 ]
 
 
@@ -775,7 +778,8 @@ def test_attend_every_row_mixed_widths(case):
     """The matrix-core attend on every query row of a causal layer (row blocks whose last row
     comes before a key split's groups stop early, and splits of one or a few groups), with each
     token's V width and each channel's K width drawn independently from {0, 2, 4, 8, 16}, so
-    the lanes of one wave decode different widths side by side."""
+    the lanes of one wave decode different widths side by side.  The layers with more than 24
+    row tiles per KV head take the decode-once launches, the others the one-pass kernel."""
     name, hq, hkv, d, N, Nq, causal = case
     print(f"case {name}", flush=True)
     x = make_inputs(hq, hkv, d, N, Nq, seed=zlib.crc32(name.encode()) % 1000)
