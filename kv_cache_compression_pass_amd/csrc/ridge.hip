@@ -15,8 +15,10 @@
 //                  L_ik L_jk^T, and the tile (kb+1, kb+1) then factors itself and inverts its L
 //                  (look-ahead); in the same launch the forward solve moves one block: Y_k =
 //                  L_kk^-1 B_k, and B_i -= L_ik Y_k for every i > k
-//   ridge_back     the backward solve, one launch per block row k from the last: X_k =
-//                  L_kk^-T Y_k, Y_i -= L_ki^T X_k for every i < k; X_k is V_c's rows
+//   ridge_back2    the backward solve, one launch per pair of block rows from the last: X_k =
+//                  L_kk^-T Y_k, then the row above and its X_{k-1}, then Y_i -= L_ki^T X_k +
+//                  L_{k-1},i^T X_{k-1} for every i < k - 1; the X rows are V_c's rows
+//                  (ridge_back takes a lone row 0 when the number of block rows is odd)
 // Every sum has a fixed order, so results are deterministic.  The matrix is padded to a
 // multiple of 64 with an identity block, which leaves the solution unchanged.
 #include "common.hpp"
