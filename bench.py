@@ -182,6 +182,30 @@ def ridge_figure(args, stream, dev):
             "status": kvc.kvc_get_device_status(ws)}
 
 
+def copy_rate(stream, dev, mib=512, reps=10):
+    """The streaming rate this GPU sustains in the same run: a plain device copy of MIB MiB
+    (reads MIB, writes MIB), median of REPS launches.  Context for the pack's HBM figure: the
+    published 8 TB/s is a peak that no streaming kernel reaches."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    ts.sort()
+    ms = ts[len(ts) // 2]
+    del src, dst
+    return 2.0 * 4 * n / (ms * 1e-3) / 1e9
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -412,9 +436,12 @@ def main():
 
     pb = pack_algorithmic_bytes(hdr, bk.cpu().numpy(), d)
     pack_ms = float(np.mean(per_call["quantize_pack"]))
+    pack_gbs = (pb["k"] + pb["v"]) / (pack_ms * 1e-3) / 1e9
+    copy_gbs = copy_rate(stream, dev)
     pack = {"ms": round(pack_ms, 5), "bytes_k": pb["k"], "bytes_v": pb["v"],
-            "gbs": round((pb["k"] + pb["v"]) / (pack_ms * 1e-3) / 1e9, 1),
-            "hbm_frac": round((pb["k"] + pb["v"]) / (pack_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            "gbs": round(pack_gbs, 1),
+            "hbm_frac": round(pack_gbs / PEAK_HBM_GBS, 4),
+            "copy_gbs": round(copy_gbs, 1), "frac_of_copy": round(pack_gbs / copy_gbs, 4)}
 
     out = {
         "metric": METRIC,

@@ -302,9 +302,10 @@ pack_place(const uint8_t* __restrict__ bits_v, const uint8_t* __restrict__ bits_
 //  * a value whose fp32 v lies within 2^(b-21) of a half-integer (over 2.6 times the error
 //    bound 3 * 2^-24 * v for v < 2^b) is decided again with the defining fp64 division,
 //    reading the value back through src.fetch().  The codes equal those of that definition.
+// quantize_ct is the same quantiser at a compile-time width (the V blocks, whose width is uniform).
 // Src provides elem(e) (value e as float), refresh() (makes the held registers opaque, so
 // that a later pass unpacks them afresh instead of keeping every unpacked value alive) and
-// fetch(e) (value e read back from memory).
+// fetch(e) (value e again for the fp64 decision, from memory or from the lane's registers).
 __device__ __forceinline__ float min3_raw(float a, float b, float c) {
   float r;
   asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
@@ -322,11 +323,20 @@ __device__ __forceinline__ uint32_t crumbs_of(uint32_t w) {
   return (t | (t >> 12)) & 0xFFu;
 }
 
+// Near-boundary flags of a group, one bit per value in value order: flags = 2 * flags + (|t| > lim),
+// one compare and one add-with-carry per value (value e of 32 ends at bit 31 - e).
+__device__ __forceinline__ uint32_t shift_in_flag(uint32_t flags, float t, float lim) {
+  asm("v_cmp_gt_f32_e64 vcc, |%1|, %2\n\tv_addc_co_u32_e32 %0, vcc, %0, %0, vcc"
+      : "+v"(flags) : "v"(t), "v"(lim) : "vcc");
+  return flags;
+}
+
+// min and max of the first m_own of a lane's 32 values (all 32 when FULL)
 template <bool FULL, class Src>
-__device__ __forceinline__ void quantize_rt(Src& src, int m_own, int b, uint32_t* __restrict__ dst,
-                                            float* __restrict__ par) {
+__device__ __forceinline__ void group_min_max(const Src& src, int m_own, float& mn, float& mx) {
   constexpr int NE = 32;
-  float mn = src.elem(0), mx = mn;
+  mn = src.elem(0);
+  mx = mn;
 #pragma unroll
   for (int e = 1; e < NE - 1; e += 2) {
     const float a = (FULL || e < m_own) ? src.elem(e) : mn;
@@ -336,12 +346,18 @@ __device__ __forceinline__ void quantize_rt(Src& src, int m_own, int b, uint32_t
     mn = min3_raw(mn, a, c);
     mx = max3_raw(mx, a2, c2);
   }
-  {
-    const float a = (FULL || NE - 1 < m_own) ? src.elem(NE - 1) : mn;
-    const float a2 = (FULL || NE - 1 < m_own) ? a : mx;
-    mn = min3_raw(mn, a, a);
-    mx = max3_raw(mx, a2, a2);
-  }
+  const float a = (FULL || NE - 1 < m_own) ? src.elem(NE - 1) : mn;
+  const float a2 = (FULL || NE - 1 < m_own) ? a : mx;
+  mn = min3_raw(mn, a, a);
+  mx = max3_raw(mx, a2, a2);
+}
+
+template <bool FULL, class Src>
+__device__ __forceinline__ void quantize_rt(Src& src, int m_own, int b, uint32_t* __restrict__ dst,
+                                            float* __restrict__ par) {
+  constexpr int NE = 32;
+  float mn, mx;
+  group_min_max<FULL>(src, m_own, mn, mx);
   const int maxi = (1 << b) - 1;
   const float s = (float)(((double)mx - (double)mn) / (double)maxi);
   const float lim = 0.5f - __uint_as_float((uint32_t)(b - 21 + 127) << 23);   // 1/2 - 2^(b-21)
@@ -354,21 +370,22 @@ __device__ __forceinline__ void quantize_rt(Src& src, int m_own, int b, uint32_t
     const float rs = 1.0f / s;
     const bool fin = __builtin_isfinite(rs);
     const float rsf = fin ? rs : 0.f;
-    uint32_t near = fin ? 0u : 0xFFFFFFFFu;        // an infinite 1/s sends every value to fp64
+    uint32_t near = 0u;
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
       const float v = (src.elem(e) - mn) * rsf;
       const float r = rintf(v);
-      if (FULL || e < m_own) near |= (fabsf(v - r) > lim) ? (1u << e) : 0u;
+      near = shift_in_flag(near, v - r, lim);
       const float code = (FULL || e < m_own) ? r : 0.f;
       w8[e >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(code, e & 3, w8[e >> 2]);
     }
-    if (!FULL) near &= (m_own >= 32) ? 0xFFFFFFFFu : ((1u << m_own) - 1u);
+    if (!fin) near = 0xFFFFFFFFu;                  // an infinite 1/s sends every value to fp64
+    if (!FULL) near &= (m_own >= 32) ? 0xFFFFFFFFu : ~(0xFFFFFFFFu >> m_own);   // values e < m_own
     // values near a rounding boundary (rare): decide them with the defining fp64 division
     const double sd = (double)s;
     while (near != 0u) {
-      const int e = __builtin_ctz(near);
-      near &= near - 1u;
+      const int e = __builtin_clz(near);
+      near &= ~(0x80000000u >> e);
       const double vd = rint(((double)src.fetch(e) - (double)mn) / sd);
       const float code = (float)(vd < 0.0 ? 0.0 : (vd > (double)maxi ? (double)maxi : vd));
 #pragma unroll
@@ -395,6 +412,68 @@ __device__ __forceinline__ void quantize_rt(Src& src, int m_own, int b, uint32_t
   *reinterpret_cast<float2*>(par) = make_float2(s, mn);
 }
 
+// The same quantiser at a width B in {2, 4, 8} fixed at compile time, for a lane's 32 values
+// (all valid).  At 2 and 4 bits the codes of a 16-bit half word are gathered as an exact fp32
+// sum  sum_j code_j * 2^(B j)  (integers below 2^16, so every fma is exact) and converted once;
+// at 8 bits each code goes to its byte directly.
+template <int B, class Src>
+__device__ __forceinline__ void quantize_ct(Src& src, uint32_t* __restrict__ dst, float* __restrict__ par) {
+  constexpr int NE = 32, NW = B;                   // B code words per group
+  constexpr int maxi = (1 << B) - 1;
+  constexpr int PER = 16 / B;                      // codes per 16-bit half word (B < 8)
+  float mn, mx;
+  group_min_max<true>(src, NE, mn, mx);
+  const float s = (float)(((double)mx - (double)mn) / (double)maxi);
+  const float lim = 0.5f - __uint_as_float((uint32_t)(B - 21 + 127) << 23);   // 1/2 - 2^(B-21)
+  uint32_t wd[NW];
+#pragma unroll
+  for (int i = 0; i < NW; ++i) wd[i] = 0u;
+  if (s != 0.f) {
+    src.refresh();
+    const float rs = 1.0f / s;
+    const bool fin = __builtin_isfinite(rs);
+    const float rsf = fin ? rs : 0.f;
+    uint32_t near = 0u;
+    if constexpr (B == 8) {
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const float v = (src.elem(e) - mn) * rsf;
+        const float r = rintf(v);
+        near = shift_in_flag(near, v - r, lim);
+        wd[e >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(r, e & 3, wd[e >> 2]);
+      }
+    } else {
+      float acc[NE / PER];
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const float v = (src.elem(e) - mn) * rsf;
+        const float r = rintf(v);
+        near = shift_in_flag(near, v - r, lim);
+        const int a = e / PER, j = e % PER;
+        acc[a] = j == 0 ? r : __builtin_fmaf(r, (float)(1u << (B * j)), acc[a]);
+      }
+#pragma unroll
+      for (int i = 0; i < NW; ++i) wd[i] = (uint32_t)acc[2 * i] | ((uint32_t)acc[2 * i + 1] << 16);
+    }
+    if (!fin) near = 0xFFFFFFFFu;                  // an infinite 1/s sends every value to fp64
+    // values near a rounding boundary (rare): decide them with the defining fp64 division
+    const double sd = (double)s;
+    while (near != 0u) {
+      const int e = __builtin_clz(near);
+      near &= ~(0x80000000u >> e);
+      const double vd = rint(((double)src.fetch(e) - (double)mn) / sd);
+      const uint32_t code = (uint32_t)(vd < 0.0 ? 0.0 : (vd > (double)maxi ? (double)maxi : vd));
+      const int sh = (e * B) & 31;
+#pragma unroll
+      for (int i = 0; i < NW; ++i)
+        if (i == ((e * B) >> 5)) wd[i] = (wd[i] & ~((uint32_t)maxi << sh)) | (code << sh);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NW; ++i) dst[i] = wd[i];
+  *reinterpret_cast<float2*>(par) = make_float2(s, mn);
+}
+
 // A lane's 32 values of one group as 16 packed bf16 pairs (element 2i in the low half of
 // w[i]); Fetch reads value e back from memory.
 template <class Fetch>
@@ -409,6 +488,26 @@ struct PairSrc {
     for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(w[i]));
   }
   __device__ __forceinline__ float fetch(int e) const { return fetch_fn(e); }
+};
+
+// The same 32 values, read back for the fp64 decision from the lane's own registers (a select
+// over the 16 words) instead of from memory: a K wave meets several such values per group, and
+// a dependent global load for each cost more than the select.
+struct RegPairSrc {
+  uint32_t w[16];
+  __device__ __forceinline__ float elem(int e) const {
+    return (e & 1) ? __uint_as_float(w[e >> 1] & 0xFFFF0000u) : __uint_as_float(w[e >> 1] << 16);
+  }
+  __device__ __forceinline__ void refresh() {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(w[i]));
+  }
+  __device__ __forceinline__ float fetch(int e) const {
+    uint32_t x = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x = (i == (e >> 1)) ? w[i] : x;
+    return (e & 1) ? __uint_as_float(x & 0xFFFF0000u) : __uint_as_float(x << 16);
+  }
 };
 
 // K: one wave per (group j of 32 retained tokens, head g).  Lane l < D/2 holds channels 2l and
@@ -432,8 +531,7 @@ __device__ __forceinline__ void pack_k_group(const uint16_t* __restrict__ k, int
     const int4 info = *reinterpret_cast<const int4*>(kchc + ((int64_t)g * D + c) * 4);
     const int b = info.z;
     uint32_t* dst = k_words + hp[18] + j * hp[20] + info.x;
-    auto fetch = [&](int e) { return __uint_as_float((uint32_t)kh[(int64_t)tk[e] * D + c] << 16); };
-    PairSrc<decltype(fetch)> src{{}, fetch};
+    RegPairSrc src{{}};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const uint32_t lo = ld[2 * i], hi = ld[2 * i + 1];
@@ -503,7 +601,9 @@ __device__ __forceinline__ void pack_v_slab(const uint16_t* __restrict__ v, int6
     return;
   }
   float* par = v_par + 2 * (hp[13 + z] + pos * GPR + grp);
-  quantize_rt<true>(src, 32, b, dst, par);
+  if (z == 0) quantize_ct<2>(src, dst, par);       // the width is uniform over the block
+  else if (z == 1) quantize_ct<4>(src, dst, par);
+  else quantize_ct<8>(src, dst, par);
 }
 
 template <int D>
