@@ -588,6 +588,29 @@ __device__ __forceinline__ bool may_carry(float c, int64_t s, uint64_t pre, int 
   return any;
 }
 
+// The values a thread's UPT units are decided by, all requested before any is used: the cost
+// c_u = float32(w_u * sigma_u) (V/K stages; the same product as everywhere else, so the same bits)
+// or the score (top-k).  Unit j is ubase + j * ustep of the segment at woff; units past seg_len
+// read the segment's last unit (always in bounds) and are never used.  A loop that loaded each
+// unit where it is needed waited one memory round trip per unit.
+template <int UPT>
+__device__ __forceinline__ void load_costs(const float* __restrict__ weight, const float* __restrict__ sigma,
+                                           int64_t woff, int64_t ubase, int64_t ustep, int64_t seg_len,
+                                           float (&cw)[UPT]) {
+  float sg[UPT];
+#pragma unroll
+  for (int j = 0; j < UPT; ++j) {
+    const int64_t u = ubase + j * ustep;
+    const int64_t uc = u < seg_len ? u : seg_len - 1;
+    cw[j] = weight[woff + uc];
+    sg[j] = sigma ? sigma[uc] : 1.0f;
+  }
+  if (sigma) {
+#pragma unroll
+    for (int j = 0; j < UPT; ++j) cw[j] = cw[j] * sg[j];
+  }
+}
+
 // Histogram of one pass over the keys of the current prefix set.  V/K: the 4 step keys of each
 // unit, weight = step rate.  Top-k: 32-bit score keys, 1 per token, weight 1, one segment per KV
 // head.  The set's smallest and largest keys go out once per block.
@@ -609,12 +632,15 @@ alloc_hist(AllocWs a, const float* __restrict__ weight, const float* __restrict_
   const uint64_t pre = s.prefix & dg.himask;
   const uint64_t dmask = (1ull << (dg.hi - dg.lo)) - 1;
   const int64_t base = (int64_t)blockIdx.x * (NT * UPT);
+  float cw[UPT];
+  load_costs<UPT>(weight, TOPK ? nullptr : sigma, TOPK ? (int64_t)seg * seg_len : 0, base + threadIdx.x, NT,
+                  seg_len, cw);
 #pragma unroll
   for (int j = 0; j < UPT; ++j) {
     const int64_t ul = base + threadIdx.x + j * NT;
     if (ul >= seg_len) continue;
     if (TOPK) {
-      const uint64_t key = score_key(weight[(int64_t)seg * seg_len + ul]);
+      const uint64_t key = score_key(cw[j]);
       if ((key & dg.himask) == pre) {
         const int b = (int)((key >> dg.lo) & dmask);
         atomicAdd((unsigned long long*)&h[b], 1ull);
@@ -622,17 +648,42 @@ alloc_hist(AllocWs a, const float* __restrict__ weight, const float* __restrict_
         kmx = key > kmx ? key : kmx;
       }
     } else {
-      // The float64 keys only where their float32 bounds may reach the prefix set (after the first
-      // pass, few units).  Key k of a thread's units often falls in the same bin as the previous
-      // one (nearly always on the first passes, where the bins are exponent ranges): each k's rates
-      // are summed in registers while the bin repeats, so the LDS atomics, which serialise on a
-      // shared address, come once per run.
+      // A key's prefix and digit come from its float32 bounds when the whole interval
+      // [ak - margin, ak + margin] that holds the exact key shares its bits at and above the digit's
+      // lowest bit: on the first passes, whose digit cells (2^53 and 2^42 patterns) are far wider
+      // than the margin (2^33), nearly every key.  Only the units with a key across a cell edge, or
+      // with estimates that are not normal floats, compute the float64 quotients, and then only
+      // where their bounds may reach the prefix set (after the first passes, few units).  A key
+      // decided by its bounds enters the set's extremes as its interval, so the extremes then differ
+      // and the single-value exit waits for a pass on exact keys: the selection stays exact.
+      // Key k of a thread's units often falls in the same bin as the previous one (nearly always on
+      // the first passes, where the bins are exponent ranges): each k's rates are summed in
+      // registers while the bin repeats, so the LDS atomics, which serialise on a shared address,
+      // come once per run.
       const int64_t sz = unit_size(stage, d, ul, a.rcount);
-      float cu = weight[ul];
-      if (sigma) cu = cu * sigma[ul];
-      if (!may_carry(cu, sz, pre, dg.hi)) continue;
+      const float cu = cw[j];
+      if (!(cu > 0.f) || sz <= 0) continue;      // no positive key
+      uint64_t ak[4], klo[4], khi[4];
+      bool by_bounds = key_bounds(cu, sz, ak);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        klo[k] = ak[k] > kKeyMargin ? ak[k] - kKeyMargin : 0ull;
+        khi[k] = ak[k] + kKeyMargin;
+        by_bounds = by_bounds && (klo[k] >> dg.lo) == (khi[k] >> dg.lo);
+      }
       uint64_t kk[4];
-      unit_keys(cu, sz, kk);
+      if (by_bounds) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) kk[k] = ak[k];
+      } else {
+        if (!may_carry(cu, sz, pre, dg.hi)) continue;
+        unit_keys(cu, sz, kk);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          klo[k] = kk[k];
+          khi[k] = kk[k];
+        }
+      }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         if (kk[k] != 0 && (kk[k] & dg.himask) == pre) {
@@ -645,8 +696,8 @@ alloc_hist(AllocWs a, const float* __restrict__ weight, const float* __restrict_
           } else {
             rs[k] += r;
           }
-          kmn = kk[k] < kmn ? kk[k] : kmn;
-          kmx = kk[k] > kmx ? kk[k] : kmx;
+          kmn = klo[k] < kmn ? klo[k] : kmn;
+          kmx = khi[k] > kmx ? khi[k] : kmx;
         }
       }
     }
@@ -701,10 +752,10 @@ alloc_select(AllocWs a, int pass, int nb) {
   }
 }
 
+// cu: the unit's cost (V/K) or score (top-k), from load_costs.
 template <bool TOPK>
-__device__ __forceinline__ int64_t unit_tie(const AllocWs& a, const float* weight, const float* sigma,
-                                            int64_t u, int64_t seg, int64_t seg_len, int stage, int d,
-                                            const SelState& s, int* n) {
+__device__ __forceinline__ int64_t unit_tie(const AllocWs& a, float cu, int64_t u, int64_t seg_len, int stage,
+                                            int d, const SelState& s, int* n) {
   if (u >= seg_len) {
     *n = 0;
     return 0;
@@ -714,12 +765,11 @@ __device__ __forceinline__ int64_t unit_tie(const AllocWs& a, const float* weigh
       *n = 0;
       return 0;
     }
-    const uint64_t key = score_key(weight[seg * seg_len + u]);
+    const uint64_t key = score_key(cu);
     *n = key > s.prefix ? 1 : 0;
     return key == s.prefix ? 1 : 0;
   }
-  float c = weight[u];
-  if (sigma) c = c * sigma[u];
+  const float c = cu;
   const int64_t sz = unit_size(stage, d, u, a.rcount);
   if (!(c > 0.f) || sz <= 0) {                 // no positive key: no step, no tie
     *n = 0;
@@ -758,11 +808,13 @@ alloc_ties(AllocWs a, const float* __restrict__ weight, const float* __restrict_
   const int seg = blockIdx.y;
   const SelState s = a.st[seg];
   const int64_t base = (int64_t)blockIdx.x * (256 * UPT) + threadIdx.x * UPT;
+  float cw[UPT];
+  load_costs<UPT>(weight, TOPK ? nullptr : sigma, TOPK ? (int64_t)seg * seg_len : 0, base, 1, seg_len, cw);
   int64_t t = 0;
 #pragma unroll
   for (int j = 0; j < UPT; ++j) {
     int n;
-    t += unit_tie<TOPK>(a, weight, sigma, base + j, seg, seg_len, stage, d, s, &n);
+    t += unit_tie<TOPK>(a, cw[j], base + j, seg_len, stage, d, s, &n);
   }
   const int64_t tot = block_scan_incl(t, wave_tot);
   if (threadIdx.x == 255) a.bsum[(int64_t)seg * gridDim.x + blockIdx.x] = tot;
@@ -781,12 +833,14 @@ alloc_assign(AllocWs a, const float* __restrict__ weight, const float* __restric
   const SelState s = a.st[seg];
   const int64_t base = (int64_t)blockIdx.x * (256 * UPT) + threadIdx.x * UPT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float cw[UPT];
+  load_costs<UPT>(weight, TOPK ? nullptr : sigma, TOPK ? (int64_t)seg * seg_len : 0, base, 1, seg_len, cw);
   int64_t tie[UPT];
   int n[UPT];
   int64_t tsum = 0;
 #pragma unroll
   for (int j = 0; j < UPT; ++j) {
-    tie[j] = unit_tie<TOPK>(a, weight, sigma, base + j, seg, seg_len, stage, d, s, &n[j]);
+    tie[j] = unit_tie<TOPK>(a, cw[j], base + j, seg_len, stage, d, s, &n[j]);
     tsum += tie[j];
   }
   const int64_t incl = block_scan_incl(tsum, wave_tot);
@@ -816,9 +870,7 @@ alloc_assign(AllocWs a, const float* __restrict__ weight, const float* __restric
       used += (int64_t)b * d;
     } else {
       used += unit_size(stage, d, u, a.rcount) * (int64_t)b;
-      float c = weight[u];
-      if (sigma) c = c * sigma[u];
-      dist += ldexp((double)c, -(int)b);
+      dist += ldexp((double)cw[j], -(int)b);
     }
   }
   const int64_t used_blk = block_scan_incl(used, wave_tot);
