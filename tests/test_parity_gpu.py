@@ -797,3 +797,58 @@ def test_attend_every_row_mixed_widths(case):
     ty, tl = H.attend_tols(x["q"], [x["k"]], [x["v"]], l_r)
     H.assert_abs(y_g.cpu().numpy(), y_r, ty, "attend output")
     H.assert_abs(l_g.cpu().numpy(), l_r, tl, "attend lse")
+
+
+def _bf16_bits(vals):
+    """bf16 bit patterns of float32 values that bf16 holds exactly."""
+    a = np.asarray(vals, dtype=np.float32).view(np.uint32)
+    assert not (a & 0xFFFF).any()
+    return (a >> 16).astype(np.uint16)
+
+
+# group patterns of 32 values: constant (scale 0: every code 0); a subnormal range of one bf16 ulp
+# (the float32 scale is subnormal and 1/scale overflows, so every value takes the float64 decision);
+# values on or next to half-integer code boundaries (round half to even, and the float64 decision
+# near a boundary)
+_TIE = [0.0, 0.5, 1.5, 2.5, 3.0, 1.0, 2.0, 0.5]
+EDGE_PATTERNS = {
+    "constant": _bf16_bits(np.full(32, 1.5)),
+    "subnormal_range": _bf16_bits(np.tile(np.array([0.0, 2.0 ** -133], np.float32), 16)),
+    "ties": _bf16_bits(np.tile(np.array(_TIE, np.float32), 4)),
+    "ties_wide": _bf16_bits(np.tile(np.array([0.0, 0.5, 7.5, 14.5, 15.0, 100.5, 127.5, 255.0], np.float32), 4)),
+}
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_pack_edge_groups(d):
+    """Quantize/pack of groups that take the quantiser's special paths, at every width and on
+    both axes: V groups along the channels of a token, K groups along the tokens of a channel.
+    Every packed buffer must match the oracle byte for byte."""
+    hq, hkv, N = 4, 2, 256
+    print(f"case pack_edge_d{d}", flush=True)
+    x = make_inputs(hq, hkv, d, N, N, seed=77 + d)
+    k, v = x["k"].copy(), x["v"].copy()
+    pats = list(EDGE_PATTERNS.values())
+    # V: token t's channel groups take the patterns in turn (the rest of the token stays random)
+    for g in range(hkv):
+        for t in range(0, 96):
+            for j in range(d // 32):
+                p = pats[(t + j) % len(pats)]
+                if (t + j) % 5 != 4:
+                    v[g, t, 32 * j:32 * (j + 1)] = p
+    # K: channel c's first three token groups take the patterns in turn
+    for g in range(hkv):
+        for c in range(d):
+            for grp in range(3):
+                p = pats[(c + grp) % len(pats)]
+                if (c + grp) % 5 != 4:
+                    k[g, 32 * grp:32 * (grp + 1), c] = p
+    widths = np.array([2, 4, 8, 16, 0], np.uint8)
+    bv = np.stack([widths[(np.arange(N) + g) % 5] for g in range(hkv)])
+    bv[:, :96] = np.array([2, 4, 8], np.uint8)[np.arange(96) % 3]     # planted tokens: quantised widths
+    bk = np.stack([widths[(np.arange(d) + 2 * g) % 5] for g in range(hkv)])
+    desc = H.desc_of(hq, hkv, d, N, N, True)
+    cache, st = H.pack(desc, H.dev_bf16(k), H.dev_bf16(v), H.dev_u8(bv), H.dev_u8(bk))
+    assert st == 0
+    ref = oracle.pack_cache(k, v, bv, bk)
+    H.compare_packed(cache.to_numpy(), ref)
