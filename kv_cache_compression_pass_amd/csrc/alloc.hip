@@ -85,6 +85,9 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// The four step keys of a unit of cost c and size s.  The passes recompute them from the weights
+// (the same float64 operations each time, so the same bits): cheaper than storing and re-reading
+// 32 bytes per unit.
 __device__ __forceinline__ void unit_keys(float c, int64_t s, uint64_t (&kk)[4]) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) kk[k] = 0;
@@ -539,15 +542,6 @@ alloc_begin(AllocWs a, int stage, int nseg, int Hkv, int64_t N, int d, int ncb, 
 
 __device__ __forceinline__ int64_t unit_size(int stage, int d, int64_t u, const int64_t* rcount) {
   return stage == KVC_ALLOC_V_TOKENS ? (int64_t)d : rcount[u / d];
-}
-
-// The four step keys of unit u, recomputed from its weight on every pass (the same float64
-// operations each time, so the same bits): cheaper than storing and re-reading 32 bytes.
-__device__ __forceinline__ void keys_of(const float* weight, const float* sigma, int stage, int d,
-                                        int64_t u, const int64_t* rcount, uint64_t (&kk)[4]) {
-  float c = weight[u];
-  if (sigma) c = c * sigma[u];
-  unit_keys(c, unit_size(stage, d, u, rcount), kk);
 }
 
 // Cheap bounds on the four step keys of a unit (cost c > 0, size s > 0), as float64 bit patterns:
